@@ -1,0 +1,152 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) attention-forward library.
+ *
+ * Computes Attention(Q,K,V) = softmax(scale * Q K^T) V tile by tile with an
+ * online softmax, so the Q_S x KV_S score matrix never exists in memory
+ * (FlashAttn operator guide, function description).  Three paths:
+ *   - prefill (Q_S >= 1) with an optional causal or boolean mask;
+ *   - incremental decode (Q_S == 1) against a padded KV cache with per-batch
+ *     actual lengths and grouped-query heads (aclnnIncreFlashAttention guide,
+ *     sections 1.1 and 4);
+ *   - FlashDecoding split-KV: stage 1 writes an unnormalised partial output
+ *     with its row maximum and exponential sum per KV chunk, stage 2 merges
+ *     them (FlashDecoding tutorial, sections 2 and 3; FlashAttn developer
+ *     guide, section 10).
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers (HBM).  The caller allocates and
+ *     owns all memory, workspace included; the library never allocates, never
+ *     synchronises the host and keeps no state between calls, so calls are
+ *     reentrant.  Buffers must stay valid until the stream has run the work.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued asynchronously; device faults surface at the caller's
+ *     next synchronisation.
+ *   - Validation is synchronous and complete before anything is enqueued: a
+ *     call that returns an error has launched nothing.  The message of the
+ *     last error on the calling thread is available from fa_last_error().
+ *   - q, k, v and out share one layout and one 16-bit storage type.
+ *       FA_BNSD: [B][N][S][D]    FA_BSND: [B][S][N][D]   (both contiguous)
+ *     BSH is BSND with H = N*D.  Base pointers must be 16-byte aligned.
+ *   - Query head n1 reads KV head n1 / g with g = num_heads / num_kv_heads:
+ *     g consecutive query heads share one KV head (FlashAttn developer guide,
+ *     1.1 MHA and GQA).
+ *   - lse is float32 [B][num_heads][q_seq] in every layout, natural log:
+ *     lse = log(sum_j exp(s_j - m)) + m (developer guide, 1.6 LSE).
+ *   - A row with no valid key (length 0, or every key masked) writes out = 0
+ *     and lse = +inf (developer guide, 1.7 RowInvalid).
+ *   - Output stores round to nearest even from fp32.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status classes after the aclnnIncreFlashAttention guide, section 4
+ * (null-pointer, invalid-parameter and runtime error codes). */
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULLPTR = 1,        /* a required pointer is NULL */
+    FA_ERR_PARAM_INVALID = 2,  /* shapes, sizes, options or alignment out of range */
+    FA_ERR_UNSUPPORTED = 3,    /* valid on the pages but not built here (e.g. head_dim 256) */
+    FA_ERR_RUNTIME = 4         /* the HIP runtime refused a launch */
+} fa_status;
+
+typedef enum { FA_BNSD = 0, FA_BSND = 1 } fa_layout;
+typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
+
+/* Mask modes (developer guide 1.5: 0 = none, 3 = causal; IFA guide 4 and 8.1:
+ * a boolean attenMask whose true entries are excluded). */
+typedef enum {
+    FA_MASK_NONE = 0,
+    FA_MASK_CAUSAL = 1,  /* key j > query i excluded (top-left aligned, absolute indices) */
+    FA_MASK_BOOL = 2     /* uint8 tensor, nonzero = excluded */
+} fa_mask_mode;
+
+typedef struct {
+    int64_t batch;            /* B >= 1 */
+    int64_t num_heads;        /* Q_N >= 1 */
+    int64_t num_kv_heads;     /* KV_N; 0 means num_heads (IFA guide 4); must divide Q_N */
+    int64_t q_seq;            /* Q_S >= 1 */
+    int64_t kv_seq;           /* KV_S >= 1: the padded cache length */
+    int64_t head_dim;         /* D: 64 or 128 built */
+    fa_layout layout;
+    fa_dtype dtype;
+    double scale;             /* softmax scale, finite (the pages default it to 1.0) */
+    /* Device int64 [batch] actual KV lengths, or NULL (= kv_seq).  Each value
+     * is clamped to [0, kv_seq] on the device; positions at or beyond it are
+     * never read into the result, whatever they hold (IFA guide 1.1; developer
+     * guide 1.4, the shorter length takes effect). */
+    const int64_t *actual_seq_lengths;
+    fa_mask_mode mask_mode;
+    /* FA_MASK_BOOL only (must be NULL otherwise): device uint8 mask addressed as
+     * mask[b*s0 + n1*s1 + i*s2 + j*s3] with mask_stride = {s0,s1,s2,s3} in
+     * elements; a stride of 0 broadcasts that axis (e.g. (B,1,1,S) or (1,1,S,S)). */
+    const uint8_t *mask;
+    int64_t mask_stride[4];
+} fa_params;
+
+/* fa_workspace_size -- phase 1 of fa_fwd (the two-phase shape of the IFA guide,
+ * section 3): bytes of device workspace fa_fwd needs for *p (0 when none).
+ * Also picks the split plan fa_fwd will use for q_seq == 1, for the device
+ * that is current on the calling thread. */
+fa_status fa_workspace_size(const fa_params *p, size_t *bytes);
+
+/* fa_fwd -- phase 2: the attention forward.  q: [B,Q_N,Q_S,D] or [B,Q_S,Q_N,D];
+ * k, v: the same layout with KV_N heads and KV_S rows; out: shape of q;
+ * lse: float32 [B,Q_N,Q_S] or NULL (not written).  q_seq == 1 without a mask
+ * runs the split-KV decode (stage 1 + combine, or stage 1 alone when one split
+ * suffices), whose split plan the library chooses (see fa_splitkv_plan); the
+ * workspace must then be at least fa_workspace_size bytes, 256-byte aligned.
+ * Every other case runs the prefill kernel and needs no workspace. */
+fa_status fa_fwd(const fa_params *p, const void *q, const void *k, const void *v,
+                 void *out, float *lse, void *workspace, size_t workspace_bytes,
+                 void *stream);
+
+/* fa_splitkv_plan -- the split-count heuristic (IFA guide 8.2: split the KV
+ * axis when B*KV_N is below 0.4 x the core count; FlashDecoding tutorial,
+ * preface: cut the cache so every core has a piece).  Host-only integer work.
+ *   num_cus: compute units to fill (<= 0: query the current device).
+ *   chunk_hint: tokens per split, a positive multiple of 64, or 0 = automatic.
+ * Returns num_splits >= 1 and chunk (a multiple of 64) with
+ * num_splits * chunk >= kv_seq, and the workspace bytes of the partials
+ * (o_part, m_part, l_part below) for that plan. */
+fa_status fa_splitkv_plan(const fa_params *p, int num_cus, int64_t chunk_hint,
+                          int64_t *num_splits, int64_t *chunk, size_t *workspace_bytes);
+
+/* fa_decode_splitkv -- FlashDecoding stage 1 (FlashDecoding tutorial 3.2;
+ * FlashAttn developer guide 10).  Requires q_seq == 1 and mask_mode NONE.
+ * Chunk c covers keys [c*chunk, (c+1)*chunk) cut at the batch's length.  For
+ * every (b, n1, c) it writes
+ *   m_part = max_j s_j,  l_part = sum_j exp(s_j - m_part),
+ *   o_part[d] = sum_j exp(s_j - m_part) v_j[d]    (NOT divided by l_part)
+ * with s_j = scale * q.k_j, natural units.  An empty chunk writes m = -inf,
+ * l = 0 and o = 0.  Layouts (float32, contiguous):
+ *   o_part [B][Q_N][num_splits][D], m_part and l_part [B][Q_N][num_splits].
+ * num_splits * chunk must cover kv_seq; chunk a positive multiple of 64. */
+fa_status fa_decode_splitkv(const fa_params *p, int64_t num_splits, int64_t chunk,
+                            const void *q, const void *k, const void *v,
+                            float *o_part, float *m_part, float *l_part, void *stream);
+
+/* fa_combine -- FlashDecoding stage 2, the LSE merge (FlashAttn developer
+ * guide 10: m = max_i m_i, l = sum_i l_i exp(m_i - m),
+ * o = sum_i o_i exp(m_i - m) / l; FlashDecoding tutorial section 2).  Reads the
+ * stage-1 layouts above for q_seq == 1 and writes out (shape of q, in p's
+ * layout and dtype) and lse (nullable) = log l + m.  Splits with m_i = -inf
+ * are skipped; a row whose splits are all empty writes 0 and +inf. */
+fa_status fa_combine(const fa_params *p, int64_t num_splits, const float *o_part,
+                     const float *m_part, const float *l_part, void *out, float *lse,
+                     void *stream);
+
+/* Text of the last non-OK status returned on the calling thread ("" if none). */
+const char *fa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

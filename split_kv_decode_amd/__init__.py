@@ -1,0 +1,185 @@
+"""Python binding of the gfx950 attention-forward library (include/fa.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libfa_mi355x.so``.  The low-level functions carry the C names
+(``fa_fwd``, ``fa_workspace_size``, ``fa_splitkv_plan``, ``fa_decode_splitkv``,
+``fa_combine``, ``fa_last_error``) and take device pointers as ints or torch
+tensors; ``fwd`` is a convenience wrapper that allocates the outputs and the
+workspace with torch on the current stream.  There is no CPU fallback: if the
+shared library is missing, loading fails with an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+from typing import Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfa_mi355x.so")
+
+FA_OK, FA_ERR_NULLPTR, FA_ERR_PARAM_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_RUNTIME = range(5)
+FA_BNSD, FA_BSND = 0, 1
+FA_F16, FA_BF16 = 0, 1
+FA_MASK_NONE, FA_MASK_CAUSAL, FA_MASK_BOOL = 0, 1, 2
+
+EXPORTS = ("fa_workspace_size", "fa_fwd", "fa_splitkv_plan", "fa_decode_splitkv", "fa_combine",
+           "fa_last_error")
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"fa status {status}: {message}")
+        self.status = status
+
+
+class FaParams(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("num_heads", ctypes.c_int64),
+                ("num_kv_heads", ctypes.c_int64), ("q_seq", ctypes.c_int64),
+                ("kv_seq", ctypes.c_int64), ("head_dim", ctypes.c_int64),
+                ("layout", ctypes.c_int), ("dtype", ctypes.c_int), ("scale", ctypes.c_double),
+                ("actual_seq_lengths", ctypes.c_void_p), ("mask_mode", ctypes.c_int),
+                ("mask", ctypes.c_void_p), ("mask_stride", ctypes.c_int64 * 4)]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load(path: Optional[str] = None):
+    """Load (once) and return the ctypes handle of the HIP library."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            p = path or LIB_PATH
+            if not os.path.exists(p):
+                raise RuntimeError(f"HIP library {p} is not built; run __graft_entry__.build() "
+                                   "(there is no CPU fallback)")
+            lib = ctypes.CDLL(p)
+            P = ctypes.POINTER
+            vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+            lib.fa_workspace_size.argtypes = [P(FaParams), P(sz)]
+            lib.fa_fwd.argtypes = [P(FaParams), vp, vp, vp, vp, vp, vp, sz, vp]
+            lib.fa_splitkv_plan.argtypes = [P(FaParams), ctypes.c_int, i64, P(i64), P(i64), P(sz)]
+            lib.fa_decode_splitkv.argtypes = [P(FaParams), i64, i64, vp, vp, vp, vp, vp, vp, vp]
+            lib.fa_combine.argtypes = [P(FaParams), i64, vp, vp, vp, vp, vp, vp]
+            for f in (lib.fa_workspace_size, lib.fa_fwd, lib.fa_splitkv_plan, lib.fa_decode_splitkv,
+                      lib.fa_combine):
+                f.restype = ctypes.c_int
+            lib.fa_last_error.argtypes = []
+            lib.fa_last_error.restype = ctypes.c_char_p
+            _lib = lib
+    return _lib
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s) -> Optional[int]:
+    if s is None:
+        return None
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream  # torch.cuda.Stream -> hipStream_t
+
+
+def fa_last_error() -> str:
+    return load().fa_last_error().decode()
+
+
+def _check(st: int):
+    if st != FA_OK:
+        raise FaError(st, fa_last_error())
+
+
+def make_params(batch, num_heads, q_seq, kv_seq, head_dim, *, num_kv_heads=0, layout="BNSD",
+                dtype="bf16", scale=1.0, actual_seq_lengths=None, mask_mode="none", mask=None,
+                mask_stride: Sequence[int] = (0, 0, 0, 0)) -> FaParams:
+    p = FaParams()
+    p.batch, p.num_heads, p.num_kv_heads = batch, num_heads, num_kv_heads
+    p.q_seq, p.kv_seq, p.head_dim = q_seq, kv_seq, head_dim
+    p.layout = {"BNSD": FA_BNSD, "BSND": FA_BSND}[layout] if isinstance(layout, str) else layout
+    p.dtype = {"f16": FA_F16, "bf16": FA_BF16}[dtype] if isinstance(dtype, str) else dtype
+    p.scale = float(scale)
+    p.actual_seq_lengths = _ptr(actual_seq_lengths)
+    p.mask_mode = ({"none": FA_MASK_NONE, "causal": FA_MASK_CAUSAL, "bool": FA_MASK_BOOL}[mask_mode]
+                   if isinstance(mask_mode, str) else mask_mode)
+    p.mask = _ptr(mask)
+    for i in range(4):
+        p.mask_stride[i] = int(mask_stride[i])
+    return p
+
+
+def fa_workspace_size(params: FaParams) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().fa_workspace_size(ctypes.byref(params), ctypes.byref(n)))
+    return n.value
+
+
+def fa_fwd(params: FaParams, q, k, v, out, lse=None, workspace=None, workspace_bytes=0, stream=None):
+    _check(load().fa_fwd(ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                         _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def fa_splitkv_plan(params: FaParams, num_cus: int = 0, chunk_hint: int = 0):
+    sp, ch, ws = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_size_t(0)
+    _check(load().fa_splitkv_plan(ctypes.byref(params), int(num_cus), int(chunk_hint),
+                                  ctypes.byref(sp), ctypes.byref(ch), ctypes.byref(ws)))
+    return sp.value, ch.value, ws.value
+
+
+def fa_decode_splitkv(params: FaParams, num_splits, chunk, q, k, v, o_part, m_part, l_part,
+                      stream=None):
+    _check(load().fa_decode_splitkv(ctypes.byref(params), int(num_splits), int(chunk), _ptr(q),
+                                    _ptr(k), _ptr(v), _ptr(o_part), _ptr(m_part), _ptr(l_part),
+                                    _stream(stream)))
+
+
+def fa_combine(params: FaParams, num_splits, o_part, m_part, l_part, out, lse=None, stream=None):
+    _check(load().fa_combine(ctypes.byref(params), int(num_splits), _ptr(o_part), _ptr(m_part),
+                             _ptr(l_part), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+# ----------------------------------------------------------------- torch conveniences
+
+def params_for(q, k, *, layout="BNSD", num_kv_heads=0, scale=1.0, actual_seq_lengths=None,
+               mask=None, mask_stride=(0, 0, 0, 0), causal=False) -> FaParams:
+    """FaParams from torch tensors q, k in ``layout`` (shapes as in include/fa.h)."""
+    import torch
+    if layout == "BNSD":
+        B, N, QS, D = q.shape
+        KVN, KVS = k.shape[1], k.shape[2]
+    else:
+        B, QS, N, D = q.shape
+        KVS, KVN = k.shape[1], k.shape[2]
+    dtype = {torch.bfloat16: "bf16", torch.float16: "f16"}[q.dtype]
+    mode = "bool" if mask is not None else ("causal" if causal else "none")
+    return make_params(B, N, QS, KVS, D, num_kv_heads=num_kv_heads or KVN, layout=layout,
+                       dtype=dtype, scale=scale, actual_seq_lengths=actual_seq_lengths,
+                       mask_mode=mode, mask=mask, mask_stride=mask_stride)
+
+
+def fwd(q, k, v, *, layout="BNSD", scale=None, actual_seq_lengths=None, mask=None,
+        mask_stride=(0, 0, 0, 0), causal=False, return_lse=False, stream=None):
+    """Attention forward on device tensors; allocates out (and lse, workspace) with torch."""
+    import torch
+    D = q.shape[-1]
+    sc = (1.0 / math.sqrt(D)) if scale is None else scale
+    p = params_for(q, k, layout=layout, scale=sc, actual_seq_lengths=actual_seq_lengths,
+                   mask=mask, mask_stride=mask_stride, causal=causal)
+    out = torch.empty_like(q)
+    lse = (torch.empty((p.batch, p.num_heads, p.q_seq), dtype=torch.float32, device=q.device)
+           if return_lse else None)
+    nbytes = fa_workspace_size(p)
+    ws = torch.empty((nbytes,), dtype=torch.uint8, device=q.device) if nbytes else None
+    s = stream if stream is not None else torch.cuda.current_stream()
+    if ws is not None and isinstance(s, torch.cuda.Stream):
+        ws.record_stream(s)
+    fa_fwd(p, q, k, v, out, lse, ws, nbytes, s)
+    return (out, lse) if return_lse else out

@@ -1,0 +1,354 @@
+// fa_api.cpp -- the C ABI declared in include/fa.h: parameter validation
+// (complete before anything is enqueued), the split-KV planner and dispatch to
+// the gfx950 kernels.  Host-only code; it never allocates device memory and
+// never synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "fa.h"
+#include "fa_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fa_status fail(fa_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+fa_status ok() { return FA_OK; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Largest products stay far below 2^62 for any accepted shape.
+constexpr int64_t kMaxDim = int64_t(1) << 31;
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+constexpr int64_t kMaxSplits = 1 << 20;
+
+struct Shape {
+    int64_t B, QN, KVN, QS, KVS, D, g;
+};
+
+fa_status check_params(const fa_params* p, Shape* s) {
+    if (!p) return fail(FA_ERR_NULLPTR, "params is NULL");
+    if (p->batch < 1 || p->batch >= kMaxDim) return fail(FA_ERR_PARAM_INVALID, "batch must be in [1, 2^31), got %lld", (long long)p->batch);
+    if (p->num_heads < 1 || p->num_heads >= kMaxDim)
+        return fail(FA_ERR_PARAM_INVALID, "num_heads must be in [1, 2^31), got %lld", (long long)p->num_heads);
+    if (p->num_kv_heads < 0 || p->num_kv_heads >= kMaxDim)
+        return fail(FA_ERR_PARAM_INVALID, "num_kv_heads must be >= 0, got %lld", (long long)p->num_kv_heads);
+    const int64_t kvn = p->num_kv_heads == 0 ? p->num_heads : p->num_kv_heads;
+    if (p->num_heads % kvn != 0)
+        return fail(FA_ERR_PARAM_INVALID, "num_heads (%lld) must be a multiple of num_kv_heads (%lld)",
+                    (long long)p->num_heads, (long long)kvn);
+    if (p->q_seq < 1 || p->q_seq >= kMaxDim) return fail(FA_ERR_PARAM_INVALID, "q_seq must be in [1, 2^31), got %lld", (long long)p->q_seq);
+    if (p->kv_seq < 1 || p->kv_seq >= kMaxDim) return fail(FA_ERR_PARAM_INVALID, "kv_seq must be in [1, 2^31), got %lld", (long long)p->kv_seq);
+    if (p->head_dim != 64 && p->head_dim != 128) {
+        if (p->head_dim > 0 && p->head_dim <= 512 && p->head_dim % 16 == 0)
+            return fail(FA_ERR_UNSUPPORTED, "head_dim %lld is not built (64 and 128 are)", (long long)p->head_dim);
+        return fail(FA_ERR_PARAM_INVALID, "head_dim must be a positive multiple of 16 up to 512, got %lld",
+                    (long long)p->head_dim);
+    }
+    if (p->layout != FA_BNSD && p->layout != FA_BSND) return fail(FA_ERR_PARAM_INVALID, "unknown layout %d", (int)p->layout);
+    if (p->dtype != FA_F16 && p->dtype != FA_BF16) return fail(FA_ERR_PARAM_INVALID, "unknown dtype %d", (int)p->dtype);
+    if (!std::isfinite(p->scale)) return fail(FA_ERR_PARAM_INVALID, "scale must be finite");
+    if (p->mask_mode != FA_MASK_NONE && p->mask_mode != FA_MASK_CAUSAL && p->mask_mode != FA_MASK_BOOL)
+        return fail(FA_ERR_PARAM_INVALID, "unknown mask_mode %d", (int)p->mask_mode);
+    if (p->mask_mode == FA_MASK_BOOL && !p->mask) return fail(FA_ERR_NULLPTR, "mask_mode BOOL needs a mask tensor");
+    if (p->mask_mode != FA_MASK_BOOL && p->mask)
+        return fail(FA_ERR_PARAM_INVALID, "a mask tensor was passed but mask_mode is not BOOL");
+    if (p->mask_mode == FA_MASK_BOOL)
+        for (int i = 0; i < 4; ++i)
+            if (p->mask_stride[i] < 0) return fail(FA_ERR_PARAM_INVALID, "mask strides must be >= 0");
+    s->B = p->batch;
+    s->QN = p->num_heads;
+    s->KVN = kvn;
+    s->QS = p->q_seq;
+    s->KVS = p->kv_seq;
+    s->D = p->head_dim;
+    s->g = p->num_heads / kvn;
+    if (s->B * s->QN > kMaxDim || s->B * kvn > kMaxDim)
+        return fail(FA_ERR_PARAM_INVALID, "batch * heads must stay below 2^31");
+    const double qe = double(s->B) * double(s->QN) * double(s->QS) * double(s->D);
+    const double ke = double(s->B) * double(s->KVN) * double(s->KVS) * double(s->D);
+    if (qe >= double(kMaxElems) || ke >= double(kMaxElems)) return fail(FA_ERR_PARAM_INVALID, "tensor too large");
+    return ok();
+}
+
+fa_status check_tensors(const void* q, const void* k, const void* v, const void* out, const float* lse) {
+    if (!q || !k || !v) return fail(FA_ERR_NULLPTR, "q, k and v must not be NULL");
+    if (!out) return fail(FA_ERR_NULLPTR, "out must not be NULL");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+        return fail(FA_ERR_PARAM_INVALID, "q, k, v and out must be 16-byte aligned");
+    if (lse && !aligned(lse, 4)) return fail(FA_ERR_PARAM_INVALID, "lse must be 4-byte aligned");
+    return ok();
+}
+
+int heads_per_workgroup(int64_t g) {
+    if (g % 8 == 0) return 8;
+    if (g % 4 == 0) return 4;
+    if (g % 2 == 0) return 2;
+    return 1;
+}
+
+int device_cus() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+    return n;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Partials {
+    size_t o_bytes, m_bytes, total;
+};
+
+Partials partial_bytes(const Shape& s, int64_t splits) {
+    Partials r;
+    const size_t rows = size_t(s.B) * size_t(s.QN) * size_t(splits);
+    r.o_bytes = round_up(rows * size_t(s.D) * sizeof(float), 256);
+    r.m_bytes = round_up(rows * sizeof(float), 256);
+    r.total = r.o_bytes + 2 * r.m_bytes;
+    return r;
+}
+
+// Split plan.  Decode reads each KV byte once, so every CU must stream: aim for
+// about four stage-1 workgroups (16 waves) per CU.  The units of independent
+// work are (b, kv head, head group); when there are fewer than that target,
+// the KV axis is cut into chunks (multiples of 64 tokens, at least 256) so that
+// units * splits reaches it.  One split means stage 1 finishes in place.
+constexpr int64_t kMinChunk = 256;
+constexpr int64_t kWgPerCu = 4;
+
+void plan_splits(const Shape& s, int num_cus, int64_t* splits, int64_t* chunk) {
+    const int gh = heads_per_workgroup(s.g);
+    const int64_t units = s.B * s.KVN * (s.g / gh);
+    const int64_t target = kWgPerCu * int64_t(num_cus > 0 ? num_cus : 256);
+    int64_t want = (target + units - 1) / units;
+    if (want < 1) want = 1;
+    int64_t c = (s.KVS + want - 1) / want;
+    c = (c + 63) / 64 * 64;
+    const int64_t kv_round = (s.KVS + 63) / 64 * 64;
+    if (c < kMinChunk) c = kMinChunk < kv_round ? kMinChunk : kv_round;
+    *chunk = c;
+    *splits = (s.KVS + c - 1) / c;
+}
+
+bool decode_path(const fa_params* p) { return p->q_seq == 1 && p->mask_mode == FA_MASK_NONE; }
+
+void fill_decode_args(const fa_params* p, const Shape& s, fa::DecodeArgs* a) {
+    std::memset(a, 0, sizeof *a);
+    a->lens = p->actual_seq_lengths;
+    a->kv_seq = s.KVS;
+    if (p->layout == FA_BNSD) {
+        a->kv_stride_s = s.D;
+        a->kv_stride_n = s.KVS * s.D;
+        a->kv_stride_b = s.KVN * s.KVS * s.D;
+    } else {
+        a->kv_stride_s = s.KVN * s.D;
+        a->kv_stride_n = s.D;
+        a->kv_stride_b = s.KVS * s.KVN * s.D;
+    }
+    a->num_heads = (int32_t)s.QN;
+    a->num_kv_heads = (int32_t)s.KVN;
+    a->group = (int32_t)s.g;
+    const int gh = heads_per_workgroup(s.g);
+    a->head_groups = (int32_t)(s.g / gh);
+    a->scale_log2 = (float)(p->scale * 1.4426950408889634);
+}
+
+fa_status launch_result(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(FA_ERR_RUNTIME, "%s launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+fa_status run_stage1(const fa_params* p, const Shape& s, int64_t splits, int64_t chunk, const void* q, const void* k,
+                     const void* v, float* o_part, float* m_part, float* l_part, void* out, float* lse,
+                     hipStream_t stream) {
+    fa::DecodeArgs a;
+    fill_decode_args(p, s, &a);
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.o_part = o_part;
+    a.m_part = m_part;
+    a.l_part = l_part;
+    a.out = out;
+    a.lse = lse;
+    a.chunk = chunk;
+    a.num_splits = (int32_t)splits;
+    const bool finish = (out != nullptr);
+    return launch_result(fa::launch_decode_stage1(a, p->dtype == FA_BF16 ? 1 : 0, (int)s.D,
+                                                  heads_per_workgroup(s.g), finish, s.B, stream),
+                         "decode stage 1");
+}
+
+fa_status run_combine(const fa_params* p, const Shape& s, int64_t splits, const float* o_part, const float* m_part,
+                      const float* l_part, void* out, float* lse, hipStream_t stream) {
+    fa::CombineArgs a;
+    a.o_part = o_part;
+    a.m_part = m_part;
+    a.l_part = l_part;
+    a.out = out;
+    a.lse = lse;
+    a.rows = s.B * s.QN;
+    a.num_splits = (int32_t)splits;
+    return launch_result(fa::launch_combine(a, p->dtype == FA_BF16 ? 1 : 0, (int)s.D, stream), "combine");
+}
+
+fa_status run_prefill(const fa_params* p, const Shape& s, const void* q, const void* k, const void* v, void* out,
+                      float* lse, hipStream_t stream) {
+    fa::PrefillArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.out = out;
+    a.lse = lse;
+    a.lens = p->actual_seq_lengths;
+    a.mask = p->mask;
+    for (int i = 0; i < 4; ++i) a.mask_stride[i] = p->mask_stride[i];
+    a.q_seq = s.QS;
+    a.kv_seq = s.KVS;
+    if (p->layout == FA_BNSD) {
+        a.q_stride_s = s.D;
+        a.q_stride_n = s.QS * s.D;
+        a.q_stride_b = s.QN * s.QS * s.D;
+        a.kv_stride_s = s.D;
+        a.kv_stride_n = s.KVS * s.D;
+        a.kv_stride_b = s.KVN * s.KVS * s.D;
+    } else {
+        a.q_stride_s = s.QN * s.D;
+        a.q_stride_n = s.D;
+        a.q_stride_b = s.QS * s.QN * s.D;
+        a.kv_stride_s = s.KVN * s.D;
+        a.kv_stride_n = s.D;
+        a.kv_stride_b = s.KVS * s.KVN * s.D;
+    }
+    a.num_heads = (int32_t)s.QN;
+    a.num_kv_heads = (int32_t)s.KVN;
+    a.group = (int32_t)s.g;
+    a.q_tiles = (int32_t)((s.QS + 127) / 128);
+    a.scale_log2 = (float)(p->scale * 1.4426950408889634);
+    const int mm = p->mask_mode == FA_MASK_NONE ? 0 : (p->mask_mode == FA_MASK_CAUSAL ? 1 : 2);
+    return launch_result(fa::launch_prefill(a, p->dtype == FA_BF16 ? 1 : 0, (int)s.D, mm, s.B, stream), "prefill");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_last_error(void) { return g_last_error.c_str(); }
+
+fa_status fa_splitkv_plan(const fa_params* p, int num_cus, int64_t chunk_hint, int64_t* num_splits, int64_t* chunk,
+                          size_t* workspace_bytes) {
+    Shape s;
+    fa_status st = check_params(p, &s);
+    if (st != FA_OK) return st;
+    if (!num_splits || !chunk) return fail(FA_ERR_NULLPTR, "num_splits and chunk outputs must not be NULL");
+    if (chunk_hint < 0 || chunk_hint % 64 != 0)
+        return fail(FA_ERR_PARAM_INVALID, "chunk_hint must be 0 or a positive multiple of 64, got %lld",
+                    (long long)chunk_hint);
+    int64_t sp, c;
+    if (chunk_hint > 0) {
+        c = chunk_hint;
+        sp = (s.KVS + c - 1) / c;
+    } else {
+        plan_splits(s, num_cus > 0 ? num_cus : device_cus(), &sp, &c);
+    }
+    if (sp > kMaxSplits) return fail(FA_ERR_PARAM_INVALID, "plan needs %lld splits (max %lld)", (long long)sp, (long long)kMaxSplits);
+    *num_splits = sp;
+    *chunk = c;
+    if (workspace_bytes) *workspace_bytes = partial_bytes(s, sp).total;
+    return ok();
+}
+
+fa_status fa_workspace_size(const fa_params* p, size_t* bytes) {
+    Shape s;
+    fa_status st = check_params(p, &s);
+    if (st != FA_OK) return st;
+    if (!bytes) return fail(FA_ERR_NULLPTR, "bytes output must not be NULL");
+    *bytes = 0;
+    if (!decode_path(p)) return ok();
+    int64_t sp, c;
+    plan_splits(s, device_cus(), &sp, &c);
+    if (sp > 1) *bytes = partial_bytes(s, sp).total;
+    return ok();
+}
+
+fa_status fa_fwd(const fa_params* p, const void* q, const void* k, const void* v, void* out, float* lse,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+    Shape s;
+    fa_status st = check_params(p, &s);
+    if (st != FA_OK) return st;
+    st = check_tensors(q, k, v, out, lse);
+    if (st != FA_OK) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (!decode_path(p)) return run_prefill(p, s, q, k, v, out, lse, hs);
+
+    int64_t sp, c;
+    plan_splits(s, device_cus(), &sp, &c);
+    if (sp > kMaxSplits) return fail(FA_ERR_PARAM_INVALID, "plan needs too many splits");
+    if (sp == 1) return run_stage1(p, s, 1, c, q, k, v, nullptr, nullptr, nullptr, out, lse, hs);
+    const Partials pb = partial_bytes(s, sp);
+    if (!workspace) return fail(FA_ERR_NULLPTR, "this call needs %zu bytes of workspace (fa_workspace_size)", pb.total);
+    if (!aligned(workspace, 256)) return fail(FA_ERR_PARAM_INVALID, "workspace must be 256-byte aligned");
+    if (workspace_bytes < pb.total)
+        return fail(FA_ERR_PARAM_INVALID, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, pb.total);
+    char* w = static_cast<char*>(workspace);
+    float* o_part = reinterpret_cast<float*>(w);
+    float* m_part = reinterpret_cast<float*>(w + pb.o_bytes);
+    float* l_part = reinterpret_cast<float*>(w + pb.o_bytes + pb.m_bytes);
+    st = run_stage1(p, s, sp, c, q, k, v, o_part, m_part, l_part, nullptr, nullptr, hs);
+    if (st != FA_OK) return st;
+    return run_combine(p, s, sp, o_part, m_part, l_part, out, lse, hs);
+}
+
+fa_status fa_decode_splitkv(const fa_params* p, int64_t num_splits, int64_t chunk, const void* q, const void* k,
+                            const void* v, float* o_part, float* m_part, float* l_part, void* stream) {
+    Shape s;
+    fa_status st = check_params(p, &s);
+    if (st != FA_OK) return st;
+    if (p->q_seq != 1) return fail(FA_ERR_PARAM_INVALID, "split-KV decode needs q_seq == 1, got %lld", (long long)p->q_seq);
+    if (p->mask_mode != FA_MASK_NONE) return fail(FA_ERR_PARAM_INVALID, "split-KV decode takes no mask");
+    if (!q || !k || !v) return fail(FA_ERR_NULLPTR, "q, k and v must not be NULL");
+    if (!o_part || !m_part || !l_part) return fail(FA_ERR_NULLPTR, "o_part, m_part and l_part must not be NULL");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+        return fail(FA_ERR_PARAM_INVALID, "q, k and v must be 16-byte aligned");
+    if (!aligned(o_part, 4) || !aligned(m_part, 4) || !aligned(l_part, 4))
+        return fail(FA_ERR_PARAM_INVALID, "partials must be 4-byte aligned");
+    if (num_splits < 1 || num_splits > kMaxSplits) return fail(FA_ERR_PARAM_INVALID, "num_splits must be in [1, 2^20]");
+    if (chunk < 64 || chunk % 64 != 0) return fail(FA_ERR_PARAM_INVALID, "chunk must be a positive multiple of 64");
+    if (num_splits * chunk < s.KVS)
+        return fail(FA_ERR_PARAM_INVALID, "num_splits * chunk (%lld) must cover kv_seq (%lld)",
+                    (long long)(num_splits * chunk), (long long)s.KVS);
+    return run_stage1(p, s, num_splits, chunk, q, k, v, o_part, m_part, l_part, nullptr, nullptr,
+                      static_cast<hipStream_t>(stream));
+}
+
+fa_status fa_combine(const fa_params* p, int64_t num_splits, const float* o_part, const float* m_part,
+                     const float* l_part, void* out, float* lse, void* stream) {
+    Shape s;
+    fa_status st = check_params(p, &s);
+    if (st != FA_OK) return st;
+    if (p->q_seq != 1) return fail(FA_ERR_PARAM_INVALID, "combine needs q_seq == 1, got %lld", (long long)p->q_seq);
+    if (!o_part || !m_part || !l_part) return fail(FA_ERR_NULLPTR, "o_part, m_part and l_part must not be NULL");
+    if (!out) return fail(FA_ERR_NULLPTR, "out must not be NULL");
+    if (!aligned(out, 16)) return fail(FA_ERR_PARAM_INVALID, "out must be 16-byte aligned");
+    if (lse && !aligned(lse, 4)) return fail(FA_ERR_PARAM_INVALID, "lse must be 4-byte aligned");
+    if (num_splits < 1 || num_splits > kMaxSplits) return fail(FA_ERR_PARAM_INVALID, "num_splits must be in [1, 2^20]");
+    return run_combine(p, s, num_splits, o_part, m_part, l_part, out, lse, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,327 @@
+// fa_decode.hip -- split-KV decode for gfx950: stage 1 (per-chunk partial
+// softmax statistics and unnormalised output) and stage 2 (the LSE combine).
+//
+// Stage 1 follows the FlashDecoding tutorial (section 3.2): each workgroup owns
+// one KV chunk of one KV head, keeps the query resident, streams the chunk's K
+// and V rows once, and writes O_c = sum_j exp(s_j - m_c) v_j (not divided by
+// l_c) together with m_c and l_c.  Stage 2 merges the chunks with the FD
+// reduction of the FlashAttn developer guide (section 10).
+//
+// Decode reads every cached K/V byte once and does ~2 FMAs per byte, so it is
+// bound by HBM bandwidth.  The kernel is laid out for that: D/8 lanes cover one
+// 16-byte-per-lane KV row, so one wave load instruction reads 4 (D=128) or
+// 8 (D=64) whole rows = 1 KiB contiguous in the BNSD layout; the next
+// iteration's K and V are in flight while the current rows are consumed; the
+// dot product is reduced across the row's lanes with DPP moves.  Each lane
+// group (the lanes of one row slot) keeps its own running max / sum / output,
+// so the streaming loop has no cross-group traffic; groups and waves are
+// merged once at the end.  The g query heads that share a KV head (GQA) are
+// processed by the same workgroup so their K/V rows are read once.
+#include "fa_device.h"
+#include "fa_kernels.h"
+
+namespace fa {
+
+template <typename ST, int D, int GH, bool FINISH>
+__global__ __launch_bounds__(256) void decode_stage1_kernel(DecodeArgs a) {
+    constexpr int LPR = D / 8;     // lanes per KV row
+    constexpr int RPL = 64 / LPR;  // rows per wave load
+    constexpr int U = (GH >= 4) ? 2 : 4;  // row slots per lane per iteration
+    constexpr int TW = RPL * U;    // tokens per wave iteration
+    constexpr int NW = 4;          // waves per workgroup
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int sub = lane % LPR;
+    const int grp = lane / LPR;
+
+    const int64_t blk = blockIdx.x;
+    const int split = (int)(blk % a.num_splits);
+    const int64_t unit = blk / a.num_splits;
+    const int hg = (int)(unit % a.head_groups);
+    const int64_t bn2 = unit / a.head_groups;
+    const int n2 = (int)(bn2 % a.num_kv_heads);
+    const int64_t b = bn2 / a.num_kv_heads;
+
+    int64_t L = a.kv_seq;
+    if (a.lens) {
+        L = a.lens[b];
+        L = L < 0 ? 0 : (L > a.kv_seq ? a.kv_seq : L);
+    }
+    const int64_t c0 = (int64_t)split * a.chunk;
+    int64_t c1 = c0 + a.chunk;
+    if (c1 > L) c1 = L;
+
+    // Resident query slice, pre-scaled by scale*log2(e) so scores are in base 2.
+    float qf[GH][8];
+#pragma unroll
+    for (int h = 0; h < GH; ++h) {
+        const int gi = hg * GH + h;
+        if (gi < a.group) {
+            const int64_t n1 = (int64_t)n2 * a.group + gi;
+            const u32x4 w = ld128(a.q + (b * a.num_heads + n1) * D + sub * 8);
+            unpack8<ST>(w, qf[h]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qf[h][e] *= a.scale_log2;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qf[h][e] = 0.f;
+        }
+    }
+
+    float m[GH], l[GH], acc[GH][8];
+#pragma unroll
+    for (int h = 0; h < GH; ++h) {
+        m[h] = kNegInf;
+        l[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    }
+
+    const int64_t head_off = b * a.kv_stride_b + (int64_t)n2 * a.kv_stride_n + sub * 8;
+    const uint16_t* kb = a.k + head_off;
+    const uint16_t* vb = a.v + head_off;
+    const int64_t ss = a.kv_stride_s;
+
+    auto load = [&](int64_t t0, u32x4* kw, u32x4* vw) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t t = t0 + u * RPL + grp;
+            if (t < c1) {
+                kw[u] = ld128(kb + t * ss);
+                vw[u] = ld128(vb + t * ss);
+            } else {
+                kw[u] = u32x4{0u, 0u, 0u, 0u};
+                vw[u] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+
+    int64_t t0 = c0 + (int64_t)wave * TW;
+    u32x4 kw[U], vw[U];
+    load(t0, kw, vw);
+    while (t0 < c1) {
+        const int64_t tn = t0 + NW * TW;
+        u32x4 kn[U], vn[U];
+        load(tn, kn, vn);
+
+        float kf[U][8], vf[U][8];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            unpack8<ST>(kw[u], kf[u]);
+            unpack8<ST>(vw[u], vf[u]);
+        }
+#pragma unroll
+        for (int h = 0; h < GH; ++h) {
+            float s[U];
+            float mx = m[h];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float part = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) part = __builtin_fmaf(qf[h][e], kf[u][e], part);
+                part = group_sum<LPR>(part);
+                s[u] = (t0 + u * RPL + grp < c1) ? part : kNegInf;
+                mx = fmaxf(mx, s[u]);
+            }
+            const float ms = (mx == kNegInf) ? 0.f : mx;
+            const float alpha = fast_exp2(m[h] - ms);
+            float psum = 0.f;
+            float p[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                p[u] = fast_exp2(s[u] - ms);
+                psum += p[u];
+            }
+            l[h] = __builtin_fmaf(l[h], alpha, psum);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float x = acc[h][e] * alpha;
+#pragma unroll
+                for (int u = 0; u < U; ++u) x = __builtin_fmaf(p[u], vf[u][e], x);
+                acc[h][e] = x;
+            }
+            m[h] = mx;
+        }
+        t0 = tn;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            kw[u] = kn[u];
+            vw[u] = vn[u];
+        }
+    }
+
+    // Merge the row-slot groups of this wave (lanes that share `sub`).
+#pragma unroll
+    for (int h = 0; h < GH; ++h) {
+        float M = m[h];
+#pragma unroll
+        for (int off = LPR; off < 64; off <<= 1) M = fmaxf(M, shfl_xor(M, off));
+        const float ms = (M == kNegInf) ? 0.f : M;
+        const float f = fast_exp2(m[h] - ms);
+        float lw = l[h] * f;
+#pragma unroll
+        for (int off = LPR; off < 64; off <<= 1) lw += shfl_xor(lw, off);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float x = acc[h][e] * f;
+#pragma unroll
+            for (int off = LPR; off < 64; off <<= 1) x += shfl_xor(x, off);
+            acc[h][e] = x;
+        }
+        m[h] = M;
+        l[h] = lw;
+    }
+
+    // Merge the waves through LDS and write the chunk's result.
+    __shared__ float s_m[NW][GH];
+    __shared__ float s_l[NW][GH];
+    __shared__ float s_acc[NW][GH][D];
+    if (grp == 0) {
+#pragma unroll
+        for (int h = 0; h < GH; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s_acc[wave][h][sub * 8 + e] = acc[h][e];
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < GH; ++h) {
+            s_m[wave][h] = m[h];
+            s_l[wave][h] = l[h];
+        }
+    }
+    __syncthreads();
+
+    for (int idx = threadIdx.x; idx < GH * D; idx += 256) {
+        const int h = idx / D;
+        const int d = idx % D;
+        const int gi = hg * GH + h;
+        if (gi >= a.group) continue;
+        float M = kNegInf;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][h]);
+        const float ms = (M == kNegInf) ? 0.f : M;
+        float Lt = 0.f, A = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float f = fast_exp2(s_m[w][h] - ms);
+            Lt = __builtin_fmaf(s_l[w][h], f, Lt);
+            A = __builtin_fmaf(s_acc[w][h][d], f, A);
+        }
+        const int64_t row = b * a.num_heads + (int64_t)n2 * a.group + gi;
+        if constexpr (FINISH) {
+            const bool empty = (M == kNegInf);
+            uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+            out[row * D + d] = to_bits<ST>(empty ? 0.f : A / Lt);
+            if (d == 0 && a.lse) a.lse[row] = empty ? kPosInf : (M + log2f(Lt)) * kLn2;
+        } else {
+            const int64_t slot = row * a.num_splits + split;
+            a.o_part[slot * D + d] = A;
+            if (d == 0) {
+                a.m_part[slot] = (M == kNegInf) ? kNegInf : M * kLn2;
+                a.l_part[slot] = Lt;
+            }
+        }
+    }
+}
+
+// Stage 2: one wavefront per (b, n1) row merges num_splits partials.
+template <typename ST, int D>
+__global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
+    constexpr int PER = D / 64;
+    const int64_t row = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int S = a.num_splits;
+    const float* mp = a.m_part + row * S;
+    const float* lp = a.l_part + row * S;
+    const float* op = a.o_part + row * S * D;
+    uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + row * D;
+
+    float mx = kNegInf;
+    for (int i = lane; i < S; i += 64) mx = fmaxf(mx, mp[i]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, shfl_xor(mx, off));
+
+    if (mx == kNegInf) {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) out[lane * PER + e] = to_bits<ST>(0.f);
+        if (lane == 0 && a.lse) a.lse[row] = kPosInf;
+        return;
+    }
+    const float mx2 = mx * kLog2e;
+    float ls = 0.f;
+    for (int i = lane; i < S; i += 64) {
+        const float mi = mp[i];
+        if (mi != kNegInf) ls = __builtin_fmaf(lp[i], fast_exp2(__builtin_fmaf(mi, kLog2e, -mx2)), ls);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ls += shfl_xor(ls, off);
+
+    float acc[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+    for (int i = 0; i < S; ++i) {
+        const float mi = mp[i];
+        if (mi == kNegInf) continue;
+        const float w = fast_exp2(__builtin_fmaf(mi, kLog2e, -mx2));
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] = __builtin_fmaf(w, op[(int64_t)i * D + lane * PER + e], acc[e]);
+    }
+    const float inv = 1.f / ls;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) out[lane * PER + e] = to_bits<ST>(acc[e] * inv);
+    if (lane == 0 && a.lse) a.lse[row] = mx + logf(ls);
+}
+
+template <typename ST, int D, int GH>
+static hipError_t dispatch_stage1(const DecodeArgs& a, bool finish, int64_t blocks, hipStream_t s) {
+    if (finish)
+        hipLaunchKernelGGL((decode_stage1_kernel<ST, D, GH, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((decode_stage1_kernel<ST, D, GH, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+template <typename ST, int D>
+static hipError_t dispatch_stage1_gh(const DecodeArgs& a, int gh, bool finish, int64_t blocks, hipStream_t s) {
+    switch (gh) {
+        case 1: return dispatch_stage1<ST, D, 1>(a, finish, blocks, s);
+        case 2: return dispatch_stage1<ST, D, 2>(a, finish, blocks, s);
+        case 4: return dispatch_stage1<ST, D, 4>(a, finish, blocks, s);
+        case 8: return dispatch_stage1<ST, D, 8>(a, finish, blocks, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_decode_stage1(const DecodeArgs& a, int dtype, int head_dim, int heads_per_wg,
+                                bool finish, int64_t batch, hipStream_t stream) {
+    const int64_t blocks = (int64_t)a.num_splits * batch * a.num_kv_heads * a.head_groups;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (dtype == 1) {
+        if (head_dim == 128) return dispatch_stage1_gh<BF16, 128>(a, heads_per_wg, finish, blocks, stream);
+        if (head_dim == 64) return dispatch_stage1_gh<BF16, 64>(a, heads_per_wg, finish, blocks, stream);
+    } else {
+        if (head_dim == 128) return dispatch_stage1_gh<F16, 128>(a, heads_per_wg, finish, blocks, stream);
+        if (head_dim == 64) return dispatch_stage1_gh<F16, 64>(a, heads_per_wg, finish, blocks, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_combine(const CombineArgs& a, int dtype, int head_dim, hipStream_t stream) {
+    if (a.rows <= 0) return hipSuccess;
+    if (a.rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)a.rows);
+    if (dtype == 1) {
+        if (head_dim == 128) hipLaunchKernelGGL((combine_kernel<BF16, 128>), grid, dim3(64), 0, stream, a);
+        else if (head_dim == 64) hipLaunchKernelGGL((combine_kernel<BF16, 64>), grid, dim3(64), 0, stream, a);
+        else return hipErrorInvalidValue;
+    } else {
+        if (head_dim == 128) hipLaunchKernelGGL((combine_kernel<F16, 128>), grid, dim3(64), 0, stream, a);
+        else if (head_dim == 64) hipLaunchKernelGGL((combine_kernel<F16, 64>), grid, dim3(64), 0, stream, a);
+        else return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace fa

@@ -1,0 +1,103 @@
+// fa_device.h -- device helpers shared by the gfx950 attention kernels:
+// 16-bit storage <-> fp32, wavefront reductions on DPP, exp2 with the log2(e)
+// folded into the scale, 128-bit loads.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kPosInf = __builtin_huge_valf();
+
+// Storage tags: the 16-bit type the tensors hold.
+struct BF16 {
+    static constexpr bool is_bf16 = true;
+};
+struct F16 {
+    static constexpr bool is_bf16 = false;
+};
+
+// Low / high 16-bit halves of a packed word -> fp32 (exact for both types).
+template <typename ST>
+__device__ __forceinline__ float lo_f32(uint32_t w) {
+    if constexpr (ST::is_bf16) {
+        return __uint_as_float(w << 16);
+    } else {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+    }
+}
+template <typename ST>
+__device__ __forceinline__ float hi_f32(uint32_t w) {
+    if constexpr (ST::is_bf16) {
+        return __uint_as_float(w & 0xffff0000u);
+    } else {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+    }
+}
+
+// Eight packed 16-bit values -> fp32[8].
+template <typename ST>
+__device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = lo_f32<ST>(w[i]);
+        f[2 * i + 1] = hi_f32<ST>(w[i]);
+    }
+}
+
+// fp32 -> 16-bit storage bits, round to nearest even.
+template <typename ST>
+__device__ __forceinline__ uint16_t to_bits(float x) {
+    if constexpr (ST::is_bf16) {
+        return __builtin_bit_cast(uint16_t, (__bf16)x);
+    } else {
+        return __builtin_bit_cast(uint16_t, (_Float16)x);
+    }
+}
+template <typename ST>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return (uint32_t)to_bits<ST>(a) | ((uint32_t)to_bits<ST>(b) << 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// DPP lane moves inside rows of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i within 8
+constexpr int kDppMirror = 0x140;      // lane i <-> 15-i within 16
+
+// Sum over aligned groups of N lanes (N in {8, 16}); every lane gets the sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+    x += dpp<kDppXor1>(x);
+    x += dpp<kDppXor2>(x);
+    x += dpp<kDppHalfMirror>(x);
+    if constexpr (N == 16) x += dpp<kDppMirror>(x);
+    return x;
+}
+
+__device__ __forceinline__ float shfl_xor(float x, int m) { return __shfl_xor(x, m, 64); }
+
+// 16-byte global load / store helpers.
+__device__ __forceinline__ u32x4 ld128(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+}  // namespace fa

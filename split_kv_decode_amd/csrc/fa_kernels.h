@@ -1,0 +1,68 @@
+// fa_kernels.h -- launch descriptors shared by the host API (fa_api.cpp) and
+// the kernel translation units.  Plain structs of device pointers and sizes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Split-KV decode, stage 1 (and the single-split path that finishes in place).
+struct DecodeArgs {
+    const uint16_t* q;        // [B][Q_N][D] (q_seq == 1: both layouts coincide)
+    const uint16_t* k;
+    const uint16_t* v;
+    const int64_t* lens;      // [B] or null
+    float* o_part;            // [B][Q_N][splits][D]
+    float* m_part;            // [B][Q_N][splits]
+    float* l_part;
+    void* out;                // single-split path: [B][Q_N][D]
+    float* lse;               // single-split path: [B][Q_N] or null
+    int64_t kv_seq;
+    int64_t chunk;            // tokens per split (multiple of 64)
+    int64_t kv_stride_s;      // elements between consecutive tokens of one head
+    int64_t kv_stride_n;      // elements between KV heads
+    int64_t kv_stride_b;      // elements between batches
+    int32_t num_splits;
+    int32_t num_heads;        // Q_N
+    int32_t num_kv_heads;     // KV_N
+    int32_t group;            // g = Q_N / KV_N
+    int32_t head_groups;      // workgroups per KV head along g
+    float scale_log2;         // scale * log2(e)
+};
+
+struct CombineArgs {
+    const float* o_part;
+    const float* m_part;
+    const float* l_part;
+    void* out;                // [B][Q_N][D]
+    float* lse;               // [B][Q_N] or null
+    int64_t rows;             // B * Q_N
+    int32_t num_splits;
+};
+
+struct PrefillArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    void* out;
+    float* lse;               // [B][Q_N][Q_S] or null
+    const int64_t* lens;
+    const uint8_t* mask;
+    int64_t mask_stride[4];
+    int64_t q_seq, kv_seq;
+    int64_t q_stride_s, q_stride_n, q_stride_b;    // elements
+    int64_t kv_stride_s, kv_stride_n, kv_stride_b;
+    int32_t num_heads, num_kv_heads, group;
+    int32_t q_tiles;
+    float scale_log2;
+};
+
+// Launchers: return hipSuccess or the launch error.  dtype: 0 = fp16, 1 = bf16.
+hipError_t launch_decode_stage1(const DecodeArgs& a, int dtype, int head_dim, int heads_per_wg,
+                                bool finish, int64_t batch, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, int dtype, int head_dim, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int mask_mode,
+                          int64_t batch, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,265 @@
+// fa_prefill.hip -- tiled attention forward on gfx950 matrix cores.
+//
+// For one (batch, query head, 128-row query tile) a workgroup of four waves
+// walks the KV sequence in tiles of 64 keys: S = scale*QK^T on MFMA, masking,
+// an online softmax (running max m, running sum l, rescale of the output by
+// exp(m_old - m_new), as in the FlashSoftmax flow of the IFA guide, section
+// 8.1), O += P V on MFMA, and the division by l deferred to the epilogue.  The
+// score matrix never leaves registers (FlashAttn operator guide, function
+// description: O(tile) memory instead of O(Q_S x KV_S)).
+//
+// Matrix-core layout.  Each wave owns 32 query rows.  The kernel computes the
+// transposed products S^T = K Q^T and O^T = V^T P^T with
+// v_mfma_f32_32x32x16_{bf16,f16}: in the 32x32 accumulator a lane holds one
+// column (= one query row) and 16 rows (= keys), which is exactly the lane
+// layout the B operand of the next MFMA wants for P^T, so P goes from the
+// score accumulators to the PV instruction without touching LDS.  The row
+// max/sum of the softmax is an in-lane reduction plus one exchange between the
+// two half-waves.  Q stays in registers for the whole KV loop; K and V tiles
+// are staged in LDS with padded rows.
+#include <type_traits>
+
+#include "fa_device.h"
+#include "fa_kernels.h"
+
+namespace fa {
+
+template <typename ST>
+struct Mfma;
+template <>
+struct Mfma<BF16> {
+    typedef bf16x8 V8;
+    typedef __bf16 E;
+    static __device__ __forceinline__ f32x16 mm(V8 a, V8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <>
+struct Mfma<F16> {
+    typedef f16x8 V8;
+    typedef _Float16 E;
+    static __device__ __forceinline__ f32x16 mm(V8 a, V8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+// Logical work index for a launch slot.  Consecutive slots are dealt round
+// robin to the 8 XCDs (each with its own L2); this remap gives every XCD a
+// contiguous range of logical tiles, so the query tiles that read the same
+// K/V head run on the same L2.
+__device__ __forceinline__ int64_t xcd_remap(int64_t slot, int64_t total) {
+    const int64_t full = total & ~int64_t(7);
+    if (slot >= full) return slot;
+    return (slot & 7) * (full >> 3) + (slot >> 3);
+}
+
+template <typename ST, int D, int MASK>
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+    using M = Mfma<ST>;
+    using V8 = typename M::V8;
+    using E = typename M::E;
+    constexpr int BM = 128;     // query rows per workgroup (32 per wave)
+    constexpr int BN = 64;      // keys per KV tile
+    constexpr int KP = D + 8;   // padded LDS row (elements)
+    constexpr int CPR = D / 8;  // 16-byte pieces per row
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * KP];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[BN * KP];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int half = lane >> 5;
+    const int col = lane & 31;
+
+    const int64_t total = (int64_t)gridDim.x;
+    const int64_t work = xcd_remap(blockIdx.x, total);
+    int qt = (int)(work % a.q_tiles);
+    const int64_t bh = work / a.q_tiles;
+    if (MASK == 1) qt = a.q_tiles - 1 - qt;  // longest causal tiles first
+    const int n1 = (int)(bh % a.num_heads);
+    const int64_t b = bh / a.num_heads;
+    const int n2 = n1 / a.group;
+
+    int64_t L = a.kv_seq;
+    if (a.lens) {
+        L = a.lens[b];
+        L = L < 0 ? 0 : (L > a.kv_seq ? a.kv_seq : L);
+    }
+    const int64_t i0 = (int64_t)qt * BM;
+    const int64_t qrow = i0 + 32 * wave + col;
+    const bool qvalid = qrow < a.q_seq;
+
+    // Q as the B operand of S^T = K Q^T: lane (col, half) holds row qrow,
+    // head-dim elements [16*kk + 8*half, +8).
+    V8 qreg[D / 16];
+    {
+        const uint16_t* qp = a.q + b * a.q_stride_b + (int64_t)n1 * a.q_stride_n + qrow * a.q_stride_s;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            u32x4 w = u32x4{0u, 0u, 0u, 0u};
+            if (qvalid) w = ld128(qp + kk * 16 + 8 * half);
+            qreg[kk] = __builtin_bit_cast(V8, w);
+        }
+    }
+
+    int64_t kv_end = L;
+    if (MASK == 1 && kv_end > i0 + BM) kv_end = i0 + BM;  // keys beyond the tile's last row
+
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+    float m_run = kNegInf, l_run = 0.f;
+
+    const int64_t kv_off = b * a.kv_stride_b + (int64_t)n2 * a.kv_stride_n;
+    const uint16_t* kp = a.k + kv_off;
+    const uint16_t* vp = a.v + kv_off;
+
+    for (int64_t j0 = 0; j0 < kv_end; j0 += BN) {
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < BN * CPR / 256; ++it) {
+            const int idx = tid + it * 256;
+            const int r = idx / CPR;
+            const int c = idx % CPR;
+            const int64_t t = j0 + r;
+            u32x4 kw = u32x4{0u, 0u, 0u, 0u}, vw = u32x4{0u, 0u, 0u, 0u};
+            if (t < L) {  // rows beyond the length stay zero whatever the cache holds
+                kw = ld128(kp + t * a.kv_stride_s + c * 8);
+                vw = ld128(vp + t * a.kv_stride_s + c * 8);
+            }
+            *reinterpret_cast<u32x4*>(&Ks[r * KP + c * 8]) = kw;
+            *reinterpret_cast<u32x4*>(&Vs[r * KP + c * 8]) = vw;
+        }
+        __syncthreads();
+
+        // S^T tiles: keys [j0 + 32*tt, +32) x the wave's 32 query rows.
+        f32x16 s[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[tt][r] = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                const V8 ka = __builtin_bit_cast(
+                    V8, *reinterpret_cast<const u32x4*>(&Ks[(tt * 32 + col) * KP + kk * 16 + 8 * half]));
+                s[tt] = M::mm(ka, qreg[kk], s[tt]);
+            }
+        }
+
+        // Scale into base 2, mask, tile row maximum.  Accumulator register r of
+        // tile tt holds key j0 + 32*tt + 8*(r/4) + 4*half + r%4.
+        float tmax = kNegInf;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t tok = j0 + tt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                bool ok = tok < L;
+                if (MASK == 1) ok = ok && tok <= qrow;
+                if (MASK == 2)
+                    ok = ok && qvalid &&
+                         a.mask[b * a.mask_stride[0] + (int64_t)n1 * a.mask_stride[1] +
+                                qrow * a.mask_stride[2] + tok * a.mask_stride[3]] == 0;
+                const float x = ok ? s[tt][r] * a.scale_log2 : kNegInf;
+                s[tt][r] = x;
+                tmax = fmaxf(tmax, x);
+            }
+        }
+        tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+        const float mnew = fmaxf(m_run, tmax);
+        const float ms = (mnew == kNegInf) ? 0.f : mnew;
+        const float alpha = fast_exp2(m_run - ms);
+
+        // P^T as the B operand of O^T = V^T P^T.  K-step ks covers keys
+        // [16*ks, +16) of the tile; slot e of half h is key 4h+e (e<4) or
+        // 8+4h+(e-4) -- the order the accumulator already holds them in.
+        V8 pb[4];
+        float psum = 0.f;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = fast_exp2(s[tt][r] - ms);
+                psum += p;
+                pb[tt * 2 + (r >> 3)][r & 7] = (E)p;
+            }
+        }
+        psum += shfl_xor(psum, 32);
+        l_run = __builtin_fmaf(l_run, alpha, psum);
+        m_run = mnew;
+
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                // A operand V^T: lane (col, half) holds head-dim row 32*dt+col
+                // at the same key slots as pb[ks].
+                const uint16_t* vb = &Vs[(ks * 16 + 4 * half) * KP + dt * 32 + col];
+                V8 va;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    va[e] = __builtin_bit_cast(E, vb[e * KP]);
+                    va[4 + e] = __builtin_bit_cast(E, vb[(8 + e) * KP]);
+                }
+                o[dt] = M::mm(va, pb[ks], o[dt]);
+            }
+        }
+    }
+
+    // Epilogue: divide by l, RowInvalid defaults, store in the q layout.
+    if (qvalid) {
+        const bool empty = (m_run == kNegInf);
+        const float inv = empty ? 0.f : 1.f / l_run;
+        uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + b * a.q_stride_b + (int64_t)n1 * a.q_stride_n +
+                       qrow * a.q_stride_s;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+                const int d0 = dt * 32 + 8 * a4 + 4 * half;
+                float x[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) x[c] = empty ? 0.f : o[dt][4 * a4 + c] * inv;
+                u32x2 w;
+                w[0] = pack2<ST>(x[0], x[1]);
+                w[1] = pack2<ST>(x[2], x[3]);
+                *reinterpret_cast<u32x2*>(op + d0) = w;
+            }
+        }
+        if (half == 0 && a.lse)
+            a.lse[(b * a.num_heads + n1) * a.q_seq + qrow] = empty ? kPosInf : (m_run + log2f(l_run)) * kLn2;
+    }
+}
+
+template <typename ST, int D>
+static hipError_t dispatch_prefill(const PrefillArgs& a, int mask_mode, int64_t blocks, hipStream_t s) {
+    const dim3 grid((unsigned)blocks), block(256);
+    switch (mask_mode) {
+        case 0: hipLaunchKernelGGL((prefill_kernel<ST, D, 0>), grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((prefill_kernel<ST, D, 1>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((prefill_kernel<ST, D, 2>), grid, block, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int mask_mode, int64_t batch,
+                          hipStream_t stream) {
+    const int64_t blocks = (int64_t)a.q_tiles * batch * a.num_heads;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (dtype == 1) {
+        if (head_dim == 128) return dispatch_prefill<BF16, 128>(a, mask_mode, blocks, stream);
+        if (head_dim == 64) return dispatch_prefill<BF16, 64>(a, mask_mode, blocks, stream);
+    } else {
+        if (head_dim == 128) return dispatch_prefill<F16, 128>(a, mask_mode, blocks, stream);
+        if (head_dim == 64) return dispatch_prefill<F16, 64>(a, mask_mode, blocks, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace fa

@@ -1,0 +1,119 @@
+"""The C-ABI library loads, exports every entry point include/fa.h declares, and
+rejects invalid calls before touching the GPU (these tests make no compute call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import split_kv_decode_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "fa.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:fa_status|const char \*)\s*(fa_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return fa.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(fa.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def params(**kw):
+    base = dict(batch=1, num_heads=32, q_seq=1, kv_seq=131072, head_dim=128, layout="BNSD",
+                dtype="bf16", scale=0.088)
+    base.update(kw)
+    b = base.pop("batch"); n = base.pop("num_heads"); qs = base.pop("q_seq")
+    kvs = base.pop("kv_seq"); d = base.pop("head_dim")
+    return fa.make_params(b, n, qs, kvs, d, **base)
+
+
+FAKE = 1 << 20  # a 16-byte-aligned non-null address; never dereferenced (validation fails first)
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(num_heads=6, num_kv_heads=4), fa.FA_ERR_PARAM_INVALID, "multiple"),
+    (dict(head_dim=256), fa.FA_ERR_UNSUPPORTED, "not built"),
+    (dict(head_dim=100), fa.FA_ERR_PARAM_INVALID, "head_dim"),
+    (dict(batch=0), fa.FA_ERR_PARAM_INVALID, "batch"),
+    (dict(q_seq=0), fa.FA_ERR_PARAM_INVALID, "q_seq"),
+    (dict(kv_seq=0), fa.FA_ERR_PARAM_INVALID, "kv_seq"),
+    (dict(scale=float("nan")), fa.FA_ERR_PARAM_INVALID, "scale"),
+    (dict(mask_mode="bool"), fa.FA_ERR_NULLPTR, "mask"),
+    (dict(mask=FAKE), fa.FA_ERR_PARAM_INVALID, "not BOOL"),
+    (dict(layout=7), fa.FA_ERR_PARAM_INVALID, "layout"),
+    (dict(dtype=5), fa.FA_ERR_PARAM_INVALID, "dtype"),
+])
+def test_fwd_rejects_invalid_parameters(lib, kw, status, text):
+    p = params(**kw)
+    st = lib.fa_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, 0, None)
+    assert st == status
+    assert text in fa.fa_last_error()
+
+
+def test_fwd_rejects_null_and_misaligned_tensors(lib):
+    p = params(q_seq=16)
+    assert lib.fa_fwd(ctypes.byref(p), None, FAKE, FAKE, FAKE, None, None, 0, None) == fa.FA_ERR_NULLPTR
+    assert lib.fa_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, None, None, None, 0, None) == fa.FA_ERR_NULLPTR
+    assert lib.fa_fwd(ctypes.byref(p), FAKE + 2, FAKE, FAKE, FAKE, None, None, 0, None) == fa.FA_ERR_PARAM_INVALID
+    assert lib.fa_fwd(None, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == fa.FA_ERR_NULLPTR
+
+
+def test_decode_entry_points_validate(lib):
+    p = params(q_seq=2)
+    st = lib.fa_decode_splitkv(ctypes.byref(p), 32, 4096, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == fa.FA_ERR_PARAM_INVALID and "q_seq == 1" in fa.fa_last_error()
+    p = params()
+    st = lib.fa_decode_splitkv(ctypes.byref(p), 31, 4096, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == fa.FA_ERR_PARAM_INVALID and "cover" in fa.fa_last_error()
+    st = lib.fa_decode_splitkv(ctypes.byref(p), 32, 4000, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == fa.FA_ERR_PARAM_INVALID and "multiple of 64" in fa.fa_last_error()
+    st = lib.fa_decode_splitkv(ctypes.byref(p), 32, 4096, FAKE, FAKE, FAKE, None, FAKE, FAKE, None)
+    assert st == fa.FA_ERR_NULLPTR
+    pm = params(mask_mode="causal")
+    st = lib.fa_decode_splitkv(ctypes.byref(pm), 32, 4096, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == fa.FA_ERR_PARAM_INVALID
+    st = lib.fa_combine(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, None, None)
+    assert st == fa.FA_ERR_PARAM_INVALID
+    st = lib.fa_combine(ctypes.byref(p), 4, FAKE, FAKE, FAKE, None, None, None)
+    assert st == fa.FA_ERR_NULLPTR
+
+
+@pytest.mark.parametrize("kw,cus,splits,chunk", [
+    (dict(), 256, 32, 4096),                                               # 128K decode, B=1, N=32
+    (dict(batch=8, num_heads=32, num_kv_heads=8, kv_seq=4096, layout="BSND"), 256, 16, 256),
+    (dict(kv_seq=100), 256, 1, 128),                                       # tiny cache: one split
+    (dict(batch=64, num_heads=32, kv_seq=1024), 256, 1, 1024),             # plenty of units
+    (dict(kv_seq=131072), 80, 10, 13120),                                  # fewer CUs
+])
+def test_split_plan(lib, kw, cus, splits, chunk):
+    p = params(**kw)
+    sp, ch, ws = fa.fa_splitkv_plan(p, num_cus=cus)
+    assert (sp, ch) == (splits, chunk)
+    assert ch % 64 == 0 and sp * ch >= p.kv_seq
+    rows = p.batch * p.num_heads * sp
+    assert ws >= rows * (p.head_dim + 2) * 4
+
+
+def test_split_plan_honours_chunk_hint(lib):
+    p = params()
+    assert fa.fa_splitkv_plan(p, num_cus=256, chunk_hint=1024)[:2] == (128, 1024)
+    with pytest.raises(fa.FaError):
+        fa.fa_splitkv_plan(p, num_cus=256, chunk_hint=1000)
+
+
+def test_prefill_needs_no_workspace(lib):
+    assert fa.fa_workspace_size(params(q_seq=128)) == 0
+    assert fa.fa_workspace_size(params(q_seq=1, mask_mode="causal")) == 0

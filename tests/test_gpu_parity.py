@@ -1,0 +1,303 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Bar (from the benchmark spec): on 16-bit outputs max |err| <= 2e-2 and mean |err| <=
+2e-3 against the oracle; |lse - lse_oracle| <= 1e-3; rows with no valid key are
+exactly 0 with lse = +inf; no NaN anywhere.  Stage-1 partials of the split-KV
+decode: m within 1e-3 absolute, l and O within 2e-3 of the oracle's partials
+relative to the partial's own scale.
+"""
+import functools
+import math
+
+import numpy as np
+import pytest
+
+import fa_synth
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU containers
+    pytest.skip("no GPU", allow_module_level=True)
+
+import split_kv_decode_amd as fa  # noqa: E402
+
+DEV = torch.device("cuda:0")
+OUT_MAX, OUT_MEAN, LSE_TOL = 2e-2, 2e-3, 1e-3
+
+
+def dev16(bits, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV)
+    return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16)
+
+
+def to_np(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def check(out, lse, ref, ref_lse, what=""):
+    """out/ref: same shape; lse/ref_lse: same shape (or lse None)."""
+    assert np.all(np.isfinite(out)), f"{what}: non-finite output"
+    err = np.abs(out - ref)
+    assert err.max() <= OUT_MAX, f"{what}: max abs err {err.max():.3e}"
+    assert err.mean() <= OUT_MEAN, f"{what}: mean abs err {err.mean():.3e}"
+    if lse is not None:
+        inv = np.isinf(ref_lse)
+        assert np.array_equal(np.isinf(lse), inv) and np.all(lse[inv] > 0), f"{what}: invalid-row lse"
+        if (~inv).any():
+            le = np.abs(lse[~inv] - ref_lse[~inv]).max()
+            assert le <= LSE_TOL, f"{what}: lse err {le:.3e}"
+        # invalid rows exactly zero
+        inv_rows = inv.reshape(-1)
+        if inv_rows.any():
+            flat = out.reshape(-1, out.shape[-1]) if out.ndim == 2 else None
+            if flat is not None:
+                assert np.all(flat[inv_rows] == 0.0)
+    return float(err.max())
+
+
+def run_fwd(inp, mask_mode=None, return_lse=True):
+    s = inp.spec
+    q, k, v = (dev16(x, s.dtype) for x in (inp.q, inp.k, inp.v))
+    lens = None if inp.lens is None else torch.from_numpy(inp.lens).to(DEV)
+    mode = mask_mode or {"none": "none", "causal": "causal", "bool_causal": "bool"}[s.mask]
+    mask = None
+    if mode == "bool":
+        mask = torch.from_numpy(inp.mask).to(DEV)
+    out, lse = fa.fwd(q, k, v, layout=s.layout, scale=s.softmax_scale, actual_seq_lengths=lens,
+                      mask=mask, mask_stride=inp.mask_strides, causal=(mode == "causal"),
+                      return_lse=True)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def rows_of(out_t, s, rows):
+    """GPU output rows (flat ids (b*QN+n1)*QS+i) as [nrows, D] fp64."""
+    o = out_t
+    if s.layout == "BSND":
+        o = o.permute(0, 2, 1, 3)
+    o = o.reshape(-1, s.D)
+    idx = torch.from_numpy(np.asarray(rows, dtype=np.int64)).to(DEV)
+    return to_np(o.index_select(0, idx))
+
+
+def full_check(inp, mask_mode=None, what=""):
+    out, lse = run_fwd(inp, mask_mode)
+    prob = oracle.Problem.from_inputs(inp, {"bool": "bool", "causal": "causal", None: None,
+                                            "none": "none"}[mask_mode])
+    ref, ref_lse = oracle.attention(prob, inp.q, inp.k, inp.v)
+    s = inp.spec
+    o_rows = rows_of(out, s, np.arange(s.B * s.QN * s.QS))
+    r_rows = ref if s.layout == "BNSD" else ref.transpose(0, 2, 1, 3)
+    r_rows = np.ascontiguousarray(r_rows).reshape(-1, s.D)
+    return check(o_rows, to_np(lse).reshape(-1), r_rows, ref_lse.reshape(-1), what)
+
+
+@functools.lru_cache(maxsize=2)
+def workload(name):
+    return fa_synth.make(fa_synth.WORKLOADS[name])
+
+
+def spec(layout="BNSD", B=1, QN=2, KVN=2, QS=1, KVS=64, D=128, dtype="bf16", std=1.0, mask="none",
+         lens=None, seed=1, scale=None):
+    return fa_synth.Spec("t", layout, B, QN, KVN, QS, KVS, D, dtype, std=std, mask=mask, lens=lens,
+                         seed=seed, scale=scale)
+
+
+# ------------------------------------------------------------------ decode (q_seq == 1)
+
+DECODE_CASES = [
+    dict(B=1, QN=1, KVN=1, KVS=1, D=128),
+    dict(B=1, QN=32, KVN=32, KVS=4096, D=128),
+    dict(B=2, QN=8, KVN=2, KVS=1000, D=128, layout="BSND", lens=(0, 1000)),
+    dict(B=3, QN=16, KVN=2, KVS=777, D=64, lens=(1, 777)),
+    dict(B=2, QN=6, KVN=2, KVS=333, D=128, dtype="f16", layout="BSND"),    # g = 3
+    dict(B=1, QN=4, KVN=4, KVS=70000, D=64, dtype="f16", std=0.5),
+    dict(B=4, QN=64, KVN=4, KVS=2048, D=128, lens=(1, 2048)),             # g = 16
+    dict(B=5, QN=2, KVN=1, KVS=300, D=128, lens=(0, 3)),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_decode_fwd_matches_oracle(case):
+    inp = fa_synth.make(spec(**case))
+    full_check(inp, what=str(case))
+
+
+def test_decode_ignores_nan_padding():
+    inp = fa_synth.make(spec(layout="BSND", B=4, QN=8, KVN=2, KVS=600, lens=(0, 600), seed=5))
+    base, base_lse = run_fwd(inp)
+    pad = fa_synth.fill_padding(inp, fa_synth.NAN_BITS["bf16"])
+    out, lse = run_fwd(pad)
+    assert torch.equal(out, base) and torch.equal(torch.isinf(lse), torch.isinf(base_lse))
+    assert torch.equal(lse[~torch.isinf(lse)], base_lse[~torch.isinf(base_lse)])
+
+
+def _partials(inp, splits, chunk):
+    s = inp.spec
+    p = fa.params_for(dev16(inp.q, s.dtype), dev16(inp.k, s.dtype), layout=s.layout,
+                      scale=s.softmax_scale,
+                      actual_seq_lengths=None)
+    lens_t = None
+    if inp.lens is not None:
+        lens_t = torch.from_numpy(inp.lens).to(DEV)
+        p.actual_seq_lengths = lens_t.data_ptr()
+    q, k, v = (dev16(x, s.dtype) for x in (inp.q, inp.k, inp.v))
+    rows = s.B * s.QN
+    o = torch.full((rows * splits * s.D,), float("nan"), device=DEV)
+    m = torch.full((rows * splits,), float("nan"), device=DEV)
+    l = torch.full((rows * splits,), float("nan"), device=DEV)
+    fa.fa_decode_splitkv(p, splits, chunk, q, k, v, o, m, l, torch.cuda.current_stream())
+    out = torch.empty_like(q)
+    lse = torch.empty((rows,), dtype=torch.float32, device=DEV)
+    fa.fa_combine(p, splits, o, m, l, out, lse, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    return (o.view(rows, splits, s.D), m.view(rows, splits), l.view(rows, splits), out, lse,
+            lens_t)
+
+
+@pytest.mark.parametrize("splits,chunk", [(1, 1024), (3, 384), (16, 64), (40, 64), (2, 4096)])
+def test_stage1_partials_and_combine(splits, chunk):
+    inp = fa_synth.make(spec(layout="BNSD", B=2, QN=8, KVN=2, KVS=1000, lens=(1, 1000), seed=9))
+    if splits * chunk < 1000:
+        pytest.skip("plan must cover the cache")
+    o, m, l, out, lse, _ = _partials(inp, splits, chunk)
+    prob = oracle.Problem.from_inputs(inp)
+    ro, rm, rl = oracle.split_partials(prob, inp.q, inp.k, inp.v, splits, chunk)
+    go, gm, gl = to_np(o), to_np(m), to_np(l)
+    empty = np.isinf(rm)
+    assert np.array_equal(np.isinf(gm) & (gm < 0), empty), "empty-split flags"
+    assert np.all(gl[empty] == 0.0) and np.all(go[empty] == 0.0)
+    live = ~empty
+    assert np.abs(gm[live] - rm[live]).max() <= 1e-3
+    assert np.all(np.abs(gl[live] - rl[live]) <= 2e-3 * rl[live])
+    tol = 2e-3 * np.abs(ro).max(axis=2, keepdims=True) + 1e-6
+    assert np.all((np.abs(go - ro) <= tol)[live]), "stage-1 O partials"
+    # combine of the GPU partials against the oracle's unsplit result
+    ref, ref_lse = oracle.attention_rows(prob, inp.q, inp.k, inp.v)
+    check(to_np(out).reshape(-1, 128), to_np(lse), ref, ref_lse, f"combine {splits}x{chunk}")
+
+
+def test_combine_alone_matches_oracle_merge():
+    """fa_combine on oracle partials (cast to fp32) against the oracle's own merge."""
+    rng = np.random.default_rng(3)
+    rows, splits, D = 12, 9, 128
+    m = rng.normal(0, 3, (rows, splits))
+    l = rng.uniform(0.5, 40, (rows, splits))
+    o = rng.normal(0, 1, (rows, splits, D)) * l[..., None]
+    m[0, :] = -np.inf; l[0, :] = 0; o[0] = 0          # all splits empty
+    m[1, 3:] = -np.inf; l[1, 3:] = 0; o[1, 3:] = 0     # some empty
+    ref, ref_lse = oracle.merge(o, m, l)
+    p = fa.make_params(rows, 1, 1, 4096, D, layout="BNSD", dtype="bf16", scale=1.0)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV)
+    out = torch.empty((rows, 1, 1, D), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((rows,), dtype=torch.float32, device=DEV)
+    fa.fa_combine(p, splits, t(o), t(m), t(l), out, lse, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    got = to_np(out).reshape(rows, D)
+    assert np.all(got[0] == 0) and math.isinf(float(lse[0])) and float(lse[0]) > 0
+    check(got, to_np(lse), ref, ref_lse, "combine")
+
+
+# ------------------------------------------------------------------ prefill
+
+PREFILL_CASES = [
+    dict(QS=1, KVS=1, D=64, mask="causal"),
+    dict(B=2, QN=4, KVN=2, QS=17, KVS=33, D=64, mask="causal"),
+    dict(B=1, QN=2, KVN=2, QS=200, KVS=200, D=128, mask="causal", layout="BSND"),
+    dict(B=2, QN=8, KVN=2, QS=129, KVS=300, D=128, lens=(0, 300)),
+    dict(B=2, QN=4, KVN=4, QS=333, KVS=333, D=64, dtype="f16", std=0.5, mask="causal",
+         lens=(100, 333)),
+    dict(B=1, QN=2, KVN=1, QS=64, KVS=64, D=128, mask="bool_causal", layout="BSND"),
+    dict(B=2, QN=8, KVN=1, QS=256, KVS=512, D=128, dtype="f16"),
+    dict(B=1, QN=3, KVN=3, QS=5, KVS=1000, D=128, lens=(1, 1000)),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_prefill_matches_oracle(case):
+    inp = fa_synth.make(spec(**case))
+    full_check(inp, what=str(case))
+
+
+def test_prefill_causal_mode_equals_bool_mask():
+    inp = fa_synth.make(spec(layout="BSND", B=1, QN=4, KVN=4, QS=300, KVS=300, mask="bool_causal",
+                             seed=17))
+    o1, l1 = run_fwd(inp, "bool")
+    o2, l2 = run_fwd(inp, "causal")
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_prefill_random_bool_mask_with_empty_rows():
+    s = spec(layout="BNSD", B=2, QN=4, KVN=2, QS=70, KVS=150, D=64, seed=19)
+    inp = fa_synth.make(s)
+    rng = np.random.default_rng(2)
+    mask = (rng.random((2, 4, 70, 150)) < 0.7).astype(np.uint8)
+    mask[1, 2, 5, :] = 1
+    inp.mask = mask
+    inp.mask_strides = (4 * 70 * 150, 70 * 150, 150, 1)
+    e = full_check(inp, "bool", "random bool mask")
+    out, lse = run_fwd(inp, "bool")
+    assert math.isinf(float(lse[1, 2, 5])) and torch.all(out[1, 2, 5] == 0)
+
+
+def test_prefill_ignores_nan_padding():
+    inp = fa_synth.make(spec(layout="BNSD", B=3, QN=2, KVN=2, QS=100, KVS=300, D=128, lens=(0, 300),
+                             mask="causal", seed=23))
+    base, bl = run_fwd(inp)
+    pad = fa_synth.fill_padding(inp, fa_synth.NAN_BITS["bf16"])
+    out, lse = run_fwd(pad)
+    assert torch.equal(out, base) and torch.equal(lse, bl)
+
+
+# ------------------------------------------------------------------ the five workloads
+
+def test_workload_prefill_small_full():
+    full_check(workload("prefill_small"), what="prefill_small")
+
+
+def test_workload_decode_gqa_full():
+    full_check(workload("decode_gqa"), what="decode_gqa")
+
+
+def test_workload_decode_128k_full():
+    full_check(workload("decode_128k"), what="decode_128k")
+
+
+@pytest.mark.parametrize("chunk", [1024, 2048, 4096])
+def test_workload_decode_128k_chunks(chunk):
+    inp = workload("decode_128k")
+    splits = 131072 // chunk
+    _, _, _, out, lse, _ = _partials(inp, splits, chunk)
+    rows = np.arange(32)
+    ref, ref_lse = oracle.attention_rows(oracle.Problem.from_inputs(inp), inp.q, inp.k, inp.v, rows)
+    check(to_np(out).reshape(-1, 128), to_np(lse), ref, ref_lse, f"128k chunk {chunk}")
+
+
+def sampled_check(name, mask_mode=None, n=3000):
+    inp = workload(name)
+    s = inp.spec
+    out, lse = run_fwd(inp, mask_mode)
+    rows = fa_synth.sample_rows(s, n, seed=11, lens=inp.lens)
+    prob = oracle.Problem.from_inputs(inp, mask_mode)
+    ref, ref_lse = oracle.attention_rows(prob, inp.q, inp.k, inp.v, rows)
+    got = rows_of(out, s, rows)
+    got_lse = to_np(lse).reshape(-1)[rows]
+    return check(got, got_lse, ref, ref_lse, name)
+
+
+def test_workload_prefill_causal_bool_sampled():
+    sampled_check("prefill_causal")
+
+
+def test_workload_prefill_causal_mode_sampled():
+    sampled_check("prefill_causal", "causal")
+
+
+def test_workload_prefill_4k_sampled():
+    sampled_check("prefill_4k")
+
+
+def test_workload_prefill_gqa_long_sampled():
+    sampled_check("prefill_gqa_long", n=2000)

@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention forward on one MI355X.
+
+One step is one pass of the whole hot path over one batch of seeded synthetic
+input, with every input already resident in HBM:
+  * decode leg -- FlashDecoding split-KV decode of a 128K-token cache (BNSD,
+    B=1, 32 heads, D=128, bf16): stage 1 (fa_decode_splitkv) + the LSE
+    combine (fa_combine), with the split plan fa_fwd would choose;
+  * prefill leg -- mask-free prefill, BSND, B=2, 32 heads, S=4096, D=128, bf16
+    (fa_fwd).
+Each kernel launch is bracketed by HIP events on the stream it runs on.
+
+The printed JSON line reports decode KV-read GB/s as ``value`` (and the prefill
+TFLOP/s beside it), a ``roofline`` object for the dominant kernel (decode stage
+1: K+V bytes per launch / its mean launch time, against 8 TB/s HBM) and one for
+the prefill kernel (4*B*N*S^2*D flop per launch against 2.5 PFLOP/s bf16 MFMA),
+and ``cpu_baseline``: the fp64 oracle timed on this host's cores on the same
+decode workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, published
+METRIC = "prefill attn TFLOP/s (%MFMA peak); decode KV GB/s (%HBM peak) on 1 MI355X"
+
+
+def sha256_of(path):
+    h = hashlib.sha256()
+    with open(path, "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(kernel_src: str, name: str):
+    """HBM bytes per launch from a committed counter summary, if it was taken on this source."""
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        parts = line.split()
+        if len(parts) >= 2 and not line.startswith("#"):
+            vals[parts[0]] = parts[1]
+    if vals.get("source_sha256") != sha256_of(kernel_src):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--legs", default="decode,prefill", help="comma list of decode,prefill")
+    ap.add_argument("--chunk", type=int, default=0, help="decode chunk (tokens); 0 = planner")
+    ap.add_argument("--copy-calibrate", action="store_true",
+                    help="also run a plain 1 GiB device copy per step (counter calibration)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fa_synth
+    import split_kv_decode_amd as fa
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    fa.load()
+    legs = [x for x in args.legs.split(",") if x]
+    stream = torch.cuda.current_stream()
+
+    def dev16(bits, dtype):
+        t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev)
+        return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16)
+
+    t_gen = time.time()
+    dec = pre = None
+    if "decode" in legs:
+        dinp = fa_synth.make(fa_synth.WORKLOADS["decode_128k"])
+        ds = dinp.spec
+        dq, dk, dv = (dev16(x, ds.dtype) for x in (dinp.q, dinp.k, dinp.v))
+        dp = fa.params_for(dq, dk, layout=ds.layout, scale=ds.softmax_scale)
+        splits, chunk, ws_bytes = fa.fa_splitkv_plan(dp, 0, args.chunk)
+        rows = ds.B * ds.QN
+        o_part = torch.empty((rows * splits * ds.D,), dtype=torch.float32, device=dev)
+        m_part = torch.empty((rows * splits,), dtype=torch.float32, device=dev)
+        l_part = torch.empty((rows * splits,), dtype=torch.float32, device=dev)
+        dout = torch.empty_like(dq)
+        dlse = torch.empty((rows,), dtype=torch.float32, device=dev)
+        kv_bytes = 2 * ds.B * ds.KVN * ds.KVS * ds.D * 2      # K and V, bf16, every row valid
+        qo_bytes = 2 * rows * ds.D * 2                         # q in, out back
+        dec = dict(inp=dinp, q=dq, k=dk, v=dv, p=dp, splits=splits, chunk=chunk,
+                   o=o_part, m=m_part, l=l_part, out=dout, lse=dlse,
+                   kv_bytes=kv_bytes, qo_bytes=qo_bytes)
+        del dinp
+    if "prefill" in legs:
+        pinp = fa_synth.make(fa_synth.WORKLOADS["prefill_4k"])
+        ps = pinp.spec
+        pq, pk, pv = (dev16(x, ps.dtype) for x in (pinp.q, pinp.k, pinp.v))
+        pp = fa.params_for(pq, pk, layout=ps.layout, scale=ps.softmax_scale)
+        pout = torch.empty_like(pq)
+        plse = torch.empty((ps.B, ps.QN, ps.QS), dtype=torch.float32, device=dev)
+        flops = 4.0 * ps.B * ps.QN * ps.QS * ps.KVS * ps.D
+        pre = dict(spec=ps, q=pq, k=pk, v=pv, p=pp, out=pout, lse=plse, flops=flops)
+        del pinp
+    copy_src = copy_dst = None
+    if args.copy_calibrate:
+        copy_src = torch.ones((1 << 29,), dtype=torch.int16, device=dev)  # 1 GiB
+        copy_dst = torch.empty_like(copy_src)
+    torch.cuda.synchronize()
+    t_gen = time.time() - t_gen
+
+    def step(ev):
+        if dec is not None:
+            ev[0].record(stream)
+            fa.fa_decode_splitkv(dec["p"], dec["splits"], dec["chunk"], dec["q"], dec["k"], dec["v"],
+                                 dec["o"], dec["m"], dec["l"], stream)
+            ev[1].record(stream)
+            fa.fa_combine(dec["p"], dec["splits"], dec["o"], dec["m"], dec["l"], dec["out"],
+                          dec["lse"], stream)
+            ev[2].record(stream)
+        if pre is not None:
+            ev[3].record(stream)
+            fa.fa_fwd(pre["p"], pre["q"], pre["k"], pre["v"], pre["out"], pre["lse"], None, 0, stream)
+            ev[4].record(stream)
+        if copy_src is not None:
+            copy_dst.copy_(copy_src)
+
+    def new_events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+
+    for _ in range(args.warmup):
+        step(new_events())
+    torch.cuda.synchronize()
+
+    events = [new_events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    def mean_ms(a, b):
+        return float(np.mean([ev[a].elapsed_time(ev[b]) for ev in events]))
+
+    out = {"metric": METRIC, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded N(0,1) bf16, RNE-rounded)"}
+    config = {"workload": "+".join(legs), "parallelism": "single GPU"}
+    csrc = os.path.join(ROOT, "split_kv_decode_amd", "csrc")
+    if dec is not None:
+        s1 = mean_ms(0, 1)
+        cb = mean_ms(1, 2)
+        leg = s1 + cb
+        value = (dec["kv_bytes"] + dec["qo_bytes"]) / (leg * 1e-3) / 1e9
+        s1_gbs = (dec["kv_bytes"] + dec["qo_bytes"]) / (s1 * 1e-3) / 1e9
+        traffic = stored_traffic(os.path.join(csrc, "fa_decode.hip"), "decode_stage1_128k")
+        out["value"] = round(value, 2)
+        out["decode"] = {"workload": "decode_128k: BNSD B=1 Q_N=KV_N=32 Q_S=1 KV_S=131072 D=128 bf16",
+                         "num_splits": dec["splits"], "chunk": dec["chunk"],
+                         "stage1_ms": round(s1, 5), "combine_ms": round(cb, 5),
+                         "leg_ms": round(leg, 5), "kv_gbs": round(value, 2),
+                         "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4)}
+        out["roofline"] = {"kernel": "decode_stage1_kernel<BF16,128,1,false>", "bound": "hbm",
+                           "achieved": round(s1_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(s1_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                           "algorithmic_bytes_per_launch": dec["kv_bytes"] + dec["qo_bytes"]}
+        config.update({"decode_B": 1, "decode_heads": 32, "decode_kv_seq": 131072, "head_dim": 128})
+    if pre is not None:
+        pm = mean_ms(3, 4)
+        tflops = pre["flops"] / (pm * 1e-3) / 1e12
+        ps = pre["spec"]
+        traffic = stored_traffic(os.path.join(csrc, "fa_prefill.hip"), "prefill_4k")
+        out["prefill"] = {"workload": "prefill_4k: BSND B=2 N=32 S=4096 D=128 bf16, no mask",
+                          "ms": round(pm, 5), "tflops": round(tflops, 2),
+                          "frac_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+        out["roofline_prefill"] = {"kernel": "prefill_kernel<BF16,128,0>", "bound": "mfma",
+                                   "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                                   "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                                   "traffic": traffic, "algorithmic_flop_per_launch": pre["flops"]}
+        if dec is None:
+            out["value"] = round(tflops, 2)
+            out["unit"] = "TFLOP/s"
+        config.update({"prefill_B": ps.B, "prefill_heads": ps.QN, "prefill_seq": ps.QS})
+    out["config"] = config
+
+    if dec is not None and not args.no_cpu_baseline:
+        import oracle
+        inp = dec["inp"]
+        prob = oracle.Problem.from_inputs(inp)
+        threads = oracle.default_threads()
+        n, t_cpu = 0, 0.0
+        while t_cpu < args.cpu_seconds:
+            t1 = time.perf_counter()
+            oracle.attention_rows(prob, inp.q, inp.k, inp.v, None, threads)
+            t_cpu += time.perf_counter() - t1
+            n += 1
+        cpu_gbs = n * (dec["kv_bytes"] + dec["qo_bytes"]) / t_cpu / 1e9
+        out["cpu_baseline"] = {"value": round(cpu_gbs, 4), "unit": "GB/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"the whole decode_128k workload (32 rows x 131072 keys), "
+                                         f"{n} pass(es) in {t_cpu:.1f} s, fp64"}
+    out["setup_s"] = round(t_gen, 1)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -240,7 +240,8 @@ fa_status run_prefill(const fa_params* p, const Shape& s, const void* q, const v
     a.num_kv_heads = (int32_t)s.KVN;
     a.group = (int32_t)s.g;
     a.q_tiles = (int32_t)((s.QS + 127) / 128);
-    a.scale_log2 = (float)(p->scale * 1.4426950408889634);
+    a.negate_q = p->scale < 0 ? 1 : 0;
+    a.scale_log2 = (float)(std::fabs(p->scale) * 1.4426950408889634);
     const int mm = p->mask_mode == FA_MASK_NONE ? 0 : (p->mask_mode == FA_MASK_CAUSAL ? 1 : 2);
     return launch_result(fa::launch_prefill(a, p->dtype == FA_BF16 ? 1 : 0, (int)s.D, mm, s.B, stream), "prefill");
 }

@@ -225,52 +225,100 @@ __global__ __launch_bounds__(256) void decode_stage1_kernel(DecodeArgs a) {
     }
 }
 
-// Stage 2: one wavefront per (b, n1) row merges num_splits partials.
+// Stage 2: one workgroup of 256 threads per (b, n1) row merges num_splits
+// partials.  Thread t owns four head-dim columns (t % (D/4)) of one split group
+// (t / (D/4)); the partial-output loads do not depend on the weights, so every
+// load of the row is in flight at once and the kernel costs about two memory
+// latencies.
+constexpr int kCombineWeightsLds = 2048;
+
+__device__ __forceinline__ float block_max256(float x, float* red) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, shfl_xor(x, off));
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = x;
+    __syncthreads();
+    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__device__ __forceinline__ float block_sum256(float x, float* red) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += shfl_xor(x, off);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = x;
+    __syncthreads();
+    return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
 template <typename ST, int D>
-__global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
-    constexpr int PER = D / 64;
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+    constexpr int NQ = D / 4;      // float4 columns per row
+    constexpr int NG = 256 / NQ;   // split groups
+    __shared__ float red[4];
+    __shared__ float s_w[kCombineWeightsLds];
+    __shared__ f32x4 s_acc[NG][NQ];
+
     const int64_t row = blockIdx.x;
-    const int lane = threadIdx.x;
+    const int t = threadIdx.x;
+    const int dq = t % NQ;
+    const int sg = t / NQ;
     const int S = a.num_splits;
     const float* mp = a.m_part + row * S;
     const float* lp = a.l_part + row * S;
-    const float* op = a.o_part + row * S * D;
+    const float* op = a.o_part + row * (int64_t)S * D;
     uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + row * D;
 
     float mx = kNegInf;
-    for (int i = lane; i < S; i += 64) mx = fmaxf(mx, mp[i]);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, shfl_xor(mx, off));
-
-    if (mx == kNegInf) {
-#pragma unroll
-        for (int e = 0; e < PER; ++e) out[lane * PER + e] = to_bits<ST>(0.f);
-        if (lane == 0 && a.lse) a.lse[row] = kPosInf;
+    for (int i = t; i < S; i += 256) mx = fmaxf(mx, mp[i]);
+    mx = block_max256(mx, red);
+    if (mx == kNegInf) {  // every split empty: RowInvalid defaults
+        if (t < NQ) {
+            u32x2 z;
+            z[0] = 0u;
+            z[1] = 0u;
+            *reinterpret_cast<u32x2*>(out + 4 * t) = z;
+        }
+        if (t == 0 && a.lse) a.lse[row] = kPosInf;
         return;
     }
     const float mx2 = mx * kLog2e;
     float ls = 0.f;
-    for (int i = lane; i < S; i += 64) {
+    for (int i = t; i < S; i += 256) {
         const float mi = mp[i];
-        if (mi != kNegInf) ls = __builtin_fmaf(lp[i], fast_exp2(__builtin_fmaf(mi, kLog2e, -mx2)), ls);
+        const float w = (mi == kNegInf) ? 0.f : fast_exp2(__builtin_fmaf(mi, kLog2e, -mx2));
+        if (i < kCombineWeightsLds) s_w[i] = w;
+        ls = __builtin_fmaf(w, lp[i], ls);
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) ls += shfl_xor(ls, off);
+    ls = block_sum256(ls, red);  // its barriers also publish s_w
 
-    float acc[PER];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-    for (int i = 0; i < S; ++i) {
-        const float mi = mp[i];
-        if (mi == kNegInf) continue;
-        const float w = fast_exp2(__builtin_fmaf(mi, kLog2e, -mx2));
-#pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] = __builtin_fmaf(w, op[(int64_t)i * D + lane * PER + e], acc[e]);
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int i = sg; i < S; i += NG) {
+        const f32x4 o = *reinterpret_cast<const f32x4*>(op + (int64_t)i * D + 4 * dq);
+        float w;
+        if (i < kCombineWeightsLds) {
+            w = s_w[i];
+        } else {
+            const float mi = mp[i];
+            w = (mi == kNegInf) ? 0.f : fast_exp2(__builtin_fmaf(mi, kLog2e, -mx2));
+        }
+        if (w != 0.f) acc += w * o;  // empty splits are skipped whatever their O holds
     }
-    const float inv = 1.f / ls;
+    s_acc[sg][dq] = acc;
+    __syncthreads();
+    if (t < NQ) {
+        f32x4 sum = s_acc[0][t];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) out[lane * PER + e] = to_bits<ST>(acc[e] * inv);
-    if (lane == 0 && a.lse) a.lse[row] = mx + logf(ls);
+        for (int g = 1; g < NG; ++g) sum += s_acc[g][t];
+        const float inv = 1.f / ls;
+        u32x2 w;
+        w[0] = pack2<ST>(sum[0] * inv, sum[1] * inv);
+        w[1] = pack2<ST>(sum[2] * inv, sum[3] * inv);
+        *reinterpret_cast<u32x2*>(out + 4 * t) = w;
+        if (t == 0 && a.lse) a.lse[row] = mx + logf(ls);
+    }
 }
 
 template <typename ST, int D, int GH>
@@ -313,12 +361,12 @@ hipError_t launch_combine(const CombineArgs& a, int dtype, int head_dim, hipStre
     if (a.rows > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)a.rows);
     if (dtype == 1) {
-        if (head_dim == 128) hipLaunchKernelGGL((combine_kernel<BF16, 128>), grid, dim3(64), 0, stream, a);
-        else if (head_dim == 64) hipLaunchKernelGGL((combine_kernel<BF16, 64>), grid, dim3(64), 0, stream, a);
+        if (head_dim == 128) hipLaunchKernelGGL((combine_kernel<BF16, 128>), grid, dim3(256), 0, stream, a);
+        else if (head_dim == 64) hipLaunchKernelGGL((combine_kernel<BF16, 64>), grid, dim3(256), 0, stream, a);
         else return hipErrorInvalidValue;
     } else {
-        if (head_dim == 128) hipLaunchKernelGGL((combine_kernel<F16, 128>), grid, dim3(64), 0, stream, a);
-        else if (head_dim == 64) hipLaunchKernelGGL((combine_kernel<F16, 64>), grid, dim3(64), 0, stream, a);
+        if (head_dim == 128) hipLaunchKernelGGL((combine_kernel<F16, 128>), grid, dim3(256), 0, stream, a);
+        else if (head_dim == 64) hipLaunchKernelGGL((combine_kernel<F16, 64>), grid, dim3(256), 0, stream, a);
         else return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -55,6 +55,7 @@ struct PrefillArgs {
     int64_t kv_stride_s, kv_stride_n, kv_stride_b;
     int32_t num_heads, num_kv_heads, group;
     int32_t q_tiles;
+    int32_t negate_q;         // 1 when scale < 0: q's sign is flipped, scale_log2 = |scale|*log2(e)
     float scale_log2;
 };
 

@@ -53,17 +53,30 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t slot, int64_t total) {
     return (slot & 7) * (full >> 3) + (slot >> 3);
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i receives element i%4 of the 8-byte pieces addressed by lanes
+// i/4, i/4+4, i/4+8 and i/4+12 of its group.
+__device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+
 template <typename ST, int D, int MASK>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     using M = Mfma<ST>;
     using V8 = typename M::V8;
     using E = typename M::E;
-    constexpr int BM = 128;     // query rows per workgroup (32 per wave)
-    constexpr int BN = 64;      // keys per KV tile
-    constexpr int KP = D + 8;   // padded LDS row (elements)
-    constexpr int CPR = D / 8;  // 16-byte pieces per row
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * KP];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[BN * KP];
+    constexpr int BM = 128;      // query rows per workgroup (32 per wave)
+    constexpr int BN = 64;       // keys per KV tile
+    constexpr int KP = D + 8;    // K row pitch in LDS: 16 rows of a b128 read hit distinct banks
+    constexpr int VP = D + 32;   // V row pitch: the 4 rows of a transposing read hit distinct banks
+    constexpr int CPR = D / 8;   // 16-byte pieces per row
+    constexpr int NLD = BN * CPR / 256;  // 16-byte loads per thread per tile, for K and for V
+    constexpr float kTau = 8.f;  // rescale only when a row max grows by more than 2^8
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KP];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * VP];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -86,55 +99,94 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         L = L < 0 ? 0 : (L > a.kv_seq ? a.kv_seq : L);
     }
     const int64_t i0 = (int64_t)qt * BM;
-    const int64_t qrow = i0 + 32 * wave + col;
+    const int64_t wrow0 = i0 + 32 * wave;  // first query row of this wave
+    const int64_t qrow = wrow0 + col;
     const bool qvalid = qrow < a.q_seq;
 
     // Q as the B operand of S^T = K Q^T: lane (col, half) holds row qrow,
-    // head-dim elements [16*kk + 8*half, +8).
+    // head-dim elements [16*kk + 8*half, +8).  A negative scale is folded in
+    // by flipping the sign bits, so scores are scaled by |scale| * log2(e) > 0
+    // and the row max can be taken before scaling.
     V8 qreg[D / 16];
     {
         const uint16_t* qp = a.q + b * a.q_stride_b + (int64_t)n1 * a.q_stride_n + qrow * a.q_stride_s;
+        const uint32_t flip = a.negate_q ? 0x80008000u : 0u;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
             u32x4 w = u32x4{0u, 0u, 0u, 0u};
             if (qvalid) w = ld128(qp + kk * 16 + 8 * half);
+            w ^= flip;
             qreg[kk] = __builtin_bit_cast(V8, w);
         }
     }
+    const float c = a.scale_log2;
 
     int64_t kv_end = L;
     if (MASK == 1 && kv_end > i0 + BM) kv_end = i0 + BM;  // keys beyond the tile's last row
+    const int ntiles = (int)((kv_end + BN - 1) / BN);
 
     f32x16 o[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-    float m_run = kNegInf, l_run = 0.f;
+    float m_run = kNegInf;  // per query row, in scaled base-2 units (same in both halves)
+    float l_half = 0.f;     // this half-wave's share of the row sum
 
     const int64_t kv_off = b * a.kv_stride_b + (int64_t)n2 * a.kv_stride_n;
     const uint16_t* kp = a.k + kv_off;
     const uint16_t* vp = a.v + kv_off;
 
-    for (int64_t j0 = 0; j0 < kv_end; j0 += BN) {
-        __syncthreads();
+    // Global -> register prefetch of one KV tile, register -> LDS store.
+    u32x4 kr[NLD], vr[NLD];
+    auto gload = [&](int64_t j0) {
 #pragma unroll
-        for (int it = 0; it < BN * CPR / 256; ++it) {
+        for (int it = 0; it < NLD; ++it) {
+            const int idx = tid + it * 256;
+            const int64_t t = j0 + idx / CPR;
+            const int cc = idx % CPR;
+            if (t < L) {  // rows beyond the length stay zero whatever the cache holds
+                kr[it] = ld128(kp + t * a.kv_stride_s + cc * 8);
+                vr[it] = ld128(vp + t * a.kv_stride_s + cc * 8);
+            } else {
+                kr[it] = u32x4{0u, 0u, 0u, 0u};
+                vr[it] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+        for (int it = 0; it < NLD; ++it) {
             const int idx = tid + it * 256;
             const int r = idx / CPR;
-            const int c = idx % CPR;
-            const int64_t t = j0 + r;
-            u32x4 kw = u32x4{0u, 0u, 0u, 0u}, vw = u32x4{0u, 0u, 0u, 0u};
-            if (t < L) {  // rows beyond the length stay zero whatever the cache holds
-                kw = ld128(kp + t * a.kv_stride_s + c * 8);
-                vw = ld128(vp + t * a.kv_stride_s + c * 8);
-            }
-            *reinterpret_cast<u32x4*>(&Ks[r * KP + c * 8]) = kw;
-            *reinterpret_cast<u32x4*>(&Vs[r * KP + c * 8]) = vw;
+            const int cc = idx % CPR;
+            *reinterpret_cast<u32x4*>(&Ks[buf][r * KP + cc * 8]) = kr[it];
+            *reinterpret_cast<u32x4*>(&Vs[buf][r * VP + cc * 8]) = vr[it];
         }
-        __syncthreads();
+    };
 
-        // S^T tiles: keys [j0 + 32*tt, +32) x the wave's 32 query rows.
+    // Per-lane source offsets of the transposing V reads (see lds_read_tr):
+    // 16-lane group G = lane/16 serves head-dim columns 16*(G&1) + [0,16) of a
+    // 32-column tile and key slots 4*(G>>1) + [0,4); source lane L = lane%16
+    // points at key row L/4 of those four, columns 4*(L%4) + [0,4).
+    const int trG = lane >> 4;
+    const int trL = lane & 15;
+    const int tr_off = (4 * (trG >> 1) + (trL >> 2)) * VP + 16 * (trG & 1) + 4 * (trL & 3);
+
+    if (ntiles > 0) {
+        gload(0);
+        lstore(0);
+    }
+    __syncthreads();
+
+    for (int jt = 0; jt < ntiles; ++jt) {
+        const int buf = jt & 1;
+        const int64_t j0 = (int64_t)jt * BN;
+        if (jt + 1 < ntiles) gload(j0 + BN);  // next tile in flight during this one
+        const uint16_t* Kb = Ks[buf];
+        const uint16_t* Vb = Vs[buf];
+
+        // S^T tiles: keys [j0 + 32*tt, +32) x the wave's 32 query rows (raw q.k).
         f32x16 s[2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -143,34 +195,53 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) {
                 const V8 ka = __builtin_bit_cast(
-                    V8, *reinterpret_cast<const u32x4*>(&Ks[(tt * 32 + col) * KP + kk * 16 + 8 * half]));
+                    V8, *reinterpret_cast<const u32x4*>(&Kb[(tt * 32 + col) * KP + kk * 16 + 8 * half]));
                 s[tt] = M::mm(ka, qreg[kk], s[tt]);
             }
         }
 
-        // Scale into base 2, mask, tile row maximum.  Accumulator register r of
-        // tile tt holds key j0 + 32*tt + 8*(r/4) + 4*half + r%4.
+        // Masking is needed only on tiles that cross the length, the causal
+        // diagonal of this wave's rows, or under a boolean mask.  Accumulator
+        // register r of tile tt holds key j0 + 32*tt + 8*(r/4) + 4*half + r%4.
+        const bool need_mask = (j0 + BN > L) || (MASK == 1 && j0 + BN - 1 > wrow0) || (MASK == 2);
         float tmax = kNegInf;
+        if (need_mask) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
+            for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t tok = j0 + tt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                bool ok = tok < L;
-                if (MASK == 1) ok = ok && tok <= qrow;
-                if (MASK == 2)
-                    ok = ok && qvalid &&
-                         a.mask[b * a.mask_stride[0] + (int64_t)n1 * a.mask_stride[1] +
-                                qrow * a.mask_stride[2] + tok * a.mask_stride[3]] == 0;
-                const float x = ok ? s[tt][r] * a.scale_log2 : kNegInf;
-                s[tt][r] = x;
-                tmax = fmaxf(tmax, x);
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t tok = j0 + tt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                    bool ok = tok < L;
+                    if (MASK == 1) ok = ok && tok <= qrow;
+                    if (MASK == 2)
+                        ok = ok && qvalid &&
+                             a.mask[b * a.mask_stride[0] + (int64_t)n1 * a.mask_stride[1] +
+                                    qrow * a.mask_stride[2] + tok * a.mask_stride[3]] == 0;
+                    s[tt][r] = ok ? s[tt][r] : kNegInf;
+                    tmax = fmaxf(tmax, s[tt][r]);
+                }
             }
+        } else {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[tt][r]);
         }
-        tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-        const float mnew = fmaxf(m_run, tmax);
-        const float ms = (mnew == kNegInf) ? 0.f : mnew;
-        const float alpha = fast_exp2(m_run - ms);
+        tmax = fmaxf(tmax, shfl_xor(tmax, 32)) * c;
+
+        // Lazy rescale: keep the running max unless some row of the wave grew
+        // by more than kTau; exponentials then stay below 2^kTau.
+        if (__any(tmax > m_run + kTau)) {
+            const float mnew = fmaxf(m_run, tmax);
+            const float alpha = fast_exp2(m_run - ((mnew == kNegInf) ? 0.f : mnew));
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+            l_half *= alpha;
+            m_run = mnew;
+        }
+        const float nm = (m_run == kNegInf) ? 0.f : -m_run;
 
         // P^T as the B operand of O^T = V^T P^T.  K-step ks covers keys
         // [16*ks, +16) of the tile; slot e of half h is key 4h+e (e<4) or
@@ -181,36 +252,35 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float p = fast_exp2(s[tt][r] - ms);
+                const float p = fast_exp2(__builtin_fmaf(s[tt][r], c, nm));
                 psum += p;
                 pb[tt * 2 + (r >> 3)][r & 7] = (E)p;
             }
         }
-        psum += shfl_xor(psum, 32);
-        l_run = __builtin_fmaf(l_run, alpha, psum);
-        m_run = mnew;
+        l_half += psum;
 
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-#pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 // A operand V^T: lane (col, half) holds head-dim row 32*dt+col
-                // at the same key slots as pb[ks].
-                const uint16_t* vb = &Vs[(ks * 16 + 4 * half) * KP + dt * 32 + col];
-                V8 va;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    va[e] = __builtin_bit_cast(E, vb[e * KP]);
-                    va[4 + e] = __builtin_bit_cast(E, vb[(8 + e) * KP]);
-                }
+                // at the key slots of pb[ks]; two transposing reads give the
+                // slots 0..3 (keys 4h+[0,4)) and 4..7 (keys 8+4h+[0,4)).
+                const uint16_t* vb = Vb + ks * 16 * VP + dt * 32 + tr_off;
+                const s16x4 lo = lds_read_tr(vb);
+                const s16x4 hi = lds_read_tr(vb + 8 * VP);
+                const V8 va = __builtin_bit_cast(
+                    V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 o[dt] = M::mm(va, pb[ks], o[dt]);
             }
         }
+
+        if (jt + 1 < ntiles) lstore(buf ^ 1);
+        __syncthreads();
     }
 
     // Epilogue: divide by l, RowInvalid defaults, store in the q layout.
+    const float l_run = l_half + shfl_xor(l_half, 32);
     if (qvalid) {
         const bool empty = (m_run == kNegInf);
         const float inv = empty ? 0.f : 1.f / l_run;
@@ -223,7 +293,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                 const int d0 = dt * 32 + 8 * a4 + 4 * half;
                 float x[4];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) x[c] = empty ? 0.f : o[dt][4 * a4 + c] * inv;
+                for (int cc = 0; cc < 4; ++cc) x[cc] = empty ? 0.f : o[dt][4 * a4 + cc] * inv;
                 u32x2 w;
                 w[0] = pack2<ST>(x[0], x[1]);
                 w[1] = pack2<ST>(x[2], x[3]);

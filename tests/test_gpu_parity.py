@@ -116,6 +116,7 @@ DECODE_CASES = [
     dict(B=1, QN=4, KVN=4, KVS=70000, D=64, dtype="f16", std=0.5),
     dict(B=4, QN=64, KVN=4, KVS=2048, D=128, lens=(1, 2048)),             # g = 16
     dict(B=5, QN=2, KVN=1, KVS=300, D=128, lens=(0, 3)),
+    dict(B=2, QN=4, KVN=2, KVS=500, D=128, scale=-0.09),
 ]
 
 
@@ -212,6 +213,8 @@ PREFILL_CASES = [
     dict(B=1, QN=2, KVN=1, QS=64, KVS=64, D=128, mask="bool_causal", layout="BSND"),
     dict(B=2, QN=8, KVN=1, QS=256, KVS=512, D=128, dtype="f16"),
     dict(B=1, QN=3, KVN=3, QS=5, KVS=1000, D=128, lens=(1, 1000)),
+    dict(B=1, QN=2, KVN=1, QS=150, KVS=150, D=128, mask="causal", scale=-0.09),
+    dict(B=1, QN=2, KVN=2, QS=96, KVS=200, D=64, scale=-0.125, layout="BSND"),
 ]
 
 

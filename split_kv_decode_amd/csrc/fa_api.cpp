@@ -209,6 +209,10 @@ fa_status run_combine(const fa_params* p, const Shape& s, int64_t splits, const 
 
 fa_status run_prefill(const fa_params* p, const Shape& s, const void* q, const void* k, const void* v, void* out,
                       float* lse, hipStream_t stream) {
+    // The prefill kernel addresses one 64-row KV tile with 32-bit byte offsets.
+    const int64_t kv_row_elems = p->layout == FA_BNSD ? s.D : s.KVN * s.D;
+    if (kv_row_elems * 2 * 64 >= (int64_t(1) << 31))
+        return fail(FA_ERR_UNSUPPORTED, "prefill needs num_kv_heads * head_dim < 2^24 in the BSND layout");
     fa::PrefillArgs a;
     std::memset(&a, 0, sizeof a);
     a.q = static_cast<const uint16_t*>(q);

@@ -100,4 +100,25 @@ __device__ __forceinline__ float shfl_xor(float x, int m) { return __shfl_xor(x,
 // 16-byte global load / store helpers.
 __device__ __forceinline__ u32x4 ld128(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// x from lane (lane ^ 32): v_permlane32_swap exchanges the upper half-wave of
+// its first operand with the lower half-wave of its second, without LDS.
+__device__ __forceinline__ float xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from global memory straight into LDS (buffer_load ... lds):
+// lane i of the wave writes dst + 16*i (dst is wave-uniform).  Byte offsets at
+// or past nrec read as zero through the buffer resource's range check.  The
+// resource type exists only in the device compilation pass.
+__device__ __forceinline__ void lds_dma16(const void* base, int nrec, lds_void* dst, int voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+#endif
+}
+
 }  // namespace fa

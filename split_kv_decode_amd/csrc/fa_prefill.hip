@@ -15,8 +15,21 @@
 // layout the B operand of the next MFMA wants for P^T, so P goes from the
 // score accumulators to the PV instruction without touching LDS.  The row
 // max/sum of the softmax is an in-lane reduction plus one exchange between the
-// two half-waves.  Q stays in registers for the whole KV loop; K and V tiles
-// are staged in LDS with padded rows.
+// two half-waves (v_permlane32_swap).  Q stays in registers for the whole KV
+// loop.
+//
+// Memory path.  K and V tiles go from HBM straight into LDS with buffer loads
+// (no staging registers), double buffered so the next tile is in flight while
+// the current one is consumed; the buffer range check returns zeros for rows
+// at or past the batch's length, whatever the cache holds there.  LDS rows are
+// unpadded and 16-byte chunks are XOR-swizzled so that both read patterns --
+// 16 rows at one chunk for K, and the transposing ds_read_b64_tr_b16 reads
+// that build V^T operands -- are free of bank conflicts.
+//
+// Softmax.  Exponentials are taken against the running max before the tile's
+// max is known, and the output is rescaled only when a row max grows by more
+// than 2^8 (wave-uniform test); both keep the vector work per tile close to
+// one FMA, one exp, one add, half a max and half a convert per score.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -59,8 +72,21 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
 // lane i receives element i%4 of the 8-byte pieces addressed by lanes
 // i/4, i/4+4, i/4+8 and i/4+12 of its group.
-__device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
+__device__ __forceinline__ s16x4 lds_read_tr(const unsigned char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+
+// 16-byte-chunk swizzle of the unpadded LDS rows (period 16 rows).  For both
+// read patterns of the kernel the lanes served together hit distinct banks:
+// 16 consecutive rows at one logical chunk (the K reads) and four consecutive
+// rows x four consecutive chunks (the transposing V reads).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (D == 128) {
+        return ((r & 3) << 2) | ((r >> 2) & 3);
+    } else {
+        return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+    }
 }
 
 template <typename ST, int D, int MASK>
@@ -68,19 +94,22 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     using M = Mfma<ST>;
     using V8 = typename M::V8;
     using E = typename M::E;
-    constexpr int BM = 128;      // query rows per workgroup (32 per wave)
-    constexpr int BN = 64;       // keys per KV tile
-    constexpr int KP = D + 8;    // K row pitch in LDS: 16 rows of a b128 read hit distinct banks
-    constexpr int VP = D + 32;   // V row pitch: the 4 rows of a transposing read hit distinct banks
-    constexpr int CPR = D / 8;   // 16-byte pieces per row
-    constexpr int NLD = BN * CPR / 256;  // 16-byte loads per thread per tile, for K and for V
-    constexpr float kTau = 8.f;  // rescale only when a row max grows by more than 2^8
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KP];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * VP];
+    constexpr int BM = 128;             // query rows per workgroup (32 per wave)
+    constexpr int BN = 64;              // keys per KV tile
+    constexpr int RB = D * 2;           // bytes per LDS row (unpadded)
+    constexpr int TB = BN * RB;         // bytes per K or V tile
+    constexpr int CPR = D / 8;          // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;       // rows per direct-to-LDS wave load
+    constexpr int NIW = TB / 1024 / 4;  // wave loads per wave per tile (K, and again V)
+    constexpr float kTau = 8.f;         // rescale only when a row max grows by more than 2^8
+    __shared__ __attribute__((aligned(1024))) unsigned char sK0[TB];
+    __shared__ __attribute__((aligned(1024))) unsigned char sK1[TB];
+    __shared__ __attribute__((aligned(1024))) unsigned char sV0[TB];
+    __shared__ __attribute__((aligned(1024))) unsigned char sV1[TB];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: LDS DMA bases stay in SGPRs
     const int half = lane >> 5;
     const int col = lane & 31;
 
@@ -130,81 +159,87 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-    float m_run = kNegInf;  // per query row, in scaled base-2 units (same in both halves)
+    float m_run = kNegInf;  // per query row, scaled base-2 units (same in both halves)
     float l_half = 0.f;     // this half-wave's share of the row sum
 
-    const int64_t kv_off = b * a.kv_stride_b + (int64_t)n2 * a.kv_stride_n;
-    const uint16_t* kp = a.k + kv_off;
-    const uint16_t* vp = a.v + kv_off;
-
-    // Global -> register prefetch of one KV tile, register -> LDS store.
-    u32x4 kr[NLD], vr[NLD];
-    auto gload = [&](int64_t j0) {
+    // Direct-to-LDS tile loads.  Wave load I of a tile fills LDS bytes
+    // [1024*I, +1024): lane i writes 16 bytes at 16*i, i.e. row RPI*I + i/CPR,
+    // physical chunk i%CPR, which holds logical chunk (i%CPR) ^ swz(row).  The
+    // buffer resource of a tile covers only its rows below the length.
+    const int64_t row_bytes = a.kv_stride_s * 2;
+    const char* kbase = reinterpret_cast<const char*>(a.k + b * a.kv_stride_b + (int64_t)n2 * a.kv_stride_n);
+    const char* vbase = reinterpret_cast<const char*>(a.v + b * a.kv_stride_b + (int64_t)n2 * a.kv_stride_n);
+    int voff[NIW];
 #pragma unroll
-        for (int it = 0; it < NLD; ++it) {
-            const int idx = tid + it * 256;
-            const int64_t t = j0 + idx / CPR;
-            const int cc = idx % CPR;
-            if (t < L) {  // rows beyond the length stay zero whatever the cache holds
-                kr[it] = ld128(kp + t * a.kv_stride_s + cc * 8);
-                vr[it] = ld128(vp + t * a.kv_stride_s + cc * 8);
-            } else {
-                kr[it] = u32x4{0u, 0u, 0u, 0u};
-                vr[it] = u32x4{0u, 0u, 0u, 0u};
-            }
-        }
-    };
-    auto lstore = [&](int buf) {
+    for (int w = 0; w < NIW; ++w) {
+        const int r = RPI * (wave * NIW + w) + lane / CPR;
+        voff[w] = (int)(r * row_bytes) + (((lane % CPR) ^ swz<D>(r)) << 4);
+    }
+    auto issue_tile = [&](int jt, unsigned char* dK, unsigned char* dV) __attribute__((always_inline)) {
+        const int64_t j0 = (int64_t)jt * BN;
+        int64_t rows = L - j0;
+        rows = rows < 0 ? 0 : (rows > BN ? BN : rows);
+        const int nrec = (int)(rows * row_bytes);
+        const char* kt = kbase + j0 * row_bytes;
+        const char* vt = vbase + j0 * row_bytes;
 #pragma unroll
-        for (int it = 0; it < NLD; ++it) {
-            const int idx = tid + it * 256;
-            const int r = idx / CPR;
-            const int cc = idx % CPR;
-            *reinterpret_cast<u32x4*>(&Ks[buf][r * KP + cc * 8]) = kr[it];
-            *reinterpret_cast<u32x4*>(&Vs[buf][r * VP + cc * 8]) = vr[it];
+        for (int w = 0; w < NIW; ++w) {
+            const int I = wave * NIW + w;
+            lds_dma16(kt, nrec, (lds_void*)(dK + I * 1024), voff[w]);
+            lds_dma16(vt, nrec, (lds_void*)(dV + I * 1024), voff[w]);
         }
     };
 
-    // Per-lane source offsets of the transposing V reads (see lds_read_tr):
+    // Per-lane LDS read addresses.  K (A operand of S^T = K Q^T): rows col and
+    // 32+col, logical chunk 2*kk+half.  V (transposing reads, see lds_read_tr):
     // 16-lane group G = lane/16 serves head-dim columns 16*(G&1) + [0,16) of a
-    // 32-column tile and key slots 4*(G>>1) + [0,4); source lane L = lane%16
-    // points at key row L/4 of those four, columns 4*(L%4) + [0,4).
+    // 32-column tile and key slots 4*(G>>1) + [0,4); its source lane Ls =
+    // lane%16 addresses key row Ls/4 of those four (+8 for the second read),
+    // logical chunk 4*dt + 2*(G&1) + (Ls&3)/2, byte (Ls&1)*8 of it.
+    const int krow0 = col, krow1 = 32 + col;
+    const int ks0 = swz<D>(krow0), ks1 = swz<D>(krow1);
     const int trG = lane >> 4;
     const int trL = lane & 15;
-    const int tr_off = (4 * (trG >> 1) + (trL >> 2)) * VP + 16 * (trG & 1) + 4 * (trL & 3);
+    const int vrow_lo = 4 * (trG >> 1) + (trL >> 2);
+    const int vrow_hi = vrow_lo + 8;
+    const int vs_lo = swz<D>(vrow_lo), vs_hi = swz<D>(vrow_hi);
+    const int vx = 2 * (trG & 1) + ((trL & 3) >> 1);
+    const int vbyte = (trL & 1) * 8;
 
-    if (ntiles > 0) {
-        gload(0);
-        lstore(0);
-    }
+    if (ntiles > 0) issue_tile(0, sK0, sV0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    for (int jt = 0; jt < ntiles; ++jt) {
-        const int buf = jt & 1;
+    // One KV tile: its K/V are in (Kb, Vb); the next tile is loaded into
+    // (nK, nV) meanwhile.  The loop below is unrolled by two so every LDS
+    // access names a fixed buffer (which also lets the compiler see that the
+    // tile being read is not the one the in-flight loads write).
+    auto step = [&](int jt, const unsigned char* Kb, const unsigned char* Vb, unsigned char* nK,
+                    unsigned char* nV) __attribute__((always_inline)) {
         const int64_t j0 = (int64_t)jt * BN;
-        if (jt + 1 < ntiles) gload(j0 + BN);  // next tile in flight during this one
-        const uint16_t* Kb = Ks[buf];
-        const uint16_t* Vb = Vs[buf];
+        if (jt + 1 < ntiles) issue_tile(jt + 1, nK, nV);
 
-        // S^T tiles: keys [j0 + 32*tt, +32) x the wave's 32 query rows (raw q.k).
+        // S^T tiles: keys [j0 + 32*tt, +32) x the wave's 32 query rows (raw
+        // q.k); the two accumulation chains are interleaved.
         f32x16 s[2];
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[tt][r] = 0.f;
 #pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) {
-                const V8 ka = __builtin_bit_cast(
-                    V8, *reinterpret_cast<const u32x4*>(&Kb[(tt * 32 + col) * KP + kk * 16 + 8 * half]));
-                s[tt] = M::mm(ka, qreg[kk], s[tt]);
-            }
+        for (int kk = 0; kk < D / 16; ++kk) {
+            const V8 ka0 = __builtin_bit_cast(
+                V8, *reinterpret_cast<const u32x4*>(Kb + krow0 * RB + (((2 * kk + half) ^ ks0) << 4)));
+            const V8 ka1 = __builtin_bit_cast(
+                V8, *reinterpret_cast<const u32x4*>(Kb + krow1 * RB + (((2 * kk + half) ^ ks1) << 4)));
+            s[0] = M::mm(ka0, qreg[kk], s[0]);
+            s[1] = M::mm(ka1, qreg[kk], s[1]);
         }
 
         // Masking is needed only on tiles that cross the length, the causal
         // diagonal of this wave's rows, or under a boolean mask.  Accumulator
         // register r of tile tt holds key j0 + 32*tt + 8*(r/4) + 4*half + r%4.
         const bool need_mask = (j0 + BN > L) || (MASK == 1 && j0 + BN - 1 > wrow0) || (MASK == 2);
-        float tmax = kNegInf;
         if (need_mask) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
@@ -218,19 +253,37 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
                              a.mask[b * a.mask_stride[0] + (int64_t)n1 * a.mask_stride[1] +
                                     qrow * a.mask_stride[2] + tok * a.mask_stride[3]] == 0;
                     s[tt][r] = ok ? s[tt][r] : kNegInf;
-                    tmax = fmaxf(tmax, s[tt][r]);
                 }
             }
-        } else {
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[tt][r]);
         }
-        tmax = fmaxf(tmax, shfl_xor(tmax, 32)) * c;
+        float tmax = kNegInf;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[tt][r]);
+        tmax = fmaxf(tmax, xor32(tmax)) * c;
 
-        // Lazy rescale: keep the running max unless some row of the wave grew
-        // by more than kTau; exponentials then stay below 2^kTau.
+        // P^T as the B operand of O^T = V^T P^T.  K-step ks covers keys
+        // [16*ks, +16) of the tile; slot e of half h is key 4h+e (e<4) or
+        // 8+4h+(e-4) -- the order the accumulator already holds them in.
+        // Exponentials are taken against the running max; in the rare case a
+        // row max grew by more than 2^kTau they are recomputed after the
+        // rescale, so every exponential stays below 2^kTau.
+        V8 pb[4];
+        float psum = 0.f;
+        auto exps = [&](float nmx) __attribute__((always_inline)) {
+            psum = 0.f;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float p = fast_exp2(__builtin_fmaf(s[tt][r], c, nmx));
+                    psum += p;
+                    pb[tt * 2 + (r >> 3)][r & 7] = (E)p;
+                }
+            }
+        };
+        exps((m_run == kNegInf) ? 0.f : -m_run);
         if (__any(tmax > m_run + kTau)) {
             const float mnew = fmaxf(m_run, tmax);
             const float alpha = fast_exp2(m_run - ((mnew == kNegInf) ? 0.f : mnew));
@@ -240,47 +293,36 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
                 for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
             l_half *= alpha;
             m_run = mnew;
-        }
-        const float nm = (m_run == kNegInf) ? 0.f : -m_run;
-
-        // P^T as the B operand of O^T = V^T P^T.  K-step ks covers keys
-        // [16*ks, +16) of the tile; slot e of half h is key 4h+e (e<4) or
-        // 8+4h+(e-4) -- the order the accumulator already holds them in.
-        V8 pb[4];
-        float psum = 0.f;
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = fast_exp2(__builtin_fmaf(s[tt][r], c, nm));
-                psum += p;
-                pb[tt * 2 + (r >> 3)][r & 7] = (E)p;
-            }
+            exps((m_run == kNegInf) ? 0.f : -m_run);
         }
         l_half += psum;
 
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
+        for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
+            for (int dt = 0; dt < D / 32; ++dt) {
                 // A operand V^T: lane (col, half) holds head-dim row 32*dt+col
-                // at the key slots of pb[ks]; two transposing reads give the
+                // at the key slots of pb[ks]; the two transposing reads give
                 // slots 0..3 (keys 4h+[0,4)) and 4..7 (keys 8+4h+[0,4)).
-                const uint16_t* vb = Vb + ks * 16 * VP + dt * 32 + tr_off;
-                const s16x4 lo = lds_read_tr(vb);
-                const s16x4 hi = lds_read_tr(vb + 8 * VP);
-                const V8 va = __builtin_bit_cast(
-                    V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                const int lc = 4 * dt + vx;
+                const unsigned char* vb = Vb + ks * 16 * RB;
+                const s16x4 lo = lds_read_tr(vb + vrow_lo * RB + ((lc ^ vs_lo) << 4) + vbyte);
+                const s16x4 hi = lds_read_tr(vb + vrow_hi * RB + ((lc ^ vs_hi) << 4) + vbyte);
+                const V8 va = __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 o[dt] = M::mm(va, pb[ks], o[dt]);
             }
         }
 
-        if (jt + 1 < ntiles) lstore(buf ^ 1);
-        __syncthreads();
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of the next tile landed
+        __syncthreads();  // ... and everyone else's; this tile is consumed
+    };
+    for (int jt = 0; jt < ntiles; jt += 2) {
+        step(jt, sK0, sV0, sK1, sV1);
+        if (jt + 1 < ntiles) step(jt + 1, sK1, sV1, sK0, sV0);
     }
 
     // Epilogue: divide by l, RowInvalid defaults, store in the q layout.
-    const float l_run = l_half + shfl_xor(l_half, 32);
+    const float l_run = l_half + xor32(l_half);
     if (qvalid) {
         const bool empty = (m_run == kNegInf);
         const float inv = empty ? 0.f : 1.f / l_run;

@@ -71,6 +71,8 @@ def main():
                     help="also run a plain 1 GiB device copy per step (counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the per-workload report of the other configurations")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -224,8 +226,64 @@ def main():
                                "kind": "oracle",
                                "sample": f"the whole decode_128k workload (32 rows x 131072 keys), "
                                          f"{n} pass(es) in {t_cpu:.1f} s, fp64"}
+    if not args.no_extra:
+        out["workloads"] = extra_workloads(fa, fa_synth, np, torch, dev16, stream)
     out["setup_s"] = round(t_gen, 1)
     print(json.dumps(out))
+
+
+def extra_workloads(fa, fa_synth, np, torch, dev16, stream, warmup=3, iters=10):
+    """Time the other configurations with fa_fwd (events on the launch stream)."""
+    res = {}
+    cases = [("prefill_small", None), ("decode_gqa", None), ("prefill_causal", "bool"),
+             ("prefill_causal", "causal"), ("prefill_gqa_long", None)]
+    for name, mode in cases:
+        inp = fa_synth.make(fa_synth.WORKLOADS[name])
+        s = inp.spec
+        q, k, v = (dev16(x, s.dtype) for x in (inp.q, inp.k, inp.v))
+        lens = None if inp.lens is None else torch.from_numpy(inp.lens).to(q.device)
+        m = mode or {"none": "none", "causal": "causal", "bool_causal": "bool"}[s.mask]
+        mask = torch.from_numpy(inp.mask).to(q.device) if m == "bool" else None
+        p = fa.params_for(q, k, layout=s.layout, scale=s.softmax_scale, actual_seq_lengths=lens,
+                          mask=mask, mask_stride=inp.mask_strides, causal=(m == "causal"))
+        out = torch.empty_like(q)
+        lse = torch.empty((s.B, s.QN, s.QS), dtype=torch.float32, device=q.device)
+        nbytes = fa.fa_workspace_size(p)
+        ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=q.device)
+        for _ in range(warmup):
+            fa.fa_fwd(p, q, k, v, out, lse, ws, nbytes, stream)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(iters)]
+        for a, b in evs:
+            a.record(stream)
+            fa.fa_fwd(p, q, k, v, out, lse, ws, nbytes, stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        key = name if mode is None else f"{name}_{mode}"
+        if s.QS == 1:
+            L = np.full(s.B, s.KVS) if inp.lens is None else np.clip(inp.lens, 0, s.KVS)
+            nb = float(L.sum()) * s.KVN * s.D * 2 * 2 + 2 * s.B * s.QN * s.D * 2
+            gbs = nb / (ms * 1e-3) / 1e9
+            res[key] = {"ms": round(ms, 5), "kv_gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                        "bytes": nb, "doc": s.doc}
+        else:
+            S = s.QS
+            if m == "none" and inp.lens is None:
+                fl = 4.0 * s.B * s.QN * S * s.KVS * s.D
+            else:
+                L = np.full(s.B, s.KVS) if inp.lens is None else np.clip(inp.lens, 0, s.KVS).astype(np.float64)
+                if m == "none":
+                    pairs = L * S
+                else:  # causal: row i sees min(i + 1, L) keys
+                    pairs = L * (L + 1) / 2 + np.maximum(S - L, 0) * L
+                fl = 4.0 * s.QN * s.D * float(np.sum(pairs))
+            tf = fl / (ms * 1e-3) / 1e12
+            res[key] = {"ms": round(ms, 5), "tflops": round(tf, 2),
+                        "frac_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "flop": fl, "doc": s.doc}
+        del q, k, v, out, lse, ws, mask, inp
+        torch.cuda.empty_cache()
+    return res
 
 
 if __name__ == "__main__":

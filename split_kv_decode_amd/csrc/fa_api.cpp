@@ -246,7 +246,16 @@ fa_status run_prefill(const fa_params* p, const Shape& s, const void* q, const v
     a.q_tiles = (int32_t)((s.QS + 127) / 128);
     a.negate_q = p->scale < 0 ? 1 : 0;
     a.scale_log2 = (float)(std::fabs(p->scale) * 1.4426950408889634);
-    const int mm = p->mask_mode == FA_MASK_NONE ? 0 : (p->mask_mode == FA_MASK_CAUSAL ? 1 : 2);
+    int mm = p->mask_mode == FA_MASK_NONE ? 0 : (p->mask_mode == FA_MASK_CAUSAL ? 1 : 2);
+    // A boolean mask whose rows are contiguous, 16-byte aligned key runs is
+    // staged through LDS tile by tile (instantiation 3); any other stride
+    // pattern is read element by element (instantiation 2).
+    if (mm == 2) {
+        const int64_t* st = p->mask_stride;
+        const bool rows_ok = st[3] == 1 && aligned(p->mask, 16) && st[0] % 16 == 0 && st[1] % 16 == 0 &&
+                             st[2] % 16 == 0 && s.KVS % 16 == 0 && st[2] < (int64_t(1) << 23);
+        if (rows_ok) mm = 3;
+    }
     return launch_result(fa::launch_prefill(a, p->dtype == FA_BF16 ? 1 : 0, (int)s.D, mm, s.B, stream), "prefill");
 }
 

@@ -106,6 +106,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char sK1[TB];
     __shared__ __attribute__((aligned(1024))) unsigned char sV0[TB];
     __shared__ __attribute__((aligned(1024))) unsigned char sV1[TB];
+    // MASK 3: the boolean mask tile (128 query rows x 64 keys, one byte each),
+    // chunk-major: 16-byte chunk c of row r at (c*128 + r)*16.
+    constexpr int MT = (MASK == 3) ? BM * BN : 16;
+    __shared__ __attribute__((aligned(1024))) unsigned char sM0[MT];
+    __shared__ __attribute__((aligned(1024))) unsigned char sM1[MT];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -175,7 +180,22 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         const int r = RPI * (wave * NIW + w) + lane / CPR;
         voff[w] = (int)(r * row_bytes) + (((lane % CPR) ^ swz<D>(r)) << 4);
     }
-    auto issue_tile = [&](int jt, unsigned char* dK, unsigned char* dV) __attribute__((always_inline)) {
+    // MASK 3 mask tile: wave w loads chunk w (keys 16*w .. 16*w+15) of all
+    // 128 rows, 64 rows per wave load.  The resource stops at the last valid
+    // row's last key, so nothing past the mask tensor is read.
+    const char* mbase = reinterpret_cast<const char*>(a.mask) + b * a.mask_stride[0] +
+                        (int64_t)n1 * a.mask_stride[1] + i0 * a.mask_stride[2];
+    int moff[2] = {0, 0};
+    int mrec_rows = 0;
+    if (MASK == 3) {
+#pragma unroll
+        for (int w = 0; w < 2; ++w) moff[w] = (int)((w * 64 + lane) * a.mask_stride[2]) + wave * 16;
+        int64_t rv = a.q_seq - i0;
+        rv = rv > BM ? BM : rv;
+        mrec_rows = (int)((rv - 1) * a.mask_stride[2]);
+    }
+    auto issue_tile = [&](int jt, unsigned char* dK, unsigned char* dV, unsigned char* dM)
+                          __attribute__((always_inline)) {
         const int64_t j0 = (int64_t)jt * BN;
         int64_t rows = L - j0;
         rows = rows < 0 ? 0 : (rows > BN ? BN : rows);
@@ -187,6 +207,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
             const int I = wave * NIW + w;
             lds_dma16(kt, nrec, (lds_void*)(dK + I * 1024), voff[w]);
             lds_dma16(vt, nrec, (lds_void*)(dV + I * 1024), voff[w]);
+        }
+        if (MASK == 3) {
+            int64_t keys = a.kv_seq - j0;
+            keys = keys > BN ? BN : keys;
+            const int mrec = mrec_rows + (int)keys;
+#pragma unroll
+            for (int w = 0; w < 2; ++w)
+                lds_dma16(mbase + j0, mrec, (lds_void*)(dM + (2 * wave + w) * 1024), moff[w]);
         }
     };
 
@@ -206,7 +234,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     const int vx = 2 * (trG & 1) + ((trL & 3) >> 1);
     const int vbyte = (trL & 1) * 8;
 
-    if (ntiles > 0) issue_tile(0, sK0, sV0);
+    if (ntiles > 0) issue_tile(0, sK0, sV0, sM0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
@@ -214,10 +242,40 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     // (nK, nV) meanwhile.  The loop below is unrolled by two so every LDS
     // access names a fixed buffer (which also lets the compiler see that the
     // tile being read is not the one the in-flight loads write).
-    auto step = [&](int jt, const unsigned char* Kb, const unsigned char* Vb, unsigned char* nK,
-                    unsigned char* nV) __attribute__((always_inline)) {
+    auto step = [&](int jt, const unsigned char* Kb, const unsigned char* Vb, const unsigned char* Mb,
+                    unsigned char* nK, unsigned char* nV, unsigned char* nM) __attribute__((always_inline)) {
         const int64_t j0 = (int64_t)jt * BN;
-        if (jt + 1 < ntiles) issue_tile(jt + 1, nK, nV);
+        if (jt + 1 < ntiles) issue_tile(jt + 1, nK, nV, nM);
+
+        // MASK 3: this lane's 32 mask bytes -- word (tt, g) holds keys
+        // 32*tt + 8*g + 4*half + [0,4) of row 32*wave + col -- and a
+        // wave-uniform skip of tiles the mask excludes entirely for its rows.
+        uint32_t mw[2][4];
+        if (MASK == 3) {
+            bool lane_all = !qvalid || j0 >= L;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int ch = 2 * tt + (g >> 1);
+                    mw[tt][g] = *reinterpret_cast<const uint32_t*>(
+                        Mb + (ch * BM + 32 * wave + col) * 16 + 8 * (g & 1) + 4 * half);
+                }
+            }
+            bool none_zero = true;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    none_zero = none_zero && (((mw[tt][g] - 0x01010101u) & ~mw[tt][g] & 0x80808080u) == 0u);
+            lane_all = lane_all || none_zero;
+            if (__all(lane_all)) {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                __syncthreads();
+                return;
+            }
+            asm volatile("" ::: "memory");  // re-read the words after the QK MFMAs instead of holding them
+        }
 
         // S^T tiles: keys [j0 + 32*tt, +32) x the wave's 32 query rows (raw
         // q.k); the two accumulation chains are interleaved.
@@ -239,7 +297,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         // Masking is needed only on tiles that cross the length, the causal
         // diagonal of this wave's rows, or under a boolean mask.  Accumulator
         // register r of tile tt holds key j0 + 32*tt + 8*(r/4) + 4*half + r%4.
-        const bool need_mask = (j0 + BN > L) || (MASK == 1 && j0 + BN - 1 > wrow0) || (MASK == 2);
+        const bool need_mask = (j0 + BN > L) || (MASK == 1 && j0 + BN - 1 > wrow0) || (MASK >= 2);
+        if (MASK == 3) {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    mw[tt][g] = *reinterpret_cast<const uint32_t*>(
+                        Mb + ((2 * tt + (g >> 1)) * BM + 32 * wave + col) * 16 + 8 * (g & 1) + 4 * half);
+        }
         if (need_mask) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
@@ -252,6 +318,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
                         ok = ok && qvalid &&
                              a.mask[b * a.mask_stride[0] + (int64_t)n1 * a.mask_stride[1] +
                                     qrow * a.mask_stride[2] + tok * a.mask_stride[3]] == 0;
+                    if (MASK == 3) ok = ok && qvalid && ((mw[tt][r >> 2] >> (8 * (r & 3))) & 0xffu) == 0u;
                     s[tt][r] = ok ? s[tt][r] : kNegInf;
                 }
             }
@@ -317,8 +384,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         __syncthreads();  // ... and everyone else's; this tile is consumed
     };
     for (int jt = 0; jt < ntiles; jt += 2) {
-        step(jt, sK0, sV0, sK1, sV1);
-        if (jt + 1 < ntiles) step(jt + 1, sK1, sV1, sK0, sV0);
+        step(jt, sK0, sV0, sM0, sK1, sV1, sM1);
+        if (jt + 1 < ntiles) step(jt + 1, sK1, sV1, sM1, sK0, sV0, sM0);
     }
 
     // Epilogue: divide by l, RowInvalid defaults, store in the q layout.
@@ -354,6 +421,7 @@ static hipError_t dispatch_prefill(const PrefillArgs& a, int mask_mode, int64_t 
         case 0: hipLaunchKernelGGL((prefill_kernel<ST, D, 0>), grid, block, 0, s, a); break;
         case 1: hipLaunchKernelGGL((prefill_kernel<ST, D, 1>), grid, block, 0, s, a); break;
         case 2: hipLaunchKernelGGL((prefill_kernel<ST, D, 2>), grid, block, 0, s, a); break;
+        case 3: hipLaunchKernelGGL((prefill_kernel<ST, D, 3>), grid, block, 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

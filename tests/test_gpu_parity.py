@@ -245,6 +245,68 @@ def test_prefill_random_bool_mask_with_empty_rows():
     assert math.isinf(float(lse[1, 2, 5])) and torch.all(out[1, 2, 5] == 0)
 
 
+def _bool_mask_run(inp, mask_np, strides, byte_offset=0):
+    """fa_fwd with a boolean mask given as a (possibly offset) device byte buffer."""
+    s = inp.spec
+    q, k, v = (dev16(x, s.dtype) for x in (inp.q, inp.k, inp.v))
+    lens = None if inp.lens is None else torch.from_numpy(inp.lens).to(DEV)
+    flat = np.zeros(mask_np.size + 64, np.uint8)
+    flat[byte_offset:byte_offset + mask_np.size] = mask_np.reshape(-1)
+    buf = torch.from_numpy(flat).to(DEV)
+    p = fa.params_for(q, k, layout=s.layout, scale=s.softmax_scale, actual_seq_lengths=lens,
+                      mask=buf.data_ptr() + byte_offset, mask_stride=strides)
+    out = torch.empty_like(q)
+    lse = torch.empty((s.B, s.QN, s.QS), dtype=torch.float32, device=DEV)
+    fa.fa_fwd(p, q, k, v, out, lse, None, 0, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("byte_offset", [0, 1], ids=["lds_staged", "elementwise"])
+def test_prefill_bool_mask_both_paths(byte_offset):
+    """Rows of 16-byte aligned keys go through LDS (with per-wave tile skipping);
+    a misaligned mask pointer takes the element-wise path.  Both match the oracle."""
+    s = spec(layout="BNSD", B=2, QN=4, KVN=2, QS=200, KVS=320, D=128, lens=(150, 320), seed=29)
+    inp = fa_synth.make(s)
+    rng = np.random.default_rng(5)
+    mask = (rng.random((2, 4, 200, 320)) < 0.5).astype(np.uint8)
+    mask[:, :, :, 256:] = 1          # a fully masked key tile
+    mask[1, 3, :128, :] = 1          # a fully masked query tile of one head
+    mask[0, 2, 77, :] = 1            # an empty row
+    strides = (4 * 200 * 320, 200 * 320, 320, 1)
+    out, lse = _bool_mask_run(inp, mask, strides, byte_offset)
+    inp.mask, inp.mask_strides = mask, strides
+    prob = oracle.Problem.from_inputs(inp, "bool")
+    ref, ref_lse = oracle.attention(prob, inp.q, inp.k, inp.v)
+    o_rows = rows_of(out, s, np.arange(s.B * s.QN * s.QS))
+    check(o_rows, to_np(lse).reshape(-1), ref.reshape(-1, s.D), ref_lse.reshape(-1), "bool mask")
+    assert math.isinf(float(lse[0, 2, 77])) and torch.all(out[0, 2, 77] == 0)
+
+
+def test_prefill_broadcast_bool_mask_matches_oracle():
+    """A (B,1,1,S) mask (one key mask per batch, as in the IFA example) broadcast over heads and rows."""
+    s = spec(layout="BSND", B=3, QN=4, KVN=4, QS=130, KVS=256, D=64, seed=31)
+    inp = fa_synth.make(s)
+    rng = np.random.default_rng(8)
+    mask = (rng.random((3, 1, 1, 256)) < 0.3).astype(np.uint8)
+    strides = (256, 0, 0, 1)
+    out, lse = _bool_mask_run(inp, mask, strides)
+    inp.mask, inp.mask_strides = mask, strides
+    prob = oracle.Problem.from_inputs(inp, "bool")
+    ref, ref_lse = oracle.attention(prob, inp.q, inp.k, inp.v)
+    o_rows = rows_of(out, s, np.arange(s.B * s.QN * s.QS))
+    r_rows = np.ascontiguousarray(ref.transpose(0, 2, 1, 3)).reshape(-1, s.D)
+    check(o_rows, to_np(lse).reshape(-1), r_rows, ref_lse.reshape(-1), "broadcast bool mask")
+
+
+def test_prefill_staged_causal_mask_equals_causal_mode():
+    inp = fa_synth.make(spec(layout="BSND", B=1, QN=4, KVN=2, QS=320, KVS=320, mask="bool_causal",
+                             seed=37))
+    o1, l1 = run_fwd(inp, "bool")
+    o2, l2 = run_fwd(inp, "causal")
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 def test_prefill_ignores_nan_padding():
     inp = fa_synth.make(spec(layout="BNSD", B=3, QN=2, KVN=2, QS=100, KVS=300, D=128, lens=(0, 300),
                              mask="causal", seed=23))

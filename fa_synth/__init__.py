@@ -231,3 +231,37 @@ def sample_rows(spec: Spec, n: int, seed: int = 7, lens: Optional[np.ndarray] = 
     extra = rng.integers(0, total, size=max(0, n - len(picks)))
     picks.update(int(x) for x in extra)
     return np.array(sorted(picks), dtype=np.int64)
+
+
+def to_paged(inp: Inputs, block_size: int, kv_layout: str = "PA_BBND", seed: int = 0,
+             spare_blocks: int = 3):
+    """Store the K/V cache of ``inp`` as a paged cache (FlashAttn developer guide 1.2).
+
+    Token j of batch b goes to row j % block_size of physical block
+    block_table[b][j // block_size]; physical blocks are a seeded permutation
+    with ``spare_blocks`` unused ones filled with NaN (they must never be read).
+    PA_BBND blocks are [block_size][KV_N][D]; PA_BNBD blocks [KV_N][block_size][D].
+    Returns (k_paged, v_paged, block_table int32 [B, max_blocks], num_blocks).
+    """
+    s = inp.spec
+    max_blocks = -(-s.KVS // block_size)
+    nb = s.B * max_blocks + spare_blocks
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(nb)
+    table = perm[: s.B * max_blocks].reshape(s.B, max_blocks).astype(np.int32)
+    nan = NAN_BITS[s.dtype]
+    out = []
+    for x in (inp.k, inp.v):
+        xb = x if s.layout == BNSD else x.transpose(0, 2, 1, 3)  # -> [B, KVN, KVS, D]
+        pad = np.full((s.B, s.KVN, max_blocks * block_size, s.D), nan, np.uint16)
+        pad[:, :, : s.KVS] = xb
+        blocks = pad.reshape(s.B, s.KVN, max_blocks, block_size, s.D)
+        if kv_layout == "PA_BBND":
+            phys = np.full((nb, block_size, s.KVN, s.D), nan, np.uint16)
+            src = blocks.transpose(0, 2, 3, 1, 4)                      # [B, blk, bs, KVN, D]
+        else:
+            phys = np.full((nb, s.KVN, block_size, s.D), nan, np.uint16)
+            src = blocks.transpose(0, 2, 1, 3, 4)                      # [B, blk, KVN, bs, D]
+        phys[table.reshape(-1)] = src.reshape((s.B * max_blocks,) + phys.shape[1:])
+        out.append(np.ascontiguousarray(phys))
+    return out[0], out[1], table, nb

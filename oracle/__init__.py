@@ -45,7 +45,10 @@ class _Problem(ctypes.Structure):
                 ("lens", ctypes.POINTER(ctypes.c_int64)),
                 ("mask_mode", ctypes.c_int32),
                 ("mask", ctypes.POINTER(ctypes.c_uint8)),
-                ("mask_stride", ctypes.c_int64 * 4)]
+                ("mask_stride", ctypes.c_int64 * 4),
+                ("kv_layout", ctypes.c_int32),
+                ("block_table", ctypes.POINTER(ctypes.c_int32)),
+                ("block_size", ctypes.c_int64), ("max_blocks", ctypes.c_int64)]
 
 
 def _load():
@@ -88,13 +91,18 @@ class Problem:
     """Shapes and options of one attention-forward call, as the oracle sees them."""
 
     def __init__(self, B, QN, KVN, QS, KVS, D, layout="BNSD", dtype="bf16", scale=1.0,
-                 lens=None, mask_mode="none", mask=None, mask_strides=(0, 0, 0, 0)):
+                 lens=None, mask_mode="none", mask=None, mask_strides=(0, 0, 0, 0),
+                 kv_layout="contiguous", block_table=None, block_size=0):
         self.B, self.QN, self.KVN, self.QS, self.KVS, self.D = B, QN, KVN, QS, KVS, D
         self.layout, self.dtype, self.scale = layout, dtype, float(scale)
         self.lens = None if lens is None else np.ascontiguousarray(lens, dtype=np.int64)
         self.mask_mode = mask_mode
         self.mask = None if mask is None else np.ascontiguousarray(mask, dtype=np.uint8)
         self.mask_strides = tuple(int(s) for s in mask_strides)
+        self.kv_layout = kv_layout          # "contiguous", "PA_BBND" or "PA_BNBD"
+        self.block_table = (None if block_table is None
+                            else np.ascontiguousarray(block_table, dtype=np.int32))
+        self.block_size = int(block_size)
 
     @classmethod
     def from_inputs(cls, inp, mask_mode: Optional[str] = None):
@@ -116,6 +124,10 @@ class Problem:
         p.mask = _ptr(self.mask, ctypes.c_uint8)
         for i in range(4):
             p.mask_stride[i] = self.mask_strides[i]
+        p.kv_layout = {"contiguous": 0, "PA_BBND": 1, "PA_BNBD": 2}[self.kv_layout]
+        p.block_table = _ptr(self.block_table, ctypes.c_int32)
+        p.block_size = self.block_size
+        p.max_blocks = 0 if self.block_table is None else self.block_table.shape[-1]
         return p
 
     def nrows(self) -> int:

@@ -28,6 +28,9 @@
  *   - orc_merge: the FD reduction m = max_c m_c, l = sum_c l_c exp(m_c - m),
  *     o = sum_c O_c exp(m_c - m) / l, lse = log l + m (FlashAttn developer
  *     guide 10, FD block formula; FlashDecoding tutorial section 2).
+ *   - Paged KV caches (FlashAttn developer guide 1.2): token j of batch b is
+ *     row j % block_size of physical block block_table[b][j / block_size];
+ *     PA_BBND blocks are [block_size][KV_N][D], PA_BNBD blocks [KV_N][block_size][D].
  *
  * Two passes per row (scores and max first, then exponentials), natural exp
  * and log, no blocking or reordering beyond that.
@@ -47,6 +50,9 @@ typedef struct {
     int32_t mask_mode;          /* 0 none, 1 causal (j > i excluded), 2 boolean tensor */
     const uint8_t *mask;        /* mode 2: nonzero = excluded */
     int64_t mask_stride[4];     /* element strides for (b, n1, i, j); 0 broadcasts */
+    int32_t kv_layout;          /* 0 = as layout, 1 = paged BBND, 2 = paged BNBD */
+    const int32_t *block_table; /* [B][max_blocks] physical block ids */
+    int64_t block_size, max_blocks;
 } orc_problem;
 
 static double dec16(int32_t dtype, uint16_t h)
@@ -77,6 +83,12 @@ static int64_t q_index(const orc_problem *p, int64_t b, int64_t n, int64_t i)
 
 static int64_t kv_index(const orc_problem *p, int64_t b, int64_t n, int64_t j)
 {
+    if (p->kv_layout != 0) {
+        const int64_t blk = p->block_table[b * p->max_blocks + j / p->block_size];
+        const int64_t r = j % p->block_size;
+        return p->kv_layout == 1 ? ((blk * p->block_size + r) * p->KVN + n) * p->D
+                                 : ((blk * p->KVN + n) * p->block_size + r) * p->D;
+    }
     return p->layout == 0 ? ((b * p->KVN + n) * p->KVS + j) * p->D
                           : ((b * p->KVS + j) * p->KVN + n) * p->D;
 }
@@ -202,6 +214,8 @@ static int check(const orc_problem *p)
     if (!p || p->B < 0 || p->QN <= 0 || p->KVN <= 0 || p->QS < 0 || p->KVS < 0 || p->D <= 0) return -1;
     if (p->QN % p->KVN != 0) return -2;
     if (p->mask_mode == 2 && !p->mask) return -3;
+    if (p->kv_layout != 0 && (!p->block_table || p->block_size <= 0 || p->max_blocks <= 0 ||
+                              p->KVS > p->max_blocks * p->block_size)) return -5;
     return 0;
 }
 

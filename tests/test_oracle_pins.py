@@ -348,3 +348,40 @@ def test_generator_is_deterministic_and_rounds_to_nearest_even():
     got = fa_synth.f32_to_bf16_bits(x)
     # ties go to even: 1+2^-8 -> 1.0 (0x3F80); 1+3*2^-8 -> 1+2^-6 (0x3F82); above tie rounds up
     assert list(got) == [0x3F80, 0x3F82, 0x3F81]
+
+
+# ---------------------------------------------------------------- paged KV cache
+
+@pytest.mark.parametrize("kv_layout", ["PA_BBND", "PA_BNBD"])
+@pytest.mark.parametrize("layout", ["BNSD", "BSND"])
+def test_paged_cache_equals_contiguous(kv_layout, layout):
+    """A paged cache (FlashAttn guide 1.2) holds the same logical K/V: the oracle must give
+    the contiguous result, and never touch the NaN-filled spare blocks or padding."""
+    inp = tiny(layout=layout, B=3, QN=8, KVN=2, QS=1, KVS=70, D=16, lens=(0, 70), seed=61)
+    p = prob_of(inp)
+    out, lse = oracle.attention(p, inp.q, inp.k, inp.v)
+    kp, vp, table, _ = fa_synth.to_paged(inp, 16, kv_layout, seed=3)
+    pp = oracle.Problem(3, 8, 2, 1, 70, 16, layout, "bf16", p.scale, inp.lens, "none",
+                        kv_layout=kv_layout, block_table=table, block_size=16)
+    out2, lse2 = oracle.attention(pp, inp.q, kp, vp)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+    o, m, l = oracle.split_partials(pp, inp.q, kp, vp, splits=3, chunk=32)
+    o0, m0, l0 = oracle.split_partials(p, inp.q, inp.k, inp.v, splits=3, chunk=32)
+    assert np.array_equal(o, o0) and np.array_equal(m, m0) and np.array_equal(l, l0)
+
+
+def test_paged_block_gather_by_hand():
+    """Closed check of the indirection: with one-row-per-block paging (block_size 1 is not a
+    legal GPU block size, but the oracle's indexing is general) the value rows seen by a
+    query with Q=0 are exactly the rows the table points to, so out = their mean."""
+    inp = tiny(layout="BNSD", B=1, QN=1, KVN=1, QS=1, KVS=4, D=8, seed=62)
+    table = np.array([[2, 0, 3, 1]], np.int32)
+    vp = np.zeros((4, 1, 1, 8), np.uint16)      # PA_BBND with block_size 1
+    kp = np.zeros((4, 1, 1, 8), np.uint16)
+    for j in range(4):
+        vp[table[0, j], 0, 0] = inp.v[0, 0, j]
+        kp[table[0, j], 0, 0] = inp.k[0, 0, j]
+    pp = oracle.Problem(1, 1, 1, 1, 4, 8, "BNSD", "bf16", 0.5, None, "none",
+                        kv_layout="PA_BBND", block_table=table, block_size=1)
+    out, _ = oracle.attention(pp, np.zeros_like(inp.q), kp, vp)
+    assert np.allclose(out[0, 0, 0], dec(inp.v, "bf16")[0, 0].mean(axis=0), atol=1e-14)

@@ -187,7 +187,7 @@ def main():
                          "stage1_ms": round(s1, 5), "combine_ms": round(cb, 5),
                          "leg_ms": round(leg, 5), "kv_gbs": round(value, 2),
                          "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4)}
-        out["roofline"] = {"kernel": "decode_stage1_kernel<BF16,128,1,false>", "bound": "hbm",
+        out["roofline"] = {"kernel": "decode_stage1_kernel<BF16,128,1,false,false>", "bound": "hbm",
                            "achieved": round(s1_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(s1_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                            "algorithmic_bytes_per_launch": dec["kv_bytes"] + dec["qo_bytes"]}
@@ -235,17 +235,35 @@ def main():
 def extra_workloads(fa, fa_synth, np, torch, dev16, stream, warmup=3, iters=10):
     """Time the other configurations with fa_fwd (events on the launch stream)."""
     res = {}
-    cases = [("prefill_small", None), ("decode_gqa", None), ("prefill_causal", "bool"),
-             ("prefill_causal", "causal"), ("prefill_gqa_long", None)]
-    for name, mode in cases:
+    # (workload, mask mode override, paged cache (kv_layout, block_size) or None)
+    cases = [("prefill_small", None, None), ("decode_gqa", None, None),
+             ("decode_gqa", None, ("PA_BBND", 128)), ("decode_128k", None, ("PA_BNBD", 128)),
+             ("prefill_causal", "bool", None), ("prefill_causal", "causal", None),
+             ("prefill_gqa_long", None, None)]
+    for name, mode, paging in cases:
         inp = fa_synth.make(fa_synth.WORKLOADS[name])
         s = inp.spec
-        q, k, v = (dev16(x, s.dtype) for x in (inp.q, inp.k, inp.v))
+        block_table = None
+        if paging is None:
+            q, k, v = (dev16(x, s.dtype) for x in (inp.q, inp.k, inp.v))
+        else:
+            if inp.lens is None:  # a paged cache always carries per-batch lengths
+                inp.lens = np.full(s.B, s.KVS, dtype=np.int64)
+            kp, vp, table, nblocks = fa_synth.to_paged(inp, paging[1], paging[0])
+            q, k, v = dev16(inp.q, s.dtype), dev16(kp, s.dtype), dev16(vp, s.dtype)
+            block_table = torch.from_numpy(table).to(q.device)
+            del kp, vp
         lens = None if inp.lens is None else torch.from_numpy(inp.lens).to(q.device)
         m = mode or {"none": "none", "causal": "causal", "bool_causal": "bool"}[s.mask]
         mask = torch.from_numpy(inp.mask).to(q.device) if m == "bool" else None
-        p = fa.params_for(q, k, layout=s.layout, scale=s.softmax_scale, actual_seq_lengths=lens,
-                          mask=mask, mask_stride=inp.mask_strides, causal=(m == "causal"))
+        if paging is None:
+            p = fa.params_for(q, k, layout=s.layout, scale=s.softmax_scale, actual_seq_lengths=lens,
+                              mask=mask, mask_stride=inp.mask_strides, causal=(m == "causal"))
+        else:
+            p = fa.make_params(s.B, s.QN, 1, s.KVS, s.D, num_kv_heads=s.KVN, layout=s.layout,
+                               dtype=s.dtype, scale=s.softmax_scale, actual_seq_lengths=lens,
+                               kv_layout=paging[0], block_table=block_table, block_size=paging[1],
+                               max_blocks_per_seq=block_table.shape[1], num_blocks=nblocks)
         out = torch.empty_like(q)
         lse = torch.empty((s.B, s.QN, s.QS), dtype=torch.float32, device=q.device)
         nbytes = fa.fa_workspace_size(p)
@@ -261,12 +279,15 @@ def extra_workloads(fa, fa_synth, np, torch, dev16, stream, warmup=3, iters=10):
         torch.cuda.synchronize()
         ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
         key = name if mode is None else f"{name}_{mode}"
+        if paging is not None:
+            key = f"{name}_paged_{paging[0]}_bs{paging[1]}"
         if s.QS == 1:
             L = np.full(s.B, s.KVS) if inp.lens is None else np.clip(inp.lens, 0, s.KVS)
             nb = float(L.sum()) * s.KVN * s.D * 2 * 2 + 2 * s.B * s.QN * s.D * 2
             gbs = nb / (ms * 1e-3) / 1e9
             res[key] = {"ms": round(ms, 5), "kv_gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-                        "bytes": nb, "doc": s.doc}
+                        "bytes": nb, "doc": s.doc,
+                        "kv_cache": "contiguous" if paging is None else f"{paging[0]}, block_size {paging[1]}"}
         else:
             S = s.QS
             if m == "none" and inp.lens is None:
@@ -281,7 +302,7 @@ def extra_workloads(fa, fa_synth, np, torch, dev16, stream, warmup=3, iters=10):
             tf = fl / (ms * 1e-3) / 1e12
             res[key] = {"ms": round(ms, 5), "tflops": round(tf, 2),
                         "frac_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "flop": fl, "doc": s.doc}
-        del q, k, v, out, lse, ws, mask, inp
+        del q, k, v, out, lse, ws, mask, inp, block_table
         torch.cuda.empty_cache()
     return res
 

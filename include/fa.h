@@ -27,6 +27,8 @@
  *   - q, k, v and out share one layout and one 16-bit storage type.
  *       FA_BNSD: [B][N][S][D]    FA_BSND: [B][S][N][D]   (both contiguous)
  *     BSH is BSND with H = N*D.  Base pointers must be 16-byte aligned.
+ *   - k and v are either contiguous in that layout (FA_KV_CONTIGUOUS) or a
+ *     paged cache (FA_KV_PAGED_*, decode only; see fa_params.kv_layout).
  *   - Query head n1 reads KV head n1 / g with g = num_heads / num_kv_heads:
  *     g consecutive query heads share one KV head (FlashAttn developer guide,
  *     1.1 MHA and GQA).
@@ -67,6 +69,20 @@ typedef enum {
     FA_MASK_BOOL = 2     /* uint8 tensor, nonzero = excluded */
 } fa_mask_mode;
 
+/* KV cache storage (FlashAttn developer guide 1.2, PagedAttention, and its
+ * layout_kv table): contiguous [B][KV_S][KV_N][D] / [B][KV_N][KV_S][D] as
+ * set by `layout`, or fixed-size physical blocks indexed by a block table.
+ *   FA_KV_PAGED_BBND: k, v are [num_blocks][block_size][KV_N][D] (BSND inside a block)
+ *   FA_KV_PAGED_BNBD: k, v are [num_blocks][KV_N][block_size][D] (BNSD inside a block)
+ * Token j of batch b lives in row j % block_size of physical block
+ * block_table[b * max_blocks_per_seq + j / block_size].  q, out and lse keep
+ * `layout`.  The NZ fractal block format of the pages is not provided. */
+typedef enum {
+    FA_KV_CONTIGUOUS = 0,
+    FA_KV_PAGED_BBND = 1,
+    FA_KV_PAGED_BNBD = 2
+} fa_kv_layout;
+
 typedef struct {
     int64_t batch;            /* B >= 1 */
     int64_t num_heads;        /* Q_N >= 1 */
@@ -88,6 +104,23 @@ typedef struct {
      * elements; a stride of 0 broadcasts that axis (e.g. (B,1,1,S) or (1,1,S,S)). */
     const uint8_t *mask;
     int64_t mask_stride[4];
+    /* Paged KV cache (all zero / NULL for FA_KV_CONTIGUOUS, where a non-NULL
+     * block_table is an error).  A paged cache needs q_seq == 1, mask NONE and
+     * actual_seq_lengths (developer guide 1.2 makes the per-batch lengths
+     * mandatory with paging); prefill on a paged cache returns
+     * FA_ERR_UNSUPPORTED.
+     *   block_table: device int32 [batch][max_blocks_per_seq], row-major.
+     *     Entries of blocks a batch's length reaches must lie in
+     *     [0, num_blocks); the kernels clamp them into that range so a bad
+     *     entry reads a wrong block rather than out-of-bounds memory.
+     *   block_size: tokens per block, a multiple of 16 in [16, 1024].
+     *   max_blocks_per_seq >= 1, with kv_seq <= max_blocks_per_seq * block_size.
+     *   num_blocks >= 1: physical blocks held by k and by v. */
+    fa_kv_layout kv_layout;
+    const int32_t *block_table;
+    int64_t block_size;
+    int64_t max_blocks_per_seq;
+    int64_t num_blocks;
 } fa_params;
 
 /* fa_workspace_size -- phase 1 of fa_fwd (the two-phase shape of the IFA guide,
@@ -127,7 +160,9 @@ fa_status fa_splitkv_plan(const fa_params *p, int num_cus, int64_t chunk_hint,
  * with s_j = scale * q.k_j, natural units.  An empty chunk writes m = -inf,
  * l = 0 and o = 0.  Layouts (float32, contiguous):
  *   o_part [B][Q_N][num_splits][D], m_part and l_part [B][Q_N][num_splits].
- * num_splits * chunk must cover kv_seq; chunk a positive multiple of 64. */
+ * num_splits * chunk must cover kv_seq; chunk a positive multiple of 64
+ * (with a paged cache also at most 1016 * block_size, the block ids of one
+ * chunk being staged on chip; fa_splitkv_plan respects this). */
 fa_status fa_decode_splitkv(const fa_params *p, int64_t num_splits, int64_t chunk,
                             const void *q, const void *k, const void *v,
                             float *o_part, float *m_part, float *l_part, void *stream);

@@ -23,6 +23,8 @@ FA_OK, FA_ERR_NULLPTR, FA_ERR_PARAM_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_RUNTIME 
 FA_BNSD, FA_BSND = 0, 1
 FA_F16, FA_BF16 = 0, 1
 FA_MASK_NONE, FA_MASK_CAUSAL, FA_MASK_BOOL = 0, 1, 2
+FA_KV_CONTIGUOUS, FA_KV_PAGED_BBND, FA_KV_PAGED_BNBD = 0, 1, 2
+KV_LAYOUTS = {"contiguous": FA_KV_CONTIGUOUS, "PA_BBND": FA_KV_PAGED_BBND, "PA_BNBD": FA_KV_PAGED_BNBD}
 
 EXPORTS = ("fa_workspace_size", "fa_fwd", "fa_splitkv_plan", "fa_decode_splitkv", "fa_combine",
            "fa_last_error")
@@ -40,7 +42,10 @@ class FaParams(ctypes.Structure):
                 ("kv_seq", ctypes.c_int64), ("head_dim", ctypes.c_int64),
                 ("layout", ctypes.c_int), ("dtype", ctypes.c_int), ("scale", ctypes.c_double),
                 ("actual_seq_lengths", ctypes.c_void_p), ("mask_mode", ctypes.c_int),
-                ("mask", ctypes.c_void_p), ("mask_stride", ctypes.c_int64 * 4)]
+                ("mask", ctypes.c_void_p), ("mask_stride", ctypes.c_int64 * 4),
+                ("kv_layout", ctypes.c_int), ("block_table", ctypes.c_void_p),
+                ("block_size", ctypes.c_int64), ("max_blocks_per_seq", ctypes.c_int64),
+                ("num_blocks", ctypes.c_int64)]
 
 
 _lock = threading.Lock()
@@ -100,7 +105,8 @@ def _check(st: int):
 
 def make_params(batch, num_heads, q_seq, kv_seq, head_dim, *, num_kv_heads=0, layout="BNSD",
                 dtype="bf16", scale=1.0, actual_seq_lengths=None, mask_mode="none", mask=None,
-                mask_stride: Sequence[int] = (0, 0, 0, 0)) -> FaParams:
+                mask_stride: Sequence[int] = (0, 0, 0, 0), kv_layout="contiguous", block_table=None,
+                block_size=0, max_blocks_per_seq=0, num_blocks=0) -> FaParams:
     p = FaParams()
     p.batch, p.num_heads, p.num_kv_heads = batch, num_heads, num_kv_heads
     p.q_seq, p.kv_seq, p.head_dim = q_seq, kv_seq, head_dim
@@ -113,6 +119,9 @@ def make_params(batch, num_heads, q_seq, kv_seq, head_dim, *, num_kv_heads=0, la
     p.mask = _ptr(mask)
     for i in range(4):
         p.mask_stride[i] = int(mask_stride[i])
+    p.kv_layout = KV_LAYOUTS[kv_layout] if isinstance(kv_layout, str) else kv_layout
+    p.block_table = _ptr(block_table)
+    p.block_size, p.max_blocks_per_seq, p.num_blocks = block_size, max_blocks_per_seq, num_blocks
     return p
 
 
@@ -149,30 +158,45 @@ def fa_combine(params: FaParams, num_splits, o_part, m_part, l_part, out, lse=No
 # ----------------------------------------------------------------- torch conveniences
 
 def params_for(q, k, *, layout="BNSD", num_kv_heads=0, scale=1.0, actual_seq_lengths=None,
-               mask=None, mask_stride=(0, 0, 0, 0), causal=False) -> FaParams:
-    """FaParams from torch tensors q, k in ``layout`` (shapes as in include/fa.h)."""
+               mask=None, mask_stride=(0, 0, 0, 0), causal=False, kv_layout="contiguous",
+               block_table=None) -> FaParams:
+    """FaParams from torch tensors q, k in ``layout`` (shapes as in include/fa.h).
+
+    With a paged ``kv_layout`` k is [num_blocks, block_size, KV_N, D] (PA_BBND) or
+    [num_blocks, KV_N, block_size, D] (PA_BNBD), block_table is int32
+    [B, max_blocks_per_seq], and kv_seq is max_blocks_per_seq * block_size.
+    """
     import torch
     if layout == "BNSD":
         B, N, QS, D = q.shape
-        KVN, KVS = k.shape[1], k.shape[2]
     else:
         B, QS, N, D = q.shape
-        KVS, KVN = k.shape[1], k.shape[2]
+    extra = {}
+    if kv_layout == "contiguous":
+        KVN, KVS = (k.shape[1], k.shape[2]) if layout == "BNSD" else (k.shape[2], k.shape[1])
+    else:
+        nb, bs, KVN = ((k.shape[0], k.shape[1], k.shape[2]) if kv_layout == "PA_BBND"
+                       else (k.shape[0], k.shape[2], k.shape[1]))
+        KVS = block_table.shape[1] * bs
+        extra = dict(kv_layout=kv_layout, block_table=block_table, block_size=bs,
+                     max_blocks_per_seq=block_table.shape[1], num_blocks=nb)
     dtype = {torch.bfloat16: "bf16", torch.float16: "f16"}[q.dtype]
     mode = "bool" if mask is not None else ("causal" if causal else "none")
     return make_params(B, N, QS, KVS, D, num_kv_heads=num_kv_heads or KVN, layout=layout,
                        dtype=dtype, scale=scale, actual_seq_lengths=actual_seq_lengths,
-                       mask_mode=mode, mask=mask, mask_stride=mask_stride)
+                       mask_mode=mode, mask=mask, mask_stride=mask_stride, **extra)
 
 
 def fwd(q, k, v, *, layout="BNSD", scale=None, actual_seq_lengths=None, mask=None,
-        mask_stride=(0, 0, 0, 0), causal=False, return_lse=False, stream=None):
+        mask_stride=(0, 0, 0, 0), causal=False, return_lse=False, stream=None,
+        kv_layout="contiguous", block_table=None):
     """Attention forward on device tensors; allocates out (and lse, workspace) with torch."""
     import torch
     D = q.shape[-1]
     sc = (1.0 / math.sqrt(D)) if scale is None else scale
     p = params_for(q, k, layout=layout, scale=sc, actual_seq_lengths=actual_seq_lengths,
-                   mask=mask, mask_stride=mask_stride, causal=causal)
+                   mask=mask, mask_stride=mask_stride, causal=causal, kv_layout=kv_layout,
+                   block_table=block_table)
     out = torch.empty_like(q)
     lse = (torch.empty((p.batch, p.num_heads, p.q_seq), dtype=torch.float32, device=q.device)
            if return_lse else None)

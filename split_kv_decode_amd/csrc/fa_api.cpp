@@ -6,6 +6,7 @@
 
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -70,6 +71,30 @@ fa_status check_params(const fa_params* p, Shape* s) {
     if (p->mask_mode == FA_MASK_BOOL)
         for (int i = 0; i < 4; ++i)
             if (p->mask_stride[i] < 0) return fail(FA_ERR_PARAM_INVALID, "mask strides must be >= 0");
+    if (p->kv_layout != FA_KV_CONTIGUOUS && p->kv_layout != FA_KV_PAGED_BBND && p->kv_layout != FA_KV_PAGED_BNBD)
+        return fail(FA_ERR_PARAM_INVALID, "unknown kv_layout %d", (int)p->kv_layout);
+    if (p->kv_layout == FA_KV_CONTIGUOUS) {
+        if (p->block_table) return fail(FA_ERR_PARAM_INVALID, "a block_table was passed but kv_layout is contiguous");
+    } else {
+        if (!p->block_table) return fail(FA_ERR_NULLPTR, "a paged kv_layout needs a block_table");
+        if (!p->actual_seq_lengths)
+            return fail(FA_ERR_NULLPTR, "a paged kv_layout needs actual_seq_lengths");
+        if (p->block_size < 16 || p->block_size > 1024 || p->block_size % 16 != 0)
+            return fail(FA_ERR_PARAM_INVALID, "block_size must be a multiple of 16 in [16, 1024], got %lld",
+                        (long long)p->block_size);
+        if (p->max_blocks_per_seq < 1 || p->max_blocks_per_seq >= kMaxDim)
+            return fail(FA_ERR_PARAM_INVALID, "max_blocks_per_seq must be in [1, 2^31), got %lld",
+                        (long long)p->max_blocks_per_seq);
+        if (p->num_blocks < 1 || p->num_blocks >= kMaxDim)
+            return fail(FA_ERR_PARAM_INVALID, "num_blocks must be in [1, 2^31), got %lld", (long long)p->num_blocks);
+        if (p->kv_seq > p->max_blocks_per_seq * p->block_size)
+            return fail(FA_ERR_PARAM_INVALID, "kv_seq (%lld) exceeds max_blocks_per_seq * block_size (%lld)",
+                        (long long)p->kv_seq, (long long)(p->max_blocks_per_seq * p->block_size));
+        if (p->batch * p->max_blocks_per_seq >= kMaxDim)
+            return fail(FA_ERR_PARAM_INVALID, "batch * max_blocks_per_seq must stay below 2^31");
+        if (p->q_seq != 1 || p->mask_mode != FA_MASK_NONE)
+            return fail(FA_ERR_UNSUPPORTED, "a paged KV cache is built for decode only (q_seq == 1, no mask)");
+    }
     s->B = p->batch;
     s->QN = p->num_heads;
     s->KVN = kvn;
@@ -80,7 +105,9 @@ fa_status check_params(const fa_params* p, Shape* s) {
     if (s->B * s->QN > kMaxDim || s->B * kvn > kMaxDim)
         return fail(FA_ERR_PARAM_INVALID, "batch * heads must stay below 2^31");
     const double qe = double(s->B) * double(s->QN) * double(s->QS) * double(s->D);
-    const double ke = double(s->B) * double(s->KVN) * double(s->KVS) * double(s->D);
+    const double ke = p->kv_layout == FA_KV_CONTIGUOUS
+                          ? double(s->B) * double(s->KVN) * double(s->KVS) * double(s->D)
+                          : double(p->num_blocks) * double(p->block_size) * double(s->KVN) * double(s->D);
     if (qe >= double(kMaxElems) || ke >= double(kMaxElems)) return fail(FA_ERR_PARAM_INVALID, "tensor too large");
     return ok();
 }
@@ -131,7 +158,13 @@ Partials partial_bytes(const Shape& s, int64_t splits) {
 constexpr int64_t kMinChunk = 256;
 constexpr int64_t kWgPerCu = 4;
 
-void plan_splits(const Shape& s, int num_cus, int64_t* splits, int64_t* chunk) {
+// Largest chunk of a paged cache: its block ids (at most chunk/block_size + 1)
+// must fit the stage-1 kernel's LDS table.
+int64_t paged_chunk_cap(const fa_params* p) {
+    return p->kv_layout == FA_KV_CONTIGUOUS ? INT64_MAX : (fa::kPagedTableLds - 8) * p->block_size;
+}
+
+void plan_splits(const fa_params* p, const Shape& s, int num_cus, int64_t* splits, int64_t* chunk) {
     const int gh = heads_per_workgroup(s.g);
     const int64_t units = s.B * s.KVN * (s.g / gh);
     const int64_t target = kWgPerCu * int64_t(num_cus > 0 ? num_cus : 256);
@@ -141,6 +174,7 @@ void plan_splits(const Shape& s, int num_cus, int64_t* splits, int64_t* chunk) {
     c = (c + 63) / 64 * 64;
     const int64_t kv_round = (s.KVS + 63) / 64 * 64;
     if (c < kMinChunk) c = kMinChunk < kv_round ? kMinChunk : kv_round;
+    if (c > paged_chunk_cap(p)) c = paged_chunk_cap(p);
     *chunk = c;
     *splits = (s.KVS + c - 1) / c;
 }
@@ -151,7 +185,15 @@ void fill_decode_args(const fa_params* p, const Shape& s, fa::DecodeArgs* a) {
     std::memset(a, 0, sizeof *a);
     a->lens = p->actual_seq_lengths;
     a->kv_seq = s.KVS;
-    if (p->layout == FA_BNSD) {
+    if (p->kv_layout == FA_KV_PAGED_BBND) {
+        a->kv_stride_s = s.KVN * s.D;
+        a->kv_stride_n = s.D;
+        a->kv_stride_blk = p->block_size * s.KVN * s.D;
+    } else if (p->kv_layout == FA_KV_PAGED_BNBD) {
+        a->kv_stride_s = s.D;
+        a->kv_stride_n = p->block_size * s.D;
+        a->kv_stride_blk = s.KVN * p->block_size * s.D;
+    } else if (p->layout == FA_BNSD) {
         a->kv_stride_s = s.D;
         a->kv_stride_n = s.KVS * s.D;
         a->kv_stride_b = s.KVN * s.KVS * s.D;
@@ -159,6 +201,12 @@ void fill_decode_args(const fa_params* p, const Shape& s, fa::DecodeArgs* a) {
         a->kv_stride_s = s.KVN * s.D;
         a->kv_stride_n = s.D;
         a->kv_stride_b = s.KVS * s.KVN * s.D;
+    }
+    if (p->kv_layout != FA_KV_CONTIGUOUS) {
+        a->block_table = p->block_table;
+        a->block_size = (int32_t)p->block_size;
+        a->max_blocks = (int32_t)p->max_blocks_per_seq;
+        a->num_blocks = (int32_t)p->num_blocks;
     }
     a->num_heads = (int32_t)s.QN;
     a->num_kv_heads = (int32_t)s.KVN;
@@ -274,12 +322,15 @@ fa_status fa_splitkv_plan(const fa_params* p, int num_cus, int64_t chunk_hint, i
     if (chunk_hint < 0 || chunk_hint % 64 != 0)
         return fail(FA_ERR_PARAM_INVALID, "chunk_hint must be 0 or a positive multiple of 64, got %lld",
                     (long long)chunk_hint);
+    if (chunk_hint > paged_chunk_cap(p))
+        return fail(FA_ERR_PARAM_INVALID, "chunk_hint %lld exceeds %lld tokens (1016 blocks of the paged cache)",
+                    (long long)chunk_hint, (long long)paged_chunk_cap(p));
     int64_t sp, c;
     if (chunk_hint > 0) {
         c = chunk_hint;
         sp = (s.KVS + c - 1) / c;
     } else {
-        plan_splits(s, num_cus > 0 ? num_cus : device_cus(), &sp, &c);
+        plan_splits(p, s, num_cus > 0 ? num_cus : device_cus(), &sp, &c);
     }
     if (sp > kMaxSplits) return fail(FA_ERR_PARAM_INVALID, "plan needs %lld splits (max %lld)", (long long)sp, (long long)kMaxSplits);
     *num_splits = sp;
@@ -296,7 +347,7 @@ fa_status fa_workspace_size(const fa_params* p, size_t* bytes) {
     *bytes = 0;
     if (!decode_path(p)) return ok();
     int64_t sp, c;
-    plan_splits(s, device_cus(), &sp, &c);
+    plan_splits(p, s, device_cus(), &sp, &c);
     if (sp > 1) *bytes = partial_bytes(s, sp).total;
     return ok();
 }
@@ -312,7 +363,7 @@ fa_status fa_fwd(const fa_params* p, const void* q, const void* k, const void* v
     if (!decode_path(p)) return run_prefill(p, s, q, k, v, out, lse, hs);
 
     int64_t sp, c;
-    plan_splits(s, device_cus(), &sp, &c);
+    plan_splits(p, s, device_cus(), &sp, &c);
     if (sp > kMaxSplits) return fail(FA_ERR_PARAM_INVALID, "plan needs too many splits");
     if (sp == 1) return run_stage1(p, s, 1, c, q, k, v, nullptr, nullptr, nullptr, out, lse, hs);
     const Partials pb = partial_bytes(s, sp);
@@ -344,6 +395,9 @@ fa_status fa_decode_splitkv(const fa_params* p, int64_t num_splits, int64_t chun
         return fail(FA_ERR_PARAM_INVALID, "partials must be 4-byte aligned");
     if (num_splits < 1 || num_splits > kMaxSplits) return fail(FA_ERR_PARAM_INVALID, "num_splits must be in [1, 2^20]");
     if (chunk < 64 || chunk % 64 != 0) return fail(FA_ERR_PARAM_INVALID, "chunk must be a positive multiple of 64");
+    if (chunk > paged_chunk_cap(p))
+        return fail(FA_ERR_PARAM_INVALID, "chunk %lld exceeds %lld tokens (1016 blocks of the paged cache)",
+                    (long long)chunk, (long long)paged_chunk_cap(p));
     if (num_splits * chunk < s.KVS)
         return fail(FA_ERR_PARAM_INVALID, "num_splits * chunk (%lld) must cover kv_seq (%lld)",
                     (long long)(num_splits * chunk), (long long)s.KVS);

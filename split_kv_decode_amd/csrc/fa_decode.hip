@@ -10,19 +10,25 @@
 // Decode reads every cached K/V byte once and does ~2 FMAs per byte, so it is
 // bound by HBM bandwidth.  The kernel is laid out for that: D/8 lanes cover one
 // 16-byte-per-lane KV row, so one wave load instruction reads 4 (D=128) or
-// 8 (D=64) whole rows = 1 KiB contiguous in the BNSD layout; the next
-// iteration's K and V are in flight while the current rows are consumed; the
+// 8 (D=64) whole rows = 1 KiB contiguous in the BNSD layout; the K and V of
+// the next two iterations are in flight while the current rows are consumed; the
 // dot product is reduced across the row's lanes with DPP moves.  Each lane
 // group (the lanes of one row slot) keeps its own running max / sum / output,
 // so the streaming loop has no cross-group traffic; groups and waves are
 // merged once at the end.  The g query heads that share a KV head (GQA) are
 // processed by the same workgroup so their K/V rows are read once.
+//
+// With a paged cache (FlashAttn developer guide 1.2, PagedAttention) the
+// workgroup first stages the physical block ids of its chunk in LDS; every lane
+// then follows its row slots block by block with an incrementally advanced
+// (block, row) cursor, so the streaming loop adds one LDS read and one address
+// multiply per row and no division.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
 namespace fa {
 
-template <typename ST, int D, int GH, bool FINISH>
+template <typename ST, int D, int GH, bool FINISH, bool PAGED>
 __global__ __launch_bounds__(256) void decode_stage1_kernel(DecodeArgs a) {
     constexpr int LPR = D / 8;     // lanes per KV row
     constexpr int RPL = 64 / LPR;  // rows per wave load
@@ -78,32 +84,73 @@ __global__ __launch_bounds__(256) void decode_stage1_kernel(DecodeArgs a) {
         for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
     }
 
-    const int64_t head_off = b * a.kv_stride_b + (int64_t)n2 * a.kv_stride_n + sub * 8;
+    const int64_t head_off = (PAGED ? 0 : b * a.kv_stride_b) + (int64_t)n2 * a.kv_stride_n + sub * 8;
     const uint16_t* kb = a.k + head_off;
     const uint16_t* vb = a.v + head_off;
     const int64_t ss = a.kv_stride_s;
 
-    auto load = [&](int64_t t0, u32x4* kw, u32x4* vw) {
+    // Paged cache: block ids of the chunk's logical blocks [cb, cb + nblk),
+    // clamped into the physical range, and per-slot (block, row) cursors that
+    // follow the positions load() is called with (t0 + k*NW*TW, k = 0, 1, ...).
+    __shared__ int32_t s_blk[PAGED ? kPagedTableLds : 1];
+    int pb[U], pr[U];
+    int step_q = 0, step_r = 0;
+    if constexpr (PAGED) {
+        const int bs = a.block_size;
+        const int64_t cb = c0 / bs;
+        const int64_t nblk = (c1 > c0) ? (c1 - 1) / bs - cb + 1 : 0;
+        const int32_t* tb = a.block_table + b * a.max_blocks + cb;
+        for (int i = threadIdx.x; i < nblk; i += 256) {
+            int32_t id = tb[i];
+            id = id < 0 ? 0 : (id >= a.num_blocks ? a.num_blocks - 1 : id);
+            s_blk[i] = id;
+        }
+        __syncthreads();
+        const int rel0 = (int)(c0 - cb * bs) + wave * TW + grp;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            pb[u] = (rel0 + u * RPL) / bs;
+            pr[u] = (rel0 + u * RPL) % bs;
+        }
+        step_q = (NW * TW) / bs;
+        step_r = (NW * TW) % bs;
+    }
+
+    auto load = [&](int64_t t0, u32x4* kw, u32x4* vw) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t t = t0 + u * RPL + grp;
             if (t < c1) {
-                kw[u] = ld128(kb + t * ss);
-                vw[u] = ld128(vb + t * ss);
+                int64_t off;
+                if constexpr (PAGED)
+                    off = (int64_t)s_blk[pb[u]] * a.kv_stride_blk + (int64_t)pr[u] * ss;
+                else
+                    off = t * ss;
+                kw[u] = ld128(kb + off);
+                vw[u] = ld128(vb + off);
             } else {
                 kw[u] = u32x4{0u, 0u, 0u, 0u};
                 vw[u] = u32x4{0u, 0u, 0u, 0u};
+            }
+            if constexpr (PAGED) {
+                pb[u] += step_q;
+                pr[u] += step_r;
+                if (pr[u] >= a.block_size) {
+                    pr[u] -= a.block_size;
+                    pb[u] += 1;
+                }
             }
         }
     };
 
     int64_t t0 = c0 + (int64_t)wave * TW;
-    u32x4 kw[U], vw[U];
+    u32x4 kw[U], vw[U], kn[U], vn[U];
     load(t0, kw, vw);
+    load(t0 + NW * TW, kn, vn);
     while (t0 < c1) {
         const int64_t tn = t0 + NW * TW;
-        u32x4 kn[U], vn[U];
-        load(tn, kn, vn);
+        u32x4 kn2[U], vn2[U];
+        load(tn + NW * TW, kn2, vn2);
 
         float kf[U][8], vf[U][8];
 #pragma unroll
@@ -148,6 +195,8 @@ __global__ __launch_bounds__(256) void decode_stage1_kernel(DecodeArgs a) {
         for (int u = 0; u < U; ++u) {
             kw[u] = kn[u];
             vw[u] = vn[u];
+            kn[u] = kn2[u];
+            vn[u] = vn2[u];
         }
     }
 
@@ -321,13 +370,19 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     }
 }
 
+template <typename ST, int D, int GH, bool PAGED>
+static hipError_t dispatch_stage1_fin(const DecodeArgs& a, bool finish, int64_t blocks, hipStream_t s) {
+    if (finish)
+        hipLaunchKernelGGL((decode_stage1_kernel<ST, D, GH, true, PAGED>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((decode_stage1_kernel<ST, D, GH, false, PAGED>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
 template <typename ST, int D, int GH>
 static hipError_t dispatch_stage1(const DecodeArgs& a, bool finish, int64_t blocks, hipStream_t s) {
-    if (finish)
-        hipLaunchKernelGGL((decode_stage1_kernel<ST, D, GH, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((decode_stage1_kernel<ST, D, GH, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-    return hipGetLastError();
+    if (a.block_table) return dispatch_stage1_fin<ST, D, GH, true>(a, finish, blocks, s);
+    return dispatch_stage1_fin<ST, D, GH, false>(a, finish, blocks, s);
 }
 
 template <typename ST, int D>

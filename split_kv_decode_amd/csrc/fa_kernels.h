@@ -22,7 +22,15 @@ struct DecodeArgs {
     int64_t chunk;            // tokens per split (multiple of 64)
     int64_t kv_stride_s;      // elements between consecutive tokens of one head
     int64_t kv_stride_n;      // elements between KV heads
-    int64_t kv_stride_b;      // elements between batches
+    int64_t kv_stride_b;      // elements between batches (contiguous cache)
+    // Paged cache (block_table non-null): token j of batch b is row j % block_size
+    // of physical block block_table[b * max_blocks + j / block_size]; kv_stride_s
+    // and kv_stride_n then step inside a block, kv_stride_blk between blocks.
+    const int32_t* block_table;
+    int64_t kv_stride_blk;
+    int32_t block_size;
+    int32_t max_blocks;
+    int32_t num_blocks;
     int32_t num_splits;
     int32_t num_heads;        // Q_N
     int32_t num_kv_heads;     // KV_N
@@ -58,6 +66,10 @@ struct PrefillArgs {
     int32_t negate_q;         // 1 when scale < 0: q's sign is flipped, scale_log2 = |scale|*log2(e)
     float scale_log2;
 };
+
+// Block ids one paged stage-1 workgroup stages in LDS: a chunk may touch at most
+// this many blocks.
+constexpr int kPagedTableLds = 1024;
 
 // Launchers: return hipSuccess or the launch error.  dtype: 0 = fp16, 1 = bf16.
 hipError_t launch_decode_stage1(const DecodeArgs& a, int dtype, int head_dim, int heads_per_wg,

@@ -117,3 +117,48 @@ def test_split_plan_honours_chunk_hint(lib):
 def test_prefill_needs_no_workspace(lib):
     assert fa.fa_workspace_size(params(q_seq=128)) == 0
     assert fa.fa_workspace_size(params(q_seq=1, mask_mode="causal")) == 0
+
+
+# ---------------------------------------------------------------- paged KV cache
+
+def paged(**kw):
+    base = dict(kv_layout="PA_BBND", block_table=FAKE, block_size=128, max_blocks_per_seq=1024,
+                num_blocks=1024, actual_seq_lengths=FAKE)
+    base.update(kw)
+    return params(**base)
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(kv_layout=9), fa.FA_ERR_PARAM_INVALID, "kv_layout"),
+    (dict(block_table=None), fa.FA_ERR_NULLPTR, "block_table"),
+    (dict(actual_seq_lengths=None), fa.FA_ERR_NULLPTR, "actual_seq_lengths"),
+    (dict(block_size=8), fa.FA_ERR_PARAM_INVALID, "block_size"),
+    (dict(block_size=40), fa.FA_ERR_PARAM_INVALID, "block_size"),
+    (dict(block_size=2048), fa.FA_ERR_PARAM_INVALID, "block_size"),
+    (dict(max_blocks_per_seq=0), fa.FA_ERR_PARAM_INVALID, "max_blocks_per_seq"),
+    (dict(num_blocks=0), fa.FA_ERR_PARAM_INVALID, "num_blocks"),
+    (dict(max_blocks_per_seq=1023), fa.FA_ERR_PARAM_INVALID, "exceeds"),    # 1023*128 < 131072
+    (dict(q_seq=16), fa.FA_ERR_UNSUPPORTED, "decode only"),
+    (dict(mask_mode="causal"), fa.FA_ERR_UNSUPPORTED, "decode only"),
+    (dict(kv_layout="contiguous"), fa.FA_ERR_PARAM_INVALID, "contiguous"),  # table without paging
+])
+def test_paged_params_validated(lib, kw, status, text):
+    p = paged(**kw)
+    st = lib.fa_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None)
+    assert st == status
+    assert text in fa.fa_last_error()
+
+
+def test_paged_plan_caps_chunk_to_the_lds_table(lib):
+    # 64 batches x 16 KV heads fill the chip without splitting, so the contiguous
+    # plan takes the whole cache as one chunk; with 16-token blocks a chunk may
+    # span at most 1016 blocks.
+    kw = dict(batch=64, num_heads=16, kv_seq=40000)
+    assert fa.fa_splitkv_plan(params(**kw), num_cus=256)[:2] == (1, 40000)
+    sp, ch, _ = fa.fa_splitkv_plan(paged(block_size=16, max_blocks_per_seq=2500, **kw), num_cus=256)
+    assert (sp, ch) == (3, 1016 * 16)
+    p = paged(block_size=16, max_blocks_per_seq=2500, **kw)
+    with pytest.raises(fa.FaError, match="exceeds"):
+        fa.fa_splitkv_plan(p, num_cus=256, chunk_hint=1024 * 16)
+    st = lib.fa_decode_splitkv(ctypes.byref(p), 2, 1024 * 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == fa.FA_ERR_PARAM_INVALID and "exceeds" in fa.fa_last_error()

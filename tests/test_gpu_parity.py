@@ -201,6 +201,113 @@ def test_combine_alone_matches_oracle_merge():
     check(got, to_np(lse), ref, ref_lse, "combine")
 
 
+# ------------------------------------------------------------------ paged KV cache (decode)
+
+def _paged_params(inp, kv_layout, table, bs, nb, lens_t):
+    s = inp.spec
+    return fa.make_params(s.B, s.QN, 1, s.KVS, s.D, num_kv_heads=s.KVN, layout=s.layout,
+                          dtype=s.dtype, scale=s.softmax_scale, actual_seq_lengths=lens_t,
+                          kv_layout=kv_layout, block_table=table, block_size=bs,
+                          max_blocks_per_seq=table.shape[1], num_blocks=nb)
+
+
+def run_paged(inp, kv_layout, bs, seed=0, table_tail=None):
+    """fa_fwd on the paged copy of inp's cache (spare blocks and padding hold NaN).
+
+    table_tail: value written into the block-table entries past each batch's last
+    used block (they must never be read)."""
+    s = inp.spec
+    kp, vp, table, nb = fa_synth.to_paged(inp, bs, kv_layout, seed=seed)
+    if table_tail is not None:
+        for b in range(s.B):
+            table[b, -(-int(inp.lens[b]) // bs):] = table_tail
+    q, k, v = dev16(inp.q, s.dtype), dev16(kp, s.dtype), dev16(vp, s.dtype)
+    lens_t = torch.from_numpy(inp.lens).to(DEV)
+    tab_t = torch.from_numpy(table).to(DEV)
+    p = _paged_params(inp, kv_layout, tab_t, bs, nb, lens_t)
+    out = torch.empty_like(q)
+    lse = torch.empty((s.B, s.QN, 1), dtype=torch.float32, device=DEV)
+    nbytes = fa.fa_workspace_size(p)
+    ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=DEV)
+    fa.fa_fwd(p, q, k, v, out, lse, ws, nbytes, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    return out, lse, table
+
+
+PAGED_CASES = [
+    dict(kv_layout="PA_BBND", bs=16, B=3, QN=8, KVN=2, KVS=1000, D=128, layout="BSND", lens=(0, 1000)),
+    dict(kv_layout="PA_BNBD", bs=128, B=2, QN=32, KVN=8, KVS=4096, D=128, lens=(1, 4096)),
+    dict(kv_layout="PA_BBND", bs=48, B=4, QN=16, KVN=2, KVS=700, D=64, dtype="f16", std=0.5,
+         lens=(1, 700)),
+    dict(kv_layout="PA_BNBD", bs=1024, B=1, QN=4, KVN=4, KVS=20000, D=128, lens=(19000, 20000)),
+    dict(kv_layout="PA_BNBD", bs=16, B=2, QN=6, KVN=2, KVS=333, D=128, layout="BSND", lens=(1, 333)),
+]
+
+
+@pytest.mark.parametrize("case", PAGED_CASES, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_paged_decode_matches_oracle_and_contiguous(case):
+    case = dict(case)
+    kv_layout, bs = case.pop("kv_layout"), case.pop("bs")
+    inp = fa_synth.make(spec(seed=71, **case))
+    out, lse, table = run_paged(inp, kv_layout, bs, seed=5)
+    s = inp.spec
+    kp, vp, _, _ = fa_synth.to_paged(inp, bs, kv_layout, seed=5)
+    prob = oracle.Problem(s.B, s.QN, s.KVN, 1, s.KVS, s.D, s.layout, s.dtype, s.softmax_scale,
+                          inp.lens, "none", kv_layout=kv_layout, block_table=table, block_size=bs)
+    ref, ref_lse = oracle.attention(prob, inp.q, kp, vp)
+    r_rows = np.ascontiguousarray(ref if s.layout == "BNSD" else ref.transpose(0, 2, 1, 3))
+    check(rows_of(out, s, np.arange(s.B * s.QN)), to_np(lse).reshape(-1),
+          r_rows.reshape(-1, s.D), ref_lse.reshape(-1), f"paged {case}")
+    # Same split plan and the same per-token arithmetic as the contiguous cache.
+    c_out, c_lse = run_fwd(inp)
+    assert torch.equal(out, c_out)
+    assert torch.equal(lse.reshape(-1), c_lse.reshape(-1))
+
+
+def test_paged_decode_never_reads_unused_table_entries():
+    inp = fa_synth.make(spec(layout="BNSD", B=4, QN=8, KVN=2, KVS=900, lens=(0, 900), seed=72))
+    base, base_lse, _ = run_paged(inp, "PA_BBND", 32, seed=6)
+    for tail in (-1, 1 << 30):
+        out, lse, _ = run_paged(inp, "PA_BBND", 32, seed=6, table_tail=tail)
+        assert torch.equal(out, base) and torch.equal(torch.isinf(lse), torch.isinf(base_lse))
+
+
+@pytest.mark.parametrize("bs,chunk,splits", [(48, 64, 19), (16, 16256, 2), (64, 320, 63)])
+def test_paged_stage1_partials(bs, chunk, splits):
+    """Chunks that cut blocks (48 vs 64), a chunk whose 1016 block ids fill the LDS
+    table, and a chunk that is a multiple of the block size."""
+    KVS = 20000 if chunk == 16256 else 900
+    inp = fa_synth.make(spec(layout="BSND", B=2, QN=4, KVN=2, KVS=KVS,
+                             lens=(KVS // 2, KVS), seed=73))
+    if splits * chunk < KVS:
+        splits = -(-KVS // chunk)
+    s = inp.spec
+    kp, vp, table, nb = fa_synth.to_paged(inp, bs, "PA_BNBD", seed=8)
+    q, k, v = dev16(inp.q, s.dtype), dev16(kp, s.dtype), dev16(vp, s.dtype)
+    lens_t = torch.from_numpy(inp.lens).to(DEV)
+    tab_t = torch.from_numpy(table).to(DEV)
+    p = _paged_params(inp, "PA_BNBD", tab_t, bs, nb, lens_t)
+    rows = s.B * s.QN
+    o = torch.full((rows * splits * s.D,), float("nan"), device=DEV)
+    m = torch.full((rows * splits,), float("nan"), device=DEV)
+    l = torch.full((rows * splits,), float("nan"), device=DEV)
+    fa.fa_decode_splitkv(p, splits, chunk, q, k, v, o, m, l, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    prob = oracle.Problem(s.B, s.QN, s.KVN, 1, s.KVS, s.D, s.layout, s.dtype, s.softmax_scale,
+                          inp.lens, "none", kv_layout="PA_BNBD", block_table=table, block_size=bs)
+    ro, rm, rl = oracle.split_partials(prob, inp.q, kp, vp, splits, chunk)
+    go, gm, gl = (to_np(x) for x in (o.view(rows, splits, s.D), m.view(rows, splits),
+                                     l.view(rows, splits)))
+    empty = np.isinf(rm)
+    assert np.array_equal(np.isinf(gm) & (gm < 0), empty)
+    assert np.all(gl[empty] == 0.0) and np.all(go[empty] == 0.0)
+    live = ~empty
+    assert np.abs(gm[live] - rm[live]).max() <= 1e-3
+    assert np.all(np.abs(gl[live] - rl[live]) <= 2e-3 * rl[live])
+    tol = 2e-3 * np.abs(ro).max(axis=2, keepdims=True) + 1e-6
+    assert np.all((np.abs(go - ro) <= tol)[live])
+
+
 # ------------------------------------------------------------------ prefill
 
 PREFILL_CASES = [

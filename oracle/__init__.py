@@ -48,7 +48,8 @@ class _Problem(ctypes.Structure):
                 ("mask_stride", ctypes.c_int64 * 4),
                 ("kv_layout", ctypes.c_int32),
                 ("block_table", ctypes.POINTER(ctypes.c_int32)),
-                ("block_size", ctypes.c_int64), ("max_blocks", ctypes.c_int64)]
+                ("block_size", ctypes.c_int64), ("max_blocks", ctypes.c_int64),
+                ("win_left", ctypes.c_int64), ("win_right", ctypes.c_int64)]
 
 
 def _load():
@@ -58,8 +59,8 @@ def _load():
             if _LIB_OVERRIDE:
                 lib = ctypes.CDLL(_LIB_OVERRIDE)
             else:
-                if not os.path.exists(_LIB):
-                    build(force=False)
+                if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                    build(force=True)  # missing or older than its source
                 lib = ctypes.CDLL(_LIB)
             P = ctypes.POINTER
             u16p, f64p, i64p = P(ctypes.c_uint16), P(ctypes.c_double), P(ctypes.c_int64)
@@ -92,7 +93,7 @@ class Problem:
 
     def __init__(self, B, QN, KVN, QS, KVS, D, layout="BNSD", dtype="bf16", scale=1.0,
                  lens=None, mask_mode="none", mask=None, mask_strides=(0, 0, 0, 0),
-                 kv_layout="contiguous", block_table=None, block_size=0):
+                 kv_layout="contiguous", block_table=None, block_size=0, window=(-1, -1)):
         self.B, self.QN, self.KVN, self.QS, self.KVS, self.D = B, QN, KVN, QS, KVS, D
         self.layout, self.dtype, self.scale = layout, dtype, float(scale)
         self.lens = None if lens is None else np.ascontiguousarray(lens, dtype=np.int64)
@@ -103,6 +104,7 @@ class Problem:
         self.block_table = (None if block_table is None
                             else np.ascontiguousarray(block_table, dtype=np.int32))
         self.block_size = int(block_size)
+        self.window = (int(window[0]), int(window[1]))  # mask_mode "window": (win_left, win_right)
 
     @classmethod
     def from_inputs(cls, inp, mask_mode: Optional[str] = None):
@@ -120,7 +122,8 @@ class Problem:
         p.dtype = 1 if self.dtype == "bf16" else 0
         p.scale = self.scale
         p.lens = _ptr(self.lens, ctypes.c_int64)
-        p.mask_mode = {"none": 0, "causal": 1, "bool": 2}[self.mask_mode]
+        p.mask_mode = {"none": 0, "causal": 1, "bool": 2, "window": 3}[self.mask_mode]
+        p.win_left, p.win_right = self.window
         p.mask = _ptr(self.mask, ctypes.c_uint8)
         for i in range(4):
             p.mask_stride[i] = self.mask_strides[i]

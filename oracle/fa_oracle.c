@@ -28,6 +28,9 @@
  *   - orc_merge: the FD reduction m = max_c m_c, l = sum_c l_c exp(m_c - m),
  *     o = sum_c O_c exp(m_c - m) / l, lse = log l + m (FlashAttn developer
  *     guide 10, FD block formula; FlashDecoding tutorial section 2).
+ *   - Window mask (developer guide 1.5, mask mode 4): query row i keeps the
+ *     band of keys i - win_left <= j <= i + win_right; a negative bound is
+ *     unbounded on that side (the guide sets both to -1 when no window is used).
  *   - Paged KV caches (FlashAttn developer guide 1.2): token j of batch b is
  *     row j % block_size of physical block block_table[b][j / block_size];
  *     PA_BBND blocks are [block_size][KV_N][D], PA_BNBD blocks [KV_N][block_size][D].
@@ -47,12 +50,13 @@ typedef struct {
     int32_t dtype;              /* 0 = fp16, 1 = bf16 storage */
     double scale;
     const int64_t *lens;        /* [B] actual KV lengths, or NULL (= KV_S) */
-    int32_t mask_mode;          /* 0 none, 1 causal (j > i excluded), 2 boolean tensor */
+    int32_t mask_mode;          /* 0 none, 1 causal (j > i excluded), 2 boolean tensor, 3 window */
     const uint8_t *mask;        /* mode 2: nonzero = excluded */
     int64_t mask_stride[4];     /* element strides for (b, n1, i, j); 0 broadcasts */
     int32_t kv_layout;          /* 0 = as layout, 1 = paged BBND, 2 = paged BNBD */
     const int32_t *block_table; /* [B][max_blocks] physical block ids */
     int64_t block_size, max_blocks;
+    int64_t win_left, win_right; /* mode 3: keys i - win_left .. i + win_right; < 0 unbounded */
 } orc_problem;
 
 static double dec16(int32_t dtype, uint16_t h)
@@ -104,6 +108,10 @@ static int64_t row_length(const orc_problem *p, int64_t b)
 static int key_valid(const orc_problem *p, int64_t b, int64_t n1, int64_t i, int64_t j)
 {
     if (p->mask_mode == 1 && j > i) return 0;
+    if (p->mask_mode == 3) {
+        if (p->win_left >= 0 && j < i - p->win_left) return 0;
+        if (p->win_right >= 0 && j > i + p->win_right) return 0;
+    }
     if (p->mask_mode == 2) {
         const int64_t *st = p->mask_stride;
         if (p->mask[b * st[0] + n1 * st[1] + i * st[2] + j * st[3]] != 0) return 0;

@@ -32,6 +32,10 @@ MUTANTS = [
     ("value_row_offset", "const uint16_t *vr = v + kv_index(p, b, n2, j);",
      "const uint16_t *vr = v + kv_index(p, b, n2, j > 0 ? j - 1 : 0);"),
     ("bf16_decode_shift", "uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h << 15;"),
+    ("window_left_bound", "if (p->win_left >= 0 && j < i - p->win_left) return 0;",
+     "if (p->win_left >= 0 && j <= i - p->win_left) return 0;"),
+    ("window_right_sign", "if (p->win_right >= 0 && j > i + p->win_right) return 0;",
+     "if (p->win_right >= 0 && j > i - p->win_right) return 0;"),
     ("paged_row_offset", "const int64_t r = j % p->block_size;", "const int64_t r = (j + 1) % p->block_size;"),
     ("paged_bnbd_order", ": ((blk * p->KVN + n) * p->block_size + r) * p->D;",
      ": ((blk * p->block_size + r) * p->KVN + n) * p->D;"),

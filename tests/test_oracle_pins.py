@@ -385,3 +385,68 @@ def test_paged_block_gather_by_hand():
                         kv_layout="PA_BBND", block_table=table, block_size=1)
     out, _ = oracle.attention(pp, np.zeros_like(inp.q), kp, vp)
     assert np.allclose(out[0, 0, 0], dec(inp.v, "bf16")[0, 0].mean(axis=0), atol=1e-14)
+
+
+# ---------------------------------------------------------------- window mask
+
+def _band(QS, KVS, wl, wr):
+    """Keep-matrix of the window band built from numpy's triangle routines."""
+    keep = np.ones((QS, KVS), dtype=bool)
+    if wr >= 0:
+        keep &= np.tril(np.ones((QS, KVS), dtype=bool), k=wr)
+    if wl >= 0:
+        keep &= np.triu(np.ones((QS, KVS), dtype=bool), k=-wl)
+    return keep
+
+
+@pytest.mark.parametrize("wl,wr", [(3, 0), (0, 2), (5, 7), (-1, 4), (6, -1), (0, 0), (40, 40)])
+@pytest.mark.parametrize("layout", ["BNSD", "BSND"])
+def test_window_equals_band_bool_mask(wl, wr, layout):
+    """Window mode (FlashAttn guide 1.5, mode 4) against the same band given as a boolean
+    tensor, through the whole-matrix brute force (a separate route)."""
+    inp = tiny(layout=layout, B=2, QN=4, KVN=2, QS=21, KVS=26, D=16, lens=(9, 26), seed=81)
+    s = inp.spec
+    pw = oracle.Problem(s.B, s.QN, s.KVN, s.QS, s.KVS, s.D, layout, "bf16", s.softmax_scale,
+                        inp.lens, "window", window=(wl, wr))
+    mask = (~_band(s.QS, s.KVS, wl, wr)).astype(np.uint8)
+    pb = oracle.Problem(s.B, s.QN, s.KVN, s.QS, s.KVS, s.D, layout, "bf16", s.softmax_scale,
+                        inp.lens, "bool", mask, (0, 0, s.KVS, 1))
+    o1, l1 = oracle.attention(pw, inp.q, inp.k, inp.v)
+    o2, l2 = brute.attention(pb, inp.q, inp.k, inp.v)
+    assert np.array_equal(np.isinf(l1), np.isinf(l2))
+    fin = np.isfinite(l1)
+    assert np.allclose(l1[fin], l2[fin], rtol=1e-12, atol=1e-12)
+    assert np.allclose(o1, o2, rtol=1e-12, atol=1e-12)
+
+
+def test_window_special_cases():
+    """(-1, 0) is the causal mask, (-1, -1) no mask, (0, 0) the diagonal alone:
+    out_i = v_i and lse_i = scale * q_i . k_i in closed form."""
+    inp = tiny(layout="BNSD", B=1, QN=2, KVN=1, QS=12, KVS=12, D=16, seed=82)
+    s = inp.spec
+    mk = lambda mode, w=(-1, -1): oracle.Problem(1, 2, 1, 12, 12, 16, "BNSD", "bf16",
+                                                 s.softmax_scale, None, mode, window=w)
+    oc, lc = oracle.attention(mk("causal"), inp.q, inp.k, inp.v)
+    ow, lw = oracle.attention(mk("window", (-1, 0)), inp.q, inp.k, inp.v)
+    assert np.array_equal(oc, ow) and np.array_equal(lc, lw)
+    on, ln_ = oracle.attention(mk("none"), inp.q, inp.k, inp.v)
+    ow, lw = oracle.attention(mk("window", (-1, -1)), inp.q, inp.k, inp.v)
+    assert np.array_equal(on, ow) and np.array_equal(ln_, lw)
+    od, ld = oracle.attention(mk("window", (0, 0)), inp.q, inp.k, inp.v)
+    Q, K, V = (dec(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    for n1 in range(2):
+        assert np.array_equal(od[0, n1], V[0, 0])
+        assert np.allclose(ld[0, n1], s.softmax_scale * np.einsum("id,id->i", Q[0, n1], K[0, 0]),
+                           atol=1e-13)
+
+
+def test_window_sdpa_pin():
+    """Window band as an attention mask of torch's float64 SDPA (a library routine)."""
+    inp = tiny(layout="BNSD", B=1, QN=3, KVN=3, QS=30, KVS=30, D=16, scale=0.3, seed=83)
+    s = inp.spec
+    keep = _band(30, 30, 4, 2)
+    Q, K, V = (dec(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    ref = _sdpa(Q, K, V, 0.3, 1, attn_mask=keep)
+    p = oracle.Problem(1, 3, 3, 30, 30, 16, "BNSD", "bf16", 0.3, None, "window", window=(4, 2))
+    out, _ = oracle.attention(p, inp.q, inp.k, inp.v)
+    assert np.allclose(out, ref, rtol=1e-10, atol=1e-10)

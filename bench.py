@@ -239,7 +239,8 @@ def extra_workloads(fa, fa_synth, np, torch, dev16, stream, warmup=3, iters=10):
     cases = [("prefill_small", None, None), ("decode_gqa", None, None),
              ("decode_gqa", None, ("PA_BBND", 128)), ("decode_128k", None, ("PA_BNBD", 128)),
              ("prefill_causal", "bool", None), ("prefill_causal", "causal", None),
-             ("prefill_gqa_long", None, None)]
+             ("prefill_4k", "window", None), ("prefill_gqa_long", None, None)]
+    window = (1024, 0)  # sliding window of the last 1025 keys
     for name, mode, paging in cases:
         inp = fa_synth.make(fa_synth.WORKLOADS[name])
         s = inp.spec
@@ -258,7 +259,8 @@ def extra_workloads(fa, fa_synth, np, torch, dev16, stream, warmup=3, iters=10):
         mask = torch.from_numpy(inp.mask).to(q.device) if m == "bool" else None
         if paging is None:
             p = fa.params_for(q, k, layout=s.layout, scale=s.softmax_scale, actual_seq_lengths=lens,
-                              mask=mask, mask_stride=inp.mask_strides, causal=(m == "causal"))
+                              mask=mask, mask_stride=inp.mask_strides, causal=(m == "causal"),
+                              window=window if m == "window" else None)
         else:
             p = fa.make_params(s.B, s.QN, 1, s.KVS, s.D, num_kv_heads=s.KVN, layout=s.layout,
                                dtype=s.dtype, scale=s.softmax_scale, actual_seq_lengths=lens,
@@ -279,6 +281,8 @@ def extra_workloads(fa, fa_synth, np, torch, dev16, stream, warmup=3, iters=10):
         torch.cuda.synchronize()
         ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
         key = name if mode is None else f"{name}_{mode}"
+        if mode == "window":
+            key = f"{name}_window{window[0]}_{window[1]}"
         if paging is not None:
             key = f"{name}_paged_{paging[0]}_bs{paging[1]}"
         if s.QS == 1:
@@ -292,6 +296,12 @@ def extra_workloads(fa, fa_synth, np, torch, dev16, stream, warmup=3, iters=10):
             S = s.QS
             if m == "none" and inp.lens is None:
                 fl = 4.0 * s.B * s.QN * S * s.KVS * s.D
+            elif m == "window":  # row i sees keys max(0, i - wl) .. min(L - 1, i + wr)
+                L = np.full(s.B, s.KVS) if inp.lens is None else np.clip(inp.lens, 0, s.KVS)
+                i = np.arange(S, dtype=np.float64)
+                pairs = sum(np.clip(np.minimum(Lb - 1, i + window[1]) - np.maximum(0, i - window[0]) + 1,
+                                    0, None).sum() for Lb in L)
+                fl = 4.0 * s.QN * s.D * float(pairs)
             else:
                 L = np.full(s.B, s.KVS) if inp.lens is None else np.clip(inp.lens, 0, s.KVS).astype(np.float64)
                 if m == "none":

@@ -61,12 +61,13 @@ typedef enum {
 typedef enum { FA_BNSD = 0, FA_BSND = 1 } fa_layout;
 typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
 
-/* Mask modes (developer guide 1.5: 0 = none, 3 = causal; IFA guide 4 and 8.1:
- * a boolean attenMask whose true entries are excluded). */
+/* Mask modes (developer guide 1.5: 0 = none, 3 = causal, 4 = window; IFA
+ * guide 4 and 8.1: a boolean attenMask whose true entries are excluded). */
 typedef enum {
     FA_MASK_NONE = 0,
     FA_MASK_CAUSAL = 1,  /* key j > query i excluded (top-left aligned, absolute indices) */
-    FA_MASK_BOOL = 2     /* uint8 tensor, nonzero = excluded */
+    FA_MASK_BOOL = 2,    /* uint8 tensor, nonzero = excluded */
+    FA_MASK_WINDOW = 3   /* band: key j kept iff i - win_left <= j <= i + win_right */
 } fa_mask_mode;
 
 /* KV cache storage (FlashAttn developer guide 1.2, PagedAttention, and its
@@ -121,6 +122,12 @@ typedef struct {
     int64_t block_size;
     int64_t max_blocks_per_seq;
     int64_t num_blocks;
+    /* FA_MASK_WINDOW only (ignored otherwise): tokens kept before and after the
+     * query's own index (developer guide 1.5, win_left / win_right); -1 leaves
+     * that side unbounded, so (-1, 0) is the causal mask and (-1, -1) no mask.
+     * Values below -1 are invalid.  Tiles wholly outside the band are skipped. */
+    int64_t win_left;
+    int64_t win_right;
 } fa_params;
 
 /* fa_workspace_size -- phase 1 of fa_fwd (the two-phase shape of the IFA guide,

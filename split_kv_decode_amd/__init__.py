@@ -22,7 +22,9 @@ LIB_PATH = os.path.join(HERE, "libfa_mi355x.so")
 FA_OK, FA_ERR_NULLPTR, FA_ERR_PARAM_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_RUNTIME = range(5)
 FA_BNSD, FA_BSND = 0, 1
 FA_F16, FA_BF16 = 0, 1
-FA_MASK_NONE, FA_MASK_CAUSAL, FA_MASK_BOOL = 0, 1, 2
+FA_MASK_NONE, FA_MASK_CAUSAL, FA_MASK_BOOL, FA_MASK_WINDOW = 0, 1, 2, 3
+MASK_MODES = {"none": FA_MASK_NONE, "causal": FA_MASK_CAUSAL, "bool": FA_MASK_BOOL,
+              "window": FA_MASK_WINDOW}
 FA_KV_CONTIGUOUS, FA_KV_PAGED_BBND, FA_KV_PAGED_BNBD = 0, 1, 2
 KV_LAYOUTS = {"contiguous": FA_KV_CONTIGUOUS, "PA_BBND": FA_KV_PAGED_BBND, "PA_BNBD": FA_KV_PAGED_BNBD}
 
@@ -45,7 +47,8 @@ class FaParams(ctypes.Structure):
                 ("mask", ctypes.c_void_p), ("mask_stride", ctypes.c_int64 * 4),
                 ("kv_layout", ctypes.c_int), ("block_table", ctypes.c_void_p),
                 ("block_size", ctypes.c_int64), ("max_blocks_per_seq", ctypes.c_int64),
-                ("num_blocks", ctypes.c_int64)]
+                ("num_blocks", ctypes.c_int64), ("win_left", ctypes.c_int64),
+                ("win_right", ctypes.c_int64)]
 
 
 _lock = threading.Lock()
@@ -106,7 +109,8 @@ def _check(st: int):
 def make_params(batch, num_heads, q_seq, kv_seq, head_dim, *, num_kv_heads=0, layout="BNSD",
                 dtype="bf16", scale=1.0, actual_seq_lengths=None, mask_mode="none", mask=None,
                 mask_stride: Sequence[int] = (0, 0, 0, 0), kv_layout="contiguous", block_table=None,
-                block_size=0, max_blocks_per_seq=0, num_blocks=0) -> FaParams:
+                block_size=0, max_blocks_per_seq=0, num_blocks=0, win_left=-1,
+                win_right=-1) -> FaParams:
     p = FaParams()
     p.batch, p.num_heads, p.num_kv_heads = batch, num_heads, num_kv_heads
     p.q_seq, p.kv_seq, p.head_dim = q_seq, kv_seq, head_dim
@@ -114,8 +118,8 @@ def make_params(batch, num_heads, q_seq, kv_seq, head_dim, *, num_kv_heads=0, la
     p.dtype = {"f16": FA_F16, "bf16": FA_BF16}[dtype] if isinstance(dtype, str) else dtype
     p.scale = float(scale)
     p.actual_seq_lengths = _ptr(actual_seq_lengths)
-    p.mask_mode = ({"none": FA_MASK_NONE, "causal": FA_MASK_CAUSAL, "bool": FA_MASK_BOOL}[mask_mode]
-                   if isinstance(mask_mode, str) else mask_mode)
+    p.mask_mode = MASK_MODES[mask_mode] if isinstance(mask_mode, str) else mask_mode
+    p.win_left, p.win_right = int(win_left), int(win_right)
     p.mask = _ptr(mask)
     for i in range(4):
         p.mask_stride[i] = int(mask_stride[i])
@@ -159,12 +163,13 @@ def fa_combine(params: FaParams, num_splits, o_part, m_part, l_part, out, lse=No
 
 def params_for(q, k, *, layout="BNSD", num_kv_heads=0, scale=1.0, actual_seq_lengths=None,
                mask=None, mask_stride=(0, 0, 0, 0), causal=False, kv_layout="contiguous",
-               block_table=None) -> FaParams:
+               block_table=None, window=None) -> FaParams:
     """FaParams from torch tensors q, k in ``layout`` (shapes as in include/fa.h).
 
     With a paged ``kv_layout`` k is [num_blocks, block_size, KV_N, D] (PA_BBND) or
     [num_blocks, KV_N, block_size, D] (PA_BNBD), block_table is int32
     [B, max_blocks_per_seq], and kv_seq is max_blocks_per_seq * block_size.
+    ``window=(win_left, win_right)`` selects the window mask (-1 = unbounded side).
     """
     import torch
     if layout == "BNSD":
@@ -182,6 +187,9 @@ def params_for(q, k, *, layout="BNSD", num_kv_heads=0, scale=1.0, actual_seq_len
                      max_blocks_per_seq=block_table.shape[1], num_blocks=nb)
     dtype = {torch.bfloat16: "bf16", torch.float16: "f16"}[q.dtype]
     mode = "bool" if mask is not None else ("causal" if causal else "none")
+    if window is not None:
+        mode = "window"
+        extra.update(win_left=window[0], win_right=window[1])
     return make_params(B, N, QS, KVS, D, num_kv_heads=num_kv_heads or KVN, layout=layout,
                        dtype=dtype, scale=scale, actual_seq_lengths=actual_seq_lengths,
                        mask_mode=mode, mask=mask, mask_stride=mask_stride, **extra)
@@ -189,14 +197,14 @@ def params_for(q, k, *, layout="BNSD", num_kv_heads=0, scale=1.0, actual_seq_len
 
 def fwd(q, k, v, *, layout="BNSD", scale=None, actual_seq_lengths=None, mask=None,
         mask_stride=(0, 0, 0, 0), causal=False, return_lse=False, stream=None,
-        kv_layout="contiguous", block_table=None):
+        kv_layout="contiguous", block_table=None, window=None):
     """Attention forward on device tensors; allocates out (and lse, workspace) with torch."""
     import torch
     D = q.shape[-1]
     sc = (1.0 / math.sqrt(D)) if scale is None else scale
     p = params_for(q, k, layout=layout, scale=sc, actual_seq_lengths=actual_seq_lengths,
                    mask=mask, mask_stride=mask_stride, causal=causal, kv_layout=kv_layout,
-                   block_table=block_table)
+                   block_table=block_table, window=window)
     out = torch.empty_like(q)
     lse = (torch.empty((p.batch, p.num_heads, p.q_seq), dtype=torch.float32, device=q.device)
            if return_lse else None)

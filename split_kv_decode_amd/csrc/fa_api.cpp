@@ -63,8 +63,12 @@ fa_status check_params(const fa_params* p, Shape* s) {
     if (p->layout != FA_BNSD && p->layout != FA_BSND) return fail(FA_ERR_PARAM_INVALID, "unknown layout %d", (int)p->layout);
     if (p->dtype != FA_F16 && p->dtype != FA_BF16) return fail(FA_ERR_PARAM_INVALID, "unknown dtype %d", (int)p->dtype);
     if (!std::isfinite(p->scale)) return fail(FA_ERR_PARAM_INVALID, "scale must be finite");
-    if (p->mask_mode != FA_MASK_NONE && p->mask_mode != FA_MASK_CAUSAL && p->mask_mode != FA_MASK_BOOL)
+    if (p->mask_mode != FA_MASK_NONE && p->mask_mode != FA_MASK_CAUSAL && p->mask_mode != FA_MASK_BOOL &&
+        p->mask_mode != FA_MASK_WINDOW)
         return fail(FA_ERR_PARAM_INVALID, "unknown mask_mode %d", (int)p->mask_mode);
+    if (p->mask_mode == FA_MASK_WINDOW && (p->win_left < -1 || p->win_right < -1))
+        return fail(FA_ERR_PARAM_INVALID, "win_left and win_right must be >= -1 (-1 = unbounded), got %lld, %lld",
+                    (long long)p->win_left, (long long)p->win_right);
     if (p->mask_mode == FA_MASK_BOOL && !p->mask) return fail(FA_ERR_NULLPTR, "mask_mode BOOL needs a mask tensor");
     if (p->mask_mode != FA_MASK_BOOL && p->mask)
         return fail(FA_ERR_PARAM_INVALID, "a mask tensor was passed but mask_mode is not BOOL");
@@ -294,7 +298,14 @@ fa_status run_prefill(const fa_params* p, const Shape& s, const void* q, const v
     a.q_tiles = (int32_t)((s.QS + 127) / 128);
     a.negate_q = p->scale < 0 ? 1 : 0;
     a.scale_log2 = (float)(std::fabs(p->scale) * 1.4426950408889634);
-    int mm = p->mask_mode == FA_MASK_NONE ? 0 : (p->mask_mode == FA_MASK_CAUSAL ? 1 : 2);
+    // Window bounds as 32-bit distances from the query row: |key - row| < 2^31.
+    auto win = [](int64_t w) { return (w < 0 || w > 0x7fffffff) ? int32_t(0x7fffffff) : int32_t(w); };
+    a.win_left = win(p->win_left);
+    a.win_right = win(p->win_right);
+    int mm = 0;
+    if (p->mask_mode == FA_MASK_CAUSAL) mm = 1;
+    if (p->mask_mode == FA_MASK_BOOL) mm = 2;
+    if (p->mask_mode == FA_MASK_WINDOW) mm = 4;
     // A boolean mask whose rows are contiguous, 16-byte aligned key runs is
     // staged through LDS tile by tile (instantiation 3); any other stride
     // pattern is read element by element (instantiation 2).

@@ -65,6 +65,8 @@ struct PrefillArgs {
     int32_t q_tiles;
     int32_t negate_q;         // 1 when scale < 0: q's sign is flipped, scale_log2 = |scale|*log2(e)
     float scale_log2;
+    int32_t win_left;         // window mask: keys qrow - win_left .. qrow + win_right kept;
+    int32_t win_right;        // 0x7fffffff = unbounded on that side
 };
 
 // Block ids one paged stage-1 workgroup stages in LDS: a chunk may touch at most

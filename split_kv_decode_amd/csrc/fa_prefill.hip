@@ -26,6 +26,13 @@
 // 16 rows at one chunk for K, and the transposing ds_read_b64_tr_b16 reads
 // that build V^T operands -- are free of bank conflicts.
 //
+// Masks.  MASK 0 none; 1 causal from indices (tiles past the diagonal are
+// not visited); 2 a boolean tensor read element by element; 3 a boolean
+// tensor with contiguous key rows, staged through LDS with the K/V tiles;
+// 4 the window band of the FlashAttn developer guide (1.5, mode 4): only the
+// KV tiles that intersect the band of the query tile are visited, and a wave
+// skips tiles outside the band of its 32 rows.
+//
 // Softmax.  Exponentials are taken against the running max before the tile's
 // max is known, and the output is rescaled only when a row max grows by more
 // than 2^8 (wave-uniform test); both keep the vector work per tile close to
@@ -155,8 +162,18 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     }
     const float c = a.scale_log2;
 
+    // KV tiles [jt0, ntiles) can hold visible keys for this query tile: causal
+    // stops at the tile's last row, a window spans from the first row's left
+    // edge to the last row's right edge.
     int64_t kv_end = L;
     if (MASK == 1 && kv_end > i0 + BM) kv_end = i0 + BM;  // keys beyond the tile's last row
+    int jt0 = 0;
+    if (MASK == 4) {
+        const int64_t i_last = (i0 + BM < a.q_seq ? i0 + BM : a.q_seq) - 1;
+        if (kv_end > i_last + a.win_right + 1) kv_end = i_last + a.win_right + 1;
+        const int64_t key_lo = i0 - a.win_left;
+        if (key_lo > 0) jt0 = (int)(key_lo / BN);
+    }
     const int ntiles = (int)((kv_end + BN - 1) / BN);
 
     f32x16 o[D / 32];
@@ -234,7 +251,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     const int vx = 2 * (trG & 1) + ((trL & 3) >> 1);
     const int vbyte = (trL & 1) * 8;
 
-    if (ntiles > 0) issue_tile(0, sK0, sV0, sM0);
+    if (ntiles > jt0) issue_tile(jt0, sK0, sV0, sM0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
@@ -276,6 +293,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
             }
             asm volatile("" ::: "memory");  // re-read the words after the QK MFMAs instead of holding them
         }
+        // MASK 4: a tile wholly left or right of the band of every row of
+        // this wave is skipped (wave-uniform).
+        if (MASK == 4) {
+            if (j0 + BN - 1 < wrow0 - a.win_left || j0 > wrow0 + 31 + a.win_right) {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                __syncthreads();
+                return;
+            }
+        }
 
         // S^T tiles: keys [j0 + 32*tt, +32) x the wave's 32 query rows (raw
         // q.k); the two accumulation chains are interleaved.
@@ -297,7 +323,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         // Masking is needed only on tiles that cross the length, the causal
         // diagonal of this wave's rows, or under a boolean mask.  Accumulator
         // register r of tile tt holds key j0 + 32*tt + 8*(r/4) + 4*half + r%4.
-        const bool need_mask = (j0 + BN > L) || (MASK == 1 && j0 + BN - 1 > wrow0) || (MASK >= 2);
+        const bool need_mask = (j0 + BN > L) || (MASK == 1 && j0 + BN - 1 > wrow0) || (MASK == 2) ||
+                               (MASK == 3) ||
+                               (MASK == 4 && (j0 < wrow0 + 31 - a.win_left || j0 + BN - 1 > wrow0 + a.win_right));
         if (MASK == 3) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
@@ -319,6 +347,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
                              a.mask[b * a.mask_stride[0] + (int64_t)n1 * a.mask_stride[1] +
                                     qrow * a.mask_stride[2] + tok * a.mask_stride[3]] == 0;
                     if (MASK == 3) ok = ok && qvalid && ((mw[tt][r >> 2] >> (8 * (r & 3))) & 0xffu) == 0u;
+                    if (MASK == 4) {
+                        const int dj = (int)(tok - qrow);
+                        ok = ok && dj >= -a.win_left && dj <= a.win_right;
+                    }
                     s[tt][r] = ok ? s[tt][r] : kNegInf;
                 }
             }
@@ -383,7 +415,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of the next tile landed
         __syncthreads();  // ... and everyone else's; this tile is consumed
     };
-    for (int jt = 0; jt < ntiles; jt += 2) {
+    for (int jt = jt0; jt < ntiles; jt += 2) {
         step(jt, sK0, sV0, sM0, sK1, sV1, sM1);
         if (jt + 1 < ntiles) step(jt + 1, sK1, sV1, sM1, sK0, sV0, sM0);
     }
@@ -422,6 +454,7 @@ static hipError_t dispatch_prefill(const PrefillArgs& a, int mask_mode, int64_t 
         case 1: hipLaunchKernelGGL((prefill_kernel<ST, D, 1>), grid, block, 0, s, a); break;
         case 2: hipLaunchKernelGGL((prefill_kernel<ST, D, 2>), grid, block, 0, s, a); break;
         case 3: hipLaunchKernelGGL((prefill_kernel<ST, D, 3>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((prefill_kernel<ST, D, 4>), grid, block, 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

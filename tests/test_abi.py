@@ -55,6 +55,9 @@ FAKE = 1 << 20  # a 16-byte-aligned non-null address; never dereferenced (valida
     (dict(mask=FAKE), fa.FA_ERR_PARAM_INVALID, "not BOOL"),
     (dict(layout=7), fa.FA_ERR_PARAM_INVALID, "layout"),
     (dict(dtype=5), fa.FA_ERR_PARAM_INVALID, "dtype"),
+    (dict(mask_mode="window", win_left=-2), fa.FA_ERR_PARAM_INVALID, "win_left"),
+    (dict(mask_mode="window", win_right=-7), fa.FA_ERR_PARAM_INVALID, "win_right"),
+    (dict(mask_mode=9), fa.FA_ERR_PARAM_INVALID, "mask_mode"),
 ])
 def test_fwd_rejects_invalid_parameters(lib, kw, status, text):
     p = params(**kw)

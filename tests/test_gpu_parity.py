@@ -423,6 +423,68 @@ def test_prefill_ignores_nan_padding():
     assert torch.equal(out, base) and torch.equal(lse, bl)
 
 
+# ------------------------------------------------------------------ window mask
+
+def run_window(inp, window):
+    s = inp.spec
+    q, k, v = (dev16(x, s.dtype) for x in (inp.q, inp.k, inp.v))
+    lens = None if inp.lens is None else torch.from_numpy(inp.lens).to(DEV)
+    out, lse = fa.fwd(q, k, v, layout=s.layout, scale=s.softmax_scale, actual_seq_lengths=lens,
+                      window=window, return_lse=True)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def window_prob(inp, window):
+    s = inp.spec
+    return oracle.Problem(s.B, s.QN, s.KVN, s.QS, s.KVS, s.D, s.layout, s.dtype, s.softmax_scale,
+                          inp.lens, "window", window=window)
+
+
+WINDOW_CASES = [
+    (dict(layout="BSND", B=2, QN=4, KVN=2, QS=300, KVS=300, D=128), (64, 0)),
+    (dict(B=1, QN=4, KVN=4, QS=200, KVS=500, D=64, dtype="f16", std=0.5, lens=(100, 500)), (10, 30)),
+    (dict(B=1, QN=2, KVN=1, QS=130, KVS=130, D=128), (0, 0)),
+    (dict(B=2, QN=2, KVN=2, QS=300, KVS=300, D=128, lens=(50, 60)), (20, 0)),   # rows with no key
+    (dict(B=1, QN=8, KVN=2, QS=1, KVS=700, D=128, lens=(300, 700)), (0, 200)),  # decode row
+    (dict(B=1, QN=2, KVN=2, QS=257, KVS=1000, D=64, layout="BSND"), (-1, 100)),
+    (dict(B=1, QN=2, KVN=2, QS=400, KVS=400, D=128, scale=-0.09), (150, -1)),
+]
+
+
+@pytest.mark.parametrize("case,window", WINDOW_CASES,
+                         ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()) if isinstance(c, dict) else str(c))
+def test_window_matches_oracle(case, window):
+    inp = fa_synth.make(spec(seed=91, **case))
+    s = inp.spec
+    out, lse = run_window(inp, window)
+    ref, ref_lse = oracle.attention_rows(window_prob(inp, window), inp.q, inp.k, inp.v)
+    check(rows_of(out, s, np.arange(s.B * s.QN * s.QS)), to_np(lse).reshape(-1), ref, ref_lse,
+          f"window {window} {case}")
+
+
+def test_window_special_cases_equal_causal_and_none():
+    """(-1, 0) reproduces the causal mode and (-1, -1) the unmasked kernel bit for bit."""
+    inp = fa_synth.make(spec(layout="BNSD", B=1, QN=4, KVN=2, QS=333, KVS=333, lens=(200, 333),
+                             seed=92))
+    o1, l1 = run_window(inp, (-1, 0))
+    o2, l2 = run_fwd(inp, "causal")
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    o1, l1 = run_window(inp, (-1, -1))
+    o2, l2 = run_fwd(inp, "none")
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_window_4k_sampled():
+    """Sliding window of 1024 keys on the 4096-token prefill shape (sampled rows)."""
+    inp = workload("prefill_4k")
+    s = inp.spec
+    out, lse = run_window(inp, (1024, 0))
+    rows = fa_synth.sample_rows(s, 2000, seed=12, lens=inp.lens)
+    ref, ref_lse = oracle.attention_rows(window_prob(inp, (1024, 0)), inp.q, inp.k, inp.v, rows)
+    check(rows_of(out, s, rows), to_np(lse).reshape(-1)[rows], ref, ref_lse, "window 4k")
+
+
 # ------------------------------------------------------------------ the five workloads
 
 def test_workload_prefill_small_full():

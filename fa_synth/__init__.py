@@ -265,3 +265,58 @@ def to_paged(inp: Inputs, block_size: int, kv_layout: str = "PA_BBND", seed: int
         phys[table.reshape(-1)] = src.reshape((s.B * max_blocks,) + phys.shape[1:])
         out.append(np.ascontiguousarray(phys))
     return out[0], out[1], table, nb
+
+
+@dataclass
+class PackedInputs:
+    """Packed variable-length (TND) inputs: sequences laid end to end."""
+    q: np.ndarray                 # uint16 [Q_T, QN, D]
+    k: np.ndarray                 # uint16 [KV_T, KVN, D]
+    v: np.ndarray
+    cu_q: np.ndarray              # int32 [B + 1]
+    cu_kv: np.ndarray             # int32 [B + 1]
+    q_lens: np.ndarray            # int64 [B]
+    kv_lens: np.ndarray           # int64 [B]
+    QN: int
+    KVN: int
+    D: int
+    dtype: str
+    scale: float
+
+
+def make_packed(B: int, QN: int, KVN: int, D: int, dtype: str = "bf16", q_lens=(1, 512),
+                kv_lens=None, std: float = 1.0, scale: Optional[float] = None,
+                seed: int = 0) -> PackedInputs:
+    """Seeded TND inputs (FlashAttn developer guide 1.3, Packed Sequence).
+
+    Draw order: rng = default_rng(seed); the B query lengths as inclusive
+    integers in q_lens; the B KV lengths likewise in kv_lens (None: equal to the
+    query lengths, self-attention prefill); then Q, K, V as standard_normal *
+    std rounded to the storage type.
+    """
+    rng = np.random.default_rng(seed)
+    ql = rng.integers(q_lens[0], q_lens[1], endpoint=True, size=B).astype(np.int64)
+    kl = ql.copy() if kv_lens is None else rng.integers(kv_lens[0], kv_lens[1], endpoint=True,
+                                                         size=B).astype(np.int64)
+    cu_q = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+    cu_kv = np.concatenate([[0], np.cumsum(kl)]).astype(np.int32)
+
+    def draw(shape):
+        x = rng.standard_normal(shape, dtype=np.float32)
+        if std != 1.0:
+            x *= np.float32(std)
+        return round_bits(x, dtype)
+
+    q = draw((int(cu_q[-1]), QN, D))
+    k = draw((int(cu_kv[-1]), KVN, D))
+    v = draw((int(cu_kv[-1]), KVN, D))
+    sc = (1.0 / math.sqrt(D)) if scale is None else float(scale)
+    return PackedInputs(q, k, v, cu_q, cu_kv, ql, kl, QN, KVN, D, dtype, sc)
+
+
+# Ragged self-attention prefill in the packed layout: 16 sequences of 256..8192
+# tokens, GQA 32/8, causal (the length mix of the ragged long-prefill workload,
+# without the padding).
+PACKED_WORKLOADS = {
+    "prefill_varlen": dict(B=16, QN=32, KVN=8, D=128, dtype="bf16", q_lens=(256, 8192), seed=1006),
+}

@@ -49,7 +49,9 @@ class _Problem(ctypes.Structure):
                 ("kv_layout", ctypes.c_int32),
                 ("block_table", ctypes.POINTER(ctypes.c_int32)),
                 ("block_size", ctypes.c_int64), ("max_blocks", ctypes.c_int64),
-                ("win_left", ctypes.c_int64), ("win_right", ctypes.c_int64)]
+                ("win_left", ctypes.c_int64), ("win_right", ctypes.c_int64),
+                ("cu_q", ctypes.POINTER(ctypes.c_int32)), ("cu_kv", ctypes.POINTER(ctypes.c_int32)),
+                ("used_q", ctypes.POINTER(ctypes.c_int32))]
 
 
 def _load():
@@ -93,7 +95,8 @@ class Problem:
 
     def __init__(self, B, QN, KVN, QS, KVS, D, layout="BNSD", dtype="bf16", scale=1.0,
                  lens=None, mask_mode="none", mask=None, mask_strides=(0, 0, 0, 0),
-                 kv_layout="contiguous", block_table=None, block_size=0, window=(-1, -1)):
+                 kv_layout="contiguous", block_table=None, block_size=0, window=(-1, -1),
+                 cu_seqlens_q=None, cu_seqlens_kv=None, seqused_q=None):
         self.B, self.QN, self.KVN, self.QS, self.KVS, self.D = B, QN, KVN, QS, KVS, D
         self.layout, self.dtype, self.scale = layout, dtype, float(scale)
         self.lens = None if lens is None else np.ascontiguousarray(lens, dtype=np.int64)
@@ -105,6 +108,11 @@ class Problem:
                             else np.ascontiguousarray(block_table, dtype=np.int32))
         self.block_size = int(block_size)
         self.window = (int(window[0]), int(window[1]))  # mask_mode "window": (win_left, win_right)
+        # layout "TND": QS / KVS are the packed totals Q_T / KV_T; sequence b spans
+        # cu_seqlens[b] .. cu_seqlens[b+1]; seqused_q truncates its query rows.
+        i32 = lambda a: None if a is None else np.ascontiguousarray(a, dtype=np.int32)
+        self.cu_seqlens_q, self.cu_seqlens_kv = i32(cu_seqlens_q), i32(cu_seqlens_kv)
+        self.seqused_q = i32(seqused_q)
 
     @classmethod
     def from_inputs(cls, inp, mask_mode: Optional[str] = None):
@@ -118,7 +126,10 @@ class Problem:
     def _c(self):
         p = _Problem()
         p.B, p.QN, p.KVN, p.QS, p.KVS, p.D = self.B, self.QN, self.KVN, self.QS, self.KVS, self.D
-        p.layout = 0 if self.layout == "BNSD" else 1
+        p.layout = {"BNSD": 0, "BSND": 1, "TND": 2}[self.layout]
+        p.cu_q = _ptr(self.cu_seqlens_q, ctypes.c_int32)
+        p.cu_kv = _ptr(self.cu_seqlens_kv, ctypes.c_int32)
+        p.used_q = _ptr(self.seqused_q, ctypes.c_int32)
         p.dtype = 1 if self.dtype == "bf16" else 0
         p.scale = self.scale
         p.lens = _ptr(self.lens, ctypes.c_int64)
@@ -134,7 +145,7 @@ class Problem:
         return p
 
     def nrows(self) -> int:
-        return self.B * self.QN * self.QS
+        return self.QN * self.QS if self.layout == "TND" else self.B * self.QN * self.QS
 
 
 def _u16(a):
@@ -162,8 +173,10 @@ def attention_rows(prob: Problem, q, k, v, rows=None, threads: Optional[int] = N
 
 
 def rows_to_layout(prob: Problem, out_rows, lse_rows):
-    """Flat-row results (every row) -> out in the q layout and lse [B, QN, QS]."""
+    """Flat-row results (every row) -> out in the q layout and lse [B, QN, QS] ([Q_T, QN] for TND)."""
     B, QN, QS, D = prob.B, prob.QN, prob.QS, prob.D
+    if prob.layout == "TND":
+        return np.ascontiguousarray(out_rows.reshape(QS, QN, D)), lse_rows.reshape(QS, QN)
     o = out_rows.reshape(B, QN, QS, D)
     if prob.layout == "BSND":
         o = o.transpose(0, 2, 1, 3)

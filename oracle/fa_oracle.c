@@ -31,6 +31,16 @@
  *   - Window mask (developer guide 1.5, mask mode 4): query row i keeps the
  *     band of keys i - win_left <= j <= i + win_right; a negative bound is
  *     unbounded on that side (the guide sets both to -1 when no window is used).
+ *   - Packed variable-length layout TND (developer guide 1.3 and 1.4): q is
+ *     (Q_T, Q_N, D) and k, v (KV_T, KV_N, D), the sequences laid end to end;
+ *     sequence b holds q rows cu_seqlens_q[b] .. cu_seqlens_q[b+1] - 1 and kv
+ *     rows cu_seqlens_kv[b] .. cu_seqlens_kv[b+1] - 1.  The per-batch lengths,
+ *     when given, truncate (the shorter takes effect): seqused_q for the query
+ *     rows, the actual KV lengths for the keys.  Indices i, j of masks are
+ *     positions inside the sequence.  A query row past its sequence's used
+ *     length is not computed and keeps the initial output (0 and lse = +inf,
+ *     the output initialisation the developer guide describes).  Rows are
+ *     numbered t * Q_N + n1, the (Q_T, Q_N) order of the TND lse.
  *   - Paged KV caches (FlashAttn developer guide 1.2): token j of batch b is
  *     row j % block_size of physical block block_table[b][j / block_size];
  *     PA_BBND blocks are [block_size][KV_N][D], PA_BNBD blocks [KV_N][block_size][D].
@@ -46,7 +56,7 @@
 
 typedef struct {
     int64_t B, QN, KVN, QS, KVS, D;
-    int32_t layout;             /* 0 = BNSD, 1 = BSND (q, k, v, out alike) */
+    int32_t layout;             /* 0 = BNSD, 1 = BSND, 2 = TND (q, k, v, out alike) */
     int32_t dtype;              /* 0 = fp16, 1 = bf16 storage */
     double scale;
     const int64_t *lens;        /* [B] actual KV lengths, or NULL (= KV_S) */
@@ -57,6 +67,8 @@ typedef struct {
     const int32_t *block_table; /* [B][max_blocks] physical block ids */
     int64_t block_size, max_blocks;
     int64_t win_left, win_right; /* mode 3: keys i - win_left .. i + win_right; < 0 unbounded */
+    const int32_t *cu_q, *cu_kv; /* TND: [B + 1] sequence starts (QS = Q_T, KVS = KV_T) */
+    const int32_t *used_q;      /* TND: [B] used query rows, or NULL */
 } orc_problem;
 
 static double dec16(int32_t dtype, uint16_t h)
@@ -81,6 +93,7 @@ static double dec16(int32_t dtype, uint16_t h)
 
 static int64_t q_index(const orc_problem *p, int64_t b, int64_t n, int64_t i)
 {
+    if (p->layout == 2) return ((p->cu_q[b] + i) * p->QN + n) * p->D;
     return p->layout == 0 ? ((b * p->QN + n) * p->QS + i) * p->D
                           : ((b * p->QS + i) * p->QN + n) * p->D;
 }
@@ -93,15 +106,19 @@ static int64_t kv_index(const orc_problem *p, int64_t b, int64_t n, int64_t j)
         return p->kv_layout == 1 ? ((blk * p->block_size + r) * p->KVN + n) * p->D
                                  : ((blk * p->KVN + n) * p->block_size + r) * p->D;
     }
+    if (p->layout == 2) return ((p->cu_kv[b] + j) * p->KVN + n) * p->D;
     return p->layout == 0 ? ((b * p->KVN + n) * p->KVS + j) * p->D
                           : ((b * p->KVS + j) * p->KVN + n) * p->D;
 }
 
+/* Keys of batch b: the cache length (the sequence's own length in TND),
+ * truncated by the actual length when one is given. */
 static int64_t row_length(const orc_problem *p, int64_t b)
 {
-    int64_t L = p->lens ? p->lens[b] : p->KVS;
+    const int64_t cap = p->layout == 2 ? (int64_t)p->cu_kv[b + 1] - p->cu_kv[b] : p->KVS;
+    int64_t L = p->lens ? p->lens[b] : cap;
     if (L < 0) L = 0;
-    if (L > p->KVS) L = p->KVS;
+    if (L > cap) L = cap;
     return L;
 }
 
@@ -162,7 +179,7 @@ typedef struct {
     const orc_problem *p;
     const uint16_t *q, *k, *v;
     int64_t nrows;
-    const int64_t *rows;        /* flat row ids (b*QN + n1)*QS + i, or NULL for all */
+    const int64_t *rows;        /* flat row ids (b*QN + n1)*QS + i (TND: t*QN + n1), or NULL for all */
     int64_t splits, chunk;      /* split mode when splits > 0 */
     double *out, *lse;          /* attention mode: [nrows][D], [nrows] */
     double *o_part, *m_part, *l_part; /* split mode: [nrows][splits][D], [nrows][splits] */
@@ -179,9 +196,33 @@ static void *worker(void *arg)
     if (!s || !ok || !qd) { free(s); free(ok); free(qd); return (void *)1; }
     for (int64_t r = jb->tid; r < jb->nrows; r += jb->nthreads) {
         const int64_t row = jb->rows ? jb->rows[r] : r;
-        const int64_t i = row % p->QS;
-        const int64_t n1 = (row / p->QS) % p->QN;
-        const int64_t b = row / (p->QS * p->QN);
+        int64_t i, n1, b;
+        int computed = 1;
+        if (p->layout == 2) { /* row = t * Q_N + n1; t lies in sequence b */
+            const int64_t t = row / p->QN;
+            n1 = row % p->QN;
+            b = 0;
+            while (b < p->B && p->cu_q[b + 1] <= t) ++b;
+            i = b < p->B ? t - p->cu_q[b] : 0;
+            if (b == p->B || (p->used_q && i >= p->used_q[b])) computed = 0;
+        } else {
+            i = row % p->QS;
+            n1 = (row / p->QS) % p->QN;
+            b = row / (p->QS * p->QN);
+        }
+        if (!computed) { /* outside every sequence's used rows: initial output */
+            if (jb->splits == 0) {
+                for (int64_t d = 0; d < p->D; ++d) jb->out[r * p->D + d] = 0.0;
+                jb->lse[r] = INFINITY;
+            } else {
+                for (int64_t c = 0; c < jb->splits; ++c) {
+                    for (int64_t d = 0; d < p->D; ++d) jb->o_part[(r * jb->splits + c) * p->D + d] = 0.0;
+                    jb->m_part[r * jb->splits + c] = -INFINITY;
+                    jb->l_part[r * jb->splits + c] = 0.0;
+                }
+            }
+            continue;
+        }
         const int64_t L = row_length(p, b);
         const uint16_t *qr = jb->q + q_index(p, b, n1, i);
         for (int64_t d = 0; d < p->D; ++d) qd[d] = dec16(p->dtype, qr[d]);
@@ -224,6 +265,13 @@ static int check(const orc_problem *p)
     if (p->mask_mode == 2 && !p->mask) return -3;
     if (p->kv_layout != 0 && (!p->block_table || p->block_size <= 0 || p->max_blocks <= 0 ||
                               p->KVS > p->max_blocks * p->block_size)) return -5;
+    if (p->layout == 2) { /* well-formed cumulative lengths within the packed tensors */
+        if (!p->cu_q || !p->cu_kv || p->kv_layout != 0) return -6;
+        if (p->cu_q[0] != 0 || p->cu_kv[0] != 0) return -6;
+        for (int64_t b = 0; b < p->B; ++b)
+            if (p->cu_q[b + 1] < p->cu_q[b] || p->cu_kv[b + 1] < p->cu_kv[b]) return -6;
+        if (p->cu_q[p->B] > p->QS || p->cu_kv[p->B] > p->KVS) return -6;
+    }
     return 0;
 }
 

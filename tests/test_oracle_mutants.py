@@ -21,7 +21,7 @@ MUTANTS = [
     ("causal_off_by_one", "if (p->mask_mode == 1 && j > i) return 0;",
      "if (p->mask_mode == 1 && j >= i) return 0;"),
     ("lse_base2", "jb->lse[r] = log(l) + m;", "jb->lse[r] = log2(l) + m;"),
-    ("length_ignored", "int64_t L = p->lens ? p->lens[b] : p->KVS;", "int64_t L = p->KVS;"),
+    ("length_ignored", "int64_t L = p->lens ? p->lens[b] : cap;", "int64_t L = cap;"),
     ("mask_polarity", "if (p->mask[b * st[0] + n1 * st[1] + i * st[2] + j * st[3]] != 0) return 0;",
      "if (p->mask[b * st[0] + n1 * st[1] + i * st[2] + j * st[3]] == 0) return 0;"),
     ("merge_weight_sign", "const double w = exp(m[c] - mg);", "const double w = exp(mg - m[c]);"),
@@ -36,6 +36,9 @@ MUTANTS = [
      "if (p->win_left >= 0 && j <= i - p->win_left) return 0;"),
     ("window_right_sign", "if (p->win_right >= 0 && j > i + p->win_right) return 0;",
      "if (p->win_right >= 0 && j > i - p->win_right) return 0;"),
+    ("tnd_kv_offsets", "if (p->layout == 2) return ((p->cu_kv[b] + j) * p->KVN + n) * p->D;",
+     "if (p->layout == 2) return ((p->cu_q[b] + j) * p->KVN + n) * p->D;"),
+    ("tnd_used_rows", "(p->used_q && i >= p->used_q[b])", "(p->used_q && i > p->used_q[b])"),
     ("paged_row_offset", "const int64_t r = j % p->block_size;", "const int64_t r = (j + 1) % p->block_size;"),
     ("paged_bnbd_order", ": ((blk * p->KVN + n) * p->block_size + r) * p->D;",
      ": ((blk * p->block_size + r) * p->KVN + n) * p->D;"),

@@ -450,3 +450,58 @@ def test_window_sdpa_pin():
     p = oracle.Problem(1, 3, 3, 30, 30, 16, "BNSD", "bf16", 0.3, None, "window", window=(4, 2))
     out, _ = oracle.attention(p, inp.q, inp.k, inp.v)
     assert np.allclose(out, ref, rtol=1e-10, atol=1e-10)
+
+
+# ---------------------------------------------------------------- packed variable length (TND)
+
+def _tnd_prob(x, mode="none", lens=None, seqused_q=None, window=(-1, -1)):
+    B = len(x.cu_q) - 1
+    return oracle.Problem(B, x.QN, x.KVN, int(x.cu_q[-1]), int(x.cu_kv[-1]), x.D, "TND", x.dtype,
+                          x.scale, lens, mode, window=window, cu_seqlens_q=x.cu_q,
+                          cu_seqlens_kv=x.cu_kv, seqused_q=seqused_q)
+
+
+@pytest.mark.parametrize("mode", ["none", "causal"])
+def test_tnd_equals_brute_force_per_sequence(mode):
+    """The packed layout (FlashAttn guide 1.3) is the padded one without padding: every
+    sequence of a TND batch must give the whole-matrix brute force of that sequence alone."""
+    x = fa_synth.make_packed(4, 4, 2, 16, q_lens=(1, 23), kv_lens=(1, 31), seed=101)
+    out, lse = oracle.attention(_tnd_prob(x, mode), x.q, x.k, x.v)
+    for b in range(4):
+        q0, q1, k0, k1 = x.cu_q[b], x.cu_q[b + 1], x.cu_kv[b], x.cu_kv[b + 1]
+        pb = oracle.Problem(1, 4, 2, int(q1 - q0), int(k1 - k0), 16, "BSND", "bf16", x.scale,
+                            None, mode)
+        ro, rl = brute.attention(pb, x.q[None, q0:q1], x.k[None, k0:k1], x.v[None, k0:k1])
+        assert np.allclose(out[q0:q1], ro[0], rtol=1e-12, atol=1e-12)
+        fin = np.isfinite(rl[0].T)
+        assert np.array_equal(np.isinf(lse[q0:q1]), np.isinf(rl[0].T))
+        assert np.allclose(lse[q0:q1][fin], rl[0].T[fin], rtol=1e-12, atol=1e-12)
+
+
+def test_tnd_truncation_and_unused_rows():
+    """seqused_q leaves the rows past it at the initial output (0, lse +inf); the KV
+    lengths truncate each sequence's keys (the shorter of the two takes effect)."""
+    x = fa_synth.make_packed(3, 2, 1, 16, q_lens=(5, 12), seed=102)
+    used = np.array([3, 0, 100], np.int32)
+    kv_lens = np.array([2, 5, 1000], np.int64)
+    out, lse = oracle.attention(_tnd_prob(x, "none", kv_lens, used), x.q, x.k, x.v)
+    for b in range(3):
+        q0, q1, k0 = x.cu_q[b], x.cu_q[b + 1], x.cu_kv[b]
+        nq = min(int(used[b]), int(q1 - q0))
+        L = min(int(kv_lens[b]), int(x.cu_kv[b + 1] - k0))
+        assert np.all(out[q0 + nq:q1] == 0) and np.all(np.isposinf(lse[q0 + nq:q1]))
+        if nq:
+            pb = oracle.Problem(1, 2, 1, nq, L, 16, "BSND", "bf16", x.scale, None, "none")
+            ro, rl = brute.attention(pb, x.q[None, q0:q0 + nq], x.k[None, k0:k0 + L],
+                                     x.v[None, k0:k0 + L])
+            assert np.allclose(out[q0:q0 + nq], ro[0], rtol=1e-12, atol=1e-12)
+            assert np.allclose(lse[q0:q0 + nq], rl[0].T, rtol=1e-12, atol=1e-12)
+
+
+def test_tnd_rejects_malformed_offsets():
+    x = fa_synth.make_packed(2, 2, 2, 16, q_lens=(3, 5), seed=103)
+    bad = x.cu_q.copy(); bad[1] = bad[2] + 1
+    p = oracle.Problem(2, 2, 2, int(x.cu_q[-1]), int(x.cu_kv[-1]), 16, "TND", "bf16", 1.0, None,
+                       "none", cu_seqlens_q=bad, cu_seqlens_kv=x.cu_kv)
+    with pytest.raises(ValueError):
+        oracle.attention(p, x.q, x.k, x.v)

@@ -314,7 +314,40 @@ def extra_workloads(fa, fa_synth, np, torch, dev16, stream, warmup=3, iters=10):
                         "frac_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "flop": fl, "doc": s.doc}
         del q, k, v, out, lse, ws, mask, inp, block_table
         torch.cuda.empty_cache()
+    res.update(packed_workload(fa, fa_synth, np, torch, dev16, stream, warmup, iters))
     return res
+
+
+def packed_workload(fa, fa_synth, np, torch, dev16, stream, warmup, iters):
+    """The ragged causal prefill in the packed (TND) layout, schedule kernel included."""
+    x = fa_synth.make_packed(**fa_synth.PACKED_WORKLOADS["prefill_varlen"])
+    q, k, v = dev16(x.q, x.dtype), dev16(x.k, x.dtype), dev16(x.v, x.dtype)
+    cu_q = torch.from_numpy(x.cu_q).to(q.device)
+    cu_kv = torch.from_numpy(x.cu_kv).to(q.device)
+    p = fa.params_for(q, k, layout="TND", scale=x.scale, causal=True, cu_seqlens_q=cu_q,
+                      cu_seqlens_kv=cu_kv)
+    out = torch.empty_like(q)
+    lse = torch.empty((p.q_seq, p.num_heads), dtype=torch.float32, device=q.device)
+    nbytes = fa.fa_workspace_size(p)
+    ws = torch.empty((nbytes,), dtype=torch.uint8, device=q.device)
+    for _ in range(warmup):
+        fa.fa_fwd(p, q, k, v, out, lse, ws, nbytes, stream)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for a, b in evs:
+        a.record(stream)
+        fa.fa_fwd(p, q, k, v, out, lse, ws, nbytes, stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    L = x.q_lens.astype(np.float64)
+    fl = 4.0 * x.QN * x.D * float(np.sum(L * (L + 1) / 2))
+    tf = fl / (ms * 1e-3) / 1e12
+    return {"prefill_varlen_causal": {
+        "ms": round(ms, 5), "tflops": round(tf, 2), "frac_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+        "flop": fl, "doc": "packed (TND) causal prefill, 16 sequences of U{256..8192} tokens "
+                           f"(total {int(x.cu_q[-1])}), Q_N=32, KV_N=8, D=128, bf16; "
+                           "includes the work-list kernel"}}
 
 
 if __name__ == "__main__":

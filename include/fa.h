@@ -26,14 +26,18 @@
  *     last error on the calling thread is available from fa_last_error().
  *   - q, k, v and out share one layout and one 16-bit storage type.
  *       FA_BNSD: [B][N][S][D]    FA_BSND: [B][S][N][D]   (both contiguous)
+ *       FA_TND:  [T][N][D], the B sequences packed end to end (developer
+ *                guide 1.3); q_seq / kv_seq are then the totals Q_T / KV_T
+ *                and cu_seqlens_q / cu_seqlens_kv give the boundaries.
  *     BSH is BSND with H = N*D.  Base pointers must be 16-byte aligned.
  *   - k and v are either contiguous in that layout (FA_KV_CONTIGUOUS) or a
  *     paged cache (FA_KV_PAGED_*, decode only; see fa_params.kv_layout).
  *   - Query head n1 reads KV head n1 / g with g = num_heads / num_kv_heads:
  *     g consecutive query heads share one KV head (FlashAttn developer guide,
  *     1.1 MHA and GQA).
- *   - lse is float32 [B][num_heads][q_seq] in every layout, natural log:
- *     lse = log(sum_j exp(s_j - m)) + m (developer guide, 1.6 LSE).
+ *   - lse is float32 [B][num_heads][q_seq] in BNSD and BSND and [Q_T][num_heads]
+ *     in TND (developer guide 1.6 gives both shapes), natural log:
+ *     lse = log(sum_j exp(s_j - m)) + m.
  *   - A row with no valid key (length 0, or every key masked) writes out = 0
  *     and lse = +inf (developer guide, 1.7 RowInvalid).
  *   - Output stores round to nearest even from fp32.
@@ -58,7 +62,7 @@ typedef enum {
     FA_ERR_RUNTIME = 4         /* the HIP runtime refused a launch */
 } fa_status;
 
-typedef enum { FA_BNSD = 0, FA_BSND = 1 } fa_layout;
+typedef enum { FA_BNSD = 0, FA_BSND = 1, FA_TND = 2 } fa_layout;
 typedef enum { FA_F16 = 0, FA_BF16 = 1 } fa_dtype;
 
 /* Mask modes (developer guide 1.5: 0 = none, 3 = causal, 4 = window; IFA
@@ -128,6 +132,23 @@ typedef struct {
      * Values below -1 are invalid.  Tiles wholly outside the band are skipped. */
     int64_t win_left;
     int64_t win_right;
+    /* FA_TND only (must be NULL otherwise), device int32 (developer guide 1.4):
+     *   cu_seqlens_q, cu_seqlens_kv: [batch + 1], starting at 0 and
+     *     non-decreasing; sequence b owns q rows [cu_q[b], cu_q[b+1]) and kv
+     *     rows [cu_kv[b], cu_kv[b+1]); cu_q[batch] <= q_seq, cu_kv[batch] <= kv_seq.
+     *     The kernels clamp every offset into its tensor, so malformed values
+     *     give wrong rows, never out-of-bounds accesses.
+     *   seqused_q: [batch] or NULL: query rows of sequence b actually used;
+     *     the shorter of it and the sequence length takes effect.
+     * actual_seq_lengths (int64) truncates each sequence's keys the same way.
+     * Query rows not used by any sequence (past seqused_q, or past
+     * cu_seqlens_q[batch]) are written as 0 with lse = +inf, the output
+     * initialisation the developer guide describes.  TND always runs the
+     * prefill kernel, needs batch <= 16383 and a workspace of
+     * fa_workspace_size bytes for its work list, and no paged cache. */
+    const int32_t *cu_seqlens_q;
+    const int32_t *cu_seqlens_kv;
+    const int32_t *seqused_q;
 } fa_params;
 
 /* fa_workspace_size -- phase 1 of fa_fwd (the two-phase shape of the IFA guide,
@@ -142,7 +163,9 @@ fa_status fa_workspace_size(const fa_params *p, size_t *bytes);
  * runs the split-KV decode (stage 1 + combine, or stage 1 alone when one split
  * suffices), whose split plan the library chooses (see fa_splitkv_plan); the
  * workspace must then be at least fa_workspace_size bytes, 256-byte aligned.
- * Every other case runs the prefill kernel and needs no workspace. */
+ * Every other case runs the prefill kernel and needs no workspace, except
+ * the packed layout FA_TND, which needs fa_workspace_size bytes (256-byte
+ * aligned) for the cost-ordered list of its query tiles. */
 fa_status fa_fwd(const fa_params *p, const void *q, const void *k, const void *v,
                  void *out, float *lse, void *workspace, size_t workspace_bytes,
                  void *stream);

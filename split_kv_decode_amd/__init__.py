@@ -20,7 +20,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfa_mi355x.so")
 
 FA_OK, FA_ERR_NULLPTR, FA_ERR_PARAM_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_RUNTIME = range(5)
-FA_BNSD, FA_BSND = 0, 1
+FA_BNSD, FA_BSND, FA_TND = 0, 1, 2
+LAYOUTS = {"BNSD": FA_BNSD, "BSND": FA_BSND, "TND": FA_TND}
 FA_F16, FA_BF16 = 0, 1
 FA_MASK_NONE, FA_MASK_CAUSAL, FA_MASK_BOOL, FA_MASK_WINDOW = 0, 1, 2, 3
 MASK_MODES = {"none": FA_MASK_NONE, "causal": FA_MASK_CAUSAL, "bool": FA_MASK_BOOL,
@@ -48,7 +49,8 @@ class FaParams(ctypes.Structure):
                 ("kv_layout", ctypes.c_int), ("block_table", ctypes.c_void_p),
                 ("block_size", ctypes.c_int64), ("max_blocks_per_seq", ctypes.c_int64),
                 ("num_blocks", ctypes.c_int64), ("win_left", ctypes.c_int64),
-                ("win_right", ctypes.c_int64)]
+                ("win_right", ctypes.c_int64), ("cu_seqlens_q", ctypes.c_void_p),
+                ("cu_seqlens_kv", ctypes.c_void_p), ("seqused_q", ctypes.c_void_p)]
 
 
 _lock = threading.Lock()
@@ -110,11 +112,13 @@ def make_params(batch, num_heads, q_seq, kv_seq, head_dim, *, num_kv_heads=0, la
                 dtype="bf16", scale=1.0, actual_seq_lengths=None, mask_mode="none", mask=None,
                 mask_stride: Sequence[int] = (0, 0, 0, 0), kv_layout="contiguous", block_table=None,
                 block_size=0, max_blocks_per_seq=0, num_blocks=0, win_left=-1,
-                win_right=-1) -> FaParams:
+                win_right=-1, cu_seqlens_q=None, cu_seqlens_kv=None, seqused_q=None) -> FaParams:
     p = FaParams()
     p.batch, p.num_heads, p.num_kv_heads = batch, num_heads, num_kv_heads
     p.q_seq, p.kv_seq, p.head_dim = q_seq, kv_seq, head_dim
-    p.layout = {"BNSD": FA_BNSD, "BSND": FA_BSND}[layout] if isinstance(layout, str) else layout
+    p.layout = LAYOUTS[layout] if isinstance(layout, str) else layout
+    p.cu_seqlens_q, p.cu_seqlens_kv = _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv)
+    p.seqused_q = _ptr(seqused_q)
     p.dtype = {"f16": FA_F16, "bf16": FA_BF16}[dtype] if isinstance(dtype, str) else dtype
     p.scale = float(scale)
     p.actual_seq_lengths = _ptr(actual_seq_lengths)
@@ -163,21 +167,30 @@ def fa_combine(params: FaParams, num_splits, o_part, m_part, l_part, out, lse=No
 
 def params_for(q, k, *, layout="BNSD", num_kv_heads=0, scale=1.0, actual_seq_lengths=None,
                mask=None, mask_stride=(0, 0, 0, 0), causal=False, kv_layout="contiguous",
-               block_table=None, window=None) -> FaParams:
+               block_table=None, window=None, cu_seqlens_q=None, cu_seqlens_kv=None,
+               seqused_q=None) -> FaParams:
     """FaParams from torch tensors q, k in ``layout`` (shapes as in include/fa.h).
 
     With a paged ``kv_layout`` k is [num_blocks, block_size, KV_N, D] (PA_BBND) or
     [num_blocks, KV_N, block_size, D] (PA_BNBD), block_table is int32
     [B, max_blocks_per_seq], and kv_seq is max_blocks_per_seq * block_size.
     ``window=(win_left, win_right)`` selects the window mask (-1 = unbounded side).
+    With ``layout="TND"`` q is [Q_T, N, D], k is [KV_T, KV_N, D] and the int32
+    cu_seqlens_q / cu_seqlens_kv ([B + 1]) and seqused_q ([B]) are device tensors.
     """
     import torch
-    if layout == "BNSD":
+    extra = {}
+    if layout == "TND":
+        QS, N, D = q.shape
+        B = cu_seqlens_q.shape[0] - 1
+        extra = dict(cu_seqlens_q=cu_seqlens_q, cu_seqlens_kv=cu_seqlens_kv, seqused_q=seqused_q)
+    elif layout == "BNSD":
         B, N, QS, D = q.shape
     else:
         B, QS, N, D = q.shape
-    extra = {}
-    if kv_layout == "contiguous":
+    if layout == "TND":
+        KVS, KVN = k.shape[0], k.shape[1]
+    elif kv_layout == "contiguous":
         KVN, KVS = (k.shape[1], k.shape[2]) if layout == "BNSD" else (k.shape[2], k.shape[1])
     else:
         nb, bs, KVN = ((k.shape[0], k.shape[1], k.shape[2]) if kv_layout == "PA_BBND"
@@ -197,17 +210,19 @@ def params_for(q, k, *, layout="BNSD", num_kv_heads=0, scale=1.0, actual_seq_len
 
 def fwd(q, k, v, *, layout="BNSD", scale=None, actual_seq_lengths=None, mask=None,
         mask_stride=(0, 0, 0, 0), causal=False, return_lse=False, stream=None,
-        kv_layout="contiguous", block_table=None, window=None):
+        kv_layout="contiguous", block_table=None, window=None, cu_seqlens_q=None,
+        cu_seqlens_kv=None, seqused_q=None):
     """Attention forward on device tensors; allocates out (and lse, workspace) with torch."""
     import torch
     D = q.shape[-1]
     sc = (1.0 / math.sqrt(D)) if scale is None else scale
     p = params_for(q, k, layout=layout, scale=sc, actual_seq_lengths=actual_seq_lengths,
                    mask=mask, mask_stride=mask_stride, causal=causal, kv_layout=kv_layout,
-                   block_table=block_table, window=window)
+                   block_table=block_table, window=window, cu_seqlens_q=cu_seqlens_q,
+                   cu_seqlens_kv=cu_seqlens_kv, seqused_q=seqused_q)
     out = torch.empty_like(q)
-    lse = (torch.empty((p.batch, p.num_heads, p.q_seq), dtype=torch.float32, device=q.device)
-           if return_lse else None)
+    lse_shape = (p.q_seq, p.num_heads) if layout == "TND" else (p.batch, p.num_heads, p.q_seq)
+    lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device) if return_lse else None
     nbytes = fa_workspace_size(p)
     ws = torch.empty((nbytes,), dtype=torch.uint8, device=q.device) if nbytes else None
     s = stream if stream is not None else torch.cuda.current_stream()

@@ -60,7 +60,21 @@ fa_status check_params(const fa_params* p, Shape* s) {
         return fail(FA_ERR_PARAM_INVALID, "head_dim must be a positive multiple of 16 up to 512, got %lld",
                     (long long)p->head_dim);
     }
-    if (p->layout != FA_BNSD && p->layout != FA_BSND) return fail(FA_ERR_PARAM_INVALID, "unknown layout %d", (int)p->layout);
+    if (p->layout != FA_BNSD && p->layout != FA_BSND && p->layout != FA_TND)
+        return fail(FA_ERR_PARAM_INVALID, "unknown layout %d", (int)p->layout);
+    if (p->layout == FA_TND) {
+        if (!p->cu_seqlens_q || !p->cu_seqlens_kv)
+            return fail(FA_ERR_NULLPTR, "the TND layout needs cu_seqlens_q and cu_seqlens_kv");
+        if (p->batch > fa::kVarlenMaxBatch)
+            return fail(FA_ERR_PARAM_INVALID, "the TND layout takes at most %d sequences, got %lld",
+                        fa::kVarlenMaxBatch, (long long)p->batch);
+        if (p->kv_layout != FA_KV_CONTIGUOUS)
+            return fail(FA_ERR_UNSUPPORTED, "a paged KV cache with the TND layout is not built");
+        if (p->mask_mode == FA_MASK_BOOL)
+            return fail(FA_ERR_UNSUPPORTED, "a boolean mask tensor with the TND layout is not built");
+    } else if (p->cu_seqlens_q || p->cu_seqlens_kv || p->seqused_q) {
+        return fail(FA_ERR_PARAM_INVALID, "cu_seqlens / seqused_q are for the TND layout only");
+    }
     if (p->dtype != FA_F16 && p->dtype != FA_BF16) return fail(FA_ERR_PARAM_INVALID, "unknown dtype %d", (int)p->dtype);
     if (!std::isfinite(p->scale)) return fail(FA_ERR_PARAM_INVALID, "scale must be finite");
     if (p->mask_mode != FA_MASK_NONE && p->mask_mode != FA_MASK_CAUSAL && p->mask_mode != FA_MASK_BOOL &&
@@ -108,9 +122,9 @@ fa_status check_params(const fa_params* p, Shape* s) {
     s->g = p->num_heads / kvn;
     if (s->B * s->QN > kMaxDim || s->B * kvn > kMaxDim)
         return fail(FA_ERR_PARAM_INVALID, "batch * heads must stay below 2^31");
-    const double qe = double(s->B) * double(s->QN) * double(s->QS) * double(s->D);
+    const double qe = (p->layout == FA_TND ? 1.0 : double(s->B)) * double(s->QN) * double(s->QS) * double(s->D);
     const double ke = p->kv_layout == FA_KV_CONTIGUOUS
-                          ? double(s->B) * double(s->KVN) * double(s->KVS) * double(s->D)
+                          ? (p->layout == FA_TND ? 1.0 : double(s->B)) * double(s->KVN) * double(s->KVS) * double(s->D)
                           : double(p->num_blocks) * double(p->block_size) * double(s->KVN) * double(s->D);
     if (qe >= double(kMaxElems) || ke >= double(kMaxElems)) return fail(FA_ERR_PARAM_INVALID, "tensor too large");
     return ok();
@@ -183,7 +197,15 @@ void plan_splits(const fa_params* p, const Shape& s, int num_cus, int64_t* split
     *splits = (s.KVS + c - 1) / c;
 }
 
-bool decode_path(const fa_params* p) { return p->q_seq == 1 && p->mask_mode == FA_MASK_NONE; }
+bool decode_path(const fa_params* p) {
+    return p->q_seq == 1 && p->mask_mode == FA_MASK_NONE && p->layout != FA_TND;
+}
+
+// Packed layout: entries of the cost-ordered work list, one per 128-row query
+// tile of every sequence plus the rows past the last sequence.  The sum over
+// the B + 1 sequences of ceil(rows / 128) is at most ceil(Q_T / 128) + B + 1.
+int64_t varlen_capacity(const Shape& s) { return (s.QS + 127) / 128 + s.B + 1; }
+size_t varlen_bytes(const Shape& s) { return round_up(size_t(varlen_capacity(s)) * 8, 256); }
 
 void fill_decode_args(const fa_params* p, const Shape& s, fa::DecodeArgs* a) {
     std::memset(a, 0, sizeof *a);
@@ -260,7 +282,7 @@ fa_status run_combine(const fa_params* p, const Shape& s, int64_t splits, const 
 }
 
 fa_status run_prefill(const fa_params* p, const Shape& s, const void* q, const void* k, const void* v, void* out,
-                      float* lse, hipStream_t stream) {
+                      float* lse, void* workspace, hipStream_t stream) {
     // The prefill kernel addresses one 64-row KV tile with 32-bit byte offsets.
     const int64_t kv_row_elems = p->layout == FA_BNSD ? s.D : s.KVN * s.D;
     if (kv_row_elems * 2 * 64 >= (int64_t(1) << 31))
@@ -292,6 +314,14 @@ fa_status run_prefill(const fa_params* p, const Shape& s, const void* q, const v
         a.kv_stride_n = s.D;
         a.kv_stride_b = s.KVS * s.KVN * s.D;
     }
+    if (p->layout == FA_TND) {  // [T][N][D]: rows of a sequence are BSND rows
+        a.q_stride_s = s.QN * s.D;
+        a.q_stride_n = s.D;
+        a.q_stride_b = 0;
+        a.kv_stride_s = s.KVN * s.D;
+        a.kv_stride_n = s.D;
+        a.kv_stride_b = 0;
+    }
     a.num_heads = (int32_t)s.QN;
     a.num_kv_heads = (int32_t)s.KVN;
     a.group = (int32_t)s.g;
@@ -314,6 +344,30 @@ fa_status run_prefill(const fa_params* p, const Shape& s, const void* q, const v
         const bool rows_ok = st[3] == 1 && aligned(p->mask, 16) && st[0] % 16 == 0 && st[1] % 16 == 0 &&
                              st[2] % 16 == 0 && s.KVS % 16 == 0 && st[2] < (int64_t(1) << 23);
         if (rows_ok) mm = 3;
+    }
+    if (p->layout == FA_TND) {
+        fa::VarlenScheduleArgs sa;
+        std::memset(&sa, 0, sizeof sa);
+        sa.cu_q = p->cu_seqlens_q;
+        sa.cu_kv = p->cu_seqlens_kv;
+        sa.used_q = p->seqused_q;
+        sa.lens = p->actual_seq_lengths;
+        sa.work = static_cast<int32_t*>(workspace);
+        sa.q_total = s.QS;
+        sa.kv_total = s.KVS;
+        sa.batch = (int32_t)s.B;
+        sa.capacity = (int32_t)varlen_capacity(s);
+        sa.mask_mode = mm;
+        sa.win_left = a.win_left;
+        sa.win_right = a.win_right;
+        fa_status st = launch_result(fa::launch_varlen_schedule(sa, stream), "packed-batch schedule");
+        if (st != FA_OK) return st;
+        a.cu_q = p->cu_seqlens_q;
+        a.cu_kv = p->cu_seqlens_kv;
+        a.used_q = p->seqused_q;
+        a.work = sa.work;
+        a.work_items = sa.capacity;
+        a.batch = (int32_t)s.B;
     }
     return launch_result(fa::launch_prefill(a, p->dtype == FA_BF16 ? 1 : 0, (int)s.D, mm, s.B, stream), "prefill");
 }
@@ -356,6 +410,10 @@ fa_status fa_workspace_size(const fa_params* p, size_t* bytes) {
     if (st != FA_OK) return st;
     if (!bytes) return fail(FA_ERR_NULLPTR, "bytes output must not be NULL");
     *bytes = 0;
+    if (p->layout == FA_TND) {
+        *bytes = varlen_bytes(s);
+        return ok();
+    }
     if (!decode_path(p)) return ok();
     int64_t sp, c;
     plan_splits(p, s, device_cus(), &sp, &c);
@@ -371,7 +429,14 @@ fa_status fa_fwd(const fa_params* p, const void* q, const void* k, const void* v
     st = check_tensors(q, k, v, out, lse);
     if (st != FA_OK) return st;
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    if (!decode_path(p)) return run_prefill(p, s, q, k, v, out, lse, hs);
+    if (p->layout == FA_TND) {
+        const size_t need = varlen_bytes(s);
+        if (!workspace) return fail(FA_ERR_NULLPTR, "the TND layout needs %zu bytes of workspace (fa_workspace_size)", need);
+        if (!aligned(workspace, 256)) return fail(FA_ERR_PARAM_INVALID, "workspace must be 256-byte aligned");
+        if (workspace_bytes < need)
+            return fail(FA_ERR_PARAM_INVALID, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+    }
+    if (!decode_path(p)) return run_prefill(p, s, q, k, v, out, lse, workspace, hs);
 
     int64_t sp, c;
     plan_splits(p, s, device_cus(), &sp, &c);
@@ -396,6 +461,7 @@ fa_status fa_decode_splitkv(const fa_params* p, int64_t num_splits, int64_t chun
     Shape s;
     fa_status st = check_params(p, &s);
     if (st != FA_OK) return st;
+    if (p->layout == FA_TND) return fail(FA_ERR_UNSUPPORTED, "split-KV decode is built for BNSD and BSND");
     if (p->q_seq != 1) return fail(FA_ERR_PARAM_INVALID, "split-KV decode needs q_seq == 1, got %lld", (long long)p->q_seq);
     if (p->mask_mode != FA_MASK_NONE) return fail(FA_ERR_PARAM_INVALID, "split-KV decode takes no mask");
     if (!q || !k || !v) return fail(FA_ERR_NULLPTR, "q, k and v must not be NULL");
@@ -421,6 +487,7 @@ fa_status fa_combine(const fa_params* p, int64_t num_splits, const float* o_part
     Shape s;
     fa_status st = check_params(p, &s);
     if (st != FA_OK) return st;
+    if (p->layout == FA_TND) return fail(FA_ERR_UNSUPPORTED, "combine is built for BNSD and BSND");
     if (p->q_seq != 1) return fail(FA_ERR_PARAM_INVALID, "combine needs q_seq == 1, got %lld", (long long)p->q_seq);
     if (!o_part || !m_part || !l_part) return fail(FA_ERR_NULLPTR, "o_part, m_part and l_part must not be NULL");
     if (!out) return fail(FA_ERR_NULLPTR, "out must not be NULL");

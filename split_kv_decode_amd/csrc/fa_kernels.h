@@ -67,7 +67,61 @@ struct PrefillArgs {
     float scale_log2;
     int32_t win_left;         // window mask: keys qrow - win_left .. qrow + win_right kept;
     int32_t win_right;        // 0x7fffffff = unbounded on that side
+    // Packed layout (work != null): sequence b spans q rows [cu_q[b], cu_q[b+1])
+    // and kv rows [cu_kv[b], cu_kv[b+1]) of the [T][N][D] tensors; q_seq and
+    // kv_seq are the totals.  The work list holds (sequence, 128-row q tile)
+    // pairs, heaviest first; sequence index `batch` stands for the rows past
+    // the last sequence.  Entries (-1, -1) pad the list.
+    const int32_t* cu_q;
+    const int32_t* cu_kv;
+    const int32_t* used_q;    // [batch] or null
+    const int32_t* work;      // [work_items][2]
+    int32_t work_items;
+    int32_t batch;
 };
+
+// Geometry of one packed sequence, with every offset clamped into its tensor.
+struct SeqGeom {
+    int64_t q0, q_full, q_used;  // first q row, rows owned, rows computed
+    int64_t k0, kv_len;          // first kv row, keys visible (after truncation)
+};
+
+__device__ __forceinline__ SeqGeom seq_geometry(const int32_t* cu_q, const int32_t* cu_kv, const int32_t* used_q,
+                                                const int64_t* lens, int64_t b, int64_t batch, int64_t q_total,
+                                                int64_t kv_total) {
+    auto clampi = [](int64_t x, int64_t lo, int64_t hi) { return x < lo ? lo : (x > hi ? hi : x); };
+    SeqGeom g;
+    if (b >= batch) {  // rows past the last sequence: owned, never computed
+        g.q0 = clampi(cu_q[batch], 0, q_total);
+        g.q_full = q_total - g.q0;
+        g.q_used = 0;
+        g.k0 = 0;
+        g.kv_len = 0;
+        return g;
+    }
+    g.q0 = clampi(cu_q[b], 0, q_total);
+    g.q_full = clampi(cu_q[b + 1], g.q0, q_total) - g.q0;
+    g.q_used = used_q ? clampi(used_q[b], 0, g.q_full) : g.q_full;
+    g.k0 = clampi(cu_kv[b], 0, kv_total);
+    g.kv_len = clampi(cu_kv[b + 1], g.k0, kv_total) - g.k0;
+    if (lens) g.kv_len = clampi(lens[b], 0, g.kv_len);
+    return g;
+}
+
+// Cost-ordered work list of a packed batch (one workgroup of 1024 threads).
+struct VarlenScheduleArgs {
+    const int32_t* cu_q;
+    const int32_t* cu_kv;
+    const int32_t* used_q;
+    const int64_t* lens;
+    int32_t* work;            // [capacity][2]
+    int64_t q_total, kv_total;
+    int32_t batch;
+    int32_t capacity;
+    int32_t mask_mode;        // prefill mask instantiation (1 causal, 4 window: fewer tiles)
+    int32_t win_left, win_right;
+};
+constexpr int kVarlenMaxBatch = 16383;
 
 // Block ids one paged stage-1 workgroup stages in LDS: a chunk may touch at most
 // this many blocks.
@@ -79,5 +133,6 @@ hipError_t launch_decode_stage1(const DecodeArgs& a, int dtype, int head_dim, in
 hipError_t launch_combine(const CombineArgs& a, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int mask_mode,
                           int64_t batch, hipStream_t stream);
+hipError_t launch_varlen_schedule(const VarlenScheduleArgs& a, hipStream_t stream);
 
 }  // namespace fa

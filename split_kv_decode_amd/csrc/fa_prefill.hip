@@ -125,24 +125,56 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     const int half = lane >> 5;
     const int col = lane & 31;
 
-    const int64_t total = (int64_t)gridDim.x;
-    const int64_t work = xcd_remap(blockIdx.x, total);
-    int qt = (int)(work % a.q_tiles);
-    const int64_t bh = work / a.q_tiles;
-    if (MASK == 1) qt = a.q_tiles - 1 - qt;  // longest causal tiles first
-    const int n1 = (int)(bh % a.num_heads);
-    const int64_t b = bh / a.num_heads;
+    int qt, n1;
+    int64_t b, L;
+    int64_t q_used = a.q_seq, q_full = a.q_seq;  // query rows computed / written
+    int64_t q_off, kv_off;                       // element offsets of (b) in q/out and k/v
+    int64_t lse_row0, lse_step;                  // lse index of (n1, row i) = lse_row0 + i * lse_step
+    if (a.work) {
+        // Packed layout: block 8k + x (dispatched to XCD x) takes head k % N of
+        // work item 8*(k / N) + x, so the heaviest items spread over all XCDs
+        // and the heads of one item (which share K/V under GQA) share an L2.
+        const int x = (int)(blockIdx.x & 7);
+        const int64_t kk = blockIdx.x >> 3;
+        const int64_t item = (kk / a.num_heads) * 8 + x;
+        n1 = (int)(kk % a.num_heads);
+        if (item >= a.work_items) return;
+        const int32_t wb = a.work[2 * item];
+        if (wb < 0) return;
+        b = wb;
+        qt = a.work[2 * item + 1];
+        const SeqGeom sg = seq_geometry(a.cu_q, a.cu_kv, a.used_q, a.lens, b, a.batch, a.q_seq, a.kv_seq);
+        q_used = sg.q_used;
+        q_full = sg.q_full;
+        L = sg.kv_len;
+        q_off = sg.q0 * a.q_stride_s;
+        kv_off = sg.k0 * a.kv_stride_s;
+        lse_row0 = sg.q0 * a.num_heads + n1;
+        lse_step = a.num_heads;
+    } else {
+        const int64_t total = (int64_t)gridDim.x;
+        const int64_t work = xcd_remap(blockIdx.x, total);
+        qt = (int)(work % a.q_tiles);
+        const int64_t bh = work / a.q_tiles;
+        if (MASK == 1) qt = a.q_tiles - 1 - qt;  // longest causal tiles first
+        n1 = (int)(bh % a.num_heads);
+        b = bh / a.num_heads;
+        L = a.kv_seq;
+        if (a.lens) {
+            L = a.lens[b];
+            L = L < 0 ? 0 : (L > a.kv_seq ? a.kv_seq : L);
+        }
+        q_off = b * a.q_stride_b;
+        kv_off = b * a.kv_stride_b;
+        lse_row0 = (b * a.num_heads + n1) * a.q_seq;
+        lse_step = 1;
+    }
     const int n2 = n1 / a.group;
 
-    int64_t L = a.kv_seq;
-    if (a.lens) {
-        L = a.lens[b];
-        L = L < 0 ? 0 : (L > a.kv_seq ? a.kv_seq : L);
-    }
     const int64_t i0 = (int64_t)qt * BM;
     const int64_t wrow0 = i0 + 32 * wave;  // first query row of this wave
     const int64_t qrow = wrow0 + col;
-    const bool qvalid = qrow < a.q_seq;
+    const bool qvalid = qrow < q_used;
 
     // Q as the B operand of S^T = K Q^T: lane (col, half) holds row qrow,
     // head-dim elements [16*kk + 8*half, +8).  A negative scale is folded in
@@ -150,7 +182,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     // and the row max can be taken before scaling.
     V8 qreg[D / 16];
     {
-        const uint16_t* qp = a.q + b * a.q_stride_b + (int64_t)n1 * a.q_stride_n + qrow * a.q_stride_s;
+        const uint16_t* qp = a.q + q_off + (int64_t)n1 * a.q_stride_n + qrow * a.q_stride_s;
         const uint32_t flip = a.negate_q ? 0x80008000u : 0u;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
@@ -169,7 +201,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     if (MASK == 1 && kv_end > i0 + BM) kv_end = i0 + BM;  // keys beyond the tile's last row
     int jt0 = 0;
     if (MASK == 4) {
-        const int64_t i_last = (i0 + BM < a.q_seq ? i0 + BM : a.q_seq) - 1;
+        const int64_t i_last = (i0 + BM < q_used ? i0 + BM : q_used) - 1;
         if (kv_end > i_last + a.win_right + 1) kv_end = i_last + a.win_right + 1;
         const int64_t key_lo = i0 - a.win_left;
         if (key_lo > 0) jt0 = (int)(key_lo / BN);
@@ -189,8 +221,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     // physical chunk i%CPR, which holds logical chunk (i%CPR) ^ swz(row).  The
     // buffer resource of a tile covers only its rows below the length.
     const int64_t row_bytes = a.kv_stride_s * 2;
-    const char* kbase = reinterpret_cast<const char*>(a.k + b * a.kv_stride_b + (int64_t)n2 * a.kv_stride_n);
-    const char* vbase = reinterpret_cast<const char*>(a.v + b * a.kv_stride_b + (int64_t)n2 * a.kv_stride_n);
+    const char* kbase = reinterpret_cast<const char*>(a.k + kv_off + (int64_t)n2 * a.kv_stride_n);
+    const char* vbase = reinterpret_cast<const char*>(a.v + kv_off + (int64_t)n2 * a.kv_stride_n);
     int voff[NIW];
 #pragma unroll
     for (int w = 0; w < NIW; ++w) {
@@ -207,7 +239,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     if (MASK == 3) {
 #pragma unroll
         for (int w = 0; w < 2; ++w) moff[w] = (int)((w * 64 + lane) * a.mask_stride[2]) + wave * 16;
-        int64_t rv = a.q_seq - i0;
+        int64_t rv = q_used - i0;
         rv = rv > BM ? BM : rv;
         mrec_rows = (int)((rv - 1) * a.mask_stride[2]);
     }
@@ -420,12 +452,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         if (jt + 1 < ntiles) step(jt + 1, sK1, sV1, sM1, sK0, sV0, sM0);
     }
 
-    // Epilogue: divide by l, RowInvalid defaults, store in the q layout.
+    // Epilogue: divide by l, RowInvalid defaults, store in the q layout.  Rows
+    // a packed sequence owns but does not use get the initial 0 / +inf.
     const float l_run = l_half + xor32(l_half);
-    if (qvalid) {
-        const bool empty = (m_run == kNegInf);
+    if (qrow < q_full) {
+        const bool empty = !qvalid || (m_run == kNegInf);
         const float inv = empty ? 0.f : 1.f / l_run;
-        uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + b * a.q_stride_b + (int64_t)n1 * a.q_stride_n +
+        uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + q_off + (int64_t)n1 * a.q_stride_n +
                        qrow * a.q_stride_s;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
@@ -441,8 +474,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
                 *reinterpret_cast<u32x2*>(op + d0) = w;
             }
         }
-        if (half == 0 && a.lse)
-            a.lse[(b * a.num_heads + n1) * a.q_seq + qrow] = empty ? kPosInf : (m_run + log2f(l_run)) * kLn2;
+        if (half == 0 && a.lse) a.lse[lse_row0 + qrow * lse_step] = empty ? kPosInf : (m_run + log2f(l_run)) * kLn2;
     }
 }
 
@@ -462,7 +494,8 @@ static hipError_t dispatch_prefill(const PrefillArgs& a, int mask_mode, int64_t 
 
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int mask_mode, int64_t batch,
                           hipStream_t stream) {
-    const int64_t blocks = (int64_t)a.q_tiles * batch * a.num_heads;
+    const int64_t blocks = a.work ? (int64_t)(a.work_items + 7) / 8 * 8 * a.num_heads
+                                  : (int64_t)a.q_tiles * batch * a.num_heads;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (dtype == 1) {

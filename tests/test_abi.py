@@ -165,3 +165,42 @@ def test_paged_plan_caps_chunk_to_the_lds_table(lib):
         fa.fa_splitkv_plan(p, num_cus=256, chunk_hint=1024 * 16)
     st = lib.fa_decode_splitkv(ctypes.byref(p), 2, 1024 * 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
     assert st == fa.FA_ERR_PARAM_INVALID and "exceeds" in fa.fa_last_error()
+
+
+# ---------------------------------------------------------------- packed layout (TND)
+
+def tnd(**kw):
+    base = dict(batch=4, q_seq=1000, kv_seq=1200, layout="TND", cu_seqlens_q=FAKE,
+                cu_seqlens_kv=FAKE, mask_mode="causal")
+    base.update(kw)
+    return params(**base)
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(cu_seqlens_q=None), fa.FA_ERR_NULLPTR, "cu_seqlens"),
+    (dict(cu_seqlens_kv=None), fa.FA_ERR_NULLPTR, "cu_seqlens"),
+    (dict(batch=16384), fa.FA_ERR_PARAM_INVALID, "at most"),
+    (dict(mask_mode="bool", mask=FAKE, mask_stride=(0, 0, 1, 1)), fa.FA_ERR_UNSUPPORTED, "boolean"),
+    (dict(kv_layout="PA_BBND", block_table=FAKE, block_size=16, max_blocks_per_seq=100,
+          num_blocks=100, actual_seq_lengths=FAKE), fa.FA_ERR_UNSUPPORTED, "paged"),
+    (dict(layout="BSND"), fa.FA_ERR_PARAM_INVALID, "TND layout only"),
+])
+def test_tnd_params_validated(lib, kw, status, text):
+    p = tnd(**kw)
+    st = lib.fa_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None)
+    assert st == status
+    assert text in fa.fa_last_error()
+
+
+def test_tnd_workspace(lib):
+    p = tnd()
+    # one (sequence, tile) pair per 128-row tile: ceil(1000/128) + 4 + 1 entries of 8 bytes
+    assert fa.fa_workspace_size(p) == 256
+    assert fa.fa_workspace_size(tnd(q_seq=1 << 20, batch=1000)) == ((8192 + 1001) * 8 + 255) // 256 * 256
+    st = lib.fa_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, 0, None)
+    assert st == fa.FA_ERR_NULLPTR and "workspace" in fa.fa_last_error()
+    st = lib.fa_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE, 64, None)
+    assert st == fa.FA_ERR_PARAM_INVALID and "too small" in fa.fa_last_error()
+    pd = tnd(q_seq=4, mask_mode="none")
+    st = lib.fa_decode_splitkv(ctypes.byref(pd), 1, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == fa.FA_ERR_UNSUPPORTED

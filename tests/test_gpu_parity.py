@@ -485,6 +485,96 @@ def test_window_4k_sampled():
     check(rows_of(out, s, rows), to_np(lse).reshape(-1)[rows], ref, ref_lse, "window 4k")
 
 
+# ------------------------------------------------------------------ packed variable length (TND)
+
+def run_packed(x, mode="none", window=None, seqused_q=None, kv_lens=None, extra_rows=0):
+    """fa_fwd on packed inputs; extra_rows appends q rows owned by no sequence."""
+    q_bits = x.q
+    if extra_rows:
+        pad = fa_synth.round_bits(np.ones((extra_rows, x.QN, x.D), np.float32), x.dtype)
+        q_bits = np.concatenate([x.q, pad])
+    q, k, v = dev16(q_bits, x.dtype), dev16(x.k, x.dtype), dev16(x.v, x.dtype)
+    t32 = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(DEV)
+    lens_t = None if kv_lens is None else torch.from_numpy(np.asarray(kv_lens, np.int64)).to(DEV)
+    out, lse = fa.fwd(q, k, v, layout="TND", scale=x.scale, causal=(mode == "causal"),
+                      window=window, actual_seq_lengths=lens_t, cu_seqlens_q=t32(x.cu_q),
+                      cu_seqlens_kv=t32(x.cu_kv), seqused_q=t32(seqused_q), return_lse=True)
+    torch.cuda.synchronize()
+    return out, lse, q_bits
+
+
+def packed_prob(x, q_total, mode="none", window=(-1, -1), seqused_q=None, kv_lens=None):
+    return oracle.Problem(len(x.cu_q) - 1, x.QN, x.KVN, q_total, int(x.cu_kv[-1]), x.D, "TND",
+                          x.dtype, x.scale, kv_lens, mode, window=window, cu_seqlens_q=x.cu_q,
+                          cu_seqlens_kv=x.cu_kv, seqused_q=seqused_q)
+
+
+PACKED_CASES = [
+    (dict(B=5, QN=4, KVN=2, D=128, q_lens=(1, 300)), "none", None),
+    (dict(B=5, QN=4, KVN=2, D=128, q_lens=(1, 300)), "causal", None),
+    (dict(B=4, QN=8, KVN=2, D=128, q_lens=(1, 200), kv_lens=(0, 500)), "causal", None),
+    (dict(B=3, QN=2, KVN=2, D=64, dtype="f16", std=0.5, q_lens=(100, 400)), "window", (50, 10)),
+    (dict(B=7, QN=2, KVN=1, D=128, q_lens=(0, 3)), "none", None),                 # tiny and empty
+    (dict(B=2, QN=2, KVN=2, D=64, q_lens=(129, 260), scale=-0.1), "causal", None),
+]
+
+
+@pytest.mark.parametrize("case,mode,window", PACKED_CASES,
+                         ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()) if isinstance(c, dict) else str(c))
+def test_packed_matches_oracle(case, mode, window):
+    x = fa_synth.make_packed(seed=111, **case)
+    out, lse, q_bits = run_packed(x, mode, window)
+    prob = packed_prob(x, int(x.cu_q[-1]), mode, window or (-1, -1))
+    ref, ref_lse = oracle.attention(prob, q_bits, x.k, x.v)
+    check(to_np(out).reshape(-1, x.D), to_np(lse).reshape(-1), ref.reshape(-1, x.D),
+          ref_lse.reshape(-1), f"packed {case} {mode}")
+
+
+def test_packed_truncation_and_unowned_rows():
+    """seqused_q, KV lengths, an empty sequence and q rows past the last sequence
+    (written as 0 with lse +inf)."""
+    x = fa_synth.make_packed(4, 4, 2, 128, q_lens=(0, 300), seed=112)
+    used = np.array([5, 0, 1000, 130], np.int32)
+    kv_lens = np.array([300, 7, 0, 64], np.int64)
+    out, lse, q_bits = run_packed(x, "causal", seqused_q=used, kv_lens=kv_lens, extra_rows=77)
+    prob = packed_prob(x, q_bits.shape[0], "causal", seqused_q=used, kv_lens=kv_lens)
+    ref, ref_lse = oracle.attention(prob, q_bits, x.k, x.v)
+    got = to_np(out).reshape(-1, x.D)
+    check(got, to_np(lse).reshape(-1), ref.reshape(-1, x.D), ref_lse.reshape(-1), "packed trunc")
+    tail = got.reshape(-1, x.QN, x.D)[int(x.cu_q[-1]):]
+    assert np.all(tail == 0) and torch.all(torch.isposinf(lse[int(x.cu_q[-1]):]))
+
+
+def test_packed_equals_each_sequence_alone():
+    """Every sequence of the packed batch gives, bit for bit, the BSND kernel on that
+    sequence alone: same tiles, same order, same arithmetic."""
+    x = fa_synth.make_packed(5, 8, 2, 128, q_lens=(1, 400), seed=113)
+    out, lse, _ = run_packed(x, "causal")
+    for b in range(5):
+        q0, q1, k0, k1 = (int(v) for v in (x.cu_q[b], x.cu_q[b + 1], x.cu_kv[b], x.cu_kv[b + 1]))
+        if q1 == q0:
+            continue
+        q = dev16(x.q[None, q0:q1], x.dtype)
+        k, v = dev16(x.k[None, k0:k1], x.dtype), dev16(x.v[None, k0:k1], x.dtype)
+        o1, l1 = fa.fwd(q, k, v, layout="BSND", scale=x.scale, causal=True, return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(out[q0:q1], o1[0])
+        assert torch.equal(lse[q0:q1], l1[0].transpose(0, 1))
+
+
+def test_workload_prefill_varlen_sampled():
+    x = fa_synth.make_packed(**fa_synth.PACKED_WORKLOADS["prefill_varlen"])
+    out, lse, _ = run_packed(x, "causal")
+    T = int(x.cu_q[-1])
+    rng = np.random.default_rng(13)
+    # rows t*QN + n1: every sequence's first and last row plus a random sample
+    ts = np.concatenate([x.cu_q[:-1], x.cu_q[1:] - 1, rng.integers(0, T, 1500)])
+    rows = np.unique(ts.astype(np.int64) * x.QN + rng.integers(0, x.QN, ts.size))
+    ref, ref_lse = oracle.attention_rows(packed_prob(x, T, "causal"), x.q, x.k, x.v, rows)
+    got = to_np(out).reshape(-1, x.D)[rows]
+    check(got, to_np(lse).reshape(-1)[rows], ref, ref_lse, "prefill_varlen")
+
+
 # ------------------------------------------------------------------ the five workloads
 
 def test_workload_prefill_small_full():

@@ -239,7 +239,8 @@ def extra_workloads(fa, fa_synth, np, torch, dev16, stream, warmup=3, iters=10):
     cases = [("prefill_small", None, None), ("decode_gqa", None, None),
              ("decode_gqa", None, ("PA_BBND", 128)), ("decode_128k", None, ("PA_BNBD", 128)),
              ("prefill_causal", "bool", None), ("prefill_causal", "causal", None),
-             ("prefill_4k", "window", None), ("prefill_gqa_long", None, None)]
+             ("prefill_4k", "window", None), ("prefill_gqa_long", None, None),
+             ("prefill_4k_d256", None, None)]
     window = (1024, 0)  # sliding window of the last 1025 keys
     for name, mode, paging in cases:
         inp = fa_synth.make(fa_synth.WORKLOADS[name])

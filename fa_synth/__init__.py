@@ -142,6 +142,11 @@ WORKLOADS = {
 WORKLOADS["prefill_4k"] = WORKLOADS["prefill_causal"].with_(
     name="prefill_4k", mask="none", seed=1004,
     doc="mask-free prefill, BSND, B=2, N=32, S=4096, D=128, bf16 N(0,1)")
+# The same flop count with the head dimension of the 256-wide rows of the
+# FlashAttn guide's configuration table.
+WORKLOADS["prefill_4k_d256"] = WORKLOADS["prefill_4k"].with_(
+    name="prefill_4k_d256", QN=16, KVN=16, D=256, seed=1007,
+    doc="mask-free prefill, BSND, B=2, N=16, S=4096, D=256, bf16 N(0,1)")
 
 
 @dataclass

@@ -58,7 +58,7 @@ typedef enum {
     FA_OK = 0,
     FA_ERR_NULLPTR = 1,        /* a required pointer is NULL */
     FA_ERR_PARAM_INVALID = 2,  /* shapes, sizes, options or alignment out of range */
-    FA_ERR_UNSUPPORTED = 3,    /* valid on the pages but not built here (e.g. head_dim 256) */
+    FA_ERR_UNSUPPORTED = 3,    /* valid on the pages but not built here (e.g. head_dim 192) */
     FA_ERR_RUNTIME = 4         /* the HIP runtime refused a launch */
 } fa_status;
 
@@ -94,7 +94,7 @@ typedef struct {
     int64_t num_kv_heads;     /* KV_N; 0 means num_heads (IFA guide 4); must divide Q_N */
     int64_t q_seq;            /* Q_S >= 1 */
     int64_t kv_seq;           /* KV_S >= 1: the padded cache length */
-    int64_t head_dim;         /* D: 64 or 128 built */
+    int64_t head_dim;         /* D: 64, 128 and 256 built */
     fa_layout layout;
     fa_dtype dtype;
     double scale;             /* softmax scale, finite (the pages default it to 1.0) */

@@ -54,9 +54,9 @@ fa_status check_params(const fa_params* p, Shape* s) {
                     (long long)p->num_heads, (long long)kvn);
     if (p->q_seq < 1 || p->q_seq >= kMaxDim) return fail(FA_ERR_PARAM_INVALID, "q_seq must be in [1, 2^31), got %lld", (long long)p->q_seq);
     if (p->kv_seq < 1 || p->kv_seq >= kMaxDim) return fail(FA_ERR_PARAM_INVALID, "kv_seq must be in [1, 2^31), got %lld", (long long)p->kv_seq);
-    if (p->head_dim != 64 && p->head_dim != 128) {
+    if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256) {
         if (p->head_dim > 0 && p->head_dim <= 512 && p->head_dim % 16 == 0)
-            return fail(FA_ERR_UNSUPPORTED, "head_dim %lld is not built (64 and 128 are)", (long long)p->head_dim);
+            return fail(FA_ERR_UNSUPPORTED, "head_dim %lld is not built (64, 128 and 256 are)", (long long)p->head_dim);
         return fail(FA_ERR_PARAM_INVALID, "head_dim must be a positive multiple of 16 up to 512, got %lld",
                     (long long)p->head_dim);
     }

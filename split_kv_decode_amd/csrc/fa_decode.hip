@@ -9,8 +9,8 @@
 //
 // Decode reads every cached K/V byte once and does ~2 FMAs per byte, so it is
 // bound by HBM bandwidth.  The kernel is laid out for that: D/8 lanes cover one
-// 16-byte-per-lane KV row, so one wave load instruction reads 4 (D=128) or
-// 8 (D=64) whole rows = 1 KiB contiguous in the BNSD layout; the K and V of
+// 16-byte-per-lane KV row, so one wave load instruction reads 2 (D=256), 4
+// (D=128) or 8 (D=64) whole rows = 1 KiB contiguous in the BNSD layout; the K and V of
 // the next two iterations are in flight while the current rows are consumed; the
 // dot product is reduced across the row's lanes with DPP moves.  Each lane
 // group (the lanes of one row slot) keeps its own running max / sum / output,
@@ -404,9 +404,11 @@ hipError_t launch_decode_stage1(const DecodeArgs& a, int dtype, int head_dim, in
     if (dtype == 1) {
         if (head_dim == 128) return dispatch_stage1_gh<BF16, 128>(a, heads_per_wg, finish, blocks, stream);
         if (head_dim == 64) return dispatch_stage1_gh<BF16, 64>(a, heads_per_wg, finish, blocks, stream);
+        if (head_dim == 256) return dispatch_stage1_gh<BF16, 256>(a, heads_per_wg, finish, blocks, stream);
     } else {
         if (head_dim == 128) return dispatch_stage1_gh<F16, 128>(a, heads_per_wg, finish, blocks, stream);
         if (head_dim == 64) return dispatch_stage1_gh<F16, 64>(a, heads_per_wg, finish, blocks, stream);
+        if (head_dim == 256) return dispatch_stage1_gh<F16, 256>(a, heads_per_wg, finish, blocks, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -418,10 +420,12 @@ hipError_t launch_combine(const CombineArgs& a, int dtype, int head_dim, hipStre
     if (dtype == 1) {
         if (head_dim == 128) hipLaunchKernelGGL((combine_kernel<BF16, 128>), grid, dim3(256), 0, stream, a);
         else if (head_dim == 64) hipLaunchKernelGGL((combine_kernel<BF16, 64>), grid, dim3(256), 0, stream, a);
+        else if (head_dim == 256) hipLaunchKernelGGL((combine_kernel<BF16, 256>), grid, dim3(256), 0, stream, a);
         else return hipErrorInvalidValue;
     } else {
         if (head_dim == 128) hipLaunchKernelGGL((combine_kernel<F16, 128>), grid, dim3(256), 0, stream, a);
         else if (head_dim == 64) hipLaunchKernelGGL((combine_kernel<F16, 64>), grid, dim3(256), 0, stream, a);
+        else if (head_dim == 256) hipLaunchKernelGGL((combine_kernel<F16, 256>), grid, dim3(256), 0, stream, a);
         else return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -84,18 +84,21 @@ constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i within 8
 constexpr int kDppMirror = 0x140;      // lane i <-> 15-i within 16
 
-// Sum over aligned groups of N lanes (N in {8, 16}); every lane gets the sum.
+__device__ __forceinline__ float shfl_xor(float x, int m) { return __shfl_xor(x, m, 64); }
+
+// Sum over aligned groups of N lanes (N in {8, 16, 32}); every lane gets the
+// sum.  Inside 16-lane rows the steps are DPP moves; the step between two
+// rows goes through a lane permute.
 template <int N>
 __device__ __forceinline__ float group_sum(float x) {
-    static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+    static_assert(N == 8 || N == 16 || N == 32, "group of 8, 16 or 32 lanes");
     x += dpp<kDppXor1>(x);
     x += dpp<kDppXor2>(x);
     x += dpp<kDppHalfMirror>(x);
-    if constexpr (N == 16) x += dpp<kDppMirror>(x);
+    if constexpr (N >= 16) x += dpp<kDppMirror>(x);
+    if constexpr (N == 32) x += shfl_xor(x, 16);
     return x;
 }
-
-__device__ __forceinline__ float shfl_xor(float x, int m) { return __shfl_xor(x, m, 64); }
 
 // 16-byte global load / store helpers.
 __device__ __forceinline__ u32x4 ld128(const void* p) { return *reinterpret_cast<const u32x4*>(p); }

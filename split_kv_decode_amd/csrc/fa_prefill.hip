@@ -89,15 +89,19 @@ __device__ __forceinline__ s16x4 lds_read_tr(const unsigned char* p) {
 // rows x four consecutive chunks (the transposing V reads).
 template <int D>
 __device__ __forceinline__ int swz(int r) {
-    if constexpr (D == 128) {
+    // Rows of 256 and 512 bytes both start at bank 0, so D = 256 shares the
+    // D = 128 pattern (it only permutes the low four chunk bits).
+    if constexpr (D == 128 || D == 256) {
         return ((r & 3) << 2) | ((r >> 2) & 3);
     } else {
         return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
     }
 }
 
+// D = 256 holds 64 + 128 registers of Q and O per lane, so it runs one
+// workgroup per CU with the accumulators in the AGPR half of the file.
 template <typename ST, int D, int MASK>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(PrefillArgs a) {
     using M = Mfma<ST>;
     using V8 = typename M::V8;
     using E = typename M::E;
@@ -350,6 +354,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
                 V8, *reinterpret_cast<const u32x4*>(Kb + krow1 * RB + (((2 * kk + half) ^ ks1) << 4)));
             s[0] = M::mm(ka0, qreg[kk], s[0]);
             s[1] = M::mm(ka1, qreg[kk], s[1]);
+            // D = 256: keep the scheduler from hoisting all 32 K reads ahead
+            // of the MFMAs (register pressure at one wave per SIMD).
+            if constexpr (D == 256)
+                if ((kk & 3) == 3) asm volatile("" ::: "memory");
         }
 
         // Masking is needed only on tiles that cross the length, the causal
@@ -442,6 +450,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
                 const V8 va = __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 o[dt] = M::mm(va, pb[ks], o[dt]);
             }
+            if constexpr (D == 256) asm volatile("" ::: "memory");
         }
 
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of the next tile landed
@@ -501,9 +510,11 @@ hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int mas
     if (dtype == 1) {
         if (head_dim == 128) return dispatch_prefill<BF16, 128>(a, mask_mode, blocks, stream);
         if (head_dim == 64) return dispatch_prefill<BF16, 64>(a, mask_mode, blocks, stream);
+        if (head_dim == 256) return dispatch_prefill<BF16, 256>(a, mask_mode, blocks, stream);
     } else {
         if (head_dim == 128) return dispatch_prefill<F16, 128>(a, mask_mode, blocks, stream);
         if (head_dim == 64) return dispatch_prefill<F16, 64>(a, mask_mode, blocks, stream);
+        if (head_dim == 256) return dispatch_prefill<F16, 256>(a, mask_mode, blocks, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -45,7 +45,7 @@ FAKE = 1 << 20  # a 16-byte-aligned non-null address; never dereferenced (valida
 
 @pytest.mark.parametrize("kw,status,text", [
     (dict(num_heads=6, num_kv_heads=4), fa.FA_ERR_PARAM_INVALID, "multiple"),
-    (dict(head_dim=256), fa.FA_ERR_UNSUPPORTED, "not built"),
+    (dict(head_dim=192), fa.FA_ERR_UNSUPPORTED, "not built"),
     (dict(head_dim=100), fa.FA_ERR_PARAM_INVALID, "head_dim"),
     (dict(batch=0), fa.FA_ERR_PARAM_INVALID, "batch"),
     (dict(q_seq=0), fa.FA_ERR_PARAM_INVALID, "q_seq"),

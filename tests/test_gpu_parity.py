@@ -117,6 +117,9 @@ DECODE_CASES = [
     dict(B=4, QN=64, KVN=4, KVS=2048, D=128, lens=(1, 2048)),             # g = 16
     dict(B=5, QN=2, KVN=1, KVS=300, D=128, lens=(0, 3)),
     dict(B=2, QN=4, KVN=2, KVS=500, D=128, scale=-0.09),
+    dict(B=2, QN=8, KVN=2, KVS=3000, D=256, lens=(0, 3000)),               # D = 256
+    dict(B=1, QN=16, KVN=16, KVS=20000, D=256, dtype="f16", layout="BSND"),
+    dict(B=3, QN=8, KVN=1, KVS=333, D=256, lens=(1, 333)),                  # g = 8
 ]
 
 
@@ -241,6 +244,7 @@ PAGED_CASES = [
          lens=(1, 700)),
     dict(kv_layout="PA_BNBD", bs=1024, B=1, QN=4, KVN=4, KVS=20000, D=128, lens=(19000, 20000)),
     dict(kv_layout="PA_BNBD", bs=16, B=2, QN=6, KVN=2, KVS=333, D=128, layout="BSND", lens=(1, 333)),
+    dict(kv_layout="PA_BBND", bs=64, B=2, QN=8, KVN=2, KVS=1500, D=256, lens=(1, 1500)),
 ]
 
 
@@ -322,6 +326,9 @@ PREFILL_CASES = [
     dict(B=1, QN=3, KVN=3, QS=5, KVS=1000, D=128, lens=(1, 1000)),
     dict(B=1, QN=2, KVN=1, QS=150, KVS=150, D=128, mask="causal", scale=-0.09),
     dict(B=1, QN=2, KVN=2, QS=96, KVS=200, D=64, scale=-0.125, layout="BSND"),
+    dict(B=2, QN=4, KVN=2, QS=300, KVS=300, D=256, mask="causal"),          # D = 256
+    dict(B=1, QN=2, KVN=1, QS=129, KVS=700, D=256, dtype="f16", layout="BSND", lens=(1, 700)),
+    dict(B=1, QN=2, KVN=2, QS=64, KVS=64, D=256, mask="bool_causal"),
 ]
 
 
@@ -369,11 +376,12 @@ def _bool_mask_run(inp, mask_np, strides, byte_offset=0):
     return out, lse
 
 
+@pytest.mark.parametrize("D", [128, 256])
 @pytest.mark.parametrize("byte_offset", [0, 1], ids=["lds_staged", "elementwise"])
-def test_prefill_bool_mask_both_paths(byte_offset):
+def test_prefill_bool_mask_both_paths(byte_offset, D):
     """Rows of 16-byte aligned keys go through LDS (with per-wave tile skipping);
     a misaligned mask pointer takes the element-wise path.  Both match the oracle."""
-    s = spec(layout="BNSD", B=2, QN=4, KVN=2, QS=200, KVS=320, D=128, lens=(150, 320), seed=29)
+    s = spec(layout="BNSD", B=2, QN=4, KVN=2, QS=200, KVS=320, D=D, lens=(150, 320), seed=29)
     inp = fa_synth.make(s)
     rng = np.random.default_rng(5)
     mask = (rng.random((2, 4, 200, 320)) < 0.5).astype(np.uint8)
@@ -449,6 +457,7 @@ WINDOW_CASES = [
     (dict(B=1, QN=8, KVN=2, QS=1, KVS=700, D=128, lens=(300, 700)), (0, 200)),  # decode row
     (dict(B=1, QN=2, KVN=2, QS=257, KVS=1000, D=64, layout="BSND"), (-1, 100)),
     (dict(B=1, QN=2, KVN=2, QS=400, KVS=400, D=128, scale=-0.09), (150, -1)),
+    (dict(B=1, QN=2, KVN=1, QS=300, KVS=300, D=256), (70, 5)),
 ]
 
 
@@ -516,6 +525,7 @@ PACKED_CASES = [
     (dict(B=3, QN=2, KVN=2, D=64, dtype="f16", std=0.5, q_lens=(100, 400)), "window", (50, 10)),
     (dict(B=7, QN=2, KVN=1, D=128, q_lens=(0, 3)), "none", None),                 # tiny and empty
     (dict(B=2, QN=2, KVN=2, D=64, q_lens=(129, 260), scale=-0.1), "causal", None),
+    (dict(B=3, QN=4, KVN=2, D=256, q_lens=(1, 300)), "causal", None),
 ]
 
 

@@ -316,6 +316,42 @@ def extra_workloads(fa, fa_synth, np, torch, dev16, stream, warmup=3, iters=10):
         del q, k, v, out, lse, ws, mask, inp, block_table
         torch.cuda.empty_cache()
     res.update(packed_workload(fa, fa_synth, np, torch, dev16, stream, warmup, iters))
+    res.update(fused_decode(fa, fa_synth, np, torch, dev16, stream, warmup, iters))
+    return res
+
+
+def fused_decode(fa, fa_synth, np, torch, dev16, stream, warmup, iters):
+    """The single-launch split-KV (fa_decode_fused) on the two decode workloads, with the
+    split plan fa_fwd picks, for comparison with fa_fwd's stage 1 + combine."""
+    res = {}
+    for name in ("decode_128k", "decode_gqa"):
+        inp = fa_synth.make(fa_synth.WORKLOADS[name])
+        s = inp.spec
+        q, k, v = (dev16(x, s.dtype) for x in (inp.q, inp.k, inp.v))
+        lens = None if inp.lens is None else torch.from_numpy(inp.lens).to(q.device)
+        p = fa.params_for(q, k, layout=s.layout, scale=s.softmax_scale, actual_seq_lengths=lens)
+        sp, ch, nbytes = fa.fa_splitkv_plan(p)
+        ws = torch.zeros((nbytes,), dtype=torch.uint8, device=q.device)
+        out = torch.empty_like(q)
+        lse = torch.empty((s.B, s.QN, 1), dtype=torch.float32, device=q.device)
+        for _ in range(warmup):
+            fa.fa_decode_fused(p, sp, ch, q, k, v, ws, nbytes, out, lse, stream)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(iters)]
+        for a, b in evs:
+            a.record(stream)
+            fa.fa_decode_fused(p, sp, ch, q, k, v, ws, nbytes, out, lse, stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        L = np.full(s.B, s.KVS) if inp.lens is None else np.clip(inp.lens, 0, s.KVS)
+        nb = float(L.sum()) * s.KVN * s.D * 2 * 2 + 2 * s.B * s.QN * s.D * 2
+        gbs = nb / (ms * 1e-3) / 1e9
+        res[f"{name}_fused_single_launch"] = {
+            "ms": round(ms, 5), "kv_gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "bytes": nb, "num_splits": sp, "doc": s.doc + "; fa_decode_fused (one launch)"}
+        del q, k, v, ws, out, lse, inp
+        torch.cuda.empty_cache()
     return res
 
 

@@ -160,9 +160,12 @@ fa_status fa_workspace_size(const fa_params *p, size_t *bytes);
 /* fa_fwd -- phase 2: the attention forward.  q: [B,Q_N,Q_S,D] or [B,Q_S,Q_N,D];
  * k, v: the same layout with KV_N heads and KV_S rows; out: shape of q;
  * lse: float32 [B,Q_N,Q_S] or NULL (not written).  q_seq == 1 without a mask
- * runs the split-KV decode (stage 1 + combine, or stage 1 alone when one split
- * suffices), whose split plan the library chooses (see fa_splitkv_plan); the
- * workspace must then be at least fa_workspace_size bytes, 256-byte aligned.
+ * runs the split-KV decode, whose split plan the library chooses (see
+ * fa_splitkv_plan): one split is a single stage-1 launch that writes the
+ * output; more run stage 1 and then fa_combine's kernel (measured faster on
+ * MI355X than the fused single launch of fa_decode_fused).  The workspace
+ * must then be at least fa_workspace_size bytes, 256-byte aligned; its
+ * contents need no initialisation.
  * Every other case runs the prefill kernel and needs no workspace, except
  * the packed layout FA_TND, which needs fa_workspace_size bytes (256-byte
  * aligned) for the cost-ordered list of its query tiles. */
@@ -196,6 +199,27 @@ fa_status fa_splitkv_plan(const fa_params *p, int num_cus, int64_t chunk_hint,
 fa_status fa_decode_splitkv(const fa_params *p, int64_t num_splits, int64_t chunk,
                             const void *q, const void *k, const void *v,
                             float *o_part, float *m_part, float *l_part, void *stream);
+
+/* fa_decode_fused -- FlashDecoding in ONE launch (FlashAttn developer guide:
+ * the FD block and the FA/FD overlap, whose SyncAll this replaces).  Stage 1
+ * as in fa_decode_splitkv, writing its partials into `workspace`; the last
+ * workgroup to finish a (batch, KV head, head group) unit merges that unit's
+ * rows (fa_combine's reduction) into out / lse and resets the unit's counter.
+ *   num_splits: 1..256 (1 = one chunk, no merge and no workspace needed);
+ *   chunk as for fa_decode_splitkv.
+ *   workspace: at least the bytes fa_splitkv_plan reports, 256-byte aligned:
+ *     o_part, m_part, l_part (fa_decode_splitkv's layouts, each region
+ *     256-byte aligned) followed by one uint32 counter per unit.  CONTRACT:
+ *     the counters must be zero before the first call -- zero-fill the
+ *     workspace once after allocating it; every completed call leaves them
+ *     zero, so the same workspace can be reused (also from a captured graph)
+ *     without clearing.  Calls that share a workspace must not overlap.
+ * On MI355X this is slower than stage 1 + fa_combine (the merging workgroup's
+ * device-coherent reads cost more than the second launch), so fa_fwd does not
+ * use it. */
+fa_status fa_decode_fused(const fa_params *p, int64_t num_splits, int64_t chunk,
+                          const void *q, const void *k, const void *v, void *workspace,
+                          size_t workspace_bytes, void *out, float *lse, void *stream);
 
 /* fa_combine -- FlashDecoding stage 2, the LSE merge (FlashAttn developer
  * guide 10: m = max_i m_i, l = sum_i l_i exp(m_i - m),

@@ -3,7 +3,7 @@
 Argument marshalling only: every step of the computation runs in the HIP
 kernels of ``libfa_mi355x.so``.  The low-level functions carry the C names
 (``fa_fwd``, ``fa_workspace_size``, ``fa_splitkv_plan``, ``fa_decode_splitkv``,
-``fa_combine``, ``fa_last_error``) and take device pointers as ints or torch
+``fa_decode_fused``, ``fa_combine``, ``fa_last_error``) and take device pointers as ints or torch
 tensors; ``fwd`` is a convenience wrapper that allocates the outputs and the
 workspace with torch on the current stream.  There is no CPU fallback: if the
 shared library is missing, loading fails with an error.
@@ -29,8 +29,8 @@ MASK_MODES = {"none": FA_MASK_NONE, "causal": FA_MASK_CAUSAL, "bool": FA_MASK_BO
 FA_KV_CONTIGUOUS, FA_KV_PAGED_BBND, FA_KV_PAGED_BNBD = 0, 1, 2
 KV_LAYOUTS = {"contiguous": FA_KV_CONTIGUOUS, "PA_BBND": FA_KV_PAGED_BBND, "PA_BNBD": FA_KV_PAGED_BNBD}
 
-EXPORTS = ("fa_workspace_size", "fa_fwd", "fa_splitkv_plan", "fa_decode_splitkv", "fa_combine",
-           "fa_last_error")
+EXPORTS = ("fa_workspace_size", "fa_fwd", "fa_splitkv_plan", "fa_decode_splitkv", "fa_decode_fused",
+           "fa_combine", "fa_last_error")
 
 
 class FaError(RuntimeError):
@@ -74,8 +74,9 @@ def load(path: Optional[str] = None):
             lib.fa_splitkv_plan.argtypes = [P(FaParams), ctypes.c_int, i64, P(i64), P(i64), P(sz)]
             lib.fa_decode_splitkv.argtypes = [P(FaParams), i64, i64, vp, vp, vp, vp, vp, vp, vp]
             lib.fa_combine.argtypes = [P(FaParams), i64, vp, vp, vp, vp, vp, vp]
+            lib.fa_decode_fused.argtypes = [P(FaParams), i64, i64, vp, vp, vp, vp, sz, vp, vp, vp]
             for f in (lib.fa_workspace_size, lib.fa_fwd, lib.fa_splitkv_plan, lib.fa_decode_splitkv,
-                      lib.fa_combine):
+                      lib.fa_combine, lib.fa_decode_fused):
                 f.restype = ctypes.c_int
             lib.fa_last_error.argtypes = []
             lib.fa_last_error.restype = ctypes.c_char_p
@@ -156,6 +157,13 @@ def fa_decode_splitkv(params: FaParams, num_splits, chunk, q, k, v, o_part, m_pa
     _check(load().fa_decode_splitkv(ctypes.byref(params), int(num_splits), int(chunk), _ptr(q),
                                     _ptr(k), _ptr(v), _ptr(o_part), _ptr(m_part), _ptr(l_part),
                                     _stream(stream)))
+
+
+def fa_decode_fused(params: FaParams, num_splits, chunk, q, k, v, workspace, workspace_bytes, out,
+                    lse=None, stream=None):
+    _check(load().fa_decode_fused(ctypes.byref(params), int(num_splits), int(chunk), _ptr(q), _ptr(k),
+                                  _ptr(v), _ptr(workspace), int(workspace_bytes), _ptr(out), _ptr(lse),
+                                  _stream(stream)))
 
 
 def fa_combine(params: FaParams, num_splits, o_part, m_part, l_part, out, lse=None, stream=None):

@@ -156,15 +156,19 @@ int device_cus() {
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Partials {
-    size_t o_bytes, m_bytes, total;
+    size_t o_bytes, m_bytes, c_bytes, total;
 };
 
+// Workspace of a split plan: o_part, m_part, l_part (fa_decode_splitkv's
+// layouts), then one counter per stage-1 unit for the fused plan.
 Partials partial_bytes(const Shape& s, int64_t splits) {
     Partials r;
     const size_t rows = size_t(s.B) * size_t(s.QN) * size_t(splits);
     r.o_bytes = round_up(rows * size_t(s.D) * sizeof(float), 256);
     r.m_bytes = round_up(rows * sizeof(float), 256);
-    r.total = r.o_bytes + 2 * r.m_bytes;
+    const size_t units = size_t(s.B) * size_t(s.KVN) * size_t(s.g / heads_per_workgroup(s.g));
+    r.c_bytes = round_up(units * sizeof(unsigned), 256);
+    r.total = r.o_bytes + 2 * r.m_bytes + r.c_bytes;
     return r;
 }
 
@@ -248,8 +252,8 @@ fa_status launch_result(hipError_t e, const char* what) {
 }
 
 fa_status run_stage1(const fa_params* p, const Shape& s, int64_t splits, int64_t chunk, const void* q, const void* k,
-                     const void* v, float* o_part, float* m_part, float* l_part, void* out, float* lse,
-                     hipStream_t stream) {
+                     const void* v, float* o_part, float* m_part, float* l_part, unsigned* counters, void* out,
+                     float* lse, hipStream_t stream) {
     fa::DecodeArgs a;
     fill_decode_args(p, s, &a);
     a.q = static_cast<const uint16_t*>(q);
@@ -262,7 +266,8 @@ fa_status run_stage1(const fa_params* p, const Shape& s, int64_t splits, int64_t
     a.lse = lse;
     a.chunk = chunk;
     a.num_splits = (int32_t)splits;
-    const bool finish = (out != nullptr);
+    a.counters = counters;
+    const bool finish = (out != nullptr && counters == nullptr);
     return launch_result(fa::launch_decode_stage1(a, p->dtype == FA_BF16 ? 1 : 0, (int)s.D,
                                                   heads_per_workgroup(s.g), finish, s.B, stream),
                          "decode stage 1");
@@ -441,7 +446,7 @@ fa_status fa_fwd(const fa_params* p, const void* q, const void* k, const void* v
     int64_t sp, c;
     plan_splits(p, s, device_cus(), &sp, &c);
     if (sp > kMaxSplits) return fail(FA_ERR_PARAM_INVALID, "plan needs too many splits");
-    if (sp == 1) return run_stage1(p, s, 1, c, q, k, v, nullptr, nullptr, nullptr, out, lse, hs);
+    if (sp == 1) return run_stage1(p, s, 1, c, q, k, v, nullptr, nullptr, nullptr, nullptr, out, lse, hs);
     const Partials pb = partial_bytes(s, sp);
     if (!workspace) return fail(FA_ERR_NULLPTR, "this call needs %zu bytes of workspace (fa_workspace_size)", pb.total);
     if (!aligned(workspace, 256)) return fail(FA_ERR_PARAM_INVALID, "workspace must be 256-byte aligned");
@@ -451,7 +456,7 @@ fa_status fa_fwd(const fa_params* p, const void* q, const void* k, const void* v
     float* o_part = reinterpret_cast<float*>(w);
     float* m_part = reinterpret_cast<float*>(w + pb.o_bytes);
     float* l_part = reinterpret_cast<float*>(w + pb.o_bytes + pb.m_bytes);
-    st = run_stage1(p, s, sp, c, q, k, v, o_part, m_part, l_part, nullptr, nullptr, hs);
+    st = run_stage1(p, s, sp, c, q, k, v, o_part, m_part, l_part, nullptr, nullptr, nullptr, hs);
     if (st != FA_OK) return st;
     return run_combine(p, s, sp, o_part, m_part, l_part, out, lse, hs);
 }
@@ -478,8 +483,41 @@ fa_status fa_decode_splitkv(const fa_params* p, int64_t num_splits, int64_t chun
     if (num_splits * chunk < s.KVS)
         return fail(FA_ERR_PARAM_INVALID, "num_splits * chunk (%lld) must cover kv_seq (%lld)",
                     (long long)(num_splits * chunk), (long long)s.KVS);
-    return run_stage1(p, s, num_splits, chunk, q, k, v, o_part, m_part, l_part, nullptr, nullptr,
+    return run_stage1(p, s, num_splits, chunk, q, k, v, o_part, m_part, l_part, nullptr, nullptr, nullptr,
                       static_cast<hipStream_t>(stream));
+}
+
+fa_status fa_decode_fused(const fa_params* p, int64_t num_splits, int64_t chunk, const void* q, const void* k,
+                          const void* v, void* workspace, size_t workspace_bytes, void* out, float* lse, void* stream) {
+    Shape s;
+    fa_status st = check_params(p, &s);
+    if (st != FA_OK) return st;
+    if (p->layout == FA_TND) return fail(FA_ERR_UNSUPPORTED, "split-KV decode is built for BNSD and BSND");
+    if (p->q_seq != 1) return fail(FA_ERR_PARAM_INVALID, "split-KV decode needs q_seq == 1, got %lld", (long long)p->q_seq);
+    if (p->mask_mode != FA_MASK_NONE) return fail(FA_ERR_PARAM_INVALID, "split-KV decode takes no mask");
+    st = check_tensors(q, k, v, out, lse);
+    if (st != FA_OK) return st;
+    if (num_splits < 1 || num_splits > fa::kFusedMaxSplits)
+        return fail(FA_ERR_PARAM_INVALID, "the fused decode takes 1 to %d splits, got %lld", fa::kFusedMaxSplits,
+                    (long long)num_splits);
+    if (chunk < 64 || chunk % 64 != 0) return fail(FA_ERR_PARAM_INVALID, "chunk must be a positive multiple of 64");
+    if (chunk > paged_chunk_cap(p))
+        return fail(FA_ERR_PARAM_INVALID, "chunk %lld exceeds %lld tokens (1016 blocks of the paged cache)",
+                    (long long)chunk, (long long)paged_chunk_cap(p));
+    if (num_splits * chunk < s.KVS)
+        return fail(FA_ERR_PARAM_INVALID, "num_splits * chunk (%lld) must cover kv_seq (%lld)",
+                    (long long)(num_splits * chunk), (long long)s.KVS);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (num_splits == 1) return run_stage1(p, s, 1, chunk, q, k, v, nullptr, nullptr, nullptr, nullptr, out, lse, hs);
+    const Partials pb = partial_bytes(s, num_splits);
+    if (!workspace) return fail(FA_ERR_NULLPTR, "the fused decode needs %zu bytes of workspace", pb.total);
+    if (!aligned(workspace, 256)) return fail(FA_ERR_PARAM_INVALID, "workspace must be 256-byte aligned");
+    if (workspace_bytes < pb.total)
+        return fail(FA_ERR_PARAM_INVALID, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, pb.total);
+    char* w = static_cast<char*>(workspace);
+    return run_stage1(p, s, num_splits, chunk, q, k, v, reinterpret_cast<float*>(w),
+                      reinterpret_cast<float*>(w + pb.o_bytes), reinterpret_cast<float*>(w + pb.o_bytes + pb.m_bytes),
+                      reinterpret_cast<unsigned*>(w + pb.o_bytes + 2 * pb.m_bytes), out, lse, hs);
 }
 
 fa_status fa_combine(const fa_params* p, int64_t num_splits, const float* o_part, const float* m_part,

@@ -18,6 +18,15 @@
 // merged once at the end.  The g query heads that share a KV head (GQA) are
 // processed by the same workgroup so their K/V rows are read once.
 //
+// Fused split-KV (one launch): after writing its chunk's partials with
+// device-coherent stores a workgroup counts itself done on a per-unit counter
+// (a vector atomic on global memory), and the workgroup that completes the
+// count merges that unit's rows with the FD reduction right away and resets
+// the counter, so no second kernel waits for the whole grid.  This takes the
+// place of the pages' SyncAll between the split and the reduction (FlashAttn
+// developer guide, FA/FD overlap): rows are merged as soon as their own
+// chunks finish.
+//
 // With a paged cache (FlashAttn developer guide 1.2, PagedAttention) the
 // workgroup first stages the physical block ids of its chunk in LDS; every lane
 // then follows its row slots block by block with an incrementally advanced
@@ -28,7 +37,11 @@
 
 namespace fa {
 
-template <typename ST, int D, int GH, bool FINISH, bool PAGED>
+// Stage-1 output modes: partials only, the final output of a one-split plan,
+// or partials plus the in-kernel merge of the fused plan.
+constexpr int kPartial = 0, kFinish = 1, kFused = 2;
+
+template <typename ST, int D, int GH, int MODE, bool PAGED>
 __global__ __launch_bounds__(256) void decode_stage1_kernel(DecodeArgs a) {
     constexpr int LPR = D / 8;     // lanes per KV row
     constexpr int RPL = 64 / LPR;  // rows per wave load
@@ -258,21 +271,150 @@ __global__ __launch_bounds__(256) void decode_stage1_kernel(DecodeArgs a) {
             A = __builtin_fmaf(s_acc[w][h][d], f, A);
         }
         const int64_t row = b * a.num_heads + (int64_t)n2 * a.group + gi;
-        if constexpr (FINISH) {
+        if constexpr (MODE == kFinish) {
             const bool empty = (M == kNegInf);
             uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
             out[row * D + d] = to_bits<ST>(empty ? 0.f : A / Lt);
             if (d == 0 && a.lse) a.lse[row] = empty ? kPosInf : (M + log2f(Lt)) * kLn2;
         } else {
             const int64_t slot = row * a.num_splits + split;
-            a.o_part[slot * D + d] = A;
-            if (d == 0) {
-                a.m_part[slot] = (M == kNegInf) ? kNegInf : M * kLn2;
-                a.l_part[slot] = Lt;
+            const float mo = (M == kNegInf) ? kNegInf : M * kLn2;
+            if constexpr (MODE == kFused) {  // device-coherent stores: another CU's L2 may merge them
+                __hip_atomic_store(a.o_part + slot * D + d, A, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (d == 0) {
+                    __hip_atomic_store(a.m_part + slot, mo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(a.l_part + slot, Lt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            } else {
+                a.o_part[slot * D + d] = A;
+                if (d == 0) {
+                    a.m_part[slot] = mo;
+                    a.l_part[slot] = Lt;
+                }
+            }
+        }
+    }
+
+    if constexpr (MODE == kFused) {
+        // Count this chunk and let the workgroup that completes the unit's
+        // count merge its rows.  The partials were written with device-scope
+        // (L2-coherent) stores and are read back with device-scope loads, so
+        // no cache write-back or invalidation is needed -- a device-scope
+        // fence would write back and invalidate this XCD's whole L2 in every
+        // workgroup.  Each thread waits for its stores to complete before the
+        // barrier, so they are performed before the counter moves.
+        __shared__ int s_last;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x == 0)
+            s_last = (__hip_atomic_fetch_add(a.counters + unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                      (unsigned)(a.num_splits - 1));
+        __syncthreads();
+        if (!s_last) return;
+        // Every chunk of the unit has counted: leave the counter at zero for
+        // the next call on this workspace.
+        if (threadIdx.x == 0) __hip_atomic_store(a.counters + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        auto ld = [](const float* p) __attribute__((always_inline)) {
+            return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        };
+
+        const int S = a.num_splits;
+        __shared__ float s_w[GH][kFusedMaxSplits];
+        __shared__ float s_inv[GH], s_lse[GH];
+        // Weights: one wave per query head, each lane's m and l loads issued
+        // together (S <= 256: up to four per lane).
+        for (int h = wave; h < GH; h += NW) {
+            const int gi = hg * GH + h;
+            if (gi >= a.group) continue;
+            const int64_t row = b * a.num_heads + (int64_t)n2 * a.group + gi;
+            const float* mp = a.m_part + row * S;
+            const float* lp = a.l_part + row * S;
+            float mv[kFusedMaxSplits / 64], lv[kFusedMaxSplits / 64];
+#pragma unroll
+            for (int j = 0; j < kFusedMaxSplits / 64; ++j) {
+                const int i = lane + 64 * j;
+                mv[j] = (i < S) ? ld(mp + i) : kNegInf;
+                lv[j] = (i < S) ? ld(lp + i) : 0.f;
+            }
+            float mx = kNegInf;
+#pragma unroll
+            for (int j = 0; j < kFusedMaxSplits / 64; ++j) mx = fmaxf(mx, mv[j]);
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, shfl_xor(mx, off));
+            const float mx2 = mx * kLog2e;
+            float ls = 0.f;
+#pragma unroll
+            for (int j = 0; j < kFusedMaxSplits / 64; ++j) {
+                const int i = lane + 64 * j;
+                const float w = (mv[j] == kNegInf) ? 0.f : fast_exp2(__builtin_fmaf(mv[j], kLog2e, -mx2));
+                if (i < S) s_w[h][i] = w;
+                ls = __builtin_fmaf(w, lv[j], ls);
+            }
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) ls += shfl_xor(ls, off);
+            if (lane == 0) {
+                s_inv[h] = (mx == kNegInf) ? 0.f : 1.f / ls;
+                s_lse[h] = (mx == kNegInf) ? kPosInf : mx + logf(ls);
+            }
+        }
+        __syncthreads();
+        // Outputs: TPO threads per (head, column), each summing a share of the
+        // splits with 16 loads in flight at a time; shares meet in LDS.
+        constexpr int OUTS = GH * D;
+        constexpr int TPO = (OUTS >= 256) ? 1 : 256 / OUTS;
+        __shared__ float s_part[(TPO > 1) ? 256 : 1];
+        uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+        for (int idx = threadIdx.x; idx < OUTS * TPO; idx += 256) {
+            const int o = idx % OUTS;
+            const int share = idx / OUTS;
+            const int h = o / D;
+            const int d = o % D;
+            const int gi = hg * GH + h;
+            float A = 0.f;
+            if (gi < a.group) {
+                const int64_t row = b * a.num_heads + (int64_t)n2 * a.group + gi;
+                const float* op = a.o_part + row * (int64_t)S * D + d;
+                for (int i0 = share * 16; i0 < S; i0 += 16 * TPO) {
+                    float ov[16];
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const int i = i0 + j;
+                        ov[j] = (i < S && s_w[h][i] != 0.f) ? ld(op + (int64_t)i * D) : 0.f;  // empty chunks skipped
+                    }
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        if (i0 + j < S) A = __builtin_fmaf(s_w[h][i0 + j], ov[j], A);
+                }
+            }
+            if constexpr (TPO > 1) {
+                s_part[idx] = A;
+            } else if (gi < a.group) {
+                const int64_t row = b * a.num_heads + (int64_t)n2 * a.group + gi;
+                out[row * D + d] = to_bits<ST>(A * s_inv[h]);
+                if (d == 0 && a.lse) a.lse[row] = s_lse[h];
+            }
+        }
+        if constexpr (TPO > 1) {
+            __syncthreads();
+            if (threadIdx.x < OUTS) {
+                const int o = threadIdx.x;
+                const int h = o / D;
+                const int d = o % D;
+                const int gi = hg * GH + h;
+                if (gi < a.group) {
+                    float A = 0.f;
+#pragma unroll
+                    for (int t = 0; t < TPO; ++t) A += s_part[t * OUTS + o];
+                    const int64_t row = b * a.num_heads + (int64_t)n2 * a.group + gi;
+                    out[row * D + d] = to_bits<ST>(A * s_inv[h]);
+                    if (d == 0 && a.lse) a.lse[row] = s_lse[h];
+                }
             }
         }
     }
 }
+
+
 
 // Stage 2: one workgroup of 256 threads per (b, n1) row merges num_splits
 // partials.  Thread t owns four head-dim columns (t % (D/4)) of one split group
@@ -372,10 +514,14 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 
 template <typename ST, int D, int GH, bool PAGED>
 static hipError_t dispatch_stage1_fin(const DecodeArgs& a, bool finish, int64_t blocks, hipStream_t s) {
-    if (finish)
-        hipLaunchKernelGGL((decode_stage1_kernel<ST, D, GH, true, PAGED>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((decode_stage1_kernel<ST, D, GH, false, PAGED>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    const dim3 grid((unsigned)blocks);
+    if (finish) {
+        hipLaunchKernelGGL((decode_stage1_kernel<ST, D, GH, kFinish, PAGED>), grid, dim3(256), 0, s, a);
+    } else if (a.counters) {
+        hipLaunchKernelGGL((decode_stage1_kernel<ST, D, GH, kFused, PAGED>), grid, dim3(256), 0, s, a);
+    } else {
+        hipLaunchKernelGGL((decode_stage1_kernel<ST, D, GH, kPartial, PAGED>), grid, dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 

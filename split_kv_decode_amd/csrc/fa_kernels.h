@@ -31,6 +31,9 @@ struct DecodeArgs {
     int32_t block_size;
     int32_t max_blocks;
     int32_t num_blocks;
+    // Fused plan: [units] counters (units = B * KV_N * head_groups), zero on
+    // entry and left zero; out / lse then receive the merged result.
+    unsigned* counters;
     int32_t num_splits;
     int32_t num_heads;        // Q_N
     int32_t num_kv_heads;     // KV_N
@@ -126,6 +129,9 @@ constexpr int kVarlenMaxBatch = 16383;
 // Block ids one paged stage-1 workgroup stages in LDS: a chunk may touch at most
 // this many blocks.
 constexpr int kPagedTableLds = 1024;
+
+// Largest split count the fused stage-1 merge handles (its weights sit in LDS).
+constexpr int kFusedMaxSplits = 256;
 
 // Launchers: return hipSuccess or the launch error.  dtype: 0 = fp16, 1 = bf16.
 hipError_t launch_decode_stage1(const DecodeArgs& a, int dtype, int head_dim, int heads_per_wg,

@@ -204,3 +204,18 @@ def test_tnd_workspace(lib):
     pd = tnd(q_seq=4, mask_mode="none")
     st = lib.fa_decode_splitkv(ctypes.byref(pd), 1, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
     assert st == fa.FA_ERR_UNSUPPORTED
+
+
+def test_fused_decode_validates(lib):
+    p = params()
+    st = lib.fa_decode_fused(ctypes.byref(p), 512, 256, FAKE, FAKE, FAKE, FAKE, 1 << 30, FAKE, None, None)
+    assert st == fa.FA_ERR_PARAM_INVALID and "1 to 256" in fa.fa_last_error()
+    st = lib.fa_decode_fused(ctypes.byref(p), 32, 4096, FAKE, FAKE, FAKE, None, 0, FAKE, None, None)
+    assert st == fa.FA_ERR_NULLPTR and "workspace" in fa.fa_last_error()
+    st = lib.fa_decode_fused(ctypes.byref(p), 32, 4096, FAKE, FAKE, FAKE, FAKE, 1024, FAKE, None, None)
+    assert st == fa.FA_ERR_PARAM_INVALID and "too small" in fa.fa_last_error()
+    st = lib.fa_decode_fused(ctypes.byref(p), 16, 4096, FAKE, FAKE, FAKE, FAKE, 1 << 30, FAKE, None, None)
+    assert st == fa.FA_ERR_PARAM_INVALID and "cover" in fa.fa_last_error()
+    pq = params(q_seq=4)
+    st = lib.fa_decode_fused(ctypes.byref(pq), 32, 4096, FAKE, FAKE, FAKE, FAKE, 1 << 30, FAKE, None, None)
+    assert st == fa.FA_ERR_PARAM_INVALID

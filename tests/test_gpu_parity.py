@@ -120,6 +120,8 @@ DECODE_CASES = [
     dict(B=2, QN=8, KVN=2, KVS=3000, D=256, lens=(0, 3000)),               # D = 256
     dict(B=1, QN=16, KVN=16, KVS=20000, D=256, dtype="f16", layout="BSND"),
     dict(B=3, QN=8, KVN=1, KVS=333, D=256, lens=(1, 333)),                  # g = 8
+    dict(B=1, QN=1, KVN=1, KVS=131072, D=128),   # 512 splits: stage 1 + combine kernels
+    dict(B=2, QN=1, KVN=1, KVS=60000, D=64, lens=(0, 60000)),   # fused, one unit empty or not
 ]
 
 
@@ -136,6 +138,85 @@ def test_decode_ignores_nan_padding():
     out, lse = run_fwd(pad)
     assert torch.equal(out, base) and torch.equal(torch.isinf(lse), torch.isinf(base_lse))
     assert torch.equal(lse[~torch.isinf(lse)], base_lse[~torch.isinf(base_lse)])
+
+
+FUSED_CASES = [
+    (dict(B=1, QN=32, KVN=32, KVS=131072, D=128), 32, 4096),     # the 128K decode plan
+    (dict(layout="BSND", B=8, QN=32, KVN=8, KVS=4096, D=128, lens=(1, 4096)), 16, 256),
+    (dict(B=3, QN=16, KVN=2, KVS=777, D=64, lens=(0, 777)), 13, 64),          # empty units
+    (dict(B=2, QN=8, KVN=2, KVS=3000, D=256, dtype="f16", lens=(1, 3000)), 5, 640),
+    (dict(B=1, QN=2, KVN=1, KVS=300, D=128), 1, 320),                         # one split
+    (dict(B=1, QN=4, KVN=4, KVS=32768, D=128), 256, 128),                     # the most splits
+]
+
+
+def _fused_setup(inp, splits, chunk):
+    s = inp.spec
+    q, k, v = (dev16(x, s.dtype) for x in (inp.q, inp.k, inp.v))
+    lens = None if inp.lens is None else torch.from_numpy(inp.lens).to(DEV)
+    p = fa.params_for(q, k, layout=s.layout, scale=s.softmax_scale, actual_seq_lengths=lens)
+    _, _, nbytes = fa.fa_splitkv_plan(p, chunk_hint=chunk)
+    ws = torch.zeros((nbytes,), dtype=torch.uint8, device=DEV)  # zero once: the counter contract
+    return q, k, v, lens, p, ws, nbytes
+
+
+@pytest.mark.parametrize("case,splits,chunk", FUSED_CASES,
+                         ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()) if isinstance(c, dict) else str(c))
+def test_decode_fused_matches_oracle(case, splits, chunk):
+    """The single-launch split-KV: the workgroup that completes a unit merges it.
+    Two calls in a row on one workspace agree bit for bit (the counters come back to 0)."""
+    inp = fa_synth.make(spec(seed=43, **case))
+    s = inp.spec
+    q, k, v, lens, p, ws, nbytes = _fused_setup(inp, splits, chunk)
+    outs = []
+    for _ in range(2):
+        out = torch.empty_like(q)
+        lse = torch.empty((s.B, s.QN, 1), dtype=torch.float32, device=DEV)
+        fa.fa_decode_fused(p, splits, chunk, q, k, v, ws, nbytes, out, lse, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        outs.append((out, lse))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    if splits > 1:
+        units = s.B * s.KVN * (s.g // max(h for h in (8, 4, 2, 1) if s.g % h == 0))
+        n_counter_words = -(-(units * 4) // 256) * 64   # the trailing 256-byte-aligned region
+        assert torch.count_nonzero(ws.view(torch.int32)[-n_counter_words:]) == 0
+    out, lse = outs[0]
+    prob = oracle.Problem.from_inputs(inp)
+    ref, ref_lse = oracle.attention_rows(prob, inp.q, inp.k, inp.v)
+    check(rows_of(out, s, np.arange(s.B * s.QN)), to_np(lse).reshape(-1), ref, ref_lse, f"fused {case}")
+
+
+def test_decode_fused_graph_replays():
+    """The fused decode captured in a HIP graph: every replay (with new q and eager work in
+    between, the workspace never cleared again) must equal the eager two-kernel result."""
+    inp = fa_synth.make(spec(layout="BSND", B=4, QN=16, KVN=4, KVS=3000, lens=(1, 3000), seed=41))
+    s = inp.spec
+    splits, chunk = 12, 256
+    q, k, v, lens, p, ws, nbytes = _fused_setup(inp, splits, chunk)
+    out = torch.empty_like(q)
+    lse = torch.empty((s.B, s.QN, 1), dtype=torch.float32, device=DEV)
+    qg = q.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm up off the capture
+        fa.fa_decode_fused(p, splits, chunk, qg, k, v, ws, nbytes, out, lse, side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fa.fa_decode_fused(p, splits, chunk, qg, k, v, ws, nbytes, out, lse,
+                           torch.cuda.current_stream())
+    for rep in range(4):
+        qn = torch.randn(q.shape, device=DEV).to(q.dtype)
+        qg.copy_(qn)
+        graph.replay()
+        torch.cuda.synchronize()
+        ref_out, ref_lse = fa.fwd(qn, k, v, layout=s.layout, scale=s.softmax_scale,
+                                  actual_seq_lengths=lens, return_lse=True)
+        torch.cuda.synchronize()
+        err = (out.float() - ref_out.float()).abs().max().item()
+        assert err <= OUT_MAX, f"replay {rep}: {err}"
+        assert (lse - ref_lse).abs().max().item() <= 1e-5, f"replay {rep}"
 
 
 def _partials(inp, splits, chunk):

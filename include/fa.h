@@ -175,7 +175,10 @@ fa_status fa_fwd(const fa_params *p, const void *q, const void *k, const void *v
 
 /* fa_splitkv_plan -- the split-count heuristic (IFA guide 8.2: split the KV
  * axis when B*KV_N is below 0.4 x the core count; FlashDecoding tutorial,
- * preface: cut the cache so every core has a piece).  Host-only integer work.
+ * preface: cut the cache so every core has a piece).  Host-side work: the
+ * target is as many stage-1 workgroups as the CUs hold at once, from the HIP
+ * occupancy calculator for the instantiation that will run (4 per CU when no
+ * device answers), so the stage-1 grid is one round.
  *   num_cus: compute units to fill (<= 0: query the current device).
  *   chunk_hint: tokens per split, a positive multiple of 64, or 0 = automatic.
  * Returns num_splits >= 1 and chunk (a multiple of 64) with
@@ -194,8 +197,10 @@ fa_status fa_splitkv_plan(const fa_params *p, int num_cus, int64_t chunk_hint,
  * l = 0 and o = 0.  Layouts (float32, contiguous):
  *   o_part [B][Q_N][num_splits][D], m_part and l_part [B][Q_N][num_splits].
  * num_splits * chunk must cover kv_seq; chunk a positive multiple of 64
- * (with a paged cache also at most 1016 * block_size, the block ids of one
- * chunk being staged on chip; fa_splitkv_plan respects this). */
+ * and at most a cap (a paged cache: 1016 * block_size, the block ids of one
+ * chunk being staged on chip; a contiguous one: (chunk + 256) rows of one
+ * head within 2^31 bytes, the K/V offsets being 32-bit); fa_splitkv_plan
+ * respects both. */
 fa_status fa_decode_splitkv(const fa_params *p, int64_t num_splits, int64_t chunk,
                             const void *q, const void *k, const void *v,
                             float *o_part, float *m_part, float *l_part, void *stream);

@@ -173,30 +173,38 @@ Partials partial_bytes(const Shape& s, int64_t splits) {
 }
 
 // Split plan.  Decode reads each KV byte once, so every CU must stream: aim for
-// about four stage-1 workgroups (16 waves) per CU.  The units of independent
-// work are (b, kv head, head group); when there are fewer than that target,
-// the KV axis is cut into chunks (multiples of 64 tokens, at least 256) so that
-// units * splits reaches it.  One split means stage 1 finishes in place.
+// as many stage-1 workgroups as the CUs hold at once (the occupancy of the
+// instantiation that will run, four per CU when no device answers), so the
+// grid is one full round with no straggling second one.  The units of
+// independent work are (b, kv head, head group); when there are fewer than
+// that target, the KV axis is cut into chunks (multiples of 64 tokens, at
+// least 256) so that units * splits reaches it.  One split means stage 1
+// finishes in place.
 constexpr int64_t kMinChunk = 256;
 constexpr int64_t kWgPerCu = 4;
 
-// Largest chunk of a paged cache: its block ids (at most chunk/block_size + 1)
-// must fit the stage-1 kernel's LDS table.
-int64_t paged_chunk_cap(const fa_params* p) {
-    return p->kv_layout == FA_KV_CONTIGUOUS ? INT64_MAX : (fa::kPagedTableLds - 8) * p->block_size;
+// Largest chunk: a paged cache's block ids (at most chunk/block_size + 1) must
+// fit the stage-1 kernel's LDS table; a contiguous chunk (plus the rows loaded
+// ahead of it) must stay addressable with 32-bit byte offsets.
+int64_t chunk_cap(const fa_params* p, const Shape& s) {
+    if (p->kv_layout != FA_KV_CONTIGUOUS) return (fa::kPagedTableLds - 8) * p->block_size;
+    const int64_t row_bytes = (p->layout == FA_BNSD ? s.D : s.KVN * s.D) * 2;
+    return ((int64_t(0x7fffffff) / row_bytes - 256) / 64) * 64;
 }
 
 void plan_splits(const fa_params* p, const Shape& s, int num_cus, int64_t* splits, int64_t* chunk) {
     const int gh = heads_per_workgroup(s.g);
     const int64_t units = s.B * s.KVN * (s.g / gh);
-    const int64_t target = kWgPerCu * int64_t(num_cus > 0 ? num_cus : 256);
+    const int resident = fa::decode_stage1_residency(p->dtype == FA_BF16 ? 1 : 0, (int)s.D, gh,
+                                                     p->kv_layout != FA_KV_CONTIGUOUS);
+    const int64_t target = (resident > 0 ? resident : kWgPerCu) * int64_t(num_cus > 0 ? num_cus : 256);
     int64_t want = (target + units - 1) / units;
     if (want < 1) want = 1;
     int64_t c = (s.KVS + want - 1) / want;
     c = (c + 63) / 64 * 64;
     const int64_t kv_round = (s.KVS + 63) / 64 * 64;
     if (c < kMinChunk) c = kMinChunk < kv_round ? kMinChunk : kv_round;
-    if (c > paged_chunk_cap(p)) c = paged_chunk_cap(p);
+    if (c > chunk_cap(p, s)) c = chunk_cap(p, s);
     *chunk = c;
     *splits = (s.KVS + c - 1) / c;
 }
@@ -392,9 +400,9 @@ fa_status fa_splitkv_plan(const fa_params* p, int num_cus, int64_t chunk_hint, i
     if (chunk_hint < 0 || chunk_hint % 64 != 0)
         return fail(FA_ERR_PARAM_INVALID, "chunk_hint must be 0 or a positive multiple of 64, got %lld",
                     (long long)chunk_hint);
-    if (chunk_hint > paged_chunk_cap(p))
-        return fail(FA_ERR_PARAM_INVALID, "chunk_hint %lld exceeds %lld tokens (1016 blocks of the paged cache)",
-                    (long long)chunk_hint, (long long)paged_chunk_cap(p));
+    if (chunk_hint > chunk_cap(p, s))
+        return fail(FA_ERR_PARAM_INVALID, "chunk_hint %lld exceeds the largest chunk, %lld tokens",
+                    (long long)chunk_hint, (long long)chunk_cap(p, s));
     int64_t sp, c;
     if (chunk_hint > 0) {
         c = chunk_hint;
@@ -477,9 +485,9 @@ fa_status fa_decode_splitkv(const fa_params* p, int64_t num_splits, int64_t chun
         return fail(FA_ERR_PARAM_INVALID, "partials must be 4-byte aligned");
     if (num_splits < 1 || num_splits > kMaxSplits) return fail(FA_ERR_PARAM_INVALID, "num_splits must be in [1, 2^20]");
     if (chunk < 64 || chunk % 64 != 0) return fail(FA_ERR_PARAM_INVALID, "chunk must be a positive multiple of 64");
-    if (chunk > paged_chunk_cap(p))
-        return fail(FA_ERR_PARAM_INVALID, "chunk %lld exceeds %lld tokens (1016 blocks of the paged cache)",
-                    (long long)chunk, (long long)paged_chunk_cap(p));
+    if (chunk > chunk_cap(p, s))
+        return fail(FA_ERR_PARAM_INVALID, "chunk %lld exceeds the largest chunk, %lld tokens", (long long)chunk,
+                    (long long)chunk_cap(p, s));
     if (num_splits * chunk < s.KVS)
         return fail(FA_ERR_PARAM_INVALID, "num_splits * chunk (%lld) must cover kv_seq (%lld)",
                     (long long)(num_splits * chunk), (long long)s.KVS);
@@ -501,9 +509,9 @@ fa_status fa_decode_fused(const fa_params* p, int64_t num_splits, int64_t chunk,
         return fail(FA_ERR_PARAM_INVALID, "the fused decode takes 1 to %d splits, got %lld", fa::kFusedMaxSplits,
                     (long long)num_splits);
     if (chunk < 64 || chunk % 64 != 0) return fail(FA_ERR_PARAM_INVALID, "chunk must be a positive multiple of 64");
-    if (chunk > paged_chunk_cap(p))
-        return fail(FA_ERR_PARAM_INVALID, "chunk %lld exceeds %lld tokens (1016 blocks of the paged cache)",
-                    (long long)chunk, (long long)paged_chunk_cap(p));
+    if (chunk > chunk_cap(p, s))
+        return fail(FA_ERR_PARAM_INVALID, "chunk %lld exceeds the largest chunk, %lld tokens", (long long)chunk,
+                    (long long)chunk_cap(p, s));
     if (num_splits * chunk < s.KVS)
         return fail(FA_ERR_PARAM_INVALID, "num_splits * chunk (%lld) must cover kv_seq (%lld)",
                     (long long)(num_splits * chunk), (long long)s.KVS);

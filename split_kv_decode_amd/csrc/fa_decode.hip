@@ -45,7 +45,10 @@ template <typename ST, int D, int GH, int MODE, bool PAGED>
 __global__ __launch_bounds__(256) void decode_stage1_kernel(DecodeArgs a) {
     constexpr int LPR = D / 8;     // lanes per KV row
     constexpr int RPL = 64 / LPR;  // rows per wave load
-    constexpr int U = (GH >= 4) ? 2 : 4;  // row slots per lane per iteration
+    constexpr int U = 2;                   // row slots per lane per iteration
+    constexpr int DEPTH = (GH >= 4) ? 1 : 2;  // iterations of K/V loads in flight ahead
+    // (both chosen so the common instantiations stay within 128 VGPRs: four
+    // workgroups per CU, the residency the split plan assumes)
     constexpr int TW = RPL * U;    // tokens per wave iteration
     constexpr int NW = 4;          // waves per workgroup
 
@@ -71,225 +74,300 @@ __global__ __launch_bounds__(256) void decode_stage1_kernel(DecodeArgs a) {
     int64_t c1 = c0 + a.chunk;
     if (c1 > L) c1 = L;
 
-    // Resident query slice, pre-scaled by scale*log2(e) so scores are in base 2.
-    float qf[GH][8];
-#pragma unroll
-    for (int h = 0; h < GH; ++h) {
-        const int gi = hg * GH + h;
-        if (gi < a.group) {
-            const int64_t n1 = (int64_t)n2 * a.group + gi;
-            const u32x4 w = ld128(a.q + (b * a.num_heads + n1) * D + sub * 8);
-            unpack8<ST>(w, qf[h]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qf[h][e] *= a.scale_log2;
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qf[h][e] = 0.f;
-        }
-    }
-
-    float m[GH], l[GH], acc[GH][8];
-#pragma unroll
-    for (int h = 0; h < GH; ++h) {
-        m[h] = kNegInf;
-        l[h] = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-    }
-
-    const int64_t head_off = (PAGED ? 0 : b * a.kv_stride_b) + (int64_t)n2 * a.kv_stride_n + sub * 8;
-    const uint16_t* kb = a.k + head_off;
-    const uint16_t* vb = a.v + head_off;
-    const int64_t ss = a.kv_stride_s;
-
-    // Paged cache: block ids of the chunk's logical blocks [cb, cb + nblk),
-    // clamped into the physical range, and per-slot (block, row) cursors that
-    // follow the positions load() is called with (t0 + k*NW*TW, k = 0, 1, ...).
-    __shared__ int32_t s_blk[PAGED ? kPagedTableLds : 1];
-    int pb[U], pr[U];
-    int step_q = 0, step_r = 0;
-    if constexpr (PAGED) {
-        const int bs = a.block_size;
-        const int64_t cb = c0 / bs;
-        const int64_t nblk = (c1 > c0) ? (c1 - 1) / bs - cb + 1 : 0;
-        const int32_t* tb = a.block_table + b * a.max_blocks + cb;
-        for (int i = threadIdx.x; i < nblk; i += 256) {
-            int32_t id = tb[i];
-            id = id < 0 ? 0 : (id >= a.num_blocks ? a.num_blocks - 1 : id);
-            s_blk[i] = id;
-        }
-        __syncthreads();
-        const int rel0 = (int)(c0 - cb * bs) + wave * TW + grp;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            pb[u] = (rel0 + u * RPL) / bs;
-            pr[u] = (rel0 + u * RPL) % bs;
-        }
-        step_q = (NW * TW) / bs;
-        step_r = (NW * TW) % bs;
-    }
-
-    auto load = [&](int64_t t0, u32x4* kw, u32x4* vw) __attribute__((always_inline)) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t t = t0 + u * RPL + grp;
-            if (t < c1) {
-                int64_t off;
-                if constexpr (PAGED)
-                    off = (int64_t)s_blk[pb[u]] * a.kv_stride_blk + (int64_t)pr[u] * ss;
-                else
-                    off = t * ss;
-                kw[u] = ld128(kb + off);
-                vw[u] = ld128(vb + off);
-            } else {
-                kw[u] = u32x4{0u, 0u, 0u, 0u};
-                vw[u] = u32x4{0u, 0u, 0u, 0u};
-            }
-            if constexpr (PAGED) {
-                pb[u] += step_q;
-                pr[u] += step_r;
-                if (pr[u] >= a.block_size) {
-                    pr[u] -= a.block_size;
-                    pb[u] += 1;
-                }
-            }
-        }
-    };
-
-    int64_t t0 = c0 + (int64_t)wave * TW;
-    u32x4 kw[U], vw[U], kn[U], vn[U];
-    load(t0, kw, vw);
-    load(t0 + NW * TW, kn, vn);
-    while (t0 < c1) {
-        const int64_t tn = t0 + NW * TW;
-        u32x4 kn2[U], vn2[U];
-        load(tn + NW * TW, kn2, vn2);
-
-        float kf[U][8], vf[U][8];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            unpack8<ST>(kw[u], kf[u]);
-            unpack8<ST>(vw[u], vf[u]);
-        }
+    if (c1 > c0) {
+        // Resident query slice, kept in its 16-bit storage form: q.k is taken with
+        // packed two-element dot products (fp32 accumulation) straight on the
+        // loaded K words, and the score is scaled by scale*log2(e) afterwards.
+        u32x4 qp[GH];
 #pragma unroll
         for (int h = 0; h < GH; ++h) {
-            float s[U];
-            float mx = m[h];
+            const int gi = hg * GH + h;
+            qp[h] = u32x4{0u, 0u, 0u, 0u};
+            if (gi < a.group) {
+                const int64_t n1 = (int64_t)n2 * a.group + gi;
+                qp[h] = ld128(a.q + (b * a.num_heads + n1) * D + sub * 8);
+            }
+        }
+        const float c = a.scale_log2;
+
+        // Per lane group and query head: a reference max m (scores are
+        // exponentiated against it and it moves only when a score exceeds it by
+        // more than 2^kTau), the true running max tm, the sum l and the output.
+        constexpr float kTau = 8.f;
+        float m[GH], tm[GH], l[GH], acc[GH][8];
+#pragma unroll
+        for (int h = 0; h < GH; ++h) {
+            m[h] = kNegInf;
+            tm[h] = kNegInf;
+            l[h] = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+        }
+
+        const int64_t head_off = (PAGED ? 0 : b * a.kv_stride_b) + (int64_t)n2 * a.kv_stride_n + sub * 8;
+        const uint16_t* kb = a.k + head_off;
+        const uint16_t* vb = a.v + head_off;
+        const int64_t ss = a.kv_stride_s;
+
+        // Contiguous cache: one buffer resource per tensor, based at this head's
+        // first row of the chunk and ending after its last valid row, so rows at
+        // or past the length load as zeros without a branch and each load takes
+        // a 32-bit offset (the host keeps (chunk + 256) rows below 2^31 bytes).
+        const int row_bytes = (int)(ss * 2);
+        const int64_t rbase = PAGED ? 0 : b * a.kv_stride_b + (int64_t)n2 * a.kv_stride_n + c0 * ss;
+        const int nrec = (!PAGED && c1 > c0) ? (int)((c1 - c0) * ss * 2) : 0;
+        const buf_rsrc rk = make_rsrc(a.k + rbase, nrec);  // unused by the paged instantiation
+        const buf_rsrc rv = make_rsrc(a.v + rbase, nrec);
+
+        // Paged cache: block ids of the chunk's logical blocks [cb, cb + nblk),
+        // clamped into the physical range, and per-slot (block, row) cursors that
+        // follow the positions load() is called with (t0 + k*NW*TW, k = 0, 1, ...).
+        __shared__ int32_t s_blk[PAGED ? kPagedTableLds : 1];
+        int pb[U], pr[U];
+        int step_q = 0, step_r = 0;
+        if constexpr (PAGED) {
+            const int bs = a.block_size;
+            const int64_t cb = c0 / bs;
+            const int64_t nblk = (c1 > c0) ? (c1 - 1) / bs - cb + 1 : 0;
+            const int32_t* tb = a.block_table + b * a.max_blocks + cb;
+            for (int i = threadIdx.x; i < nblk; i += 256) {
+                int32_t id = tb[i];
+                id = id < 0 ? 0 : (id >= a.num_blocks ? a.num_blocks - 1 : id);
+                s_blk[i] = id;
+            }
+            __syncthreads();
+            const int rel0 = (int)(c0 - cb * bs) + wave * TW + grp;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                float part = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) part = __builtin_fmaf(qf[h][e], kf[u][e], part);
-                part = group_sum<LPR>(part);
-                s[u] = (t0 + u * RPL + grp < c1) ? part : kNegInf;
-                mx = fmaxf(mx, s[u]);
+                pb[u] = (rel0 + u * RPL) / bs;
+                pr[u] = (rel0 + u * RPL) % bs;
             }
-            const float ms = (mx == kNegInf) ? 0.f : mx;
-            const float alpha = fast_exp2(m[h] - ms);
-            float psum = 0.f;
-            float p[U];
+            step_q = (NW * TW) / bs;
+            step_r = (NW * TW) % bs;
+        }
+
+        auto load = [&](int64_t t0, u32x4* kw, u32x4* vw) __attribute__((always_inline)) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                p[u] = fast_exp2(s[u] - ms);
-                psum += p[u];
+                const int64_t t = t0 + u * RPL + grp;
+                if constexpr (!PAGED) {
+                    const int voff = (int)(t - c0) * row_bytes + sub * 16;
+                    kw[u] = buf_ld128(rk, voff);
+                    vw[u] = buf_ld128(rv, voff);
+                } else if (t < c1) {
+                    const int64_t off = (int64_t)s_blk[pb[u]] * a.kv_stride_blk + (int64_t)pr[u] * ss;
+                    kw[u] = ld128(kb + off);
+                    vw[u] = ld128(vb + off);
+                } else {
+                    kw[u] = u32x4{0u, 0u, 0u, 0u};
+                    vw[u] = u32x4{0u, 0u, 0u, 0u};
+                }
+                if constexpr (PAGED) {
+                    pb[u] += step_q;
+                    pr[u] += step_r;
+                    if (pr[u] >= a.block_size) {
+                        pr[u] -= a.block_size;
+                        pb[u] += 1;
+                    }
+                }
             }
-            l[h] = __builtin_fmaf(l[h], alpha, psum);
+        };
+
+        // One iteration: the rows at t0 (+ slot and group offsets) are in (kw, vw).
+        auto consume = [&](int64_t t0, const u32x4* kw, const u32x4* vw) __attribute__((always_inline)) {
+            float vf[U][8];
+#pragma unroll
+            for (int u = 0; u < U; ++u) unpack8<ST>(vw[u], vf[u]);
+#pragma unroll
+            for (int h = 0; h < GH; ++h) {
+                float s[U];
+                float mx = kNegInf;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    float part = dot8<ST>(qp[h], kw[u]);
+                    part = group_sum<LPR>(part) * c;
+                    s[u] = (t0 + u * RPL + grp < c1) ? part : kNegInf;
+                    mx = fmaxf(mx, s[u]);
+                }
+                tm[h] = fmaxf(tm[h], mx);
+                if (mx > m[h] + kTau) {  // rare after the first rows: rescale to the new reference
+                    const float alpha = fast_exp2(m[h] - mx);
+                    l[h] *= alpha;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+                    m[h] = mx;
+                }
+                const float ms = (m[h] == kNegInf) ? 0.f : m[h];
+                float psum = 0.f;
+                float p[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    p[u] = fast_exp2(s[u] - ms);
+                    psum += p[u];
+                }
+                l[h] += psum;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float x = acc[h][e];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) x = __builtin_fmaf(p[u], vf[u][e], x);
+                    acc[h][e] = x;
+                }
+            }
+        };
+
+        // Ring of DEPTH + 1 load buffers: the loop is unrolled over the ring so
+        // every buffer keeps a fixed role (no register rotation), and the rows
+        // DEPTH iterations ahead are in flight while one is consumed.
+        constexpr int64_t STEP = NW * TW;
+        int64_t t0 = c0 + (int64_t)wave * TW;
+        u32x4 kA[U], vA[U], kB[U], vB[U];
+        load(t0, kA, vA);
+        if constexpr (DEPTH == 1) {
+            while (true) {
+                if (t0 >= c1) break;
+                load(t0 + STEP, kB, vB);
+                consume(t0, kA, vA);
+                t0 += STEP;
+                if (t0 >= c1) break;
+                load(t0 + STEP, kA, vA);
+                consume(t0, kB, vB);
+                t0 += STEP;
+            }
+        } else {
+            u32x4 kC[U], vC[U];
+            load(t0 + STEP, kB, vB);
+            while (true) {
+                if (t0 >= c1) break;
+                load(t0 + 2 * STEP, kC, vC);
+                consume(t0, kA, vA);
+                t0 += STEP;
+                if (t0 >= c1) break;
+                load(t0 + 2 * STEP, kA, vA);
+                consume(t0, kB, vB);
+                t0 += STEP;
+                if (t0 >= c1) break;
+                load(t0 + 2 * STEP, kB, vB);
+                consume(t0, kC, vC);
+                t0 += STEP;
+            }
+        }
+
+        // Move each lane group from its reference max to the true max, then merge
+        // the row-slot groups of this wave (lanes that share `sub`).
+#pragma unroll
+        for (int h = 0; h < GH; ++h) {
+            if (tm[h] != kNegInf && tm[h] != m[h]) {
+                const float f = fast_exp2(m[h] - tm[h]);
+                l[h] *= f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] *= f;
+            }
+            m[h] = tm[h];
+            float M = m[h];
+#pragma unroll
+            for (int off = LPR; off < 64; off <<= 1) M = fmaxf(M, shfl_xor(M, off));
+            const float ms = (M == kNegInf) ? 0.f : M;
+            const float f = fast_exp2(m[h] - ms);
+            float lw = l[h] * f;
+#pragma unroll
+            for (int off = LPR; off < 64; off <<= 1) lw += shfl_xor(lw, off);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                float x = acc[h][e] * alpha;
+                float x = acc[h][e] * f;
 #pragma unroll
-                for (int u = 0; u < U; ++u) x = __builtin_fmaf(p[u], vf[u][e], x);
+                for (int off = LPR; off < 64; off <<= 1) x += shfl_xor(x, off);
                 acc[h][e] = x;
             }
-            m[h] = mx;
+            m[h] = M;
+            l[h] = lw;
         }
-        t0 = tn;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            kw[u] = kn[u];
-            vw[u] = vn[u];
-            kn[u] = kn2[u];
-            vn[u] = vn2[u];
-        }
-    }
 
-    // Merge the row-slot groups of this wave (lanes that share `sub`).
+        // Merge the waves through LDS and write the chunk's result.
+        __shared__ float s_m[NW][GH];
+        __shared__ float s_l[NW][GH];
+        __shared__ float s_acc[NW][GH][D];
+        if (grp == 0) {
 #pragma unroll
-    for (int h = 0; h < GH; ++h) {
-        float M = m[h];
+            for (int h = 0; h < GH; ++h)
 #pragma unroll
-        for (int off = LPR; off < 64; off <<= 1) M = fmaxf(M, shfl_xor(M, off));
-        const float ms = (M == kNegInf) ? 0.f : M;
-        const float f = fast_exp2(m[h] - ms);
-        float lw = l[h] * f;
-#pragma unroll
-        for (int off = LPR; off < 64; off <<= 1) lw += shfl_xor(lw, off);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float x = acc[h][e] * f;
-#pragma unroll
-            for (int off = LPR; off < 64; off <<= 1) x += shfl_xor(x, off);
-            acc[h][e] = x;
+                for (int e = 0; e < 8; ++e) s_acc[wave][h][sub * 8 + e] = acc[h][e];
         }
-        m[h] = M;
-        l[h] = lw;
-    }
+        if (lane == 0) {
+#pragma unroll
+            for (int h = 0; h < GH; ++h) {
+                s_m[wave][h] = m[h];
+                s_l[wave][h] = l[h];
+            }
+        }
+        __syncthreads();
 
-    // Merge the waves through LDS and write the chunk's result.
-    __shared__ float s_m[NW][GH];
-    __shared__ float s_l[NW][GH];
-    __shared__ float s_acc[NW][GH][D];
-    if (grp == 0) {
+        for (int idx = threadIdx.x; idx < GH * D; idx += 256) {
+            const int h = idx / D;
+            const int d = idx % D;
+            const int gi = hg * GH + h;
+            if (gi >= a.group) continue;
+            float M = kNegInf;
 #pragma unroll
-        for (int h = 0; h < GH; ++h)
+            for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][h]);
+            const float ms = (M == kNegInf) ? 0.f : M;
+            float Lt = 0.f, A = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s_acc[wave][h][sub * 8 + e] = acc[h][e];
-    }
-    if (lane == 0) {
-#pragma unroll
-        for (int h = 0; h < GH; ++h) {
-            s_m[wave][h] = m[h];
-            s_l[wave][h] = l[h];
-        }
-    }
-    __syncthreads();
-
-    for (int idx = threadIdx.x; idx < GH * D; idx += 256) {
-        const int h = idx / D;
-        const int d = idx % D;
-        const int gi = hg * GH + h;
-        if (gi >= a.group) continue;
-        float M = kNegInf;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][h]);
-        const float ms = (M == kNegInf) ? 0.f : M;
-        float Lt = 0.f, A = 0.f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            const float f = fast_exp2(s_m[w][h] - ms);
-            Lt = __builtin_fmaf(s_l[w][h], f, Lt);
-            A = __builtin_fmaf(s_acc[w][h][d], f, A);
-        }
-        const int64_t row = b * a.num_heads + (int64_t)n2 * a.group + gi;
-        if constexpr (MODE == kFinish) {
-            const bool empty = (M == kNegInf);
-            uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
-            out[row * D + d] = to_bits<ST>(empty ? 0.f : A / Lt);
-            if (d == 0 && a.lse) a.lse[row] = empty ? kPosInf : (M + log2f(Lt)) * kLn2;
-        } else {
-            const int64_t slot = row * a.num_splits + split;
-            const float mo = (M == kNegInf) ? kNegInf : M * kLn2;
-            if constexpr (MODE == kFused) {  // device-coherent stores: another CU's L2 may merge them
-                __hip_atomic_store(a.o_part + slot * D + d, A, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (d == 0) {
-                    __hip_atomic_store(a.m_part + slot, mo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(a.l_part + slot, Lt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
+            for (int w = 0; w < NW; ++w) {
+                const float f = fast_exp2(s_m[w][h] - ms);
+                Lt = __builtin_fmaf(s_l[w][h], f, Lt);
+                A = __builtin_fmaf(s_acc[w][h][d], f, A);
+            }
+            const int64_t row = b * a.num_heads + (int64_t)n2 * a.group + gi;
+            if constexpr (MODE == kFinish) {
+                const bool empty = (M == kNegInf);
+                uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+                out[row * D + d] = to_bits<ST>(empty ? 0.f : A / Lt);
+                if (d == 0 && a.lse) a.lse[row] = empty ? kPosInf : (M + log2f(Lt)) * kLn2;
             } else {
-                a.o_part[slot * D + d] = A;
-                if (d == 0) {
-                    a.m_part[slot] = mo;
-                    a.l_part[slot] = Lt;
+                const int64_t slot = row * a.num_splits + split;
+                const float mo = (M == kNegInf) ? kNegInf : M * kLn2;
+                if constexpr (MODE == kFused) {  // device-coherent stores: another CU's L2 may merge them
+                    __hip_atomic_store(a.o_part + slot * D + d, A, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (d == 0) {
+                        __hip_atomic_store(a.m_part + slot, mo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_store(a.l_part + slot, Lt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                } else {
+                    a.o_part[slot * D + d] = A;
+                    if (d == 0) {
+                        a.m_part[slot] = mo;
+                        a.l_part[slot] = Lt;
+                    }
+                }
+            }
+        }
+    } else {
+        // A chunk at or past the length: its empty partial (or the row
+        // defaults of a one-split plan) without touching K or V.
+        for (int idx = threadIdx.x; idx < GH * D; idx += 256) {
+            const int h = idx / D;
+            const int d = idx % D;
+            const int gi = hg * GH + h;
+            if (gi >= a.group) continue;
+            const int64_t row = b * a.num_heads + (int64_t)n2 * a.group + gi;
+            if constexpr (MODE == kFinish) {
+                reinterpret_cast<uint16_t*>(a.out)[row * D + d] = 0;
+                if (d == 0 && a.lse) a.lse[row] = kPosInf;
+            } else {
+                const int64_t slot = row * a.num_splits + split;
+                if constexpr (MODE == kFused) {
+                    __hip_atomic_store(a.o_part + slot * D + d, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (d == 0) {
+                        __hip_atomic_store(a.m_part + slot, kNegInf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_store(a.l_part + slot, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                } else {
+                    a.o_part[slot * D + d] = 0.f;
+                    if (d == 0) {
+                        a.m_part[slot] = kNegInf;
+                        a.l_part[slot] = 0.f;
+                    }
                 }
             }
         }
@@ -540,6 +618,40 @@ static hipError_t dispatch_stage1_gh(const DecodeArgs& a, int gh, bool finish, i
         case 8: return dispatch_stage1<ST, D, 8>(a, finish, blocks, s);
         default: return hipErrorInvalidValue;
     }
+}
+
+template <typename ST, int D>
+static const void* stage1_symbol(int gh, bool paged) {
+    switch (gh) {
+        case 1: return paged ? (const void*)&decode_stage1_kernel<ST, D, 1, kPartial, true>
+                             : (const void*)&decode_stage1_kernel<ST, D, 1, kPartial, false>;
+        case 2: return paged ? (const void*)&decode_stage1_kernel<ST, D, 2, kPartial, true>
+                             : (const void*)&decode_stage1_kernel<ST, D, 2, kPartial, false>;
+        case 4: return paged ? (const void*)&decode_stage1_kernel<ST, D, 4, kPartial, true>
+                             : (const void*)&decode_stage1_kernel<ST, D, 4, kPartial, false>;
+        case 8: return paged ? (const void*)&decode_stage1_kernel<ST, D, 8, kPartial, true>
+                             : (const void*)&decode_stage1_kernel<ST, D, 8, kPartial, false>;
+        default: return nullptr;
+    }
+}
+
+int decode_stage1_residency(int dtype, int head_dim, int heads_per_wg, bool paged) {
+    const void* f = nullptr;
+    if (dtype == 1) {
+        if (head_dim == 64) f = stage1_symbol<BF16, 64>(heads_per_wg, paged);
+        if (head_dim == 128) f = stage1_symbol<BF16, 128>(heads_per_wg, paged);
+        if (head_dim == 256) f = stage1_symbol<BF16, 256>(heads_per_wg, paged);
+    } else {
+        if (head_dim == 64) f = stage1_symbol<F16, 64>(heads_per_wg, paged);
+        if (head_dim == 128) f = stage1_symbol<F16, 128>(heads_per_wg, paged);
+        if (head_dim == 256) f = stage1_symbol<F16, 256>(heads_per_wg, paged);
+    }
+    int n = 0;
+    if (!f || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 256, 0) != hipSuccess) {
+        (void)hipGetLastError();  // no device answered: leave no sticky error behind
+        return 0;
+    }
+    return n;
 }
 
 hipError_t launch_decode_stage1(const DecodeArgs& a, int dtype, int head_dim, int heads_per_wg,

@@ -56,6 +56,30 @@ __device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
     }
 }
 
+// Dot product of eight packed 16-bit values with fp32 accumulation
+// (v_dot2c_f32_{bf16,f16}: each step adds two exact products).
+template <typename ST>
+__device__ __forceinline__ float dot8(const u32x4 a, const u32x4 b) {
+    // The pairs are taken with vector shuffles of the whole 8-element value:
+    // bit-casting single 32-bit lanes of the 128-bit vector has been seen to
+    // make the compiler read the first register of the tuple for every pair.
+    float r = 0.f;
+    if constexpr (ST::is_bf16) {
+        const bf16x8 av = __builtin_bit_cast(bf16x8, a), bv = __builtin_bit_cast(bf16x8, b);
+        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(av, av, 0, 1), __builtin_shufflevector(bv, bv, 0, 1), r, false);
+        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(av, av, 2, 3), __builtin_shufflevector(bv, bv, 2, 3), r, false);
+        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(av, av, 4, 5), __builtin_shufflevector(bv, bv, 4, 5), r, false);
+        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(av, av, 6, 7), __builtin_shufflevector(bv, bv, 6, 7), r, false);
+    } else {
+        const f16x8 av = __builtin_bit_cast(f16x8, a), bv = __builtin_bit_cast(f16x8, b);
+        r = __builtin_amdgcn_fdot2(__builtin_shufflevector(av, av, 0, 1), __builtin_shufflevector(bv, bv, 0, 1), r, false);
+        r = __builtin_amdgcn_fdot2(__builtin_shufflevector(av, av, 2, 3), __builtin_shufflevector(bv, bv, 2, 3), r, false);
+        r = __builtin_amdgcn_fdot2(__builtin_shufflevector(av, av, 4, 5), __builtin_shufflevector(bv, bv, 4, 5), r, false);
+        r = __builtin_amdgcn_fdot2(__builtin_shufflevector(av, av, 6, 7), __builtin_shufflevector(bv, bv, 6, 7), r, false);
+    }
+    return r;
+}
+
 // fp32 -> 16-bit storage bits, round to nearest even.
 template <typename ST>
 __device__ __forceinline__ uint16_t to_bits(float x) {
@@ -109,6 +133,22 @@ __device__ __forceinline__ float xor32(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
+
+// Buffer resources: a base address and a byte range; a load at or past the
+// range returns zeros.  The resource type exists only in the device pass.
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+__device__ __forceinline__ buf_rsrc make_rsrc(const void* base, int nrec) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_ld128(buf_rsrc r, int voff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+#else
+struct buf_rsrc {};
+__device__ buf_rsrc make_rsrc(const void*, int);
+__device__ u32x4 buf_ld128(buf_rsrc, int);
+#endif
 
 typedef __attribute__((address_space(3))) void lds_void;
 

@@ -136,6 +136,9 @@ constexpr int kFusedMaxSplits = 256;
 // Launchers: return hipSuccess or the launch error.  dtype: 0 = fp16, 1 = bf16.
 hipError_t launch_decode_stage1(const DecodeArgs& a, int dtype, int head_dim, int heads_per_wg,
                                 bool finish, int64_t batch, hipStream_t stream);
+// Stage-1 workgroups one CU holds at once for this instantiation, from the
+// runtime's occupancy calculator; 0 when no device answers.
+int decode_stage1_residency(int dtype, int head_dim, int heads_per_wg, bool paged);
 hipError_t launch_combine(const CombineArgs& a, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int mask_mode,
                           int64_t batch, hipStream_t stream);

@@ -187,7 +187,7 @@ def main():
                          "stage1_ms": round(s1, 5), "combine_ms": round(cb, 5),
                          "leg_ms": round(leg, 5), "kv_gbs": round(value, 2),
                          "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4)}
-        out["roofline"] = {"kernel": "decode_stage1_kernel<BF16,128,1,false,false>", "bound": "hbm",
+        out["roofline"] = {"kernel": "decode_stage1_kernel<BF16,128,1,0,false>", "bound": "hbm",
                            "achieved": round(s1_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(s1_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                            "algorithmic_bytes_per_launch": dec["kv_bytes"] + dec["qo_bytes"]}

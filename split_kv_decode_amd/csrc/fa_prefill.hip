@@ -28,7 +28,9 @@
 //
 // Masks.  MASK 0 none; 1 causal from indices (tiles past the diagonal are
 // not visited); 2 a boolean tensor read element by element; 3 a boolean
-// tensor with contiguous key rows, staged through LDS with the K/V tiles;
+// tensor with contiguous key rows, staged through LDS with the K/V tiles (a
+// wave skips a tile its rows mask entirely, and the element tests of a tile
+// that masks none of its rows);
 // 4 the window band of the FlashAttn developer guide (1.5, mode 4): only the
 // KV tiles that intersect the band of the query tile are visited, and a wave
 // skips tiles outside the band of its 32 rows.
@@ -304,6 +306,7 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
         // 32*tt + 8*g + 4*half + [0,4) of row 32*wave + col -- and a
         // wave-uniform skip of tiles the mask excludes entirely for its rows.
         uint32_t mw[2][4];
+        bool mask_clear = false;  // MASK 3: no key of this tile is masked for any row of the wave
         if (MASK == 3) {
             bool lane_all = !qvalid || j0 >= L;
 #pragma unroll
@@ -322,6 +325,12 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
                 for (int g = 0; g < 4; ++g)
                     none_zero = none_zero && (((mw[tt][g] - 0x01010101u) & ~mw[tt][g] & 0x80808080u) == 0u);
             lane_all = lane_all || none_zero;
+            uint32_t any_set = 0u;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) any_set |= mw[tt][g];
+            mask_clear = __all(any_set == 0u);
             if (__all(lane_all)) {
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 __syncthreads();
@@ -364,7 +373,7 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
         // diagonal of this wave's rows, or under a boolean mask.  Accumulator
         // register r of tile tt holds key j0 + 32*tt + 8*(r/4) + 4*half + r%4.
         const bool need_mask = (j0 + BN > L) || (MASK == 1 && j0 + BN - 1 > wrow0) || (MASK == 2) ||
-                               (MASK == 3) ||
+                               (MASK == 3 && !mask_clear) ||
                                (MASK == 4 && (j0 < wrow0 + 31 - a.win_left || j0 + BN - 1 > wrow0 + a.win_right));
         if (MASK == 3) {
 #pragma unroll

@@ -4,6 +4,7 @@
 // never synchronises.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -146,10 +147,43 @@ int heads_per_workgroup(int64_t g) {
     return 1;
 }
 
+// Per-device facts the planner needs on every decode call, queried once per
+// device (HIP device attribute and occupancy queries cost host time that a
+// per-token serving loop should not pay).  Entries are written once with the
+// same value by any thread that races to fill them.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+// Stage-1 residency per device and (dtype, D, heads per workgroup, paged):
+// 2 x 3 x 4 x 2 = 48 instantiations; 0 = not asked yet, -1 = no answer.
+std::atomic<int> g_resident[kMaxDevices][48];
+
+int current_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+    return dev;
+}
+
 int device_cus() {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    const int dev = current_device();
+    if (dev < 0) return 256;
+    int n = g_cus[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+    g_cus[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+int stage1_residency(int dtype, int D, int gh, bool paged) {
+    const int dev = current_device();
+    const int di = D == 64 ? 0 : (D == 128 ? 1 : 2);
+    const int gi = gh == 1 ? 0 : (gh == 2 ? 1 : (gh == 4 ? 2 : 3));
+    const int key = ((dtype * 3 + di) * 4 + gi) * 2 + (paged ? 1 : 0);
+    if (dev >= 0) {
+        const int cached = g_resident[dev][key].load(std::memory_order_relaxed);
+        if (cached != 0) return cached > 0 ? cached : 0;
+    }
+    const int n = fa::decode_stage1_residency(dtype, D, gh, paged);
+    if (dev >= 0) g_resident[dev][key].store(n > 0 ? n : -1, std::memory_order_relaxed);
     return n;
 }
 
@@ -195,8 +229,7 @@ int64_t chunk_cap(const fa_params* p, const Shape& s) {
 void plan_splits(const fa_params* p, const Shape& s, int num_cus, int64_t* splits, int64_t* chunk) {
     const int gh = heads_per_workgroup(s.g);
     const int64_t units = s.B * s.KVN * (s.g / gh);
-    const int resident = fa::decode_stage1_residency(p->dtype == FA_BF16 ? 1 : 0, (int)s.D, gh,
-                                                     p->kv_layout != FA_KV_CONTIGUOUS);
+    const int resident = stage1_residency(p->dtype == FA_BF16 ? 1 : 0, (int)s.D, gh, p->kv_layout != FA_KV_CONTIGUOUS);
     const int64_t target = (resident > 0 ? resident : kWgPerCu) * int64_t(num_cus > 0 ? num_cus : 256);
     int64_t want = (target + units - 1) / units;
     if (want < 1) want = 1;

@@ -8,7 +8,10 @@ input, with every input already resident in HBM:
     combine (fa_combine), with the split plan fa_fwd would choose;
   * prefill leg -- mask-free prefill, BSND, B=2, 32 heads, S=4096, D=128, bf16
     (fa_fwd).
-Each kernel launch is bracketed by HIP events on the stream it runs on.
+Each kernel launch is bracketed by HIP events on the stream it runs on, and the
+median over the timed steps is reported (p10 / p90 beside it).  Before every
+timed decode call a 1 GiB buffer is read outside the events, so the KV cache is
+not served from the 256 MB of L2 + MALL.
 
 The printed JSON line reports decode KV-read GB/s as ``value`` (and the prefill
 TFLOP/s beside it), a ``roofline`` object for the dominant kernel (decode stage
@@ -126,6 +129,11 @@ def main():
         flops = 4.0 * ps.B * ps.QN * ps.QS * ps.KVS * ps.D
         pre = dict(spec=ps, q=pq, k=pk, v=pv, p=pp, out=pout, lse=plse, flops=flops)
         del pinp
+    # Read before every timed decode call, outside its events, so the 256 MB of
+    # L2 + MALL holds none of the KV cache when the call starts.  A read leaves
+    # the caches clean; a write would leave dirty lines whose write-back then
+    # competes with the decode's reads.
+    flush = torch.ones((1 << 28,), dtype=torch.int32, device=dev) if dec is not None else None
     copy_src = copy_dst = None
     if args.copy_calibrate:
         copy_src = torch.ones((1 << 29,), dtype=torch.int16, device=dev)  # 1 GiB
@@ -135,6 +143,7 @@ def main():
 
     def step(ev):
         if dec is not None:
+            flush.sum()
             ev[0].record(stream)
             fa.fa_decode_splitkv(dec["p"], dec["splits"], dec["chunk"], dec["q"], dec["k"], dec["v"],
                                  dec["o"], dec["m"], dec["l"], stream)
@@ -165,8 +174,12 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    def mean_ms(a, b):
-        return float(np.mean([ev[a].elapsed_time(ev[b]) for ev in events]))
+    def stats_ms(a, b):
+        t = np.array([ev[a].elapsed_time(ev[b]) for ev in events])
+        return float(np.median(t)), float(np.percentile(t, 10)), float(np.percentile(t, 90))
+
+    def median_ms(a, b):  # p10 / p90 are reported beside it
+        return stats_ms(a, b)[0]
 
     out = {"metric": METRIC, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
@@ -175,30 +188,37 @@ def main():
     config = {"workload": "+".join(legs), "parallelism": "single GPU"}
     csrc = os.path.join(ROOT, "split_kv_decode_amd", "csrc")
     if dec is not None:
-        s1 = mean_ms(0, 1)
-        cb = mean_ms(1, 2)
+        s1 = median_ms(0, 1)
+        cb = median_ms(1, 2)
         leg = s1 + cb
         value = (dec["kv_bytes"] + dec["qo_bytes"]) / (leg * 1e-3) / 1e9
         s1_gbs = (dec["kv_bytes"] + dec["qo_bytes"]) / (s1 * 1e-3) / 1e9
         traffic = stored_traffic(os.path.join(csrc, "fa_decode.hip"), "decode_stage1_128k")
         out["value"] = round(value, 2)
+        legs_t = np.array([ev[0].elapsed_time(ev[2]) for ev in events])
         out["decode"] = {"workload": "decode_128k: BNSD B=1 Q_N=KV_N=32 Q_S=1 KV_S=131072 D=128 bf16",
                          "num_splits": dec["splits"], "chunk": dec["chunk"],
                          "stage1_ms": round(s1, 5), "combine_ms": round(cb, 5),
                          "leg_ms": round(leg, 5), "kv_gbs": round(value, 2),
-                         "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4)}
+                         "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+                         "leg_ms_p10_p90": [round(float(np.percentile(legs_t, 10)), 5),
+                                            round(float(np.percentile(legs_t, 90)), 5)],
+                         "timing": "median over the timed steps; a 1 GiB buffer is read before each "
+                                   "decode call, outside its events, so no KV is cached"}
         out["roofline"] = {"kernel": "decode_stage1_kernel<BF16,128,1,0,false>", "bound": "hbm",
                            "achieved": round(s1_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(s1_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                            "algorithmic_bytes_per_launch": dec["kv_bytes"] + dec["qo_bytes"]}
         config.update({"decode_B": 1, "decode_heads": 32, "decode_kv_seq": 131072, "head_dim": 128})
     if pre is not None:
-        pm = mean_ms(3, 4)
+        pm = median_ms(3, 4)
         tflops = pre["flops"] / (pm * 1e-3) / 1e12
         ps = pre["spec"]
         traffic = stored_traffic(os.path.join(csrc, "fa_prefill.hip"), "prefill_4k")
+        _, p10, p90 = stats_ms(3, 4)
         out["prefill"] = {"workload": "prefill_4k: BSND B=2 N=32 S=4096 D=128 bf16, no mask",
-                          "ms": round(pm, 5), "tflops": round(tflops, 2),
+                          "ms": round(pm, 5), "ms_p10_p90": [round(p10, 5), round(p90, 5)],
+                          "tflops": round(tflops, 2),
                           "frac_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
         out["roofline_prefill"] = {"kernel": "prefill_kernel<BF16,128,0>", "bound": "mfma",
                                    "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
@@ -232,9 +252,28 @@ def main():
     print(json.dumps(out))
 
 
-def extra_workloads(fa, fa_synth, np, torch, dev16, stream, warmup=3, iters=10):
-    """Time the other configurations with fa_fwd (events on the launch stream)."""
+def timed(fn, torch, np, stream, warmup, iters, flush=None):
+    """Median ms of fn() over iters calls, each between events on the stream; with a flush
+    buffer, the buffer is read before each call, outside its events."""
+    for _ in range(warmup):
+        fn()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for a, b in evs:
+        if flush is not None:
+            flush.sum()
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+
+def extra_workloads(fa, fa_synth, np, torch, dev16, stream, warmup=3, iters=20):
+    """Time the other configurations with fa_fwd (events on the launch stream; decode calls
+    start with no KV in L2 or MALL)."""
     res = {}
+    flush = torch.ones((1 << 28,), dtype=torch.int32, device=torch.device("cuda:0"))
     # (workload, mask mode override, paged cache (kv_layout, block_size) or None)
     cases = [("prefill_small", None, None), ("decode_gqa", None, None),
              ("decode_gqa", None, ("PA_BBND", 128)), ("decode_128k", None, ("PA_BNBD", 128)),
@@ -271,16 +310,8 @@ def extra_workloads(fa, fa_synth, np, torch, dev16, stream, warmup=3, iters=10):
         lse = torch.empty((s.B, s.QN, s.QS), dtype=torch.float32, device=q.device)
         nbytes = fa.fa_workspace_size(p)
         ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=q.device)
-        for _ in range(warmup):
-            fa.fa_fwd(p, q, k, v, out, lse, ws, nbytes, stream)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(iters)]
-        for a, b in evs:
-            a.record(stream)
-            fa.fa_fwd(p, q, k, v, out, lse, ws, nbytes, stream)
-            b.record(stream)
-        torch.cuda.synchronize()
-        ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        ms = timed(lambda: fa.fa_fwd(p, q, k, v, out, lse, ws, nbytes, stream), torch, np, stream,
+                   warmup, iters, flush if s.QS == 1 else None)
         key = name if mode is None else f"{name}_{mode}"
         if mode == "window":
             key = f"{name}_window{window[0]}_{window[1]}"
@@ -316,11 +347,11 @@ def extra_workloads(fa, fa_synth, np, torch, dev16, stream, warmup=3, iters=10):
         del q, k, v, out, lse, ws, mask, inp, block_table
         torch.cuda.empty_cache()
     res.update(packed_workload(fa, fa_synth, np, torch, dev16, stream, warmup, iters))
-    res.update(fused_decode(fa, fa_synth, np, torch, dev16, stream, warmup, iters))
+    res.update(fused_decode(fa, fa_synth, np, torch, dev16, stream, warmup, iters, flush))
     return res
 
 
-def fused_decode(fa, fa_synth, np, torch, dev16, stream, warmup, iters):
+def fused_decode(fa, fa_synth, np, torch, dev16, stream, warmup, iters, flush):
     """The single-launch split-KV (fa_decode_fused) on the two decode workloads, with the
     split plan fa_fwd picks, for comparison with fa_fwd's stage 1 + combine."""
     res = {}
@@ -334,16 +365,8 @@ def fused_decode(fa, fa_synth, np, torch, dev16, stream, warmup, iters):
         ws = torch.zeros((nbytes,), dtype=torch.uint8, device=q.device)
         out = torch.empty_like(q)
         lse = torch.empty((s.B, s.QN, 1), dtype=torch.float32, device=q.device)
-        for _ in range(warmup):
-            fa.fa_decode_fused(p, sp, ch, q, k, v, ws, nbytes, out, lse, stream)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(iters)]
-        for a, b in evs:
-            a.record(stream)
-            fa.fa_decode_fused(p, sp, ch, q, k, v, ws, nbytes, out, lse, stream)
-            b.record(stream)
-        torch.cuda.synchronize()
-        ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        ms = timed(lambda: fa.fa_decode_fused(p, sp, ch, q, k, v, ws, nbytes, out, lse, stream), torch,
+                   np, stream, warmup, iters, flush)
         L = np.full(s.B, s.KVS) if inp.lens is None else np.clip(inp.lens, 0, s.KVS)
         nb = float(L.sum()) * s.KVN * s.D * 2 * 2 + 2 * s.B * s.QN * s.D * 2
         gbs = nb / (ms * 1e-3) / 1e9
@@ -367,16 +390,8 @@ def packed_workload(fa, fa_synth, np, torch, dev16, stream, warmup, iters):
     lse = torch.empty((p.q_seq, p.num_heads), dtype=torch.float32, device=q.device)
     nbytes = fa.fa_workspace_size(p)
     ws = torch.empty((nbytes,), dtype=torch.uint8, device=q.device)
-    for _ in range(warmup):
-        fa.fa_fwd(p, q, k, v, out, lse, ws, nbytes, stream)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(iters)]
-    for a, b in evs:
-        a.record(stream)
-        fa.fa_fwd(p, q, k, v, out, lse, ws, nbytes, stream)
-        b.record(stream)
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ms = timed(lambda: fa.fa_fwd(p, q, k, v, out, lse, ws, nbytes, stream), torch, np, stream,
+               warmup, iters)
     L = x.q_lens.astype(np.float64)
     fl = 4.0 * x.QN * x.D * float(np.sum(L * (L + 1) / 2))
     tf = fl / (ms * 1e-3) / 1e12

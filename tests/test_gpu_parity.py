@@ -407,6 +407,8 @@ PREFILL_CASES = [
     dict(B=1, QN=3, KVN=3, QS=5, KVS=1000, D=128, lens=(1, 1000)),
     dict(B=1, QN=2, KVN=1, QS=150, KVS=150, D=128, mask="causal", scale=-0.09),
     dict(B=1, QN=2, KVN=2, QS=96, KVS=200, D=64, scale=-0.125, layout="BSND"),
+    dict(B=1, QN=2, KVN=2, QS=300, KVS=77, D=128, scale=-0.07, layout="BSND"),  # 256-row tiles, ragged
+    dict(B=2, QN=4, KVN=2, QS=513, KVS=640, D=128, lens=(0, 640)),
     dict(B=2, QN=4, KVN=2, QS=300, KVS=300, D=256, mask="causal"),          # D = 256
     dict(B=1, QN=2, KVN=1, QS=129, KVS=700, D=256, dtype="f16", layout="BSND", lens=(1, 700)),
     dict(B=1, QN=2, KVN=2, QS=64, KVS=64, D=256, mask="bool_causal"),

@@ -37,8 +37,9 @@
 //
 // Softmax.  Exponentials are taken against the running max before the tile's
 // max is known, and the output is rescaled only when a row max grows by more
-// than 2^8 (wave-uniform test); both keep the vector work per tile close to
-// one FMA, one exp, one add, half a max and half a convert per score.
+// than 2^8 (wave-uniform test, decided from the sum of the exponentials, so
+// the tile max itself is computed only on that rare path); the vector work
+// per tile is about one FMA, one exp, one add and half a convert per score.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
     constexpr int CPR = D / 8;          // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;       // rows per direct-to-LDS wave load
     constexpr int NIW = TB / 1024 / 4;  // wave loads per wave per tile (K, and again V)
-    constexpr float kTau = 8.f;         // rescale only when a row max grows by more than 2^8
+    constexpr float kPmax = 256.f;      // rescale only when an exponential could exceed 2^8
     __shared__ __attribute__((aligned(1024))) unsigned char sK0[TB];
     __shared__ __attribute__((aligned(1024))) unsigned char sK1[TB];
     __shared__ __attribute__((aligned(1024))) unsigned char sV0[TB];
@@ -404,19 +405,13 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
                 }
             }
         }
-        float tmax = kNegInf;
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[tt][r]);
-        tmax = fmaxf(tmax, xor32(tmax)) * c;
 
         // P^T as the B operand of O^T = V^T P^T.  K-step ks covers keys
         // [16*ks, +16) of the tile; slot e of half h is key 4h+e (e<4) or
         // 8+4h+(e-4) -- the order the accumulator already holds them in.
         // Exponentials are taken against the running max; in the rare case a
-        // row max grew by more than 2^kTau they are recomputed after the
-        // rescale, so every exponential stays below 2^kTau.
+        // row max grew by more than 8 they are recomputed after the rescale,
+        // so every exponential stays below kPmax = 2^8.
         V8 pb[4];
         float psum = 0.f;
         auto exps = [&](float nmx) __attribute__((always_inline)) {
@@ -432,7 +427,18 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
             }
         };
         exps((m_run == kNegInf) ? 0.f : -m_run);
-        if (__any(tmax > m_run + kTau)) {
+        // Every p >= 0, so a half-row sum of at most kPmax proves no score
+        // exceeded the running max by more than 8: the tile max is needed
+        // only on the rare path that moves the max (or while a row of the
+        // query has seen no valid key yet, so an empty row keeps m = -inf;
+        // rows past the query length never trigger it).
+        if (__any(psum > kPmax || (m_run == kNegInf && qvalid))) {
+            float tmax = kNegInf;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[tt][r]);
+            tmax = fmaxf(tmax, xor32(tmax)) * c;
             const float mnew = fmaxf(m_run, tmax);
             const float alpha = fast_exp2(m_run - ((mnew == kNegInf) ? 0.f : mnew));
 #pragma unroll
@@ -521,7 +527,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     constexpr int RPI = 64 / CPR;
     constexpr int NIW = TB / 1024 / NWV;  // wave loads per wave per tile (K, and again V)
     static_assert(NIW >= 1, "tile too small for 8 waves");
-    constexpr float kTau = 8.f;
+    constexpr float kPmax = 256.f;
     __shared__ __attribute__((aligned(1024))) unsigned char sK0[TB];
     __shared__ __attribute__((aligned(1024))) unsigned char sK1[TB];
     __shared__ __attribute__((aligned(1024))) unsigned char sV0[TB];
@@ -654,12 +660,6 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
                 }
             }
         }
-        float tmax = kNegInf;
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[tt][r]);
-        tmax = fmaxf(tmax, xor32(tmax)) * c;
         float psum = 0.f;
         auto exps = [&](float nmx) __attribute__((always_inline)) {
             psum = 0.f;
@@ -674,7 +674,18 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
             }
         };
         exps((m_run == kNegInf) ? 0.f : -m_run);
-        if (__any(tmax > m_run + kTau)) {
+        // Every p >= 0, so a half-row sum of at most kPmax proves no score
+        // exceeded the running max by more than 8: the tile max is needed
+        // only on the rare path that moves the max (or while a row of the
+        // query has seen no valid key yet, so an empty row keeps m = -inf;
+        // rows past the query length never trigger it).
+        if (__any(psum > kPmax || (m_run == kNegInf && qvalid))) {
+            float tmax = kNegInf;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[tt][r]);
+            tmax = fmaxf(tmax, xor32(tmax)) * c;
             const float mnew = fmaxf(m_run, tmax);
             const float alpha = fast_exp2(m_run - ((mnew == kNegInf) ? 0.f : mnew));
 #pragma unroll

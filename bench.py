@@ -133,7 +133,7 @@ def main():
     # L2 + MALL holds none of the KV cache when the call starts.  A read leaves
     # the caches clean; a write would leave dirty lines whose write-back then
     # competes with the decode's reads.
-    flush = torch.ones((1 << 28,), dtype=torch.int32, device=dev) if dec is not None else None
+    flush = torch.ones((1 << 28,), dtype=torch.float32, device=dev) if dec is not None else None
     copy_src = copy_dst = None
     if args.copy_calibrate:
         copy_src = torch.ones((1 << 29,), dtype=torch.int16, device=dev)  # 1 GiB
@@ -220,7 +220,7 @@ def main():
                           "ms": round(pm, 5), "ms_p10_p90": [round(p10, 5), round(p90, 5)],
                           "tflops": round(tflops, 2),
                           "frac_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
-        out["roofline_prefill"] = {"kernel": "prefill_kernel<BF16,128,0>", "bound": "mfma",
+        out["roofline_prefill"] = {"kernel": "prefill_pp_kernel<BF16,128>", "bound": "mfma",
                                    "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                                    "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                                    "traffic": traffic, "algorithmic_flop_per_launch": pre["flops"]}
@@ -273,7 +273,7 @@ def extra_workloads(fa, fa_synth, np, torch, dev16, stream, warmup=3, iters=20):
     """Time the other configurations with fa_fwd (events on the launch stream; decode calls
     start with no KV in L2 or MALL)."""
     res = {}
-    flush = torch.ones((1 << 28,), dtype=torch.int32, device=torch.device("cuda:0"))
+    flush = torch.ones((1 << 28,), dtype=torch.float32, device=torch.device("cuda:0"))
     # (workload, mask mode override, paged cache (kv_layout, block_size) or None)
     cases = [("prefill_small", None, None), ("decode_gqa", None, None),
              ("decode_gqa", None, ("PA_BBND", 128)), ("decode_128k", None, ("PA_BNBD", 128)),

@@ -166,9 +166,17 @@ fa_status fa_workspace_size(const fa_params *p, size_t *bytes);
  * MI355X than the fused single launch of fa_decode_fused).  The workspace
  * must then be at least fa_workspace_size bytes, 256-byte aligned; its
  * contents need no initialisation.
- * Every other case runs the prefill kernel and needs no workspace, except
- * the packed layout FA_TND, which needs fa_workspace_size bytes (256-byte
- * aligned) for the cost-ordered list of its query tiles. */
+ * Every other case runs the prefill kernel.  The packed layout FA_TND needs
+ * fa_workspace_size bytes (256-byte aligned) for the cost-ordered list of its
+ * query tiles.  A boolean mask whose rows are contiguous, 16-byte aligned key
+ * runs (mask_stride[3] == 1; the pointer, the other strides and kv_seq
+ * multiples of 16) takes an optional workspace of fa_workspace_size bytes:
+ * given one (256-byte aligned, else FA_ERR_PARAM_INVALID, as for one too
+ * small), a first kernel summarises the mask per tile of 128 query rows x 64
+ * keys (any key visible, any key masked) and the prefill then skips the tiles
+ * the mask hides entirely, as the developer guide (1.5) does for the window
+ * mode; with workspace NULL it visits every tile.  The results are the same
+ * either way.  Other prefill cases take no workspace (it is ignored). */
 fa_status fa_fwd(const fa_params *p, const void *q, const void *k, const void *v,
                  void *out, float *lse, void *workspace, size_t workspace_bytes,
                  void *stream);

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfa_mi355x.so")
 OBJDIR = os.path.join(HERE, "_build")
 
-SOURCES = ["fa_api.cpp", "fa_decode.hip", "fa_prefill.hip", "fa_varlen.hip"]
+SOURCES = ["fa_api.cpp", "fa_decode.hip", "fa_prefill.hip", "fa_varlen.hip", "fa_masksum.hip"]
 ARCH = "gfx950"
 
 # hipcc flags for every translation unit.  Packed fp32 instructions are turned
@@ -50,7 +50,7 @@ def build(verbose: bool = False, extra=()) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
         objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
     tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

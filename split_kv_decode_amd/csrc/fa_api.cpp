@@ -252,6 +252,41 @@ bool decode_path(const fa_params* p) {
 int64_t varlen_capacity(const Shape& s) { return (s.QS + 127) / 128 + s.B + 1; }
 size_t varlen_bytes(const Shape& s) { return round_up(size_t(varlen_capacity(s)) * 8, 256); }
 
+// Prefill kernel instantiation for the mask: 0 none, 1 causal, 2 boolean
+// tensor read element by element, 3 boolean tensor staged through LDS (rows
+// of contiguous, 16-byte aligned key runs), 4 window.
+int prefill_mask_kind(const fa_params* p, const Shape& s) {
+    if (p->mask_mode == FA_MASK_CAUSAL) return 1;
+    if (p->mask_mode == FA_MASK_WINDOW) return 4;
+    if (p->mask_mode != FA_MASK_BOOL) return 0;
+    const int64_t* st = p->mask_stride;
+    const bool rows_ok = st[3] == 1 && aligned(p->mask, 16) && st[0] % 16 == 0 && st[1] % 16 == 0 &&
+                         st[2] % 16 == 0 && s.KVS % 16 == 0 && st[2] < (int64_t(1) << 23);
+    return rows_ok ? 3 : 2;
+}
+
+// Staged boolean mask: geometry of its per-tile summary (one row of words
+// per mask slice and 128-row query tile).  blocks == 0 when the mask is not
+// staged, or the summary would need more than 2^31 - 1 workgroups.
+struct MaskSummaryGeom {
+    int64_t q_tiles, words, slices_n, blocks;
+    size_t bytes;
+};
+MaskSummaryGeom mask_summary_geom(const fa_params* p, const Shape& s) {
+    MaskSummaryGeom g{0, 0, 0, 0, 0};
+    if (p->layout == FA_TND || decode_path(p) || prefill_mask_kind(p, s) != 3) return g;
+    const int64_t kv_tiles = (s.KVS + fa::kMaskKeysPerTile - 1) / fa::kMaskKeysPerTile;
+    g.q_tiles = (s.QS + fa::kMaskRowsPerTile - 1) / fa::kMaskRowsPerTile;
+    g.words = (kv_tiles + fa::kMaskTilesPerWord - 1) / fa::kMaskTilesPerWord;
+    g.slices_n = p->mask_stride[1] ? s.QN : 1;
+    const int64_t slices = (p->mask_stride[0] ? s.B : 1) * g.slices_n;
+    const double blocks = double(slices) * double(g.q_tiles) * double(g.words);
+    if (blocks > double(0x7fffffff)) return MaskSummaryGeom{0, 0, 0, 0, 0};
+    g.blocks = slices * g.q_tiles * g.words;
+    g.bytes = round_up(size_t(g.blocks) * 4, 256);
+    return g;
+}
+
 void fill_decode_args(const fa_params* p, const Shape& s, fa::DecodeArgs* a) {
     std::memset(a, 0, sizeof *a);
     a->lens = p->actual_seq_lengths;
@@ -378,18 +413,27 @@ fa_status run_prefill(const fa_params* p, const Shape& s, const void* q, const v
     auto win = [](int64_t w) { return (w < 0 || w > 0x7fffffff) ? int32_t(0x7fffffff) : int32_t(w); };
     a.win_left = win(p->win_left);
     a.win_right = win(p->win_right);
-    int mm = 0;
-    if (p->mask_mode == FA_MASK_CAUSAL) mm = 1;
-    if (p->mask_mode == FA_MASK_BOOL) mm = 2;
-    if (p->mask_mode == FA_MASK_WINDOW) mm = 4;
-    // A boolean mask whose rows are contiguous, 16-byte aligned key runs is
-    // staged through LDS tile by tile (instantiation 3); any other stride
-    // pattern is read element by element (instantiation 2).
-    if (mm == 2) {
-        const int64_t* st = p->mask_stride;
-        const bool rows_ok = st[3] == 1 && aligned(p->mask, 16) && st[0] % 16 == 0 && st[1] % 16 == 0 &&
-                             st[2] % 16 == 0 && s.KVS % 16 == 0 && st[2] < (int64_t(1) << 23);
-        if (rows_ok) mm = 3;
+    const int mm = prefill_mask_kind(p, s);
+    // A staged boolean mask with a workspace is summarised per tile first, so
+    // the prefill skips the tiles it masks entirely and the mask loads of
+    // tiles it does not mask at all.
+    const MaskSummaryGeom mg = mask_summary_geom(p, s);
+    if (mg.blocks > 0 && workspace) {
+        fa::MaskSummaryArgs ma;
+        std::memset(&ma, 0, sizeof ma);
+        ma.mask = p->mask;
+        for (int i = 0; i < 4; ++i) ma.mask_stride[i] = p->mask_stride[i];
+        ma.q_seq = s.QS;
+        ma.kv_seq = s.KVS;
+        ma.q_tiles = (int32_t)mg.q_tiles;
+        ma.words = (int32_t)mg.words;
+        ma.slices_n = (int32_t)mg.slices_n;
+        ma.blocks = mg.blocks;
+        ma.out = static_cast<uint32_t*>(workspace);
+        fa_status st = launch_result(fa::launch_mask_summary(ma, stream), "mask summary");
+        if (st != FA_OK) return st;
+        a.mask_cls = ma.out;
+        a.cls_words = ma.words;
     }
     if (p->layout == FA_TND) {
         fa::VarlenScheduleArgs sa;
@@ -460,7 +504,10 @@ fa_status fa_workspace_size(const fa_params* p, size_t* bytes) {
         *bytes = varlen_bytes(s);
         return ok();
     }
-    if (!decode_path(p)) return ok();
+    if (!decode_path(p)) {
+        *bytes = mask_summary_geom(p, s).bytes;
+        return ok();
+    }
     int64_t sp, c;
     plan_splits(p, s, device_cus(), &sp, &c);
     if (sp > 1) *bytes = partial_bytes(s, sp).total;
@@ -482,7 +529,18 @@ fa_status fa_fwd(const fa_params* p, const void* q, const void* k, const void* v
         if (workspace_bytes < need)
             return fail(FA_ERR_PARAM_INVALID, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
     }
-    if (!decode_path(p)) return run_prefill(p, s, q, k, v, out, lse, workspace, hs);
+    if (!decode_path(p)) {
+        // A staged boolean mask takes an optional workspace for its summary;
+        // without one the prefill runs unchanged, visiting every KV tile.
+        const size_t need = mask_summary_geom(p, s).bytes;
+        if (p->layout != FA_TND && need && workspace) {
+            if (!aligned(workspace, 256)) return fail(FA_ERR_PARAM_INVALID, "workspace must be 256-byte aligned");
+            if (workspace_bytes < need)
+                return fail(FA_ERR_PARAM_INVALID, "workspace too small: %zu bytes given, %zu needed", workspace_bytes,
+                            need);
+        }
+        return run_prefill(p, s, q, k, v, out, lse, p->layout == FA_TND || need ? workspace : nullptr, hs);
+    }
 
     int64_t sp, c;
     plan_splits(p, s, device_cus(), &sp, &c);

@@ -81,6 +81,30 @@ struct PrefillArgs {
     const int32_t* work;      // [work_items][2]
     int32_t work_items;
     int32_t batch;
+    // Boolean mask staged through LDS (instantiation 3): an optional summary
+    // of the mask (MaskSummaryArgs), cls_words words per (slice, q tile).
+    const uint32_t* mask_cls;
+    int32_t cls_words;
+};
+
+// Summary of a boolean mask over the prefill's tiles of 128 query rows x 64
+// keys.  Slice (sb, sn) is the mask at b = sb, n = sn (a broadcast dimension,
+// stride 0, has one slice).  Each (slice, q tile) owns a row of `words` 32-bit
+// words, word w covering KV tiles 16*w .. 16*w+15 with two bits per tile:
+// bit 0 set when some key of the tile is visible to some query row of the
+// tile, bit 1 set when some key is masked for some row.  A tile holding no
+// key (past kv_seq) reads 0.  Entry (slice, qt, w) is at
+// out[((sb * slices_n + sn) * q_tiles + qt) * words + w].
+constexpr int kMaskRowsPerTile = 128;
+constexpr int kMaskKeysPerTile = 64;
+constexpr int kMaskTilesPerWord = 16;
+struct MaskSummaryArgs {
+    const uint8_t* mask;
+    int64_t mask_stride[4];
+    int64_t q_seq, kv_seq;    // kv_seq a multiple of 16, rows 16-byte aligned
+    int32_t q_tiles, words, slices_n;
+    int64_t blocks;           // slices * q_tiles * words
+    uint32_t* out;
 };
 
 // Geometry of one packed sequence, with every offset clamped into its tensor.
@@ -143,5 +167,6 @@ hipError_t launch_combine(const CombineArgs& a, int dtype, int head_dim, hipStre
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int mask_mode,
                           int64_t batch, hipStream_t stream);
 hipError_t launch_varlen_schedule(const VarlenScheduleArgs& a, hipStream_t stream);
+hipError_t launch_mask_summary(const MaskSummaryArgs& a, hipStream_t stream);
 
 }  // namespace fa

@@ -30,7 +30,10 @@
 // not visited); 2 a boolean tensor read element by element; 3 a boolean
 // tensor with contiguous key rows, staged through LDS with the K/V tiles (a
 // wave skips a tile its rows mask entirely, and the element tests of a tile
-// that masks none of its rows);
+// that masks none of its rows; given a per-tile summary of the mask, the
+// workgroup visits only the tiles between the first and the last one with a
+// visible key and loads neither tiles with none nor the mask of tiles that
+// mask nothing);
 // 4 the window band of the FlashAttn developer guide (1.5, mode 4): only the
 // KV tiles that intersect the band of the query tile are visited, and a wave
 // skips tiles outside the band of its 32 rows.
@@ -116,6 +119,7 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
     constexpr int RPI = 64 / CPR;       // rows per direct-to-LDS wave load
     constexpr int NIW = TB / 1024 / 4;  // wave loads per wave per tile (K, and again V)
     constexpr float kPmax = 256.f;      // rescale only when an exponential could exceed 2^8
+    static_assert(BM == kMaskRowsPerTile && BN == kMaskKeysPerTile, "mask summary tiles");
     __shared__ __attribute__((aligned(1024))) unsigned char sK0[TB];
     __shared__ __attribute__((aligned(1024))) unsigned char sK1[TB];
     __shared__ __attribute__((aligned(1024))) unsigned char sV0[TB];
@@ -163,7 +167,7 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
         const int64_t work = xcd_remap(blockIdx.x, total);
         qt = (int)(work % a.q_tiles);
         const int64_t bh = work / a.q_tiles;
-        if (MASK == 1) qt = a.q_tiles - 1 - qt;  // longest causal tiles first
+        if (MASK == 1 || MASK == 3) qt = a.q_tiles - 1 - qt;  // longest causal tiles first
         n1 = (int)(bh % a.num_heads);
         b = bh / a.num_heads;
         L = a.kv_seq;
@@ -213,7 +217,43 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
         const int64_t key_lo = i0 - a.win_left;
         if (key_lo > 0) jt0 = (int)(key_lo / BN);
     }
-    const int ntiles = (int)((kv_end + BN - 1) / BN);
+    int ntiles = (int)((kv_end + BN - 1) / BN);
+
+    // MASK 3 with a summary of the mask: the row of tile classes of this
+    // query tile (two bits per KV tile: some key visible, some key masked).
+    // Lane l keeps word l, KV tiles 16l .. 16l+15; the first and the last
+    // tile with a visible key bound the loop.  Tiles past the 64 words the
+    // lanes keep count as partly masked.
+    const bool summary = (MASK == 3) && a.mask_cls != nullptr;
+    uint32_t cls_word = 0xffffffffu;
+    if (MASK == 3 && summary) {
+        const int64_t sn = a.mask_stride[1] ? a.num_heads : 1;
+        const int64_t slice = (a.mask_stride[0] ? b : 0) * sn + (a.mask_stride[1] ? n1 : 0);
+        const uint32_t* crow = a.mask_cls + (slice * a.q_tiles + qt) * a.cls_words;
+        int first = 0x7fffffff, last = -1;
+        for (int w = lane; w < a.cls_words; w += 64) {
+            const uint32_t x = crow[w];
+            if (w == lane) cls_word = x;
+            const uint32_t live = x & 0x55555555u;
+            if (live) {
+                first = min(first, 16 * w + (__builtin_ctz(live) >> 1));
+                last = max(last, 16 * w + ((31 - __builtin_clz(live)) >> 1));
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            first = min(first, __shfl_xor(first, off, 64));
+            last = max(last, __shfl_xor(last, off, 64));
+        }
+        first = __builtin_amdgcn_readfirstlane(first);
+        last = __builtin_amdgcn_readfirstlane(last);
+        if (first > jt0) jt0 = first;
+        if (last + 1 < ntiles) ntiles = last + 1;
+    }
+    auto tile_cls = [&](int jt) __attribute__((always_inline)) -> uint32_t {
+        if (!summary || jt >= 64 * 16) return 3u;
+        return (__builtin_amdgcn_readlane(cls_word, jt >> 4) >> (2 * (jt & 15))) & 3u;
+    };
 
     f32x16 o[D / 32];
 #pragma unroll
@@ -252,6 +292,8 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
     }
     auto issue_tile = [&](int jt, unsigned char* dK, unsigned char* dV, unsigned char* dM)
                           __attribute__((always_inline)) {
+        const uint32_t cls = (MASK == 3) ? tile_cls(jt) : 3u;
+        if (MASK == 3 && !(cls & 1u)) return;  // no visible key: nothing to load
         const int64_t j0 = (int64_t)jt * BN;
         int64_t rows = L - j0;
         rows = rows < 0 ? 0 : (rows > BN ? BN : rows);
@@ -264,7 +306,7 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
             lds_dma16(kt, nrec, (lds_void*)(dK + I * 1024), voff[w]);
             lds_dma16(vt, nrec, (lds_void*)(dV + I * 1024), voff[w]);
         }
-        if (MASK == 3) {
+        if (MASK == 3 && (cls & 2u)) {
             int64_t keys = a.kv_seq - j0;
             keys = keys > BN ? BN : keys;
             const int mrec = mrec_rows + (int)keys;
@@ -308,8 +350,13 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
         // wave-uniform skip of tiles the mask excludes entirely for its rows.
         uint32_t mw[2][4];
         bool mask_clear = false;  // MASK 3: no key of this tile is masked for any row of the wave
-        if (MASK == 3) {
-            bool lane_all = !qvalid || j0 >= L;
+        // With a summary, class 1 (no key masked) loaded no mask tile and
+        // needs no tests; a tile with no visible key (bit 0 clear) loaded
+        // nothing and is skipped by the test below whatever the LDS holds.
+        const uint32_t cls = (MASK == 3) ? tile_cls(jt) : 3u;
+        if (MASK == 3 && cls == 1u) mask_clear = true;
+        if (MASK == 3 && cls != 1u) {
+            bool lane_all = !qvalid || j0 >= L || !(cls & 1u);
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
@@ -381,8 +428,10 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
-                    mw[tt][g] = *reinterpret_cast<const uint32_t*>(
-                        Mb + ((2 * tt + (g >> 1)) * BM + 32 * wave + col) * 16 + 8 * (g & 1) + 4 * half);
+                    mw[tt][g] = (cls != 1u) ? *reinterpret_cast<const uint32_t*>(
+                                                 Mb + ((2 * tt + (g >> 1)) * BM + 32 * wave + col) * 16 +
+                                                 8 * (g & 1) + 4 * half)
+                                           : 0u;
         }
         if (need_mask) {
 #pragma unroll

@@ -192,6 +192,27 @@ def test_tnd_params_validated(lib, kw, status, text):
     assert text in fa.fa_last_error()
 
 
+def test_bool_mask_summary_workspace(lib):
+    # A staged boolean mask (unit key stride, 16-byte multiples) asks for its
+    # per-tile summary: one 32-bit word per 16 KV tiles of 64 keys, per mask
+    # slice (broadcast axes count once) and 128-row query tile.
+    bcast = params(batch=2, q_seq=4096, kv_seq=4096, mask_mode="bool", mask=FAKE,
+                   mask_stride=(0, 0, 4096, 1))
+    assert fa.fa_workspace_size(bcast) == 256 * (((32 * 4 * 4) + 255) // 256)
+    per_bn = params(batch=2, num_heads=4, q_seq=1000, kv_seq=1040, mask_mode="bool", mask=FAKE,
+                    mask_stride=(4 * 1000 * 1040, 1000 * 1040, 1040, 1))
+    # 8 slices x ceil(1000/128) = 8 q tiles x ceil(ceil(1040/64)/16) = 2 words
+    assert fa.fa_workspace_size(per_bn) == ((8 * 8 * 2 * 4) + 255) // 256 * 256
+    # element-wise masks (key stride != 1) take no workspace
+    assert fa.fa_workspace_size(params(q_seq=256, kv_seq=256, mask_mode="bool", mask=FAKE,
+                                       mask_stride=(0, 0, 1, 256))) == 0
+    # a misaligned or short workspace is refused before anything runs
+    st = lib.fa_fwd(ctypes.byref(bcast), FAKE, FAKE, FAKE, FAKE, None, FAKE + 16, 1 << 20, None)
+    assert st == fa.FA_ERR_PARAM_INVALID and "aligned" in fa.fa_last_error()
+    st = lib.fa_fwd(ctypes.byref(bcast), FAKE, FAKE, FAKE, FAKE, None, FAKE, 64, None)
+    assert st == fa.FA_ERR_PARAM_INVALID and "too small" in fa.fa_last_error()
+
+
 def test_tnd_workspace(lib):
     p = tnd()
     # one (sequence, tile) pair per 128-row tile: ceil(1000/128) + 4 + 1 entries of 8 bytes

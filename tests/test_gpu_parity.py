@@ -442,8 +442,10 @@ def test_prefill_random_bool_mask_with_empty_rows():
     assert math.isinf(float(lse[1, 2, 5])) and torch.all(out[1, 2, 5] == 0)
 
 
-def _bool_mask_run(inp, mask_np, strides, byte_offset=0):
-    """fa_fwd with a boolean mask given as a (possibly offset) device byte buffer."""
+def _bool_mask_run(inp, mask_np, strides, byte_offset=0, summary=False):
+    """fa_fwd with a boolean mask given as a (possibly offset) device byte buffer;
+    with summary=True the workspace fa_workspace_size asks for is passed, so a
+    staged mask is summarised per tile first."""
     s = inp.spec
     q, k, v = (dev16(x, s.dtype) for x in (inp.q, inp.k, inp.v))
     lens = None if inp.lens is None else torch.from_numpy(inp.lens).to(DEV)
@@ -454,7 +456,9 @@ def _bool_mask_run(inp, mask_np, strides, byte_offset=0):
                       mask=buf.data_ptr() + byte_offset, mask_stride=strides)
     out = torch.empty_like(q)
     lse = torch.empty((s.B, s.QN, s.QS), dtype=torch.float32, device=DEV)
-    fa.fa_fwd(p, q, k, v, out, lse, None, 0, torch.cuda.current_stream())
+    nbytes = fa.fa_workspace_size(p) if summary else 0
+    ws = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device=DEV) if nbytes else None
+    fa.fa_fwd(p, q, k, v, out, lse, ws, nbytes, torch.cuda.current_stream())
     torch.cuda.synchronize()
     return out, lse
 
@@ -495,6 +499,73 @@ def test_prefill_broadcast_bool_mask_matches_oracle():
     o_rows = rows_of(out, s, np.arange(s.B * s.QN * s.QS))
     r_rows = np.ascontiguousarray(ref.transpose(0, 2, 1, 3)).reshape(-1, s.D)
     check(o_rows, to_np(lse).reshape(-1), r_rows, ref_lse.reshape(-1), "broadcast bool mask")
+
+
+def _block_mask(rng, shape, p_dead, p_full, blk=(64, 64)):
+    """Random mask built from blocks that are fully masked, fully visible or random."""
+    m = (rng.random(shape) < 0.5).astype(np.uint8)
+    nb_i = -(-shape[-2] // blk[0])
+    nb_j = -(-shape[-1] // blk[1])
+    kind = rng.random(shape[:-2] + (nb_i, nb_j))
+    for idx in np.ndindex(*kind.shape):
+        *lead, bi, bj = idx
+        sl = tuple(lead) + (slice(bi * blk[0], (bi + 1) * blk[0]), slice(bj * blk[1], (bj + 1) * blk[1]))
+        if kind[idx] < p_dead:
+            m[sl] = 1
+        elif kind[idx] < p_dead + p_full:
+            m[sl] = 0
+    return m
+
+
+SUMMARY_CASES = [
+    # per-(b, n) block-sparse mask, ragged lengths, interior dead tiles
+    dict(s=dict(layout="BNSD", B=2, QN=4, KVN=2, QS=300, KVS=1024, D=128, lens=(700, 1024), seed=41),
+         shape=(2, 4, 300, 1024), bcast=(False, False), blk=(64, 64)),
+    # broadcast causal pattern, sizes that are not tile multiples
+    dict(s=dict(layout="BSND", B=2, QN=4, KVN=4, QS=464, KVS=464, D=64, seed=43),
+         shape=(1, 1, 464, 464), bcast=(True, True), blk=None),
+    # per-batch mask broadcast over heads, D = 256, 32-key blocks
+    dict(s=dict(layout="BNSD", B=2, QN=4, KVN=1, QS=200, KVS=640, D=256, dtype="f16", seed=47),
+         shape=(2, 1, 200, 640), bcast=(False, True), blk=(32, 32)),
+    # more KV tiles (1040) than the lanes keep classes for (1024): tiles past
+    # them run as partly masked, the loop bounds still come from the summary
+    dict(s=dict(layout="BNSD", B=1, QN=1, KVN=1, QS=130, KVS=66560, D=64, seed=53),
+         shape=(1, 1, 130, 66560), bcast=(False, False), blk=(128, 1024)),
+]
+
+
+@pytest.mark.parametrize("case", SUMMARY_CASES, ids=lambda c: "{layout}-QS{QS}-KVS{KVS}-D{D}".format(**c["s"]))
+def test_prefill_mask_summary_changes_nothing(case):
+    """The per-tile summary of a staged mask only removes work: outputs with and
+    without it are identical, and match the oracle."""
+    s = spec(**case["s"])
+    inp = fa_synth.make(s)
+    rng = np.random.default_rng(case["s"]["seed"])
+    shape = case["shape"]
+    if case["blk"] is None:
+        mask = np.triu(np.ones(shape[-2:], np.uint8), 1).reshape(shape)
+    else:
+        mask = _block_mask(rng, shape, 0.4, 0.3, case["blk"])
+    if shape[-1] > 60000:   # first and last visible tiles far apart, past tile 1024
+        mask[..., :, :] = 1
+        mask[..., :, 64 * 3:64 * 5] = (rng.random((shape[-2], 128)) < 0.5)
+        mask[..., :, 64 * 1030:64 * 1031] = 0
+        mask[..., :, 64 * 1033:64 * 1034 - 5] = (rng.random((shape[-2], 59)) < 0.5)
+    mask[tuple(0 for _ in shape[:-2]) + (3,)] = 1      # an empty row
+    st_i, st_j = shape[-1], 1
+    st_n = 0 if case["bcast"][1] else shape[-2] * shape[-1]
+    st_b = 0 if case["bcast"][0] else shape[1] * shape[-2] * shape[-1]
+    strides = (st_b, st_n, st_i, st_j)
+    o0, l0 = _bool_mask_run(inp, mask, strides, summary=False)
+    o1, l1 = _bool_mask_run(inp, mask, strides, summary=True)
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    inp.mask, inp.mask_strides = mask, strides
+    prob = oracle.Problem.from_inputs(inp, "bool")
+    ref, ref_lse = oracle.attention(prob, inp.q, inp.k, inp.v)
+    o_rows = rows_of(o1, s, np.arange(s.B * s.QN * s.QS))
+    r_rows = ref if s.layout == "BNSD" else ref.transpose(0, 2, 1, 3)
+    r_rows = np.ascontiguousarray(r_rows).reshape(-1, s.D)
+    check(o_rows, to_np(l1).reshape(-1), r_rows, ref_lse.reshape(-1), "mask summary")
 
 
 def test_prefill_staged_causal_mask_equals_causal_mode():

@@ -5,11 +5,12 @@
 // and most of the rest hold no masked one.  For the window mode the
 // FlashAttn developer guide (1.5) has the kernel skip the tiles with no valid
 // key from the band's bounds; for a tensor mask the same facts are read from
-// the tensor once, before the prefill runs.  One workgroup covers one
-// (mask slice, 128-row query tile, 16 KV tiles of 64 keys): each wave reads
-// every fourth row of the slab, 16 bytes per lane, and records whether it saw
-// a zero byte (a visible key) and a non-zero byte (a masked key); a ballot
-// per wave and an OR over the four waves give two bits per KV tile.
+// the tensor once, before the prefill runs.  One workgroup of 16 waves covers
+// one (mask slice, 128-row query tile, 16 KV tiles of 64 keys): each wave
+// reads eight rows of the slab, 16 bytes per lane with all eight loads in
+// flight, and records whether it saw a zero byte (a visible key) and a
+// non-zero byte (a masked key); a ballot per wave and an OR over the waves
+// give two bits per KV tile.
 //
 // The prefill then visits only the KV tiles between the first and the last
 // tile with a visible key, issues no loads for tiles in between that have
@@ -21,10 +22,8 @@
 
 namespace fa {
 
-constexpr int kSumThreads = 256;
+constexpr int kSumThreads = 1024;
 constexpr int kSumWaves = kSumThreads / 64;
-
-__device__ __forceinline__ bool has_zero_byte(uint32_t x) { return ((x - 0x01010101u) & ~x & 0x80808080u) != 0u; }
 
 __global__ __launch_bounds__(kSumThreads) void mask_summary_kernel(MaskSummaryArgs a) {
     constexpr int RPW = kMaskRowsPerTile / kSumWaves;  // rows per wave
@@ -47,21 +46,28 @@ __global__ __launch_bounds__(kSumThreads) void mask_summary_kernel(MaskSummaryAr
     // multiple of 16, so a chunk is either wholly inside the row or past it.
     const int64_t key = w * (kMaskTilesPerWord * kMaskKeysPerTile) + 16 * lane;
     const uint8_t* base = a.mask + sb * a.mask_stride[0] + sn * a.mask_stride[1] + row0 * a.mask_stride[2] + key;
-    bool vis = false, msk = false;
+    // zero_bits collects the high bit of every zero byte seen (a visible
+    // key), any_bits every bit of every byte (a masked key).
+    uint32_t zero_bits = 0u, any_bits = 0u;
     if (key < a.kv_seq) {
-#pragma unroll 8
-        for (int i = 0; i < RPW; ++i) {
-            const int64_t r = wave + (int64_t)kSumWaves * i;
-            if (r < rows) {
-                const u32x4 x = ld128(base + r * a.mask_stride[2]);
+        u32x4 x[RPW];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    vis = vis || has_zero_byte(x[e]);
-                    msk = msk || x[e] != 0u;
-                }
-            }
+        for (int i = 0; i < RPW; ++i) {
+            // Rows past the query length re-read the last row (rows >= 1),
+            // which leaves both flags unchanged and keeps the loads unbranched.
+            int64_t r = (int64_t)wave * RPW + i;
+            r = r < rows ? r : rows - 1;
+            x[i] = ld128(base + r * a.mask_stride[2]);
         }
+#pragma unroll
+        for (int i = 0; i < RPW; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                zero_bits |= (x[i][e] - 0x01010101u) & ~x[i][e] & 0x80808080u;
+                any_bits |= x[i][e];
+            }
     }
+    const bool vis = zero_bits != 0u, msk = any_bits != 0u;
     // Lanes 4t .. 4t+3 hold the 64 keys of KV tile t of the word.
     __shared__ uint64_t s_vis[kSumWaves], s_msk[kSumWaves];
     const uint64_t bv = __ballot(vis);

@@ -356,36 +356,30 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
         const uint32_t cls = (MASK == 3) ? tile_cls(jt) : 3u;
         if (MASK == 3 && cls == 1u) mask_clear = true;
         if (MASK == 3 && cls != 1u) {
-            bool lane_all = !qvalid || j0 >= L || !(cls & 1u);
+            // zero_bytes gathers the top bit of every zero (visible) byte of
+            // the lane's 32 keys, any_set every masked bit; bitwise so the
+            // tests stay branch-free.
+            uint32_t zero_bytes = 0u, any_set = 0u;
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int ch = 2 * tt + (g >> 1);
-                    mw[tt][g] = *reinterpret_cast<const uint32_t*>(
+                    const uint32_t w = *reinterpret_cast<const uint32_t*>(
                         Mb + (ch * BM + 32 * wave + col) * 16 + 8 * (g & 1) + 4 * half);
+                    zero_bytes |= (w - 0x01010101u) & ~w & 0x80808080u;
+                    any_set |= w;
                 }
             }
-            bool none_zero = true;
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    none_zero = none_zero && (((mw[tt][g] - 0x01010101u) & ~mw[tt][g] & 0x80808080u) == 0u);
-            lane_all = lane_all || none_zero;
-            uint32_t any_set = 0u;
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) any_set |= mw[tt][g];
+            const bool lane_all = !qvalid | (j0 >= L) | !(cls & 1u) | (zero_bytes == 0u);
             mask_clear = __all(any_set == 0u);
             if (__all(lane_all)) {
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 __syncthreads();
                 return;
             }
-            asm volatile("" ::: "memory");  // re-read the words after the QK MFMAs instead of holding them
         }
+        if (MASK == 3) asm volatile("" ::: "memory");  // re-read the words after the QK MFMAs instead of holding them
         // MASK 4: a tile wholly left or right of the band of every row of
         // this wave is skipped (wave-uniform).
         if (MASK == 4) {
@@ -423,15 +417,15 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
         const bool need_mask = (j0 + BN > L) || (MASK == 1 && j0 + BN - 1 > wrow0) || (MASK == 2) ||
                                (MASK == 3 && !mask_clear) ||
                                (MASK == 4 && (j0 < wrow0 + 31 - a.win_left || j0 + BN - 1 > wrow0 + a.win_right));
+        // MASK 3: the lane's mask words, read whatever the class (a tile that
+        // masks nothing left stale bytes here, which mask_clear overrides).
         if (MASK == 3) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
-                    mw[tt][g] = (cls != 1u) ? *reinterpret_cast<const uint32_t*>(
-                                                 Mb + ((2 * tt + (g >> 1)) * BM + 32 * wave + col) * 16 +
-                                                 8 * (g & 1) + 4 * half)
-                                           : 0u;
+                    mw[tt][g] = *reinterpret_cast<const uint32_t*>(
+                        Mb + ((2 * tt + (g >> 1)) * BM + 32 * wave + col) * 16 + 8 * (g & 1) + 4 * half);
         }
         if (need_mask) {
 #pragma unroll
@@ -445,7 +439,8 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
                         ok = ok && qvalid &&
                              a.mask[b * a.mask_stride[0] + (int64_t)n1 * a.mask_stride[1] +
                                     qrow * a.mask_stride[2] + tok * a.mask_stride[3]] == 0;
-                    if (MASK == 3) ok = ok && qvalid && ((mw[tt][r >> 2] >> (8 * (r & 3))) & 0xffu) == 0u;
+                    if (MASK == 3)
+                        ok = ok & qvalid & (mask_clear | (((mw[tt][r >> 2] >> (8 * (r & 3))) & 0xffu) == 0u));
                     if (MASK == 4) {
                         const int dj = (int)(tok - qrow);
                         ok = ok && dj >= -a.win_left && dj <= a.win_right;

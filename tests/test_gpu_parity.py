@@ -568,6 +568,55 @@ def test_prefill_mask_summary_changes_nothing(case):
     check(o_rows, to_np(l1).reshape(-1), r_rows, ref_lse.reshape(-1), "mask summary")
 
 
+def _expected_summary(mask, strides, B, QN, QS, KVS):
+    """The per-tile classes fa_fwd writes to its workspace for a staged mask:
+    per (slice, 128-row q tile) a row of 32-bit words, 16 KV tiles of 64 keys
+    per word, bit 0 = some key visible, bit 1 = some key masked."""
+    flat = mask.reshape(-1)
+    sb = B if strides[0] else 1
+    sn = QN if strides[1] else 1
+    qt_n = -(-QS // 128)
+    words = -(-(-(-KVS // 64)) // 16)
+    out = np.zeros((sb, sn, qt_n, words), np.uint32)
+    for b in range(sb):
+        for n in range(sn):
+            base = b * strides[0] + n * strides[1]
+            rows = np.arange(QS)[:, None] * strides[2] + np.arange(KVS)[None, :] * strides[3]
+            m = flat[base + rows]
+            for qt in range(qt_n):
+                for jt in range(-(-KVS // 64)):
+                    sub = m[qt * 128:(qt + 1) * 128, jt * 64:(jt + 1) * 64]
+                    c = int((sub == 0).any()) | (int((sub != 0).any()) << 1)
+                    out[b, n, qt, jt // 16] |= np.uint32(c << (2 * (jt % 16)))
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("case", [0, 1], ids=["causal_broadcast", "per_head_blocks"])
+def test_mask_summary_words(case):
+    """The summary kernel's words, read back from the caller's workspace, equal
+    the classes computed from the mask on the host."""
+    if case == 0:
+        s = spec(layout="BSND", B=2, QN=4, KVN=4, QS=464, KVS=1200, D=64, seed=59)
+        mask = np.triu(np.ones((464, 1200), np.uint8), 1)[None, None]
+        strides = (0, 0, 1200, 1)
+    else:
+        s = spec(layout="BNSD", B=1, QN=3, KVN=1, QS=200, KVS=1104, D=128, seed=61)
+        mask = _block_mask(np.random.default_rng(61), (1, 3, 200, 1104), 0.4, 0.3, (64, 64))
+        strides = (0, 200 * 1104, 1104, 1)
+    inp = fa_synth.make(s)
+    q, k, v = (dev16(x, s.dtype) for x in (inp.q, inp.k, inp.v))
+    buf = torch.from_numpy(np.ascontiguousarray(mask).reshape(-1)).to(DEV)
+    p = fa.params_for(q, k, layout=s.layout, scale=s.softmax_scale, mask=buf, mask_stride=strides)
+    nbytes = fa.fa_workspace_size(p)
+    ws = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(q)
+    fa.fa_fwd(p, q, k, v, out, None, ws, nbytes, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    want = _expected_summary(mask, strides, s.B, s.QN, s.QS, s.KVS)
+    got = ws.cpu().numpy()[:want.size * 4].view(np.uint32)
+    assert np.array_equal(got, want)
+
+
 def test_prefill_staged_causal_mask_equals_causal_mode():
     inp = fa_synth.make(spec(layout="BSND", B=1, QN=4, KVN=2, QS=320, KVS=320, mask="bool_causal",
                              seed=37))

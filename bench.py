@@ -252,11 +252,19 @@ def main():
     print(json.dumps(out))
 
 
-def timed(fn, torch, np, stream, warmup, iters, flush=None):
+def timed(fn, torch, np, stream, warmup, iters, flush=None, warm_s=0.25):
     """Median ms of fn() over iters calls, each between events on the stream; with a flush
-    buffer, the buffer is read before each call, outside its events."""
-    for _ in range(warmup):
+    buffer, the buffer is read before each call, outside its events.  The warmup runs at
+    least `warmup` calls and at least warm_s seconds: the GPU idles while the next
+    workload's inputs are generated on the host, and its clock needs some tens of
+    milliseconds of load to come back up."""
+    t_end = time.perf_counter() + warm_s
+    n = 0
+    while n < warmup or time.perf_counter() < t_end:
         fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(iters)]
     for a, b in evs:

@@ -208,7 +208,10 @@ fa_status fa_splitkv_plan(const fa_params *p, int num_cus, int64_t chunk_hint,
  * and at most a cap (a paged cache: 1016 * block_size, the block ids of one
  * chunk being staged on chip; a contiguous one: (chunk + 256) rows of one
  * head within 2^31 bytes, the K/V offsets being 32-bit); fa_splitkv_plan
- * respects both. */
+ * respects both.  With 4 to 32 query heads per KV head, head_dim 64 or 128
+ * and a contiguous cache, the chunk runs on the matrix cores (the query heads
+ * of a KV head are the rows of one tile; P is rounded to the input type before
+ * the PV product, as in the prefill); other shapes use the vector units. */
 fa_status fa_decode_splitkv(const fa_params *p, int64_t num_splits, int64_t chunk,
                             const void *q, const void *k, const void *v,
                             float *o_part, float *m_part, float *l_part, void *stream);

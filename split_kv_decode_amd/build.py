@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfa_mi355x.so")
 OBJDIR = os.path.join(HERE, "_build")
 
-SOURCES = ["fa_api.cpp", "fa_decode.hip", "fa_prefill.hip", "fa_varlen.hip", "fa_masksum.hip"]
+SOURCES = ["fa_api.cpp", "fa_decode.hip", "fa_decode_mfma.hip", "fa_prefill.hip", "fa_varlen.hip", "fa_masksum.hip"]
 ARCH = "gfx950"
 
 # hipcc flags for every translation unit.  Packed fp32 instructions are turned

@@ -154,8 +154,9 @@ int heads_per_workgroup(int64_t g) {
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cus[kMaxDevices];
 // Stage-1 residency per device and (dtype, D, heads per workgroup, paged):
-// 2 x 3 x 4 x 2 = 48 instantiations; 0 = not asked yet, -1 = no answer.
-std::atomic<int> g_resident[kMaxDevices][48];
+// 2 x 3 x 4 x 2 = 48 instantiations, then the matrix-core stage 1 per
+// (dtype, D in {64, 128}); 0 = not asked yet, -1 = no answer.
+std::atomic<int> g_resident[kMaxDevices][52];
 
 int current_device() {
     int dev = 0;
@@ -185,6 +186,30 @@ int stage1_residency(int dtype, int D, int gh, bool paged) {
     const int n = fa::decode_stage1_residency(dtype, D, gh, paged);
     if (dev >= 0) g_resident[dev][key].store(n > 0 ? n : -1, std::memory_order_relaxed);
     return n;
+}
+
+int mfma_residency(int dtype, int D) {
+    const int dev = current_device();
+    const int key = 48 + dtype * 2 + (D == 64 ? 0 : 1);
+    if (dev >= 0) {
+        const int cached = g_resident[dev][key].load(std::memory_order_relaxed);
+        if (cached != 0) return cached > 0 ? cached : 0;
+    }
+    const int n = fa::decode_mfma_residency(dtype, D);
+    if (dev >= 0) g_resident[dev][key].store(n > 0 ? n : -1, std::memory_order_relaxed);
+    return n;
+}
+
+// Grouped query heads (4 to 32 per KV head) over a contiguous cache run the
+// matrix-core stage 1: the heads of a KV head form the rows of one matrix
+// tile, where the vector-ALU stage 1 spends a dot-product reduction and an
+// exponential per head on every lane of a row's group and is bound by that
+// vector work rather than by HBM.  Its tiles address 64 rows with 32-bit
+// offsets.
+bool mfma_decode(const fa_params* p, const Shape& s) {
+    const int64_t row_bytes = (p->layout == FA_BNSD ? s.D : s.KVN * s.D) * 2;
+    return p->kv_layout == FA_KV_CONTIGUOUS && s.g >= 4 && s.g <= 32 && (s.D == 64 || s.D == 128) &&
+           row_bytes * 64 < (int64_t(1) << 31);
 }
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -228,8 +253,11 @@ int64_t chunk_cap(const fa_params* p, const Shape& s) {
 
 void plan_splits(const fa_params* p, const Shape& s, int num_cus, int64_t* splits, int64_t* chunk) {
     const int gh = heads_per_workgroup(s.g);
-    const int64_t units = s.B * s.KVN * (s.g / gh);
-    const int resident = stage1_residency(p->dtype == FA_BF16 ? 1 : 0, (int)s.D, gh, p->kv_layout != FA_KV_CONTIGUOUS);
+    const bool mm = mfma_decode(p, s);
+    const int64_t units = mm ? s.B * s.KVN : s.B * s.KVN * (s.g / gh);
+    const int resident = mm ? mfma_residency(p->dtype == FA_BF16 ? 1 : 0, (int)s.D)
+                            : stage1_residency(p->dtype == FA_BF16 ? 1 : 0, (int)s.D, gh,
+                                               p->kv_layout != FA_KV_CONTIGUOUS);
     const int64_t target = (resident > 0 ? resident : kWgPerCu) * int64_t(num_cus > 0 ? num_cus : 256);
     int64_t want = (target + units - 1) / units;
     if (want < 1) want = 1;
@@ -344,6 +372,9 @@ fa_status run_stage1(const fa_params* p, const Shape& s, int64_t splits, int64_t
     a.num_splits = (int32_t)splits;
     a.counters = counters;
     const bool finish = (out != nullptr && counters == nullptr);
+    if (counters == nullptr && mfma_decode(p, s))
+        return launch_result(fa::launch_decode_mfma(a, p->dtype == FA_BF16 ? 1 : 0, (int)s.D, finish, s.B, stream),
+                             "decode stage 1");
     return launch_result(fa::launch_decode_stage1(a, p->dtype == FA_BF16 ? 1 : 0, (int)s.D,
                                                   heads_per_workgroup(s.g), finish, s.B, stream),
                          "decode stage 1");

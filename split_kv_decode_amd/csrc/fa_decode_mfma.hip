@@ -1,0 +1,341 @@
+// fa_decode_mfma.hip -- split-KV decode stage 1 on the matrix cores for
+// grouped query heads.
+//
+// Under GQA (IFA guide 1.1, numKeyValueHeads) the g query heads that share a
+// KV head read the same K and V rows.  The vector-ALU stage 1 takes one dot
+// product per (row, head) with a 16-lane reduction and an exponential on
+// every lane of the row's group, which makes it bound by vector work rather
+// than HBM once g reaches 4.  Here the g heads are the rows of a 32-row
+// matrix tile instead: S^T = K Q^T and O^T = V^T P^T on
+// v_mfma_f32_32x32x16_{bf16,f16} exactly as in the prefill kernel, with the
+// rows past g zero (their results are dropped).  A workgroup of two waves
+// takes one (batch, KV head, chunk) unit; K and V tiles of 64 keys go HBM ->
+// LDS with direct buffer loads, double buffered; wave w handles keys
+// [32w, 32w+32) of each tile with its own online softmax (running max,
+// lazy rescale as in the prefill), and the two waves are merged through LDS
+// at the end.  The partial (unnormalised O, max in natural-log units, sum)
+// has the layout and meaning of the vector-ALU stage 1 (FlashDecoding
+// tutorial, stage 1), so the same combine kernel (stage 2) merges it; a
+// one-split plan writes the output and lse in place.
+#include <type_traits>
+
+#include "fa_device.h"
+#include "fa_kernels.h"
+#include "fa_mfma.h"
+
+namespace fa {
+
+template <typename ST, int D, bool FINISH>
+__global__ __launch_bounds__(128, 2) void decode_mfma_kernel(DecodeArgs a) {
+    using M = Mfma<ST>;
+    using V8 = typename M::V8;
+    using E = typename M::E;
+    constexpr int NWV = 2;              // waves per workgroup
+    constexpr int BN = 64;              // keys per KV tile
+    constexpr int RB = D * 2;           // bytes per LDS row
+    constexpr int TB = BN * RB;         // bytes per K or V tile
+    constexpr int CPR = D / 8;          // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;       // rows per wave load
+    constexpr int NIW = TB / 1024 / NWV;
+    constexpr float kPmax = 256.f;
+    static_assert(NIW >= 1, "tile too small for two waves");
+    __shared__ __attribute__((aligned(1024))) unsigned char sK0[TB];
+    __shared__ __attribute__((aligned(1024))) unsigned char sK1[TB];
+    __shared__ __attribute__((aligned(1024))) unsigned char sV0[TB];
+    __shared__ __attribute__((aligned(1024))) unsigned char sV1[TB];
+    __shared__ float s_m[NWV][32], s_l[NWV][32];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = lane >> 5;
+    const int col = lane & 31;
+
+    const int64_t blk = blockIdx.x;
+    const int split = (int)(blk % a.num_splits);
+    const int64_t unit = blk / a.num_splits;
+    const int n2 = (int)(unit % a.num_kv_heads);
+    const int64_t b = unit / a.num_kv_heads;
+    const int g = a.group;
+
+    int64_t L = a.kv_seq;
+    if (a.lens) {
+        L = a.lens[b];
+        L = L < 0 ? 0 : (L > a.kv_seq ? a.kv_seq : L);
+    }
+    const int64_t c0 = (int64_t)split * a.chunk;
+    int64_t c1 = c0 + a.chunk;
+    if (c1 > L) c1 = L;
+
+    if (c1 <= c0) {
+        // A chunk at or past the length: its empty partial (or the row
+        // defaults of a one-split plan) without touching K or V.
+        for (int idx = tid; idx < g * D; idx += 128) {
+            const int h = idx / D;
+            const int d = idx % D;
+            const int64_t row = b * a.num_heads + (int64_t)n2 * g + h;
+            if constexpr (FINISH) {
+                reinterpret_cast<uint16_t*>(a.out)[row * D + d] = 0;
+                if (d == 0 && a.lse) a.lse[row] = kPosInf;
+            } else {
+                const int64_t slot = row * a.num_splits + split;
+                a.o_part[slot * D + d] = 0.f;
+                if (d == 0) {
+                    a.m_part[slot] = kNegInf;
+                    a.l_part[slot] = 0.f;
+                }
+            }
+        }
+        return;
+    }
+
+    // Q^T as the B operand: lane (col, half) holds head n2*g + col, head-dim
+    // elements [16*kk + 8*half, +8).  A negative scale flips the sign bits so
+    // the scores are scaled by |scale| * log2(e) > 0.
+    const bool qvalid = col < g;
+    const float c = fabsf(a.scale_log2);
+    V8 qreg[D / 16];
+    {
+        const uint16_t* qp = a.q + (b * a.num_heads + (int64_t)n2 * g + col) * D;
+        const uint32_t flip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            u32x4 w = u32x4{0u, 0u, 0u, 0u};
+            if (qvalid) w = ld128(qp + kk * 16 + 8 * half);
+            w ^= flip;
+            qreg[kk] = __builtin_bit_cast(V8, w);
+        }
+    }
+
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+    float m_run = kNegInf;  // per head (lane column): reference max, scaled base-2 units
+    float tm = kNegInf;     // true running max (the partial reports it)
+    float l_half = 0.f;
+
+    // Tile jt holds keys c0 + 64*jt + [0, 64); the buffer resource stops at
+    // the chunk's end, so rows past it land as zeros.
+    const int64_t row_bytes = a.kv_stride_s * 2;
+    const int64_t head_off = b * a.kv_stride_b + (int64_t)n2 * a.kv_stride_n;
+    const char* kbase = reinterpret_cast<const char*>(a.k + head_off) + c0 * row_bytes;
+    const char* vbase = reinterpret_cast<const char*>(a.v + head_off) + c0 * row_bytes;
+    const int64_t nkeys = c1 - c0;
+    const int ntiles = (int)((nkeys + BN - 1) / BN);
+    int voff[NIW];
+#pragma unroll
+    for (int w = 0; w < NIW; ++w) {
+        const int r = RPI * (wave * NIW + w) + lane / CPR;
+        voff[w] = (int)(r * row_bytes) + (((lane % CPR) ^ swz<D>(r)) << 4);
+    }
+    auto issue_tile = [&](int jt, unsigned char* dK, unsigned char* dV) __attribute__((always_inline)) {
+        int64_t rows = nkeys - (int64_t)jt * BN;
+        rows = rows > BN ? BN : rows;
+        const int nrec = (int)(rows * row_bytes);
+        const char* kt = kbase + (int64_t)jt * BN * row_bytes;
+        const char* vt = vbase + (int64_t)jt * BN * row_bytes;
+#pragma unroll
+        for (int w = 0; w < NIW; ++w) {
+            const int I = wave * NIW + w;
+            lds_dma16(kt, nrec, (lds_void*)(dK + I * 1024), voff[w]);
+            lds_dma16(vt, nrec, (lds_void*)(dV + I * 1024), voff[w]);
+        }
+    };
+
+    // LDS read addressing (as in the prefill): K rows 32*wave + col at logical
+    // chunk 2*kk + half; V^T through transposing reads of rows
+    // 32*wave + 16*ks + {vrow_lo, vrow_hi}.
+    const int krow = 32 * wave + col;
+    const int ksw = swz<D>(krow);
+    const int trG = lane >> 4;
+    const int trL = lane & 15;
+    const int vrow_lo = 4 * (trG >> 1) + (trL >> 2);
+    const int vrow_hi = vrow_lo + 8;
+    const int vx = 2 * (trG & 1) + ((trL & 3) >> 1);
+    const int vbyte = (trL & 1) * 8;
+
+    issue_tile(0, sK0, sV0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    auto step = [&](int jt, const unsigned char* Kb, const unsigned char* Vb, unsigned char* nK,
+                    unsigned char* nV) __attribute__((always_inline)) {
+        if (jt + 1 < ntiles) issue_tile(jt + 1, nK, nV);
+        // S^T: keys 32*wave + [0, 32) of the tile x the 32 head rows.
+        f32x16 s;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            const V8 ka = __builtin_bit_cast(
+                V8, *reinterpret_cast<const u32x4*>(Kb + krow * RB + (((2 * kk + half) ^ ksw) << 4)));
+            s = M::mm(ka, qreg[kk], s);
+        }
+        // Register r holds key 32*wave + 8*(r/4) + 4*half + r%4 of the tile.
+        const int64_t kt0 = (int64_t)jt * BN + 32 * wave;
+        if (kt0 + 32 > nkeys) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t key = kt0 + 8 * (r >> 2) + 4 * half + (r & 3);
+                s[r] = key < nkeys ? s[r] : kNegInf;
+            }
+        }
+        {
+            float tmx = kNegInf;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) tmx = fmaxf(tmx, s[r]);
+            tm = fmaxf(tm, fmaxf(tmx, xor32(tmx)) * c);
+        }
+        V8 pb[2];
+        float psum = 0.f;
+        auto exps = [&](float nmx) __attribute__((always_inline)) {
+            psum = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = fast_exp2(__builtin_fmaf(s[r], c, nmx));
+                psum += p;
+                pb[r >> 3][r & 7] = (E)p;
+            }
+        };
+        exps((m_run == kNegInf) ? 0.f : -m_run);
+        // Lazy rescale, as in the prefill: a half-row sum of at most kPmax
+        // shows no score passed the running max by more than 8.
+        if (__any(psum > kPmax || (m_run == kNegInf && qvalid))) {
+            float tmax = kNegInf;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
+            tmax = fmaxf(tmax, xor32(tmax)) * c;
+            const float mnew = fmaxf(m_run, tmax);
+            const float alpha = fast_exp2(m_run - ((mnew == kNegInf) ? 0.f : mnew));
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+            l_half *= alpha;
+            m_run = mnew;
+            exps((m_run == kNegInf) ? 0.f : -m_run);
+        }
+        l_half += psum;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) {
+                const int lc = 4 * dt + vx;
+                const unsigned char* vb = Vb + (32 * wave + 16 * ks) * RB;
+                const int rlo = 32 * wave + 16 * ks + vrow_lo, rhi = rlo + 8;
+                const s16x4 lo = lds_read_tr(vb + vrow_lo * RB + ((lc ^ swz<D>(rlo)) << 4) + vbyte);
+                const s16x4 hi = lds_read_tr(vb + vrow_hi * RB + ((lc ^ swz<D>(rhi)) << 4) + vbyte);
+                const V8 va = __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                o[dt] = M::mm(va, pb[ks], o[dt]);
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
+    for (int jt = 0; jt < ntiles; jt += 2) {
+        step(jt, sK0, sV0, sK1, sV1);
+        if (jt + 1 < ntiles) step(jt + 1, sK1, sV1, sK0, sV0);
+    }
+
+    // Merge the two waves through LDS (the K buffers are free now; wave w
+    // writes its [head][D] outputs to sK<w>): per head, M = max of the waves'
+    // maxima, A = sum f_w O_w, L = sum f_w l_w with f_w = 2^(m_w - M).
+    static_assert(32 * D * 4 == TB, "one wave's outputs fill one K buffer");
+    float* s_ow = reinterpret_cast<float*>(wave ? sK1 : sK0);
+    const float* s_o0 = reinterpret_cast<const float*>(sK0);
+    const float* s_o1 = reinterpret_cast<const float*>(sK1);
+    // Move from the reference max to the true max, as the partial reports
+    // the chunk's maximum score.
+    float l_run = l_half + xor32(l_half);
+    if (tm != kNegInf && tm != m_run) {
+        const float f = fast_exp2(m_run - tm);
+        l_run *= f;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[dt][r] *= f;
+    }
+    m_run = tm;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int d = dt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            s_ow[col * D + d] = o[dt][r];
+        }
+    if (half == 0) {
+        s_m[wave][col] = m_run;
+        s_l[wave][col] = l_run;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < g * D; idx += 128) {
+        const int h = idx / D;
+        const int d = idx % D;
+        const float m0 = s_m[0][h], m1 = s_m[1][h];
+        const float Mx = fmaxf(m0, m1);
+        const float ms = (Mx == kNegInf) ? 0.f : Mx;
+        const float f0 = fast_exp2(m0 - ms), f1 = fast_exp2(m1 - ms);
+        const float A = __builtin_fmaf(s_o1[h * D + d], f1, s_o0[h * D + d] * f0);
+        const float Lt = __builtin_fmaf(s_l[1][h], f1, s_l[0][h] * f0);
+        const int64_t row = b * a.num_heads + (int64_t)n2 * g + h;
+        if constexpr (FINISH) {
+            const bool empty = (Mx == kNegInf);
+            reinterpret_cast<uint16_t*>(a.out)[row * D + d] = to_bits<ST>(empty ? 0.f : A / Lt);
+            if (d == 0 && a.lse) a.lse[row] = empty ? kPosInf : (Mx + log2f(Lt)) * kLn2;
+        } else {
+            const int64_t slot = row * a.num_splits + split;
+            a.o_part[slot * D + d] = A;
+            if (d == 0) {
+                a.m_part[slot] = (Mx == kNegInf) ? kNegInf : Mx * kLn2;
+                a.l_part[slot] = Lt;
+            }
+        }
+    }
+}
+
+template <typename ST, int D>
+static const void* mfma_symbol() {
+    return (const void*)&decode_mfma_kernel<ST, D, false>;
+}
+
+int decode_mfma_residency(int dtype, int head_dim) {
+    const void* f = nullptr;
+    if (head_dim == 64) f = dtype == 1 ? mfma_symbol<BF16, 64>() : mfma_symbol<F16, 64>();
+    if (head_dim == 128) f = dtype == 1 ? mfma_symbol<BF16, 128>() : mfma_symbol<F16, 128>();
+    int n = 0;
+    if (!f || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 128, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return n;
+}
+
+template <typename ST, int D>
+static hipError_t dispatch_mfma(const DecodeArgs& a, bool finish, int64_t blocks, hipStream_t s) {
+    const dim3 grid((unsigned)blocks), block(128);
+    if (finish)
+        hipLaunchKernelGGL((decode_mfma_kernel<ST, D, true>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((decode_mfma_kernel<ST, D, false>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, bool finish, int64_t batch,
+                              hipStream_t stream) {
+    if (a.group < 1 || a.group > 32 || a.block_table) return hipErrorInvalidValue;
+    const int64_t blocks = (int64_t)a.num_splits * batch * a.num_kv_heads;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (dtype == 1) {
+        if (head_dim == 128) return dispatch_mfma<BF16, 128>(a, finish, blocks, stream);
+        if (head_dim == 64) return dispatch_mfma<BF16, 64>(a, finish, blocks, stream);
+    } else {
+        if (head_dim == 128) return dispatch_mfma<F16, 128>(a, finish, blocks, stream);
+        if (head_dim == 64) return dispatch_mfma<F16, 64>(a, finish, blocks, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace fa

@@ -164,6 +164,13 @@ hipError_t launch_decode_stage1(const DecodeArgs& a, int dtype, int head_dim, in
 // runtime's occupancy calculator; 0 when no device answers.
 int decode_stage1_residency(int dtype, int head_dim, int heads_per_wg, bool paged);
 hipError_t launch_combine(const CombineArgs& a, int dtype, int head_dim, hipStream_t stream);
+// Matrix-core stage 1 for grouped heads (1 <= group <= 32, contiguous cache,
+// head_dim 64 or 128): one workgroup per (batch, KV head, split), the same
+// partial layout as launch_decode_stage1 (finish = one-split plan writing out
+// and lse).  head_groups is ignored.
+int decode_mfma_residency(int dtype, int head_dim);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, bool finish, int64_t batch,
+                              hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int mask_mode,
                           int64_t batch, hipStream_t stream);
 hipError_t launch_varlen_schedule(const VarlenScheduleArgs& a, hipStream_t stream);

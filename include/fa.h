@@ -154,7 +154,9 @@ typedef struct {
 /* fa_workspace_size -- phase 1 of fa_fwd (the two-phase shape of the IFA guide,
  * section 3): bytes of device workspace fa_fwd needs for *p (0 when none).
  * Also picks the split plan fa_fwd will use for q_seq == 1, for the device
- * that is current on the calling thread. */
+ * that is current on the calling thread: fa_splitkv_plan's fixed chunks, or,
+ * for 4 to 32 query heads per KV head with actual_seq_lengths on a contiguous
+ * cache, pieces balanced over the actual lengths (derived on the device). */
 fa_status fa_workspace_size(const fa_params *p, size_t *bytes);
 
 /* fa_fwd -- phase 2: the attention forward.  q: [B,Q_N,Q_S,D] or [B,Q_S,Q_N,D];

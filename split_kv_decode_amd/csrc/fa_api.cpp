@@ -270,6 +270,33 @@ void plan_splits(const fa_params* p, const Shape& s, int num_cus, int64_t* split
     *splits = (s.KVS + c - 1) / c;
 }
 
+// The plan fa_fwd runs for q_seq == 1.  With per-batch lengths the
+// matrix-core stage 1 takes a length-balanced schedule instead of fixed
+// chunks: the lengths live on the device, so the kernels derive the pieces
+// from them (bal_locate), every piece about the same work, none empty; the
+// host sizes the launch (target + B * KV_N workgroups) and the partials
+// (slots per row: at most ceil(kv_seq / 64) and ceil(target / KV_N) + 1).
+struct DecodePlan {
+    int64_t splits;  // fixed plan: chunks; balanced plan: slots per row
+    int64_t chunk;
+    int32_t bal_nwg; // 0 = fixed plan
+};
+DecodePlan decode_plan(const fa_params* p, const Shape& s) {
+    DecodePlan d;
+    plan_splits(p, s, device_cus(), &d.splits, &d.chunk);
+    d.bal_nwg = 0;
+    if (mfma_decode(p, s) && p->actual_seq_lengths && d.splits > 1) {
+        const int res = mfma_residency(p->dtype == FA_BF16 ? 1 : 0, (int)s.D);
+        const int64_t nwg = int64_t(res > 0 ? res : 2) * device_cus();
+        const int64_t by_len = (s.KVS + 63) / 64;
+        const int64_t by_wg = (nwg + s.KVN - 1) / s.KVN + 1;
+        d.bal_nwg = (int32_t)nwg;
+        d.splits = by_len < by_wg ? by_len : by_wg;
+        d.chunk = 64;
+    }
+    return d;
+}
+
 bool decode_path(const fa_params* p) {
     return p->q_seq == 1 && p->mask_mode == FA_MASK_NONE && p->layout != FA_TND;
 }
@@ -348,6 +375,7 @@ void fill_decode_args(const fa_params* p, const Shape& s, fa::DecodeArgs* a) {
     const int gh = heads_per_workgroup(s.g);
     a->head_groups = (int32_t)(s.g / gh);
     a->scale_log2 = (float)(p->scale * 1.4426950408889634);
+    a->batch = (int32_t)s.B;
 }
 
 fa_status launch_result(hipError_t e, const char* what) {
@@ -357,7 +385,7 @@ fa_status launch_result(hipError_t e, const char* what) {
 
 fa_status run_stage1(const fa_params* p, const Shape& s, int64_t splits, int64_t chunk, const void* q, const void* k,
                      const void* v, float* o_part, float* m_part, float* l_part, unsigned* counters, void* out,
-                     float* lse, hipStream_t stream) {
+                     float* lse, hipStream_t stream, int32_t bal_nwg = 0) {
     fa::DecodeArgs a;
     fill_decode_args(p, s, &a);
     a.q = static_cast<const uint16_t*>(q);
@@ -371,6 +399,7 @@ fa_status run_stage1(const fa_params* p, const Shape& s, int64_t splits, int64_t
     a.chunk = chunk;
     a.num_splits = (int32_t)splits;
     a.counters = counters;
+    a.bal_nwg = bal_nwg;
     const bool finish = (out != nullptr && counters == nullptr);
     if (counters == nullptr && mfma_decode(p, s))
         return launch_result(fa::launch_decode_mfma(a, p->dtype == FA_BF16 ? 1 : 0, (int)s.D, finish, s.B, stream),
@@ -381,8 +410,15 @@ fa_status run_stage1(const fa_params* p, const Shape& s, int64_t splits, int64_t
 }
 
 fa_status run_combine(const fa_params* p, const Shape& s, int64_t splits, const float* o_part, const float* m_part,
-                      const float* l_part, void* out, float* lse, hipStream_t stream) {
+                      const float* l_part, void* out, float* lse, hipStream_t stream, int32_t bal_nwg = 0) {
     fa::CombineArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.bal_nwg = bal_nwg;
+    a.lens = p->actual_seq_lengths;
+    a.kv_seq = s.KVS;
+    a.batch = (int32_t)s.B;
+    a.num_heads = (int32_t)s.QN;
+    a.num_kv_heads = (int32_t)s.KVN;
     a.o_part = o_part;
     a.m_part = m_part;
     a.l_part = l_part;
@@ -539,9 +575,8 @@ fa_status fa_workspace_size(const fa_params* p, size_t* bytes) {
         *bytes = mask_summary_geom(p, s).bytes;
         return ok();
     }
-    int64_t sp, c;
-    plan_splits(p, s, device_cus(), &sp, &c);
-    if (sp > 1) *bytes = partial_bytes(s, sp).total;
+    const DecodePlan dp = decode_plan(p, s);
+    if (dp.splits > 1 || dp.bal_nwg > 0) *bytes = partial_bytes(s, dp.splits).total;
     return ok();
 }
 
@@ -573,10 +608,11 @@ fa_status fa_fwd(const fa_params* p, const void* q, const void* k, const void* v
         return run_prefill(p, s, q, k, v, out, lse, p->layout == FA_TND || need ? workspace : nullptr, hs);
     }
 
-    int64_t sp, c;
-    plan_splits(p, s, device_cus(), &sp, &c);
+    const DecodePlan dp = decode_plan(p, s);
+    const int64_t sp = dp.splits, c = dp.chunk;
     if (sp > kMaxSplits) return fail(FA_ERR_PARAM_INVALID, "plan needs too many splits");
-    if (sp == 1) return run_stage1(p, s, 1, c, q, k, v, nullptr, nullptr, nullptr, nullptr, out, lse, hs);
+    if (sp == 1 && dp.bal_nwg == 0)
+        return run_stage1(p, s, 1, c, q, k, v, nullptr, nullptr, nullptr, nullptr, out, lse, hs);
     const Partials pb = partial_bytes(s, sp);
     if (!workspace) return fail(FA_ERR_NULLPTR, "this call needs %zu bytes of workspace (fa_workspace_size)", pb.total);
     if (!aligned(workspace, 256)) return fail(FA_ERR_PARAM_INVALID, "workspace must be 256-byte aligned");
@@ -586,9 +622,9 @@ fa_status fa_fwd(const fa_params* p, const void* q, const void* k, const void* v
     float* o_part = reinterpret_cast<float*>(w);
     float* m_part = reinterpret_cast<float*>(w + pb.o_bytes);
     float* l_part = reinterpret_cast<float*>(w + pb.o_bytes + pb.m_bytes);
-    st = run_stage1(p, s, sp, c, q, k, v, o_part, m_part, l_part, nullptr, nullptr, nullptr, hs);
+    st = run_stage1(p, s, sp, c, q, k, v, o_part, m_part, l_part, nullptr, nullptr, nullptr, hs, dp.bal_nwg);
     if (st != FA_OK) return st;
-    return run_combine(p, s, sp, o_part, m_part, l_part, out, lse, hs);
+    return run_combine(p, s, sp, o_part, m_part, l_part, out, lse, hs, dp.bal_nwg);
 }
 
 fa_status fa_decode_splitkv(const fa_params* p, int64_t num_splits, int64_t chunk, const void* q, const void* k,

@@ -533,10 +533,16 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     const int t = threadIdx.x;
     const int dq = t % NQ;
     const int sg = t / NQ;
-    const int S = a.num_splits;
-    const float* mp = a.m_part + row * S;
-    const float* lp = a.l_part + row * S;
-    const float* op = a.o_part + row * (int64_t)S * D;
+    const int SS = a.num_splits;  // slots per row
+    int S = SS;                   // slots this row uses
+    if (a.bal_nwg > 0) {          // length-balanced plan: the pieces of this row's batch
+        const int64_t tstar = bal_tstar(a.lens, a.batch, a.kv_seq, a.num_kv_heads, a.bal_nwg);
+        const int64_t nb = bal_pieces(a.lens, row / a.num_heads, a.kv_seq, tstar);
+        S = (int)(nb < SS ? nb : SS);
+    }
+    const float* mp = a.m_part + row * SS;
+    const float* lp = a.l_part + row * SS;
+    const float* op = a.o_part + row * (int64_t)SS * D;
     uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + row * D;
 
     float mx = kNegInf;

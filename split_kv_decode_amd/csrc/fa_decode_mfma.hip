@@ -52,20 +52,32 @@ __global__ __launch_bounds__(128, 2) void decode_mfma_kernel(DecodeArgs a) {
     const int col = lane & 31;
 
     const int64_t blk = blockIdx.x;
-    const int split = (int)(blk % a.num_splits);
-    const int64_t unit = blk / a.num_splits;
-    const int n2 = (int)(unit % a.num_kv_heads);
-    const int64_t b = unit / a.num_kv_heads;
     const int g = a.group;
-
-    int64_t L = a.kv_seq;
-    if (a.lens) {
-        L = a.lens[b];
-        L = L < 0 ? 0 : (L > a.kv_seq ? a.kv_seq : L);
+    int64_t split, b, c0, c1;
+    int n2;
+    if (a.bal_nwg > 0) {
+        // Length-balanced pieces: tstar tiles each, cut at the batch's length.
+        const int64_t tstar = bal_tstar(a.lens, a.batch, a.kv_seq, a.num_kv_heads, a.bal_nwg);
+        int64_t nb;
+        if (!bal_locate(a.lens, a.batch, a.kv_seq, a.num_kv_heads, tstar, blk, &b, &n2, &split, &nb)) return;
+        const int64_t L = bal_len(a.lens, b, a.kv_seq);
+        c0 = split * tstar * 64;
+        c1 = c0 + tstar * 64;
+        if (c1 > L) c1 = L;
+    } else {
+        split = blk % a.num_splits;
+        const int64_t unit = blk / a.num_splits;
+        n2 = (int)(unit % a.num_kv_heads);
+        b = unit / a.num_kv_heads;
+        int64_t L = a.kv_seq;
+        if (a.lens) {
+            L = a.lens[b];
+            L = L < 0 ? 0 : (L > a.kv_seq ? a.kv_seq : L);
+        }
+        c0 = split * a.chunk;
+        c1 = c0 + a.chunk;
+        if (c1 > L) c1 = L;
     }
-    const int64_t c0 = (int64_t)split * a.chunk;
-    int64_t c1 = c0 + a.chunk;
-    if (c1 > L) c1 = L;
 
     if (c1 <= c0) {
         // A chunk at or past the length: its empty partial (or the row
@@ -325,7 +337,9 @@ static hipError_t dispatch_mfma(const DecodeArgs& a, bool finish, int64_t blocks
 hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, bool finish, int64_t batch,
                               hipStream_t stream) {
     if (a.group < 1 || a.group > 32 || a.block_table) return hipErrorInvalidValue;
-    const int64_t blocks = (int64_t)a.num_splits * batch * a.num_kv_heads;
+    if (a.bal_nwg > 0 && (finish || !a.lens || a.batch != batch)) return hipErrorInvalidValue;
+    const int64_t blocks = a.bal_nwg > 0 ? (int64_t)a.bal_nwg + batch * a.num_kv_heads
+                                         : (int64_t)a.num_splits * batch * a.num_kv_heads;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (dtype == 1) {

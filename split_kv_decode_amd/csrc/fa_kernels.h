@@ -40,6 +40,11 @@ struct DecodeArgs {
     int32_t group;            // g = Q_N / KV_N
     int32_t head_groups;      // workgroups per KV head along g
     float scale_log2;         // scale * log2(e)
+    // Matrix-core stage 1 only: a length-balanced schedule (bal_nwg > 0, see
+    // bal_locate) instead of num_splits fixed chunks; num_splits is then the
+    // slot count per row of the partials.
+    int32_t bal_nwg;
+    int32_t batch;            // B (read by the balanced schedule)
 };
 
 struct CombineArgs {
@@ -49,7 +54,13 @@ struct CombineArgs {
     void* out;                // [B][Q_N][D]
     float* lse;               // [B][Q_N] or null
     int64_t rows;             // B * Q_N
-    int32_t num_splits;
+    int32_t num_splits;       // slots per row
+    // Length-balanced plan (bal_nwg > 0): row (b, n1) holds the pieces of
+    // batch b only, their count computed as the stage-1 kernel did.
+    int32_t bal_nwg;
+    const int64_t* lens;
+    int64_t kv_seq;
+    int32_t batch, num_heads, num_kv_heads;
 };
 
 struct PrefillArgs {
@@ -164,6 +175,65 @@ hipError_t launch_decode_stage1(const DecodeArgs& a, int dtype, int head_dim, in
 // runtime's occupancy calculator; 0 when no device answers.
 int decode_stage1_residency(int dtype, int head_dim, int heads_per_wg, bool paged);
 hipError_t launch_combine(const CombineArgs& a, int dtype, int head_dim, hipStream_t stream);
+// Length-balanced decode schedule (matrix-core stage 1 with per-batch
+// lengths).  Batch b has T_b = ceil(L_b / 64) tiles per KV head; with
+// W = KV_N * sum_b T_b and a target of nwg workgroups, a piece holds
+// tstar = max(1, ceil(W / nwg)) tiles and batch b has n_b = ceil(T_b / tstar)
+// pieces per KV head, so every piece is about the same work whatever the
+// lengths.  Workgroups are numbered batch-major, then KV head, then piece; at
+// most nwg + B * KV_N of them are needed.  All lanes of a wave call these
+// (the results are wave-uniform).
+__device__ __forceinline__ int64_t bal_len(const int64_t* lens, int64_t b, int64_t kv_seq) {
+    int64_t L = lens[b];
+    return L < 0 ? 0 : (L > kv_seq ? kv_seq : L);
+}
+__device__ __forceinline__ int64_t bal_tstar(const int64_t* lens, int64_t batch, int64_t kv_seq, int32_t kv_heads,
+                                             int32_t nwg) {
+    const int lane = threadIdx.x & 63;
+    long long w = 0;
+    for (int64_t b = lane; b < batch; b += 64) w += (bal_len(lens, b, kv_seq) + 63) / 64;
+    for (int off = 32; off > 0; off >>= 1) w += __shfl_xor(w, off, 64);
+    const int64_t W = (int64_t)w * kv_heads;
+    const int64_t t = (W + nwg - 1) / nwg;
+    return t < 1 ? 1 : t;
+}
+__device__ __forceinline__ int64_t bal_pieces(const int64_t* lens, int64_t b, int64_t kv_seq, int64_t tstar) {
+    const int64_t T = (bal_len(lens, b, kv_seq) + 63) / 64;
+    return (T + tstar - 1) / tstar;
+}
+// Workgroup w -> (batch, KV head, piece, pieces of the batch); false when w
+// is past the last piece.
+__device__ __forceinline__ bool bal_locate(const int64_t* lens, int64_t batch, int64_t kv_seq, int32_t kv_heads,
+                                           int64_t tstar, int64_t w, int64_t* b_out, int* n2_out, int64_t* j_out,
+                                           int64_t* nb_out) {
+    const int lane = threadIdx.x & 63;
+    long long acc = 0;  // workgroups of the batches before this block of 64
+    for (int64_t base = 0; base < batch; base += 64) {
+        const int64_t b = base + lane;
+        const long long cnt = b < batch ? (long long)bal_pieces(lens, b, kv_seq, tstar) * kv_heads : 0;
+        long long x = cnt;  // inclusive scan over the lanes
+        for (int off = 1; off < 64; off <<= 1) {
+            const long long y = __shfl_up(x, off, 64);
+            if (lane >= off) x += y;
+        }
+        const bool hit = cnt > 0 && w >= acc + (x - cnt) && w < acc + x;
+        const unsigned long long m = __ballot(hit);
+        if (m) {
+            const int src = __builtin_ctzll(m);
+            const long long start = acc + __shfl(x - cnt, src, 64);
+            const long long nb = __shfl(cnt, src, 64) / kv_heads;
+            const long long rem = (long long)w - start;
+            *b_out = base + src;
+            *n2_out = (int)(rem / nb);
+            *j_out = rem % nb;
+            *nb_out = nb;
+            return true;
+        }
+        acc += __shfl(x, 63, 64);
+    }
+    return false;
+}
+
 // Matrix-core stage 1 for grouped heads (1 <= group <= 32, contiguous cache,
 // head_dim 64 or 128): one workgroup per (batch, KV head, split), the same
 // partial layout as launch_decode_stage1 (finish = one-split plan writing out

@@ -127,6 +127,7 @@ DECODE_CASES = [
     dict(B=3, QN=8, KVN=2, KVS=200, D=128, dtype="f16", lens=(0, 200)),    # g = 4, one split
     dict(B=2, QN=16, KVN=4, KVS=1500, D=64, scale=-0.07, layout="BSND"),   # g = 4, negative scale
     dict(B=6, QN=24, KVN=3, KVS=777, D=128, lens=(1, 40)),                  # g = 8, short lengths
+    dict(B=70, QN=8, KVN=2, KVS=1300, D=64, lens=(0, 1300)),   # balanced plan over > 64 batches
 ]
 
 

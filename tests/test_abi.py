@@ -213,6 +213,30 @@ def test_bool_mask_summary_workspace(lib):
     assert st == fa.FA_ERR_PARAM_INVALID and "too small" in fa.fa_last_error()
 
 
+def _partial_bytes(rows, splits, D, units):
+    r256 = lambda x: (x + 255) // 256 * 256
+    return r256(rows * splits * D * 4) + 2 * r256(rows * splits * 4) + r256(units * 4)
+
+
+def test_decode_workspace_fixed_and_balanced_plans(lib):
+    """Host planning without a device (the planner falls back to 256 CUs and no
+    occupancy answer): grouped heads with per-batch lengths take the
+    length-balanced plan, whose slots per row are min(ceil(kv_seq/64),
+    ceil(target/KV_N) + 1) with target = 2 workgroups x 256 CUs."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("the expected sizes assume the planner's no-device fallbacks")
+    base = dict(batch=1, num_heads=32, num_kv_heads=8, q_seq=1, kv_seq=4096)
+    fixed = fa.fa_workspace_size(params(**base))
+    # fixed plan: 8 units, 4 x 256 target -> 128 splits wanted -> 256-token chunks -> 16 splits
+    assert fixed == _partial_bytes(32, 16, 128, 8)
+    bal = fa.fa_workspace_size(params(actual_seq_lengths=FAKE, **base))
+    assert bal == _partial_bytes(32, min(4096 // 64, 512 // 8 + 1), 128, 8)
+    # vector path (g = 2) keeps the fixed plan with or without lengths
+    g2 = dict(base, num_kv_heads=16)
+    assert fa.fa_workspace_size(params(actual_seq_lengths=FAKE, **g2)) == fa.fa_workspace_size(params(**g2))
+
+
 def test_tnd_workspace(lib):
     p = tnd()
     # one (sequence, tile) pair per 128-row tile: ceil(1000/128) + 4 + 1 entries of 8 bytes

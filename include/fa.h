@@ -155,8 +155,9 @@ typedef struct {
  * section 3): bytes of device workspace fa_fwd needs for *p (0 when none).
  * Also picks the split plan fa_fwd will use for q_seq == 1, for the device
  * that is current on the calling thread: fa_splitkv_plan's fixed chunks, or,
- * for 4 to 32 query heads per KV head with actual_seq_lengths on a contiguous
- * cache, pieces balanced over the actual lengths (derived on the device). */
+ * for 4 to 32 query heads per KV head (head_dim 64 or 128) with
+ * actual_seq_lengths, pieces balanced over the actual lengths (derived on the
+ * device). */
 fa_status fa_workspace_size(const fa_params *p, size_t *bytes);
 
 /* fa_fwd -- phase 2: the attention forward.  q: [B,Q_N,Q_S,D] or [B,Q_S,Q_N,D];
@@ -210,10 +211,11 @@ fa_status fa_splitkv_plan(const fa_params *p, int num_cus, int64_t chunk_hint,
  * and at most a cap (a paged cache: 1016 * block_size, the block ids of one
  * chunk being staged on chip; a contiguous one: (chunk + 256) rows of one
  * head within 2^31 bytes, the K/V offsets being 32-bit); fa_splitkv_plan
- * respects both.  With 4 to 32 query heads per KV head, head_dim 64 or 128
- * and a contiguous cache, the chunk runs on the matrix cores (the query heads
- * of a KV head are the rows of one tile; P is rounded to the input type before
- * the PV product, as in the prefill); other shapes use the vector units. */
+ * respects both.  With 4 to 32 query heads per KV head and head_dim 64 or
+ * 128 (contiguous or paged cache), the chunk runs on the matrix cores (the
+ * query heads of a KV head are the rows of one tile; P is rounded to the input
+ * type before the PV product, as in the prefill); other shapes use the vector
+ * units. */
 fa_status fa_decode_splitkv(const fa_params *p, int64_t num_splits, int64_t chunk,
                             const void *q, const void *k, const void *v,
                             float *o_part, float *m_part, float *l_part, void *stream);

@@ -155,8 +155,8 @@ constexpr int kMaxDevices = 64;
 std::atomic<int> g_cus[kMaxDevices];
 // Stage-1 residency per device and (dtype, D, heads per workgroup, paged):
 // 2 x 3 x 4 x 2 = 48 instantiations, then the matrix-core stage 1 per
-// (dtype, D in {64, 128}); 0 = not asked yet, -1 = no answer.
-std::atomic<int> g_resident[kMaxDevices][52];
+// (dtype, D in {64, 128}, paged); 0 = not asked yet, -1 = no answer.
+std::atomic<int> g_resident[kMaxDevices][56];
 
 int current_device() {
     int dev = 0;
@@ -188,28 +188,33 @@ int stage1_residency(int dtype, int D, int gh, bool paged) {
     return n;
 }
 
-int mfma_residency(int dtype, int D) {
+int mfma_residency(int dtype, int D, bool paged) {
     const int dev = current_device();
-    const int key = 48 + dtype * 2 + (D == 64 ? 0 : 1);
+    const int key = 48 + (dtype * 2 + (D == 64 ? 0 : 1)) * 2 + (paged ? 1 : 0);
     if (dev >= 0) {
         const int cached = g_resident[dev][key].load(std::memory_order_relaxed);
         if (cached != 0) return cached > 0 ? cached : 0;
     }
-    const int n = fa::decode_mfma_residency(dtype, D);
+    const int n = fa::decode_mfma_residency(dtype, D, paged);
     if (dev >= 0) g_resident[dev][key].store(n > 0 ? n : -1, std::memory_order_relaxed);
     return n;
 }
 
-// Grouped query heads (4 to 32 per KV head) over a contiguous cache run the
-// matrix-core stage 1: the heads of a KV head form the rows of one matrix
-// tile, where the vector-ALU stage 1 spends a dot-product reduction and an
-// exponential per head on every lane of a row's group and is bound by that
-// vector work rather than by HBM.  Its tiles address 64 rows with 32-bit
-// offsets.
+// Grouped query heads (4 to 32 per KV head) run the matrix-core stage 1: the
+// heads of a KV head form the rows of one matrix tile, where the vector-ALU
+// stage 1 spends a dot-product reduction and an exponential per head on
+// every lane of a row's group and is bound by that vector work rather than
+// by HBM.  Its tiles address 64 rows with 32-bit offsets; on a paged cache a
+// wave load of 4 or 8 rows stays in one block (block sizes are multiples of
+// 16).
+int64_t kv_row_bytes(const fa_params* p, const Shape& s) {
+    if (p->kv_layout == FA_KV_PAGED_BBND) return s.KVN * s.D * 2;
+    if (p->kv_layout == FA_KV_PAGED_BNBD) return s.D * 2;
+    return (p->layout == FA_BNSD ? s.D : s.KVN * s.D) * 2;
+}
 bool mfma_decode(const fa_params* p, const Shape& s) {
-    const int64_t row_bytes = (p->layout == FA_BNSD ? s.D : s.KVN * s.D) * 2;
-    return p->kv_layout == FA_KV_CONTIGUOUS && s.g >= 4 && s.g <= 32 && (s.D == 64 || s.D == 128) &&
-           row_bytes * 64 < (int64_t(1) << 31);
+    return s.g >= 4 && s.g <= 32 && (s.D == 64 || s.D == 128) && kv_row_bytes(p, s) * 64 < (int64_t(1) << 31) &&
+           (p->kv_layout == FA_KV_CONTIGUOUS || p->block_size % 16 == 0);
 }
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -255,7 +260,7 @@ void plan_splits(const fa_params* p, const Shape& s, int num_cus, int64_t* split
     const int gh = heads_per_workgroup(s.g);
     const bool mm = mfma_decode(p, s);
     const int64_t units = mm ? s.B * s.KVN : s.B * s.KVN * (s.g / gh);
-    const int resident = mm ? mfma_residency(p->dtype == FA_BF16 ? 1 : 0, (int)s.D)
+    const int resident = mm ? mfma_residency(p->dtype == FA_BF16 ? 1 : 0, (int)s.D, p->kv_layout != FA_KV_CONTIGUOUS)
                             : stage1_residency(p->dtype == FA_BF16 ? 1 : 0, (int)s.D, gh,
                                                p->kv_layout != FA_KV_CONTIGUOUS);
     const int64_t target = (resident > 0 ? resident : kWgPerCu) * int64_t(num_cus > 0 ? num_cus : 256);
@@ -286,10 +291,15 @@ DecodePlan decode_plan(const fa_params* p, const Shape& s) {
     plan_splits(p, s, device_cus(), &d.splits, &d.chunk);
     d.bal_nwg = 0;
     if (mfma_decode(p, s) && p->actual_seq_lengths && d.splits > 1) {
-        const int res = mfma_residency(p->dtype == FA_BF16 ? 1 : 0, (int)s.D);
+        const bool paged = p->kv_layout != FA_KV_CONTIGUOUS;
+        const int res = mfma_residency(p->dtype == FA_BF16 ? 1 : 0, (int)s.D, paged);
         const int64_t nwg = int64_t(res > 0 ? res : 2) * device_cus();
         const int64_t by_len = (s.KVS + 63) / 64;
         const int64_t by_wg = (nwg + s.KVN - 1) / s.KVN + 1;
+        // A paged piece's block ids are staged on chip: bound the largest
+        // piece (every batch at full length) by the table.
+        const int64_t tmax = (s.KVN * s.B * by_len + nwg - 1) / nwg;
+        if (paged && tmax * 64 / p->block_size + 2 > fa::kPagedTableLds) return d;
         d.bal_nwg = (int32_t)nwg;
         d.splits = by_len < by_wg ? by_len : by_wg;
         d.chunk = 64;

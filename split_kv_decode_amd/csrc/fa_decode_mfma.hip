@@ -25,7 +25,7 @@
 
 namespace fa {
 
-template <typename ST, int D, bool FINISH>
+template <typename ST, int D, bool FINISH, bool PAGED>
 __global__ __launch_bounds__(128, 2) void decode_mfma_kernel(DecodeArgs a) {
     using M = Mfma<ST>;
     using V8 = typename M::V8;
@@ -131,28 +131,64 @@ __global__ __launch_bounds__(128, 2) void decode_mfma_kernel(DecodeArgs a) {
     // Tile jt holds keys c0 + 64*jt + [0, 64); the buffer resource stops at
     // the chunk's end, so rows past it land as zeros.
     const int64_t row_bytes = a.kv_stride_s * 2;
-    const int64_t head_off = b * a.kv_stride_b + (int64_t)n2 * a.kv_stride_n;
-    const char* kbase = reinterpret_cast<const char*>(a.k + head_off) + c0 * row_bytes;
-    const char* vbase = reinterpret_cast<const char*>(a.v + head_off) + c0 * row_bytes;
+    const int64_t head_off = PAGED ? (int64_t)n2 * a.kv_stride_n : b * a.kv_stride_b + (int64_t)n2 * a.kv_stride_n;
+    const char* kbase = reinterpret_cast<const char*>(a.k + head_off) + (PAGED ? 0 : c0 * row_bytes);
+    const char* vbase = reinterpret_cast<const char*>(a.v + head_off) + (PAGED ? 0 : c0 * row_bytes);
     const int64_t nkeys = c1 - c0;
     const int ntiles = (int)((nkeys + BN - 1) / BN);
+    // Paged cache: the block ids of the chunk's logical blocks [cb, cb + nblk),
+    // clamped into the physical range.  A wave load covers RPI (4 or 8)
+    // consecutive rows, and block sizes are multiples of 16, so its rows lie in
+    // one block: each wave load takes its own block base.
+    __shared__ int32_t s_blk[PAGED ? kPagedTableLds : 1];
+    int64_t cb = 0;
+    if constexpr (PAGED) {
+        const int bs = a.block_size;
+        cb = c0 / bs;
+        const int64_t nblk = (c1 - 1) / bs - cb + 1;
+        const int32_t* tb = a.block_table + b * a.max_blocks + cb;
+        for (int64_t i = tid; i < nblk && i < kPagedTableLds; i += 128) {
+            int32_t id = tb[i];
+            id = id < 0 ? 0 : (id >= a.num_blocks ? a.num_blocks - 1 : id);
+            s_blk[i] = id;
+        }
+        __syncthreads();
+    }
     int voff[NIW];
 #pragma unroll
     for (int w = 0; w < NIW; ++w) {
         const int r = RPI * (wave * NIW + w) + lane / CPR;
-        voff[w] = (int)(r * row_bytes) + (((lane % CPR) ^ swz<D>(r)) << 4);
+        const int rr = PAGED ? lane / CPR : r;  // paged: offsets from the wave load's first row
+        voff[w] = (int)(rr * row_bytes) + (((lane % CPR) ^ swz<D>(r)) << 4);
     }
     auto issue_tile = [&](int jt, unsigned char* dK, unsigned char* dV) __attribute__((always_inline)) {
-        int64_t rows = nkeys - (int64_t)jt * BN;
-        rows = rows > BN ? BN : rows;
-        const int nrec = (int)(rows * row_bytes);
-        const char* kt = kbase + (int64_t)jt * BN * row_bytes;
-        const char* vt = vbase + (int64_t)jt * BN * row_bytes;
+        if constexpr (PAGED) {
+            const int bs = a.block_size;
 #pragma unroll
-        for (int w = 0; w < NIW; ++w) {
-            const int I = wave * NIW + w;
-            lds_dma16(kt, nrec, (lds_void*)(dK + I * 1024), voff[w]);
-            lds_dma16(vt, nrec, (lds_void*)(dV + I * 1024), voff[w]);
+            for (int w = 0; w < NIW; ++w) {
+                const int I = wave * NIW + w;
+                const int64_t t = c0 + (int64_t)jt * BN + RPI * I;  // first key of this wave load
+                int64_t rows = c1 - t;
+                rows = rows < 0 ? 0 : (rows > RPI ? RPI : rows);
+                const int nrec = (int)(rows * row_bytes);
+                const int64_t lb = t / bs - cb;
+                const int32_t id = s_blk[lb < kPagedTableLds - 1 ? lb : kPagedTableLds - 1];
+                const int64_t off = ((int64_t)id * a.kv_stride_blk + (t % bs) * a.kv_stride_s) * 2;
+                lds_dma16(kbase + off, nrec, (lds_void*)(dK + I * 1024), voff[w]);
+                lds_dma16(vbase + off, nrec, (lds_void*)(dV + I * 1024), voff[w]);
+            }
+        } else {
+            int64_t rows = nkeys - (int64_t)jt * BN;
+            rows = rows > BN ? BN : rows;
+            const int nrec = (int)(rows * row_bytes);
+            const char* kt = kbase + (int64_t)jt * BN * row_bytes;
+            const char* vt = vbase + (int64_t)jt * BN * row_bytes;
+#pragma unroll
+            for (int w = 0; w < NIW; ++w) {
+                const int I = wave * NIW + w;
+                lds_dma16(kt, nrec, (lds_void*)(dK + I * 1024), voff[w]);
+                lds_dma16(vt, nrec, (lds_void*)(dV + I * 1024), voff[w]);
+            }
         }
     };
 
@@ -308,14 +344,15 @@ __global__ __launch_bounds__(128, 2) void decode_mfma_kernel(DecodeArgs a) {
 }
 
 template <typename ST, int D>
-static const void* mfma_symbol() {
-    return (const void*)&decode_mfma_kernel<ST, D, false>;
+static const void* mfma_symbol(bool paged) {
+    return paged ? (const void*)&decode_mfma_kernel<ST, D, false, true>
+                 : (const void*)&decode_mfma_kernel<ST, D, false, false>;
 }
 
-int decode_mfma_residency(int dtype, int head_dim) {
+int decode_mfma_residency(int dtype, int head_dim, bool paged) {
     const void* f = nullptr;
-    if (head_dim == 64) f = dtype == 1 ? mfma_symbol<BF16, 64>() : mfma_symbol<F16, 64>();
-    if (head_dim == 128) f = dtype == 1 ? mfma_symbol<BF16, 128>() : mfma_symbol<F16, 128>();
+    if (head_dim == 64) f = dtype == 1 ? mfma_symbol<BF16, 64>(paged) : mfma_symbol<F16, 64>(paged);
+    if (head_dim == 128) f = dtype == 1 ? mfma_symbol<BF16, 128>(paged) : mfma_symbol<F16, 128>(paged);
     int n = 0;
     if (!f || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 128, 0) != hipSuccess) {
         (void)hipGetLastError();
@@ -327,16 +364,24 @@ int decode_mfma_residency(int dtype, int head_dim) {
 template <typename ST, int D>
 static hipError_t dispatch_mfma(const DecodeArgs& a, bool finish, int64_t blocks, hipStream_t s) {
     const dim3 grid((unsigned)blocks), block(128);
-    if (finish)
-        hipLaunchKernelGGL((decode_mfma_kernel<ST, D, true>), grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL((decode_mfma_kernel<ST, D, false>), grid, block, 0, s, a);
+    if (a.block_table) {
+        if (finish)
+            hipLaunchKernelGGL((decode_mfma_kernel<ST, D, true, true>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((decode_mfma_kernel<ST, D, false, true>), grid, block, 0, s, a);
+    } else {
+        if (finish)
+            hipLaunchKernelGGL((decode_mfma_kernel<ST, D, true, false>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((decode_mfma_kernel<ST, D, false, false>), grid, block, 0, s, a);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, bool finish, int64_t batch,
                               hipStream_t stream) {
-    if (a.group < 1 || a.group > 32 || a.block_table) return hipErrorInvalidValue;
+    if (a.group < 1 || a.group > 32) return hipErrorInvalidValue;
+    if (a.block_table && (a.block_size < 16 || a.block_size % 16 != 0)) return hipErrorInvalidValue;
     if (a.bal_nwg > 0 && (finish || !a.lens || a.batch != batch)) return hipErrorInvalidValue;
     const int64_t blocks = a.bal_nwg > 0 ? (int64_t)a.bal_nwg + batch * a.num_kv_heads
                                          : (int64_t)a.num_splits * batch * a.num_kv_heads;

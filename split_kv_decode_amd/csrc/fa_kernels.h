@@ -234,11 +234,11 @@ __device__ __forceinline__ bool bal_locate(const int64_t* lens, int64_t batch, i
     return false;
 }
 
-// Matrix-core stage 1 for grouped heads (1 <= group <= 32, contiguous cache,
-// head_dim 64 or 128): one workgroup per (batch, KV head, split), the same
+// Matrix-core stage 1 for grouped heads (1 <= group <= 32, contiguous or
+// paged cache with block sizes a multiple of 16, head_dim 64 or 128): one workgroup per (batch, KV head, split), the same
 // partial layout as launch_decode_stage1 (finish = one-split plan writing out
 // and lse).  head_groups is ignored.
-int decode_mfma_residency(int dtype, int head_dim);
+int decode_mfma_residency(int dtype, int head_dim, bool paged);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, bool finish, int64_t batch,
                               hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int mask_mode,

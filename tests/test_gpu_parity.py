@@ -338,6 +338,9 @@ PAGED_CASES = [
     dict(kv_layout="PA_BNBD", bs=1024, B=1, QN=4, KVN=4, KVS=20000, D=128, lens=(19000, 20000)),
     dict(kv_layout="PA_BNBD", bs=16, B=2, QN=6, KVN=2, KVS=333, D=128, layout="BSND", lens=(1, 333)),
     dict(kv_layout="PA_BBND", bs=64, B=2, QN=8, KVN=2, KVS=1500, D=256, lens=(1, 1500)),
+    # matrix-core stage 1 on paged caches: blocks smaller than a 64-key tile
+    dict(kv_layout="PA_BNBD", bs=16, B=3, QN=32, KVN=4, KVS=900, D=64, lens=(0, 900)),
+    dict(kv_layout="PA_BBND", bs=32, B=2, QN=64, KVN=4, KVS=2100, D=128, lens=(1, 2100)),
 ]
 
 
@@ -355,15 +358,11 @@ def test_paged_decode_matches_oracle_and_contiguous(case):
     r_rows = np.ascontiguousarray(ref if s.layout == "BNSD" else ref.transpose(0, 2, 1, 3))
     check(rows_of(out, s, np.arange(s.B * s.QN)), to_np(lse).reshape(-1),
           r_rows.reshape(-1, s.D), ref_lse.reshape(-1), f"paged {case}")
-    # Same split plan and the same per-token arithmetic as the contiguous cache,
-    # except where the contiguous cache takes the matrix-core stage 1 (4 to 32
-    # query heads per KV head, D of 64 or 128): both are checked against the
-    # oracle above.
-    g = s.QN // s.KVN
-    if not (4 <= g <= 32 and s.D in (64, 128)):
-        c_out, c_lse = run_fwd(inp)
-        assert torch.equal(out, c_out)
-        assert torch.equal(lse.reshape(-1), c_lse.reshape(-1))
+    # Same split plan and the same per-token arithmetic as the contiguous cache
+    # (both take the vector or both the matrix-core stage 1).
+    c_out, c_lse = run_fwd(inp)
+    assert torch.equal(out, c_out)
+    assert torch.equal(lse.reshape(-1), c_lse.reshape(-1))
 
 
 def test_paged_decode_never_reads_unused_table_entries():

@@ -11,7 +11,6 @@ shared library is missing, loading fails with an error.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 import threading
 from typing import Optional, Sequence
@@ -216,15 +215,16 @@ def params_for(q, k, *, layout="BNSD", num_kv_heads=0, scale=1.0, actual_seq_len
                        mask_mode=mode, mask=mask, mask_stride=mask_stride, **extra)
 
 
-def fwd(q, k, v, *, layout="BNSD", scale=None, actual_seq_lengths=None, mask=None,
+def fwd(q, k, v, *, layout="BNSD", scale=1.0, actual_seq_lengths=None, mask=None,
         mask_stride=(0, 0, 0, 0), causal=False, return_lse=False, stream=None,
         kv_layout="contiguous", block_table=None, window=None, cu_seqlens_q=None,
         cu_seqlens_kv=None, seqused_q=None):
-    """Attention forward on device tensors; allocates out (and lse, workspace) with torch."""
+    """Attention forward on device tensors; allocates out (and lse, workspace) with torch.
+    scale defaults to 1.0, the default of the softmax scale in the attention
+    formula of the FlashAttn developer guide's introduction; pass 1/sqrt(D) for
+    the usual attention scale."""
     import torch
-    D = q.shape[-1]
-    sc = (1.0 / math.sqrt(D)) if scale is None else scale
-    p = params_for(q, k, layout=layout, scale=sc, actual_seq_lengths=actual_seq_lengths,
+    p = params_for(q, k, layout=layout, scale=scale, actual_seq_lengths=actual_seq_lengths,
                    mask=mask, mask_stride=mask_stride, causal=causal, kv_layout=kv_layout,
                    block_table=block_table, window=window, cu_seqlens_q=cu_seqlens_q,
                    cu_seqlens_kv=cu_seqlens_kv, seqused_q=seqused_q)

@@ -79,6 +79,15 @@ __global__ __launch_bounds__(128, 2) void decode_mfma_kernel(DecodeArgs a) {
         if (c1 > L) c1 = L;
     }
 
+    // The unit is the same on every lane; stating it keeps the K/V addresses
+    // and buffer resources in scalar registers (without it every tile load
+    // runs in a loop over the lanes' distinct resources).
+    b = uni64(b);
+    split = uni64(split);
+    c0 = uni64(c0);
+    c1 = uni64(c1);
+    n2 = __builtin_amdgcn_readfirstlane(n2);
+
     if (c1 <= c0) {
         // A chunk at or past the length: its empty partial (or the row
         // defaults of a one-split plan) without touching K or V.
@@ -172,7 +181,7 @@ __global__ __launch_bounds__(128, 2) void decode_mfma_kernel(DecodeArgs a) {
                 rows = rows < 0 ? 0 : (rows > RPI ? RPI : rows);
                 const int nrec = (int)(rows * row_bytes);
                 const int64_t lb = t / bs - cb;
-                const int32_t id = s_blk[lb < kPagedTableLds - 1 ? lb : kPagedTableLds - 1];
+                const int32_t id = __builtin_amdgcn_readfirstlane(s_blk[lb < kPagedTableLds - 1 ? lb : kPagedTableLds - 1]);
                 const int64_t off = ((int64_t)id * a.kv_stride_blk + (t % bs) * a.kv_stride_s) * 2;
                 lds_dma16(kbase + off, nrec, (lds_void*)(dK + I * 1024), voff[w]);
                 lds_dma16(vbase + off, nrec, (lds_void*)(dV + I * 1024), voff[w]);

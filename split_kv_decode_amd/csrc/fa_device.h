@@ -124,6 +124,15 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// x as a wave-uniform value (lane 0's): for values every lane computes alike
+// that the compiler cannot prove uniform.
+__device__ __forceinline__ int64_t uni64(int64_t x) {
+    const uint64_t u = (uint64_t)x;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // 16-byte global load / store helpers.
 __device__ __forceinline__ u32x4 ld128(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
@@ -163,5 +172,34 @@ __device__ __forceinline__ void lds_dma16(const void* base, int nrec, lds_void* 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
 #endif
 }
+
+// The same load issued from inline assembly, for loops that order their tile
+// loads themselves (an explicit vmcnt wait and a barrier before a tile is
+// read).  Through the builtin the compiler sees an LDS write and, where it
+// cannot prove that a later LDS read touches another buffer (or at a barrier's
+// fence), waits for every load in flight, which stalls the next tile's
+// prefetch behind the current tile's work.  Here the resource (built once per
+// tile by make_dma_rsrc) and the LDS address are wave-uniform, and M0 carries
+// the LDS address as the instruction requires.
+typedef uint32_t dma_rsrc __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ dma_rsrc make_dma_rsrc(const void* base, int nrec) {
+    const uint64_t p = (uint64_t)base;
+    dma_rsrc r;
+    r[0] = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32)) & 0xffffu;  // stride 0
+    r[2] = __builtin_amdgcn_readfirstlane((uint32_t)nrec);
+    r[3] = 0x00020000u;
+    return r;
+}
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16_unordered(dma_rsrc r, lds_void* dst, int voff) {
+    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m), "v"(voff), "s"(r)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 }  // namespace fa

@@ -248,19 +248,20 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
         const int nrec = (int)(rows * row_bytes);
         const char* kt = kbase + j0 * row_bytes;
         const char* vt = vbase + j0 * row_bytes;
+        const dma_rsrc rk = make_dma_rsrc(kt, nrec), rv = make_dma_rsrc(vt, nrec);
 #pragma unroll
         for (int w = 0; w < NIW; ++w) {
             const int I = wave * NIW + w;
-            lds_dma16(kt, nrec, (lds_void*)(dK + I * 1024), voff[w]);
-            lds_dma16(vt, nrec, (lds_void*)(dV + I * 1024), voff[w]);
+            lds_dma16_unordered(rk, (lds_void*)(dK + I * 1024), voff[w]);
+            lds_dma16_unordered(rv, (lds_void*)(dV + I * 1024), voff[w]);
         }
         if (MASK == 3 && (cls & 2u)) {
             int64_t keys = a.kv_seq - j0;
             keys = keys > BN ? BN : keys;
             const int mrec = mrec_rows + (int)keys;
+            const dma_rsrc rm = make_dma_rsrc(mbase + j0, mrec);
 #pragma unroll
-            for (int w = 0; w < 2; ++w)
-                lds_dma16(mbase + j0, mrec, (lds_void*)(dM + (2 * wave + w) * 1024), moff[w]);
+            for (int w = 0; w < 2; ++w) lds_dma16_unordered(rm, (lds_void*)(dM + (2 * wave + w) * 1024), moff[w]);
         }
     };
 
@@ -595,8 +596,9 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     auto issue = [&](const char* base, int jt, unsigned char* dst) __attribute__((always_inline)) {
         const int nrec = tile_rec(jt);
         const char* t = base + (int64_t)jt * BN * row_bytes;
+        const dma_rsrc r = make_dma_rsrc(t, nrec);
 #pragma unroll
-        for (int w = 0; w < NIW; ++w) lds_dma16(t, nrec, (lds_void*)(dst + (wave * NIW + w) * 1024), voff[w]);
+        for (int w = 0; w < NIW; ++w) lds_dma16_unordered(r, (lds_void*)(dst + (wave * NIW + w) * 1024), voff[w]);
     };
 
     const int krow0 = col, krow1 = 32 + col;
@@ -694,7 +696,10 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     // Phase 2j (even) and 2j+1 (odd) for slot j = {K(jt0+j), V(jt0+j-1)},
     // j = 0 .. nt.  Buffers: K(t) in sK[t&1], V(t) in sV[t&1] (t relative to
     // jt0).  The loop is unrolled by two slots so every LDS access names a
-    // fixed buffer.
+    // fixed buffer.  The barrier between the two phases of a slot only keeps
+    // the groups in step: no LDS data crosses it, so it carries no memory
+    // fence (a fence would wait for the slot's tile loads there and expose
+    // their latency); the barrier at the slot's end orders the loads.
     if (nt > 0) issue(kbase, jt0, sK0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -712,11 +717,11 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
             if constexpr (G == 0) {
                 if (live_prev) pv(Vp);
                 if (live_cur) qk(Kc);
-                __syncthreads();
+                __builtin_amdgcn_s_barrier();
                 if (live_cur) softmax(jt0 + j);
             } else {
                 if (live_prev) softmax(jt0 + j - 1);
-                __syncthreads();
+                __builtin_amdgcn_s_barrier();
                 if (live_prev) pv(Vp);
                 if (live_cur) qk(Kc);
             }

@@ -496,10 +496,13 @@ __global__ __launch_bounds__(256) void decode_stage1_kernel(DecodeArgs a) {
 
 // Stage 2: one workgroup of 256 threads per (b, n1) row merges num_splits
 // partials.  Thread t owns four head-dim columns (t % (D/4)) of one split group
-// (t / (D/4)); the partial-output loads do not depend on the weights, so every
-// load of the row is in flight at once and the kernel costs about two memory
-// latencies.
+// (t / (D/4)).  Its first partial-output loads, the row's m and l, and (for a
+// length-balanced plan) the batch lengths are all issued before anything is
+// reduced, so the common case -- a few dozen splits -- costs one memory
+// latency plus the block reductions; slots past the row's piece count (stale
+// in a balanced plan) are loaded but never weighted.
 constexpr int kCombineWeightsLds = 2048;
+constexpr int kCombinePreload = 4;  // partial-output loads per thread issued up front
 
 __device__ __forceinline__ float block_max256(float x, float* red) {
 #pragma unroll
@@ -534,19 +537,34 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     const int dq = t % NQ;
     const int sg = t / NQ;
     const int SS = a.num_splits;  // slots per row
+    const float* mp = a.m_part + row * SS;
+    const float* lp = a.l_part + row * SS;
+    const float* op = a.o_part + row * (int64_t)SS * D;
+    uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + row * D;
+
+    // Loads that need nothing else first: slot t's m and l, and this thread's
+    // first kCombinePreload partial outputs.  Indexes past the row's slots
+    // re-read its last slot (unbranched loads stay in flight together); those
+    // values are never used.
+    const int tc = t < SS ? t : SS - 1;
+    const float m_t = mp[tc];
+    const float l_t = lp[tc];
+    f32x4 o_pre[kCombinePreload];
+#pragma unroll
+    for (int u = 0; u < kCombinePreload; ++u) {
+        int i = sg + u * NG;
+        i = i < SS ? i : SS - 1;
+        o_pre[u] = *reinterpret_cast<const f32x4*>(op + (int64_t)i * D + 4 * dq);
+    }
     int S = SS;                   // slots this row uses
     if (a.bal_nwg > 0) {          // length-balanced plan: the pieces of this row's batch
         const int64_t tstar = bal_tstar(a.lens, a.batch, a.kv_seq, a.num_kv_heads, a.bal_nwg);
         const int64_t nb = bal_pieces(a.lens, row / a.num_heads, a.kv_seq, tstar);
         S = (int)(nb < SS ? nb : SS);
     }
-    const float* mp = a.m_part + row * SS;
-    const float* lp = a.l_part + row * SS;
-    const float* op = a.o_part + row * (int64_t)SS * D;
-    uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + row * D;
 
-    float mx = kNegInf;
-    for (int i = t; i < S; i += 256) mx = fmaxf(mx, mp[i]);
+    float mx = t < S ? m_t : kNegInf;
+    for (int i = t + 256; i < S; i += 256) mx = fmaxf(mx, mp[i]);
     mx = block_max256(mx, red);
     if (mx == kNegInf) {  // every split empty: RowInvalid defaults
         if (t < NQ) {
@@ -559,27 +577,39 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
         return;
     }
     const float mx2 = mx * kLog2e;
+    auto weight = [&](float mi) __attribute__((always_inline)) {
+        return (mi == kNegInf) ? 0.f : fast_exp2(__builtin_fmaf(mi, kLog2e, -mx2));
+    };
     float ls = 0.f;
-    for (int i = t; i < S; i += 256) {
-        const float mi = mp[i];
-        const float w = (mi == kNegInf) ? 0.f : fast_exp2(__builtin_fmaf(mi, kLog2e, -mx2));
+    if (t < S) {
+        const float w = weight(m_t);
+        if (t < kCombineWeightsLds) s_w[t] = w;
+        ls = w * l_t;
+    }
+    for (int i = t + 256; i < S; i += 256) {
+        const float w = weight(mp[i]);
         if (i < kCombineWeightsLds) s_w[i] = w;
         ls = __builtin_fmaf(w, lp[i], ls);
     }
     ls = block_sum256(ls, red);  // its barriers also publish s_w
 
+    auto w_of = [&](int i) __attribute__((always_inline)) {
+        return i < kCombineWeightsLds ? s_w[i] : weight(mp[i]);
+    };
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int i = sg; i < S; i += NG) {
-        const f32x4 o = *reinterpret_cast<const f32x4*>(op + (int64_t)i * D + 4 * dq);
-        float w;
-        if (i < kCombineWeightsLds) {
-            w = s_w[i];
-        } else {
-            const float mi = mp[i];
-            w = (mi == kNegInf) ? 0.f : fast_exp2(__builtin_fmaf(mi, kLog2e, -mx2));
+#pragma unroll
+    for (int u = 0; u < kCombinePreload; ++u) {
+        const int i = sg + u * NG;
+        if (i < S) {
+            const float w = w_of(i);
+            if (w != 0.f) acc += w * o_pre[u];  // empty splits are skipped whatever their O holds
         }
-        if (w != 0.f) acc += w * o;  // empty splits are skipped whatever their O holds
+    }
+#pragma unroll 4
+    for (int i = sg + kCombinePreload * NG; i < S; i += NG) {
+        const f32x4 o = *reinterpret_cast<const f32x4*>(op + (int64_t)i * D + 4 * dq);
+        const float w = w_of(i);
+        if (w != 0.f) acc += w * o;
     }
     s_acc[sg][dq] = acc;
     __syncthreads();

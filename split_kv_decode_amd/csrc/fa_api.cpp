@@ -293,7 +293,12 @@ DecodePlan decode_plan(const fa_params* p, const Shape& s) {
     if (mfma_decode(p, s) && p->actual_seq_lengths && d.splits > 1) {
         const bool paged = p->kv_layout != FA_KV_CONTIGUOUS;
         const int res = mfma_residency(p->dtype == FA_BF16 ? 1 : 0, (int)s.D, paged);
-        const int64_t nwg = int64_t(res > 0 ? res : 2) * device_cus();
+        const int64_t slots = int64_t(res > 0 ? res : 2) * device_cus();
+        // Rounding each batch's pieces up adds at most one piece per (batch,
+        // KV head): aim at slots - B*KV_N pieces so the whole grid (target +
+        // B*KV_N workgroups) fits in the resident slots and runs as one round.
+        const int64_t units = s.B * s.KVN;
+        const int64_t nwg = slots - units > (slots + 1) / 2 ? slots - units : (slots + 1) / 2;
         const int64_t by_len = (s.KVS + 63) / 64;
         const int64_t by_wg = (nwg + s.KVN - 1) / s.KVN + 1;
         // A paged piece's block ids are staged on chip: bound the largest

@@ -222,7 +222,8 @@ def test_decode_workspace_fixed_and_balanced_plans(lib):
     """Host planning without a device (the planner falls back to 256 CUs and no
     occupancy answer): grouped heads with per-batch lengths take the
     length-balanced plan, whose slots per row are min(ceil(kv_seq/64),
-    ceil(target/KV_N) + 1) with target = 2 workgroups x 256 CUs."""
+    ceil(target/KV_N) + 1) with target = 2 workgroups x 256 CUs - B*KV_N (so the
+    grid of target + B*KV_N workgroups is one resident round)."""
     import torch
     if torch.cuda.is_available():
         pytest.skip("the expected sizes assume the planner's no-device fallbacks")
@@ -231,7 +232,10 @@ def test_decode_workspace_fixed_and_balanced_plans(lib):
     # fixed plan: 8 units, 4 x 256 target -> 128 splits wanted -> 256-token chunks -> 16 splits
     assert fixed == _partial_bytes(32, 16, 128, 8)
     bal = fa.fa_workspace_size(params(actual_seq_lengths=FAKE, **base))
-    assert bal == _partial_bytes(32, min(4096 // 64, 512 // 8 + 1), 128, 8)
+    assert bal == _partial_bytes(32, min(4096 // 64, -(-(512 - 8) // 8) + 1), 128, 8)
+    # B = 8: target 512 - 64 = 448 -> 57 slots per row
+    b8 = dict(base, batch=8)
+    assert fa.fa_workspace_size(params(actual_seq_lengths=FAKE, **b8)) == _partial_bytes(8 * 32, 448 // 8 + 1, 128, 64)
     # vector path (g = 2) keeps the fixed plan with or without lengths
     g2 = dict(base, num_kv_heads=16)
     assert fa.fa_workspace_size(params(actual_seq_lengths=FAKE, **g2)) == fa.fa_workspace_size(params(**g2))

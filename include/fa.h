@@ -214,8 +214,9 @@ fa_status fa_splitkv_plan(const fa_params *p, int num_cus, int64_t chunk_hint,
  * respects both.  With 4 to 32 query heads per KV head and head_dim 64 or
  * 128 (contiguous or paged cache), the chunk runs on the matrix cores (the
  * query heads of a KV head are the rows of one tile; P is rounded to the input
- * type before the PV product, as in the prefill); other shapes use the vector
- * units. */
+ * type before the PV product, as in the prefill; chunks of at most 512 tokens
+ * run on one-wave workgroups, longer ones on two-wave workgroups); other
+ * shapes use the vector units. */
 fa_status fa_decode_splitkv(const fa_params *p, int64_t num_splits, int64_t chunk,
                             const void *q, const void *k, const void *v,
                             float *o_part, float *m_part, float *l_part, void *stream);

@@ -155,8 +155,8 @@ constexpr int kMaxDevices = 64;
 std::atomic<int> g_cus[kMaxDevices];
 // Stage-1 residency per device and (dtype, D, heads per workgroup, paged):
 // 2 x 3 x 4 x 2 = 48 instantiations, then the matrix-core stage 1 per
-// (dtype, D in {64, 128}, paged); 0 = not asked yet, -1 = no answer.
-std::atomic<int> g_resident[kMaxDevices][56];
+// (dtype, D in {64, 128}, paged, waves); 0 = not asked yet, -1 = no answer.
+std::atomic<int> g_resident[kMaxDevices][64];
 
 int current_device() {
     int dev = 0;
@@ -188,14 +188,14 @@ int stage1_residency(int dtype, int D, int gh, bool paged) {
     return n;
 }
 
-int mfma_residency(int dtype, int D, bool paged) {
+int mfma_residency(int dtype, int D, bool paged, int waves) {
     const int dev = current_device();
-    const int key = 48 + (dtype * 2 + (D == 64 ? 0 : 1)) * 2 + (paged ? 1 : 0);
+    const int key = 48 + ((dtype * 2 + (D == 64 ? 0 : 1)) * 2 + (paged ? 1 : 0)) * 2 + (waves == 1 ? 0 : 1);
     if (dev >= 0) {
         const int cached = g_resident[dev][key].load(std::memory_order_relaxed);
         if (cached != 0) return cached > 0 ? cached : 0;
     }
-    const int n = fa::decode_mfma_residency(dtype, D, paged);
+    const int n = fa::decode_mfma_residency(dtype, D, paged, waves);
     if (dev >= 0) g_resident[dev][key].store(n > 0 ? n : -1, std::memory_order_relaxed);
     return n;
 }
@@ -256,13 +256,19 @@ int64_t chunk_cap(const fa_params* p, const Shape& s) {
     return ((int64_t(0x7fffffff) / row_bytes - 256) / 64) * 64;
 }
 
-void plan_splits(const fa_params* p, const Shape& s, int num_cus, int64_t* splits, int64_t* chunk) {
+// The matrix-core stage 1 runs one wave per workgroup for chunks of at most
+// kShortChunk tokens (a few tiles: the time is load latency, and smaller
+// workgroups keep more loads in flight per CU) and two waves otherwise.
+constexpr int64_t kShortChunk = 512;
+int mfma_waves(int64_t chunk) { return chunk <= kShortChunk ? 1 : 2; }
+
+void plan_splits(const fa_params* p, const Shape& s, int num_cus, int64_t* splits, int64_t* chunk, int waves = 2) {
     const int gh = heads_per_workgroup(s.g);
     const bool mm = mfma_decode(p, s);
+    const bool paged = p->kv_layout != FA_KV_CONTIGUOUS;
     const int64_t units = mm ? s.B * s.KVN : s.B * s.KVN * (s.g / gh);
-    const int resident = mm ? mfma_residency(p->dtype == FA_BF16 ? 1 : 0, (int)s.D, p->kv_layout != FA_KV_CONTIGUOUS)
-                            : stage1_residency(p->dtype == FA_BF16 ? 1 : 0, (int)s.D, gh,
-                                               p->kv_layout != FA_KV_CONTIGUOUS);
+    const int resident = mm ? mfma_residency(p->dtype == FA_BF16 ? 1 : 0, (int)s.D, paged, waves)
+                            : stage1_residency(p->dtype == FA_BF16 ? 1 : 0, (int)s.D, gh, paged);
     const int64_t target = (resident > 0 ? resident : kWgPerCu) * int64_t(num_cus > 0 ? num_cus : 256);
     int64_t want = (target + units - 1) / units;
     if (want < 1) want = 1;
@@ -273,6 +279,8 @@ void plan_splits(const fa_params* p, const Shape& s, int num_cus, int64_t* split
     if (c > chunk_cap(p, s)) c = chunk_cap(p, s);
     *chunk = c;
     *splits = (s.KVS + c - 1) / c;
+    // Short chunks: plan again for the one-wave workgroups (more of them fit).
+    if (mm && waves == 2 && *splits > 1 && mfma_waves(c) == 1) plan_splits(p, s, num_cus, splits, chunk, 1);
 }
 
 // The plan fa_fwd runs for q_seq == 1.  With per-batch lengths the
@@ -285,29 +293,41 @@ struct DecodePlan {
     int64_t splits;  // fixed plan: chunks; balanced plan: slots per row
     int64_t chunk;
     int32_t bal_nwg; // 0 = fixed plan
+    int waves;       // matrix-core stage 1: waves per workgroup
 };
+// Balanced plan for a wave count; false when a paged piece could outgrow the
+// on-chip block table.
+bool balanced_plan(const fa_params* p, const Shape& s, int waves, DecodePlan* d) {
+    const bool paged = p->kv_layout != FA_KV_CONTIGUOUS;
+    const int res = mfma_residency(p->dtype == FA_BF16 ? 1 : 0, (int)s.D, paged, waves);
+    const int64_t slots = int64_t(res > 0 ? res : 2) * device_cus();
+    // Rounding each batch's pieces up adds at most one piece per (batch,
+    // KV head): aim at slots - B*KV_N pieces so the whole grid (target +
+    // B*KV_N workgroups) fits in the resident slots and runs as one round.
+    const int64_t units = s.B * s.KVN;
+    const int64_t nwg = slots - units > (slots + 1) / 2 ? slots - units : (slots + 1) / 2;
+    const int64_t by_len = (s.KVS + 63) / 64;
+    const int64_t by_wg = (nwg + s.KVN - 1) / s.KVN + 1;
+    // A paged piece's block ids are staged on chip: bound the largest
+    // piece (every batch at full length) by the table.
+    const int64_t tmax = (s.KVN * s.B * by_len + nwg - 1) / nwg;
+    if (paged && tmax * 64 / p->block_size + 2 > fa::kPagedTableLds) return false;
+    d->bal_nwg = (int32_t)nwg;
+    d->splits = by_len < by_wg ? by_len : by_wg;
+    d->chunk = 64;
+    d->waves = waves;
+    return true;
+}
 DecodePlan decode_plan(const fa_params* p, const Shape& s) {
     DecodePlan d;
     plan_splits(p, s, device_cus(), &d.splits, &d.chunk);
     d.bal_nwg = 0;
+    d.waves = mfma_waves(d.chunk);
     if (mfma_decode(p, s) && p->actual_seq_lengths && d.splits > 1) {
-        const bool paged = p->kv_layout != FA_KV_CONTIGUOUS;
-        const int res = mfma_residency(p->dtype == FA_BF16 ? 1 : 0, (int)s.D, paged);
-        const int64_t slots = int64_t(res > 0 ? res : 2) * device_cus();
-        // Rounding each batch's pieces up adds at most one piece per (batch,
-        // KV head): aim at slots - B*KV_N pieces so the whole grid (target +
-        // B*KV_N workgroups) fits in the resident slots and runs as one round.
-        const int64_t units = s.B * s.KVN;
-        const int64_t nwg = slots - units > (slots + 1) / 2 ? slots - units : (slots + 1) / 2;
-        const int64_t by_len = (s.KVS + 63) / 64;
-        const int64_t by_wg = (nwg + s.KVN - 1) / s.KVN + 1;
-        // A paged piece's block ids are staged on chip: bound the largest
-        // piece (every batch at full length) by the table.
-        const int64_t tmax = (s.KVN * s.B * by_len + nwg - 1) / nwg;
-        if (paged && tmax * 64 / p->block_size + 2 > fa::kPagedTableLds) return d;
-        d.bal_nwg = (int32_t)nwg;
-        d.splits = by_len < by_wg ? by_len : by_wg;
-        d.chunk = 64;
+        // The balanced pieces share out what the fixed chunks would cover at
+        // full lengths, so they are no longer: the fixed plan's wave count holds.
+        DecodePlan b = d;
+        if (balanced_plan(p, s, d.waves, &b)) d = b;
     }
     return d;
 }
@@ -400,7 +420,7 @@ fa_status launch_result(hipError_t e, const char* what) {
 
 fa_status run_stage1(const fa_params* p, const Shape& s, int64_t splits, int64_t chunk, const void* q, const void* k,
                      const void* v, float* o_part, float* m_part, float* l_part, unsigned* counters, void* out,
-                     float* lse, hipStream_t stream, int32_t bal_nwg = 0) {
+                     float* lse, hipStream_t stream, int32_t bal_nwg = 0, int waves = 0) {
     fa::DecodeArgs a;
     fill_decode_args(p, s, &a);
     a.q = static_cast<const uint16_t*>(q);
@@ -417,7 +437,8 @@ fa_status run_stage1(const fa_params* p, const Shape& s, int64_t splits, int64_t
     a.bal_nwg = bal_nwg;
     const bool finish = (out != nullptr && counters == nullptr);
     if (counters == nullptr && mfma_decode(p, s))
-        return launch_result(fa::launch_decode_mfma(a, p->dtype == FA_BF16 ? 1 : 0, (int)s.D, finish, s.B, stream),
+        return launch_result(fa::launch_decode_mfma(a, p->dtype == FA_BF16 ? 1 : 0, (int)s.D, finish,
+                                                    waves > 0 ? waves : mfma_waves(chunk), s.B, stream),
                              "decode stage 1");
     return launch_result(fa::launch_decode_stage1(a, p->dtype == FA_BF16 ? 1 : 0, (int)s.D,
                                                   heads_per_workgroup(s.g), finish, s.B, stream),
@@ -637,7 +658,8 @@ fa_status fa_fwd(const fa_params* p, const void* q, const void* k, const void* v
     float* o_part = reinterpret_cast<float*>(w);
     float* m_part = reinterpret_cast<float*>(w + pb.o_bytes);
     float* l_part = reinterpret_cast<float*>(w + pb.o_bytes + pb.m_bytes);
-    st = run_stage1(p, s, sp, c, q, k, v, o_part, m_part, l_part, nullptr, nullptr, nullptr, hs, dp.bal_nwg);
+    st = run_stage1(p, s, sp, c, q, k, v, o_part, m_part, l_part, nullptr, nullptr, nullptr, hs, dp.bal_nwg,
+                    dp.waves);
     if (st != FA_OK) return st;
     return run_combine(p, s, sp, o_part, m_part, l_part, out, lse, hs, dp.bal_nwg);
 }

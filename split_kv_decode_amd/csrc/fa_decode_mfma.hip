@@ -8,12 +8,16 @@
 // than HBM once g reaches 4.  Here the g heads are the rows of a 32-row
 // matrix tile instead: S^T = K Q^T and O^T = V^T P^T on
 // v_mfma_f32_32x32x16_{bf16,f16} exactly as in the prefill kernel, with the
-// rows past g zero (their results are dropped).  A workgroup of two waves
-// takes one (batch, KV head, chunk) unit; K and V tiles of 64 keys go HBM ->
-// LDS with direct buffer loads, double buffered; wave w handles keys
+// rows past g zero (their results are dropped).  A workgroup of NWV waves
+// takes one (batch, KV head, chunk) unit; K and V tiles of 32*NWV keys go
+// HBM -> LDS with direct buffer loads, double buffered; wave w handles keys
 // [32w, 32w+32) of each tile with its own online softmax (running max,
-// lazy rescale as in the prefill), and the two waves are merged through LDS
-// at the end.  The partial (unnormalised O, max in natural-log units, sum)
+// lazy rescale as in the prefill), and two waves are merged through LDS at
+// the end.  Two waves (64-key tiles, 64 KB of LDS at D = 128) suit long
+// chunks; one wave (32-key tiles, 32 KB) lets five workgroups share a CU, which keeps
+// more tile loads in flight when the chunks are a few tiles long and the
+// load latency, not the bandwidth, sets the time.  The partial
+// (unnormalised O, max in natural-log units, sum)
 // has the layout and meaning of the vector-ALU stage 1 (FlashDecoding
 // tutorial, stage 1), so the same combine kernel (stage 2) merges it; a
 // one-split plan writes the output and lse in place.
@@ -25,25 +29,26 @@
 
 namespace fa {
 
-template <typename ST, int D, bool FINISH, bool PAGED>
-__global__ __launch_bounds__(128, 2) void decode_mfma_kernel(DecodeArgs a) {
+template <typename ST, int D, bool FINISH, bool PAGED, int NWV>
+__global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(DecodeArgs a) {
+    static_assert(NWV == 1 || NWV == 2, "one or two waves");
     using M = Mfma<ST>;
     using V8 = typename M::V8;
     using E = typename M::E;
-    constexpr int NWV = 2;              // waves per workgroup
-    constexpr int BN = 64;              // keys per KV tile
+    constexpr int BN = 32 * NWV;        // keys per KV tile (32 per wave)
+    constexpr int NT = 64 * NWV;        // threads
     constexpr int RB = D * 2;           // bytes per LDS row
     constexpr int TB = BN * RB;         // bytes per K or V tile
     constexpr int CPR = D / 8;          // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;       // rows per wave load
     constexpr int NIW = TB / 1024 / NWV;
     constexpr float kPmax = 256.f;
-    static_assert(NIW >= 1, "tile too small for two waves");
+    static_assert(NIW >= 1, "tile too small");
     __shared__ __attribute__((aligned(1024))) unsigned char sK0[TB];
     __shared__ __attribute__((aligned(1024))) unsigned char sK1[TB];
     __shared__ __attribute__((aligned(1024))) unsigned char sV0[TB];
     __shared__ __attribute__((aligned(1024))) unsigned char sV1[TB];
-    __shared__ float s_m[NWV][32], s_l[NWV][32];
+    __shared__ float s_m[NWV][32], s_l[NWV][32];  // two waves: the merge
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -91,7 +96,7 @@ __global__ __launch_bounds__(128, 2) void decode_mfma_kernel(DecodeArgs a) {
     if (c1 <= c0) {
         // A chunk at or past the length: its empty partial (or the row
         // defaults of a one-split plan) without touching K or V.
-        for (int idx = tid; idx < g * D; idx += 128) {
+        for (int idx = tid; idx < g * D; idx += NT) {
             const int h = idx / D;
             const int d = idx % D;
             const int64_t row = b * a.num_heads + (int64_t)n2 * g + h;
@@ -156,7 +161,7 @@ __global__ __launch_bounds__(128, 2) void decode_mfma_kernel(DecodeArgs a) {
         cb = c0 / bs;
         const int64_t nblk = (c1 - 1) / bs - cb + 1;
         const int32_t* tb = a.block_table + b * a.max_blocks + cb;
-        for (int64_t i = tid; i < nblk && i < kPagedTableLds; i += 128) {
+        for (int64_t i = tid; i < nblk && i < kPagedTableLds; i += NT) {
             int32_t id = tb[i];
             id = id < 0 ? 0 : (id >= a.num_blocks ? a.num_blocks - 1 : id);
             s_blk[i] = id;
@@ -296,100 +301,160 @@ __global__ __launch_bounds__(128, 2) void decode_mfma_kernel(DecodeArgs a) {
         if (jt + 1 < ntiles) step(jt + 1, sK1, sV1, sK0, sV0);
     }
 
-    // Merge the two waves through LDS (the K buffers are free now; wave w
-    // writes its [head][D] outputs to sK<w>): per head, M = max of the waves'
-    // maxima, A = sum f_w O_w, L = sum f_w l_w with f_w = 2^(m_w - M).
-    static_assert(32 * D * 4 == TB, "one wave's outputs fill one K buffer");
-    float* s_ow = reinterpret_cast<float*>(wave ? sK1 : sK0);
-    const float* s_o0 = reinterpret_cast<const float*>(sK0);
-    const float* s_o1 = reinterpret_cast<const float*>(sK1);
-    // Move from the reference max to the true max, as the partial reports
-    // the chunk's maximum score.
-    float l_run = l_half + xor32(l_half);
-    if (tm != kNegInf && tm != m_run) {
-        const float f = fast_exp2(m_run - tm);
-        l_run *= f;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[dt][r] *= f;
-    }
-    m_run = tm;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int d = dt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            s_ow[col * D + d] = o[dt][r];
+    if constexpr (NWV == 1) {
+        // Move from the reference max to the true max, as the partial reports
+        // the chunk's maximum score; lane (col, half) then holds head col,
+        // head-dim elements dt*32 + 8*(r/4) + 4*half + [0, 4).
+        float l_run = l_half + xor32(l_half);
+        if (tm != kNegInf && tm != m_run) {
+            const float f = fast_exp2(m_run - tm);
+            l_run *= f;
+    #pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) o[dt][r] *= f;
         }
-    if (half == 0) {
-        s_m[wave][col] = m_run;
-        s_l[wave][col] = l_run;
-    }
-    __syncthreads();
-    for (int idx = tid; idx < g * D; idx += 128) {
-        const int h = idx / D;
-        const int d = idx % D;
-        const float m0 = s_m[0][h], m1 = s_m[1][h];
-        const float Mx = fmaxf(m0, m1);
-        const float ms = (Mx == kNegInf) ? 0.f : Mx;
-        const float f0 = fast_exp2(m0 - ms), f1 = fast_exp2(m1 - ms);
-        const float A = __builtin_fmaf(s_o1[h * D + d], f1, s_o0[h * D + d] * f0);
-        const float Lt = __builtin_fmaf(s_l[1][h], f1, s_l[0][h] * f0);
-        const int64_t row = b * a.num_heads + (int64_t)n2 * g + h;
-        if constexpr (FINISH) {
-            const bool empty = (Mx == kNegInf);
-            reinterpret_cast<uint16_t*>(a.out)[row * D + d] = to_bits<ST>(empty ? 0.f : A / Lt);
-            if (d == 0 && a.lse) a.lse[row] = empty ? kPosInf : (Mx + log2f(Lt)) * kLn2;
-        } else {
-            const int64_t slot = row * a.num_splits + split;
-            a.o_part[slot * D + d] = A;
-            if (d == 0) {
-                a.m_part[slot] = (Mx == kNegInf) ? kNegInf : Mx * kLn2;
-                a.l_part[slot] = Lt;
+        if (qvalid) {
+            const int64_t row = b * a.num_heads + (int64_t)n2 * g + col;
+            const bool empty = (tm == kNegInf);
+            if constexpr (FINISH) {
+                const float inv = empty ? 0.f : 1.f / l_run;
+                uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + row * D;
+    #pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt)
+    #pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const int d = dt * 32 + 8 * q4 + 4 * half;
+                        u32x2 w;
+                        w[0] = pack2<ST>(o[dt][4 * q4] * inv, o[dt][4 * q4 + 1] * inv);
+                        w[1] = pack2<ST>(o[dt][4 * q4 + 2] * inv, o[dt][4 * q4 + 3] * inv);
+                        *reinterpret_cast<u32x2*>(op + d) = w;
+                    }
+                if (half == 0 && a.lse) a.lse[row] = empty ? kPosInf : (tm + log2f(l_run)) * kLn2;
+            } else {
+                const int64_t slot = row * a.num_splits + split;
+                float* op = a.o_part + slot * D;
+    #pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt)
+    #pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const int d = dt * 32 + 8 * q4 + 4 * half;
+                        *reinterpret_cast<f32x4*>(op + d) =
+                            f32x4{o[dt][4 * q4], o[dt][4 * q4 + 1], o[dt][4 * q4 + 2], o[dt][4 * q4 + 3]};
+                    }
+                if (half == 0) {
+                    a.m_part[slot] = empty ? kNegInf : tm * kLn2;
+                    a.l_part[slot] = l_run;
+                }
+            }
+        }
+    } else {
+        // Merge the two waves through LDS (the K buffers are free now; wave w
+        // writes its [head][D] outputs to sK<w>): per head, M = max of the waves'
+        // maxima, A = sum f_w O_w, L = sum f_w l_w with f_w = 2^(m_w - M).
+        static_assert(32 * D * 4 == TB, "one wave's outputs fill one K buffer");
+        float* s_ow = reinterpret_cast<float*>(wave ? sK1 : sK0);
+        const float* s_o0 = reinterpret_cast<const float*>(sK0);
+        const float* s_o1 = reinterpret_cast<const float*>(sK1);
+        // Move from the reference max to the true max, as the partial reports
+        // the chunk's maximum score.
+        float l_run = l_half + xor32(l_half);
+        if (tm != kNegInf && tm != m_run) {
+            const float f = fast_exp2(m_run - tm);
+            l_run *= f;
+    #pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) o[dt][r] *= f;
+        }
+        m_run = tm;
+    #pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+    #pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int d = dt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                s_ow[col * D + d] = o[dt][r];
+            }
+        if (half == 0) {
+            s_m[wave][col] = m_run;
+            s_l[wave][col] = l_run;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < g * D; idx += NT) {
+            const int h = idx / D;
+            const int d = idx % D;
+            const float m0 = s_m[0][h], m1 = s_m[1][h];
+            const float Mx = fmaxf(m0, m1);
+            const float ms = (Mx == kNegInf) ? 0.f : Mx;
+            const float f0 = fast_exp2(m0 - ms), f1 = fast_exp2(m1 - ms);
+            const float A = __builtin_fmaf(s_o1[h * D + d], f1, s_o0[h * D + d] * f0);
+            const float Lt = __builtin_fmaf(s_l[1][h], f1, s_l[0][h] * f0);
+            const int64_t row = b * a.num_heads + (int64_t)n2 * g + h;
+            if constexpr (FINISH) {
+                const bool empty = (Mx == kNegInf);
+                reinterpret_cast<uint16_t*>(a.out)[row * D + d] = to_bits<ST>(empty ? 0.f : A / Lt);
+                if (d == 0 && a.lse) a.lse[row] = empty ? kPosInf : (Mx + log2f(Lt)) * kLn2;
+            } else {
+                const int64_t slot = row * a.num_splits + split;
+                a.o_part[slot * D + d] = A;
+                if (d == 0) {
+                    a.m_part[slot] = (Mx == kNegInf) ? kNegInf : Mx * kLn2;
+                    a.l_part[slot] = Lt;
+                }
             }
         }
     }
 }
 
-template <typename ST, int D>
+template <typename ST, int D, int NWV>
 static const void* mfma_symbol(bool paged) {
-    return paged ? (const void*)&decode_mfma_kernel<ST, D, false, true>
-                 : (const void*)&decode_mfma_kernel<ST, D, false, false>;
+    return paged ? (const void*)&decode_mfma_kernel<ST, D, false, true, NWV>
+                 : (const void*)&decode_mfma_kernel<ST, D, false, false, NWV>;
 }
 
-int decode_mfma_residency(int dtype, int head_dim, bool paged) {
-    const void* f = nullptr;
-    if (head_dim == 64) f = dtype == 1 ? mfma_symbol<BF16, 64>(paged) : mfma_symbol<F16, 64>(paged);
-    if (head_dim == 128) f = dtype == 1 ? mfma_symbol<BF16, 128>(paged) : mfma_symbol<F16, 128>(paged);
+template <int NWV>
+static const void* mfma_symbol_for(int dtype, int head_dim, bool paged) {
+    if (head_dim == 64) return dtype == 1 ? mfma_symbol<BF16, 64, NWV>(paged) : mfma_symbol<F16, 64, NWV>(paged);
+    if (head_dim == 128) return dtype == 1 ? mfma_symbol<BF16, 128, NWV>(paged) : mfma_symbol<F16, 128, NWV>(paged);
+    return nullptr;
+}
+
+int decode_mfma_residency(int dtype, int head_dim, bool paged, int waves) {
+    const void* f = waves == 1 ? mfma_symbol_for<1>(dtype, head_dim, paged) : mfma_symbol_for<2>(dtype, head_dim, paged);
     int n = 0;
-    if (!f || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 128, 0) != hipSuccess) {
+    if (!f || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 64 * waves, 0) != hipSuccess) {
         (void)hipGetLastError();
         return 0;
     }
     return n;
 }
 
-template <typename ST, int D>
+template <typename ST, int D, int NWV>
 static hipError_t dispatch_mfma(const DecodeArgs& a, bool finish, int64_t blocks, hipStream_t s) {
-    const dim3 grid((unsigned)blocks), block(128);
+    const dim3 grid((unsigned)blocks), block(64 * NWV);
     if (a.block_table) {
         if (finish)
-            hipLaunchKernelGGL((decode_mfma_kernel<ST, D, true, true>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((decode_mfma_kernel<ST, D, true, true, NWV>), grid, block, 0, s, a);
         else
-            hipLaunchKernelGGL((decode_mfma_kernel<ST, D, false, true>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((decode_mfma_kernel<ST, D, false, true, NWV>), grid, block, 0, s, a);
     } else {
         if (finish)
-            hipLaunchKernelGGL((decode_mfma_kernel<ST, D, true, false>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((decode_mfma_kernel<ST, D, true, false, NWV>), grid, block, 0, s, a);
         else
-            hipLaunchKernelGGL((decode_mfma_kernel<ST, D, false, false>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((decode_mfma_kernel<ST, D, false, false, NWV>), grid, block, 0, s, a);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, bool finish, int64_t batch,
+template <typename ST, int D>
+static hipError_t dispatch_mfma_waves(const DecodeArgs& a, bool finish, int waves, int64_t blocks, hipStream_t s) {
+    return waves == 1 ? dispatch_mfma<ST, D, 1>(a, finish, blocks, s) : dispatch_mfma<ST, D, 2>(a, finish, blocks, s);
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, bool finish, int waves, int64_t batch,
                               hipStream_t stream) {
     if (a.group < 1 || a.group > 32) return hipErrorInvalidValue;
+    if (waves != 1 && waves != 2) return hipErrorInvalidValue;
     if (a.block_table && (a.block_size < 16 || a.block_size % 16 != 0)) return hipErrorInvalidValue;
     if (a.bal_nwg > 0 && (finish || !a.lens || a.batch != batch)) return hipErrorInvalidValue;
     const int64_t blocks = a.bal_nwg > 0 ? (int64_t)a.bal_nwg + batch * a.num_kv_heads
@@ -397,11 +462,11 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, bool
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (dtype == 1) {
-        if (head_dim == 128) return dispatch_mfma<BF16, 128>(a, finish, blocks, stream);
-        if (head_dim == 64) return dispatch_mfma<BF16, 64>(a, finish, blocks, stream);
+        if (head_dim == 128) return dispatch_mfma_waves<BF16, 128>(a, finish, waves, blocks, stream);
+        if (head_dim == 64) return dispatch_mfma_waves<BF16, 64>(a, finish, waves, blocks, stream);
     } else {
-        if (head_dim == 128) return dispatch_mfma<F16, 128>(a, finish, blocks, stream);
-        if (head_dim == 64) return dispatch_mfma<F16, 64>(a, finish, blocks, stream);
+        if (head_dim == 128) return dispatch_mfma_waves<F16, 128>(a, finish, waves, blocks, stream);
+        if (head_dim == 64) return dispatch_mfma_waves<F16, 64>(a, finish, waves, blocks, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -235,11 +235,14 @@ __device__ __forceinline__ bool bal_locate(const int64_t* lens, int64_t batch, i
 }
 
 // Matrix-core stage 1 for grouped heads (1 <= group <= 32, contiguous or
-// paged cache with block sizes a multiple of 16, head_dim 64 or 128): one workgroup per (batch, KV head, split), the same
-// partial layout as launch_decode_stage1 (finish = one-split plan writing out
-// and lse).  head_groups is ignored.
-int decode_mfma_residency(int dtype, int head_dim, bool paged);
-hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, bool finish, int64_t batch,
+// paged cache with block sizes a multiple of 16, head_dim 64 or 128): one
+// workgroup per (batch, KV head, split), the same partial layout as
+// launch_decode_stage1 (finish = one-split plan writing out and lse).  waves
+// = 2: two waves share 64-key tiles and merge at the end; waves = 1: one wave
+// per workgroup on 32-key tiles, a quarter of the LDS, so more workgroups
+// (and more tile loads) per CU for short pieces.
+int decode_mfma_residency(int dtype, int head_dim, bool paged, int waves);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, bool finish, int waves, int64_t batch,
                               hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int mask_mode,
                           int64_t batch, hipStream_t stream);

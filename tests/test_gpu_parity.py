@@ -128,6 +128,10 @@ DECODE_CASES = [
     dict(B=2, QN=16, KVN=4, KVS=1500, D=64, scale=-0.07, layout="BSND"),   # g = 4, negative scale
     dict(B=6, QN=24, KVN=3, KVS=777, D=128, lens=(1, 40)),                  # g = 8, short lengths
     dict(B=70, QN=8, KVN=2, KVS=1300, D=64, lens=(0, 1300)),   # balanced plan over > 64 batches
+    # chunks above 512 tokens (on 256 CUs) take the two-wave, 64-key-tile stage 1;
+    # the cases above run one wave on 32-key tiles
+    dict(B=1, QN=32, KVN=8, KVS=40000, D=128),                       # g = 4, fixed chunks
+    dict(B=2, QN=16, KVN=4, KVS=40000, D=64, lens=(1, 40000)),       # g = 4, balanced pieces
 ]
 
 
@@ -341,6 +345,7 @@ PAGED_CASES = [
     # matrix-core stage 1 on paged caches: blocks smaller than a 64-key tile
     dict(kv_layout="PA_BNBD", bs=16, B=3, QN=32, KVN=4, KVS=900, D=64, lens=(0, 900)),
     dict(kv_layout="PA_BBND", bs=32, B=2, QN=64, KVN=4, KVS=2100, D=128, lens=(1, 2100)),
+    dict(kv_layout="PA_BBND", bs=64, B=1, QN=32, KVN=8, KVS=40000, D=128, lens=(30000, 40000)),  # two waves
 ]
 
 

@@ -309,9 +309,9 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2))) v
         if (tm != kNegInf && tm != m_run) {
             const float f = fast_exp2(m_run - tm);
             l_run *= f;
-    #pragma unroll
+#pragma unroll
             for (int dt = 0; dt < D / 32; ++dt)
-    #pragma unroll
+#pragma unroll
                 for (int r = 0; r < 16; ++r) o[dt][r] *= f;
         }
         if (qvalid) {
@@ -320,9 +320,9 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2))) v
             if constexpr (FINISH) {
                 const float inv = empty ? 0.f : 1.f / l_run;
                 uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + row * D;
-    #pragma unroll
+#pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt)
-    #pragma unroll
+#pragma unroll
                     for (int q4 = 0; q4 < 4; ++q4) {
                         const int d = dt * 32 + 8 * q4 + 4 * half;
                         u32x2 w;
@@ -334,9 +334,9 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2))) v
             } else {
                 const int64_t slot = row * a.num_splits + split;
                 float* op = a.o_part + slot * D;
-    #pragma unroll
+#pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt)
-    #pragma unroll
+#pragma unroll
                     for (int q4 = 0; q4 < 4; ++q4) {
                         const int d = dt * 32 + 8 * q4 + 4 * half;
                         *reinterpret_cast<f32x4*>(op + d) =
@@ -362,15 +362,15 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2))) v
         if (tm != kNegInf && tm != m_run) {
             const float f = fast_exp2(m_run - tm);
             l_run *= f;
-    #pragma unroll
+#pragma unroll
             for (int dt = 0; dt < D / 32; ++dt)
-    #pragma unroll
+#pragma unroll
                 for (int r = 0; r < 16; ++r) o[dt][r] *= f;
         }
         m_run = tm;
-    #pragma unroll
+#pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
-    #pragma unroll
+#pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int d = dt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
                 s_ow[col * D + d] = o[dt][r];

@@ -153,7 +153,8 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2))) v
     // Paged cache: the block ids of the chunk's logical blocks [cb, cb + nblk),
     // clamped into the physical range.  A wave load covers RPI (4 or 8)
     // consecutive rows, and block sizes are multiples of 16, so its rows lie in
-    // one block: each wave load takes its own block base.
+    // one block: each wave load takes its own block base.  (Past the chunk's
+    // end a load reads nothing -- its byte range is 0 -- whatever block it names.)
     __shared__ int32_t s_blk[PAGED ? kPagedTableLds : 1];
     int64_t cb = 0;
     if constexpr (PAGED) {
@@ -175,6 +176,15 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2))) v
         const int rr = PAGED ? lane / CPR : r;  // paged: offsets from the wave load's first row
         voff[w] = (int)(rr * row_bytes) + (((lane % CPR) ^ swz<D>(r)) << 4);
     }
+    // Paged: a (logical block, row in block) cursor at this wave's next wave
+    // load, advanced by additions only (tiles are issued in order): one
+    // division here instead of a 64-bit division per wave load.
+    int cur_blk = 0, cur_row = 0;
+    if constexpr (PAGED) {
+        const int64_t t0 = c0 + RPI * (wave * NIW);
+        cur_blk = (int)(t0 / a.block_size - cb);
+        cur_row = (int)(t0 % a.block_size);
+    }
     auto issue_tile = [&](int jt, unsigned char* dK, unsigned char* dV) __attribute__((always_inline)) {
         if constexpr (PAGED) {
             const int bs = a.block_size;
@@ -185,11 +195,27 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2))) v
                 int64_t rows = c1 - t;
                 rows = rows < 0 ? 0 : (rows > RPI ? RPI : rows);
                 const int nrec = (int)(rows * row_bytes);
-                const int64_t lb = t / bs - cb;
-                const int32_t id = __builtin_amdgcn_readfirstlane(s_blk[lb < kPagedTableLds - 1 ? lb : kPagedTableLds - 1]);
-                const int64_t off = ((int64_t)id * a.kv_stride_blk + (t % bs) * a.kv_stride_s) * 2;
+                const int lb = cur_blk < kPagedTableLds - 1 ? cur_blk : kPagedTableLds - 1;
+                const int32_t id = __builtin_amdgcn_readfirstlane(s_blk[lb]);
+                const int64_t off = ((int64_t)id * a.kv_stride_blk + (int64_t)cur_row * a.kv_stride_s) * 2;
                 lds_dma16(kbase + off, nrec, (lds_void*)(dK + I * 1024), voff[w]);
                 lds_dma16(vbase + off, nrec, (lds_void*)(dV + I * 1024), voff[w]);
+                // Next wave load: RPI rows on (RPI <= 8 < 16 <= bs: at most one
+                // block boundary).
+                cur_row += RPI;
+                if (cur_row >= bs) {
+                    cur_row -= bs;
+                    ++cur_blk;
+                }
+            }
+            // Two waves: the other wave's 32 rows of the tile lie between this
+            // wave's loads of consecutive tiles.
+            if constexpr (NWV == 2) {
+                cur_row += 32;
+                while (cur_row >= bs) {
+                    cur_row -= bs;
+                    ++cur_blk;
+                }
             }
         } else {
             int64_t rows = nkeys - (int64_t)jt * BN;

@@ -261,6 +261,8 @@ int64_t chunk_cap(const fa_params* p, const Shape& s) {
 // workgroups keep more loads in flight per CU) and two waves otherwise.
 constexpr int64_t kShortChunk = 512;
 int mfma_waves(int64_t chunk) { return chunk <= kShortChunk ? 1 : 2; }
+// A one-wave workgroup keeps a paged chunk's block ids in a register.
+static_assert(kShortChunk / 16 + 2 <= fa::kLaneBlocks, "one-wave paged chunks outgrow the block-id register");
 
 void plan_splits(const fa_params* p, const Shape& s, int num_cus, int64_t* splits, int64_t* chunk, int waves = 2) {
     const int gh = heads_per_workgroup(s.g);
@@ -311,7 +313,8 @@ bool balanced_plan(const fa_params* p, const Shape& s, int waves, DecodePlan* d)
     // A paged piece's block ids are staged on chip: bound the largest
     // piece (every batch at full length) by the table.
     const int64_t tmax = (s.KVN * s.B * by_len + nwg - 1) / nwg;
-    if (paged && tmax * 64 / p->block_size + 2 > fa::kPagedTableLds) return false;
+    const int64_t table = waves == 1 ? fa::kLaneBlocks : fa::kPagedTableLds;
+    if (paged && tmax * 64 / p->block_size + 2 > table) return false;
     d->bal_nwg = (int32_t)nwg;
     d->splits = by_len < by_wg ? by_len : by_wg;
     d->chunk = 64;

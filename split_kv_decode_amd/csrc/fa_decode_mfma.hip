@@ -155,19 +155,24 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2))) v
     // consecutive rows, and block sizes are multiples of 16, so its rows lie in
     // one block: each wave load takes its own block base.  (Past the chunk's
     // end a load reads nothing -- its byte range is 0 -- whatever block it names.)
-    __shared__ int32_t s_blk[PAGED ? kPagedTableLds : 1];
+    // Two waves stage the ids in LDS; one wave keeps them in a register, lane
+    // i holding block i (its chunks span at most kLaneBlocks blocks, which the
+    // host plan guarantees), so its LDS stays at the two tile buffers.
+    __shared__ int32_t s_blk[(PAGED && NWV == 2) ? kPagedTableLds : 1];
+    int32_t lane_blk = 0;
     int64_t cb = 0;
     if constexpr (PAGED) {
         const int bs = a.block_size;
         cb = c0 / bs;
         const int64_t nblk = (c1 - 1) / bs - cb + 1;
         const int32_t* tb = a.block_table + b * a.max_blocks + cb;
-        for (int64_t i = tid; i < nblk && i < kPagedTableLds; i += NT) {
-            int32_t id = tb[i];
-            id = id < 0 ? 0 : (id >= a.num_blocks ? a.num_blocks - 1 : id);
-            s_blk[i] = id;
+        auto clamp_id = [&](int32_t id) { return id < 0 ? 0 : (id >= a.num_blocks ? a.num_blocks - 1 : id); };
+        if constexpr (NWV == 1) {
+            if (lane < nblk) lane_blk = clamp_id(tb[lane]);
+        } else {
+            for (int64_t i = tid; i < nblk && i < kPagedTableLds; i += NT) s_blk[i] = clamp_id(tb[i]);
+            __syncthreads();
         }
-        __syncthreads();
     }
     int voff[NIW];
 #pragma unroll
@@ -195,8 +200,13 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2))) v
                 int64_t rows = c1 - t;
                 rows = rows < 0 ? 0 : (rows > RPI ? RPI : rows);
                 const int nrec = (int)(rows * row_bytes);
-                const int lb = cur_blk < kPagedTableLds - 1 ? cur_blk : kPagedTableLds - 1;
-                const int32_t id = __builtin_amdgcn_readfirstlane(s_blk[lb]);
+                int32_t id;
+                if constexpr (NWV == 1) {
+                    id = __builtin_amdgcn_readlane(lane_blk, cur_blk < kLaneBlocks - 1 ? cur_blk : kLaneBlocks - 1);
+                } else {
+                    const int lb = cur_blk < kPagedTableLds - 1 ? cur_blk : kPagedTableLds - 1;
+                    id = __builtin_amdgcn_readfirstlane(s_blk[lb]);
+                }
                 const int64_t off = ((int64_t)id * a.kv_stride_blk + (int64_t)cur_row * a.kv_stride_s) * 2;
                 lds_dma16(kbase + off, nrec, (lds_void*)(dK + I * 1024), voff[w]);
                 lds_dma16(vbase + off, nrec, (lds_void*)(dV + I * 1024), voff[w]);

@@ -164,6 +164,9 @@ constexpr int kVarlenMaxBatch = 16383;
 // Block ids one paged stage-1 workgroup stages in LDS: a chunk may touch at most
 // this many blocks.
 constexpr int kPagedTableLds = 1024;
+// Block ids a one-wave matrix-core decode workgroup keeps in a register (one
+// per lane): its paged chunks may span at most this many blocks.
+constexpr int kLaneBlocks = 64;
 
 // Largest split count the fused stage-1 merge handles (its weights sit in LDS).
 constexpr int kFusedMaxSplits = 256;

@@ -699,7 +699,9 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     // fixed buffer.  The barrier between the two phases of a slot only keeps
     // the groups in step: no LDS data crosses it, so it carries no memory
     // fence (a fence would wait for the slot's tile loads there and expose
-    // their latency); the barrier at the slot's end orders the loads.
+    // their latency); the barrier at the slot's end orders the loads.  The
+    // wave in its product phase runs at raised priority, so the arbiter
+    // favours its instructions over the softmax wave's on the shared SIMD.
     if (nt > 0) issue(kbase, jt0, sK0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -715,15 +717,19 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
             const bool live_prev = j >= 1;
             const bool live_cur = j < nt;
             if constexpr (G == 0) {
+                __builtin_amdgcn_s_setprio(3);
                 if (live_prev) pv(Vp);
                 if (live_cur) qk(Kc);
+                __builtin_amdgcn_s_setprio(0);
                 __builtin_amdgcn_s_barrier();
                 if (live_cur) softmax(jt0 + j);
             } else {
                 if (live_prev) softmax(jt0 + j - 1);
                 __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_s_setprio(3);
                 if (live_prev) pv(Vp);
                 if (live_cur) qk(Kc);
+                __builtin_amdgcn_s_setprio(0);
             }
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();

@@ -378,12 +378,17 @@ def test_paged_decode_never_reads_unused_table_entries():
         assert torch.equal(out, base) and torch.equal(torch.isinf(lse), torch.isinf(base_lse))
 
 
-@pytest.mark.parametrize("bs,chunk,splits", [(48, 64, 19), (16, 16256, 2), (64, 320, 63)])
-def test_paged_stage1_partials(bs, chunk, splits):
+@pytest.mark.parametrize("bs,chunk,splits,qn", [
+    (48, 64, 19, 4), (16, 16256, 2, 4), (64, 320, 63, 4),
+    # grouped heads (g = 4) on the matrix cores: the longest one-wave chunk over
+    # 16-token blocks (32 block ids in the per-lane register table), a one-wave
+    # chunk that cuts 48-token blocks, a two-wave chunk, and short chunks
+    (16, 512, 2, 8), (48, 512, 2, 8), (16, 576, 2, 8), (48, 64, 19, 8)])
+def test_paged_stage1_partials(bs, chunk, splits, qn):
     """Chunks that cut blocks (48 vs 64), a chunk whose 1016 block ids fill the LDS
     table, and a chunk that is a multiple of the block size."""
     KVS = 20000 if chunk == 16256 else 900
-    inp = fa_synth.make(spec(layout="BSND", B=2, QN=4, KVN=2, KVS=KVS,
+    inp = fa_synth.make(spec(layout="BSND", B=2, QN=qn, KVN=2, KVS=KVS,
                              lens=(KVS // 2, KVS), seed=73))
     if splits * chunk < KVS:
         splits = -(-KVS // chunk)
@@ -411,6 +416,10 @@ def test_paged_stage1_partials(bs, chunk, splits):
     assert np.abs(gm[live] - rm[live]).max() <= 1e-3
     assert np.all(np.abs(gl[live] - rl[live]) <= 2e-3 * rl[live])
     tol = 2e-3 * np.abs(ro).max(axis=2, keepdims=True) + 1e-6
+    if qn // 2 >= 4:  # matrix-core stage 1: P rounded to 16 bits (bound as in the contiguous test)
+        ro_abs, _, _ = oracle.split_partials(prob, inp.q, kp, np.ascontiguousarray(vp) & np.uint16(0x7FFF),
+                                             splits, chunk)
+        tol = tol + 2.0 ** -8 * ro_abs
     assert np.all((np.abs(go - ro) <= tol)[live])
 
 

@@ -868,3 +868,53 @@ def test_workload_prefill_4k_sampled():
 
 def test_workload_prefill_gqa_long_sampled():
     sampled_check("prefill_gqa_long", n=2000)
+
+
+# ------------------------------------------------------------------ seeded shape sweep
+
+def _sweep_case(seed):
+    """A seeded draw over the parameter space the fixed cases sample by hand:
+    decode (contiguous or paged) or prefill, layout, head dim, dtype, GQA group,
+    lengths, mask, scale sign; sized so the oracle stays fast."""
+    r = np.random.default_rng(1000 + seed)
+    D = int(r.choice([64, 128, 128, 256]))
+    KVN = int(r.choice([1, 2, 4, 8]))
+    g = int(r.choice([1, 2, 3, 4, 6, 8, 16, 32]))
+    while g * KVN > 64:
+        g //= 2
+    c = dict(layout=str(r.choice(["BNSD", "BSND"])), B=int(r.integers(1, 5)), QN=g * KVN, KVN=KVN,
+             D=D, dtype=str(r.choice(["bf16", "f16"])), seed=seed)
+    if r.random() < 0.3:
+        c["scale"] = float(-r.uniform(0.03, 0.12))
+    decode = r.random() < 0.5
+    if decode:
+        c.update(QS=1, KVS=int(r.integers(1, 6000)))
+    else:
+        c.update(QS=int(r.integers(1, 400)), KVS=int(r.integers(1, 700)),
+                 mask=str(r.choice(["none", "causal"])))
+    if r.random() < 0.6:
+        lo = int(r.integers(0, c["KVS"] + 1))
+        c["lens"] = (lo, int(r.integers(lo, c["KVS"] + 1)))
+    paged = None
+    if decode and "lens" in c and r.random() < 0.5:
+        paged = (str(r.choice(["PA_BBND", "PA_BNBD"])), 16 * int(r.integers(1, 9)))
+    return c, paged
+
+
+@pytest.mark.parametrize("seed", range(64))
+def test_seeded_shape_sweep(seed):
+    case, paged = _sweep_case(seed)
+    inp = fa_synth.make(spec(**case))
+    if paged is None:
+        full_check(inp, what=f"sweep {seed}: {case}")
+        return
+    kv_layout, bs = paged
+    s = inp.spec
+    out, lse, table = run_paged(inp, kv_layout, bs, seed=seed)
+    kp, vp, _, _ = fa_synth.to_paged(inp, bs, kv_layout, seed=seed)
+    prob = oracle.Problem(s.B, s.QN, s.KVN, 1, s.KVS, s.D, s.layout, s.dtype, s.softmax_scale,
+                          inp.lens, "none", kv_layout=kv_layout, block_table=table, block_size=bs)
+    ref, ref_lse = oracle.attention(prob, inp.q, kp, vp)
+    r_rows = np.ascontiguousarray(ref if s.layout == "BNSD" else ref.transpose(0, 2, 1, 3))
+    check(rows_of(out, s, np.arange(s.B * s.QN)), to_np(lse).reshape(-1),
+          r_rows.reshape(-1, s.D), ref_lse.reshape(-1), f"sweep {seed} paged {paged}: {case}")

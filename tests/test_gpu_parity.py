@@ -874,8 +874,9 @@ def test_workload_prefill_gqa_long_sampled():
 
 def _sweep_case(seed):
     """A seeded draw over the parameter space the fixed cases sample by hand:
-    decode (contiguous or paged) or prefill, layout, head dim, dtype, GQA group,
-    lengths, mask, scale sign; sized so the oracle stays fast."""
+    decode (contiguous or paged) or prefill (no mask, causal, or the causal
+    pattern as a boolean tensor), layout, head dim, dtype, GQA group, lengths,
+    scale sign; sized so the oracle stays fast."""
     r = np.random.default_rng(1000 + seed)
     D = int(r.choice([64, 128, 128, 256]))
     KVN = int(r.choice([1, 2, 4, 8]))
@@ -891,7 +892,7 @@ def _sweep_case(seed):
         c.update(QS=1, KVS=int(r.integers(1, 6000)))
     else:
         c.update(QS=int(r.integers(1, 400)), KVS=int(r.integers(1, 700)),
-                 mask=str(r.choice(["none", "causal"])))
+                 mask=str(r.choice(["none", "causal", "bool_causal"])))
     if r.random() < 0.6:
         lo = int(r.integers(0, c["KVS"] + 1))
         c["lens"] = (lo, int(r.integers(lo, c["KVS"] + 1)))

@@ -346,18 +346,25 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[tt][r] = 0.f;
+        // K fragments read PF steps ahead of their products (a ring of
+        // PF + 1 register pairs), the order pinned with scheduling barriers.
+        constexpr int PF = (D == 256) ? 1 : 2;
+        auto kread = [&](int kk, V8* dst) __attribute__((always_inline)) {
+            dst[0] = __builtin_bit_cast(
+                V8, *reinterpret_cast<const u32x4*>(Kb + krow0 * RB + (((2 * kk + half) ^ ks0) << 4)));
+            dst[1] = __builtin_bit_cast(
+                V8, *reinterpret_cast<const u32x4*>(Kb + krow1 * RB + (((2 * kk + half) ^ ks1) << 4)));
+        };
+        V8 kring[PF + 1][2];
+#pragma unroll
+        for (int p = 0; p < PF; ++p) kread(p, kring[p]);
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-            const V8 ka0 = __builtin_bit_cast(
-                V8, *reinterpret_cast<const u32x4*>(Kb + krow0 * RB + (((2 * kk + half) ^ ks0) << 4)));
-            const V8 ka1 = __builtin_bit_cast(
-                V8, *reinterpret_cast<const u32x4*>(Kb + krow1 * RB + (((2 * kk + half) ^ ks1) << 4)));
-            s[0] = M::mm(ka0, qreg[kk], s[0]);
-            s[1] = M::mm(ka1, qreg[kk], s[1]);
-            // D = 256: keep the scheduler from hoisting all 32 K reads ahead
-            // of the MFMAs (register pressure at one wave per SIMD).
-            if constexpr (D == 256)
-                if ((kk & 3) == 3) asm volatile("" ::: "memory");
+            if (kk + PF < D / 16) kread(kk + PF, kring[(kk + PF) % (PF + 1)]);
+            __builtin_amdgcn_sched_barrier(0);
+            s[0] = M::mm(kring[kk % (PF + 1)][0], qreg[kk], s[0]);
+            s[1] = M::mm(kring[kk % (PF + 1)][1], qreg[kk], s[1]);
+            __builtin_amdgcn_sched_barrier(0);
         }
 
         // Masking is needed only on tiles that cross the length, the causal
@@ -618,14 +625,25 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[tt][r] = 0.f;
+        // K fragments read two steps ahead of their products, as in the
+        // tiled kernel.
+        constexpr int PF = 2;
+        auto kread = [&](int kk, V8* dst) __attribute__((always_inline)) {
+            dst[0] = __builtin_bit_cast(
+                V8, *reinterpret_cast<const u32x4*>(Kb + krow0 * RB + (((2 * kk + half) ^ ks0) << 4)));
+            dst[1] = __builtin_bit_cast(
+                V8, *reinterpret_cast<const u32x4*>(Kb + krow1 * RB + (((2 * kk + half) ^ ks1) << 4)));
+        };
+        V8 kring[PF + 1][2];
+#pragma unroll
+        for (int p = 0; p < PF; ++p) kread(p, kring[p]);
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-            const V8 ka0 = __builtin_bit_cast(
-                V8, *reinterpret_cast<const u32x4*>(Kb + krow0 * RB + (((2 * kk + half) ^ ks0) << 4)));
-            const V8 ka1 = __builtin_bit_cast(
-                V8, *reinterpret_cast<const u32x4*>(Kb + krow1 * RB + (((2 * kk + half) ^ ks1) << 4)));
-            s[0] = M::mm(ka0, qreg[kk], s[0]);
-            s[1] = M::mm(ka1, qreg[kk], s[1]);
+            if (kk + PF < D / 16) kread(kk + PF, kring[(kk + PF) % (PF + 1)]);
+            __builtin_amdgcn_sched_barrier(0);
+            s[0] = M::mm(kring[kk % (PF + 1)][0], qreg[kk], s[0]);
+            s[1] = M::mm(kring[kk % (PF + 1)][1], qreg[kk], s[1]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
     auto pv = [&](const unsigned char* Vb) __attribute__((always_inline)) {

@@ -38,15 +38,22 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, published
 METRIC = "prefill attn TFLOP/s (%MFMA peak); decode KV GB/s (%HBM peak) on 1 MI355X"
 
 
+# Headers every kernel source includes: a change to them changes the kernels too.
+SHARED_HEADERS = ("fa_device.h", "fa_kernels.h", "fa_mfma.h")
+
+
 def sha256_of(path):
+    """Digest of a kernel source together with the shared device headers beside it."""
     h = hashlib.sha256()
-    with open(path, "rb") as f:
-        h.update(f.read())
+    for p in (path,) + tuple(os.path.join(os.path.dirname(path), n) for n in SHARED_HEADERS):
+        with open(p, "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
 
 
 def stored_traffic(kernel_src: str, name: str):
-    """HBM bytes per launch from a committed counter summary, if it was taken on this source."""
+    """HBM bytes per launch from a committed counter summary, if it was taken on this source
+    (the kernel file and the shared headers)."""
     path = os.path.join(ROOT, "profiles", f"{name}_traffic.txt")
     if not os.path.exists(path):
         return None

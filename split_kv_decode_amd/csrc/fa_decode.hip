@@ -156,8 +156,8 @@ __global__ __launch_bounds__(256) void decode_stage1_kernel(DecodeArgs a) {
                     vw[u] = buf_ld128(rv, voff);
                 } else if (t < c1) {
                     const int64_t off = (int64_t)s_blk[pb[u]] * a.kv_stride_blk + (int64_t)pr[u] * ss;
-                    kw[u] = ld128(kb + off);
-                    vw[u] = ld128(vb + off);
+                    kw[u] = ld128_stream(kb + off);
+                    vw[u] = ld128_stream(vb + off);
                 } else {
                     kw[u] = u32x4{0u, 0u, 0u, 0u};
                     vw[u] = u32x4{0u, 0u, 0u, 0u};

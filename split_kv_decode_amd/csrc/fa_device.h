@@ -135,6 +135,10 @@ __device__ __forceinline__ int64_t uni64(int64_t x) {
 
 // 16-byte global load / store helpers.
 __device__ __forceinline__ u32x4 ld128(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+// The same load with the non-temporal hint, for data streamed once (kStreamAux).
+__device__ __forceinline__ u32x4 ld128_stream(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 
 // x from lane (lane ^ 32): v_permlane32_swap exchanges the upper half-wave of
 // its first operand with the lower half-wave of its second, without LDS.

@@ -359,6 +359,10 @@ def extra_workloads(fa, fa_synth, np, torch, dev16, stream, warmup=3, iters=20):
             tf = fl / (ms * 1e-3) / 1e12
             res[key] = {"ms": round(ms, 5), "tflops": round(tf, 2),
                         "frac_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "flop": fl, "doc": s.doc}
+            if mode is not None:  # the spec's own mask is replaced by the mode timed here
+                res[key]["mask_timed"] = {"bool": "boolean mask tensor (upper-triangular)",
+                                          "causal": "causal flag, no mask tensor",
+                                          "window": f"sliding window ({window[0]}, {window[1]})"}[mode]
         del q, k, v, out, lse, ws, mask, inp, block_table
         torch.cuda.empty_cache()
     res.update(packed_workload(fa, fa_synth, np, torch, dev16, stream, warmup, iters))

@@ -86,7 +86,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the attention path runs on one GPU; --gpus must be 1 (sharding across GPUs is not implemented)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 

@@ -112,10 +112,20 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
         lse_step = a.num_heads;
     } else {
         const int64_t total = (int64_t)gridDim.x;
-        const int64_t work = xcd_remap(blockIdx.x, total);
-        qt = (int)(work % a.q_tiles);
-        const int64_t bh = work / a.q_tiles;
-        if (MASK == 1 || MASK == 3) qt = a.q_tiles - 1 - qt;  // longest causal tiles first
+        int64_t bh;
+        if (MASK == 1 || MASK == 3) {
+            // Causal costs grow with the query tile: dispatch every head's
+            // tile of one rank before the next lighter rank (longest first
+            // over the whole grid, so no heavy tile starts near the end); the
+            // heads of a rank keep their XCD, as in the order below.
+            const int64_t heads = total / a.q_tiles;
+            qt = a.q_tiles - 1 - (int)(blockIdx.x / heads);
+            bh = xcd_remap(blockIdx.x % heads, heads);
+        } else {
+            const int64_t work = xcd_remap(blockIdx.x, total);
+            qt = (int)(work % a.q_tiles);
+            bh = work / a.q_tiles;
+        }
         n1 = (int)(bh % a.num_heads);
         b = bh / a.num_heads;
         L = a.kv_seq;

@@ -113,11 +113,13 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
     } else {
         const int64_t total = (int64_t)gridDim.x;
         int64_t bh;
-        if (MASK == 1 || MASK == 3) {
-            // Causal costs grow with the query tile: dispatch every head's
-            // tile of one rank before the next lighter rank (longest first
-            // over the whole grid, so no heavy tile starts near the end); the
-            // heads of a rank keep their XCD, as in the order below.
+        if (MASK == 1 || MASK == 3 || (MASK == 4 && a.win_left >= a.win_right)) {
+            // Causal costs grow with the query tile, and so do those of a
+            // window that reaches further back than forward (its first tiles
+            // are cut at key 0): dispatch every head's tile of one rank before
+            // the next lighter rank (longest first over the whole grid, so no
+            // heavy tile starts near the end); the heads of a rank keep their
+            // XCD, as in the order below.
             const int64_t heads = total / a.q_tiles;
             qt = a.q_tiles - 1 - (int)(blockIdx.x / heads);
             bh = xcd_remap(blockIdx.x % heads, heads);

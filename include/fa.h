@@ -252,6 +252,23 @@ fa_status fa_combine(const fa_params *p, int64_t num_splits, const float *o_part
                      const float *m_part, const float *l_part, void *out, float *lse,
                      void *stream);
 
+/* fa_fwd_noalloc -- fa_fwd for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments and results as fa_fwd without the workspace:
+ * the paths that need one (split-KV partials, the packed-layout work list,
+ * the boolean-mask summary) use a scratch array of 16 MiB that the library
+ * holds on each GPU from the time the library is loaded until the process
+ * ends.  The call itself allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); on its first call on a device it looks up
+ * that device's scratch address (hipGetSymbolAddress, with the device
+ * current) and keeps it.  A call whose fa_workspace_size exceeds 16 MiB
+ * returns FA_ERR_PARAM_INVALID and launches nothing.  The scratch needs no
+ * initialisation, but every call on one GPU shares it: calls that may
+ * overlap on one device (several streams or threads) race and must be
+ * serialised by the caller. */
+fa_status fa_fwd_noalloc(const fa_params *p, const void *q, const void *k, const void *v,
+                         void *out, float *lse, void *stream);
+
 /* Text of the last non-OK status returned on the calling thread ("" if none). */
 const char *fa_last_error(void);
 

@@ -2,8 +2,8 @@
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels of ``libfa_mi355x.so``.  The low-level functions carry the C names
-(``fa_fwd``, ``fa_workspace_size``, ``fa_splitkv_plan``, ``fa_decode_splitkv``,
-``fa_decode_fused``, ``fa_combine``, ``fa_last_error``) and take device pointers as ints or torch
+(``fa_fwd``, ``fa_fwd_noalloc``, ``fa_workspace_size``, ``fa_splitkv_plan``,
+``fa_decode_splitkv``, ``fa_decode_fused``, ``fa_combine``, ``fa_last_error``) and take device pointers as ints or torch
 tensors; ``fwd`` is a convenience wrapper that allocates the outputs and the
 workspace with torch on the current stream.  There is no CPU fallback: if the
 shared library is missing, loading fails with an error.
@@ -28,8 +28,8 @@ MASK_MODES = {"none": FA_MASK_NONE, "causal": FA_MASK_CAUSAL, "bool": FA_MASK_BO
 FA_KV_CONTIGUOUS, FA_KV_PAGED_BBND, FA_KV_PAGED_BNBD = 0, 1, 2
 KV_LAYOUTS = {"contiguous": FA_KV_CONTIGUOUS, "PA_BBND": FA_KV_PAGED_BBND, "PA_BNBD": FA_KV_PAGED_BNBD}
 
-EXPORTS = ("fa_workspace_size", "fa_fwd", "fa_splitkv_plan", "fa_decode_splitkv", "fa_decode_fused",
-           "fa_combine", "fa_last_error")
+EXPORTS = ("fa_workspace_size", "fa_fwd", "fa_fwd_noalloc", "fa_splitkv_plan", "fa_decode_splitkv",
+           "fa_decode_fused", "fa_combine", "fa_last_error")
 
 
 class FaError(RuntimeError):
@@ -70,12 +70,13 @@ def load(path: Optional[str] = None):
             vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
             lib.fa_workspace_size.argtypes = [P(FaParams), P(sz)]
             lib.fa_fwd.argtypes = [P(FaParams), vp, vp, vp, vp, vp, vp, sz, vp]
+            lib.fa_fwd_noalloc.argtypes = [P(FaParams), vp, vp, vp, vp, vp, vp]
             lib.fa_splitkv_plan.argtypes = [P(FaParams), ctypes.c_int, i64, P(i64), P(i64), P(sz)]
             lib.fa_decode_splitkv.argtypes = [P(FaParams), i64, i64, vp, vp, vp, vp, vp, vp, vp]
             lib.fa_combine.argtypes = [P(FaParams), i64, vp, vp, vp, vp, vp, vp]
             lib.fa_decode_fused.argtypes = [P(FaParams), i64, i64, vp, vp, vp, vp, sz, vp, vp, vp]
-            for f in (lib.fa_workspace_size, lib.fa_fwd, lib.fa_splitkv_plan, lib.fa_decode_splitkv,
-                      lib.fa_combine, lib.fa_decode_fused):
+            for f in (lib.fa_workspace_size, lib.fa_fwd, lib.fa_fwd_noalloc, lib.fa_splitkv_plan,
+                      lib.fa_decode_splitkv, lib.fa_combine, lib.fa_decode_fused):
                 f.restype = ctypes.c_int
             lib.fa_last_error.argtypes = []
             lib.fa_last_error.restype = ctypes.c_char_p
@@ -142,6 +143,11 @@ def fa_workspace_size(params: FaParams) -> int:
 def fa_fwd(params: FaParams, q, k, v, out, lse=None, workspace=None, workspace_bytes=0, stream=None):
     _check(load().fa_fwd(ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                          _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def fa_fwd_noalloc(params: FaParams, q, k, v, out, lse=None, stream=None):
+    _check(load().fa_fwd_noalloc(ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                 _stream(stream)))
 
 
 def fa_splitkv_plan(params: FaParams, num_cus: int = 0, chunk_hint: int = 0):

@@ -15,6 +15,10 @@
 #include "fa.h"
 #include "fa_kernels.h"
 
+// Scratch memory of fa_fwd_noalloc (16 MiB per GPU; see scratch_address).
+constexpr size_t kNoallocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -568,6 +572,27 @@ fa_status run_prefill(const fa_params* p, const Shape& s, const void* q, const v
     return launch_result(fa::launch_prefill(a, p->dtype == FA_BF16 ? 1 : 0, (int)s.D, mm, s.B, stream), "prefill");
 }
 
+// Scratch of fa_fwd_noalloc: device memory the library holds itself, so that
+// callers that cannot allocate (code under HIP graph capture, serving loops,
+// harnesses that forbid it) still run the paths that need a workspace.  One
+// copy per GPU, resident from the module's load until the process ends.  In
+// host code `scratch` only names the symbol: its device address comes from
+// hipGetSymbolAddress, asked once per device with that device current.
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of this device's scratch, or nullptr (with the error set).
+void* scratch_address(int dev) {
+    void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (ptr) return ptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+        fail(FA_ERR_RUNTIME, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+        return nullptr;
+    }
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    return ptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -739,6 +764,26 @@ fa_status fa_combine(const fa_params* p, int64_t num_splits, const float* o_part
     if (lse && !aligned(lse, 4)) return fail(FA_ERR_PARAM_INVALID, "lse must be 4-byte aligned");
     if (num_splits < 1 || num_splits > kMaxSplits) return fail(FA_ERR_PARAM_INVALID, "num_splits must be in [1, 2^20]");
     return run_combine(p, s, num_splits, o_part, m_part, l_part, out, lse, static_cast<hipStream_t>(stream));
+}
+
+fa_status fa_fwd_noalloc(const fa_params* p, const void* q, const void* k, const void* v, void* out, float* lse,
+                         void* stream) {
+    size_t need = 0;
+    fa_status st = fa_workspace_size(p, &need);
+    if (st != FA_OK) return st;
+    if (need > kNoallocScratchBytes)
+        return fail(FA_ERR_PARAM_INVALID,
+                    "fa_fwd_noalloc: this call needs %zu bytes of scratch, the library holds %zu; use fa_fwd with a "
+                    "workspace",
+                    need, kNoallocScratchBytes);
+    void* ws = nullptr;
+    if (need > 0) {
+        const int dev = current_device();
+        if (dev < 0) return fail(FA_ERR_RUNTIME, "fa_fwd_noalloc: no current HIP device");
+        ws = scratch_address(dev);
+        if (!ws) return FA_ERR_RUNTIME;
+    }
+    return fa_fwd(p, q, k, v, out, lse, ws, ws ? kNoallocScratchBytes : 0, stream);
 }
 
 }  // extern "C"

@@ -268,3 +268,18 @@ def test_fused_decode_validates(lib):
     pq = params(q_seq=4)
     st = lib.fa_decode_fused(ctypes.byref(pq), 32, 4096, FAKE, FAKE, FAKE, FAKE, 1 << 30, FAKE, None, None)
     assert st == fa.FA_ERR_PARAM_INVALID
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch(lib):
+    # the work list of a packed batch of 2^29 query tokens needs far more than the
+    # 16 MiB of scratch fa_fwd_noalloc holds: rejected before any launch (the
+    # pointers are fake and never read)
+    p = params(batch=4, num_heads=2, q_seq=1 << 29, kv_seq=1 << 29, head_dim=64, layout="TND",
+               cu_seqlens_q=FAKE, cu_seqlens_kv=FAKE)
+    assert fa.fa_workspace_size(p) > (16 << 20)
+    st = lib.fa_fwd_noalloc(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None)
+    assert st == fa.FA_ERR_PARAM_INVALID
+    assert "scratch" in fa.fa_last_error()
+    # validation errors come first, as for fa_fwd
+    bad = params(head_dim=100)
+    assert lib.fa_fwd_noalloc(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, None, None) == fa.FA_ERR_PARAM_INVALID

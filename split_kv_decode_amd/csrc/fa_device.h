@@ -211,6 +211,20 @@ __device__ __forceinline__ void lds_dma16_unordered(dma_rsrc r, lds_void* dst, i
                  : "s"(m), "v"(voff), "s"(r)
                  : "memory", "m0");
 }
+// The same load with M0 given as a wave-uniform LDS byte address computed
+// beforehand (see lds_address), so a loop issuing tile loads spends only the
+// M0 write on it.
+__device__ __forceinline__ void lds_dma16_m0(dma_rsrc r, uint32_t m0, int voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(r)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
+
+// LDS byte address of a __shared__ object, as a wave-uniform value.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)p);
+}
 
 }  // namespace fa

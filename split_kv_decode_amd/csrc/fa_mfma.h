@@ -26,6 +26,19 @@ struct Mfma<F16> {
     }
 };
 
+// Two fp32 values -> one word of the 16-bit type (element 0 in the low
+// half), rounded to nearest even, built as a two-element vector so the
+// compiler emits one packed conversion where the target has it.
+template <typename ST>
+__device__ __forceinline__ uint32_t cvt_pair(float a, float b) {
+    using E = typename Mfma<ST>::E;
+    typedef E E2 __attribute__((ext_vector_type(2)));
+    E2 v;
+    v[0] = (E)a;
+    v[1] = (E)b;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
 // Logical work index for a launch slot.  Consecutive slots are dealt round
 // robin to the 8 XCDs (each with its own L2); this remap gives every XCD a
 // contiguous range of logical tiles, so the query tiles that read the same

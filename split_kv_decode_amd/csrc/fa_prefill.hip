@@ -514,31 +514,43 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
     }
 }
 
-// Ping-pong prefill, used for the mask-free D = 128 case (measured 7 % faster
-// than prefill_kernel there; with masks, or at D = 64, it was slower): one
-// workgroup of 8 waves per CU, 256 query rows (32 per wave), each K/V tile
-// staged once for all 8 waves.  Waves 0-3 and 4-7 alternate phases separated
-// by workgroup barriers: while one group issues its MFMAs (PV of the previous
-// tile, then QK of the current one) the other runs the softmax of its current
-// tile, each SIMD holding one wave of each group.  (Timing the phases alone
-// showed that the matrix and vector work still largely add up rather than
-// overlap on this chip; the 7 % is what the whole arrangement measured.)  Slot
-// j = {K(j), V(j-1)} is resident during phases 2j and 2j+1; slot j+1 is
-// fetched during those two phases into the buffers slot j-1 used.
+// Interleaved prefill, used for the mask-free D = 128 case: one workgroup of
+// 8 waves per CU, 256 query rows (32 per wave), each 64-key K/V tile loaded
+// into LDS once for all 8 waves.  Every wave runs the same software-pipelined
+// schedule and issues its own matrix and vector work interleaved.  Slot j
+// holds K(j) and V(j-1); a wave spends it in two stages:
+//   A: the 16 products of S(j) = K(j) Q^T, each pair preceded by two
+//      exponentials of the second half (keys 32..63) of tile j-1;
+//   B: the 16 products of O += V(j-1)^T P(j-1), each preceded by one
+//      exponential of the first half (keys 0..31) of tile j.
+// The two waves a SIMD holds then both feed its matrix core between their
+// vector instructions.  (A probe of schedules on gfx950 measured the matrix
+// core 93 % busy this way, against 82 % when one wave of a SIMD issues only
+// products and the other only vector work, which is how an earlier ping-pong
+// form of this kernel was arranged; this kernel measured 3-4 % faster than
+// it.)  Within each step the order -- LDS fragment reads, vector work,
+// products -- is pinned with scheduling barriers, so a read's latency passes
+// under the vector work.  Each half-tile checks its own exponential sum for
+// the lazy rescale (a half-row sum of at most 2^8 proves no exponential of
+// the half exceeded 2^8); the rare rescale takes the maximum over what is
+// needed and recomputes what was taken against the old maximum.  K(j+1) is
+// loaded at the start of slot j and V(j) after stage A, with every scalar of
+// the load worked out beforehand; one barrier per slot releases the buffers.
 template <typename ST, int D>
-__global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
     using M = Mfma<ST>;
     using V8 = typename M::V8;
     using E = typename M::E;
     constexpr int NWV = 8;              // waves
-    constexpr int BM = 32 * NWV;        // query rows per workgroup
     constexpr int BN = 64;              // keys per KV tile
     constexpr int RB = D * 2;
     constexpr int TB = BN * RB;
     constexpr int CPR = D / 8;
     constexpr int RPI = 64 / CPR;
     constexpr int NIW = TB / 1024 / NWV;  // wave loads per wave per tile (K, and again V)
+    constexpr int KS = D / 16;            // QK steps (two products each)
     static_assert(NIW >= 1, "tile too small for 8 waves");
+    static_assert(2 * KS == 16, "two exponentials of a half tile per QK step");
     constexpr float kPmax = 256.f;
     __shared__ __attribute__((aligned(1024))) unsigned char sK0[TB];
     __shared__ __attribute__((aligned(1024))) unsigned char sK1[TB];
@@ -548,13 +560,12 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int grp = wave >> 2;  // 0: MFMAs in even phases, 1: in odd phases
     const int half = lane >> 5;
     const int col = lane & 31;
 
     const int64_t total = (int64_t)gridDim.x;
     const int64_t work = xcd_remap(blockIdx.x, total);
-    int qt = (int)(work % a.q_tiles);
+    const int qt = (int)(work % a.q_tiles);
     const int64_t bh = work / a.q_tiles;
     const int n1 = (int)(bh % a.num_heads);
     const int64_t b = bh / a.num_heads;
@@ -568,17 +579,16 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     const int64_t lse_row0 = (b * a.num_heads + n1) * a.q_seq;
     const int n2 = n1 / a.group;
 
-    const int64_t i0 = (int64_t)qt * BM;
-    const int64_t wrow0 = i0 + 32 * wave;
-    const int64_t qrow = wrow0 + col;
+    const int64_t i0 = (int64_t)qt * (32 * NWV);
+    const int64_t qrow = i0 + 32 * wave + col;
     const bool qvalid = qrow < q_used;
 
-    V8 qreg[D / 16];
+    V8 qreg[KS];
     {
         const uint16_t* qp = a.q + q_off + (int64_t)n1 * a.q_stride_n + qrow * a.q_stride_s;
         const uint32_t flip = a.negate_q ? 0x80008000u : 0u;
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
+        for (int kk = 0; kk < KS; ++kk) {
             u32x4 w = u32x4{0u, 0u, 0u, 0u};
             if (qvalid) w = ld128(qp + kk * 16 + 8 * half);
             w ^= flip;
@@ -586,17 +596,15 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
         }
     }
     const float c = a.scale_log2;
-
-    const int nt = (int)((L + BN - 1) / BN);  // KV tiles this workgroup visits
-    constexpr int jt0 = 0;
+    const int nt = (int)((L + BN - 1) / BN);  // KV tiles
 
     f32x16 o[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-    float m_run = kNegInf;
-    float l_half = 0.f;
+    float m_run = kNegInf;  // reference max per query row (scaled base-2 units)
+    float l_half = 0.f;     // this half-wave's share of the row sum
 
     const int64_t row_bytes = a.kv_stride_s * 2;
     const char* kbase = reinterpret_cast<const char*>(a.k + kv_off + (int64_t)n2 * a.kv_stride_n);
@@ -607,19 +615,33 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
         const int r = RPI * (wave * NIW + w) + lane / CPR;
         voff[w] = (int)(r * row_bytes) + (((lane % CPR) ^ swz<D>(r)) << 4);
     }
-    auto tile_rec = [&](int jt) __attribute__((always_inline)) {
-        int64_t rows = L - (int64_t)jt * BN;
-        rows = rows < 0 ? 0 : (rows > BN ? BN : rows);
-        return (int)(rows * row_bytes);
-    };
-    auto issue = [&](const char* base, int jt, unsigned char* dst) __attribute__((always_inline)) {
-        const int nrec = tile_rec(jt);
-        const char* t = base + (int64_t)jt * BN * row_bytes;
-        const dma_rsrc r = make_dma_rsrc(t, nrec);
+    // Tile loads with their scalars worked out once: the K and V bases of
+    // this (b, n2), the bytes per row (a 64-row tile stays below 2^31 bytes,
+    // which the host checks), the key count in 32 bits and the LDS address of
+    // this wave's share of each buffer; a load then costs a few scalar
+    // instructions and the M0 write.
+    const uint64_t kb64 = (uint64_t)uni64((int64_t)(uintptr_t)kbase);
+    const uint64_t vb64 = (uint64_t)uni64((int64_t)(uintptr_t)vbase);
+    const int32_t rb32 = __builtin_amdgcn_readfirstlane((int32_t)row_bytes);
+    const int32_t L32 = __builtin_amdgcn_readfirstlane((int32_t)L);
+    const uint32_t wshare = (uint32_t)(wave * NIW * 1024);
+    const uint32_t mK0 = lds_address(sK0) + wshare, mK1 = lds_address(sK1) + wshare;
+    const uint32_t mV0 = lds_address(sV0) + wshare, mV1 = lds_address(sV1) + wshare;
+    // Bytes of a full tile, and of the last one (cut at the length).
+    const uint32_t full_bytes = (uint32_t)(BN * rb32);
+    const uint32_t last_bytes = (uint32_t)((L32 - (nt - 1) * BN) * rb32);
+    auto issue = [&](uint64_t base, int jt, uint32_t m0) __attribute__((always_inline)) {
+        const uint64_t t = base + (uint64_t)(uint32_t)jt * (uint64_t)full_bytes;
+        dma_rsrc r;
+        r[0] = (uint32_t)t;
+        r[1] = (uint32_t)(t >> 32) & 0xffffu;
+        r[2] = jt + 1 < nt ? full_bytes : last_bytes;
+        r[3] = 0x00020000u;
 #pragma unroll
-        for (int w = 0; w < NIW; ++w) lds_dma16_unordered(r, (lds_void*)(dst + (wave * NIW + w) * 1024), voff[w]);
+        for (int w = 0; w < NIW; ++w) lds_dma16_m0(r, m0 + (uint32_t)(w * 1024), voff[w]);
     };
 
+    // LDS read addressing, as in the other prefill kernels.
     const int krow0 = col, krow1 = 32 + col;
     const int ks0 = swz<D>(krow0), ks1 = swz<D>(krow1);
     const int trG = lane >> 4;
@@ -629,150 +651,247 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     const int vs_lo = swz<D>(vrow_lo), vs_hi = swz<D>(vrow_hi);
     const int vx = 2 * (trG & 1) + ((trL & 3) >> 1);
     const int vbyte = (trL & 1) * 8;
+    auto kread = [&](const unsigned char* Kb, int kk, V8* dst) __attribute__((always_inline)) {
+        dst[0] = __builtin_bit_cast(V8, *reinterpret_cast<const u32x4*>(Kb + krow0 * RB + (((2 * kk + half) ^ ks0) << 4)));
+        dst[1] = __builtin_bit_cast(V8, *reinterpret_cast<const u32x4*>(Kb + krow1 * RB + (((2 * kk + half) ^ ks1) << 4)));
+    };
+    // V^T operand of product (ks, dt): keys 16*ks + .., head-dim columns 32*dt + ..
+    auto vread = [&](const unsigned char* Vb, int i) __attribute__((always_inline)) -> V8 {
+        const int ks = i >> 2, dt = i & 3;
+        const int lc = 4 * dt + vx;
+        const unsigned char* vb = Vb + ks * 16 * RB;
+        const s16x4 lo = lds_read_tr(vb + vrow_lo * RB + ((lc ^ vs_lo) << 4) + vbyte);
+        const s16x4 hi = lds_read_tr(vb + vrow_hi * RB + ((lc ^ vs_hi) << 4) + vbyte);
+        return __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    const f32x16 zero16 = {};
 
-    f32x16 s[2];
-    V8 pb[4];
-    auto qk = [&](const unsigned char* Kb) __attribute__((always_inline)) {
+    // Stage A of a slot: S(j) into Sn (when QK), exponentials of the second
+    // half of tile j-1 (So[1]) into Pd[2..3] and their sum ps1 (when SM).
+    auto stage_a = [&](auto qk_t, auto sm_t, const unsigned char* Kb, f32x16* Sn, const f32x16* So, u32x4* Pd,
+                       float& ps1) __attribute__((always_inline)) {
+        constexpr bool QK = decltype(qk_t)::value;
+        constexpr bool SM = decltype(sm_t)::value;
+        const float nmx = (m_run == kNegInf) ? 0.f : -m_run;
+        constexpr int PF = 2;  // K fragments read two steps ahead
+        V8 kring[PF + 1][2];
+        if constexpr (QK) {
+#pragma unroll
+            for (int p = 0; p < PF; ++p) kread(Kb, p, kring[p]);
+        }
+        float acc = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            if constexpr (QK) {
+                if (kk + PF < KS) kread(Kb, kk + PF, kring[(kk + PF) % (PF + 1)]);
+            }
+            // each step in this order: fragment reads, vector work, products
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (SM) {
+                const int r = 2 * kk;
+                const float p0 = fast_exp2(__builtin_fmaf(So[1][r], c, nmx));
+                const float p1 = fast_exp2(__builtin_fmaf(So[1][r + 1], c, nmx));
+                acc += p0;
+                acc += p1;
+                uint32_t w = cvt_pair<ST>(p0, p1);
+                // keep the sum and the conversion in this step (the compiler
+                // would otherwise sink them past the products)
+                asm volatile("" : "+v"(acc), "+v"(w));
+                Pd[2 + (r >> 3)][(r & 7) >> 1] = w;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (QK) {
+                const V8* kf = kring[kk % (PF + 1)];
+                Sn[0] = M::mm(kf[0], qreg[kk], kk == 0 ? zero16 : Sn[0]);
+                Sn[1] = M::mm(kf[1], qreg[kk], kk == 0 ? zero16 : Sn[1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (SM) ps1 = acc;
+    };
+    // Stage B: O += V(j-1)^T P(j-1) (when PV, Po = P(j-1)), exponentials of
+    // the first half of tile j (Sn[0]) into Pn[0..1] and their sum ps0 (when SM).
+    auto stage_b = [&](auto pv_t, auto sm_t, const unsigned char* Vb, const u32x4* Po, const f32x16* Sn, u32x4* Pn,
+                       float& ps0) __attribute__((always_inline)) {
+        constexpr bool PV = decltype(pv_t)::value;
+        constexpr bool SM = decltype(sm_t)::value;
+        const float nmx = (m_run == kNegInf) ? 0.f : -m_run;
+        constexpr int VPF = 3;  // V operands read three products ahead
+        V8 vring[VPF + 1];
+        if constexpr (PV) {
+#pragma unroll
+            for (int p = 0; p < VPF; ++p) vring[p] = vread(Vb, p);
+        }
+        float acc = 0.f, pprev = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if constexpr (PV) {
+                if (i + VPF < 16) vring[(i + VPF) % (VPF + 1)] = vread(Vb, i + VPF);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (SM) {
+                const float p = fast_exp2(__builtin_fmaf(Sn[0][i], c, nmx));
+                acc += p;
+                if (i & 1) {
+                    uint32_t w = cvt_pair<ST>(pprev, p);
+                    asm volatile("" : "+v"(acc), "+v"(w));
+                    Pn[i >> 3][(i & 7) >> 1] = w;
+                } else {
+                    pprev = p;
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (PV) o[i & 3] = M::mm(vring[i % (VPF + 1)], __builtin_bit_cast(V8, Po[i >> 2]), o[i & 3]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (SM) ps0 = acc;
+    };
+    // Rare paths.  After stage B, the first half of tile j exceeded its bound
+    // (or the row has seen no key yet): the reference moves to the maximum of
+    // the whole tile, so its second half cannot exceed it later; O (which
+    // holds tile j-1 by then) and the row sum are rescaled, and the first
+    // half's exponentials are taken again.
+    auto rescale_b = [&](const f32x16* St, u32x4* Pt, float& ps0) __attribute__((always_inline)) {
+        float tmax = kNegInf;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[tt][r] = 0.f;
-        // K fragments read two steps ahead of their products, as in the
-        // tiled kernel.
-        constexpr int PF = 2;
-        auto kread = [&](int kk, V8* dst) __attribute__((always_inline)) {
-            dst[0] = __builtin_bit_cast(
-                V8, *reinterpret_cast<const u32x4*>(Kb + krow0 * RB + (((2 * kk + half) ^ ks0) << 4)));
-            dst[1] = __builtin_bit_cast(
-                V8, *reinterpret_cast<const u32x4*>(Kb + krow1 * RB + (((2 * kk + half) ^ ks1) << 4)));
-        };
-        V8 kring[PF + 1][2];
+            for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, St[tt][r]);
+        tmax = fmaxf(tmax, xor32(tmax)) * c;
+        const float mnew = fmaxf(m_run, tmax);
+        const float alpha = fast_exp2(m_run - ((mnew == kNegInf) ? 0.f : mnew));
 #pragma unroll
-        for (int p = 0; p < PF; ++p) kread(p, kring[p]);
+        for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-            if (kk + PF < D / 16) kread(kk + PF, kring[(kk + PF) % (PF + 1)]);
-            __builtin_amdgcn_sched_barrier(0);
-            s[0] = M::mm(kring[kk % (PF + 1)][0], qreg[kk], s[0]);
-            s[1] = M::mm(kring[kk % (PF + 1)][1], qreg[kk], s[1]);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+        l_half *= alpha;
+        m_run = mnew;
+        const float nmx = (m_run == kNegInf) ? 0.f : -m_run;
+        float s0 = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            const float p0 = fast_exp2(__builtin_fmaf(St[0][r], c, nmx));
+            const float p1 = fast_exp2(__builtin_fmaf(St[0][r + 1], c, nmx));
+            s0 += p0;
+            s0 += p1;
+            Pt[r >> 3][(r & 7) >> 1] = cvt_pair<ST>(p0, p1);
         }
+        ps0 = s0;
     };
-    auto pv = [&](const unsigned char* Vb) __attribute__((always_inline)) {
+    // After stage A, the second half of tile j-1 exceeded its bound (its
+    // first half passed, so its scores lie below the reference + 8): the
+    // reference moves to the second half's maximum, O (tiles before j-1) and
+    // the row sum are rescaled, the second half's exponentials are taken
+    // again and the first half's 16-bit values and sum are scaled by the same
+    // factor (at most one more rounding of those values, on this rare path).
+    auto rescale_a = [&](const f32x16* St, u32x4* Pt, float& ps0, float& ps1) __attribute__((always_inline)) {
+        float tmax = kNegInf;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, St[1][r]);
+        tmax = fmaxf(tmax, xor32(tmax)) * c;
+        const float mnew = fmaxf(m_run, tmax);
+        const float alpha = fast_exp2(m_run - mnew);  // m_run is finite here: the first half set it
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) {
-                const int lc = 4 * dt + vx;
-                const unsigned char* vb = Vb + ks * 16 * RB;
-                const s16x4 lo = lds_read_tr(vb + vrow_lo * RB + ((lc ^ vs_lo) << 4) + vbyte);
-                const s16x4 hi = lds_read_tr(vb + vrow_hi * RB + ((lc ^ vs_hi) << 4) + vbyte);
-                const V8 va = __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                o[dt] = M::mm(va, pb[ks], o[dt]);
-            }
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+        l_half *= alpha;
+        m_run = mnew;
+        const float nmx = -m_run;
+        float s1 = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            const float p0 = fast_exp2(__builtin_fmaf(St[1][r], c, nmx));
+            const float p1 = fast_exp2(__builtin_fmaf(St[1][r + 1], c, nmx));
+            s1 += p0;
+            s1 += p1;
+            Pt[2 + (r >> 3)][(r & 7) >> 1] = cvt_pair<ST>(p0, p1);
         }
-    };
-    auto softmax = [&](int jt) __attribute__((always_inline)) {
-        const int64_t j0 = (int64_t)jt * BN;
-        if (j0 + BN > L) {  // the tile crosses the length
+        ps1 = s1;
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int64_t tok = j0 + tt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                    s[tt][r] = tok < L ? s[tt][r] : kNegInf;
-                }
-            }
+        for (int wd = 0; wd < 8; ++wd) {
+            const uint32_t x = Pt[wd >> 2][wd & 3];
+            Pt[wd >> 2][wd & 3] = cvt_pair<ST>(lo_f32<ST>(x) * alpha, hi_f32<ST>(x) * alpha);
         }
-        float psum = 0.f;
-        auto exps = [&](float nmx) __attribute__((always_inline)) {
-            psum = 0.f;
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = fast_exp2(__builtin_fmaf(s[tt][r], c, nmx));
-                    psum += p;
-                    pb[tt * 2 + (r >> 3)][r & 7] = (E)p;
-                }
-            }
-        };
-        exps((m_run == kNegInf) ? 0.f : -m_run);
-        // Every p >= 0, so a half-row sum of at most kPmax proves no score
-        // exceeded the running max by more than 8: the tile max is needed
-        // only on the rare path that moves the max (or while a row of the
-        // query has seen no valid key yet, so an empty row keeps m = -inf;
-        // rows past the query length never trigger it).
-        if (__any(psum > kPmax || (m_run == kNegInf && qvalid))) {
-            float tmax = kNegInf;
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[tt][r]);
-            tmax = fmaxf(tmax, xor32(tmax)) * c;
-            const float mnew = fmaxf(m_run, tmax);
-            const float alpha = fast_exp2(m_run - ((mnew == kNegInf) ? 0.f : mnew));
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-            l_half *= alpha;
-            m_run = mnew;
-            exps((m_run == kNegInf) ? 0.f : -m_run);
-        }
-        l_half += psum;
+        ps0 *= alpha;
     };
 
-    // Phase 2j (even) and 2j+1 (odd) for slot j = {K(jt0+j), V(jt0+j-1)},
-    // j = 0 .. nt.  Buffers: K(t) in sK[t&1], V(t) in sV[t&1] (t relative to
-    // jt0).  The loop is unrolled by two slots so every LDS access names a
-    // fixed buffer.  The barrier between the two phases of a slot only keeps
-    // the groups in step: no LDS data crosses it, so it carries no memory
-    // fence (a fence would wait for the slot's tile loads there and expose
-    // their latency); the barrier at the slot's end orders the loads.  The
-    // wave in its product phase runs at raised priority, so the arbiter
-    // favours its instructions over the softmax wave's on the shared SIMD.
-    if (nt > 0) issue(kbase, jt0, sK0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    // Each group runs its own copy of the loop (G is a compile-time constant),
-    // so the two phase orders do not merge their register live ranges.
-    auto run = [&](auto gtag) __attribute__((always_inline)) {
-        constexpr int G = decltype(gtag)::value;
-        auto slot = [&](int j, const unsigned char* Kc, const unsigned char* Vp, unsigned char* Kn,
-                        unsigned char* Vn) __attribute__((always_inline)) {
-            // Kc = K(j), Vp = V(j-1); fetch K(j+1) into Kn and V(j) into Vn.
-            if (j + 1 < nt) issue(kbase, jt0 + j + 1, Kn);
-            if (j < nt) issue(vbase, jt0 + j, Vn);
-            const bool live_prev = j >= 1;
-            const bool live_cur = j < nt;
-            if constexpr (G == 0) {
-                __builtin_amdgcn_s_setprio(3);
-                if (live_prev) pv(Vp);
-                if (live_cur) qk(Kc);
-                __builtin_amdgcn_s_setprio(0);
-                __builtin_amdgcn_s_barrier();
-                if (live_cur) softmax(jt0 + j);
-            } else {
-                if (live_prev) softmax(jt0 + j - 1);
-                __builtin_amdgcn_s_barrier();
-                __builtin_amdgcn_s_setprio(3);
-                if (live_prev) pv(Vp);
-                if (live_cur) qk(Kc);
-                __builtin_amdgcn_s_setprio(0);
-            }
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
-        };
-        for (int j = 0; j <= nt; j += 2) {
-            slot(j, sK0, sV1, sK1, sV0);
-            if (j + 1 <= nt) slot(j + 1, sK1, sV0, sK0, sV1);
+    f32x16 SA[2], SB[2];
+    u32x4 PA[4], PB[4];
+    float ps0 = 0.f, ps1 = 0.f;
+    // Slot j (PAR = j & 1): K(j) in sK[PAR], V(j-1) in sV[PAR ^ 1]; tiles
+    // j+1 (K) and j (V) are fetched into the other buffers.  S(j) goes to
+    // SA for even j, SB for odd j; P(j) likewise to PA / PB.
+    auto slot = [&](auto par_t, auto first_t, auto last_t, int j) __attribute__((always_inline)) {
+        constexpr int PAR = decltype(par_t)::value;
+        constexpr bool FIRST = decltype(first_t)::value;  // j == 0: no tile j-1
+        constexpr bool LAST = decltype(last_t)::value;    // j == nt: no tile j
+        const unsigned char* Kc = PAR ? sK1 : sK0;
+        const unsigned char* Vp = PAR ? sV0 : sV1;
+        const uint32_t mKn = PAR ? mK0 : mK1;
+        const uint32_t mVn = PAR ? mV1 : mV0;
+        f32x16* Sn = PAR ? SB : SA;
+        f32x16* So = PAR ? SA : SB;
+        u32x4* Pn = PAR ? PB : PA;
+        u32x4* Po = PAR ? PA : PB;
+        // K(j+1) now and V(j) after stage A, into the buffers the previous
+        // slot released (issued together, the 8 waves' loads queue for the
+        // address unit at the slot's start)
+        if (j + 1 < nt) issue(kb64, j + 1, mKn);
+        stage_a(std::integral_constant<bool, !LAST>{}, std::integral_constant<bool, !FIRST>{}, Kc, Sn, So, Po, ps1);
+        if (j < nt) issue(vb64, j, mVn);
+        if constexpr (!FIRST) {
+            // second half of tile j-1 above its bound: rare rescale, then the
+            // row sum takes the whole tile
+            if (__any(ps1 > kPmax)) rescale_a(So, Po, ps0, ps1);
+            l_half += ps0 + ps1;
         }
+        if constexpr (!LAST) {
+            // the last tile crosses the length: its keys at or past it are excluded
+            const int32_t j0 = j * BN;
+            if (j0 + BN > L32) {
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int32_t tok = j0 + tt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                        Sn[tt][r] = tok < L32 ? Sn[tt][r] : kNegInf;
+                    }
+            }
+        }
+        stage_b(std::integral_constant<bool, !FIRST>{}, std::integral_constant<bool, !LAST>{}, Vp, Po, Sn, Pn, ps0);
+        if constexpr (!LAST) {
+            // first half of tile j above its bound, or a row that has seen no
+            // key yet: rare rescale against the whole tile's maximum
+            if (__any(ps0 > kPmax || (m_run == kNegInf && qvalid))) rescale_b(Sn, Pn, ps0);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of slot j+1 landed
+        __syncthreads();                                   // ... and everyone else's
     };
-    if (grp == 0)
-        run(std::integral_constant<int, 0>{});
-    else
-        run(std::integral_constant<int, 1>{});
+    using T0 = std::integral_constant<int, 0>;
+    using T1 = std::integral_constant<int, 1>;
+    using BT = std::true_type;
+    using BF = std::false_type;
+
+    if (nt > 0) {
+        issue(kb64, 0, mK0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        slot(T0{}, BT{}, BF{}, 0);
+        int j = 1;
+        for (; j + 1 < nt; j += 2) {
+            slot(T1{}, BF{}, BF{}, j);
+            slot(T0{}, BF{}, BF{}, j + 1);
+        }
+        if (j < nt) {
+            slot(T1{}, BF{}, BF{}, j);
+            ++j;
+        }
+        if (nt & 1)
+            slot(T1{}, BF{}, BT{}, nt);
+        else
+            slot(T0{}, BF{}, BT{}, nt);
+    }
 
     const float l_run = l_half + xor32(l_half);
     if (qvalid) {
@@ -797,7 +916,6 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     }
 }
 
-
 template <typename ST, int D>
 static hipError_t dispatch_prefill(const PrefillArgs& a, int mask_mode, int64_t blocks, hipStream_t s) {
     const dim3 grid((unsigned)blocks), block(256);
@@ -813,19 +931,19 @@ static hipError_t dispatch_prefill(const PrefillArgs& a, int mask_mode, int64_t 
 }
 
 template <typename ST>
-static hipError_t launch_pp(const PrefillArgs& a0, int64_t batch, hipStream_t s) {
+static hipError_t launch_il(const PrefillArgs& a0, int64_t batch, hipStream_t s) {
     PrefillArgs a = a0;
     a.q_tiles = (int32_t)((a.q_seq + 255) / 256);
     const int64_t blocks = (int64_t)a.q_tiles * batch * a.num_heads;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((prefill_pp_kernel<ST, 128>), dim3((unsigned)blocks), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((prefill_il_kernel<ST, 128>), dim3((unsigned)blocks), dim3(512), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int mask_mode, int64_t batch,
                           hipStream_t stream) {
     if (!a.work && mask_mode == 0 && head_dim == 128 && a.q_seq > 0 && batch > 0)
-        return dtype == 1 ? launch_pp<BF16>(a, batch, stream) : launch_pp<F16>(a, batch, stream);
+        return dtype == 1 ? launch_il<BF16>(a, batch, stream) : launch_il<F16>(a, batch, stream);
     const int64_t blocks = a.work ? (int64_t)(a.work_items + 7) / 8 * 8 * a.num_heads
                                   : (int64_t)a.q_tiles * batch * a.num_heads;
     if (blocks <= 0) return hipSuccess;

@@ -109,7 +109,8 @@ class Problem:
         self.block_size = int(block_size)
         self.window = (int(window[0]), int(window[1]))  # mask_mode "window": (win_left, win_right)
         # layout "TND": QS / KVS are the packed totals Q_T / KV_T; sequence b spans
-        # cu_seqlens[b] .. cu_seqlens[b+1]; seqused_q truncates its query rows.
+        # cu_seqlens[b] .. cu_seqlens[b+1].  seqused_q ([B], any layout) truncates
+        # each batch's query rows: rows past it keep the initial output (0, +inf).
         i32 = lambda a: None if a is None else np.ascontiguousarray(a, dtype=np.int32)
         self.cu_seqlens_q, self.cu_seqlens_kv = i32(cu_seqlens_q), i32(cu_seqlens_kv)
         self.seqused_q = i32(seqused_q)

@@ -41,6 +41,10 @@
  *     length is not computed and keeps the initial output (0 and lse = +inf,
  *     the output initialisation the developer guide describes).  Rows are
  *     numbered t * Q_N + n1, the (Q_T, Q_N) order of the TND lse.
+ *   - seqused_q with the padded layouts BNSD / BSND (developer guide 1.4: the
+ *     per-batch used lengths apply to every layout; only cu_seqlens is
+ *     TND-only): query rows i >= seqused_q[b] of batch b are not computed and
+ *     keep the initial output, 0 and lse = +inf, as in TND.
  *   - Paged KV caches (FlashAttn developer guide 1.2): token j of batch b is
  *     row j % block_size of physical block block_table[b][j / block_size];
  *     PA_BBND blocks are [block_size][KV_N][D], PA_BNBD blocks [KV_N][block_size][D].
@@ -68,7 +72,7 @@ typedef struct {
     int64_t block_size, max_blocks;
     int64_t win_left, win_right; /* mode 3: keys i - win_left .. i + win_right; < 0 unbounded */
     const int32_t *cu_q, *cu_kv; /* TND: [B + 1] sequence starts (QS = Q_T, KVS = KV_T) */
-    const int32_t *used_q;      /* TND: [B] used query rows, or NULL */
+    const int32_t *used_q;      /* [B] used query rows (any layout), or NULL */
 } orc_problem;
 
 static double dec16(int32_t dtype, uint16_t h)
@@ -209,6 +213,7 @@ static void *worker(void *arg)
             i = row % p->QS;
             n1 = (row / p->QS) % p->QN;
             b = row / (p->QS * p->QN);
+            if (p->used_q && i >= p->used_q[b]) computed = 0; /* past the used rows */
         }
         if (!computed) { /* outside every sequence's used rows: initial output */
             if (jb->splits == 0) {

@@ -38,7 +38,9 @@ MUTANTS = [
      "if (p->win_right >= 0 && j > i - p->win_right) return 0;"),
     ("tnd_kv_offsets", "if (p->layout == 2) return ((p->cu_kv[b] + j) * p->KVN + n) * p->D;",
      "if (p->layout == 2) return ((p->cu_q[b] + j) * p->KVN + n) * p->D;"),
-    ("tnd_used_rows", "(p->used_q && i >= p->used_q[b])", "(p->used_q && i > p->used_q[b])"),
+    ("tnd_used_rows", "(p->used_q && i >= p->used_q[b]))", "(p->used_q && i > p->used_q[b]))"),
+    ("padded_used_rows", "if (p->used_q && i >= p->used_q[b]) computed = 0;",
+     "if (p->used_q && i > p->used_q[b]) computed = 0;"),
     ("paged_row_offset", "const int64_t r = j % p->block_size;", "const int64_t r = (j + 1) % p->block_size;"),
     ("paged_bnbd_order", ": ((blk * p->KVN + n) * p->block_size + r) * p->D;",
      ": ((blk * p->block_size + r) * p->KVN + n) * p->D;"),

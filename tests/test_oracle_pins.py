@@ -262,10 +262,13 @@ def test_partials_of_single_token_chunks():
                 assert m[r, c] == -np.inf and l[r, c] == 0.0 and np.all(o[r, c] == 0.0)
 
 
-def test_merge_agrees_with_lse_weight_form_and_sequential_merge():
-    """Page 2 (IFA guide 8.3) weights normalised split results by exp(lse_i)/sum exp(lse_j);
-    page 3 (tutorial 3.3) merges the splits one by one with a running max.  Both must give
-    the oracle's merge."""
+def test_merge_agrees_with_lse_weight_form_and_is_order_free():
+    """Page 2 (IFA guide 8.3) weights normalised split results by exp(lse_i)/sum exp(lse_j):
+    that form must give the oracle's merge.  The merge is also a reduction that does not
+    depend on how the splits are grouped (FlashAttn developer guide 10, FD block; the
+    tutorial, section 2): any order of the splits, and merging each half first and then
+    the two halves' results (each as a one-key partial m = lse, l = 1, O = out), give
+    the same output."""
     inp = tiny(layout="BNSD", B=2, QN=4, KVN=2, QS=1, KVS=50, D=16, lens=(10, 50), seed=45)
     p = prob_of(inp)
     o, m, l = oracle.split_partials(p, inp.q, inp.k, inp.v, splits=7, chunk=8)
@@ -276,15 +279,24 @@ def test_merge_agrees_with_lse_weight_form_and_sequential_merge():
         res_i = o[r, live] / l[r, live][:, None]
         scale_i = np.exp(lse_i) / np.exp(lse_i).sum()
         assert np.allclose((res_i * scale_i[:, None]).sum(axis=0), out[r], atol=1e-12)
-        gm, gl, go = -np.inf, 0.0, np.zeros(16)
-        for c in range(7):
-            if not np.isfinite(m[r, c]):
-                continue
-            nm = max(gm, m[r, c])
-            fg, fi = math.exp(gm - nm), math.exp(m[r, c] - nm)
-            gl, go, gm = gl * fg + l[r, c] * fi, go * fg + o[r, c] * fi, nm
-        assert np.allclose(go / gl, out[r], atol=1e-12)
-        assert lse[r] == pytest.approx(gm + math.log(gl), abs=1e-12)
+    rng = np.random.default_rng(7)
+    perm = rng.permutation(7)
+    out_p, lse_p = oracle.merge(o[:, perm], m[:, perm], l[:, perm])
+    assert np.allclose(out_p, out, atol=1e-12) and np.allclose(lse_p, lse, atol=1e-12)
+
+    def as_partial(o_h, lse_h):  # a merged result as one partial: empty rows stay empty
+        empty = np.isinf(lse_h)
+        return (np.where(empty[:, None], 0.0, o_h), np.where(empty, -np.inf, lse_h),
+                np.where(empty, 0.0, 1.0))
+    for cut in (1, 3, 6):
+        oa, la = oracle.merge(o[:, :cut], m[:, :cut], l[:, :cut])
+        ob, lb = oracle.merge(o[:, cut:], m[:, cut:], l[:, cut:])
+        pa, pb = as_partial(oa, la), as_partial(ob, lb)
+        o2 = np.stack([pa[0], pb[0]], axis=1)
+        m2 = np.stack([pa[1], pb[1]], axis=1)
+        l2 = np.stack([pa[2], pb[2]], axis=1)
+        out2, lse2 = oracle.merge(o2, m2, l2)
+        assert np.allclose(out2, out, atol=1e-12) and np.allclose(lse2, lse, atol=1e-12)
 
 
 def test_gqa_equals_repeated_kv_mha():
@@ -505,3 +517,25 @@ def test_tnd_rejects_malformed_offsets():
                        "none", cu_seqlens_q=bad, cu_seqlens_kv=x.cu_kv)
     with pytest.raises(ValueError):
         oracle.attention(p, x.q, x.k, x.v)
+
+
+@pytest.mark.parametrize("layout", ["BNSD", "BSND"])
+def test_seqused_q_on_padded_layouts(layout):
+    """seqused_q (developer guide 1.4, any layout) truncates each batch's query rows:
+    rows below it equal the untruncated result (pinned against the whole-matrix brute
+    force), rows at or past it are 0 with lse = +inf; values above Q_S change nothing."""
+    spec = fa_synth.Spec("su", layout, 3, 4, 2, 9, 13, 16, "bf16", lens=(2, 13), seed=131)
+    inp = fa_synth.make(spec)
+    used = np.array([4, 0, 100], np.int32)
+    full = oracle.Problem.from_inputs(inp)
+    trunc = oracle.Problem(3, 4, 2, 9, 13, 16, layout, "bf16", spec.softmax_scale, inp.lens, "none",
+                           seqused_q=used)
+    out, lse = oracle.attention(trunc, inp.q, inp.k, inp.v)
+    ref, ref_lse = brute.attention(full, inp.q, inp.k, inp.v)
+    for b in range(3):
+        nq = min(int(used[b]), 9)
+        o_b = out[b] if layout == "BNSD" else out[b].transpose(1, 0, 2)   # [QN, QS, D]
+        r_b = ref[b] if layout == "BNSD" else ref[b].transpose(1, 0, 2)
+        assert np.allclose(o_b[:, :nq], r_b[:, :nq], rtol=1e-12, atol=1e-12)
+        assert np.allclose(lse[b][:, :nq], ref_lse[b][:, :nq], rtol=1e-12, atol=1e-12)
+        assert np.all(o_b[:, nq:] == 0) and np.all(np.isposinf(lse[b][:, nq:]))

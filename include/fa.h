@@ -110,10 +110,11 @@ typedef struct {
     const uint8_t *mask;
     int64_t mask_stride[4];
     /* Paged KV cache (all zero / NULL for FA_KV_CONTIGUOUS, where a non-NULL
-     * block_table is an error).  A paged cache needs q_seq == 1, mask NONE and
-     * actual_seq_lengths (developer guide 1.2 makes the per-batch lengths
-     * mandatory with paging); prefill on a paged cache returns
-     * FA_ERR_UNSUPPORTED.
+     * block_table is an error).  A paged cache needs actual_seq_lengths
+     * (developer guide 1.2 makes the per-batch lengths mandatory with paging)
+     * and a split-KV shape: q_seq == 1 without a mask or seqused_q (any
+     * head_dim), or head_dim 64 / 128 with g * q_seq <= 128 (g = num_heads /
+     * num_kv_heads, any mask); other paged calls return FA_ERR_UNSUPPORTED.
      *   block_table: device int32 [batch][max_blocks_per_seq], row-major.
      *     Entries of blocks a batch's length reaches must lie in
      *     [0, num_blocks); the kernels clamp them into that range so a bad
@@ -126,20 +127,26 @@ typedef struct {
     int64_t block_size;
     int64_t max_blocks_per_seq;
     int64_t num_blocks;
-    /* FA_MASK_WINDOW only (ignored otherwise): tokens kept before and after the
-     * query's own index (developer guide 1.5, win_left / win_right); -1 leaves
-     * that side unbounded, so (-1, 0) is the causal mask and (-1, -1) no mask.
-     * Values below -1 are invalid.  Tiles wholly outside the band are skipped. */
+    /* FA_MASK_WINDOW: tokens kept before and after the query's own index
+     * (developer guide 1.5, win_left / win_right); -1 leaves that side
+     * unbounded, so (-1, 0) is the causal mask and (-1, -1) no mask.  Values
+     * below -1 are invalid.  Tiles wholly outside the band are skipped.  In
+     * every other mask mode both must be -1 (the guide requires it without a
+     * window), else FA_ERR_PARAM_INVALID. */
     int64_t win_left;
     int64_t win_right;
-    /* FA_TND only (must be NULL otherwise), device int32 (developer guide 1.4):
+    /* Device int32 (developer guide 1.4).  cu_seqlens_q and cu_seqlens_kv are
+     * for FA_TND only (must be NULL otherwise); seqused_q applies to every
+     * layout.
      *   cu_seqlens_q, cu_seqlens_kv: [batch + 1], starting at 0 and
      *     non-decreasing; sequence b owns q rows [cu_q[b], cu_q[b+1]) and kv
      *     rows [cu_kv[b], cu_kv[b+1]); cu_q[batch] <= q_seq, cu_kv[batch] <= kv_seq.
      *     The kernels clamp every offset into its tensor, so malformed values
      *     give wrong rows, never out-of-bounds accesses.
-     *   seqused_q: [batch] or NULL: query rows of sequence b actually used;
-     *     the shorter of it and the sequence length takes effect.
+     *   seqused_q: [batch] or NULL: query rows of batch / sequence b
+     *     actually used; the shorter of it and q_seq (the sequence length in
+     *     TND) takes effect.  Rows at or past it are written as 0 with
+     *     lse = +inf, in every layout.
      * actual_seq_lengths (int64) truncates each sequence's keys the same way.
      * Query rows not used by any sequence (past seqused_q, or past
      * cu_seqlens_q[batch]) are written as 0 with lse = +inf, the output
@@ -162,14 +169,21 @@ fa_status fa_workspace_size(const fa_params *p, size_t *bytes);
 
 /* fa_fwd -- phase 2: the attention forward.  q: [B,Q_N,Q_S,D] or [B,Q_S,Q_N,D];
  * k, v: the same layout with KV_N heads and KV_S rows; out: shape of q;
- * lse: float32 [B,Q_N,Q_S] or NULL (not written).  q_seq == 1 without a mask
- * runs the split-KV decode, whose split plan the library chooses (see
- * fa_splitkv_plan): one split is a single stage-1 launch that writes the
- * output; more run stage 1 and then fa_combine's kernel (measured faster on
- * MI355X than the fused single launch of fa_decode_fused).  The workspace
- * must then be at least fa_workspace_size bytes, 256-byte aligned; its
- * contents need no initialisation.
- * Every other case runs the prefill kernel.  The packed layout FA_TND needs
+ * lse: float32 [B,Q_N,Q_S] or NULL (not written).  The split-KV path
+ * (FlashAttn developer guide 1.9: FlashDecode cuts the KV axis when the
+ * query rows alone cannot occupy the cores, e.g. S1 = 1) runs
+ *   - q_seq == 1 without a mask or seqused_q (any head_dim), and
+ *   - with head_dim 64 or 128 and g * q_seq <= 128: q_seq == 1 with any
+ *     mask or seqused_q (the decode of the IFA guide with its attenMask),
+ *     a paged cache, and a few query positions against a long cache when
+ *     the prefill's query tiles would occupy fewer workgroups than there
+ *     are CUs;
+ * with a split plan the library chooses (see fa_splitkv_plan): one split is
+ * a single stage-1 launch that writes the output; more run stage 1 and then
+ * fa_combine's kernel (measured faster on MI355X than the fused single
+ * launch of fa_decode_fused).  The workspace must then be at least
+ * fa_workspace_size bytes, 256-byte aligned; its contents need no
+ * initialisation.  Every other case runs the prefill kernels.  The packed layout FA_TND needs
  * fa_workspace_size bytes (256-byte aligned) for the cost-ordered list of its
  * query tiles.  A boolean mask whose rows are contiguous, 16-byte aligned key
  * runs (mask_stride[3] == 1; the pointer, the other strides and kv_seq
@@ -199,14 +213,19 @@ fa_status fa_splitkv_plan(const fa_params *p, int num_cus, int64_t chunk_hint,
                           int64_t *num_splits, int64_t *chunk, size_t *workspace_bytes);
 
 /* fa_decode_splitkv -- FlashDecoding stage 1 (FlashDecoding tutorial 3.2;
- * FlashAttn developer guide 10).  Requires q_seq == 1 and mask_mode NONE.
- * Chunk c covers keys [c*chunk, (c+1)*chunk) cut at the batch's length.  For
- * every (b, n1, c) it writes
+ * FlashAttn developer guide 10).  Takes q_seq == 1 without a mask or
+ * seqused_q (any head_dim), or, with head_dim 64 / 128 and
+ * g * q_seq <= 128, any q_seq, mask and seqused_q (else
+ * FA_ERR_UNSUPPORTED).  Chunk c covers keys [c*chunk, (c+1)*chunk) cut at
+ * the batch's length.  For every row (b, n1, i) and chunk c it writes, over
+ * the keys of the chunk the row sees (mask, length, seqused_q),
  *   m_part = max_j s_j,  l_part = sum_j exp(s_j - m_part),
  *   o_part[d] = sum_j exp(s_j - m_part) v_j[d]    (NOT divided by l_part)
- * with s_j = scale * q.k_j, natural units.  An empty chunk writes m = -inf,
- * l = 0 and o = 0.  Layouts (float32, contiguous):
- *   o_part [B][Q_N][num_splits][D], m_part and l_part [B][Q_N][num_splits].
+ * with s_j = scale * q.k_j, natural units.  A chunk the row sees no key of
+ * writes m = -inf, l = 0 and o = 0.  Layouts (float32, contiguous; row
+ * (b, n1, i) = (b * Q_N + n1) * q_seq + i):
+ *   o_part [B][Q_N][q_seq][num_splits][D] (16-byte aligned),
+ *   m_part and l_part [B][Q_N][q_seq][num_splits] (4-byte aligned).
  * num_splits * chunk must cover kv_seq; chunk a positive multiple of 64
  * and at most a cap (a paged cache: 1016 * block_size, the block ids of one
  * chunk being staged on chip; a contiguous one: (chunk + 256) rows of one
@@ -215,7 +234,8 @@ fa_status fa_splitkv_plan(const fa_params *p, int num_cus, int64_t chunk_hint,
  * 128 (contiguous or paged cache), the chunk runs on the matrix cores (the
  * query heads of a KV head are the rows of one tile; P is rounded to the input
  * type before the PV product, as in the prefill; chunks of at most 512 tokens
- * run on one-wave workgroups, longer ones on two-wave workgroups); other
+ * run on one-wave workgroups, longer ones on two-wave workgroups), and so
+ * does every call with several query positions, a mask or seqused_q; other
  * shapes use the vector units. */
 fa_status fa_decode_splitkv(const fa_params *p, int64_t num_splits, int64_t chunk,
                             const void *q, const void *k, const void *v,
@@ -228,7 +248,8 @@ fa_status fa_decode_splitkv(const fa_params *p, int64_t num_splits, int64_t chun
  * rows (fa_combine's reduction) into out / lse and resets the unit's counter.
  *   num_splits: 1..256 (1 = one chunk, no merge and no workspace needed);
  *   chunk as for fa_decode_splitkv.
- *   workspace: at least the bytes fa_splitkv_plan reports, 256-byte aligned:
+ * Takes q_seq == 1 without a mask or seqused_q (else FA_ERR_UNSUPPORTED).
+ *   workspace: at least the bytes fa_decode_fused_plan reports, 256-byte aligned:
  *     o_part, m_part, l_part (fa_decode_splitkv's layouts, each region
  *     256-byte aligned) followed by one uint32 counter per unit.  CONTRACT:
  *     the counters must be zero before the first call -- zero-fill the
@@ -242,12 +263,23 @@ fa_status fa_decode_fused(const fa_params *p, int64_t num_splits, int64_t chunk,
                           const void *q, const void *k, const void *v, void *workspace,
                           size_t workspace_bytes, void *out, float *lse, void *stream);
 
+/* fa_decode_fused_plan -- the split plan for fa_decode_fused: as
+ * fa_splitkv_plan, but sized for the vector stage 1 that the fused launch
+ * runs (its residency and its units of batch, KV head and head group) and
+ * capped at the fused merge's 256 splits (the chunk grows instead).
+ * num_cus <= 0 queries the current device.  Returns FA_ERR_UNSUPPORTED for
+ * shapes fa_decode_fused does not take, or when 256 chunks of the largest
+ * chunk cannot cover kv_seq. */
+fa_status fa_decode_fused_plan(const fa_params *p, int num_cus, int64_t *num_splits, int64_t *chunk,
+                               size_t *workspace_bytes);
+
 /* fa_combine -- FlashDecoding stage 2, the LSE merge (FlashAttn developer
  * guide 10: m = max_i m_i, l = sum_i l_i exp(m_i - m),
  * o = sum_i o_i exp(m_i - m) / l; FlashDecoding tutorial section 2).  Reads the
- * stage-1 layouts above for q_seq == 1 and writes out (shape of q, in p's
- * layout and dtype) and lse (nullable) = log l + m.  Splits with m_i = -inf
- * are skipped; a row whose splits are all empty writes 0 and +inf. */
+ * stage-1 layouts above (any q_seq; o_part 16-byte aligned) and writes out
+ * (shape of q, in p's layout and dtype) and lse (nullable, [B][Q_N][Q_S])
+ * = log l + m.  Splits with m_i = -inf are skipped; a row whose splits are
+ * all empty writes 0 and +inf. */
 fa_status fa_combine(const fa_params *p, int64_t num_splits, const float *o_part,
                      const float *m_part, const float *l_part, void *out, float *lse,
                      void *stream);

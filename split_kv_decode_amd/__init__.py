@@ -28,8 +28,8 @@ MASK_MODES = {"none": FA_MASK_NONE, "causal": FA_MASK_CAUSAL, "bool": FA_MASK_BO
 FA_KV_CONTIGUOUS, FA_KV_PAGED_BBND, FA_KV_PAGED_BNBD = 0, 1, 2
 KV_LAYOUTS = {"contiguous": FA_KV_CONTIGUOUS, "PA_BBND": FA_KV_PAGED_BBND, "PA_BNBD": FA_KV_PAGED_BNBD}
 
-EXPORTS = ("fa_workspace_size", "fa_fwd", "fa_fwd_noalloc", "fa_splitkv_plan", "fa_decode_splitkv",
-           "fa_decode_fused", "fa_combine", "fa_last_error")
+EXPORTS = ("fa_workspace_size", "fa_fwd", "fa_fwd_noalloc", "fa_splitkv_plan", "fa_decode_fused_plan",
+           "fa_decode_splitkv", "fa_decode_fused", "fa_combine", "fa_last_error")
 
 
 class FaError(RuntimeError):
@@ -72,11 +72,12 @@ def load(path: Optional[str] = None):
             lib.fa_fwd.argtypes = [P(FaParams), vp, vp, vp, vp, vp, vp, sz, vp]
             lib.fa_fwd_noalloc.argtypes = [P(FaParams), vp, vp, vp, vp, vp, vp]
             lib.fa_splitkv_plan.argtypes = [P(FaParams), ctypes.c_int, i64, P(i64), P(i64), P(sz)]
+            lib.fa_decode_fused_plan.argtypes = [P(FaParams), ctypes.c_int, P(i64), P(i64), P(sz)]
             lib.fa_decode_splitkv.argtypes = [P(FaParams), i64, i64, vp, vp, vp, vp, vp, vp, vp]
             lib.fa_combine.argtypes = [P(FaParams), i64, vp, vp, vp, vp, vp, vp]
             lib.fa_decode_fused.argtypes = [P(FaParams), i64, i64, vp, vp, vp, vp, sz, vp, vp, vp]
             for f in (lib.fa_workspace_size, lib.fa_fwd, lib.fa_fwd_noalloc, lib.fa_splitkv_plan,
-                      lib.fa_decode_splitkv, lib.fa_combine, lib.fa_decode_fused):
+                      lib.fa_decode_fused_plan, lib.fa_decode_splitkv, lib.fa_combine, lib.fa_decode_fused):
                 f.restype = ctypes.c_int
             lib.fa_last_error.argtypes = []
             lib.fa_last_error.restype = ctypes.c_char_p
@@ -131,6 +132,10 @@ def make_params(batch, num_heads, q_seq, kv_seq, head_dim, *, num_kv_heads=0, la
     p.kv_layout = KV_LAYOUTS[kv_layout] if isinstance(kv_layout, str) else kv_layout
     p.block_table = _ptr(block_table)
     p.block_size, p.max_blocks_per_seq, p.num_blocks = block_size, max_blocks_per_seq, num_blocks
+    # The struct holds raw device addresses: keep the objects they came from
+    # alive as long as the struct, so a temporary tensor passed here is not
+    # freed (and its memory handed to the next allocation) before the call.
+    p._keep = (actual_seq_lengths, mask, block_table, cu_seqlens_q, cu_seqlens_kv, seqused_q)
     return p
 
 
@@ -154,6 +159,13 @@ def fa_splitkv_plan(params: FaParams, num_cus: int = 0, chunk_hint: int = 0):
     sp, ch, ws = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_size_t(0)
     _check(load().fa_splitkv_plan(ctypes.byref(params), int(num_cus), int(chunk_hint),
                                   ctypes.byref(sp), ctypes.byref(ch), ctypes.byref(ws)))
+    return sp.value, ch.value, ws.value
+
+
+def fa_decode_fused_plan(params: FaParams, num_cus: int = 0):
+    sp, ch, ws = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_size_t(0)
+    _check(load().fa_decode_fused_plan(ctypes.byref(params), int(num_cus), ctypes.byref(sp), ctypes.byref(ch),
+                                       ctypes.byref(ws)))
     return sp.value, ch.value, ws.value
 
 
@@ -192,7 +204,7 @@ def params_for(q, k, *, layout="BNSD", num_kv_heads=0, scale=1.0, actual_seq_len
     cu_seqlens_q / cu_seqlens_kv ([B + 1]) and seqused_q ([B]) are device tensors.
     """
     import torch
-    extra = {}
+    extra = dict(seqused_q=seqused_q) if seqused_q is not None else {}
     if layout == "TND":
         QS, N, D = q.shape
         B = cu_seqlens_q.shape[0] - 1
@@ -209,7 +221,7 @@ def params_for(q, k, *, layout="BNSD", num_kv_heads=0, scale=1.0, actual_seq_len
         nb, bs, KVN = ((k.shape[0], k.shape[1], k.shape[2]) if kv_layout == "PA_BBND"
                        else (k.shape[0], k.shape[2], k.shape[1]))
         KVS = block_table.shape[1] * bs
-        extra = dict(kv_layout=kv_layout, block_table=block_table, block_size=bs,
+        extra.update(kv_layout=kv_layout, block_table=block_table, block_size=bs,
                      max_blocks_per_seq=block_table.shape[1], num_blocks=nb)
     dtype = {torch.bfloat16: "bf16", torch.float16: "f16"}[q.dtype]
     mode = "bool" if mask is not None else ("causal" if causal else "none")

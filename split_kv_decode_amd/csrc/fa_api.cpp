@@ -46,6 +46,10 @@ struct Shape {
     int64_t B, QN, KVN, QS, KVS, D, g;
 };
 
+bool fast_decode(const fa_params* p);
+bool general_split_ok(const fa_params* p, const Shape& s);
+int row_groups(const Shape& s);
+
 fa_status check_params(const fa_params* p, Shape* s) {
     if (!p) return fail(FA_ERR_NULLPTR, "params is NULL");
     if (p->batch < 1 || p->batch >= kMaxDim) return fail(FA_ERR_PARAM_INVALID, "batch must be in [1, 2^31), got %lld", (long long)p->batch);
@@ -77,16 +81,23 @@ fa_status check_params(const fa_params* p, Shape* s) {
             return fail(FA_ERR_UNSUPPORTED, "a paged KV cache with the TND layout is not built");
         if (p->mask_mode == FA_MASK_BOOL)
             return fail(FA_ERR_UNSUPPORTED, "a boolean mask tensor with the TND layout is not built");
-    } else if (p->cu_seqlens_q || p->cu_seqlens_kv || p->seqused_q) {
-        return fail(FA_ERR_PARAM_INVALID, "cu_seqlens / seqused_q are for the TND layout only");
+    } else if (p->cu_seqlens_q || p->cu_seqlens_kv) {
+        return fail(FA_ERR_PARAM_INVALID, "cu_seqlens_q / cu_seqlens_kv are for the TND layout only");
     }
     if (p->dtype != FA_F16 && p->dtype != FA_BF16) return fail(FA_ERR_PARAM_INVALID, "unknown dtype %d", (int)p->dtype);
     if (!std::isfinite(p->scale)) return fail(FA_ERR_PARAM_INVALID, "scale must be finite");
+    // The kernels scale scores by scale * log2(e) in fp32.
+    if (!std::isfinite((float)(std::fabs(p->scale) * 1.4426950408889634)))
+        return fail(FA_ERR_PARAM_INVALID, "|scale| * log2(e) must be finite in fp32, got scale %g", p->scale);
     if (p->mask_mode != FA_MASK_NONE && p->mask_mode != FA_MASK_CAUSAL && p->mask_mode != FA_MASK_BOOL &&
         p->mask_mode != FA_MASK_WINDOW)
         return fail(FA_ERR_PARAM_INVALID, "unknown mask_mode %d", (int)p->mask_mode);
     if (p->mask_mode == FA_MASK_WINDOW && (p->win_left < -1 || p->win_right < -1))
         return fail(FA_ERR_PARAM_INVALID, "win_left and win_right must be >= -1 (-1 = unbounded), got %lld, %lld",
+                    (long long)p->win_left, (long long)p->win_right);
+    // FlashAttn developer guide 1.5: without the window mode the two bounds are -1.
+    if (p->mask_mode != FA_MASK_WINDOW && (p->win_left != -1 || p->win_right != -1))
+        return fail(FA_ERR_PARAM_INVALID, "win_left and win_right must be -1 outside the window mode, got %lld, %lld",
                     (long long)p->win_left, (long long)p->win_right);
     if (p->mask_mode == FA_MASK_BOOL && !p->mask) return fail(FA_ERR_NULLPTR, "mask_mode BOOL needs a mask tensor");
     if (p->mask_mode != FA_MASK_BOOL && p->mask)
@@ -115,8 +126,6 @@ fa_status check_params(const fa_params* p, Shape* s) {
                         (long long)p->kv_seq, (long long)(p->max_blocks_per_seq * p->block_size));
         if (p->batch * p->max_blocks_per_seq >= kMaxDim)
             return fail(FA_ERR_PARAM_INVALID, "batch * max_blocks_per_seq must stay below 2^31");
-        if (p->q_seq != 1 || p->mask_mode != FA_MASK_NONE)
-            return fail(FA_ERR_UNSUPPORTED, "a paged KV cache is built for decode only (q_seq == 1, no mask)");
     }
     s->B = p->batch;
     s->QN = p->num_heads;
@@ -132,6 +141,10 @@ fa_status check_params(const fa_params* p, Shape* s) {
                           ? (p->layout == FA_TND ? 1.0 : double(s->B)) * double(s->KVN) * double(s->KVS) * double(s->D)
                           : double(p->num_blocks) * double(p->block_size) * double(s->KVN) * double(s->D);
     if (qe >= double(kMaxElems) || ke >= double(kMaxElems)) return fail(FA_ERR_PARAM_INVALID, "tensor too large");
+    if (p->kv_layout != FA_KV_CONTIGUOUS && !fast_decode(p) && !general_split_ok(p, *s))
+        return fail(FA_ERR_UNSUPPORTED,
+                    "a paged KV cache is built for the split-KV paths: one query position without a mask or used "
+                    "lengths, or head_dim 64/128 with num_heads / num_kv_heads * q_seq <= 128");
     return ok();
 }
 
@@ -231,7 +244,7 @@ struct Partials {
 // layouts), then one counter per stage-1 unit for the fused plan.
 Partials partial_bytes(const Shape& s, int64_t splits) {
     Partials r;
-    const size_t rows = size_t(s.B) * size_t(s.QN) * size_t(splits);
+    const size_t rows = size_t(s.B) * size_t(s.QN) * size_t(s.QS) * size_t(splits);
     r.o_bytes = round_up(rows * size_t(s.D) * sizeof(float), 256);
     r.m_bytes = round_up(rows * sizeof(float), 256);
     const size_t units = size_t(s.B) * size_t(s.KVN) * size_t(s.g / heads_per_workgroup(s.g));
@@ -268,11 +281,17 @@ int mfma_waves(int64_t chunk) { return chunk <= kShortChunk ? 1 : 2; }
 // A one-wave workgroup keeps a paged chunk's block ids in a register.
 static_assert(kShortChunk / 16 + 2 <= fa::kLaneBlocks, "one-wave paged chunks outgrow the block-id register");
 
+// Stage 1 runs on the matrix cores: grouped heads on the fast decode path,
+// and always on the general split path.
+bool uses_mfma(const fa_params* p, const Shape& s) { return fast_decode(p) ? mfma_decode(p, s) : true; }
+
 void plan_splits(const fa_params* p, const Shape& s, int num_cus, int64_t* splits, int64_t* chunk, int waves = 2) {
     const int gh = heads_per_workgroup(s.g);
-    const bool mm = mfma_decode(p, s);
+    const bool mm = uses_mfma(p, s);
     const bool paged = p->kv_layout != FA_KV_CONTIGUOUS;
-    const int64_t units = mm ? s.B * s.KVN : s.B * s.KVN * (s.g / gh);
+    // Units of independent work: (b, KV head) and, on the general path, its
+    // row groups.
+    const int64_t units = mm ? s.B * s.KVN * (fast_decode(p) ? 1 : row_groups(s)) : s.B * s.KVN * (s.g / gh);
     const int resident = mm ? mfma_residency(p->dtype == FA_BF16 ? 1 : 0, (int)s.D, paged, waves)
                             : stage1_residency(p->dtype == FA_BF16 ? 1 : 0, (int)s.D, gh, paged);
     const int64_t target = (resident > 0 ? resident : kWgPerCu) * int64_t(num_cus > 0 ? num_cus : 256);
@@ -330,7 +349,7 @@ DecodePlan decode_plan(const fa_params* p, const Shape& s) {
     plan_splits(p, s, device_cus(), &d.splits, &d.chunk);
     d.bal_nwg = 0;
     d.waves = mfma_waves(d.chunk);
-    if (mfma_decode(p, s) && p->actual_seq_lengths && d.splits > 1) {
+    if (fast_decode(p) && mfma_decode(p, s) && p->actual_seq_lengths && d.splits > 1) {
         // The balanced pieces share out what the fixed chunks would cover at
         // full lengths, so they are no longer: the fixed plan's wave count holds.
         DecodePlan b = d;
@@ -339,9 +358,44 @@ DecodePlan decode_plan(const fa_params* p, const Shape& s) {
     return d;
 }
 
-bool decode_path(const fa_params* p) {
-    return p->q_seq == 1 && p->mask_mode == FA_MASK_NONE && p->layout != FA_TND;
+// One query position, no mask, no used lengths: the decode kernels of
+// stage 1 (vector or matrix-core) with fixed or length-balanced pieces.
+bool fast_decode(const fa_params* p) {
+    return p->q_seq == 1 && p->mask_mode == FA_MASK_NONE && !p->seqused_q && p->layout != FA_TND;
 }
+
+// The split-KV stage 1 on the matrix cores in its general form: the g * Q_S
+// (query head, position) rows of a KV head fill up to four 32-row tiles,
+// masks (causal, window, boolean tensor) and used lengths applied per key,
+// and the combine merges the pieces (FlashAttn developer guide 1.9 and 4:
+// FlashDecode splits the KV axis when the query rows alone cannot occupy the
+// cores, e.g. S1 = 1).
+constexpr int64_t kMaxSplitRows = 128;
+bool general_split_ok(const fa_params* p, const Shape& s) {
+    return p->layout != FA_TND && (s.D == 64 || s.D == 128) && s.g * s.QS <= kMaxSplitRows &&
+           kv_row_bytes(p, s) * 64 < (int64_t(1) << 31) &&
+           (p->kv_layout == FA_KV_CONTIGUOUS || p->block_size % 16 == 0);
+}
+int row_groups(const Shape& s) { return (int)((s.g * s.QS + 31) / 32); }
+
+// Prefill workgroups for this shape: 256-row tiles for the interleaved
+// kernel (mask-free, D = 128), 128-row tiles otherwise.
+int64_t prefill_workgroups(const fa_params* p, const Shape& s) {
+    const int64_t rows = (p->mask_mode == FA_MASK_NONE && s.D == 128 && !p->seqused_q) ? 256 : 128;
+    return s.B * s.QN * ((s.QS + rows - 1) / rows);
+}
+
+enum class Path { kPrefill, kFastDecode, kSplit };
+Path choose_path(const fa_params* p, const Shape& s) {
+    if (p->layout == FA_TND) return Path::kPrefill;
+    if (fast_decode(p)) return Path::kFastDecode;
+    if (!general_split_ok(p, s)) return Path::kPrefill;
+    // One query position always splits (masked decode); a few positions split
+    // when the prefill's query tiles cannot fill the CUs.
+    if (s.QS == 1 || p->kv_layout != FA_KV_CONTIGUOUS) return Path::kSplit;
+    return prefill_workgroups(p, s) < device_cus() ? Path::kSplit : Path::kPrefill;
+}
+bool decode_path(const fa_params* p) { return fast_decode(p); }
 
 // Packed layout: entries of the cost-ordered work list, one per 128-row query
 // tile of every sequence plus the rows past the last sequence.  The sum over
@@ -371,7 +425,7 @@ struct MaskSummaryGeom {
 };
 MaskSummaryGeom mask_summary_geom(const fa_params* p, const Shape& s) {
     MaskSummaryGeom g{0, 0, 0, 0, 0};
-    if (p->layout == FA_TND || decode_path(p) || prefill_mask_kind(p, s) != 3) return g;
+    if (p->layout == FA_TND || choose_path(p, s) != Path::kPrefill || prefill_mask_kind(p, s) != 3) return g;
     const int64_t kv_tiles = (s.KVS + fa::kMaskKeysPerTile - 1) / fa::kMaskKeysPerTile;
     g.q_tiles = (s.QS + fa::kMaskRowsPerTile - 1) / fa::kMaskRowsPerTile;
     g.words = (kv_tiles + fa::kMaskTilesPerWord - 1) / fa::kMaskTilesPerWord;
@@ -417,7 +471,31 @@ void fill_decode_args(const fa_params* p, const Shape& s, fa::DecodeArgs* a) {
     const int gh = heads_per_workgroup(s.g);
     a->head_groups = (int32_t)(s.g / gh);
     a->scale_log2 = (float)(p->scale * 1.4426950408889634);
+    if (a->scale_log2 == 0.f) {  // scale 0 (or below fp32's range): every score is 0
+        a->zero_q = 1;
+        a->scale_log2 = 1.f;
+    }
     a->batch = (int32_t)s.B;
+    a->q_seq = s.QS;
+    a->q_stride_b = s.QS * s.QN * s.D;
+    a->q_stride_n = p->layout == FA_BNSD ? s.QS * s.D : s.D;
+    a->q_stride_s = p->layout == FA_BNSD ? s.D : s.QN * s.D;
+    a->out_bsnd = p->layout == FA_BSND ? 1 : 0;
+    a->row_groups = fast_decode(p) ? 1 : row_groups(s);
+    a->used_q = p->seqused_q;
+    a->mask_mode = (int32_t)p->mask_mode;  // 1 causal, 2 boolean tensor, 3 window
+    if (p->mask_mode == FA_MASK_BOOL) {
+        a->mask = p->mask;
+        for (int i = 0; i < 4; ++i) a->mask_stride[i] = p->mask_stride[i];
+        const int64_t* st = p->mask_stride;
+        a->mask_dword = (aligned(p->mask, 4) && st[3] == 1 && st[0] % 4 == 0 && st[1] % 4 == 0 && st[2] % 4 == 0 &&
+                         s.KVS % 4 == 0)
+                            ? 1
+                            : 0;
+    }
+    auto win = [](int64_t w) { return (w < 0 || w > 0x7fffffff) ? int32_t(0x7fffffff) : int32_t(w); };
+    a->win_left = win(p->win_left);
+    a->win_right = win(p->win_right);
 }
 
 fa_status launch_result(hipError_t e, const char* what) {
@@ -443,7 +521,7 @@ fa_status run_stage1(const fa_params* p, const Shape& s, int64_t splits, int64_t
     a.counters = counters;
     a.bal_nwg = bal_nwg;
     const bool finish = (out != nullptr && counters == nullptr);
-    if (counters == nullptr && mfma_decode(p, s))
+    if (counters == nullptr && uses_mfma(p, s))
         return launch_result(fa::launch_decode_mfma(a, p->dtype == FA_BF16 ? 1 : 0, (int)s.D, finish,
                                                     waves > 0 ? waves : mfma_waves(chunk), s.B, stream),
                              "decode stage 1");
@@ -467,7 +545,9 @@ fa_status run_combine(const fa_params* p, const Shape& s, int64_t splits, const 
     a.l_part = l_part;
     a.out = out;
     a.lse = lse;
-    a.rows = s.B * s.QN;
+    a.rows = s.B * s.QN * s.QS;
+    a.q_seq = s.QS;
+    a.out_bsnd = p->layout == FA_BSND ? 1 : 0;
     a.num_splits = (int32_t)splits;
     return launch_result(fa::launch_combine(a, p->dtype == FA_BF16 ? 1 : 0, (int)s.D, stream), "combine");
 }
@@ -519,6 +599,11 @@ fa_status run_prefill(const fa_params* p, const Shape& s, const void* q, const v
     a.q_tiles = (int32_t)((s.QS + 127) / 128);
     a.negate_q = p->scale < 0 ? 1 : 0;
     a.scale_log2 = (float)(std::fabs(p->scale) * 1.4426950408889634);
+    if (a.scale_log2 == 0.f) {  // scale 0 (or below fp32's range): every score is 0
+        a.zero_q = 1;
+        a.scale_log2 = 1.f;
+    }
+    a.used_q = p->seqused_q;  // padded layouts: rows past it written as 0 / +inf
     // Window bounds as 32-bit distances from the query row: |key - row| < 2^31.
     auto win = [](int64_t w) { return (w < 0 || w > 0x7fffffff) ? int32_t(0x7fffffff) : int32_t(w); };
     a.win_left = win(p->win_left);
@@ -572,6 +657,17 @@ fa_status run_prefill(const fa_params* p, const Shape& s, const void* q, const v
     return launch_result(fa::launch_prefill(a, p->dtype == FA_BF16 ? 1 : 0, (int)s.D, mm, s.B, stream), "prefill");
 }
 
+// The split-KV entry points: the fast decode shape (one position, no mask,
+// no used lengths: any head_dim) or the general matrix-core shape.
+fa_status check_split_shape(const fa_params* p, const Shape& s) {
+    if (p->layout == FA_TND) return fail(FA_ERR_UNSUPPORTED, "split-KV decode is built for BNSD and BSND");
+    if (fast_decode(p) || general_split_ok(p, s)) return ok();
+    return fail(FA_ERR_UNSUPPORTED,
+                "split-KV with several query positions, a mask or used lengths is built for head_dim 64 and 128 "
+                "with num_heads / num_kv_heads * q_seq <= %lld",
+                (long long)kMaxSplitRows);
+}
+
 // Scratch of fa_fwd_noalloc: device memory the library holds itself, so that
 // callers that cannot allocate (code under HIP graph capture, serving loops,
 // harnesses that forbid it) still run the paths that need a workspace.  One
@@ -605,6 +701,8 @@ fa_status fa_splitkv_plan(const fa_params* p, int num_cus, int64_t chunk_hint, i
     fa_status st = check_params(p, &s);
     if (st != FA_OK) return st;
     if (!num_splits || !chunk) return fail(FA_ERR_NULLPTR, "num_splits and chunk outputs must not be NULL");
+    st = check_split_shape(p, s);
+    if (st != FA_OK) return st;
     if (chunk_hint < 0 || chunk_hint % 64 != 0)
         return fail(FA_ERR_PARAM_INVALID, "chunk_hint must be 0 or a positive multiple of 64, got %lld",
                     (long long)chunk_hint);
@@ -625,6 +723,39 @@ fa_status fa_splitkv_plan(const fa_params* p, int num_cus, int64_t chunk_hint, i
     return ok();
 }
 
+fa_status fa_decode_fused_plan(const fa_params* p, int num_cus, int64_t* num_splits, int64_t* chunk,
+                               size_t* workspace_bytes) {
+    Shape s;
+    fa_status st = check_params(p, &s);
+    if (st != FA_OK) return st;
+    if (!num_splits || !chunk) return fail(FA_ERR_NULLPTR, "num_splits and chunk outputs must not be NULL");
+    if (p->layout == FA_TND || !fast_decode(p))
+        return fail(FA_ERR_UNSUPPORTED, "the fused decode takes one query position without a mask or used lengths");
+    // The fused launch runs the vector stage 1: plan with its residency and
+    // its units (b, KV head, head group), at most kFusedMaxSplits pieces.
+    const int gh = heads_per_workgroup(s.g);
+    const bool paged = p->kv_layout != FA_KV_CONTIGUOUS;
+    const int res = stage1_residency(p->dtype == FA_BF16 ? 1 : 0, (int)s.D, gh, paged);
+    const int64_t units = s.B * s.KVN * (s.g / gh);
+    const int64_t target = (res > 0 ? res : kWgPerCu) * int64_t(num_cus > 0 ? num_cus : device_cus());
+    int64_t want = (target + units - 1) / units;
+    if (want < 1) want = 1;
+    int64_t c = ((s.KVS + want - 1) / want + 63) / 64 * 64;
+    const int64_t kv_round = (s.KVS + 63) / 64 * 64;
+    if (c < kMinChunk) c = kMinChunk < kv_round ? kMinChunk : kv_round;
+    const int64_t c_min = ((s.KVS + fa::kFusedMaxSplits - 1) / fa::kFusedMaxSplits + 63) / 64 * 64;
+    if (c < c_min) c = c_min;
+    if (c > chunk_cap(p, s)) c = chunk_cap(p, s);
+    const int64_t sp = (s.KVS + c - 1) / c;
+    if (sp > fa::kFusedMaxSplits)
+        return fail(FA_ERR_UNSUPPORTED, "kv_seq %lld needs more than %d pieces of the largest chunk", (long long)s.KVS,
+                    fa::kFusedMaxSplits);
+    *num_splits = sp;
+    *chunk = c;
+    if (workspace_bytes) *workspace_bytes = sp > 1 ? partial_bytes(s, sp).total : 0;
+    return ok();
+}
+
 fa_status fa_workspace_size(const fa_params* p, size_t* bytes) {
     Shape s;
     fa_status st = check_params(p, &s);
@@ -635,7 +766,7 @@ fa_status fa_workspace_size(const fa_params* p, size_t* bytes) {
         *bytes = varlen_bytes(s);
         return ok();
     }
-    if (!decode_path(p)) {
+    if (choose_path(p, s) == Path::kPrefill) {
         *bytes = mask_summary_geom(p, s).bytes;
         return ok();
     }
@@ -659,7 +790,7 @@ fa_status fa_fwd(const fa_params* p, const void* q, const void* k, const void* v
         if (workspace_bytes < need)
             return fail(FA_ERR_PARAM_INVALID, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
     }
-    if (!decode_path(p)) {
+    if (choose_path(p, s) == Path::kPrefill) {
         // A staged boolean mask takes an optional workspace for its summary;
         // without one the prefill runs unchanged, visiting every KV tile.
         const size_t need = mask_summary_geom(p, s).bytes;
@@ -697,15 +828,15 @@ fa_status fa_decode_splitkv(const fa_params* p, int64_t num_splits, int64_t chun
     Shape s;
     fa_status st = check_params(p, &s);
     if (st != FA_OK) return st;
-    if (p->layout == FA_TND) return fail(FA_ERR_UNSUPPORTED, "split-KV decode is built for BNSD and BSND");
-    if (p->q_seq != 1) return fail(FA_ERR_PARAM_INVALID, "split-KV decode needs q_seq == 1, got %lld", (long long)p->q_seq);
-    if (p->mask_mode != FA_MASK_NONE) return fail(FA_ERR_PARAM_INVALID, "split-KV decode takes no mask");
+    st = check_split_shape(p, s);
+    if (st != FA_OK) return st;
     if (!q || !k || !v) return fail(FA_ERR_NULLPTR, "q, k and v must not be NULL");
     if (!o_part || !m_part || !l_part) return fail(FA_ERR_NULLPTR, "o_part, m_part and l_part must not be NULL");
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
         return fail(FA_ERR_PARAM_INVALID, "q, k and v must be 16-byte aligned");
-    if (!aligned(o_part, 4) || !aligned(m_part, 4) || !aligned(l_part, 4))
-        return fail(FA_ERR_PARAM_INVALID, "partials must be 4-byte aligned");
+    // o_part rows are written and read as 16-byte vectors
+    if (!aligned(o_part, 16) || !aligned(m_part, 4) || !aligned(l_part, 4))
+        return fail(FA_ERR_PARAM_INVALID, "o_part must be 16-byte aligned, m_part and l_part 4-byte aligned");
     if (num_splits < 1 || num_splits > kMaxSplits) return fail(FA_ERR_PARAM_INVALID, "num_splits must be in [1, 2^20]");
     if (chunk < 64 || chunk % 64 != 0) return fail(FA_ERR_PARAM_INVALID, "chunk must be a positive multiple of 64");
     if (chunk > chunk_cap(p, s))
@@ -724,8 +855,8 @@ fa_status fa_decode_fused(const fa_params* p, int64_t num_splits, int64_t chunk,
     fa_status st = check_params(p, &s);
     if (st != FA_OK) return st;
     if (p->layout == FA_TND) return fail(FA_ERR_UNSUPPORTED, "split-KV decode is built for BNSD and BSND");
-    if (p->q_seq != 1) return fail(FA_ERR_PARAM_INVALID, "split-KV decode needs q_seq == 1, got %lld", (long long)p->q_seq);
-    if (p->mask_mode != FA_MASK_NONE) return fail(FA_ERR_PARAM_INVALID, "split-KV decode takes no mask");
+    if (!fast_decode(p))
+        return fail(FA_ERR_UNSUPPORTED, "the fused decode takes one query position without a mask or used lengths");
     st = check_tensors(q, k, v, out, lse);
     if (st != FA_OK) return st;
     if (num_splits < 1 || num_splits > fa::kFusedMaxSplits)
@@ -757,8 +888,9 @@ fa_status fa_combine(const fa_params* p, int64_t num_splits, const float* o_part
     fa_status st = check_params(p, &s);
     if (st != FA_OK) return st;
     if (p->layout == FA_TND) return fail(FA_ERR_UNSUPPORTED, "combine is built for BNSD and BSND");
-    if (p->q_seq != 1) return fail(FA_ERR_PARAM_INVALID, "combine needs q_seq == 1, got %lld", (long long)p->q_seq);
     if (!o_part || !m_part || !l_part) return fail(FA_ERR_NULLPTR, "o_part, m_part and l_part must not be NULL");
+    if (!aligned(o_part, 16) || !aligned(m_part, 4) || !aligned(l_part, 4))  // o_part read as 16-byte vectors
+        return fail(FA_ERR_PARAM_INVALID, "o_part must be 16-byte aligned, m_part and l_part 4-byte aligned");
     if (!out) return fail(FA_ERR_NULLPTR, "out must not be NULL");
     if (!aligned(out, 16)) return fail(FA_ERR_PARAM_INVALID, "out must be 16-byte aligned");
     if (lse && !aligned(lse, 4)) return fail(FA_ERR_PARAM_INVALID, "lse must be 4-byte aligned");

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void decode_stage1_kernel(DecodeArgs a) {
         for (int h = 0; h < GH; ++h) {
             const int gi = hg * GH + h;
             qp[h] = u32x4{0u, 0u, 0u, 0u};
-            if (gi < a.group) {
+            if (gi < a.group && !a.zero_q) {  // zero_q: scale 0, every score 0
                 const int64_t n1 = (int64_t)n2 * a.group + gi;
                 qp[h] = ld128(a.q + (b * a.num_heads + n1) * D + sub * 8);
             }
@@ -375,18 +375,23 @@ __global__ __launch_bounds__(256) void decode_stage1_kernel(DecodeArgs a) {
 
     if constexpr (MODE == kFused) {
         // Count this chunk and let the workgroup that completes the unit's
-        // count merge its rows.  The partials were written with device-scope
-        // (L2-coherent) stores and are read back with device-scope loads, so
-        // no cache write-back or invalidation is needed -- a device-scope
-        // fence would write back and invalidate this XCD's whole L2 in every
-        // workgroup.  Each thread waits for its stores to complete before the
-        // barrier, so they are performed before the counter moves.
+        // count merge its rows.  Every wave's partial stores complete before
+        // the barrier; thread 0 then counts with a release at device (agent)
+        // scope, which writes this XCD's L2 back to the point where the other
+        // XCDs read, so the partials are visible device-wide before the count
+        // moves.  Only the workgroup that completes the count acquires (drops
+        // lines its caches may hold stale) before reading the other
+        // workgroups' partials: a full fence in every workgroup, which also
+        // invalidates each XCD's L2 each time, measured several times slower.
         __shared__ int s_last;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (threadIdx.x == 0)
-            s_last = (__hip_atomic_fetch_add(a.counters + unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                      (unsigned)(a.num_splits - 1));
+        if (threadIdx.x == 0) {
+            const bool last = __hip_atomic_fetch_add(a.counters + unit, 1u, __ATOMIC_RELEASE,
+                                                     __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(a.num_splits - 1);
+            if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            s_last = last;
+        }
         __syncthreads();
         if (!s_last) return;
         // Every chunk of the unit has counted: leave the counter at zero for
@@ -540,7 +545,14 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     const float* mp = a.m_part + row * SS;
     const float* lp = a.l_part + row * SS;
     const float* op = a.o_part + row * (int64_t)SS * D;
-    uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + row * D;
+    // Row (b, n1, i) = (b * Q_N + n1) * Q_S + i; in BSND its output is at
+    // ((b * Q_S + i) * Q_N + n1) * D (the same place when Q_S == 1).
+    int64_t orow = row;
+    if (a.out_bsnd && a.q_seq > 1) {
+        const int64_t i = row % a.q_seq, bn = row / a.q_seq;
+        orow = ((bn / a.num_heads) * a.q_seq + i) * a.num_heads + bn % a.num_heads;
+    }
+    uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + orow * D;
 
     // Loads that need nothing else first: slot t's m and l, and this thread's
     // first kCombinePreload partial outputs.  Indexes past the row's slots

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2))) v
     const int64_t blk = blockIdx.x;
     const int g = a.group;
     int64_t split, b, c0, c1;
-    int n2;
+    int n2, rg = 0;
     if (a.bal_nwg > 0) {
         // Length-balanced pieces: tstar tiles each, cut at the batch's length.
         const int64_t tstar = bal_tstar(a.lens, a.batch, a.kv_seq, a.num_kv_heads, a.bal_nwg);
@@ -70,8 +70,16 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2))) v
         c1 = c0 + tstar * 64;
         if (c1 > L) c1 = L;
     } else {
-        split = blk % a.num_splits;
-        const int64_t unit = blk / a.num_splits;
+        // With several row groups, the groups of one chunk are dispatched to
+        // one XCD (its L2 then serves their shared K/V reads).
+        int64_t lb = blk;
+        if (a.row_groups > 1) {
+            lb = xcd_remap(blk, (int64_t)gridDim.x);
+            rg = (int)(lb % a.row_groups);
+            lb /= a.row_groups;
+        }
+        split = lb % a.num_splits;
+        const int64_t unit = lb / a.num_splits;
         n2 = (int)(unit % a.num_kv_heads);
         b = unit / a.num_kv_heads;
         int64_t L = a.kv_seq;
@@ -92,16 +100,44 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2))) v
     c0 = uni64(c0);
     c1 = uni64(c1);
     n2 = __builtin_amdgcn_readfirstlane(n2);
+    rg = __builtin_amdgcn_readfirstlane(rg);
+
+    // Tile row col is row r = 32 * rg + col of the KV head's g * Q_S rows,
+    // head h = r / Q_S of the group at query position qi = r % Q_S.  Rows at
+    // or past the batch's used positions exist (their outputs are written, as
+    // empty) but see no key.
+    const int QS = (int)a.q_seq;
+    const int nrows = g * QS;
+    const int used = a.used_q ? min(max(a.used_q[b], 0), QS) : QS;
+    int64_t kv_hi = a.kv_seq;  // keys any live row of the batch can see, from the masks
+    if (a.mask_mode == 1 && kv_hi > used) kv_hi = used;
+    if (a.mask_mode == 3 && kv_hi > (int64_t)used + a.win_right) kv_hi = (int64_t)used + a.win_right;
+    if (used == 0) kv_hi = 0;
+    kv_hi = uni64(kv_hi);
+    if (c1 > kv_hi) c1 = kv_hi;
+
+    // Output row (b, n1, i) of tile row t of this row group, and where its
+    // output starts in the q layout.
+    auto out_row = [&](int t) __attribute__((always_inline)) {
+        const int r = 32 * rg + t;
+        return ((b * a.num_heads + (int64_t)n2 * g + r / QS) * a.q_seq + r % QS);
+    };
+    auto out_elem = [&](int t) __attribute__((always_inline)) {
+        const int r = 32 * rg + t;
+        return b * a.q_stride_b + ((int64_t)n2 * g + r / QS) * a.q_stride_n + (int64_t)(r % QS) * a.q_stride_s;
+    };
+    const int tile_rows = min(32, nrows - 32 * rg);  // rows of this row group
 
     if (c1 <= c0) {
-        // A chunk at or past the length: its empty partial (or the row
-        // defaults of a one-split plan) without touching K or V.
-        for (int idx = tid; idx < g * D; idx += NT) {
+        // A chunk at or past the length (or the masks' reach): its empty
+        // partial (or the row defaults of a one-split plan) without touching
+        // K or V.
+        for (int idx = tid; idx < tile_rows * D; idx += NT) {
             const int h = idx / D;
             const int d = idx % D;
-            const int64_t row = b * a.num_heads + (int64_t)n2 * g + h;
+            const int64_t row = out_row(h);
             if constexpr (FINISH) {
-                reinterpret_cast<uint16_t*>(a.out)[row * D + d] = 0;
+                reinterpret_cast<uint16_t*>(a.out)[out_elem(h) + d] = 0;
                 if (d == 0 && a.lse) a.lse[row] = kPosInf;
             } else {
                 const int64_t slot = row * a.num_splits + split;
@@ -118,20 +154,30 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2))) v
     // Q^T as the B operand: lane (col, half) holds head n2*g + col, head-dim
     // elements [16*kk + 8*half, +8).  A negative scale flips the sign bits so
     // the scores are scaled by |scale| * log2(e) > 0.
-    const bool qvalid = col < g;
+    const int my_r = 32 * rg + col;
+    const bool qexists = col < tile_rows;          // a row of the KV head (written)
+    const int my_h = my_r / QS, my_i = my_r % QS;  // its head in the group and query position
+    const bool qvalid = qexists && my_i < used;    // it sees keys
     const float c = fabsf(a.scale_log2);
     V8 qreg[D / 16];
     {
-        const uint16_t* qp = a.q + (b * a.num_heads + (int64_t)n2 * g + col) * D;
+        const uint16_t* qp = a.q + b * a.q_stride_b + ((int64_t)n2 * g + my_h) * a.q_stride_n + (int64_t)my_i * a.q_stride_s;
         const uint32_t flip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
             u32x4 w = u32x4{0u, 0u, 0u, 0u};
-            if (qvalid) w = ld128(qp + kk * 16 + 8 * half);
+            if (qvalid && !a.zero_q) w = ld128(qp + kk * 16 + 8 * half);
             w ^= flip;
             qreg[kk] = __builtin_bit_cast(V8, w);
         }
     }
+    // Masking beyond the chunk's end: wave-uniform flags.  A row group with
+    // rows that see no key masks them on every tile.
+    const bool dead_rows = __any(qexists && !qvalid);
+    const int mmode = a.mask_mode;
+    const uint8_t* mrow = a.mask + b * a.mask_stride[0] + ((int64_t)n2 * g + my_h) * a.mask_stride[1] +
+                          (int64_t)my_i * a.mask_stride[2];
+    const int64_t mst = a.mask_stride[3];
 
     f32x16 o[D / 32];
 #pragma unroll
@@ -261,6 +307,30 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2))) v
     auto step = [&](int jt, const unsigned char* Kb, const unsigned char* Vb, unsigned char* nK,
                     unsigned char* nV) __attribute__((always_inline)) {
         if (jt + 1 < ntiles) issue_tile(jt + 1, nK, nV);
+        // Boolean mask: bit r set when key r of this lane's (row, 16 keys) is
+        // masked; loaded before the products so the loads are in flight
+        // meanwhile.  Keys past the chunk are not read.
+        uint32_t mbits = 0u;
+        if (mmode == 2 && qvalid) {
+            const int64_t kb = c0 + (int64_t)jt * BN + 32 * wave + 4 * half;
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int64_t j = kb + 8 * q4;
+                if (a.mask_dword) {
+                    if (j < c1) {
+                        const uint32_t w = *reinterpret_cast<const uint32_t*>(mrow + j);
+                        mbits |= ((w & 0xffu) ? 1u : 0u) << (4 * q4);
+                        mbits |= ((w & 0xff00u) ? 1u : 0u) << (4 * q4 + 1);
+                        mbits |= ((w & 0xff0000u) ? 1u : 0u) << (4 * q4 + 2);
+                        mbits |= ((w & 0xff000000u) ? 1u : 0u) << (4 * q4 + 3);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (j + e < c1 && mrow[(j + e) * mst] != 0) mbits |= 1u << (4 * q4 + e);
+                }
+            }
+        }
         // S^T: keys 32*wave + [0, 32) of the tile x the 32 head rows.
         f32x16 s;
 #pragma unroll
@@ -273,11 +343,16 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2))) v
         }
         // Register r holds key 32*wave + 8*(r/4) + 4*half + r%4 of the tile.
         const int64_t kt0 = (int64_t)jt * BN + 32 * wave;
-        if (kt0 + 32 > nkeys) {
+        if (kt0 + 32 > nkeys || mmode != 0 || dead_rows) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t key = kt0 + 8 * (r >> 2) + 4 * half + (r & 3);
-                s[r] = key < nkeys ? s[r] : kNegInf;
+                const int64_t j = c0 + key;  // absolute key index
+                bool ok = key < nkeys && qvalid;
+                if (mmode == 1) ok = ok && j <= my_i;
+                if (mmode == 3) ok = ok && j >= (int64_t)my_i - a.win_left && j <= (int64_t)my_i + a.win_right;
+                if (mmode == 2) ok = ok && ((mbits >> r) & 1u) == 0u;
+                s[r] = ok ? s[r] : kNegInf;
             }
         }
         {
@@ -350,12 +425,12 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
                 for (int r = 0; r < 16; ++r) o[dt][r] *= f;
         }
-        if (qvalid) {
-            const int64_t row = b * a.num_heads + (int64_t)n2 * g + col;
+        if (qexists) {
+            const int64_t row = out_row(col);
             const bool empty = (tm == kNegInf);
             if constexpr (FINISH) {
                 const float inv = empty ? 0.f : 1.f / l_run;
-                uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + row * D;
+                uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + out_elem(col);
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -416,7 +491,7 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2))) v
             s_l[wave][col] = l_run;
         }
         __syncthreads();
-        for (int idx = tid; idx < g * D; idx += NT) {
+        for (int idx = tid; idx < tile_rows * D; idx += NT) {
             const int h = idx / D;
             const int d = idx % D;
             const float m0 = s_m[0][h], m1 = s_m[1][h];
@@ -425,10 +500,10 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2))) v
             const float f0 = fast_exp2(m0 - ms), f1 = fast_exp2(m1 - ms);
             const float A = __builtin_fmaf(s_o1[h * D + d], f1, s_o0[h * D + d] * f0);
             const float Lt = __builtin_fmaf(s_l[1][h], f1, s_l[0][h] * f0);
-            const int64_t row = b * a.num_heads + (int64_t)n2 * g + h;
+            const int64_t row = out_row(h);
             if constexpr (FINISH) {
                 const bool empty = (Mx == kNegInf);
-                reinterpret_cast<uint16_t*>(a.out)[row * D + d] = to_bits<ST>(empty ? 0.f : A / Lt);
+                reinterpret_cast<uint16_t*>(a.out)[out_elem(h) + d] = to_bits<ST>(empty ? 0.f : A / Lt);
                 if (d == 0 && a.lse) a.lse[row] = empty ? kPosInf : (Mx + log2f(Lt)) * kLn2;
             } else {
                 const int64_t slot = row * a.num_splits + split;
@@ -493,8 +568,11 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, bool
     if (waves != 1 && waves != 2) return hipErrorInvalidValue;
     if (a.block_table && (a.block_size < 16 || a.block_size % 16 != 0)) return hipErrorInvalidValue;
     if (a.bal_nwg > 0 && (finish || !a.lens || a.batch != batch)) return hipErrorInvalidValue;
+    if (a.row_groups < 1 || a.row_groups > 4 || a.group * a.q_seq > 32 * a.row_groups) return hipErrorInvalidValue;
+    if (a.bal_nwg > 0 && (a.row_groups != 1 || a.q_seq != 1 || a.mask_mode != 0 || a.used_q))
+        return hipErrorInvalidValue;
     const int64_t blocks = a.bal_nwg > 0 ? (int64_t)a.bal_nwg + batch * a.num_kv_heads
-                                         : (int64_t)a.num_splits * batch * a.num_kv_heads;
+                                         : (int64_t)a.num_splits * batch * a.num_kv_heads * a.row_groups;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (dtype == 1) {

@@ -45,15 +45,32 @@ struct DecodeArgs {
     // slot count per row of the partials.
     int32_t bal_nwg;
     int32_t batch;            // B (read by the balanced schedule)
+    // Query positions and masks (matrix-core stage 1 only; zero / null for
+    // one query position without a mask).  Partial and output rows are
+    // (b, n1, i) = (b * Q_N + n1) * q_seq + i; the g * q_seq rows of a KV head
+    // (head-major: h * q_seq + i) fill row_groups tiles of 32 rows.
+    int64_t q_seq;            // Q_S >= 1
+    int64_t q_stride_s, q_stride_n, q_stride_b;  // elements, q and out
+    int32_t row_groups;       // ceil(group * q_seq / 32), 1..4
+    int32_t out_bsnd;         // out rows in BSND order (else BNSD)
+    const int32_t* used_q;    // [B] query positions in use (seqused_q), or null
+    int32_t mask_mode;        // 0 none, 1 causal, 2 boolean tensor, 3 window
+    int32_t mask_dword;       // boolean mask read 4 keys per load (aligned, key stride 1)
+    const uint8_t* mask;
+    int64_t mask_stride[4];   // (b, n1, i, j) element strides, 0 broadcasts
+    int32_t win_left, win_right;  // window bounds, 0x7fffffff = unbounded
+    int32_t zero_q;           // scale underflows to 0 in fp32: every score is 0
 };
 
 struct CombineArgs {
     const float* o_part;
     const float* m_part;
     const float* l_part;
-    void* out;                // [B][Q_N][D]
-    float* lse;               // [B][Q_N] or null
-    int64_t rows;             // B * Q_N
+    void* out;                // shape of q: row (b, n1, i) at ((b*Q_N+n1)*Q_S+i)*D (BNSD) or ((b*Q_S+i)*Q_N+n1)*D (BSND)
+    float* lse;               // [B][Q_N][Q_S] or null
+    int64_t rows;             // B * Q_N * Q_S
+    int64_t q_seq;            // Q_S
+    int32_t out_bsnd;
     int32_t num_splits;       // slots per row
     // Length-balanced plan (bal_nwg > 0): row (b, n1) holds the pieces of
     // batch b only, their count computed as the stage-1 kernel did.
@@ -81,6 +98,7 @@ struct PrefillArgs {
     float scale_log2;
     int32_t win_left;         // window mask: keys qrow - win_left .. qrow + win_right kept;
     int32_t win_right;        // 0x7fffffff = unbounded on that side
+    int32_t zero_q;           // scale underflows to 0 in fp32: q is read as zeros (every score 0)
     // Packed layout (work != null): sequence b spans q rows [cu_q[b], cu_q[b+1])
     // and kv rows [cu_kv[b], cu_kv[b+1]) of the [T][N][D] tensors; q_seq and
     // kv_seq are the totals.  The work list holds (sequence, 128-row q tile)

@@ -139,6 +139,10 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
         kv_off = b * a.kv_stride_b;
         lse_row0 = (b * a.num_heads + n1) * a.q_seq;
         lse_step = 1;
+        if (a.used_q) {  // rows at or past the batch's used positions: written as 0 / +inf
+            const int64_t u = a.used_q[b];
+            q_used = u < 0 ? 0 : (u > a.q_seq ? a.q_seq : u);
+        }
     }
     const int n2 = n1 / a.group;
 
@@ -158,7 +162,7 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
             u32x4 w = u32x4{0u, 0u, 0u, 0u};
-            if (qvalid) w = ld128(qp + kk * 16 + 8 * half);
+            if (qvalid && !a.zero_q) w = ld128(qp + kk * 16 + 8 * half);  // zero_q: scale 0
             w ^= flip;
             qreg[kk] = __builtin_bit_cast(V8, w);
         }
@@ -178,6 +182,7 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
         if (key_lo > 0) jt0 = (int)(key_lo / BN);
     }
     int ntiles = (int)((kv_end + BN - 1) / BN);
+    if (i0 >= q_used) ntiles = jt0;  // no row of the tile is used: outputs only
 
     // MASK 3 with a summary of the mask: the row of tile classes of this
     // query tile (two bits per KV tile: some key visible, some key masked).
@@ -574,7 +579,11 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
         L = a.lens[b];
         L = L < 0 ? 0 : (L > a.kv_seq ? a.kv_seq : L);
     }
-    const int64_t q_used = a.q_seq;
+    int64_t q_used = a.q_seq;
+    if (a.used_q) {  // rows at or past the batch's used positions: written as 0 / +inf
+        const int64_t u = a.used_q[b];
+        q_used = u < 0 ? 0 : (u > a.q_seq ? a.q_seq : u);
+    }
     const int64_t q_off = b * a.q_stride_b, kv_off = b * a.kv_stride_b;
     const int64_t lse_row0 = (b * a.num_heads + n1) * a.q_seq;
     const int n2 = n1 / a.group;
@@ -590,13 +599,13 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
             u32x4 w = u32x4{0u, 0u, 0u, 0u};
-            if (qvalid) w = ld128(qp + kk * 16 + 8 * half);
+            if (qvalid && !a.zero_q) w = ld128(qp + kk * 16 + 8 * half);  // zero_q: scale 0
             w ^= flip;
             qreg[kk] = __builtin_bit_cast(V8, w);
         }
     }
     const float c = a.scale_log2;
-    const int nt = (int)((L + BN - 1) / BN);  // KV tiles
+    const int nt = (i0 >= q_used) ? 0 : (int)((L + BN - 1) / BN);  // KV tiles (none when no row is used)
 
     f32x16 o[D / 32];
 #pragma unroll
@@ -894,8 +903,8 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
     }
 
     const float l_run = l_half + xor32(l_half);
-    if (qvalid) {
-        const bool empty = (m_run == kNegInf);
+    if (qrow < a.q_seq) {
+        const bool empty = !qvalid || (m_run == kNegInf);
         const float inv = empty ? 0.f : 1.f / l_run;
         uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + q_off + (int64_t)n1 * a.q_stride_n + qrow * a.q_stride_s;
 #pragma unroll

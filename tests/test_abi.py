@@ -75,9 +75,15 @@ def test_fwd_rejects_null_and_misaligned_tensors(lib):
 
 
 def test_decode_entry_points_validate(lib):
-    p = params(q_seq=2)
+    # several query positions: built for head_dim 64 / 128 (head_dim 256 is refused
+    # before anything is launched)
+    p = params(q_seq=2, head_dim=256)
     st = lib.fa_decode_splitkv(ctypes.byref(p), 32, 4096, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
-    assert st == fa.FA_ERR_PARAM_INVALID and "q_seq == 1" in fa.fa_last_error()
+    assert st == fa.FA_ERR_UNSUPPORTED and "several query positions" in fa.fa_last_error()
+    # more than 128 (query head, position) rows per KV head
+    p = params(q_seq=5, num_heads=32, num_kv_heads=1)
+    st = lib.fa_decode_splitkv(ctypes.byref(p), 32, 4096, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == fa.FA_ERR_UNSUPPORTED
     p = params()
     st = lib.fa_decode_splitkv(ctypes.byref(p), 31, 4096, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
     assert st == fa.FA_ERR_PARAM_INVALID and "cover" in fa.fa_last_error()
@@ -85,9 +91,14 @@ def test_decode_entry_points_validate(lib):
     assert st == fa.FA_ERR_PARAM_INVALID and "multiple of 64" in fa.fa_last_error()
     st = lib.fa_decode_splitkv(ctypes.byref(p), 32, 4096, FAKE, FAKE, FAKE, None, FAKE, FAKE, None)
     assert st == fa.FA_ERR_NULLPTR
-    pm = params(mask_mode="causal")
+    pm = params(mask_mode="causal", head_dim=256)
     st = lib.fa_decode_splitkv(ctypes.byref(pm), 32, 4096, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
-    assert st == fa.FA_ERR_PARAM_INVALID
+    assert st == fa.FA_ERR_UNSUPPORTED
+    # o_part is read and written as 16-byte vectors
+    st = lib.fa_decode_splitkv(ctypes.byref(p), 32, 4096, FAKE, FAKE, FAKE, FAKE + 4, FAKE, FAKE, None)
+    assert st == fa.FA_ERR_PARAM_INVALID and "16-byte" in fa.fa_last_error()
+    st = lib.fa_combine(ctypes.byref(p), 32, FAKE + 4, FAKE, FAKE, FAKE, None, None)
+    assert st == fa.FA_ERR_PARAM_INVALID and "16-byte" in fa.fa_last_error()
     st = lib.fa_combine(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, None, None)
     assert st == fa.FA_ERR_PARAM_INVALID
     st = lib.fa_combine(ctypes.byref(p), 4, FAKE, FAKE, FAKE, None, None, None)
@@ -118,8 +129,60 @@ def test_split_plan_honours_chunk_hint(lib):
 
 
 def test_prefill_needs_no_workspace(lib):
-    assert fa.fa_workspace_size(params(q_seq=128)) == 0
-    assert fa.fa_workspace_size(params(q_seq=1, mask_mode="causal")) == 0
+    assert fa.fa_workspace_size(params(q_seq=128, batch=8)) == 0
+    # head_dim 256 with a mask: the prefill kernel, no workspace
+    assert fa.fa_workspace_size(params(q_seq=1, mask_mode="causal", head_dim=256)) == 0
+
+
+def test_split_path_routing_and_workspace(lib):
+    # masked decode, decode with used lengths, and a few query positions against a
+    # long cache take the split-KV path: partials for every (b, n1, i) row
+    for kw in (dict(q_seq=1, mask_mode="causal"), dict(q_seq=1, seqused_q=FAKE),
+               dict(q_seq=8, num_heads=32, num_kv_heads=8, kv_seq=65536),
+               dict(q_seq=1, mask_mode="window", win_left=100, win_right=0)):
+        p = params(**kw)
+        sp, ch, ws = fa.fa_splitkv_plan(p, num_cus=256)
+        assert sp > 1 and sp * ch >= p.kv_seq
+        rows = p.batch * p.num_heads * p.q_seq
+        assert ws >= rows * sp * (p.head_dim + 2) * 4
+        assert fa.fa_workspace_size(p) > 0
+    # row groups count as units of the plan: 8 heads x 4 positions of one KV head
+    # fill one 32-row tile, x 8 positions two tiles, which need half the splits
+    one = fa.fa_splitkv_plan(params(q_seq=4, num_heads=8, num_kv_heads=1, kv_seq=1 << 20), num_cus=256)
+    two = fa.fa_splitkv_plan(params(q_seq=8, num_heads=8, num_kv_heads=1, kv_seq=1 << 20), num_cus=256)
+    assert two[0] < one[0] and two[0] * 2 >= one[0] - 2
+    # enough query tiles to fill the CUs: the prefill kernel (no workspace)
+    assert fa.fa_workspace_size(params(q_seq=8, batch=64, num_heads=32, kv_seq=65536)) == 0
+
+
+def test_window_bounds_and_scale_validated(lib):
+    # developer guide 1.5: without the window mode both bounds are -1
+    for kw in (dict(win_left=0), dict(win_right=5), dict(mask_mode="causal", win_left=3)):
+        p = params(**kw)
+        assert lib.fa_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == fa.FA_ERR_PARAM_INVALID
+        assert "-1 outside the window mode" in fa.fa_last_error()
+    # scale * log2(e) must stay finite in fp32
+    p = params(scale=1e39)
+    assert lib.fa_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == fa.FA_ERR_PARAM_INVALID
+    assert "scale" in fa.fa_last_error()
+    # cu_seqlens stay TND-only; seqused_q is accepted in every layout
+    p = params(cu_seqlens_q=FAKE)
+    assert lib.fa_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == fa.FA_ERR_PARAM_INVALID
+    assert fa.fa_workspace_size(params(q_seq=64, batch=64, seqused_q=FAKE)) == 0
+
+
+def test_fused_plan_stays_within_the_fused_merge(lib):
+    # one batch, one KV head: the matrix-core plan asks for hundreds of splits, the
+    # fused launch takes at most 256 (its chunk grows instead)
+    p = params(num_heads=8, num_kv_heads=1, kv_seq=131072)
+    assert fa.fa_splitkv_plan(p, num_cus=256)[0] > 256
+    sp, ch, ws = fa.fa_decode_fused_plan(p, num_cus=256)
+    assert 1 <= sp <= 256 and sp * ch >= p.kv_seq and ch % 64 == 0
+    assert ws >= p.batch * p.num_heads * sp * (p.head_dim + 2) * 4
+    sp, ch, _ = fa.fa_decode_fused_plan(params(), num_cus=256)
+    assert sp <= 256 and sp * ch >= 131072
+    with pytest.raises(fa.FaError):
+        fa.fa_decode_fused_plan(params(mask_mode="causal"), num_cus=256)
 
 
 # ---------------------------------------------------------------- paged KV cache
@@ -141,8 +204,9 @@ def paged(**kw):
     (dict(max_blocks_per_seq=0), fa.FA_ERR_PARAM_INVALID, "max_blocks_per_seq"),
     (dict(num_blocks=0), fa.FA_ERR_PARAM_INVALID, "num_blocks"),
     (dict(max_blocks_per_seq=1023), fa.FA_ERR_PARAM_INVALID, "exceeds"),    # 1023*128 < 131072
-    (dict(q_seq=16), fa.FA_ERR_UNSUPPORTED, "decode only"),
-    (dict(mask_mode="causal"), fa.FA_ERR_UNSUPPORTED, "decode only"),
+    (dict(q_seq=16, head_dim=256), fa.FA_ERR_UNSUPPORTED, "split-KV paths"),
+    (dict(mask_mode="causal", head_dim=256), fa.FA_ERR_UNSUPPORTED, "split-KV paths"),
+    (dict(q_seq=200), fa.FA_ERR_UNSUPPORTED, "split-KV paths"),
     (dict(kv_layout="contiguous"), fa.FA_ERR_PARAM_INVALID, "contiguous"),  # table without paging
 ])
 def test_paged_params_validated(lib, kw, status, text):
@@ -267,7 +331,7 @@ def test_fused_decode_validates(lib):
     assert st == fa.FA_ERR_PARAM_INVALID and "cover" in fa.fa_last_error()
     pq = params(q_seq=4)
     st = lib.fa_decode_fused(ctypes.byref(pq), 32, 4096, FAKE, FAKE, FAKE, FAKE, 1 << 30, FAKE, None, None)
-    assert st == fa.FA_ERR_PARAM_INVALID
+    assert st == fa.FA_ERR_UNSUPPORTED
 
 
 def test_noalloc_rejects_calls_beyond_its_scratch(lib):
@@ -283,3 +347,29 @@ def test_noalloc_rejects_calls_beyond_its_scratch(lib):
     # validation errors come first, as for fa_fwd
     bad = params(head_dim=100)
     assert lib.fa_fwd_noalloc(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, None, None) == fa.FA_ERR_PARAM_INVALID
+
+
+def test_params_keep_the_tensors_they_point_to_alive():
+    """FaParams holds raw addresses; the tensors behind them must outlive a
+    temporary passed straight into params_for (else the allocator hands their
+    memory to the next tensor and the kernels read that instead)."""
+    import gc
+    import weakref
+    torch = pytest.importorskip("torch")
+    q = torch.zeros((2, 1, 4, 64), dtype=torch.bfloat16)
+    k = torch.zeros((8, 16, 2, 64), dtype=torch.bfloat16)
+    refs = []
+
+    def tmp(*shape):
+        t = torch.zeros(shape, dtype=torch.int32)
+        refs.append(weakref.ref(t))
+        return t
+
+    p = fa.params_for(q, k, layout="BSND", actual_seq_lengths=tmp(2), kv_layout="PA_BBND",
+                      block_table=tmp(2, 4), seqused_q=tmp(2))
+    gc.collect()
+    assert all(r() is not None for r in refs)
+    assert p.block_table == refs[1]().data_ptr()
+    del p
+    gc.collect()
+    assert all(r() is None for r in refs)

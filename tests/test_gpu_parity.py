@@ -6,6 +6,7 @@ exactly 0 with lse = +inf; no NaN anywhere.  Stage-1 partials of the split-KV
 decode: m within 1e-3 absolute, l and O within 2e-3 of the oracle's partials
 relative to the partial's own scale.
 """
+import dataclasses
 import functools
 import math
 
@@ -925,3 +926,231 @@ def test_seeded_shape_sweep(seed):
     r_rows = np.ascontiguousarray(ref if s.layout == "BNSD" else ref.transpose(0, 2, 1, 3))
     check(rows_of(out, s, np.arange(s.B * s.QN)), to_np(lse).reshape(-1),
           r_rows.reshape(-1, s.D), ref_lse.reshape(-1), f"sweep {seed} paged {paged}: {case}")
+
+
+# ------------------------------------------------------------------ split-KV, general rows
+# Masked decode (IFA guide 4: attenMask (B,N,1,S) or (1,N,1,S) / (B,1,1,S)), used query
+# lengths, and a few query positions against a long cache run stage 1 on the matrix
+# cores with the rows (query head, position) of a KV head in 32-row tiles, then the
+# combine (FlashAttn developer guide 1.9 and 4).
+
+def _mask_for(s, kind, seed, all_masked=None):
+    """A uint8 mask (nonzero = excluded) and its (b, n, i, j) strides.
+    kind: "b11s" (B,1,1,S) broadcast over heads and positions, "bn1s" (B,N,1,S),
+    "bnqs" (B,N,Q_S,S), "bqs_odd" (B,1,Q_S,S+3) rows with an odd pitch (byte reads)."""
+    rng = np.random.default_rng(seed)
+    if kind == "b11s":
+        m = (rng.random((s.B, 1, 1, s.KVS)) < 0.4).astype(np.uint8)
+        st = (s.KVS, 0, 0, 1)
+    elif kind == "bn1s":
+        m = (rng.random((s.B, s.QN, 1, s.KVS)) < 0.5).astype(np.uint8)
+        st = (s.QN * s.KVS, s.KVS, 0, 1)
+    elif kind == "bnqs":
+        m = (rng.random((s.B, s.QN, s.QS, s.KVS)) < 0.3).astype(np.uint8)
+        st = (s.QN * s.QS * s.KVS, s.QS * s.KVS, s.KVS, 1)
+    else:
+        pitch = s.KVS + 3
+        m = (rng.random((s.B, 1, s.QS, pitch)) < 0.3).astype(np.uint8)
+        st = (s.QS * pitch, 0, pitch, 1)
+    if all_masked is not None:  # one batch masks every key of every row
+        m[all_masked] = 1
+    return np.ascontiguousarray(m), st
+
+
+def run_general(inp, *, mask=None, mask_strides=(0, 0, 0, 0), causal=False, window=None,
+                seqused=None, paging=None, scale=None):
+    """fa.fwd on the inputs; returns (out rows [nrows, D] fp64, lse rows, oracle Problem)."""
+    s = inp.spec
+    sc = s.softmax_scale if scale is None else scale
+    q = dev16(inp.q, s.dtype)
+    lens_np = inp.lens
+    if paging is not None and lens_np is None:
+        lens_np = np.full(s.B, s.KVS, dtype=np.int64)
+    lens = None if lens_np is None else torch.from_numpy(lens_np).to(DEV)
+    kw = {}
+    if paging is None:
+        k, v = dev16(inp.k, s.dtype), dev16(inp.v, s.dtype)
+    else:
+        inp2 = dataclasses.replace(inp, lens=lens_np)
+        kp, vp, table, nblocks = fa_synth.to_paged(inp2, paging[1], paging[0], seed=3)
+        k, v = dev16(kp, s.dtype), dev16(vp, s.dtype)
+        kw = dict(kv_layout=paging[0], block_table=torch.from_numpy(table).to(DEV))
+    mask_t = None if mask is None else torch.from_numpy(mask).to(DEV)
+    su = None if seqused is None else torch.from_numpy(np.asarray(seqused, np.int32)).to(DEV)
+    out, lse = fa.fwd(q, k, v, layout=s.layout, scale=sc, actual_seq_lengths=lens, mask=mask_t,
+                      mask_stride=mask_strides, causal=causal, window=window, seqused_q=su,
+                      return_lse=True, **kw)
+    torch.cuda.synchronize()
+    mode = "bool" if mask is not None else ("causal" if causal else ("window" if window else "none"))
+    prob = oracle.Problem(s.B, s.QN, s.KVN, s.QS, s.KVS, s.D, s.layout, s.dtype, sc, lens_np, mode,
+                          mask, mask_strides, window=window if window else (-1, -1), seqused_q=seqused)
+    return rows_of(out, s, np.arange(s.B * s.QN * s.QS)), to_np(lse).reshape(-1), prob
+
+
+GENERAL_CASES = [
+    # one query position with a boolean mask: broadcast over heads, and per head, with
+    # one batch fully masked (its rows are 0 / +inf); g = 1 and g = 4; both layouts
+    (dict(B=3, QN=8, KVN=2, QS=1, KVS=5000, D=128, lens=(1, 5000)), dict(mask="b11s", all_masked=1)),
+    (dict(B=2, QN=4, KVN=4, QS=1, KVS=3000, D=64, layout="BSND"), dict(mask="bn1s", all_masked=0)),
+    (dict(B=2, QN=32, KVN=1, QS=1, KVS=2000, D=128, dtype="f16", lens=(100, 2000)), dict(mask="bn1s")),
+    (dict(B=1, QN=2, KVN=2, QS=1, KVS=777, D=128), dict(mask="bqs_odd")),          # byte-wise mask reads
+    # one query position, causal (top-left: key 0 only) and window
+    (dict(B=2, QN=8, KVN=2, QS=1, KVS=3000, D=128, lens=(1, 3000)), dict(causal=True)),
+    (dict(B=2, QN=8, KVN=8, QS=1, KVS=3000, D=128, layout="BSND"), dict(window=(0, 700))),
+    # used query lengths with one position: batch 1 uses none
+    (dict(B=3, QN=8, KVN=2, QS=1, KVS=2500, D=128, lens=(1, 2500)), dict(seqused=[1, 0, 5])),
+    # a few positions against a long cache: no mask, causal, boolean (B,N,Q_S,S)
+    (dict(B=1, QN=32, KVN=8, QS=8, KVS=65536, D=128), dict()),
+    (dict(B=1, QN=32, KVN=8, QS=8, KVS=65536, D=128, layout="BSND"), dict(causal=True)),
+    (dict(B=2, QN=8, KVN=2, QS=5, KVS=9000, D=64, lens=(3000, 9000)), dict(mask="bnqs")),
+    # four row groups (g * Q_S = 128), three (g * Q_S = 72) and odd counts
+    (dict(B=1, QN=16, KVN=2, QS=16, KVS=20000, D=128, layout="BSND"), dict()),
+    (dict(B=2, QN=24, KVN=3, QS=9, KVS=7000, D=64, dtype="f16", lens=(1, 7000)), dict(window=(40, 2))),
+    (dict(B=1, QN=3, KVN=1, QS=3, KVS=4000, D=128), dict(seqused=[2])),
+    # negative scale
+    (dict(B=1, QN=8, KVN=2, QS=4, KVS=6000, D=128, scale=-0.07), dict(mask="b11s")),
+]
+
+
+@pytest.mark.parametrize("case,opts", GENERAL_CASES,
+                         ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()) if isinstance(c, dict) else str(c))
+def test_general_split_matches_oracle(case, opts):
+    inp = fa_synth.make(spec(seed=151, **case))
+    s = inp.spec
+    o = dict(opts)
+    mask, strides = None, (0, 0, 0, 0)
+    if "mask" in o:
+        mask, strides = _mask_for(s, o.pop("mask"), 152, o.pop("all_masked", None))
+    p = fa.params_for(dev16(inp.q, s.dtype), dev16(inp.k, s.dtype), layout=s.layout,
+                      scale=s.softmax_scale, causal=o.get("causal", False), window=o.get("window"),
+                      mask=None if mask is None else torch.zeros(1, dtype=torch.uint8, device=DEV),
+                      mask_stride=strides,
+                      seqused_q=None if "seqused" not in o else torch.zeros(s.B, dtype=torch.int32, device=DEV))
+    assert fa.fa_workspace_size(p) > 0, "expected the split-KV path"
+    got, got_lse, prob = run_general(inp, mask=mask, mask_strides=strides, **o)
+    ref, ref_lse = oracle.attention_rows(prob, inp.q, inp.k, inp.v)
+    check(got, got_lse, ref, ref_lse, f"general split {case} {opts}")
+
+
+def test_general_split_ignores_nan_padding():
+    """Keys past each batch's length hold NaN: outputs are bit-identical (masked decode)."""
+    inp = fa_synth.make(spec(layout="BSND", B=3, QN=8, KVN=2, QS=1, KVS=3000, lens=(0, 3000), seed=153))
+    mask, st = _mask_for(inp.spec, "b11s", 154)
+    base = run_general(inp, mask=mask, mask_strides=st)
+    pad = fa_synth.fill_padding(inp, fa_synth.NAN_BITS["bf16"])
+    again = run_general(pad, mask=mask, mask_strides=st)
+    assert np.array_equal(base[0], again[0]) and np.array_equal(base[1], again[1])
+
+
+@pytest.mark.parametrize("paging", [("PA_BBND", 64), ("PA_BNBD", 16)])
+def test_general_split_on_paged_cache(paging):
+    """A boolean mask and several positions on a paged cache: equal to the oracle, and bit
+    for bit to the same call on the contiguous cache."""
+    inp = fa_synth.make(spec(B=2, QN=8, KVN=2, QS=3, KVS=4100, D=128, lens=(1000, 4100), seed=155))
+    mask, st = _mask_for(inp.spec, "bnqs", 156)
+    got, got_lse, prob = run_general(inp, mask=mask, mask_strides=st, paging=paging)
+    ref, ref_lse = oracle.attention_rows(prob, inp.q, inp.k, inp.v)
+    check(got, got_lse, ref, ref_lse, f"paged general {paging}")
+    base, base_lse, _ = run_general(inp, mask=mask, mask_strides=st)
+    assert np.array_equal(got, base) and np.array_equal(got_lse, base_lse)
+
+
+def test_general_stage1_partials_match_oracle_partials():
+    """fa_decode_splitkv on several positions with a boolean mask: m, l and the unnormalised
+    O of every (row, chunk) against the oracle's partials; fa_combine then gives the
+    oracle's output."""
+    inp = fa_synth.make(spec(B=2, QN=8, KVN=2, QS=4, KVS=3000, D=128, lens=(500, 3000), seed=157))
+    s = inp.spec
+    mask, st = _mask_for(s, "bnqs", 158)
+    q, k, v = (dev16(x, s.dtype) for x in (inp.q, inp.k, inp.v))
+    lens = torch.from_numpy(inp.lens).to(DEV)
+    mt = torch.from_numpy(mask).to(DEV)
+    p = fa.params_for(q, k, layout=s.layout, scale=s.softmax_scale, actual_seq_lengths=lens, mask=mt,
+                      mask_stride=st)
+    splits, chunk = 12, 256
+    rows = s.B * s.QN * s.QS
+    o_part = torch.empty((rows * splits * s.D,), dtype=torch.float32, device=DEV)
+    m_part = torch.empty((rows * splits,), dtype=torch.float32, device=DEV)
+    l_part = torch.empty((rows * splits,), dtype=torch.float32, device=DEV)
+    stream = torch.cuda.current_stream()
+    fa.fa_decode_splitkv(p, splits, chunk, q, k, v, o_part, m_part, l_part, stream)
+    out = torch.empty_like(q)
+    lse = torch.empty((s.B, s.QN, s.QS), dtype=torch.float32, device=DEV)
+    fa.fa_combine(p, splits, o_part, m_part, l_part, out, lse, stream)
+    torch.cuda.synchronize()
+    prob = oracle.Problem(s.B, s.QN, s.KVN, s.QS, s.KVS, s.D, s.layout, s.dtype, s.softmax_scale, inp.lens,
+                          "bool", mask, st)
+    ro, rm, rl = oracle.split_partials(prob, inp.q, inp.k, inp.v, splits, chunk)
+    gm = m_part.cpu().numpy().reshape(rows, splits).astype(np.float64)
+    gl = l_part.cpu().numpy().reshape(rows, splits).astype(np.float64)
+    go = o_part.cpu().numpy().reshape(rows, splits, s.D).astype(np.float64)
+    empty = np.isinf(rm)
+    assert np.array_equal(np.isinf(gm) & (gm < 0), empty), "empty-chunk flags"
+    assert np.all(gl[empty] == 0) and np.all(go[empty] == 0)
+    live = ~empty
+    assert np.abs(gm[live] - rm[live]).max() <= 1e-3
+    # l and O: relative to the partial's own scale, plus the 16-bit rounding of P, whose
+    # bound needs sum_j p_j |v_j|, the partial of the same scores with |V|
+    assert np.all(np.abs(gl[live] - rl[live]) <= 2e-3 * rl[live] + 1e-6)
+    vabs = np.ascontiguousarray(inp.v) & np.uint16(0x7FFF)
+    ro_abs, _, _ = oracle.split_partials(prob, inp.q, inp.k, vabs, splits, chunk)
+    tol = 2e-3 * np.abs(ro).max(axis=2, keepdims=True) + 2.0 ** -8 * ro_abs + 1e-6
+    assert np.all((np.abs(go - ro) <= tol)[live]), "general stage-1 O partials"
+    ref, ref_lse = oracle.attention_rows(prob, inp.q, inp.k, inp.v)
+    check(rows_of(out, s, np.arange(rows)), to_np(lse).reshape(-1), ref, ref_lse, "general combine")
+
+
+@pytest.mark.parametrize("layout,causal", [("BNSD", True), ("BSND", False), ("BNSD", False)])
+def test_prefill_seqused_q_padded_layouts(layout, causal):
+    """seqused_q on BNSD/BSND prefill (developer guide 1.4): rows past each batch's used
+    length are 0 / +inf, the rest match the oracle (tiled kernel when causal, the
+    interleaved kernel for mask-free D = 128, whole query tiles unused included)."""
+    inp = fa_synth.make(spec(layout=layout, B=3, QN=4, KVN=2, QS=600, KVS=700, D=128, lens=(300, 700),
+                             seed=159))
+    got, got_lse, prob = run_general(inp, causal=causal, seqused=[599, 0, 130])
+    ref, ref_lse = oracle.attention_rows(prob, inp.q, inp.k, inp.v)
+    check(got, got_lse, ref, ref_lse, f"prefill seqused {layout} causal={causal}")
+
+
+@pytest.mark.parametrize("case,opts", [
+    (dict(B=1, QN=2, KVN=2, QS=300, KVS=333, D=128), dict()),                       # interleaved prefill
+    (dict(B=2, QN=2, KVN=1, QS=200, KVS=250, D=64, lens=(7, 250)), dict(causal=True)),  # tiled prefill
+    (dict(B=2, QN=4, KVN=4, QS=1, KVS=1000, D=128, lens=(1, 1000)), dict()),        # vector decode
+    (dict(B=2, QN=16, KVN=4, QS=1, KVS=1500, D=128, lens=(1, 1500)), dict()),       # matrix-core decode
+    (dict(B=1, QN=8, KVN=2, QS=3, KVS=900, D=128), dict(mask="b11s")),              # general split
+])
+def test_scale_zero_gives_the_mean_of_visible_values(case, opts):
+    """scale = 0: every score is 0, so each row is the plain mean of the values it sees and
+    lse = ln(count); masked keys and keys past the length must still be excluded."""
+    inp = fa_synth.make(spec(seed=160, **case))
+    s = inp.spec
+    o = dict(opts)
+    mask, st = None, (0, 0, 0, 0)
+    if "mask" in o:
+        mask, st = _mask_for(s, o.pop("mask"), 161)
+    got, got_lse, prob = run_general(inp, mask=mask, mask_strides=st, scale=0.0, **o)
+    assert np.all(np.isfinite(got))
+    ref, ref_lse = oracle.attention_rows(prob, inp.q, inp.k, inp.v)
+    check(got, got_lse, ref, ref_lse, f"scale 0 {case}")
+
+
+@pytest.mark.parametrize("paging,g", [(("PA_BBND", 128), 4), (("PA_BNBD", 48), 4), (("PA_BBND", 128), 2),
+                                      (("PA_BBND", 128), 1), (("PA_BNBD", 64), 8)])
+def test_decode_fused_on_paged_cache(paging, g):
+    """The single-launch split-KV on a paged cache, with the fused plan: equal to the oracle."""
+    inp = fa_synth.make(spec(layout="BSND", B=3, QN=2 * g, KVN=2, QS=1, KVS=5000, lens=(1, 5000), seed=162))
+    s = inp.spec
+    kp, vp, table, nblocks = fa_synth.to_paged(inp, paging[1], paging[0], seed=4)
+    q, k, v = dev16(inp.q, s.dtype), dev16(kp, s.dtype), dev16(vp, s.dtype)
+    lens = torch.from_numpy(inp.lens).to(DEV)
+    p = fa.params_for(q, k, layout=s.layout, scale=s.softmax_scale, actual_seq_lengths=lens,
+                      kv_layout=paging[0], block_table=torch.from_numpy(table).to(DEV))
+    sp, ch, nbytes = fa.fa_decode_fused_plan(p)
+    assert sp > 1
+    ws = torch.zeros((nbytes,), dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(q)
+    lse = torch.empty((s.B, s.QN, 1), dtype=torch.float32, device=DEV)
+    fa.fa_decode_fused(p, sp, ch, q, k, v, ws, nbytes, out, lse, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.attention(oracle.Problem.from_inputs(inp), inp.q, inp.k, inp.v)
+    check(to_np(out), to_np(lse), ref, ref_lse, f"fused paged {paging}")

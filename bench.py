@@ -192,7 +192,8 @@ def main():
            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded N(0,1) bf16, RNE-rounded)"}
-    config = {"workload": "+".join(legs), "parallelism": "single GPU"}
+    config = {"workload": "+".join({"decode": "decode_128k", "prefill": "prefill_4k"}[x] for x in legs),
+              "parallelism": "single GPU"}
     csrc = os.path.join(ROOT, "split_kv_decode_amd", "csrc")
     if dec is not None:
         s1 = median_ms(0, 1)
@@ -236,6 +237,13 @@ def main():
             out["unit"] = "TFLOP/s"
         config.update({"prefill_B": ps.B, "prefill_heads": ps.QN, "prefill_seq": ps.QS})
     out["config"] = config
+    if pre is not None:
+        run = lambda: fa.fa_fwd(pre["p"], pre["q"], pre["k"], pre["v"], pre["out"], pre["lse"], None, 0, stream)
+        out["shader_clock"] = clock_under_load(run, torch, "the prefill_4k kernel")
+    elif dec is not None:
+        run = lambda: fa.fa_decode_splitkv(dec["p"], dec["splits"], dec["chunk"], dec["q"], dec["k"], dec["v"],
+                                           dec["o"], dec["m"], dec["l"], stream)
+        out["shader_clock"] = clock_under_load(run, torch, "the decode_128k stage 1")
 
     if dec is not None and not args.no_cpu_baseline:
         import oracle
@@ -250,6 +258,7 @@ def main():
             n += 1
         cpu_gbs = n * (dec["kv_bytes"] + dec["qo_bytes"]) / t_cpu / 1e9
         out["cpu_baseline"] = {"value": round(cpu_gbs, 4), "unit": "GB/s", "cores": threads,
+                               "nproc": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
                                "kind": "oracle",
                                "sample": f"the whole decode_128k workload (32 rows x 131072 keys), "
                                          f"{n} pass(es) in {t_cpu:.1f} s, fp64"}
@@ -257,6 +266,52 @@ def main():
         out["workloads"] = extra_workloads(fa, fa_synth, np, torch, dev16, stream)
     out["setup_s"] = round(t_gen, 1)
     print(json.dumps(out))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def read_sclk_mhz():
+    """Current shader clock from the driver's sysfs DPM table (the line marked '*'), or None."""
+    import glob
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        return float(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0])
+        except (OSError, ValueError, IndexError):
+            continue
+    return None
+
+
+def clock_under_load(fn, torch, what, seconds=0.5):
+    """Shader clock while fn() keeps the GPU busy, read after the timed steps (outside them):
+    batches of launches are queued and the driver's current DPM clock is sampled between them."""
+    if read_sclk_mhz() is None:
+        return {"available": False, "why": "no readable pp_dpm_sclk in /sys/class/drm on this host"}
+    samples = []
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(16):
+            fn()
+        time.sleep(0.002)
+        mhz = read_sclk_mhz()
+        if mhz is not None:
+            samples.append(mhz)
+        torch.cuda.synchronize()
+    samples.sort()
+    return {"available": True, "mhz_median": samples[len(samples) // 2], "mhz_min": samples[0],
+            "mhz_max": samples[-1], "samples": len(samples),
+            "source": f"sysfs pp_dpm_sclk, sampled while {what} ran in an untimed loop after the timed steps"}
 
 
 def timed(fn, torch, np, stream, warmup, iters, flush=None, warm_s=0.25):
@@ -367,12 +422,65 @@ def extra_workloads(fa, fa_synth, np, torch, dev16, stream, warmup=3, iters=20):
         torch.cuda.empty_cache()
     res.update(packed_workload(fa, fa_synth, np, torch, dev16, stream, warmup, iters))
     res.update(fused_decode(fa, fa_synth, np, torch, dev16, stream, warmup, iters, flush))
+    res.update(split_decode_workloads(fa, fa_synth, np, torch, dev16, stream, warmup, iters, flush))
+    return res
+
+
+def split_decode_workloads(fa, fa_synth, np, torch, dev16, stream, warmup, iters, flush):
+    """Query work too small to occupy the chip, which fa_fwd runs as split-KV on the general
+    matrix-core stage 1 (rows = query head x position) plus the combine: one query position
+    under a boolean mask, and eight positions against a 64K cache, without a mask and with a
+    causal band aligned to the cache's end given as a boolean tensor (the top-left causal
+    flag would leave those rows eight keys)."""
+    res = {}
+    rng = np.random.default_rng(1012)
+    S128, S64 = 131072, 65536
+    pad = (rng.random(S128) < 0.125) | (np.arange(S128) >= S128 - 4096)  # dropped keys + a padded tail
+    band = np.arange(S64)[None, :] > (S64 - 8 + np.arange(8))[:, None]   # key j hidden from row i
+    cases = [
+        (fa_synth.Spec("decode_128k_bool_mask", "BNSD", B=1, QN=32, KVN=32, QS=1, KVS=S128, D=128,
+                       dtype="bf16", seed=1003,
+                       doc="decode_128k (BNSD, B=1, N=32, KV_S=131072, D=128, bf16 N(0,1)) with a "
+                           "(B,1,1,S) boolean mask: 1/8 of the keys dropped at random and the last "
+                           "4096 hidden"),
+         pad.astype(np.uint8).reshape(1, S128), (S128, 0, 0, 1)),
+        (fa_synth.Spec("decode_q8_65k", "BSND", B=1, QN=32, KVN=8, QS=8, KVS=S64, D=128, dtype="bf16",
+                       seed=1013, doc="eight query positions, BSND, B=1, Q_N=32, KV_N=8, KV_S=65536, "
+                                      "D=128, bf16 N(0,1), no mask"),
+         None, (0, 0, 0, 0)),
+        (fa_synth.Spec("decode_q8_65k_tail_causal", "BSND", B=1, QN=32, KVN=8, QS=8, KVS=S64, D=128,
+                       dtype="bf16", seed=1013,
+                       doc="eight query positions against KV_S=65536 (BSND, B=1, Q_N=32, KV_N=8, "
+                           "D=128, bf16 N(0,1)) with a (1,1,8,S) boolean mask: row i sees keys "
+                           "j <= S - 8 + i"),
+         band.astype(np.uint8), (8 * S64, 0, S64, 1)),
+    ]
+    for spec, mask_np, strides in cases:
+        inp = fa_synth.make(spec)
+        q, k, v = (dev16(x, spec.dtype) for x in (inp.q, inp.k, inp.v))
+        mask = None if mask_np is None else torch.from_numpy(np.ascontiguousarray(mask_np)).to(q.device)
+        p = fa.params_for(q, k, layout=spec.layout, scale=spec.softmax_scale, mask=mask,
+                          mask_stride=strides)
+        out = torch.empty_like(q)
+        lse = torch.empty((spec.B, spec.QN, spec.QS), dtype=torch.float32, device=q.device)
+        nbytes = fa.fa_workspace_size(p)
+        ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=q.device)
+        ms = timed(lambda: fa.fa_fwd(p, q, k, v, out, lse, ws, nbytes, stream), torch, np, stream,
+                   warmup, iters, flush)
+        nb = (2.0 * spec.B * spec.KVN * spec.KVS * spec.D * 2 + 2 * spec.B * spec.QN * spec.QS * spec.D * 2
+              + (0 if mask_np is None else mask_np.size))
+        gbs = nb / (ms * 1e-3) / 1e9
+        res[spec.name] = {"ms": round(ms, 5), "kv_gbs": round(gbs, 1),
+                          "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes": nb,
+                          "path": "split-KV, general stage 1 + combine", "doc": spec.doc}
+        del q, k, v, out, lse, ws, mask, inp
+        torch.cuda.empty_cache()
     return res
 
 
 def fused_decode(fa, fa_synth, np, torch, dev16, stream, warmup, iters, flush):
     """The single-launch split-KV (fa_decode_fused) on the two decode workloads, with the
-    split plan fa_fwd picks, for comparison with fa_fwd's stage 1 + combine."""
+    fused plan (fa_decode_fused_plan), for comparison with fa_fwd's stage 1 + combine."""
     res = {}
     for name in ("decode_128k", "decode_gqa"):
         inp = fa_synth.make(fa_synth.WORKLOADS[name])
@@ -380,7 +488,7 @@ def fused_decode(fa, fa_synth, np, torch, dev16, stream, warmup, iters, flush):
         q, k, v = (dev16(x, s.dtype) for x in (inp.q, inp.k, inp.v))
         lens = None if inp.lens is None else torch.from_numpy(inp.lens).to(q.device)
         p = fa.params_for(q, k, layout=s.layout, scale=s.softmax_scale, actual_seq_lengths=lens)
-        sp, ch, nbytes = fa.fa_splitkv_plan(p)
+        sp, ch, nbytes = fa.fa_decode_fused_plan(p)
         ws = torch.zeros((nbytes,), dtype=torch.uint8, device=q.device)
         out = torch.empty_like(q)
         lse = torch.empty((s.B, s.QN, 1), dtype=torch.float32, device=q.device)

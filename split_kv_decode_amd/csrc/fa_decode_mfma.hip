@@ -300,35 +300,54 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2))) v
     const int vx = 2 * (trG & 1) + ((trL & 3) >> 1);
     const int vbyte = (trL & 1) * 8;
 
+    // Boolean mask held as whole dwords (4-aligned rows, unit key stride):
+    // this lane's four words of a tile (keys 32*wave + 8*q4 + 4*half + [0, 4))
+    // are loaded one step ahead, so the wait at the end of each step covers
+    // them and the tile's masking never waits on memory.  Words past the
+    // chunk are not read.
+    const bool mdw = (mmode == 2 && qvalid && a.mask_dword);
+    uint32_t mw[4] = {0u, 0u, 0u, 0u};
+    auto load_mask_words = [&](int jt) __attribute__((always_inline)) {
+        const int64_t kb = c0 + (int64_t)jt * BN + 32 * wave + 4 * half;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int64_t j = kb + 8 * q4;
+            mw[q4] = (j < c1) ? *reinterpret_cast<const uint32_t*>(mrow + j) : 0u;
+        }
+    };
+
     issue_tile(0, sK0, sV0);
+    if (mdw) load_mask_words(0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
     auto step = [&](int jt, const unsigned char* Kb, const unsigned char* Vb, unsigned char* nK,
                     unsigned char* nV) __attribute__((always_inline)) {
-        if (jt + 1 < ntiles) issue_tile(jt + 1, nK, nV);
         // Boolean mask: bit r set when key r of this lane's (row, 16 keys) is
-        // masked; loaded before the products so the loads are in flight
-        // meanwhile.  Keys past the chunk are not read.
+        // masked.  Keys past the chunk are not read.
         uint32_t mbits = 0u;
-        if (mmode == 2 && qvalid) {
+        if (mdw) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const uint32_t w = mw[q4];
+                mbits |= ((w & 0xffu) ? 1u : 0u) << (4 * q4);
+                mbits |= ((w & 0xff00u) ? 1u : 0u) << (4 * q4 + 1);
+                mbits |= ((w & 0xff0000u) ? 1u : 0u) << (4 * q4 + 2);
+                mbits |= ((w & 0xff000000u) ? 1u : 0u) << (4 * q4 + 3);
+            }
+        }
+        if (jt + 1 < ntiles) {
+            issue_tile(jt + 1, nK, nV);
+            if (mdw) load_mask_words(jt + 1);
+        }
+        if (mmode == 2 && qvalid && !a.mask_dword) {  // byte loads, in this step
             const int64_t kb = c0 + (int64_t)jt * BN + 32 * wave + 4 * half;
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const int64_t j = kb + 8 * q4;
-                if (a.mask_dword) {
-                    if (j < c1) {
-                        const uint32_t w = *reinterpret_cast<const uint32_t*>(mrow + j);
-                        mbits |= ((w & 0xffu) ? 1u : 0u) << (4 * q4);
-                        mbits |= ((w & 0xff00u) ? 1u : 0u) << (4 * q4 + 1);
-                        mbits |= ((w & 0xff0000u) ? 1u : 0u) << (4 * q4 + 2);
-                        mbits |= ((w & 0xff000000u) ? 1u : 0u) << (4 * q4 + 3);
-                    }
-                } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (j + e < c1 && mrow[(j + e) * mst] != 0) mbits |= 1u << (4 * q4 + e);
-                }
+                for (int e = 0; e < 4; ++e)
+                    if (j + e < c1 && mrow[(j + e) * mst] != 0) mbits |= 1u << (4 * q4 + e);
             }
         }
         // S^T: keys 32*wave + [0, 32) of the tile x the 32 head rows.

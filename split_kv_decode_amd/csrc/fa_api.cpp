@@ -49,6 +49,8 @@ struct Shape {
 bool fast_decode(const fa_params* p);
 bool general_split_ok(const fa_params* p, const Shape& s);
 int row_groups(const Shape& s);
+int prefill_mask_kind(const fa_params* p, const Shape& s);
+bool mask_in_dwords(const fa_params* p, const Shape& s);
 
 fa_status check_params(const fa_params* p, Shape* s) {
     if (!p) return fail(FA_ERR_NULLPTR, "params is NULL");
@@ -381,7 +383,7 @@ int row_groups(const Shape& s) { return (int)((s.g * s.QS + 31) / 32); }
 // Prefill workgroups for this shape: 256-row tiles for the interleaved
 // kernel (mask-free, D = 128), 128-row tiles otherwise.
 int64_t prefill_workgroups(const fa_params* p, const Shape& s) {
-    const int64_t rows = (p->mask_mode == FA_MASK_NONE && s.D == 128 && !p->seqused_q) ? 256 : 128;
+    const int64_t rows = fa::prefill_rows_per_tile((int)s.D, prefill_mask_kind(p, s), mask_in_dwords(p, s));
     return s.B * s.QN * ((s.QS + rows - 1) / rows);
 }
 
@@ -406,6 +408,16 @@ size_t varlen_bytes(const Shape& s) { return round_up(size_t(varlen_capacity(s))
 // Prefill kernel instantiation for the mask: 0 none, 1 causal, 2 boolean
 // tensor read element by element, 3 boolean tensor staged through LDS (rows
 // of contiguous, 16-byte aligned key runs), 4 window.
+// A boolean tensor whose rows are runs of 4-byte aligned keys (unit key
+// stride, strides and kv_seq multiples of 4, row offsets within 32 bits): the
+// interleaved prefill stages it with 4-byte loads.
+bool mask_in_dwords(const fa_params* p, const Shape& s) {
+    const int64_t* st = p->mask_stride;
+    return p->mask_mode == FA_MASK_BOOL && aligned(p->mask, 4) && st[3] == 1 && st[0] >= 0 && st[1] >= 0 &&
+           st[2] >= 0 && st[0] % 4 == 0 && st[1] % 4 == 0 && st[2] % 4 == 0 && s.KVS % 4 == 0 &&
+           st[2] < (int64_t(1) << 28);
+}
+
 int prefill_mask_kind(const fa_params* p, const Shape& s) {
     if (p->mask_mode == FA_MASK_CAUSAL) return 1;
     if (p->mask_mode == FA_MASK_WINDOW) return 4;
@@ -609,6 +621,7 @@ fa_status run_prefill(const fa_params* p, const Shape& s, const void* q, const v
     a.win_left = win(p->win_left);
     a.win_right = win(p->win_right);
     const int mm = prefill_mask_kind(p, s);
+    a.mask_dwords = mask_in_dwords(p, s) ? 1 : 0;
     // A staged boolean mask with a workspace is summarised per tile first, so
     // the prefill skips the tiles it masks entirely and the mask loads of
     // tiles it does not mask at all.
@@ -645,6 +658,7 @@ fa_status run_prefill(const fa_params* p, const Shape& s, const void* q, const v
         sa.mask_mode = mm;
         sa.win_left = a.win_left;
         sa.win_right = a.win_right;
+        sa.rows = fa::prefill_rows_per_tile((int)s.D, mm, a.mask_dwords != 0);
         fa_status st = launch_result(fa::launch_varlen_schedule(sa, stream), "packed-batch schedule");
         if (st != FA_OK) return st;
         a.cu_q = p->cu_seqlens_q;

@@ -220,6 +220,13 @@ __device__ __forceinline__ void lds_dma16_m0(dma_rsrc r, uint32_t m0, int voff) 
                  : "s"(m0), "v"(voff), "s"(r)
                  : "memory", "m0");
 }
+// Four bytes per lane (lane i's dword lands at M0 + 4i).
+__device__ __forceinline__ void lds_dma4_m0(dma_rsrc r, uint32_t m0, int voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(r)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // LDS byte address of a __shared__ object, as a wave-uniform value.

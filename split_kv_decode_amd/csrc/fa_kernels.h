@@ -99,6 +99,7 @@ struct PrefillArgs {
     int32_t win_left;         // window mask: keys qrow - win_left .. qrow + win_right kept;
     int32_t win_right;        // 0x7fffffff = unbounded on that side
     int32_t zero_q;           // scale underflows to 0 in fp32: q is read as zeros (every score 0)
+    int32_t mask_dwords;      // boolean tensor in runs of 4-byte aligned keys (see prefill_rows_per_tile)
     // Packed layout (work != null): sequence b spans q rows [cu_q[b], cu_q[b+1])
     // and kv rows [cu_kv[b], cu_kv[b+1]) of the [T][N][D] tensors; q_seq and
     // kv_seq are the totals.  The work list holds (sequence, 128-row q tile)
@@ -176,6 +177,7 @@ struct VarlenScheduleArgs {
     int32_t capacity;
     int32_t mask_mode;        // prefill mask instantiation (1 causal, 4 window: fewer tiles)
     int32_t win_left, win_right;
+    int32_t rows;             // query rows per tile of the prefill kernel that runs (128 or 256)
 };
 constexpr int kVarlenMaxBatch = 16383;
 
@@ -265,6 +267,10 @@ __device__ __forceinline__ bool bal_locate(const int64_t* lens, int64_t batch, i
 int decode_mfma_residency(int dtype, int head_dim, bool paged, int waves);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, bool finish, int waves, int64_t batch,
                               hipStream_t stream);
+// Query rows per prefill workgroup: 256 on the interleaved kernel (D = 128;
+// a boolean tensor not staged in 16-byte runs needs runs of 4-byte aligned
+// keys, mask_dwords), else 128.
+int prefill_rows_per_tile(int head_dim, int mask_mode, bool mask_dwords);
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int mask_mode,
                           int64_t batch, hipStream_t stream);
 hipError_t launch_varlen_schedule(const VarlenScheduleArgs& a, hipStream_t stream);

@@ -541,8 +541,9 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
 // needed and recomputes what was taken against the old maximum.  K(j+1) is
 // loaded at the start of slot j and V(j) after stage A, with every scalar of
 // the load worked out beforehand; one barrier per slot releases the buffers.
-template <typename ST, int D>
+template <typename ST, int D, int MASK>
 __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
+    static_assert(MASK >= 0 && MASK <= 4, "mask kind");
     using M = Mfma<ST>;
     using V8 = typename M::V8;
     using E = typename M::E;
@@ -561,6 +562,15 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char sK1[TB];
     __shared__ __attribute__((aligned(1024))) unsigned char sV0[TB];
     __shared__ __attribute__((aligned(1024))) unsigned char sV1[TB];
+    // The boolean mask tile (256 query rows x 64 keys, one byte each).  MASK
+    // 3: chunk-major, 16-byte chunk ch of row r at (ch*256 + r)*16; MASK 2:
+    // row-major in groups of 4 rows (layout at issue_mask_dwords).  And
+    // for MASK 3 the tile classes of the workgroup's rows (two bits per KV
+    // tile, the two 128-row summary rows combined), first 64 words.
+    constexpr int MT = (MASK == 3) ? 32 * NWV * BN : ((MASK == 2) ? 8 * NWV * 272 : 16);
+    __shared__ __attribute__((aligned(1024))) unsigned char sM0[MT];
+    __shared__ __attribute__((aligned(1024))) unsigned char sM1[MT];
+    __shared__ uint32_t s_cls[(MASK == 3) ? 64 : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -568,24 +578,64 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
     const int half = lane >> 5;
     const int col = lane & 31;
 
-    const int64_t total = (int64_t)gridDim.x;
-    const int64_t work = xcd_remap(blockIdx.x, total);
-    const int qt = (int)(work % a.q_tiles);
-    const int64_t bh = work / a.q_tiles;
-    const int n1 = (int)(bh % a.num_heads);
-    const int64_t b = bh / a.num_heads;
-    int64_t L = a.kv_seq;
-    if (a.lens) {
-        L = a.lens[b];
-        L = L < 0 ? 0 : (L > a.kv_seq ? a.kv_seq : L);
+    int qt, n1;
+    int64_t b, L;
+    int64_t q_used = a.q_seq, q_full = a.q_seq;  // query rows computed / written
+    int64_t q_off, kv_off;                       // element offsets of (b) in q/out and k/v
+    int64_t lse_row0, lse_step;                  // lse index of (n1, row i) = lse_row0 + i * lse_step
+    if (a.work) {
+        // Packed layout: block 8k + x (dispatched to XCD x) takes head k % N of
+        // work item 8*(k / N) + x, so the heaviest items spread over all XCDs
+        // and the heads of one item (which share K/V under GQA) share an L2.
+        const int x = (int)(blockIdx.x & 7);
+        const int64_t kk = blockIdx.x >> 3;
+        const int64_t item = (kk / a.num_heads) * 8 + x;
+        n1 = (int)(kk % a.num_heads);
+        if (item >= a.work_items) return;
+        const int32_t wb = a.work[2 * item];
+        if (wb < 0) return;
+        b = wb;
+        qt = a.work[2 * item + 1];
+        const SeqGeom sg = seq_geometry(a.cu_q, a.cu_kv, a.used_q, a.lens, b, a.batch, a.q_seq, a.kv_seq);
+        q_used = sg.q_used;
+        q_full = sg.q_full;
+        L = sg.kv_len;
+        q_off = sg.q0 * a.q_stride_s;
+        kv_off = sg.k0 * a.kv_stride_s;
+        lse_row0 = sg.q0 * a.num_heads + n1;
+        lse_step = a.num_heads;
+    } else {
+        const int64_t total = (int64_t)gridDim.x;
+        int64_t bh;
+        if (MASK == 1 || MASK == 2 || MASK == 3 || (MASK == 4 && a.win_left >= a.win_right)) {
+            // Costs grow with the query tile (causal, a tensor mask that may
+            // be causal, or a window reaching further back than forward):
+            // every head's tile of one rank is dispatched before the next
+            // lighter rank, the heads of a rank spread over the XCDs as below.
+            const int64_t heads = total / a.q_tiles;
+            qt = a.q_tiles - 1 - (int)(blockIdx.x / heads);
+            bh = xcd_remap(blockIdx.x % heads, heads);
+        } else {
+            const int64_t work = xcd_remap(blockIdx.x, total);
+            qt = (int)(work % a.q_tiles);
+            bh = work / a.q_tiles;
+        }
+        n1 = (int)(bh % a.num_heads);
+        b = bh / a.num_heads;
+        L = a.kv_seq;
+        if (a.lens) {
+            L = a.lens[b];
+            L = L < 0 ? 0 : (L > a.kv_seq ? a.kv_seq : L);
+        }
+        if (a.used_q) {  // rows at or past the batch's used positions: written as 0 / +inf
+            const int64_t u = a.used_q[b];
+            q_used = u < 0 ? 0 : (u > a.q_seq ? a.q_seq : u);
+        }
+        q_off = b * a.q_stride_b;
+        kv_off = b * a.kv_stride_b;
+        lse_row0 = (b * a.num_heads + n1) * a.q_seq;
+        lse_step = 1;
     }
-    int64_t q_used = a.q_seq;
-    if (a.used_q) {  // rows at or past the batch's used positions: written as 0 / +inf
-        const int64_t u = a.used_q[b];
-        q_used = u < 0 ? 0 : (u > a.q_seq ? a.q_seq : u);
-    }
-    const int64_t q_off = b * a.q_stride_b, kv_off = b * a.kv_stride_b;
-    const int64_t lse_row0 = (b * a.num_heads + n1) * a.q_seq;
     const int n2 = n1 / a.group;
 
     const int64_t i0 = (int64_t)qt * (32 * NWV);
@@ -605,7 +655,56 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
         }
     }
     const float c = a.scale_log2;
-    const int nt = (i0 >= q_used) ? 0 : (int)((L + BN - 1) / BN);  // KV tiles (none when no row is used)
+    // Keys [kbeg, kv_end) can be visible to some row of the tile: causal stops
+    // at the tile's last row, a window spans from the first row's left edge to
+    // the last used row's right edge.  The loop runs over the 64-key tiles of
+    // that range (none when no row is used).
+    int64_t kv_end = L, kbeg = 0;
+    if (MASK == 1 && kv_end > i0 + 32 * NWV) kv_end = i0 + 32 * NWV;
+    if (MASK == 4) {
+        const int64_t i_last = (i0 + 32 * NWV < q_used ? i0 + 32 * NWV : q_used) - 1;
+        if (kv_end > i_last + a.win_right + 1) kv_end = i_last + a.win_right + 1;
+        const int64_t key_lo = i0 - a.win_left;
+        if (key_lo > 0) kbeg = key_lo / BN * BN;
+    }
+    // MASK 3 with a summary of the mask: the classes of the workgroup's two
+    // 128-row tiles, OR-ed (bit 0: some key visible, bit 1: some key masked,
+    // for some row), staged for the loop; the first and last tile with a
+    // visible key bound the range.  Tiles past the 64 staged words count as
+    // partly masked.
+    const bool summary = (MASK == 3) && a.mask_cls != nullptr;
+    if (MASK == 3 && summary) {
+        const int64_t sn = a.mask_stride[1] ? a.num_heads : 1;
+        const int64_t slice = (a.mask_stride[0] ? b : 0) * sn + (a.mask_stride[1] ? n1 : 0);
+        const int64_t qt128 = (a.q_seq + kMaskRowsPerTile - 1) / kMaskRowsPerTile;
+        const int64_t r0 = 2 * (int64_t)qt;
+        const uint32_t* c0p = a.mask_cls + (slice * qt128 + r0) * a.cls_words;
+        const uint32_t* c1p = (r0 + 1 < qt128) ? c0p + a.cls_words : nullptr;
+        int first = 0x7fffffff, last = -1;
+        for (int w = lane; w < a.cls_words; w += 64) {
+            const uint32_t x = c0p[w] | (c1p ? c1p[w] : 0u);
+            if (w < 64) s_cls[w] = x;  // every wave stages all words (same values), so it reads its own writes
+            const uint32_t live = x & 0x55555555u;
+            if (live) {
+                first = min(first, 16 * w + (__builtin_ctz(live) >> 1));
+                last = max(last, 16 * w + ((31 - __builtin_clz(live)) >> 1));
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            first = min(first, __shfl_xor(first, off, 64));
+            last = max(last, __shfl_xor(last, off, 64));
+        }
+        first = __builtin_amdgcn_readfirstlane(first);
+        last = __builtin_amdgcn_readfirstlane(last);
+        if (last < 0) {
+            kv_end = 0;  // no visible key for any row
+        } else {
+            if ((int64_t)first * BN > kbeg) kbeg = (int64_t)first * BN;
+            if ((int64_t)(last + 1) * BN < kv_end) kv_end = (int64_t)(last + 1) * BN;
+        }
+    }
+    const int nt = (i0 >= q_used || kv_end <= kbeg) ? 0 : (int)((kv_end - kbeg + BN - 1) / BN);
 
     f32x16 o[D / 32];
 #pragma unroll
@@ -616,8 +715,8 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
     float l_half = 0.f;     // this half-wave's share of the row sum
 
     const int64_t row_bytes = a.kv_stride_s * 2;
-    const char* kbase = reinterpret_cast<const char*>(a.k + kv_off + (int64_t)n2 * a.kv_stride_n);
-    const char* vbase = reinterpret_cast<const char*>(a.v + kv_off + (int64_t)n2 * a.kv_stride_n);
+    const char* kbase = reinterpret_cast<const char*>(a.k + kv_off + (int64_t)n2 * a.kv_stride_n) + kbeg * row_bytes;
+    const char* vbase = reinterpret_cast<const char*>(a.v + kv_off + (int64_t)n2 * a.kv_stride_n) + kbeg * row_bytes;
     int voff[NIW];
 #pragma unroll
     for (int w = 0; w < NIW; ++w) {
@@ -632,10 +731,90 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
     const uint64_t kb64 = (uint64_t)uni64((int64_t)(uintptr_t)kbase);
     const uint64_t vb64 = (uint64_t)uni64((int64_t)(uintptr_t)vbase);
     const int32_t rb32 = __builtin_amdgcn_readfirstlane((int32_t)row_bytes);
-    const int32_t L32 = __builtin_amdgcn_readfirstlane((int32_t)L);
+    const int32_t L32 = __builtin_amdgcn_readfirstlane((int32_t)(kv_end - kbeg));  // keys in the range
+    // Visible keys of the wave's first row (wrow0), relative to the range's
+    // first key: [c_lo, c_hi] (row wrow0 + col sees [c_lo + col, c_hi + col]),
+    // and the bounds [w_lo, w_hi] within which a key is visible to every row of
+    // the wave, so a tile inside them needs no per-key mask.  All scalars: the
+    // per-lane bounds are rebuilt from the lane id on the masking path only.
+    auto clamp_rel = [](int64_t x) __attribute__((always_inline)) {
+        return (int32_t)(x < -(int64_t(1) << 30) ? -(int64_t(1) << 30) : (x > (int64_t(1) << 30) ? (int64_t(1) << 30) : x));
+    };
+    const int64_t wrow0 = i0 + 32 * wave;
+    int32_t c_lo = 0, c_hi = L32 - 1;
+    if (MASK == 1) c_hi = clamp_rel(wrow0 - kbeg);
+    if (MASK == 4) {
+        c_lo = clamp_rel(wrow0 - a.win_left - kbeg);
+        c_hi = clamp_rel(wrow0 + a.win_right - kbeg);
+    }
+    c_lo = __builtin_amdgcn_readfirstlane(c_lo);
+    c_hi = __builtin_amdgcn_readfirstlane(c_hi);
+    const int32_t w_lo = (MASK == 4) ? c_lo + 31 : 0;
+    const int32_t w_hi = min(L32 - 1, c_hi);
     const uint32_t wshare = (uint32_t)(wave * NIW * 1024);
     const uint32_t mK0 = lds_address(sK0) + wshare, mK1 = lds_address(sK1) + wshare;
     const uint32_t mV0 = lds_address(sV0) + wshare, mV1 = lds_address(sV1) + wshare;
+    // MASK 3 tile loads: wave w fills chunk w%4 (keys 16*(w%4) + [0,16)) of
+    // rows 128*(w/4) + [0,128), 64 rows per wave load; the resource stops at
+    // the last used row's last key, so nothing past the mask tensor is read.
+    const char* mbase = reinterpret_cast<const char*>(a.mask) + b * a.mask_stride[0] +
+                        (int64_t)n1 * a.mask_stride[1] + i0 * a.mask_stride[2];
+    const int32_t mst2 = __builtin_amdgcn_readfirstlane((int32_t)a.mask_stride[2]);
+    int32_t mrec_rows = 0;
+    if (MASK == 3) {
+        int64_t rv = q_used - i0;
+        rv = rv > 32 * NWV ? 32 * NWV : rv;
+        mrec_rows = __builtin_amdgcn_readfirstlane((int32_t)((rv - 1) * a.mask_stride[2]));
+    }
+    const uint32_t mM0 = lds_address(sM0) + (uint32_t)((wave & 3) * (32 * NWV) + 128 * (wave >> 2)) * 16u;
+    const uint32_t mM1 = lds_address(sM1) + (uint32_t)((wave & 3) * (32 * NWV) + 128 * (wave >> 2)) * 16u;
+    auto tile_cls = [&](int jl) __attribute__((always_inline)) -> uint32_t {
+        const int64_t jt = kbeg / BN + jl;
+        if (!summary || jt >= 64 * 16) return 3u;
+        return (__builtin_amdgcn_readfirstlane(s_cls[jt >> 4]) >> (2 * (jt & 15))) & 3u;
+    };
+    // MASK 2 tile loads (rows of 4-aligned key runs): four keys per lane, one
+    // group of 4 rows per wave load (lane l: row 4G + l/16, keys 4(l%16) +
+    // [0, 4)), wave w loading groups 8w .. 8w+7 (its own rows); group G sits at
+    // G*272 in LDS, rows 64 bytes apart (the 16-byte step between groups
+    // spreads a wave's reads over the banks).  Each group's resource stops at
+    // its last used row's last key; groups with no used row are not loaded.
+    constexpr int MGP = 272;
+    const uint32_t mE0 = lds_address(sM0) + (uint32_t)(8 * wave * MGP);
+    const uint32_t mE1 = lds_address(sM1) + (uint32_t)(8 * wave * MGP);
+    auto issue_mask_dwords = [&](int jl, uint32_t m0) __attribute__((always_inline)) {
+        const int64_t j0 = kbeg + (int64_t)jl * BN;
+        int64_t keys = a.kv_seq - j0;
+        keys = keys > BN ? BN : keys;
+        const int ln = (int)__lane_id();
+        const int voff = (ln >> 4) * mst2 + (ln & 15) * 4;
+        const uint64_t gb = (uint64_t)(uintptr_t)(mbase + j0) + (uint64_t)(int64_t)(32 * wave) * (uint64_t)(int64_t)mst2;
+        const int32_t rows = __builtin_amdgcn_readfirstlane((int32_t)(q_used - i0 - 32 * wave));
+#pragma unroll
+        for (int G = 0; G < 8; ++G) {
+            const int32_t rv = min(rows - 4 * G, 4);
+            if (rv <= 0) break;
+            const uint64_t t = gb + (uint64_t)(int64_t)(4 * G) * (uint64_t)(int64_t)mst2;
+            dma_rsrc r;
+            r[0] = (uint32_t)t;
+            r[1] = (uint32_t)(t >> 32) & 0xffffu;
+            r[2] = (uint32_t)((rv - 1) * mst2 + (int32_t)keys);
+            r[3] = 0x00020000u;
+            lds_dma4_m0(r, m0 + (uint32_t)(G * MGP), voff);
+        }
+    };
+    auto issue_mask = [&](int jl, uint32_t m0) __attribute__((always_inline)) {
+        if (!(tile_cls(jl) & 2u)) return;  // no key masked (or none visible): nothing to stage
+        const int64_t j0 = kbeg + (int64_t)jl * BN;
+        int64_t keys = a.kv_seq - j0;
+        keys = keys > BN ? BN : keys;
+        const dma_rsrc rm = make_dma_rsrc(mbase + j0, mrec_rows + (int)keys);
+        const int ln = (int)__lane_id();
+#pragma unroll
+        for (int w = 0; w < 2; ++w)
+            lds_dma16_m0(rm, m0 + (uint32_t)(w * 1024),
+                         (128 * (wave >> 2) + 64 * w + ln) * mst2 + (wave & 3) * 16);
+    };
     // Bytes of a full tile, and of the last one (cut at the length).
     const uint32_t full_bytes = (uint32_t)(BN * rb32);
     const uint32_t last_bytes = (uint32_t)((L32 - (nt - 1) * BN) * rb32);
@@ -799,14 +978,16 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
         for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, St[1][r]);
         tmax = fmaxf(tmax, xor32(tmax)) * c;
         const float mnew = fmaxf(m_run, tmax);
-        const float alpha = fast_exp2(m_run - mnew);  // m_run is finite here: the first half set it
+        // (a row that has seen no key yet -- a window's left edge, rows a
+        // wave shares -- keeps the reference -inf and exponentials against 0)
+        const float alpha = fast_exp2(m_run - ((mnew == kNegInf) ? 0.f : mnew));
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
         l_half *= alpha;
         m_run = mnew;
-        const float nmx = -m_run;
+        const float nmx = (m_run == kNegInf) ? 0.f : -m_run;
         float s1 = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
@@ -839,6 +1020,9 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
         const unsigned char* Vp = PAR ? sV0 : sV1;
         const uint32_t mKn = PAR ? mK0 : mK1;
         const uint32_t mVn = PAR ? mV1 : mV0;
+        const unsigned char* Mc = PAR ? sM1 : sM0;  // MASK 2, 3: mask tile j
+        const uint32_t mMn = PAR ? mM0 : mM1;       // ... and where tile j+1's goes
+        const uint32_t mEn = PAR ? mE0 : mE1;
         f32x16* Sn = PAR ? SB : SA;
         f32x16* So = PAR ? SA : SB;
         u32x4* Pn = PAR ? PB : PA;
@@ -846,7 +1030,11 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
         // K(j+1) now and V(j) after stage A, into the buffers the previous
         // slot released (issued together, the 8 waves' loads queue for the
         // address unit at the slot's start)
-        if (j + 1 < nt) issue(kb64, j + 1, mKn);
+        if (j + 1 < nt) {
+            issue(kb64, j + 1, mKn);
+            if constexpr (MASK == 3) issue_mask(j + 1, mMn);
+            if constexpr (MASK == 2) issue_mask_dwords(j + 1, mEn);
+        }
         stage_a(std::integral_constant<bool, !LAST>{}, std::integral_constant<bool, !FIRST>{}, Kc, Sn, So, Po, ps1);
         if (j < nt) issue(vb64, j, mVn);
         if constexpr (!FIRST) {
@@ -856,15 +1044,59 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
             l_half += ps0 + ps1;
         }
         if constexpr (!LAST) {
-            // the last tile crosses the length: its keys at or past it are excluded
+            // Keys past the range (the last tile), and for the masks the tiles
+            // that cross the diagonal or a band edge of one of the wave's rows:
+            // the excluded keys' scores become -inf.
             const int32_t j0 = j * BN;
-            if (j0 + BN > L32) {
+            uint32_t tcls = 3u;
+            if constexpr (MASK == 3) tcls = tile_cls(j);
+            if (MASK == 3 && !(tcls & 1u)) {
+                // no key of the tile visible to any row of the workgroup
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) Sn[tt][r] = kNegInf;
+            } else if (MASK == 2 || (MASK == 3 && (tcls & 2u))) {
+                // the staged mask tile: word (tt, g) of this lane holds keys
+                // 32*tt + 8*g + 4*half + [0, 4) of its row; keys past the
+                // range are excluded too
+                const int ln = (int)__lane_id();
+                const int row = 32 * wave + (ln & 31), h4 = (ln >> 5) * 4;
+                const int32_t hi = L32 - 1 - j0 - h4;
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+                    uint32_t mw[4];
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        if constexpr (MASK == 3)
+                            mw[g] = *reinterpret_cast<const uint32_t*>(
+                                Mc + ((2 * tt + (g >> 1)) * (32 * NWV) + row) * 16 + 8 * (g & 1) + h4);
+                        else
+                            mw[g] = *reinterpret_cast<const uint32_t*>(Mc + (row >> 2) * 272 + (row & 3) * 64 +
+                                                                       32 * tt + 8 * g + h4);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int32_t e = tt * 32 + 8 * (r >> 2) + (r & 3);
+                        const bool ok = e <= hi && ((mw[r >> 2] >> (8 * (r & 3))) & 0xffu) == 0u;
+                        Sn[tt][r] = ok ? Sn[tt][r] : kNegInf;
+                    }
+                }
+            } else if (j0 < w_lo || j0 + BN - 1 > w_hi) {
+                // element (tt, r) is key j0 + e + 4*half, e = 32tt + 8(r/4) + r%4
+                const int ln = (int)__lane_id();
+                const int cl = ln & 31, h4 = (ln >> 5) * 4;
+                int32_t hi = L32 - 1 - j0;
+                if (MASK != 0) hi = min(hi, c_hi - j0 + cl);
+                hi -= h4;
+                const int32_t lo = c_lo - j0 + cl - h4;
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int32_t tok = j0 + tt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                        Sn[tt][r] = tok < L32 ? Sn[tt][r] : kNegInf;
+                        const int32_t e = tt * 32 + 8 * (r >> 2) + (r & 3);
+                        const bool ok = e <= hi && (MASK != 4 || e >= lo);
+                        Sn[tt][r] = ok ? Sn[tt][r] : kNegInf;
                     }
             }
         }
@@ -884,6 +1116,8 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
 
     if (nt > 0) {
         issue(kb64, 0, mK0);
+        if constexpr (MASK == 3) issue_mask(0, mM0);
+        if constexpr (MASK == 2) issue_mask_dwords(0, mE0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         slot(T0{}, BT{}, BF{}, 0);
@@ -903,7 +1137,7 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
     }
 
     const float l_run = l_half + xor32(l_half);
-    if (qrow < a.q_seq) {
+    if (qrow < q_full) {
         const bool empty = !qvalid || (m_run == kNegInf);
         const float inv = empty ? 0.f : 1.f / l_run;
         uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + q_off + (int64_t)n1 * a.q_stride_n + qrow * a.q_stride_s;
@@ -921,7 +1155,7 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
                 *reinterpret_cast<u32x2*>(op + d0) = w;
             }
         }
-        if (half == 0 && a.lse) a.lse[lse_row0 + qrow] = empty ? kPosInf : (m_run + log2f(l_run)) * kLn2;
+        if (half == 0 && a.lse) a.lse[lse_row0 + qrow * lse_step] = empty ? kPosInf : (m_run + log2f(l_run)) * kLn2;
     }
 }
 
@@ -940,19 +1174,37 @@ static hipError_t dispatch_prefill(const PrefillArgs& a, int mask_mode, int64_t 
 }
 
 template <typename ST>
-static hipError_t launch_il(const PrefillArgs& a0, int64_t batch, hipStream_t s) {
+static hipError_t launch_il(const PrefillArgs& a0, int mask_mode, int64_t batch, hipStream_t s) {
     PrefillArgs a = a0;
     a.q_tiles = (int32_t)((a.q_seq + 255) / 256);
-    const int64_t blocks = (int64_t)a.q_tiles * batch * a.num_heads;
+    const int64_t blocks = a.work ? (int64_t)(a.work_items + 7) / 8 * 8 * a.num_heads
+                                  : (int64_t)a.q_tiles * batch * a.num_heads;
+    if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((prefill_il_kernel<ST, 128>), dim3((unsigned)blocks), dim3(512), 0, s, a);
+    const dim3 grid((unsigned)blocks), block(512);
+    switch (mask_mode) {
+        case 0: hipLaunchKernelGGL((prefill_il_kernel<ST, 128, 0>), grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((prefill_il_kernel<ST, 128, 1>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((prefill_il_kernel<ST, 128, 2>), grid, block, 0, s, a); break;
+        case 3: hipLaunchKernelGGL((prefill_il_kernel<ST, 128, 3>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((prefill_il_kernel<ST, 128, 4>), grid, block, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
+}
+
+int prefill_rows_per_tile(int head_dim, int mask_mode, bool mask_dwords) {
+    if (head_dim != 128) return 128;
+    if (mask_mode == 2 && !mask_dwords) return 128;
+    return 256;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int mask_mode, int64_t batch,
                           hipStream_t stream) {
-    if (!a.work && mask_mode == 0 && head_dim == 128 && a.q_seq > 0 && batch > 0)
-        return dtype == 1 ? launch_il<BF16>(a, batch, stream) : launch_il<F16>(a, batch, stream);
+    if (prefill_rows_per_tile(head_dim, mask_mode, a.mask_dwords != 0) == 256) {
+        if (a.q_seq <= 0 || batch <= 0) return hipSuccess;
+        return dtype == 1 ? launch_il<BF16>(a, mask_mode, batch, stream) : launch_il<F16>(a, mask_mode, batch, stream);
+    }
     const int64_t blocks = a.work ? (int64_t)(a.work_items + 7) / 8 * 8 * a.num_heads
                                   : (int64_t)a.q_tiles * batch * a.num_heads;
     if (blocks <= 0) return hipSuccess;

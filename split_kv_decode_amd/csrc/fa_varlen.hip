@@ -1,7 +1,8 @@
 // fa_varlen.hip -- work list of a packed variable-length (TND) prefill.
 //
 // The packed layout (FlashAttn developer guide 1.3) removes the padding of a
-// ragged batch, which leaves its 128-row query tiles with very different
+// ragged batch, which leaves its query tiles (128 or 256 rows, as the prefill
+// kernel that runs takes them) with very different
 // costs: a tile of a long sequence visits many more KV tiles than one of a
 // short sequence, and under a causal mask the last tiles of a sequence cost
 // the most.  The developer guide balances such work with a cost model over
@@ -23,13 +24,13 @@ constexpr int kSchedThreads = 1024;
 constexpr int kCostBins = 4096;
 
 __device__ __forceinline__ int tile_cost(const VarlenScheduleArgs& a, const SeqGeom& g, int64_t qt) {
-    const int64_t i0 = qt * 128;
+    const int64_t i0 = qt * a.rows;
     if (i0 >= g.q_used) return 1;  // only writes the initial values
     int64_t kv_end = g.kv_len;
     int64_t jt0 = 0;
-    if (a.mask_mode == 1 && kv_end > i0 + 128) kv_end = i0 + 128;
+    if (a.mask_mode == 1 && kv_end > i0 + a.rows) kv_end = i0 + a.rows;
     if (a.mask_mode == 4) {
-        const int64_t i_last = (i0 + 128 < g.q_used ? i0 + 128 : g.q_used) - 1;
+        const int64_t i_last = (i0 + a.rows < g.q_used ? i0 + a.rows : g.q_used) - 1;
         if (kv_end > i_last + a.win_right + 1) kv_end = i_last + a.win_right + 1;
         const int64_t lo = i0 - a.win_left;
         if (lo > 0) jt0 = lo / 64;
@@ -50,7 +51,7 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(VarlenSc
 
     for (int s = t; s < nseq; s += kSchedThreads) {
         const SeqGeom g = seq_geometry(a.cu_q, a.cu_kv, a.used_q, a.lens, s, a.batch, a.q_total, a.kv_total);
-        s_start[s + 1] = (int32_t)((g.q_full + 127) / 128);
+        s_start[s + 1] = (int32_t)((g.q_full + a.rows - 1) / a.rows);
     }
     if (t == 0) s_start[0] = 0;
     for (int i = t; i < kCostBins; i += kSchedThreads) s_hist[i] = 0;
@@ -141,7 +142,8 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(VarlenSc
 }
 
 hipError_t launch_varlen_schedule(const VarlenScheduleArgs& a, hipStream_t stream) {
-    if (a.batch < 0 || a.batch > kVarlenMaxBatch || a.capacity <= 0) return hipErrorInvalidValue;
+    if (a.batch < 0 || a.batch > kVarlenMaxBatch || a.capacity <= 0 || (a.rows != 128 && a.rows != 256))
+        return hipErrorInvalidValue;
     hipLaunchKernelGGL(varlen_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, a);
     return hipGetLastError();
 }

@@ -349,7 +349,7 @@ def extra_workloads(fa, fa_synth, np, torch, dev16, stream, warmup=3, iters=20):
              ("decode_gqa", None, ("PA_BBND", 128)), ("decode_128k", None, ("PA_BNBD", 128)),
              ("prefill_causal", "bool", None), ("prefill_causal", "causal", None),
              ("prefill_4k", "window", None), ("prefill_gqa_long", None, None),
-             ("prefill_4k_d256", None, None)]
+             ("prefill_4k_d256", None, None), ("prefill_4k_d256", "window", None)]
     window = (1024, 0)  # sliding window of the last 1025 keys
     for name, mode, paging in cases:
         inp = fa_synth.make(fa_synth.WORKLOADS[name])

@@ -570,8 +570,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     }
     int S = SS;                   // slots this row uses
     if (a.bal_nwg > 0) {          // length-balanced plan: the pieces of this row's batch
-        const int64_t tstar = bal_tstar(a.lens, a.batch, a.kv_seq, a.num_kv_heads, a.bal_nwg);
-        const int64_t nb = bal_pieces(a.lens, row / a.num_heads, a.kv_seq, tstar);
+        const int64_t nb = bal_row_pieces(a.lens, a.batch, a.kv_seq, a.num_kv_heads, a.bal_nwg, row / a.num_heads);
         S = (int)(nb < SS ? nb : SS);
     }
 

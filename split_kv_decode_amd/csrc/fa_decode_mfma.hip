@@ -29,6 +29,9 @@
 
 namespace fa {
 
+// s_waitcnt immediate (gfx9 encoding) for vmcnt(0) with the other counters free.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 template <typename ST, int D, bool FINISH, bool PAGED, int NWV>
 __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(DecodeArgs a) {
     static_assert(NWV == 1 || NWV == 2, "one or two waves");
@@ -62,10 +65,9 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2))) v
     int n2, rg = 0;
     if (a.bal_nwg > 0) {
         // Length-balanced pieces: tstar tiles each, cut at the batch's length.
-        const int64_t tstar = bal_tstar(a.lens, a.batch, a.kv_seq, a.num_kv_heads, a.bal_nwg);
-        int64_t nb;
-        if (!bal_locate(a.lens, a.batch, a.kv_seq, a.num_kv_heads, tstar, blk, &b, &n2, &split, &nb)) return;
-        const int64_t L = bal_len(a.lens, b, a.kv_seq);
+        int64_t tstar, L;
+        if (!bal_find(a.lens, a.batch, a.kv_seq, a.num_kv_heads, a.bal_nwg, blk, &tstar, &b, &n2, &split, &L))
+            return;
         c0 = split * tstar * 64;
         c1 = c0 + tstar * 64;
         if (c1 > L) c1 = L;
@@ -254,8 +256,13 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2))) v
                     id = __builtin_amdgcn_readfirstlane(s_blk[lb]);
                 }
                 const int64_t off = ((int64_t)id * a.kv_stride_blk + (int64_t)cur_row * a.kv_stride_s) * 2;
-                lds_dma16(kbase + off, nrec, (lds_void*)(dK + I * 1024), voff[w]);
-                lds_dma16(vbase + off, nrec, (lds_void*)(dV + I * 1024), voff[w]);
+                if constexpr (NWV == 1) {  // as for the contiguous cache below
+                    lds_dma16_stream(make_dma_rsrc(kbase + off, nrec), (lds_void*)(dK + I * 1024), voff[w]);
+                    lds_dma16_stream(make_dma_rsrc(vbase + off, nrec), (lds_void*)(dV + I * 1024), voff[w]);
+                } else {
+                    lds_dma16(kbase + off, nrec, (lds_void*)(dK + I * 1024), voff[w]);
+                    lds_dma16(vbase + off, nrec, (lds_void*)(dV + I * 1024), voff[w]);
+                }
                 // Next wave load: RPI rows on (RPI <= 8 < 16 <= bs: at most one
                 // block boundary).
                 cur_row += RPI;
@@ -277,13 +284,21 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2))) v
             int64_t rows = nkeys - (int64_t)jt * BN;
             rows = rows > BN ? BN : rows;
             const int nrec = (int)(rows * row_bytes);
-            const char* kt = kbase + (int64_t)jt * BN * row_bytes;
-            const char* vt = vbase + (int64_t)jt * BN * row_bytes;
+            const dma_rsrc rk = make_dma_rsrc(kbase + (int64_t)jt * BN * row_bytes, nrec);
+            const dma_rsrc rv = make_dma_rsrc(vbase + (int64_t)jt * BN * row_bytes, nrec);
 #pragma unroll
             for (int w = 0; w < NIW; ++w) {
                 const int I = wave * NIW + w;
-                lds_dma16(kt, nrec, (lds_void*)(dK + I * 1024), voff[w]);
-                lds_dma16(vt, nrec, (lds_void*)(dV + I * 1024), voff[w]);
+                // One wave: loads the compiler does not see (it would wait for
+                // them before every LDS read of the step).  Two waves measured
+                // faster with the compiler's loads and waits.
+                if constexpr (NWV == 1) {
+                    lds_dma16_stream(rk, (lds_void*)(dK + I * 1024), voff[w]);
+                    lds_dma16_stream(rv, (lds_void*)(dV + I * 1024), voff[w]);
+                } else {
+                    lds_dma16(kbase + (int64_t)jt * BN * row_bytes, nrec, (lds_void*)(dK + I * 1024), voff[w]);
+                    lds_dma16(vbase + (int64_t)jt * BN * row_bytes, nrec, (lds_void*)(dV + I * 1024), voff[w]);
+                }
             }
         }
     };
@@ -316,9 +331,13 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2))) v
         }
     };
 
+    // The tile loads (inline assembly) are invisible to the compiler's wait
+    // placement; the waits below are visible to it and cover its own loads
+    // (q, mask words) too, so it places none inside the loop, where a wait on
+    // those would also wait for the next tile in flight.
     issue_tile(0, sK0, sV0);
     if (mdw) load_mask_words(0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
 
     auto step = [&](int jt, const unsigned char* Kb, const unsigned char* Vb, unsigned char* nK,
@@ -351,15 +370,55 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2))) v
             }
         }
         // S^T: keys 32*wave + [0, 32) of the tile x the 32 head rows.
+        // One wave: every K fragment is read before the products, so only the
+        // first read's latency is exposed (a one-wave workgroup has no other
+        // wave of its own to hide LDS latency); two waves read as they go.
         f32x16 s;
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = 0.f;
+        if constexpr (NWV == 1) {
+            V8 kf[D / 16];
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-            const V8 ka = __builtin_bit_cast(
-                V8, *reinterpret_cast<const u32x4*>(Kb + krow * RB + (((2 * kk + half) ^ ksw) << 4)));
-            s = M::mm(ka, qreg[kk], s);
+            for (int kk = 0; kk < D / 16; ++kk)
+                kf[kk] = __builtin_bit_cast(
+                    V8, *reinterpret_cast<const u32x4*>(Kb + krow * RB + (((2 * kk + half) ^ ksw) << 4)));
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) s = M::mm(kf[kk], qreg[kk], s);
+            __builtin_amdgcn_sched_barrier(0);
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                const V8 ka = __builtin_bit_cast(
+                    V8, *reinterpret_cast<const u32x4*>(Kb + krow * RB + (((2 * kk + half) ^ ksw) << 4)));
+                s = M::mm(ka, qreg[kk], s);
+            }
         }
+        // One wave: the V^T fragments of this wave's keys, read now so their
+        // latency passes under the masking and the exponentials.
+        V8 vf[2][D / 32];
+        auto read_v = [&](int ks, int dt) __attribute__((always_inline)) {
+            const int lc = 4 * dt + vx;
+            const unsigned char* vb = Vb + (32 * wave + 16 * ks) * RB;
+            const int rlo = 32 * wave + 16 * ks + vrow_lo, rhi = rlo + 8;
+            const s16x4 lo = lds_read_tr(vb + vrow_lo * RB + ((lc ^ swz<D>(rlo)) << 4) + vbyte);
+            const s16x4 hi = lds_read_tr(vb + vrow_hi * RB + ((lc ^ swz<D>(rhi)) << 4) + vbyte);
+            return __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        if constexpr (NWV == 1)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) {
+                const int lc = 4 * dt + vx;
+                const unsigned char* vb = Vb + (32 * wave + 16 * ks) * RB;
+                const int rlo = 32 * wave + 16 * ks + vrow_lo, rhi = rlo + 8;
+                const s16x4 lo = lds_read_tr(vb + vrow_lo * RB + ((lc ^ swz<D>(rlo)) << 4) + vbyte);
+                const s16x4 hi = lds_read_tr(vb + vrow_hi * RB + ((lc ^ swz<D>(rhi)) << 4) + vbyte);
+                vf[ks][dt] = __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
         // Register r holds key 32*wave + 8*(r/4) + 4*half + r%4 of the tile.
         const int64_t kt0 = (int64_t)jt * BN + 32 * wave;
         if (kt0 + 32 > nkeys || mmode != 0 || dead_rows) {
@@ -413,17 +472,10 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) {
-                const int lc = 4 * dt + vx;
-                const unsigned char* vb = Vb + (32 * wave + 16 * ks) * RB;
-                const int rlo = 32 * wave + 16 * ks + vrow_lo, rhi = rlo + 8;
-                const s16x4 lo = lds_read_tr(vb + vrow_lo * RB + ((lc ^ swz<D>(rlo)) << 4) + vbyte);
-                const s16x4 hi = lds_read_tr(vb + vrow_hi * RB + ((lc ^ swz<D>(rhi)) << 4) + vbyte);
-                const V8 va = __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                o[dt] = M::mm(va, pb[ks], o[dt]);
-            }
+            for (int dt = 0; dt < D / 32; ++dt)
+                o[dt] = M::mm(NWV == 1 ? vf[ks][dt] : read_v(ks, dt), pb[ks], o[dt]);
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // the next tile (and mask words) landed
         __syncthreads();
     };
     for (int jt = 0; jt < ntiles; jt += 2) {

@@ -220,6 +220,15 @@ __device__ __forceinline__ void lds_dma16_m0(dma_rsrc r, uint32_t m0, int voff) 
                  : "s"(m0), "v"(voff), "s"(r)
                  : "memory", "m0");
 }
+// The same as lds_dma16_unordered for data read once (non-temporal), as the
+// decode's K/V stream: nothing the compiler tracks, so it places no wait on it.
+__device__ __forceinline__ void lds_dma16_stream(dma_rsrc r, lds_void* dst, int voff) {
+    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                 :
+                 : "s"(m), "v"(voff), "s"(r)
+                 : "memory", "m0");
+}
 // Four bytes per lane (lane i's dword lands at M0 + 4i).
 __device__ __forceinline__ void lds_dma4_m0(dma_rsrc r, uint32_t m0, int voff) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"

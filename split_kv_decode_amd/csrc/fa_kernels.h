@@ -257,6 +257,82 @@ __device__ __forceinline__ bool bal_locate(const int64_t* lens, int64_t batch, i
     return false;
 }
 
+// The same lookup from one load of the lengths when the batch fits a wave
+// (lane b holds batch b's length; the tile total, the scan and the batch's
+// length are then shuffles of it), so a workgroup starts with one memory round
+// trip instead of one per helper above, and in 32-bit arithmetic with the
+// uniform divisions done once on the scalar unit (a 64-bit division per lane
+// is a long instruction sequence).  Also returns tstar and the batch's length
+// L.  Falls back to the helpers above past 64 batches or 2^30 tiles of work.
+struct BalWave {
+    int32_t L;      // this lane's batch length (clamped), 0 past the batch
+    int32_t T;      // its 64-key tiles
+    int32_t tstar;  // tiles per piece (uniform)
+    bool ok;        // the 32-bit form applies
+};
+__device__ __forceinline__ BalWave bal_wave(const int64_t* lens, int64_t batch, int64_t kv_seq, int32_t kv_heads,
+                                            int32_t nwg) {
+    BalWave r;
+    r.ok = batch <= 64 && kv_seq < (int64_t(1) << 31);
+    if (!r.ok) return r;
+    const int lane = threadIdx.x & 63;
+    r.L = lane < batch ? (int32_t)bal_len(lens, lane, kv_seq) : 0;
+    r.T = (r.L + 63) >> 6;
+    int tot = r.T;
+    for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off, 64);
+    const int64_t W = (int64_t)__builtin_amdgcn_readfirstlane(tot) * kv_heads;
+    if (W >= (int64_t(1) << 30) || nwg <= 0) {
+        r.ok = false;
+        return r;
+    }
+    const uint32_t w32 = (uint32_t)W, n32 = (uint32_t)nwg;
+    uint32_t t = (w32 + n32 - 1) / n32;
+    r.tstar = (int32_t)(t < 1 ? 1 : t);
+    return r;
+}
+__device__ __forceinline__ bool bal_find(const int64_t* lens, int64_t batch, int64_t kv_seq, int32_t kv_heads,
+                                         int32_t nwg, int64_t w, int64_t* tstar_out, int64_t* b_out, int* n2_out,
+                                         int64_t* j_out, int64_t* L_out) {
+    const BalWave bw = bal_wave(lens, batch, kv_seq, kv_heads, nwg);
+    if (!bw.ok) {
+        const int64_t tstar = bal_tstar(lens, batch, kv_seq, kv_heads, nwg);
+        int64_t nb;
+        if (!bal_locate(lens, batch, kv_seq, kv_heads, tstar, w, b_out, n2_out, j_out, &nb)) return false;
+        *tstar_out = tstar;
+        *L_out = bal_len(lens, *b_out, kv_seq);
+        return true;
+    }
+    const int lane = threadIdx.x & 63;
+    const uint32_t ts = (uint32_t)bw.tstar;
+    const int cnt = (int)(((uint32_t)bw.T + ts - 1) / ts) * kv_heads;  // this batch's workgroups
+    int x = cnt;  // inclusive scan over the lanes
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    const bool hit = cnt > 0 && w >= x - cnt && w < x;
+    const unsigned long long m = __ballot(hit);
+    if (!m) return false;
+    const int src = __builtin_ctzll(m);
+    const uint32_t start = (uint32_t)__builtin_amdgcn_readfirstlane(__shfl(x - cnt, src, 64));
+    const uint32_t nb = (uint32_t)__builtin_amdgcn_readfirstlane(__shfl(cnt, src, 64)) / (uint32_t)kv_heads;
+    const uint32_t rem = (uint32_t)w - start;
+    *tstar_out = bw.tstar;
+    *b_out = src;
+    *n2_out = (int)(rem / nb);
+    *j_out = rem % nb;
+    *L_out = __builtin_amdgcn_readfirstlane(__shfl(bw.L, src, 64));
+    return true;
+}
+// Pieces of batch b under the plan, from one load of the lengths as above.
+__device__ __forceinline__ int64_t bal_row_pieces(const int64_t* lens, int64_t batch, int64_t kv_seq,
+                                                  int32_t kv_heads, int32_t nwg, int64_t b) {
+    const BalWave bw = bal_wave(lens, batch, kv_seq, kv_heads, nwg);
+    if (!bw.ok) return bal_pieces(lens, b, kv_seq, bal_tstar(lens, batch, kv_seq, kv_heads, nwg));
+    const uint32_t Tb = (uint32_t)__builtin_amdgcn_readfirstlane(__shfl(bw.T, (int)b, 64));
+    return (Tb + (uint32_t)bw.tstar - 1) / (uint32_t)bw.tstar;
+}
+
 // Matrix-core stage 1 for grouped heads (1 <= group <= 32, contiguous or
 // paged cache with block sizes a multiple of 16, head_dim 64 or 128): one
 // workgroup per (batch, KV head, split), the same partial layout as

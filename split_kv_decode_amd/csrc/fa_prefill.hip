@@ -347,8 +347,10 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
         }
         if (MASK == 3) asm volatile("" ::: "memory");  // re-read the words after the QK MFMAs instead of holding them
         // MASK 4: a tile wholly left or right of the band of every row of
-        // this wave is skipped (wave-uniform).
-        if (MASK == 4) {
+        // this wave is skipped (wave-uniform) at D <= 128; at D = 256 the
+        // second exit from the step costs more registers than the register
+        // file holds, and the tile runs fully masked instead.
+        if (MASK == 4 && D <= 128) {
             if (j0 + BN - 1 < wrow0 - a.win_left || j0 > wrow0 + 31 + a.win_right) {
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 __syncthreads();
@@ -494,13 +496,18 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
     }
 
     // Epilogue: divide by l, RowInvalid defaults, store in the q layout.  Rows
-    // a packed sequence owns but does not use get the initial 0 / +inf.
+    // a packed sequence owns but does not use get the initial 0 / +inf.  At
+    // D = 256 under a window or staged mask the row is taken again from the
+    // lane id, so no per-lane address computed for the q load stays live
+    // across the loop (those instantiations otherwise spill it).
     const float l_run = l_half + xor32(l_half);
-    if (qrow < q_full) {
-        const bool empty = !qvalid || (m_run == kNegInf);
+    constexpr bool kRowFromLane = D == 256 && (MASK == 3 || MASK == 4);
+    const int64_t qrow_e = kRowFromLane ? wrow0 + (int)(__lane_id() & 31) : qrow;
+    if (qrow_e < q_full) {
+        const bool empty = !(qrow_e < q_used) || (m_run == kNegInf);
         const float inv = empty ? 0.f : 1.f / l_run;
         uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + q_off + (int64_t)n1 * a.q_stride_n +
-                       qrow * a.q_stride_s;
+                       qrow_e * a.q_stride_s;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
@@ -515,7 +522,7 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
                 *reinterpret_cast<u32x2*>(op + d0) = w;
             }
         }
-        if (half == 0 && a.lse) a.lse[lse_row0 + qrow * lse_step] = empty ? kPosInf : (m_run + log2f(l_run)) * kLn2;
+        if (half == 0 && a.lse) a.lse[lse_row0 + qrow_e * lse_step] = empty ? kPosInf : (m_run + log2f(l_run)) * kLn2;
     }
 }
 
@@ -768,11 +775,22 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
     }
     const uint32_t mM0 = lds_address(sM0) + (uint32_t)((wave & 3) * (32 * NWV) + 128 * (wave >> 2)) * 16u;
     const uint32_t mM1 = lds_address(sM1) + (uint32_t)((wave & 3) * (32 * NWV) + 128 * (wave >> 2)) * 16u;
+    // Class of tile jl, asked for in increasing order: the staged word of the
+    // current 16 tiles is kept in a scalar and read from LDS once per word
+    // (an LDS read here would make the slot wait for its in-flight K reads).
+    uint32_t cword = 0u;
+    int cw_idx = -1;
     auto tile_cls = [&](int jl) __attribute__((always_inline)) -> uint32_t {
         const int64_t jt = kbeg / BN + jl;
         if (!summary || jt >= 64 * 16) return 3u;
-        return (__builtin_amdgcn_readfirstlane(s_cls[jt >> 4]) >> (2 * (jt & 15))) & 3u;
+        const int wi = (int)(jt >> 4);
+        if (wi != cw_idx) {
+            cword = __builtin_amdgcn_readfirstlane(s_cls[wi]);
+            cw_idx = wi;
+        }
+        return (cword >> (2 * (jt & 15))) & 3u;
     };
+    uint32_t cls_cur = 3u, cls_nxt = 3u;  // classes of tiles j and j+1 in slot j
     // MASK 2 tile loads (rows of 4-aligned key runs): four keys per lane, one
     // group of 4 rows per wave load (lane l: row 4G + l/16, keys 4(l%16) +
     // [0, 4)), wave w loading groups 8w .. 8w+7 (its own rows); group G sits at
@@ -803,8 +821,8 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
             lds_dma4_m0(r, m0 + (uint32_t)(G * MGP), voff);
         }
     };
-    auto issue_mask = [&](int jl, uint32_t m0) __attribute__((always_inline)) {
-        if (!(tile_cls(jl) & 2u)) return;  // no key masked (or none visible): nothing to stage
+    auto issue_mask = [&](int jl, uint32_t cls, uint32_t m0) __attribute__((always_inline)) {
+        if (!(cls & 2u)) return;  // no key masked (or none visible): nothing to stage
         const int64_t j0 = kbeg + (int64_t)jl * BN;
         int64_t keys = a.kv_seq - j0;
         keys = keys > BN ? BN : keys;
@@ -1032,7 +1050,10 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
         // address unit at the slot's start)
         if (j + 1 < nt) {
             issue(kb64, j + 1, mKn);
-            if constexpr (MASK == 3) issue_mask(j + 1, mMn);
+            if constexpr (MASK == 3) {
+                cls_nxt = tile_cls(j + 1);
+                issue_mask(j + 1, cls_nxt, mMn);
+            }
             if constexpr (MASK == 2) issue_mask_dwords(j + 1, mEn);
         }
         stage_a(std::integral_constant<bool, !LAST>{}, std::integral_constant<bool, !FIRST>{}, Kc, Sn, So, Po, ps1);
@@ -1049,7 +1070,7 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
             // the excluded keys' scores become -inf.
             const int32_t j0 = j * BN;
             uint32_t tcls = 3u;
-            if constexpr (MASK == 3) tcls = tile_cls(j);
+            if constexpr (MASK == 3) tcls = cls_cur;
             if (MASK == 3 && !(tcls & 1u)) {
                 // no key of the tile visible to any row of the workgroup
 #pragma unroll
@@ -1106,6 +1127,7 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
             // key yet: rare rescale against the whole tile's maximum
             if (__any(ps0 > kPmax || (m_run == kNegInf && qvalid))) rescale_b(Sn, Pn, ps0);
         }
+        if constexpr (MASK == 3) cls_cur = cls_nxt;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of slot j+1 landed
         __syncthreads();                                   // ... and everyone else's
     };
@@ -1116,7 +1138,10 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
 
     if (nt > 0) {
         issue(kb64, 0, mK0);
-        if constexpr (MASK == 3) issue_mask(0, mM0);
+        if constexpr (MASK == 3) {
+            cls_cur = tile_cls(0);
+            issue_mask(0, cls_cur, mM0);
+        }
         if constexpr (MASK == 2) issue_mask_dwords(0, mE0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();

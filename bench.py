@@ -24,6 +24,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -42,12 +43,25 @@ METRIC = "prefill attn TFLOP/s (%MFMA peak); decode KV GB/s (%HBM peak) on 1 MI3
 SHARED_HEADERS = ("fa_device.h", "fa_kernels.h", "fa_mfma.h")
 
 
+# A string literal (kept), or a comment (dropped).
+_C_TOKEN = re.compile(r'"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'|//[^\n]*|/\*.*?\*/', re.S)
+
+
+def code_text(src: str) -> str:
+    """C/C++ source with its comments, trailing blanks and empty lines removed: an edit to
+    comments alone leaves it unchanged."""
+    src = _C_TOKEN.sub(lambda m: m.group(0) if m.group(0)[0] in "\"'" else " ", src)
+    return "\n".join(ln.rstrip() for ln in src.splitlines() if ln.strip())
+
+
 def sha256_of(path):
-    """Digest of a kernel source together with the shared device headers beside it."""
+    """Digest of the code (comments removed) of a kernel source together with the shared
+    device headers beside it."""
     h = hashlib.sha256()
     for p in (path,) + tuple(os.path.join(os.path.dirname(path), n) for n in SHARED_HEADERS):
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
+            h.update(b"\0")
     return h.hexdigest()
 
 

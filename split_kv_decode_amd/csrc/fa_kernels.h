@@ -102,8 +102,8 @@ struct PrefillArgs {
     int32_t mask_dwords;      // boolean tensor in runs of 4-byte aligned keys (see prefill_rows_per_tile)
     // Packed layout (work != null): sequence b spans q rows [cu_q[b], cu_q[b+1])
     // and kv rows [cu_kv[b], cu_kv[b+1]) of the [T][N][D] tensors; q_seq and
-    // kv_seq are the totals.  The work list holds (sequence, 128-row q tile)
-    // pairs, heaviest first; sequence index `batch` stands for the rows past
+    // kv_seq are the totals.  The work list holds (sequence, q tile) pairs,
+    // tiles of the kernel's 128 or 256 rows, heaviest first; sequence index `batch` stands for the rows past
     // the last sequence.  Entries (-1, -1) pad the list.
     const int32_t* cu_q;
     const int32_t* cu_kv;

@@ -526,9 +526,11 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
     }
 }
 
-// Interleaved prefill, used for the mask-free D = 128 case: one workgroup of
-// 8 waves per CU, 256 query rows (32 per wave), each 64-key K/V tile loaded
-// into LDS once for all 8 waves.  Every wave runs the same software-pipelined
+// Interleaved prefill, used at D = 128 for every mask kind (a boolean tensor
+// read element by element excepted, unless its key rows are runs of 4-byte
+// aligned words) and for the packed layout: one workgroup of 8 waves per CU,
+// 256 query rows (32 per wave), each 64-key K/V tile loaded into LDS once for
+// all 8 waves.  Every wave runs the same software-pipelined
 // schedule and issues its own matrix and vector work interleaved.  Slot j
 // holds K(j) and V(j-1); a wave spends it in two stages:
 //   A: the 16 products of S(j) = K(j) Q^T, each pair preceded by two

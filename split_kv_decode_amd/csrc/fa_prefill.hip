@@ -1073,30 +1073,33 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
             const int32_t j0 = j * BN;
             uint32_t tcls = 3u;
             if constexpr (MASK == 3) tcls = cls_cur;
-            if (MASK == 3 && !(tcls & 1u)) {
-                // no key of the tile visible to any row of the workgroup
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) Sn[tt][r] = kNegInf;
-            } else if (MASK == 2 || (MASK == 3 && (tcls & 2u))) {
-                // the staged mask tile: word (tt, g) of this lane holds keys
+            // One block changes the scores (a single changed path lets the
+            // compiler keep them in the registers the products wrote; with a
+            // second one, every tile paid 32 copies where the paths join).
+            if (MASK == 2 || (MASK == 3 && (tcls != 1u || j0 + BN - 1 > w_hi))) {
+                // the staged mask tile (MASK 3: when the tile's class says a
+                // key is masked): word (tt, g) of this lane holds keys
                 // 32*tt + 8*g + 4*half + [0, 4) of its row; keys past the
-                // range are excluded too
+                // range are excluded too.  A tile with no key visible to any
+                // row of the workgroup (class bit 0 clear) is excluded whole,
+                // whether or not its mask was staged.
                 const int ln = (int)__lane_id();
                 const int row = 32 * wave + (ln & 31), h4 = (ln >> 5) * 4;
-                const int32_t hi = L32 - 1 - j0 - h4;
+                const int32_t hi = (MASK == 3 && !(tcls & 1u)) ? -0x7fffffff : L32 - 1 - j0 - h4;
+                const bool staged = MASK == 2 || (tcls & 2u);
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) {
-                    uint32_t mw[4];
+                    uint32_t mw[4] = {0u, 0u, 0u, 0u};
+                    if (staged) {
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        if constexpr (MASK == 3)
-                            mw[g] = *reinterpret_cast<const uint32_t*>(
-                                Mc + ((2 * tt + (g >> 1)) * (32 * NWV) + row) * 16 + 8 * (g & 1) + h4);
-                        else
-                            mw[g] = *reinterpret_cast<const uint32_t*>(Mc + (row >> 2) * 272 + (row & 3) * 64 +
-                                                                       32 * tt + 8 * g + h4);
+                        for (int g = 0; g < 4; ++g) {
+                            if constexpr (MASK == 3)
+                                mw[g] = *reinterpret_cast<const uint32_t*>(
+                                    Mc + ((2 * tt + (g >> 1)) * (32 * NWV) + row) * 16 + 8 * (g & 1) + h4);
+                            else
+                                mw[g] = *reinterpret_cast<const uint32_t*>(Mc + (row >> 2) * 272 + (row & 3) * 64 +
+                                                                           32 * tt + 8 * g + h4);
+                        }
                     }
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
@@ -1105,7 +1108,7 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
                         Sn[tt][r] = ok ? Sn[tt][r] : kNegInf;
                     }
                 }
-            } else if (j0 < w_lo || j0 + BN - 1 > w_hi) {
+            } else if (MASK != 2 && MASK != 3 && (j0 < w_lo || j0 + BN - 1 > w_hi)) {
                 // element (tt, r) is key j0 + e + 4*half, e = 32tt + 8(r/4) + r%4
                 const int ln = (int)__lane_id();
                 const int cl = ln & 31, h4 = (ln >> 5) * 4;

@@ -460,10 +460,33 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
             tmax = fmaxf(tmax, xor32(tmax)) * c;
             const float mnew = fmaxf(m_run, tmax);
             const float alpha = fast_exp2(m_run - ((mnew == kNegInf) ? 0.f : mnew));
+            if constexpr (D == 256) {
+                // O lives in the accumulation registers (AGPRs) of the
+                // products; scaled there in place, it needs no vector-register
+                // copy, which the compiler otherwise made at the top of every
+                // KV step whether or not this path ran.  Wait states: the
+                // last product that wrote O is many products back, and each
+                // write is followed by the two a product reading it needs.
+                asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
+                for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+                    for (int r = 0; r < 16; ++r) {
+                        float t;
+                        asm volatile(
+                            "v_accvgpr_read_b32 %1, %0\n\t"
+                            "v_mul_f32 %1, %1, %2\n\t"
+                            "v_accvgpr_write_b32 %0, %1\n\t"
+                            "s_nop 2"
+                            : "+a"(o[dt][r]), "=&v"(t)
+                            : "v"(alpha));
+                    }
+            } else {
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+            }
             l_half *= alpha;
             m_run = mnew;
             exps((m_run == kNegInf) ? 0.f : -m_run);

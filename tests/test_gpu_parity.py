@@ -443,6 +443,13 @@ PREFILL_CASES = [
     dict(B=2, QN=4, KVN=2, QS=300, KVS=300, D=256, mask="causal"),          # D = 256
     dict(B=1, QN=2, KVN=1, QS=129, KVS=700, D=256, dtype="f16", layout="BSND", lens=(1, 700)),
     dict(B=1, QN=2, KVN=2, QS=64, KVS=64, D=256, mask="bool_causal"),
+    # scale 1: scores spread over tens of units, so a row's running max moves
+    # by more than 2^8 well after its first tile and the rescale of a
+    # non-zero output runs often
+    dict(B=1, QN=2, KVN=2, QS=300, KVS=700, D=256, scale=1.0),
+    dict(B=1, QN=2, KVN=1, QS=300, KVS=700, D=256, scale=1.0, mask="causal", layout="BSND"),
+    dict(B=1, QN=2, KVN=1, QS=300, KVS=700, D=128, scale=1.0, mask="causal"),
+    dict(B=1, QN=2, KVN=2, QS=200, KVS=500, D=64, scale=0.7),
 ]
 
 

@@ -54,6 +54,37 @@ namespace fa {
 
 // D = 256 holds 64 + 128 registers of Q and O per lane, so it runs one
 // workgroup per CU with the accumulators in the AGPR half of the file.
+// O *= alpha on the rare rescale path.  At D = 256, O lives in the
+// accumulation registers (AGPRs) of the products; scaled there in place it
+// needs no vector-register copy, which the compiler otherwise made at the top
+// of every KV step whether or not this path ran.  Wait states: the last
+// product that wrote O is many products back, and each write is followed by
+// the two that a product reading it needs.
+template <int D>
+__device__ __forceinline__ void scale_acc(f32x16 (&o)[D / 32], float alpha) {
+    if constexpr (D == 256) {
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float t;
+                asm volatile(
+                    "v_accvgpr_read_b32 %1, %0\n\t"
+                    "v_mul_f32 %1, %1, %2\n\t"
+                    "v_accvgpr_write_b32 %0, %1\n\t"
+                    "s_nop 2"
+                    : "+a"(o[dt][r]), "=&v"(t)
+                    : "v"(alpha));
+            }
+    } else {
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    }
+}
+
 template <typename ST, int D, int MASK>
 __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(PrefillArgs a) {
     using M = Mfma<ST>;
@@ -460,33 +491,7 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
             tmax = fmaxf(tmax, xor32(tmax)) * c;
             const float mnew = fmaxf(m_run, tmax);
             const float alpha = fast_exp2(m_run - ((mnew == kNegInf) ? 0.f : mnew));
-            if constexpr (D == 256) {
-                // O lives in the accumulation registers (AGPRs) of the
-                // products; scaled there in place, it needs no vector-register
-                // copy, which the compiler otherwise made at the top of every
-                // KV step whether or not this path ran.  Wait states: the
-                // last product that wrote O is many products back, and each
-                // write is followed by the two a product reading it needs.
-                asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
-#pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        float t;
-                        asm volatile(
-                            "v_accvgpr_read_b32 %1, %0\n\t"
-                            "v_mul_f32 %1, %1, %2\n\t"
-                            "v_accvgpr_write_b32 %0, %1\n\t"
-                            "s_nop 2"
-                            : "+a"(o[dt][r]), "=&v"(t)
-                            : "v"(alpha));
-                    }
-            } else {
-#pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-            }
+            scale_acc<D>(o, alpha);
             l_half *= alpha;
             m_run = mnew;
             exps((m_run == kNegInf) ? 0.f : -m_run);
@@ -573,13 +578,20 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
 // needed and recomputes what was taken against the old maximum.  K(j+1) is
 // loaded at the start of slot j and V(j) after stage A, with every scalar of
 // the load worked out beforehand; one barrier per slot releases the buffers.
+template <int D>
+constexpr int il_waves() { return D == 256 ? 4 : 8; }
+
 template <typename ST, int D, int MASK>
-__global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64 * il_waves<D>(), 1) void prefill_il_kernel(PrefillArgs a) {
     static_assert(MASK >= 0 && MASK <= 4, "mask kind");
+    static_assert(D == 128 || D == 256, "head dim");
     using M = Mfma<ST>;
     using V8 = typename M::V8;
     using E = typename M::E;
-    constexpr int NWV = 8;              // waves
+    // D = 128: 8 waves, two per SIMD.  D = 256: Q (64 registers) and O (128)
+    // per lane leave room for one wave per SIMD, so 4 waves and 128 rows,
+    // with O in the accumulation registers.
+    constexpr int NWV = il_waves<D>();  // waves
     constexpr int BN = 64;              // keys per KV tile
     constexpr int RB = D * 2;
     constexpr int TB = BN * RB;
@@ -587,8 +599,12 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
     constexpr int RPI = 64 / CPR;
     constexpr int NIW = TB / 1024 / NWV;  // wave loads per wave per tile (K, and again V)
     constexpr int KS = D / 16;            // QK steps (two products each)
-    static_assert(NIW >= 1, "tile too small for 8 waves");
-    static_assert(2 * KS == 16, "two exponentials of a half tile per QK step");
+    constexpr int EPS = 16 / KS;          // exponentials of a half tile per QK step (2, or 1)
+    constexpr int NDT = D / 32;           // 32-column blocks of O
+    constexpr int NPV = 4 * NDT;          // PV products per tile (4 key steps x NDT)
+    constexpr int PPE = NPV / 16;         // PV products per exponential of a half tile (1, or 2)
+    static_assert(NIW >= 1, "tile too small for the waves");
+    static_assert(EPS * KS == 16 && PPE * 16 == NPV, "exponentials spread over the products");
     constexpr float kPmax = 256.f;
     __shared__ __attribute__((aligned(1024))) unsigned char sK0[TB];
     __shared__ __attribute__((aligned(1024))) unsigned char sK1[TB];
@@ -699,19 +715,20 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
         const int64_t key_lo = i0 - a.win_left;
         if (key_lo > 0) kbeg = key_lo / BN * BN;
     }
-    // MASK 3 with a summary of the mask: the classes of the workgroup's two
-    // 128-row tiles, OR-ed (bit 0: some key visible, bit 1: some key masked,
-    // for some row), staged for the loop; the first and last tile with a
-    // visible key bound the range.  Tiles past the 64 staged words count as
-    // partly masked.
+    // MASK 3 with a summary of the mask: the classes of the workgroup's
+    // 128-row tiles (two at D = 128), OR-ed (bit 0: some key visible, bit 1:
+    // some key masked, for some row), staged for the loop; the first and last
+    // tile with a visible key bound the range.  Tiles past the 64 staged
+    // words count as partly masked.
     const bool summary = (MASK == 3) && a.mask_cls != nullptr;
     if (MASK == 3 && summary) {
         const int64_t sn = a.mask_stride[1] ? a.num_heads : 1;
         const int64_t slice = (a.mask_stride[0] ? b : 0) * sn + (a.mask_stride[1] ? n1 : 0);
         const int64_t qt128 = (a.q_seq + kMaskRowsPerTile - 1) / kMaskRowsPerTile;
-        const int64_t r0 = 2 * (int64_t)qt;
+        constexpr int R128 = 32 * NWV / kMaskRowsPerTile;  // summary rows per query tile
+        const int64_t r0 = R128 * (int64_t)qt;
         const uint32_t* c0p = a.mask_cls + (slice * qt128 + r0) * a.cls_words;
-        const uint32_t* c1p = (r0 + 1 < qt128) ? c0p + a.cls_words : nullptr;
+        const uint32_t* c1p = (R128 == 2 && r0 + 1 < qt128) ? c0p + a.cls_words : nullptr;
         int first = 0x7fffffff, last = -1;
         for (int w = lane; w < a.cls_words; w += 64) {
             const uint32_t x = c0p[w] | (c1p ? c1p[w] : 0u);
@@ -888,7 +905,7 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
     };
     // V^T operand of product (ks, dt): keys 16*ks + .., head-dim columns 32*dt + ..
     auto vread = [&](const unsigned char* Vb, int i) __attribute__((always_inline)) -> V8 {
-        const int ks = i >> 2, dt = i & 3;
+        const int ks = i / NDT, dt = i % NDT;
         const int lc = 4 * dt + vx;
         const unsigned char* vb = Vb + ks * 16 * RB;
         const s16x4 lo = lds_read_tr(vb + vrow_lo * RB + ((lc ^ vs_lo) << 4) + vbyte);
@@ -910,7 +927,7 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
 #pragma unroll
             for (int p = 0; p < PF; ++p) kread(Kb, p, kring[p]);
         }
-        float acc = 0.f;
+        float acc = 0.f, pprev = 0.f;
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
             if constexpr (QK) {
@@ -918,7 +935,7 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
             }
             // each step in this order: fragment reads, vector work, products
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (SM) {
+            if constexpr (SM && EPS == 2) {
                 const int r = 2 * kk;
                 const float p0 = fast_exp2(__builtin_fmaf(So[1][r], c, nmx));
                 const float p1 = fast_exp2(__builtin_fmaf(So[1][r + 1], c, nmx));
@@ -929,6 +946,17 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
                 // would otherwise sink them past the products)
                 asm volatile("" : "+v"(acc), "+v"(w));
                 Pd[2 + (r >> 3)][(r & 7) >> 1] = w;
+            } else if constexpr (SM) {  // one exponential per step, converted in pairs
+                const int r = kk;
+                const float p = fast_exp2(__builtin_fmaf(So[1][r], c, nmx));
+                acc += p;
+                if (r & 1) {
+                    uint32_t w = cvt_pair<ST>(pprev, p);
+                    asm volatile("" : "+v"(acc), "+v"(w));
+                    Pd[2 + (r >> 3)][(r & 7) >> 1] = w;
+                } else {
+                    pprev = p;
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (QK) {
@@ -955,24 +983,27 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
         }
         float acc = 0.f, pprev = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < NPV; ++i) {
             if constexpr (PV) {
-                if (i + VPF < 16) vring[(i + VPF) % (VPF + 1)] = vread(Vb, i + VPF);
+                if (i + VPF < NPV) vring[(i + VPF) % (VPF + 1)] = vread(Vb, i + VPF);
             }
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (SM) {
-                const float p = fast_exp2(__builtin_fmaf(Sn[0][i], c, nmx));
-                acc += p;
-                if (i & 1) {
-                    uint32_t w = cvt_pair<ST>(pprev, p);
-                    asm volatile("" : "+v"(acc), "+v"(w));
-                    Pn[i >> 3][(i & 7) >> 1] = w;
-                } else {
-                    pprev = p;
+                if (i % PPE == 0) {
+                    const int e = i / PPE;
+                    const float p = fast_exp2(__builtin_fmaf(Sn[0][e], c, nmx));
+                    acc += p;
+                    if (e & 1) {
+                        uint32_t w = cvt_pair<ST>(pprev, p);
+                        asm volatile("" : "+v"(acc), "+v"(w));
+                        Pn[e >> 3][(e & 7) >> 1] = w;
+                    } else {
+                        pprev = p;
+                    }
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (PV) o[i & 3] = M::mm(vring[i % (VPF + 1)], __builtin_bit_cast(V8, Po[i >> 2]), o[i & 3]);
+            if constexpr (PV) o[i % NDT] = M::mm(vring[i % (VPF + 1)], __builtin_bit_cast(V8, Po[i / NDT]), o[i % NDT]);
             __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (SM) ps0 = acc;
@@ -991,10 +1022,7 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
         tmax = fmaxf(tmax, xor32(tmax)) * c;
         const float mnew = fmaxf(m_run, tmax);
         const float alpha = fast_exp2(m_run - ((mnew == kNegInf) ? 0.f : mnew));
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+        scale_acc<D>(o, alpha);
         l_half *= alpha;
         m_run = mnew;
         const float nmx = (m_run == kNegInf) ? 0.f : -m_run;
@@ -1024,10 +1052,7 @@ __global__ __launch_bounds__(512, 1) void prefill_il_kernel(PrefillArgs a) {
         // (a row that has seen no key yet -- a window's left edge, rows a
         // wave shares -- keeps the reference -inf and exponentials against 0)
         const float alpha = fast_exp2(m_run - ((mnew == kNegInf) ? 0.f : mnew));
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+        scale_acc<D>(o, alpha);
         l_half *= alpha;
         m_run = mnew;
         const float nmx = (m_run == kNegInf) ? 0.f : -m_run;
@@ -1226,37 +1251,47 @@ static hipError_t dispatch_prefill(const PrefillArgs& a, int mask_mode, int64_t 
     return hipGetLastError();
 }
 
-template <typename ST>
+template <typename ST, int D>
 static hipError_t launch_il(const PrefillArgs& a0, int mask_mode, int64_t batch, hipStream_t s) {
+    constexpr int R = 32 * il_waves<D>();  // query rows per workgroup
     PrefillArgs a = a0;
-    a.q_tiles = (int32_t)((a.q_seq + 255) / 256);
+    a.q_tiles = (int32_t)((a.q_seq + R - 1) / R);
     const int64_t blocks = a.work ? (int64_t)(a.work_items + 7) / 8 * 8 * a.num_heads
                                   : (int64_t)a.q_tiles * batch * a.num_heads;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)blocks), block(512);
+    const dim3 grid((unsigned)blocks), block(2 * R);
     switch (mask_mode) {
-        case 0: hipLaunchKernelGGL((prefill_il_kernel<ST, 128, 0>), grid, block, 0, s, a); break;
-        case 1: hipLaunchKernelGGL((prefill_il_kernel<ST, 128, 1>), grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((prefill_il_kernel<ST, 128, 2>), grid, block, 0, s, a); break;
-        case 3: hipLaunchKernelGGL((prefill_il_kernel<ST, 128, 3>), grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((prefill_il_kernel<ST, 128, 4>), grid, block, 0, s, a); break;
+        case 0: hipLaunchKernelGGL((prefill_il_kernel<ST, D, 0>), grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((prefill_il_kernel<ST, D, 1>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((prefill_il_kernel<ST, D, 2>), grid, block, 0, s, a); break;
+        case 3: hipLaunchKernelGGL((prefill_il_kernel<ST, D, 3>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((prefill_il_kernel<ST, D, 4>), grid, block, 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
+// The interleaved kernel takes head dims 128 and 256 with every mask kind
+// but a boolean tensor read element by element.
+static bool prefill_interleaved(int head_dim, int mask_mode, bool mask_dwords) {
+    return (head_dim == 128 || head_dim == 256) && !(mask_mode == 2 && !mask_dwords);
+}
+
 int prefill_rows_per_tile(int head_dim, int mask_mode, bool mask_dwords) {
-    if (head_dim != 128) return 128;
-    if (mask_mode == 2 && !mask_dwords) return 128;
-    return 256;
+    if (!prefill_interleaved(head_dim, mask_mode, mask_dwords)) return 128;
+    return head_dim == 256 ? 32 * il_waves<256>() : 32 * il_waves<128>();
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int mask_mode, int64_t batch,
                           hipStream_t stream) {
-    if (prefill_rows_per_tile(head_dim, mask_mode, a.mask_dwords != 0) == 256) {
+    if (prefill_interleaved(head_dim, mask_mode, a.mask_dwords != 0)) {
         if (a.q_seq <= 0 || batch <= 0) return hipSuccess;
-        return dtype == 1 ? launch_il<BF16>(a, mask_mode, batch, stream) : launch_il<F16>(a, mask_mode, batch, stream);
+        if (head_dim == 256)
+            return dtype == 1 ? launch_il<BF16, 256>(a, mask_mode, batch, stream)
+                              : launch_il<F16, 256>(a, mask_mode, batch, stream);
+        return dtype == 1 ? launch_il<BF16, 128>(a, mask_mode, batch, stream)
+                          : launch_il<F16, 128>(a, mask_mode, batch, stream);
     }
     const int64_t blocks = a.work ? (int64_t)(a.work_items + 7) / 8 * 8 * a.num_heads
                                   : (int64_t)a.q_tiles * batch * a.num_heads;

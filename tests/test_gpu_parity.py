@@ -502,10 +502,11 @@ def _bool_mask_run(inp, mask_np, strides, byte_offset=0, summary=False):
 
 
 @pytest.mark.parametrize("D", [128, 256])
-@pytest.mark.parametrize("byte_offset", [0, 1], ids=["lds_staged", "elementwise"])
+@pytest.mark.parametrize("byte_offset", [0, 4, 1], ids=["lds_staged", "dword_staged", "elementwise"])
 def test_prefill_bool_mask_both_paths(byte_offset, D):
-    """Rows of 16-byte aligned keys go through LDS (with per-wave tile skipping);
-    a misaligned mask pointer takes the element-wise path.  Both match the oracle."""
+    """Rows of 16-byte aligned keys go through LDS in 16-byte loads (with per-wave
+    tile skipping), rows of 4-byte aligned keys in 4-byte loads; a misaligned mask
+    pointer takes the element-wise path.  All match the oracle."""
     s = spec(layout="BNSD", B=2, QN=4, KVN=2, QS=200, KVS=320, D=D, lens=(150, 320), seed=29)
     inp = fa_synth.make(s)
     rng = np.random.default_rng(5)
@@ -773,6 +774,8 @@ PACKED_CASES = [
     (dict(B=7, QN=2, KVN=1, D=128, q_lens=(0, 3)), "none", None),                 # tiny and empty
     (dict(B=2, QN=2, KVN=2, D=64, q_lens=(129, 260), scale=-0.1), "causal", None),
     (dict(B=3, QN=4, KVN=2, D=256, q_lens=(1, 300)), "causal", None),
+    (dict(B=4, QN=4, KVN=1, D=128, q_lens=(1, 600), kv_lens=(100, 700)), "window", (200, 0)),
+    (dict(B=3, QN=2, KVN=2, D=256, dtype="f16", q_lens=(50, 400)), "window", (100, 30)),
 ]
 
 

@@ -1164,3 +1164,70 @@ def test_decode_fused_on_paged_cache(paging, g):
     torch.cuda.synchronize()
     ref, ref_lse = oracle.attention(oracle.Problem.from_inputs(inp), inp.q, inp.k, inp.v)
     check(to_np(out), to_np(lse), ref, ref_lse, f"fused paged {paging}")
+
+
+# ------------------------------------------------------------------ offsets past 2^31 elements
+
+@pytest.mark.parametrize("QN", [8, 32], ids=["vector_stage1", "matrix_core_stage1"])
+def test_decode_offsets_past_2_31_elements(QN):
+    """Decode whose last batch's K and V start at element 2^31 (4 GiB of bf16 in):
+    17 batches of 131072 keys x 8 KV heads x 128.  The far batch holds random data
+    at full length; the others random data in a short prefix (their used lengths)
+    and zeros beyond.  Each part is checked against the oracle on that part alone."""
+    B, KVN, S, D = 17, 8, 131072, 128
+    rng = np.random.default_rng(2031)
+    far = fa_synth.make(spec(layout="BSND", B=1, QN=QN, KVN=KVN, QS=1, KVS=S, D=D, seed=2032))
+    near_lens = rng.integers(1, 65, size=B - 1).astype(np.int64)
+    near = fa_synth.make(spec(layout="BSND", B=B - 1, QN=QN, KVN=KVN, QS=1, KVS=64, D=D, seed=2033))
+    near.lens = near_lens
+    k = torch.zeros((B, S, KVN, D), dtype=torch.bfloat16, device=DEV)
+    v = torch.zeros_like(k)
+    assert 16 * k.stride(0) == 2 ** 31
+    k[B - 1] = dev16(far.k, "bf16")[0]
+    v[B - 1] = dev16(far.v, "bf16")[0]
+    k[: B - 1, :64] = dev16(near.k, "bf16")
+    v[: B - 1, :64] = dev16(near.v, "bf16")
+    q = torch.cat([dev16(near.q, "bf16"), dev16(far.q, "bf16")])
+    lens = torch.from_numpy(np.concatenate([near_lens, [S]])).to(DEV)
+    out, lse = fa.fwd(q, k, v, layout="BSND", scale=far.spec.softmax_scale, actual_seq_lengths=lens,
+                      return_lse=True)
+    torch.cuda.synchronize()
+    del k, v
+    for part, sl in ((far, slice(B - 1, B)), (near, slice(0, B - 1))):
+        ref, ref_lse = oracle.attention(oracle.Problem.from_inputs(part, "none"), part.q, part.k, part.v)
+        s = part.spec
+        got = to_np(out[sl].permute(0, 2, 1, 3)).reshape(-1, D)
+        r_rows = np.ascontiguousarray(ref.transpose(0, 2, 1, 3)).reshape(-1, D)
+        check(got, to_np(lse[sl]).reshape(-1), r_rows, ref_lse.reshape(-1), f"decode past 2^31, {s.B} batches")
+
+
+def test_packed_prefill_offsets_past_2_31_elements():
+    """Packed causal prefill of 4097 sequences of 128 tokens, 32/8 heads, D = 128: the
+    last sequence's q rows start at element 2^31.  That sequence holds random data and
+    is checked against the oracle; the others are all zeros, where every row's output
+    is exactly 0 and its lse is ln(visible keys)."""
+    NS, L, QN, KVN, D = 4097, 128, 32, 8, 128
+    T = NS * L
+    last = fa_synth.make(spec(layout="BSND", B=1, QN=QN, KVN=KVN, QS=L, KVS=L, D=D, mask="causal", seed=2034))
+    q = torch.zeros((T, QN, D), dtype=torch.bfloat16, device=DEV)
+    k = torch.zeros((T, KVN, D), dtype=torch.bfloat16, device=DEV)
+    v = torch.zeros_like(k)
+    assert (T - L) * q.stride(0) == 2 ** 31
+    q[T - L:] = dev16(last.q, "bf16")[0]
+    k[T - L:] = dev16(last.k, "bf16")[0]
+    v[T - L:] = dev16(last.v, "bf16")[0]
+    cu = torch.arange(0, T + 1, L, dtype=torch.int32, device=DEV)
+    out, lse = fa.fwd(q, k, v, layout="TND", scale=last.spec.softmax_scale, causal=True,
+                      cu_seqlens_q=cu, cu_seqlens_kv=cu, return_lse=True)
+    torch.cuda.synchronize()
+    del q, k, v
+    ref, ref_lse = oracle.attention(oracle.Problem.from_inputs(last), last.q, last.k, last.v)
+    got = to_np(out[T - L:].permute(1, 0, 2)).reshape(-1, D)
+    r_rows = np.ascontiguousarray(ref.transpose(0, 2, 1, 3)).reshape(-1, D)
+    check(got, to_np(lse[T - L:].t()).reshape(-1), r_rows, ref_lse.reshape(-1), "packed prefill past 2^31")
+    for seq in (0, NS // 2, NS - 2):
+        rows = slice(seq * L, (seq + 1) * L)
+        assert torch.count_nonzero(out[rows]).item() == 0, f"sequence {seq}: non-zero output"
+        want = np.log(np.arange(1, L + 1, dtype=np.float64))[:, None]
+        err = np.abs(to_np(lse[rows]) - want).max()
+        assert err <= LSE_TOL, f"sequence {seq}: lse err {err:.3e}"

@@ -301,6 +301,18 @@ fa_status fa_combine(const fa_params *p, int64_t num_splits, const float *o_part
 fa_status fa_fwd_noalloc(const fa_params *p, const void *q, const void *k, const void *v,
                          void *out, float *lse, void *stream);
 
+/* fa_describe -- one line of text naming what fa_fwd would launch for p: the
+ * path (prefill, decode, general split), each kernel with its instantiation
+ * <dtype, head dim, mask kind> and grid, the split plan, and the workspace
+ * bytes (as fa_workspace_size).  The FlashAttn page's Quick Start finds the
+ * kernel variant a case launched (its tiling key) in the run logs; this is
+ * the same information for this library.  With the environment variable
+ * FA_LOG set (and not "0"), fa_fwd prints this line to stderr before it
+ * launches.  buf receives at most buf_bytes bytes, NUL-terminated (longer
+ * text is cut).  Validates p like fa_fwd; reads no device memory and
+ * launches nothing (on a host without a GPU the plan assumes 256 CUs). */
+fa_status fa_describe(const fa_params *p, char *buf, size_t buf_bytes);
+
 /* Text of the last non-OK status returned on the calling thread ("" if none). */
 const char *fa_last_error(void);
 

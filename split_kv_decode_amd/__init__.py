@@ -29,7 +29,7 @@ FA_KV_CONTIGUOUS, FA_KV_PAGED_BBND, FA_KV_PAGED_BNBD = 0, 1, 2
 KV_LAYOUTS = {"contiguous": FA_KV_CONTIGUOUS, "PA_BBND": FA_KV_PAGED_BBND, "PA_BNBD": FA_KV_PAGED_BNBD}
 
 EXPORTS = ("fa_workspace_size", "fa_fwd", "fa_fwd_noalloc", "fa_splitkv_plan", "fa_decode_fused_plan",
-           "fa_decode_splitkv", "fa_decode_fused", "fa_combine", "fa_last_error")
+           "fa_decode_splitkv", "fa_decode_fused", "fa_combine", "fa_describe", "fa_last_error")
 
 
 class FaError(RuntimeError):
@@ -76,8 +76,10 @@ def load(path: Optional[str] = None):
             lib.fa_decode_splitkv.argtypes = [P(FaParams), i64, i64, vp, vp, vp, vp, vp, vp, vp]
             lib.fa_combine.argtypes = [P(FaParams), i64, vp, vp, vp, vp, vp, vp]
             lib.fa_decode_fused.argtypes = [P(FaParams), i64, i64, vp, vp, vp, vp, sz, vp, vp, vp]
+            lib.fa_describe.argtypes = [P(FaParams), ctypes.c_char_p, sz]
             for f in (lib.fa_workspace_size, lib.fa_fwd, lib.fa_fwd_noalloc, lib.fa_splitkv_plan,
-                      lib.fa_decode_fused_plan, lib.fa_decode_splitkv, lib.fa_combine, lib.fa_decode_fused):
+                      lib.fa_decode_fused_plan, lib.fa_decode_splitkv, lib.fa_combine, lib.fa_decode_fused,
+                      lib.fa_describe):
                 f.restype = ctypes.c_int
             lib.fa_last_error.argtypes = []
             lib.fa_last_error.restype = ctypes.c_char_p
@@ -137,6 +139,13 @@ def make_params(batch, num_heads, q_seq, kv_seq, head_dim, *, num_kv_heads=0, la
     # freed (and its memory handed to the next allocation) before the call.
     p._keep = (actual_seq_lengths, mask, block_table, cu_seqlens_q, cu_seqlens_kv, seqused_q)
     return p
+
+
+def fa_describe(params: FaParams) -> str:
+    """The line fa_fwd would log (FA_LOG=1) for these parameters: path, kernels, plan."""
+    buf = ctypes.create_string_buffer(1024)
+    _check(load().fa_describe(ctypes.byref(params), buf, len(buf)))
+    return buf.value.decode()
 
 
 def fa_workspace_size(params: FaParams) -> int:

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 
@@ -380,8 +381,8 @@ bool general_split_ok(const fa_params* p, const Shape& s) {
 }
 int row_groups(const Shape& s) { return (int)((s.g * s.QS + 31) / 32); }
 
-// Prefill workgroups for this shape: 256-row tiles for the interleaved
-// kernel (mask-free, D = 128), 128-row tiles otherwise.
+// Prefill workgroups for this shape: the interleaved kernel's tiles (256
+// rows at D = 128, 128 at D = 256), 128-row tiles for the tiled kernel.
 int64_t prefill_workgroups(const fa_params* p, const Shape& s) {
     const int64_t rows = fa::prefill_rows_per_tile((int)s.D, prefill_mask_kind(p, s), mask_in_dwords(p, s));
     return s.B * s.QN * ((s.QS + rows - 1) / rows);
@@ -703,11 +704,86 @@ void* scratch_address(int dev) {
     return ptr;
 }
 
+// One line naming what fa_fwd launches for p: the path, each kernel with its
+// instantiation and grid, the split plan and the workspace it needs.
+std::string describe(const fa_params* p, const Shape& s) {
+    static const char* kMask[] = {"none", "causal", "bool", "window"};
+    const char* dt = p->dtype == FA_BF16 ? "BF16" : "F16";
+    const char* lay = p->layout == FA_TND ? "TND" : (p->layout == FA_BSND ? "BSND" : "BNSD");
+    const char* kv = p->kv_layout == FA_KV_PAGED_BBND ? "PA_BBND" : (p->kv_layout == FA_KV_PAGED_BNBD ? "PA_BNBD" : "contiguous");
+    const int mmode = (p->mask_mode >= 0 && p->mask_mode <= 3) ? (int)p->mask_mode : 0;
+    char head[256], body[512];
+    std::snprintf(head, sizeof head, "%s %s B=%lld Q_N=%lld KV_N=%lld Q_S=%lld KV_S=%lld D=%lld mask=%s kv=%s", lay, dt,
+                  (long long)s.B, (long long)s.QN, (long long)s.KVN, (long long)s.QS, (long long)s.KVS, (long long)s.D,
+                  kMask[mmode], kv);
+    size_t ws = 0;
+    if (p->layout == FA_TND) {
+        ws = varlen_bytes(s);
+    } else if (choose_path(p, s) == Path::kPrefill) {
+        ws = mask_summary_geom(p, s).bytes;
+    } else {
+        const DecodePlan dp = decode_plan(p, s);
+        if (dp.splits > 1 || dp.bal_nwg > 0) ws = partial_bytes(s, dp.splits).total;
+    }
+    const Path path = choose_path(p, s);
+    if (path == Path::kPrefill) {
+        const int mk = prefill_mask_kind(p, s);
+        const bool dw = mask_in_dwords(p, s);
+        const bool il = fa::prefill_interleaved((int)s.D, mk, dw);
+        const int64_t rows = fa::prefill_rows_per_tile((int)s.D, mk, dw);
+        const MaskSummaryGeom mg = mask_summary_geom(p, s);
+        char grid[96];
+        if (p->layout == FA_TND)
+            std::snprintf(grid, sizeof grid, "(work list of <= %lld items) x %lld heads", (long long)varlen_capacity(s),
+                          (long long)s.QN);
+        else
+            std::snprintf(grid, sizeof grid, "%lld", (long long)prefill_workgroups(p, s));
+        std::snprintf(body, sizeof body, "path=prefill%s%s kernel=%s<%s,%lld,%d> rows=%lld workgroups=%s%s",
+                      p->layout == FA_TND ? " pre=varlen_schedule_kernel" : "",
+                      mg.blocks > 0 ? " pre=mask_summary_kernel (with a workspace)" : "",
+                      il ? "prefill_il_kernel" : "prefill_kernel", dt, (long long)s.D, mk, (long long)rows, grid,
+                      mk == 2 ? (dw ? " mask=4-byte runs" : " mask=element-wise") : "");
+    } else {
+        const DecodePlan dp = decode_plan(p, s);
+        const bool mm = uses_mfma(p, s);
+        const bool split = dp.splits > 1 || dp.bal_nwg > 0;
+        char plan[128];
+        if (dp.bal_nwg > 0)
+            std::snprintf(plan, sizeof plan, "length-balanced pieces=%d slots/row=%lld", dp.bal_nwg, (long long)dp.splits);
+        else
+            std::snprintf(plan, sizeof plan, "splits=%lld chunk=%lld", (long long)dp.splits, (long long)dp.chunk);
+        std::snprintf(body, sizeof body, "path=%s stage1=%s%s %s%s", path == Path::kFastDecode ? "decode" : "general-split",
+                      mm ? "decode_mfma_kernel waves=" : "decode_stage1_kernel", mm ? std::to_string(dp.waves).c_str() : "",
+                      plan, split ? " then combine_kernel" : " (finishes in place)");
+    }
+    char line[900];
+    std::snprintf(line, sizeof line, "%s -> %s workspace=%zu", head, body, ws);
+    return line;
+}
+
+bool log_enabled() {
+    static const bool on = [] {
+        const char* e = std::getenv("FA_LOG");
+        return e && e[0] && std::strcmp(e, "0") != 0;
+    }();
+    return on;
+}
+
 }  // namespace
 
 extern "C" {
 
 const char* fa_last_error(void) { return g_last_error.c_str(); }
+
+fa_status fa_describe(const fa_params* p, char* buf, size_t buf_bytes) {
+    Shape s;
+    fa_status st = check_params(p, &s);
+    if (st != FA_OK) return st;
+    if (!buf || buf_bytes == 0) return fail(FA_ERR_NULLPTR, "buf must not be NULL and buf_bytes must be > 0");
+    const std::string d = describe(p, s);
+    std::snprintf(buf, buf_bytes, "%s", d.c_str());
+    return ok();
+}
 
 fa_status fa_splitkv_plan(const fa_params* p, int num_cus, int64_t chunk_hint, int64_t* num_splits, int64_t* chunk,
                           size_t* workspace_bytes) {
@@ -796,6 +872,7 @@ fa_status fa_fwd(const fa_params* p, const void* q, const void* k, const void* v
     if (st != FA_OK) return st;
     st = check_tensors(q, k, v, out, lse);
     if (st != FA_OK) return st;
+    if (log_enabled()) std::fprintf(stderr, "fa_fwd: %s\n", describe(p, s).c_str());
     hipStream_t hs = static_cast<hipStream_t>(stream);
     if (p->layout == FA_TND) {
         const size_t need = varlen_bytes(s);

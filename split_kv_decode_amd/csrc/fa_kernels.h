@@ -347,6 +347,7 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, bool
 // a boolean tensor not staged in 16-byte runs needs runs of 4-byte aligned
 // keys, mask_dwords), else 128.
 int prefill_rows_per_tile(int head_dim, int mask_mode, bool mask_dwords);
+bool prefill_interleaved(int head_dim, int mask_mode, bool mask_dwords);
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int mask_mode,
                           int64_t batch, hipStream_t stream);
 hipError_t launch_varlen_schedule(const VarlenScheduleArgs& a, hipStream_t stream);

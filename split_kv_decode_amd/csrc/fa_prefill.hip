@@ -1274,7 +1274,7 @@ static hipError_t launch_il(const PrefillArgs& a0, int mask_mode, int64_t batch,
 
 // The interleaved kernel takes head dims 128 and 256 with every mask kind
 // but a boolean tensor read element by element.
-static bool prefill_interleaved(int head_dim, int mask_mode, bool mask_dwords) {
+bool prefill_interleaved(int head_dim, int mask_mode, bool mask_dwords) {
     return (head_dim == 128 || head_dim == 256) && !(mask_mode == 2 && !mask_dwords);
 }
 

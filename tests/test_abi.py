@@ -373,3 +373,70 @@ def test_params_keep_the_tensors_they_point_to_alive():
     del p
     gc.collect()
     assert all(r() is None for r in refs)
+
+
+def test_describe_names_path_kernels_and_plan(lib):
+    """fa_describe: the line FA_LOG prints, for one shape of each path; its
+    workspace figure is fa_workspace_size's."""
+    F = 1 << 20  # fake device address: nothing is read
+    cases = [
+        (dict(batch=2, num_heads=32, q_seq=4096, kv_seq=4096, head_dim=128, layout="BSND"),
+         ["path=prefill", "prefill_il_kernel<BF16,128,0>", "rows=256", "workgroups=1024"]),
+        (dict(batch=2, num_heads=16, q_seq=4096, kv_seq=4096, head_dim=256, mask_mode="causal", dtype="f16"),
+         ["prefill_il_kernel<F16,256,1>", "rows=128", "workgroups=1024"]),
+        (dict(batch=2, num_heads=4, q_seq=300, kv_seq=320, head_dim=128, mask_mode="bool", mask=F,
+              mask_stride=(4 * 300 * 320, 300 * 320, 320, 1)),
+         ["pre=mask_summary_kernel", "prefill_il_kernel<BF16,128,3>"]),
+        (dict(batch=2, num_heads=4, q_seq=300, kv_seq=320, head_dim=128, mask_mode="bool", mask=F + 1,
+              mask_stride=(4 * 300 * 320, 300 * 320, 320, 1)),
+         ["prefill_kernel<BF16,128,2>", "mask=element-wise", "rows=128"]),
+        (dict(batch=2, num_heads=4, q_seq=300, kv_seq=320, head_dim=128, mask_mode="bool", mask=F + 4,
+              mask_stride=(4 * 300 * 320, 300 * 320, 320, 1)),
+         ["prefill_il_kernel<BF16,128,2>", "mask=4-byte runs", "rows=256"]),
+        (dict(batch=1, num_heads=32, q_seq=1, kv_seq=131072, head_dim=128),
+         ["path=decode", "stage1=decode_stage1_kernel", "then combine_kernel"]),
+        (dict(batch=8, num_heads=32, num_kv_heads=8, q_seq=1, kv_seq=4096, head_dim=128, layout="BSND",
+              actual_seq_lengths=F),
+         ["path=decode", "stage1=decode_mfma_kernel", "length-balanced", "then combine_kernel"]),
+        (dict(batch=1, num_heads=32, num_kv_heads=8, q_seq=8, kv_seq=65536, head_dim=128, layout="BSND"),
+         ["path=general-split", "stage1=decode_mfma_kernel", "then combine_kernel"]),
+        (dict(batch=16, num_heads=32, num_kv_heads=8, q_seq=55635, kv_seq=55635, head_dim=128, layout="TND",
+              mask_mode="causal", cu_seqlens_q=F, cu_seqlens_kv=F),
+         ["path=prefill", "pre=varlen_schedule_kernel", "prefill_il_kernel<BF16,128,1>", "32 heads"]),
+    ]
+    for kw, want in cases:
+        p = fa.make_params(**kw)
+        d = fa.fa_describe(p)
+        for w in want:
+            assert w in d, (w, d)
+        assert d.endswith(f"workspace={fa.fa_workspace_size(p)}"), d
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_describe(fa.make_params(1, 3, 1, 64, 128, num_kv_heads=2))
+    assert e.value.status == fa.FA_ERR_PARAM_INVALID
+    p = fa.make_params(1, 2, 1, 64, 128)
+    assert lib.fa_describe(ctypes.byref(p), None, 16) == fa.FA_ERR_NULLPTR
+    buf = ctypes.create_string_buffer(12)  # longer text is cut, NUL-terminated
+    assert lib.fa_describe(ctypes.byref(p), buf, 12) == fa.FA_OK and len(buf.value) == 11
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="launches with fake addresses: CPU-only hosts")
+def test_fa_log_prints_the_plan_before_launching():
+    """FA_LOG=1: fa_fwd prints fa_describe's line to stderr before it launches (here the
+    launch then fails: no GPU); without FA_LOG it prints nothing."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import split_kv_decode_amd as fa\n"
+            "p = fa.make_params(2, 32, 256, 256, 128, layout='BSND')\n"
+            "try:\n    fa.fa_fwd(p, 1 << 20, 1 << 20, 1 << 20, 1 << 20)\n"
+            "except fa.FaError as e:\n    print(e.status)\n") % os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for env_val, expect in (("1", True), ("0", False), (None, False)):
+        env = dict(os.environ)
+        env.pop("FA_LOG", None)
+        if env_val is not None:
+            env["FA_LOG"] = env_val
+        r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+        logged = [ln for ln in r.stderr.splitlines() if ln.startswith("fa_fwd: ")]
+        assert bool(logged) == expect, (env_val, r.stderr)
+        if expect:
+            assert "path=prefill kernel=prefill_il_kernel<BF16,128,0>" in logged[0]

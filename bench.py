@@ -486,7 +486,7 @@ def split_decode_workloads(fa, fa_synth, np, torch, dev16, stream, warmup, iters
         gbs = nb / (ms * 1e-3) / 1e9
         res[spec.name] = {"ms": round(ms, 5), "kv_gbs": round(gbs, 1),
                           "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes": nb,
-                          "path": "split-KV, general stage 1 + combine", "doc": spec.doc}
+                          "path": fa.fa_describe(p).split(" -> ")[1], "doc": spec.doc}
         del q, k, v, out, lse, ws, mask, inp
         torch.cuda.empty_cache()
     return res

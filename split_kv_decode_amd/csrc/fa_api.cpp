@@ -48,6 +48,7 @@ struct Shape {
 };
 
 bool fast_decode(const fa_params* p);
+bool vector_masked_decode(const fa_params* p, const Shape& s);
 bool general_split_ok(const fa_params* p, const Shape& s);
 int row_groups(const Shape& s);
 int prefill_mask_kind(const fa_params* p, const Shape& s);
@@ -176,7 +177,7 @@ std::atomic<int> g_cus[kMaxDevices];
 // Stage-1 residency per device and (dtype, D, heads per workgroup, paged):
 // 2 x 3 x 4 x 2 = 48 instantiations, then the matrix-core stage 1 per
 // (dtype, D in {64, 128}, paged, waves); 0 = not asked yet, -1 = no answer.
-std::atomic<int> g_resident[kMaxDevices][64];
+std::atomic<int> g_resident[kMaxDevices][96];
 
 int current_device() {
     int dev = 0;
@@ -194,16 +195,17 @@ int device_cus() {
     return n;
 }
 
-int stage1_residency(int dtype, int D, int gh, bool paged) {
+int stage1_residency(int dtype, int D, int gh, bool paged, bool masked = false) {
     const int dev = current_device();
     const int di = D == 64 ? 0 : (D == 128 ? 1 : 2);
     const int gi = gh == 1 ? 0 : (gh == 2 ? 1 : (gh == 4 ? 2 : 3));
-    const int key = ((dtype * 3 + di) * 4 + gi) * 2 + (paged ? 1 : 0);
+    // keys 0..47 unmasked, 48..63 the matrix-core kernel, 64..87 masked (contiguous)
+    const int key = masked ? 64 + (dtype * 3 + di) * 4 + gi : ((dtype * 3 + di) * 4 + gi) * 2 + (paged ? 1 : 0);
     if (dev >= 0) {
         const int cached = g_resident[dev][key].load(std::memory_order_relaxed);
         if (cached != 0) return cached > 0 ? cached : 0;
     }
-    const int n = fa::decode_stage1_residency(dtype, D, gh, paged);
+    const int n = fa::decode_stage1_residency(dtype, D, gh, paged, masked);
     if (dev >= 0) g_resident[dev][key].store(n > 0 ? n : -1, std::memory_order_relaxed);
     return n;
 }
@@ -286,7 +288,9 @@ static_assert(kShortChunk / 16 + 2 <= fa::kLaneBlocks, "one-wave paged chunks ou
 
 // Stage 1 runs on the matrix cores: grouped heads on the fast decode path,
 // and always on the general split path.
-bool uses_mfma(const fa_params* p, const Shape& s) { return fast_decode(p) ? mfma_decode(p, s) : true; }
+bool uses_mfma(const fa_params* p, const Shape& s) {
+    return (fast_decode(p) || vector_masked_decode(p, s)) ? mfma_decode(p, s) : true;
+}
 
 void plan_splits(const fa_params* p, const Shape& s, int num_cus, int64_t* splits, int64_t* chunk, int waves = 2) {
     const int gh = heads_per_workgroup(s.g);
@@ -296,7 +300,8 @@ void plan_splits(const fa_params* p, const Shape& s, int num_cus, int64_t* split
     // row groups.
     const int64_t units = mm ? s.B * s.KVN * (fast_decode(p) ? 1 : row_groups(s)) : s.B * s.KVN * (s.g / gh);
     const int resident = mm ? mfma_residency(p->dtype == FA_BF16 ? 1 : 0, (int)s.D, paged, waves)
-                            : stage1_residency(p->dtype == FA_BF16 ? 1 : 0, (int)s.D, gh, paged);
+                            : stage1_residency(p->dtype == FA_BF16 ? 1 : 0, (int)s.D, gh, paged,
+                                               vector_masked_decode(p, s));
     const int64_t target = (resident > 0 ? resident : kWgPerCu) * int64_t(num_cus > 0 ? num_cus : 256);
     int64_t want = (target + units - 1) / units;
     if (want < 1) want = 1;
@@ -367,6 +372,17 @@ bool fast_decode(const fa_params* p) {
     return p->q_seq == 1 && p->mask_mode == FA_MASK_NONE && !p->seqused_q && p->layout != FA_TND;
 }
 
+// One query position under a boolean mask tensor with unit key stride, on a
+// contiguous cache, in
+// a shape the matrix-core stage 1 does not take (fewer than 4 or more than 32
+// query heads per KV head, or head_dim 256): the vector stage 1 applies the
+// mask per key (aclnnIncreFlashAttention, attenMask of shape (B|1, N|1, 1, S))
+// and the split plan is the unmasked one.
+bool vector_masked_decode(const fa_params* p, const Shape& s) {
+    return p->q_seq == 1 && p->mask_mode == FA_MASK_BOOL && p->mask_stride[3] == 1 && !p->seqused_q &&
+           p->layout != FA_TND && p->kv_layout == FA_KV_CONTIGUOUS && !mfma_decode(p, s);
+}
+
 // The split-KV stage 1 on the matrix cores in its general form: the g * Q_S
 // (query head, position) rows of a KV head fill up to four 32-row tiles,
 // masks (causal, window, boolean tensor) and used lengths applied per key,
@@ -391,7 +407,7 @@ int64_t prefill_workgroups(const fa_params* p, const Shape& s) {
 enum class Path { kPrefill, kFastDecode, kSplit };
 Path choose_path(const fa_params* p, const Shape& s) {
     if (p->layout == FA_TND) return Path::kPrefill;
-    if (fast_decode(p)) return Path::kFastDecode;
+    if (fast_decode(p) || vector_masked_decode(p, s)) return Path::kFastDecode;
     if (!general_split_ok(p, s)) return Path::kPrefill;
     // One query position always splits (masked decode); a few positions split
     // when the prefill's query tiles cannot fill the CUs.
@@ -676,7 +692,7 @@ fa_status run_prefill(const fa_params* p, const Shape& s, const void* q, const v
 // no used lengths: any head_dim) or the general matrix-core shape.
 fa_status check_split_shape(const fa_params* p, const Shape& s) {
     if (p->layout == FA_TND) return fail(FA_ERR_UNSUPPORTED, "split-KV decode is built for BNSD and BSND");
-    if (fast_decode(p) || general_split_ok(p, s)) return ok();
+    if (fast_decode(p) || vector_masked_decode(p, s) || general_split_ok(p, s)) return ok();
     return fail(FA_ERR_UNSUPPORTED,
                 "split-KV with several query positions, a mask or used lengths is built for head_dim 64 and 128 "
                 "with num_heads / num_kv_heads * q_seq <= %lld",
@@ -752,9 +768,10 @@ std::string describe(const fa_params* p, const Shape& s) {
             std::snprintf(plan, sizeof plan, "length-balanced pieces=%d slots/row=%lld", dp.bal_nwg, (long long)dp.splits);
         else
             std::snprintf(plan, sizeof plan, "splits=%lld chunk=%lld", (long long)dp.splits, (long long)dp.chunk);
-        std::snprintf(body, sizeof body, "path=%s stage1=%s%s %s%s", path == Path::kFastDecode ? "decode" : "general-split",
+        std::snprintf(body, sizeof body, "path=%s stage1=%s%s%s %s%s", path == Path::kFastDecode ? "decode" : "general-split",
                       mm ? "decode_mfma_kernel waves=" : "decode_stage1_kernel", mm ? std::to_string(dp.waves).c_str() : "",
-                      plan, split ? " then combine_kernel" : " (finishes in place)");
+                      (!mm && p->mask_mode == FA_MASK_BOOL) ? " (masked)" : "", plan,
+                      split ? " then combine_kernel" : " (finishes in place)");
     }
     char line[900];
     std::snprintf(line, sizeof line, "%s -> %s workspace=%zu", head, body, ws);

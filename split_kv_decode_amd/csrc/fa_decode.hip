@@ -41,8 +41,12 @@ namespace fa {
 // or partials plus the in-kernel merge of the fused plan.
 constexpr int kPartial = 0, kFinish = 1, kFused = 2;
 
-template <typename ST, int D, int GH, int MODE, bool PAGED>
+// MASKED: a boolean mask tensor (one query position; contiguous cache): the
+// mask byte of each key and query head is loaded with the key's K/V row, and
+// a masked key's score is -inf.
+template <typename ST, int D, int GH, int MODE, bool PAGED, bool MASKED = false>
 __global__ __launch_bounds__(256) void decode_stage1_kernel(DecodeArgs a) {
+    static_assert(!(MASKED && (PAGED || MODE == 2)), "masked: contiguous cache, partial or finish");
     constexpr int LPR = D / 8;     // lanes per KV row
     constexpr int RPL = 64 / LPR;  // rows per wave load
     constexpr int U = 2;                   // row slots per lane per iteration
@@ -146,10 +150,29 @@ __global__ __launch_bounds__(256) void decode_stage1_kernel(DecodeArgs a) {
             step_r = (NW * TW) % bs;
         }
 
-        auto load = [&](int64_t t0, u32x4* kw, u32x4* vw) __attribute__((always_inline)) {
+        // Mask rows (query position 0, unit key stride) of the workgroup's
+        // query heads from the chunk's first key; a lane's U bytes per head
+        // are packed into one word, byte u for row slot u.
+        const uint8_t* mrow[GH];
+#pragma unroll
+        for (int h = 0; h < GH; ++h) {
+            const int64_t n1 = (int64_t)n2 * a.group + hg * GH + h;
+            mrow[h] = MASKED ? a.mask + b * a.mask_stride[0] + n1 * a.mask_stride[1] + c0 : nullptr;
+        }
+        auto load = [&](int64_t t0, u32x4* kw, u32x4* vw, uint32_t* mw) __attribute__((always_inline)) {
+            if constexpr (MASKED) {
+#pragma unroll
+                for (int h = 0; h < GH; ++h) mw[h] = 0u;
+            }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int64_t t = t0 + u * RPL + grp;
+                if constexpr (MASKED) {
+                    const int rel = (int)(t - c0);
+#pragma unroll
+                    for (int h = 0; h < GH; ++h)
+                        mw[h] |= ((t < c1) ? (uint32_t)(mrow[h][rel] != 0) : 1u) << (8 * u);
+                }
                 if constexpr (!PAGED) {
                     const int voff = (int)(t - c0) * row_bytes + sub * 16;
                     kw[u] = buf_ld128(rk, voff);
@@ -174,7 +197,8 @@ __global__ __launch_bounds__(256) void decode_stage1_kernel(DecodeArgs a) {
         };
 
         // One iteration: the rows at t0 (+ slot and group offsets) are in (kw, vw).
-        auto consume = [&](int64_t t0, const u32x4* kw, const u32x4* vw) __attribute__((always_inline)) {
+        auto consume = [&](int64_t t0, const u32x4* kw, const u32x4* vw, const uint32_t* mw)
+                           __attribute__((always_inline)) {
             float vf[U][8];
 #pragma unroll
             for (int u = 0; u < U; ++u) unpack8<ST>(vw[u], vf[u]);
@@ -186,7 +210,9 @@ __global__ __launch_bounds__(256) void decode_stage1_kernel(DecodeArgs a) {
                 for (int u = 0; u < U; ++u) {
                     float part = dot8<ST>(qp[h], kw[u]);
                     part = group_sum<LPR>(part) * c;
-                    s[u] = (t0 + u * RPL + grp < c1) ? part : kNegInf;
+                    bool keep = t0 + u * RPL + grp < c1;
+                    if constexpr (MASKED) keep = keep && ((mw[h] >> (8 * u)) & 0xffu) == 0u;
+                    s[u] = keep ? part : kNegInf;
                     mx = fmaxf(mx, s[u]);
                 }
                 tm[h] = fmaxf(tm[h], mx);
@@ -222,33 +248,35 @@ __global__ __launch_bounds__(256) void decode_stage1_kernel(DecodeArgs a) {
         constexpr int64_t STEP = NW * TW;
         int64_t t0 = c0 + (int64_t)wave * TW;
         u32x4 kA[U], vA[U], kB[U], vB[U];
-        load(t0, kA, vA);
+        constexpr int MW = MASKED ? GH : 1;
+        uint32_t mA[MW], mB[MW], mC[MW];
+        load(t0, kA, vA, mA);
         if constexpr (DEPTH == 1) {
             while (true) {
                 if (t0 >= c1) break;
-                load(t0 + STEP, kB, vB);
-                consume(t0, kA, vA);
+                load(t0 + STEP, kB, vB, mB);
+                consume(t0, kA, vA, mA);
                 t0 += STEP;
                 if (t0 >= c1) break;
-                load(t0 + STEP, kA, vA);
-                consume(t0, kB, vB);
+                load(t0 + STEP, kA, vA, mA);
+                consume(t0, kB, vB, mB);
                 t0 += STEP;
             }
         } else {
             u32x4 kC[U], vC[U];
-            load(t0 + STEP, kB, vB);
+            load(t0 + STEP, kB, vB, mB);
             while (true) {
                 if (t0 >= c1) break;
-                load(t0 + 2 * STEP, kC, vC);
-                consume(t0, kA, vA);
+                load(t0 + 2 * STEP, kC, vC, mC);
+                consume(t0, kA, vA, mA);
                 t0 += STEP;
                 if (t0 >= c1) break;
-                load(t0 + 2 * STEP, kA, vA);
-                consume(t0, kB, vB);
+                load(t0 + 2 * STEP, kA, vA, mA);
+                consume(t0, kB, vB, mB);
                 t0 += STEP;
                 if (t0 >= c1) break;
-                load(t0 + 2 * STEP, kB, vB);
-                consume(t0, kC, vC);
+                load(t0 + 2 * STEP, kB, vB, mB);
+                consume(t0, kC, vC, mC);
                 t0 += STEP;
             }
         }
@@ -652,6 +680,15 @@ static hipError_t dispatch_stage1_fin(const DecodeArgs& a, bool finish, int64_t 
 
 template <typename ST, int D, int GH>
 static hipError_t dispatch_stage1(const DecodeArgs& a, bool finish, int64_t blocks, hipStream_t s) {
+    if (a.mask) {  // boolean mask: contiguous cache, partials or the finished output
+        if (a.block_table || a.counters) return hipErrorInvalidValue;
+        const dim3 grid((unsigned)blocks);
+        if (finish)
+            hipLaunchKernelGGL((decode_stage1_kernel<ST, D, GH, kFinish, false, true>), grid, dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((decode_stage1_kernel<ST, D, GH, kPartial, false, true>), grid, dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
     if (a.block_table) return dispatch_stage1_fin<ST, D, GH, true>(a, finish, blocks, s);
     return dispatch_stage1_fin<ST, D, GH, false>(a, finish, blocks, s);
 }
@@ -668,7 +705,16 @@ static hipError_t dispatch_stage1_gh(const DecodeArgs& a, int gh, bool finish, i
 }
 
 template <typename ST, int D>
-static const void* stage1_symbol(int gh, bool paged) {
+static const void* stage1_symbol(int gh, bool paged, bool masked) {
+    if (masked) {
+        switch (gh) {
+            case 1: return (const void*)&decode_stage1_kernel<ST, D, 1, kPartial, false, true>;
+            case 2: return (const void*)&decode_stage1_kernel<ST, D, 2, kPartial, false, true>;
+            case 4: return (const void*)&decode_stage1_kernel<ST, D, 4, kPartial, false, true>;
+            case 8: return (const void*)&decode_stage1_kernel<ST, D, 8, kPartial, false, true>;
+            default: return nullptr;
+        }
+    }
     switch (gh) {
         case 1: return paged ? (const void*)&decode_stage1_kernel<ST, D, 1, kPartial, true>
                              : (const void*)&decode_stage1_kernel<ST, D, 1, kPartial, false>;
@@ -682,16 +728,16 @@ static const void* stage1_symbol(int gh, bool paged) {
     }
 }
 
-int decode_stage1_residency(int dtype, int head_dim, int heads_per_wg, bool paged) {
+int decode_stage1_residency(int dtype, int head_dim, int heads_per_wg, bool paged, bool masked) {
     const void* f = nullptr;
     if (dtype == 1) {
-        if (head_dim == 64) f = stage1_symbol<BF16, 64>(heads_per_wg, paged);
-        if (head_dim == 128) f = stage1_symbol<BF16, 128>(heads_per_wg, paged);
-        if (head_dim == 256) f = stage1_symbol<BF16, 256>(heads_per_wg, paged);
+        if (head_dim == 64) f = stage1_symbol<BF16, 64>(heads_per_wg, paged, masked);
+        if (head_dim == 128) f = stage1_symbol<BF16, 128>(heads_per_wg, paged, masked);
+        if (head_dim == 256) f = stage1_symbol<BF16, 256>(heads_per_wg, paged, masked);
     } else {
-        if (head_dim == 64) f = stage1_symbol<F16, 64>(heads_per_wg, paged);
-        if (head_dim == 128) f = stage1_symbol<F16, 128>(heads_per_wg, paged);
-        if (head_dim == 256) f = stage1_symbol<F16, 256>(heads_per_wg, paged);
+        if (head_dim == 64) f = stage1_symbol<F16, 64>(heads_per_wg, paged, masked);
+        if (head_dim == 128) f = stage1_symbol<F16, 128>(heads_per_wg, paged, masked);
+        if (head_dim == 256) f = stage1_symbol<F16, 256>(heads_per_wg, paged, masked);
     }
     int n = 0;
     if (!f || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 256, 0) != hipSuccess) {

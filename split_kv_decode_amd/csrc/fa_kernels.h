@@ -196,7 +196,7 @@ hipError_t launch_decode_stage1(const DecodeArgs& a, int dtype, int head_dim, in
                                 bool finish, int64_t batch, hipStream_t stream);
 // Stage-1 workgroups one CU holds at once for this instantiation, from the
 // runtime's occupancy calculator; 0 when no device answers.
-int decode_stage1_residency(int dtype, int head_dim, int heads_per_wg, bool paged);
+int decode_stage1_residency(int dtype, int head_dim, int heads_per_wg, bool paged, bool masked = false);
 hipError_t launch_combine(const CombineArgs& a, int dtype, int head_dim, hipStream_t stream);
 // Length-balanced decode schedule (matrix-core stage 1 with per-batch
 // lengths).  Batch b has T_b = ceil(L_b / 64) tiles per KV head; with

@@ -1004,6 +1004,11 @@ GENERAL_CASES = [
     (dict(B=2, QN=4, KVN=4, QS=1, KVS=3000, D=64, layout="BSND"), dict(mask="bn1s", all_masked=0)),
     (dict(B=2, QN=32, KVN=1, QS=1, KVS=2000, D=128, dtype="f16", lens=(100, 2000)), dict(mask="bn1s")),
     (dict(B=1, QN=2, KVN=2, QS=1, KVS=777, D=128), dict(mask="bqs_odd")),          # byte-wise mask reads
+    # the vector stage 1 with the mask (shapes without a matrix-core stage 1): g = 2
+    # with a fully masked batch, D = 256 per head, g = 48 (eight heads per workgroup)
+    (dict(B=2, QN=4, KVN=2, QS=1, KVS=3000, D=128, lens=(1, 3000)), dict(mask="b11s", all_masked=1)),
+    (dict(B=2, QN=4, KVN=4, QS=1, KVS=2000, D=256, layout="BSND"), dict(mask="bn1s", all_masked=0)),
+    (dict(B=1, QN=48, KVN=1, QS=1, KVS=1500, D=128, dtype="f16"), dict(mask="b11s")),
     # one query position, causal (top-left: key 0 only) and window
     (dict(B=2, QN=8, KVN=2, QS=1, KVS=3000, D=128, lens=(1, 3000)), dict(causal=True)),
     (dict(B=2, QN=8, KVN=8, QS=1, KVS=3000, D=128, layout="BSND"), dict(window=(0, 700))),

@@ -113,7 +113,7 @@ typedef struct {
      * block_table is an error).  A paged cache needs actual_seq_lengths
      * (developer guide 1.2 makes the per-batch lengths mandatory with paging)
      * and a split-KV shape: q_seq == 1 without a mask or seqused_q (any
-     * head_dim), or head_dim 64 / 128 with g * q_seq <= 128 (g = num_heads /
+     * head_dim), or head_dim 64 / 128 with g * q_seq <= 512 (g = num_heads /
      * num_kv_heads, any mask); other paged calls return FA_ERR_UNSUPPORTED.
      *   block_table: device int32 [batch][max_blocks_per_seq], row-major.
      *     Entries of blocks a batch's length reaches must lie in
@@ -172,12 +172,15 @@ fa_status fa_workspace_size(const fa_params *p, size_t *bytes);
  * lse: float32 [B,Q_N,Q_S] or NULL (not written).  The split-KV path
  * (FlashAttn developer guide 1.9: FlashDecode cuts the KV axis when the
  * query rows alone cannot occupy the cores, e.g. S1 = 1) runs
- *   - q_seq == 1 without a mask or seqused_q (any head_dim), and
- *   - with head_dim 64 or 128 and g * q_seq <= 128: q_seq == 1 with any
+ *   - q_seq == 1 without a mask or seqused_q (any head_dim), and q_seq == 1
+ *     with a boolean mask of unit key stride on a contiguous cache (any
+ *     head_dim);
+ *   - with head_dim 64 or 128 and g * q_seq <= 512: q_seq == 1 with any
  *     mask or seqused_q (the decode of the IFA guide with its attenMask),
  *     a paged cache, and a few query positions against a long cache when
  *     the prefill's query tiles would occupy fewer workgroups than there
- *     are CUs;
+ *     are CUs and a row can see at least 1024 keys (the causal mask is
+ *     top-left, so a causal row sees at most q_seq of them);
  * with a split plan the library chooses (see fa_splitkv_plan): one split is
  * a single stage-1 launch that writes the output; more run stage 1 and then
  * fa_combine's kernel (measured faster on MI355X than the fused single
@@ -214,8 +217,9 @@ fa_status fa_splitkv_plan(const fa_params *p, int num_cus, int64_t chunk_hint,
 
 /* fa_decode_splitkv -- FlashDecoding stage 1 (FlashDecoding tutorial 3.2;
  * FlashAttn developer guide 10).  Takes q_seq == 1 without a mask or
- * seqused_q (any head_dim), or, with head_dim 64 / 128 and
- * g * q_seq <= 128, any q_seq, mask and seqused_q (else
+ * seqused_q (any head_dim), q_seq == 1 with a boolean mask of unit key
+ * stride on a contiguous cache (any head_dim), or, with head_dim 64 / 128
+ * and g * q_seq <= 512, any q_seq, mask and seqused_q (else
  * FA_ERR_UNSUPPORTED).  Chunk c covers keys [c*chunk, (c+1)*chunk) cut at
  * the batch's length.  For every row (b, n1, i) and chunk c it writes, over
  * the keys of the chunk the row sees (mask, length, seqused_q),

@@ -148,7 +148,7 @@ fa_status check_params(const fa_params* p, Shape* s) {
     if (p->kv_layout != FA_KV_CONTIGUOUS && !fast_decode(p) && !general_split_ok(p, *s))
         return fail(FA_ERR_UNSUPPORTED,
                     "a paged KV cache is built for the split-KV paths: one query position without a mask or used "
-                    "lengths, or head_dim 64/128 with num_heads / num_kv_heads * q_seq <= 128");
+                    "lengths, or head_dim 64/128 with num_heads / num_kv_heads * q_seq <= 512");
     return ok();
 }
 
@@ -384,12 +384,12 @@ bool vector_masked_decode(const fa_params* p, const Shape& s) {
 }
 
 // The split-KV stage 1 on the matrix cores in its general form: the g * Q_S
-// (query head, position) rows of a KV head fill up to four 32-row tiles,
+// (query head, position) rows of a KV head fill up to sixteen 32-row tiles,
 // masks (causal, window, boolean tensor) and used lengths applied per key,
 // and the combine merges the pieces (FlashAttn developer guide 1.9 and 4:
 // FlashDecode splits the KV axis when the query rows alone cannot occupy the
 // cores, e.g. S1 = 1).
-constexpr int64_t kMaxSplitRows = 128;
+constexpr int64_t kMaxSplitRows = 512;
 bool general_split_ok(const fa_params* p, const Shape& s) {
     return p->layout != FA_TND && (s.D == 64 || s.D == 128) && s.g * s.QS <= kMaxSplitRows &&
            kv_row_bytes(p, s) * 64 < (int64_t(1) << 31) &&
@@ -404,15 +404,31 @@ int64_t prefill_workgroups(const fa_params* p, const Shape& s) {
     return s.B * s.QN * ((s.QS + rows - 1) / rows);
 }
 
+// Keys a query row can see at most: the causal mask is top-left (row i sees
+// keys j <= i), the window reaches win_right past the row.
+int64_t visible_keys(const fa_params* p, const Shape& s) {
+    int64_t n = s.KVS;
+    if (p->mask_mode == FA_MASK_CAUSAL && n > s.QS) n = s.QS;
+    if (p->mask_mode == FA_MASK_WINDOW && p->win_right >= 0 && n > s.QS + p->win_right) n = s.QS + p->win_right;
+    return n;
+}
+// Below this many visible keys the split's extra launch and merge cost more
+// than the idle CUs of a small prefill grid (measured on MI355X: 128 keys,
+// and a causal Q_S = 32 against 2048 keys, ran faster as a prefill; 4096
+// keys at Q_S = 64 ran 4x faster split).
+constexpr int64_t kSplitMinKeys = 1024;
+
 enum class Path { kPrefill, kFastDecode, kSplit };
 Path choose_path(const fa_params* p, const Shape& s) {
     if (p->layout == FA_TND) return Path::kPrefill;
     if (fast_decode(p) || vector_masked_decode(p, s)) return Path::kFastDecode;
     if (!general_split_ok(p, s)) return Path::kPrefill;
     // One query position always splits (masked decode); a few positions split
-    // when the prefill's query tiles cannot fill the CUs.
+    // when the prefill's query tiles cannot fill the CUs and the rows see
+    // enough keys to pay for the split.
     if (s.QS == 1 || p->kv_layout != FA_KV_CONTIGUOUS) return Path::kSplit;
-    return prefill_workgroups(p, s) < device_cus() ? Path::kSplit : Path::kPrefill;
+    return (prefill_workgroups(p, s) < device_cus() && visible_keys(p, s) >= kSplitMinKeys) ? Path::kSplit
+                                                                                          : Path::kPrefill;
 }
 bool decode_path(const fa_params* p) { return fast_decode(p); }
 

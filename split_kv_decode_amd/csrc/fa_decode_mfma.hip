@@ -639,7 +639,7 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, bool
     if (waves != 1 && waves != 2) return hipErrorInvalidValue;
     if (a.block_table && (a.block_size < 16 || a.block_size % 16 != 0)) return hipErrorInvalidValue;
     if (a.bal_nwg > 0 && (finish || !a.lens || a.batch != batch)) return hipErrorInvalidValue;
-    if (a.row_groups < 1 || a.row_groups > 4 || a.group * a.q_seq > 32 * a.row_groups) return hipErrorInvalidValue;
+    if (a.row_groups < 1 || a.row_groups > 16 || a.group * a.q_seq > 32 * a.row_groups) return hipErrorInvalidValue;
     if (a.bal_nwg > 0 && (a.row_groups != 1 || a.q_seq != 1 || a.mask_mode != 0 || a.used_q))
         return hipErrorInvalidValue;
     const int64_t blocks = a.bal_nwg > 0 ? (int64_t)a.bal_nwg + batch * a.num_kv_heads

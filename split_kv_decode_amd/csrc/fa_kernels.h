@@ -51,7 +51,7 @@ struct DecodeArgs {
     // (head-major: h * q_seq + i) fill row_groups tiles of 32 rows.
     int64_t q_seq;            // Q_S >= 1
     int64_t q_stride_s, q_stride_n, q_stride_b;  // elements, q and out
-    int32_t row_groups;       // ceil(group * q_seq / 32), 1..4
+    int32_t row_groups;       // ceil(group * q_seq / 32), 1..16
     int32_t out_bsnd;         // out rows in BSND order (else BNSD)
     const int32_t* used_q;    // [B] query positions in use (seqused_q), or null
     int32_t mask_mode;        // 0 none, 1 causal, 2 boolean tensor, 3 window

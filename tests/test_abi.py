@@ -80,8 +80,8 @@ def test_decode_entry_points_validate(lib):
     p = params(q_seq=2, head_dim=256)
     st = lib.fa_decode_splitkv(ctypes.byref(p), 32, 4096, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
     assert st == fa.FA_ERR_UNSUPPORTED and "several query positions" in fa.fa_last_error()
-    # more than 128 (query head, position) rows per KV head
-    p = params(q_seq=5, num_heads=32, num_kv_heads=1)
+    # more than 512 (query head, position) rows per KV head
+    p = params(q_seq=17, num_heads=32, num_kv_heads=1)
     st = lib.fa_decode_splitkv(ctypes.byref(p), 32, 4096, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
     assert st == fa.FA_ERR_UNSUPPORTED
     p = params()
@@ -206,7 +206,7 @@ def paged(**kw):
     (dict(max_blocks_per_seq=1023), fa.FA_ERR_PARAM_INVALID, "exceeds"),    # 1023*128 < 131072
     (dict(q_seq=16, head_dim=256), fa.FA_ERR_UNSUPPORTED, "split-KV paths"),
     (dict(mask_mode="causal", head_dim=256), fa.FA_ERR_UNSUPPORTED, "split-KV paths"),
-    (dict(q_seq=200), fa.FA_ERR_UNSUPPORTED, "split-KV paths"),
+    (dict(q_seq=600), fa.FA_ERR_UNSUPPORTED, "split-KV paths"),
     (dict(kv_layout="contiguous"), fa.FA_ERR_PARAM_INVALID, "contiguous"),  # table without paging
 ])
 def test_paged_params_validated(lib, kw, status, text):
@@ -440,3 +440,22 @@ def test_fa_log_prints_the_plan_before_launching():
         assert bool(logged) == expect, (env_val, r.stderr)
         if expect:
             assert "path=prefill kernel=prefill_il_kernel<BF16,128,0>" in logged[0]
+
+
+def test_short_query_routing_by_visible_keys(lib):
+    """A few query positions split the KV axis only when the prefill would leave CUs idle
+    and a row sees at least 1024 keys (the causal mask is top-left)."""
+    def path(**kw):
+        return fa.fa_describe(fa.make_params(**kw)).split(" -> ")[1].split()[0]
+    assert path(batch=1, num_heads=2, q_seq=128, kv_seq=128, head_dim=64) == "path=prefill"
+    assert path(batch=1, num_heads=8, q_seq=64, kv_seq=4096, head_dim=128) == "path=general-split"
+    assert path(batch=4, num_heads=8, q_seq=32, kv_seq=2048, head_dim=64, mask_mode="causal") == "path=prefill"
+    assert path(batch=2, num_heads=16, num_kv_heads=4, q_seq=128, kv_seq=16384, head_dim=128,
+                layout="BSND") == "path=general-split"                       # 512 rows per KV head
+    assert path(batch=1, num_heads=8, q_seq=64, kv_seq=8192, head_dim=128, mask_mode="window",
+                win_left=4000, win_right=0) == "path=prefill"               # rows see <= 64 keys
+    assert path(batch=1, num_heads=8, q_seq=64, kv_seq=8192, head_dim=128, mask_mode="window",
+                win_left=-1, win_right=2000) == "path=general-split"
+    assert path(batch=1, num_heads=8, q_seq=64, kv_seq=8192, head_dim=128,
+                num_kv_heads=1, mask_mode="causal") == "path=prefill"
+    assert path(batch=1, num_heads=32, num_kv_heads=1, q_seq=17, kv_seq=8192, head_dim=128) == "path=prefill"  # 544 rows

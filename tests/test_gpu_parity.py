@@ -568,8 +568,10 @@ SUMMARY_CASES = [
          shape=(2, 1, 200, 640), bcast=(False, True), blk=(32, 32)),
     # more KV tiles (1040) than the lanes keep classes for (1024): tiles past
     # them run as partly masked, the loop bounds still come from the summary
-    dict(s=dict(layout="BNSD", B=1, QN=1, KVN=1, QS=130, KVS=66560, D=64, seed=53),
-         shape=(1, 1, 130, 66560), bcast=(False, False), blk=(128, 1024)),
+    # (four query heads on one KV head, the mask broadcast over them: 520 rows
+    # per KV head, past what the split path takes, so this stays a prefill)
+    dict(s=dict(layout="BNSD", B=1, QN=4, KVN=1, QS=130, KVS=66560, D=64, seed=53),
+         shape=(1, 1, 130, 66560), bcast=(False, True), blk=(128, 1024)),
 ]
 
 
@@ -635,7 +637,7 @@ def test_mask_summary_words(case):
     """The summary kernel's words, read back from the caller's workspace, equal
     the classes computed from the mask on the host."""
     if case == 0:
-        s = spec(layout="BSND", B=2, QN=4, KVN=4, QS=464, KVS=1200, D=64, seed=59)
+        s = spec(layout="BSND", B=2, QN=4, KVN=1, QS=464, KVS=1200, D=64, seed=59)  # 1856 rows per KV head: a prefill
         mask = np.triu(np.ones((464, 1200), np.uint8), 1)[None, None]
         strides = (0, 0, 1200, 1)
     else:
@@ -1014,13 +1016,16 @@ GENERAL_CASES = [
     (dict(B=2, QN=8, KVN=8, QS=1, KVS=3000, D=128, layout="BSND"), dict(window=(0, 700))),
     # used query lengths with one position: batch 1 uses none
     (dict(B=3, QN=8, KVN=2, QS=1, KVS=2500, D=128, lens=(1, 2500)), dict(seqused=[1, 0, 5])),
-    # a few positions against a long cache: no mask, causal, boolean (B,N,Q_S,S)
+    # a few positions against a long cache: no mask, a window reaching far right, boolean (B,N,Q_S,S); a top-left causal row sees at most Q_S keys, so fa_fwd runs such calls as a prefill (the split of that mask is tested through fa_decode_splitkv)
     (dict(B=1, QN=32, KVN=8, QS=8, KVS=65536, D=128), dict()),
-    (dict(B=1, QN=32, KVN=8, QS=8, KVS=65536, D=128, layout="BSND"), dict(causal=True)),
+    (dict(B=1, QN=32, KVN=8, QS=8, KVS=65536, D=128, layout="BSND"), dict(window=(-1, 30000))),
     (dict(B=2, QN=8, KVN=2, QS=5, KVS=9000, D=64, lens=(3000, 9000)), dict(mask="bnqs")),
     # four row groups (g * Q_S = 128), three (g * Q_S = 72) and odd counts
     (dict(B=1, QN=16, KVN=2, QS=16, KVS=20000, D=128, layout="BSND"), dict()),
-    (dict(B=2, QN=24, KVN=3, QS=9, KVS=7000, D=64, dtype="f16", lens=(1, 7000)), dict(window=(40, 2))),
+    # 256 and 512 (query head, position) rows per KV head: 8 and 16 row groups
+    (dict(B=1, QN=16, KVN=4, QS=64, KVS=6000, D=128), dict()),
+    (dict(B=2, QN=16, KVN=4, QS=128, KVS=5000, D=64, layout="BSND", lens=(1000, 5000)), dict(mask="bnqs")),
+    (dict(B=2, QN=24, KVN=3, QS=9, KVS=7000, D=64, dtype="f16", lens=(1, 7000)), dict(window=(40, 2000))),
     (dict(B=1, QN=3, KVN=1, QS=3, KVS=4000, D=128), dict(seqused=[2])),
     # negative scale
     (dict(B=1, QN=8, KVN=2, QS=4, KVS=6000, D=128, scale=-0.07), dict(mask="b11s")),
@@ -1113,6 +1118,35 @@ def test_general_stage1_partials_match_oracle_partials():
     assert np.all((np.abs(go - ro) <= tol)[live]), "general stage-1 O partials"
     ref, ref_lse = oracle.attention_rows(prob, inp.q, inp.k, inp.v)
     check(rows_of(out, s, np.arange(rows)), to_np(lse).reshape(-1), ref, ref_lse, "general combine")
+
+
+@pytest.mark.parametrize("mode,window", [("causal", None), ("window", (40, 2)), ("window", (-1, 300))])
+def test_general_split_causal_and_window_explicit(mode, window):
+    """fa_decode_splitkv + fa_combine on several positions under the causal flag or a
+    window.  fa_fwd sends shapes whose rows see so few keys to the prefill; the split
+    stage 1 still takes them.  The result matches the oracle's output."""
+    inp = fa_synth.make(spec(B=2, QN=8, KVN=2, QS=6, KVS=3000, D=128, lens=(500, 3000), seed=161))
+    s = inp.spec
+    q, k, v = (dev16(x, s.dtype) for x in (inp.q, inp.k, inp.v))
+    lens = torch.from_numpy(inp.lens).to(DEV)
+    p = fa.params_for(q, k, layout=s.layout, scale=s.softmax_scale, actual_seq_lengths=lens,
+                      causal=(mode == "causal"), window=window)
+    assert "path=prefill" in fa.fa_describe(p)
+    splits, chunk = 12, 256
+    rows = s.B * s.QN * s.QS
+    o_part = torch.empty((rows * splits * s.D,), dtype=torch.float32, device=DEV)
+    m_part = torch.empty((rows * splits,), dtype=torch.float32, device=DEV)
+    l_part = torch.empty((rows * splits,), dtype=torch.float32, device=DEV)
+    stream = torch.cuda.current_stream()
+    fa.fa_decode_splitkv(p, splits, chunk, q, k, v, o_part, m_part, l_part, stream)
+    out = torch.empty_like(q)
+    lse = torch.empty((s.B, s.QN, s.QS), dtype=torch.float32, device=DEV)
+    fa.fa_combine(p, splits, o_part, m_part, l_part, out, lse, stream)
+    torch.cuda.synchronize()
+    prob = oracle.Problem(s.B, s.QN, s.KVN, s.QS, s.KVS, s.D, s.layout, s.dtype, s.softmax_scale, inp.lens,
+                          mode, window=window or (-1, -1))
+    ref, ref_lse = oracle.attention_rows(prob, inp.q, inp.k, inp.v)
+    check(rows_of(out, s, np.arange(rows)), to_np(lse).reshape(-1), ref, ref_lse, f"explicit split {mode} {window}")
 
 
 @pytest.mark.parametrize("layout,causal", [("BNSD", True), ("BSND", False), ("BNSD", False)])

@@ -179,7 +179,7 @@ fa_status fa_workspace_size(const fa_params *p, size_t *bytes);
  *     mask or seqused_q (the decode of the IFA guide with its attenMask),
  *     a paged cache, and a few query positions against a long cache when
  *     the prefill's query tiles would occupy fewer workgroups than there
- *     are CUs and a row can see at least 1024 keys (the causal mask is
+ *     are CUs and a row can see at least 640 keys (1024 at head_dim 64; the causal mask is
  *     top-left, so a causal row sees at most q_seq of them);
  * with a split plan the library chooses (see fa_splitkv_plan): one split is
  * a single stage-1 launch that writes the output; more run stage 1 and then

@@ -413,10 +413,13 @@ int64_t visible_keys(const fa_params* p, const Shape& s) {
     return n;
 }
 // Below this many visible keys the split's extra launch and merge cost more
-// than the idle CUs of a small prefill grid (measured on MI355X: 128 keys,
-// and a causal Q_S = 32 against 2048 keys, ran faster as a prefill; 4096
-// keys at Q_S = 64 ran 4x faster split).
-constexpr int64_t kSplitMinKeys = 1024;
+// than the idle CUs of a small prefill grid.  Measured on MI355X with small
+// grids (8 to 32 prefill workgroups): a prefill costs about 1.2 us per 64
+// keys at head_dim 128 and 0.8 us at 64 over a fixed ~8 us, the split
+// 14-19 us whatever the length; the two cross between 512 and 768 keys at
+// head_dim 128 (Q_S = 64: 17.1 against 17.7 us at 512, 21.7 against 17.9 at
+// 768) and near 1024 at head_dim 64 (19.0 against 19.3 us).
+int64_t split_min_keys(const Shape& s) { return s.D >= 128 ? 640 : 1024; }
 
 enum class Path { kPrefill, kFastDecode, kSplit };
 Path choose_path(const fa_params* p, const Shape& s) {
@@ -427,7 +430,7 @@ Path choose_path(const fa_params* p, const Shape& s) {
     // when the prefill's query tiles cannot fill the CUs and the rows see
     // enough keys to pay for the split.
     if (s.QS == 1 || p->kv_layout != FA_KV_CONTIGUOUS) return Path::kSplit;
-    return (prefill_workgroups(p, s) < device_cus() && visible_keys(p, s) >= kSplitMinKeys) ? Path::kSplit
+    return (prefill_workgroups(p, s) < device_cus() && visible_keys(p, s) >= split_min_keys(s)) ? Path::kSplit
                                                                                           : Path::kPrefill;
 }
 bool decode_path(const fa_params* p) { return fast_decode(p); }

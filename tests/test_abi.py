@@ -444,7 +444,8 @@ def test_fa_log_prints_the_plan_before_launching():
 
 def test_short_query_routing_by_visible_keys(lib):
     """A few query positions split the KV axis only when the prefill would leave CUs idle
-    and a row sees at least 1024 keys (the causal mask is top-left)."""
+    and a row sees enough keys (640 at head_dim 128, 1024 at 64; the causal mask is
+    top-left)."""
     def path(**kw):
         return fa.fa_describe(fa.make_params(**kw)).split(" -> ")[1].split()[0]
     assert path(batch=1, num_heads=2, q_seq=128, kv_seq=128, head_dim=64) == "path=prefill"
@@ -459,3 +460,8 @@ def test_short_query_routing_by_visible_keys(lib):
     assert path(batch=1, num_heads=8, q_seq=64, kv_seq=8192, head_dim=128,
                 num_kv_heads=1, mask_mode="causal") == "path=prefill"
     assert path(batch=1, num_heads=32, num_kv_heads=1, q_seq=17, kv_seq=8192, head_dim=128) == "path=prefill"  # 544 rows
+    # the threshold: 640 visible keys at head_dim 128, 1024 at 64
+    assert path(batch=1, num_heads=8, q_seq=64, kv_seq=768, head_dim=128) == "path=general-split"
+    assert path(batch=1, num_heads=8, q_seq=64, kv_seq=512, head_dim=128) == "path=prefill"
+    assert path(batch=2, num_heads=16, q_seq=100, kv_seq=768, head_dim=64) == "path=prefill"
+    assert path(batch=2, num_heads=16, q_seq=100, kv_seq=1024, head_dim=64) == "path=general-split"

@@ -409,7 +409,8 @@ int64_t prefill_workgroups(const fa_params* p, const Shape& s) {
 int64_t visible_keys(const fa_params* p, const Shape& s) {
     int64_t n = s.KVS;
     if (p->mask_mode == FA_MASK_CAUSAL && n > s.QS) n = s.QS;
-    if (p->mask_mode == FA_MASK_WINDOW && p->win_right >= 0 && n > s.QS + p->win_right) n = s.QS + p->win_right;
+    // (compared as n - Q_S > win_right: win_right may be as large as int64 allows)
+    if (p->mask_mode == FA_MASK_WINDOW && p->win_right >= 0 && n - s.QS > p->win_right) n = s.QS + p->win_right;
     return n;
 }
 // Below this many visible keys the split's extra launch and merge cost more

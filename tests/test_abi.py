@@ -460,6 +460,9 @@ def test_short_query_routing_by_visible_keys(lib):
     assert path(batch=1, num_heads=8, q_seq=64, kv_seq=8192, head_dim=128,
                 num_kv_heads=1, mask_mode="causal") == "path=prefill"
     assert path(batch=1, num_heads=32, num_kv_heads=1, q_seq=17, kv_seq=8192, head_dim=128) == "path=prefill"  # 544 rows
+    # a window bound near the int64 limit counts as unbounded reach (no overflow)
+    assert path(batch=1, num_heads=8, q_seq=64, kv_seq=4096, head_dim=128, mask_mode="window",
+                win_left=-1, win_right=(1 << 63) - 1) == "path=general-split"
     # the threshold: 640 visible keys at head_dim 128, 1024 at 64
     assert path(batch=1, num_heads=8, q_seq=64, kv_seq=768, head_dim=128) == "path=general-split"
     assert path(batch=1, num_heads=8, q_seq=64, kv_seq=512, head_dim=128) == "path=prefill"

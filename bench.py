@@ -227,7 +227,7 @@ def main():
                                             round(float(np.percentile(legs_t, 90)), 5)],
                          "timing": "median over the timed steps; a 1 GiB buffer is read before each "
                                    "decode call, outside its events, so no KV is cached"}
-        out["roofline"] = {"kernel": "decode_stage1_kernel<BF16,128,1,0,false>", "bound": "hbm",
+        out["roofline"] = {"kernel": "decode_stage1_kernel<BF16,128,1,0,false,false>", "bound": "hbm",
                            "achieved": round(s1_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(s1_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                            "algorithmic_bytes_per_launch": dec["kv_bytes"] + dec["qo_bytes"]}

@@ -705,6 +705,7 @@ fa_status run_prefill(const fa_params* p, const Shape& s, const void* q, const v
         a.work_items = sa.capacity;
         a.batch = (int32_t)s.B;
     }
+    a.cus = device_cus();
     return launch_result(fa::launch_prefill(a, p->dtype == FA_BF16 ? 1 : 0, (int)s.D, mm, s.B, stream), "prefill");
 }
 
@@ -772,6 +773,11 @@ std::string describe(const fa_params* p, const Shape& s) {
         if (p->layout == FA_TND)
             std::snprintf(grid, sizeof grid, "(work list of <= %lld items) x %lld heads", (long long)varlen_capacity(s),
                           (long long)s.QN);
+        else if (const int64_t pg = il ? fa::prefill_persistent_grid((int)s.D, mk, false, prefill_workgroups(p, s),
+                                                                        device_cus())
+                                       : 0)
+            std::snprintf(grid, sizeof grid, "%lld (persistent, over %lld units)", (long long)pg,
+                          (long long)prefill_workgroups(p, s));
         else
             std::snprintf(grid, sizeof grid, "%lld", (long long)prefill_workgroups(p, s));
         std::snprintf(body, sizeof body, "path=prefill%s%s kernel=%s<%s,%lld,%d> rows=%lld workgroups=%s%s",

@@ -115,6 +115,11 @@ struct PrefillArgs {
     // of the mask (MaskSummaryArgs), cls_words words per (slice, q tile).
     const uint32_t* mask_cls;
     int32_t cls_words;
+    // CUs of the device (the persistent launch's grid; set by the caller) and
+    // the units of work (query tile, head, batch) the launch covers (set by
+    // the launcher).
+    int32_t cus;
+    int64_t units;
 };
 
 // Summary of a boolean mask over the prefill's tiles of 128 query rows x 64
@@ -348,6 +353,11 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, bool
 // keys, mask_dwords), else 128.
 int prefill_rows_per_tile(int head_dim, int mask_mode, bool mask_dwords);
 bool prefill_interleaved(int head_dim, int mask_mode, bool mask_dwords);
+// Workgroups of a persistent interleaved launch (one per CU, a multiple of 8,
+// each taking units in turn), or 0 when the launch is one workgroup per unit:
+// head dim 128 without a mask or with a window, padded layouts, more units
+// than CUs.
+int64_t prefill_persistent_grid(int head_dim, int mask_mode, bool packed, int64_t units, int cus);
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int mask_mode,
                           int64_t batch, hipStream_t stream);
 hipError_t launch_varlen_schedule(const VarlenScheduleArgs& a, hipStream_t stream);

@@ -581,10 +581,11 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
 template <int D>
 constexpr int il_waves() { return D == 256 ? 4 : 8; }
 
-template <typename ST, int D, int MASK>
+template <typename ST, int D, int MASK, bool PERSIST>
 __global__ __launch_bounds__(64 * il_waves<D>(), 1) void prefill_il_kernel(PrefillArgs a) {
     static_assert(MASK >= 0 && MASK <= 4, "mask kind");
     static_assert(D == 128 || D == 256, "head dim");
+    static_assert(!PERSIST || MASK == 0 || MASK == 4, "persistent launch: mask-free or window");
     using M = Mfma<ST>;
     using V8 = typename M::V8;
     using E = typename M::E;
@@ -606,10 +607,20 @@ __global__ __launch_bounds__(64 * il_waves<D>(), 1) void prefill_il_kernel(Prefi
     static_assert(NIW >= 1, "tile too small for the waves");
     static_assert(EPS * KS == 16 && PPE * 16 == NPV, "exponentials spread over the products");
     constexpr float kPmax = 256.f;
-    __shared__ __attribute__((aligned(1024))) unsigned char sK0[TB];
-    __shared__ __attribute__((aligned(1024))) unsigned char sK1[TB];
-    __shared__ __attribute__((aligned(1024))) unsigned char sV0[TB];
-    __shared__ __attribute__((aligned(1024))) unsigned char sV1[TB];
+    // D = 128: the K and V double buffers in one array, so the distance
+    // between them is a constant the LDS reads take as their immediate offset
+    // (a buffer of its own has an address known only at link time, kept in a
+    // register).  At D = 256 the distances pass the 16-bit offset field, and
+    // the four buffers stay separate.
+    constexpr bool ONE = D == 128;
+    __shared__ __attribute__((aligned(1024))) unsigned char sKV[(ONE ? 4 : 1) * TB];
+    __shared__ __attribute__((aligned(ONE ? 4 : 1024))) unsigned char sKVb[ONE ? 4 : TB];
+    __shared__ __attribute__((aligned(ONE ? 4 : 1024))) unsigned char sKVc[ONE ? 4 : TB];
+    __shared__ __attribute__((aligned(ONE ? 4 : 1024))) unsigned char sKVd[ONE ? 4 : TB];
+    unsigned char* const sK0 = sKV;
+    unsigned char* const sK1 = ONE ? sKV + TB : sKVb;
+    unsigned char* const sV0 = ONE ? sKV + 2 * TB : sKVc;
+    unsigned char* const sV1 = ONE ? sKV + 3 * TB : sKVd;
     // The boolean mask tile (256 query rows x 64 keys, one byte each).  MASK
     // 3: chunk-major, 16-byte chunk ch of row r at (ch*256 + r)*16; MASK 2:
     // row-major in groups of 4 rows (layout at issue_mask_dwords).  And
@@ -620,621 +631,714 @@ __global__ __launch_bounds__(64 * il_waves<D>(), 1) void prefill_il_kernel(Prefi
     __shared__ __attribute__((aligned(1024))) unsigned char sM1[MT];
     __shared__ uint32_t s_cls[(MASK == 3) ? 64 : 1];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int half = lane >> 5;
-    const int col = lane & 31;
+    const int tid0 = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
 
-    int qt, n1;
-    int64_t b, L;
-    int64_t q_used = a.q_seq, q_full = a.q_seq;  // query rows computed / written
-    int64_t q_off, kv_off;                       // element offsets of (b) in q/out and k/v
-    int64_t lse_row0, lse_step;                  // lse index of (n1, row i) = lse_row0 + i * lse_step
-    if (a.work) {
-        // Packed layout: block 8k + x (dispatched to XCD x) takes head k % N of
-        // work item 8*(k / N) + x, so the heaviest items spread over all XCDs
-        // and the heads of one item (which share K/V under GQA) share an L2.
-        const int x = (int)(blockIdx.x & 7);
-        const int64_t kk = blockIdx.x >> 3;
-        const int64_t item = (kk / a.num_heads) * 8 + x;
-        n1 = (int)(kk % a.num_heads);
-        if (item >= a.work_items) return;
-        const int32_t wb = a.work[2 * item];
-        if (wb < 0) return;
-        b = wb;
-        qt = a.work[2 * item + 1];
-        const SeqGeom sg = seq_geometry(a.cu_q, a.cu_kv, a.used_q, a.lens, b, a.batch, a.q_seq, a.kv_seq);
-        q_used = sg.q_used;
-        q_full = sg.q_full;
-        L = sg.kv_len;
-        q_off = sg.q0 * a.q_stride_s;
-        kv_off = sg.k0 * a.kv_stride_s;
-        lse_row0 = sg.q0 * a.num_heads + n1;
-        lse_step = a.num_heads;
-    } else {
-        const int64_t total = (int64_t)gridDim.x;
-        int64_t bh;
-        if (MASK == 1 || MASK == 2 || MASK == 3 || (MASK == 4 && a.win_left >= a.win_right)) {
-            // Costs grow with the query tile (causal, a tensor mask that may
-            // be causal, or a window reaching further back than forward):
-            // every head's tile of one rank is dispatched before the next
-            // lighter rank, the heads of a rank spread over the XCDs as below.
-            const int64_t heads = total / a.q_tiles;
-            qt = a.q_tiles - 1 - (int)(blockIdx.x / heads);
-            bh = xcd_remap(blockIdx.x % heads, heads);
+    const int64_t units = PERSIST ? a.units : (int64_t)gridDim.x;  // launch slots
+    // The arguments as the persistent kernel reads them per unit: scalar
+    // loads from the argument segment through an opaque copy of its address,
+    // so the compiler keeps none of these values live across the KV loop (the
+    // register pressure of that would cost copies inside it).  The kernel's
+    // one argument, `a`, starts the segment.
+    auto fresh_args = []() __attribute__((always_inline)) -> const __attribute__((address_space(4))) PrefillArgs& {
+        auto kp = (const __attribute__((address_space(4))) PrefillArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+        asm volatile("" : "+s"(kp));
+        return *kp;
+    };
+    // The unit of work (query tile, head, batch) that launch slot u takes,
+    // and the range of keys [kbeg, kv_end) that can be visible to some row of
+    // its tile: causal stops at the tile's last row, a window spans from the
+    // first row's left edge to the last used row's right edge.
+    struct UnitGeom {
+        int qt, n1;
+        bool valid;
+        int64_t b, L;
+        int64_t q_used, q_full;    // query rows computed / written
+        int64_t q_off, kv_off;     // element offsets of (b) in q/out and k/v
+        int64_t lse_row0, lse_step;  // lse index of (n1, row i) = lse_row0 + i * lse_step
+        int64_t kbeg, kv_end;
+    };
+    auto unit_geom = [&](int64_t u, const auto& A) __attribute__((always_inline)) {
+        UnitGeom g{};
+        g.valid = true;
+        g.q_used = A.q_seq;
+        g.q_full = A.q_seq;
+        if (!PERSIST && A.work) {
+            // Packed layout: slot 8k + x (dispatched to XCD x) takes head k % N
+            // of work item 8*(k / N) + x, so the heaviest items spread over all
+            // XCDs and the heads of one item (which share K/V under GQA) share an L2.
+            const int x = (int)(u & 7);
+            const int64_t kk = u >> 3;
+            const int64_t item = (kk / A.num_heads) * 8 + x;
+            g.n1 = (int)(kk % A.num_heads);
+            const int32_t wb = item < A.work_items ? A.work[2 * item] : -1;
+            if (wb < 0) {
+                g.valid = false;
+                return g;
+            }
+            g.b = wb;
+            g.qt = A.work[2 * item + 1];
+            const SeqGeom sg = seq_geometry(A.cu_q, A.cu_kv, A.used_q, A.lens, g.b, A.batch, A.q_seq, A.kv_seq);
+            g.q_used = sg.q_used;
+            g.q_full = sg.q_full;
+            g.L = sg.kv_len;
+            g.q_off = sg.q0 * A.q_stride_s;
+            g.kv_off = sg.k0 * A.kv_stride_s;
+            g.lse_row0 = sg.q0 * A.num_heads + g.n1;
+            g.lse_step = A.num_heads;
         } else {
-            const int64_t work = xcd_remap(blockIdx.x, total);
-            qt = (int)(work % a.q_tiles);
-            bh = work / a.q_tiles;
+            // (32-bit unsigned in the persistent kernel, whose launcher keeps
+            // the units below 2^31: fewer registers for the divisions)
+            using UI = std::conditional_t<PERSIST, uint32_t, int64_t>;
+            const UI total = (UI)units, uu = (UI)u, tiles = (UI)A.q_tiles;
+            UI bh;
+            if (MASK == 1 || MASK == 2 || MASK == 3 || (MASK == 4 && A.win_left >= A.win_right)) {
+                // Costs grow with the query tile (causal, a tensor mask that may
+                // be causal, or a window reaching further back than forward):
+                // every head's tile of one rank is dispatched before the next
+                // lighter rank, the heads of a rank spread over the XCDs as below.
+                const UI heads = total / tiles;
+                g.qt = A.q_tiles - 1 - (int)(uu / heads);
+                bh = (UI)xcd_remap((int64_t)(uu % heads), (int64_t)heads);
+            } else {
+                const UI work = (UI)xcd_remap((int64_t)uu, (int64_t)total);
+                g.qt = (int)(work % tiles);
+                bh = work / tiles;
+            }
+            g.n1 = (int)(bh % (UI)A.num_heads);
+            g.b = (int64_t)(bh / (UI)A.num_heads);
+            g.L = A.kv_seq;
+            if (A.lens) {
+                const int64_t l = A.lens[g.b];
+                g.L = l < 0 ? 0 : (l > A.kv_seq ? A.kv_seq : l);
+            }
+            if (A.used_q) {  // rows at or past the batch's used positions: written as 0 / +inf
+                const int64_t uq = A.used_q[g.b];
+                g.q_used = uq < 0 ? 0 : (uq > A.q_seq ? A.q_seq : uq);
+            }
+            g.q_off = g.b * A.q_stride_b;
+            g.kv_off = g.b * A.kv_stride_b;
+            g.lse_row0 = (g.b * A.num_heads + g.n1) * A.q_seq;
+            g.lse_step = 1;
         }
-        n1 = (int)(bh % a.num_heads);
-        b = bh / a.num_heads;
-        L = a.kv_seq;
-        if (a.lens) {
-            L = a.lens[b];
-            L = L < 0 ? 0 : (L > a.kv_seq ? a.kv_seq : L);
+        const int64_t r0 = (int64_t)g.qt * (32 * NWV);
+        g.kv_end = g.L;
+        g.kbeg = 0;
+        if (MASK == 1 && g.kv_end > r0 + 32 * NWV) g.kv_end = r0 + 32 * NWV;
+        if (MASK == 4) {
+            const int64_t i_last = (r0 + 32 * NWV < g.q_used ? r0 + 32 * NWV : g.q_used) - 1;
+            if (g.kv_end > i_last + A.win_right + 1) g.kv_end = i_last + A.win_right + 1;
+            const int64_t key_lo = r0 - A.win_left;
+            if (key_lo > 0) g.kbeg = key_lo / BN * BN;
         }
-        if (a.used_q) {  // rows at or past the batch's used positions: written as 0 / +inf
-            const int64_t u = a.used_q[b];
-            q_used = u < 0 ? 0 : (u > a.q_seq ? a.q_seq : u);
-        }
-        q_off = b * a.q_stride_b;
-        kv_off = b * a.kv_stride_b;
-        lse_row0 = (b * a.num_heads + n1) * a.q_seq;
-        lse_step = 1;
-    }
-    const int n2 = n1 / a.group;
-
-    const int64_t i0 = (int64_t)qt * (32 * NWV);
-    const int64_t qrow = i0 + 32 * wave + col;
-    const bool qvalid = qrow < q_used;
-
+        return g;
+    };
+    // Q fragments of this lane for the unit (zeros past the used rows; the
+    // sign flipped for a negative scale, zeros for a scale that underflows).
     V8 qreg[KS];
-    {
-        const uint16_t* qp = a.q + q_off + (int64_t)n1 * a.q_stride_n + qrow * a.q_stride_s;
-        const uint32_t flip = a.negate_q ? 0x80008000u : 0u;
+    auto load_q = [&](const UnitGeom& gq, int ln, const auto& A) __attribute__((always_inline)) {
+        const int64_t row = (int64_t)gq.qt * (32 * NWV) + 32 * wave + (ln & 31);
+        const bool ok = row < gq.q_used;
+        const uint16_t* qp = A.q + gq.q_off + (int64_t)gq.n1 * A.q_stride_n + row * A.q_stride_s;
+        const uint32_t flip = A.negate_q ? 0x80008000u : 0u;
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
             u32x4 w = u32x4{0u, 0u, 0u, 0u};
-            if (qvalid && !a.zero_q) w = ld128(qp + kk * 16 + 8 * half);  // zero_q: scale 0
+            if (ok && !A.zero_q) w = ld128(qp + kk * 16 + 8 * (ln >> 5));
             w ^= flip;
             qreg[kk] = __builtin_bit_cast(V8, w);
         }
-    }
-    const float c = a.scale_log2;
-    // Keys [kbeg, kv_end) can be visible to some row of the tile: causal stops
-    // at the tile's last row, a window spans from the first row's left edge to
-    // the last used row's right edge.  The loop runs over the 64-key tiles of
-    // that range (none when no row is used).
-    int64_t kv_end = L, kbeg = 0;
-    if (MASK == 1 && kv_end > i0 + 32 * NWV) kv_end = i0 + 32 * NWV;
-    if (MASK == 4) {
-        const int64_t i_last = (i0 + 32 * NWV < q_used ? i0 + 32 * NWV : q_used) - 1;
-        if (kv_end > i_last + a.win_right + 1) kv_end = i_last + a.win_right + 1;
-        const int64_t key_lo = i0 - a.win_left;
-        if (key_lo > 0) kbeg = key_lo / BN * BN;
-    }
-    // MASK 3 with a summary of the mask: the classes of the workgroup's
-    // 128-row tiles (two at D = 128), OR-ed (bit 0: some key visible, bit 1:
-    // some key masked, for some row), staged for the loop; the first and last
-    // tile with a visible key bound the range.  Tiles past the 64 staged
-    // words count as partly masked.
-    const bool summary = (MASK == 3) && a.mask_cls != nullptr;
-    if (MASK == 3 && summary) {
-        const int64_t sn = a.mask_stride[1] ? a.num_heads : 1;
-        const int64_t slice = (a.mask_stride[0] ? b : 0) * sn + (a.mask_stride[1] ? n1 : 0);
-        const int64_t qt128 = (a.q_seq + kMaskRowsPerTile - 1) / kMaskRowsPerTile;
-        constexpr int R128 = 32 * NWV / kMaskRowsPerTile;  // summary rows per query tile
-        const int64_t r0 = R128 * (int64_t)qt;
-        const uint32_t* c0p = a.mask_cls + (slice * qt128 + r0) * a.cls_words;
-        const uint32_t* c1p = (R128 == 2 && r0 + 1 < qt128) ? c0p + a.cls_words : nullptr;
-        int first = 0x7fffffff, last = -1;
-        for (int w = lane; w < a.cls_words; w += 64) {
-            const uint32_t x = c0p[w] | (c1p ? c1p[w] : 0u);
-            if (w < 64) s_cls[w] = x;  // every wave stages all words (same values), so it reads its own writes
-            const uint32_t live = x & 0x55555555u;
-            if (live) {
-                first = min(first, 16 * w + (__builtin_ctz(live) >> 1));
-                last = max(last, 16 * w + ((31 - __builtin_clz(live)) >> 1));
+    };
+    const int64_t row_bytes = a.kv_stride_s * 2;
+    const int32_t rb32 = __builtin_amdgcn_readfirstlane((int32_t)row_bytes);
+    // A persistent launch (PERSIST) runs one workgroup per CU over the units
+    // blockIdx.x, blockIdx.x + gridDim.x, ... (gridDim.x is a multiple of 8,
+    // so every unit keeps the XCD the plain launch would give it).  The next
+    // unit's Q and first K tile are fetched during the current unit's last
+    // slot, which reads neither Q nor a K buffer.
+    int64_t unit = blockIdx.x;
+    bool fetched = false;  // Q of `unit` in qreg, its first K tile in sK0
+    for (;;) {
+        // Lane-derived values come from an opaque copy of the thread id per unit,
+        // so none is kept live across units.
+        int tid = tid0;
+        if constexpr (PERSIST) asm volatile("" : "+v"(tid));
+        const int lane = tid & 63;
+        const int half = lane >> 5;
+        const int col = lane & 31;
+        const UnitGeom ug = [&]() __attribute__((always_inline)) {
+            if constexpr (PERSIST)
+                return unit_geom(unit, fresh_args());
+            else
+                return unit_geom(unit, a);
+        }();
+        if (!ug.valid) return;
+        const int qt = ug.qt, n1 = ug.n1;
+        const int64_t b = ug.b, L = ug.L, q_used = ug.q_used, q_full = ug.q_full;
+        const int64_t q_off = ug.q_off, kv_off = ug.kv_off, lse_row0 = ug.lse_row0, lse_step = ug.lse_step;
+        const int n2 = n1 / a.group;
+
+        const int64_t i0 = (int64_t)qt * (32 * NWV);
+        const int64_t qrow = i0 + 32 * wave + col;
+        const bool qvalid = qrow < q_used;
+
+        if (!fetched) {
+            if constexpr (PERSIST)
+                load_q(ug, lane, fresh_args());
+            else
+                load_q(ug, lane, a);
+        }
+        const float c = a.scale_log2;
+        int64_t kv_end = ug.kv_end, kbeg = ug.kbeg;
+        // MASK 3 with a summary of the mask: the classes of the workgroup's
+        // 128-row tiles (two at D = 128), OR-ed (bit 0: some key visible, bit 1:
+        // some key masked, for some row), staged for the loop; the first and last
+        // tile with a visible key bound the range.  Tiles past the 64 staged
+        // words count as partly masked.
+        const bool summary = (MASK == 3) && a.mask_cls != nullptr;
+        if (MASK == 3 && summary) {
+            const int64_t sn = a.mask_stride[1] ? a.num_heads : 1;
+            const int64_t slice = (a.mask_stride[0] ? b : 0) * sn + (a.mask_stride[1] ? n1 : 0);
+            const int64_t qt128 = (a.q_seq + kMaskRowsPerTile - 1) / kMaskRowsPerTile;
+            constexpr int R128 = 32 * NWV / kMaskRowsPerTile;  // summary rows per query tile
+            const int64_t r0 = R128 * (int64_t)qt;
+            const uint32_t* c0p = a.mask_cls + (slice * qt128 + r0) * a.cls_words;
+            const uint32_t* c1p = (R128 == 2 && r0 + 1 < qt128) ? c0p + a.cls_words : nullptr;
+            int first = 0x7fffffff, last = -1;
+            for (int w = lane; w < a.cls_words; w += 64) {
+                const uint32_t x = c0p[w] | (c1p ? c1p[w] : 0u);
+                if (w < 64) s_cls[w] = x;  // every wave stages all words (same values), so it reads its own writes
+                const uint32_t live = x & 0x55555555u;
+                if (live) {
+                    first = min(first, 16 * w + (__builtin_ctz(live) >> 1));
+                    last = max(last, 16 * w + ((31 - __builtin_clz(live)) >> 1));
+                }
+            }
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                first = min(first, __shfl_xor(first, off, 64));
+                last = max(last, __shfl_xor(last, off, 64));
+            }
+            first = __builtin_amdgcn_readfirstlane(first);
+            last = __builtin_amdgcn_readfirstlane(last);
+            if (last < 0) {
+                kv_end = 0;  // no visible key for any row
+            } else {
+                if ((int64_t)first * BN > kbeg) kbeg = (int64_t)first * BN;
+                if ((int64_t)(last + 1) * BN < kv_end) kv_end = (int64_t)(last + 1) * BN;
             }
         }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            first = min(first, __shfl_xor(first, off, 64));
-            last = max(last, __shfl_xor(last, off, 64));
-        }
-        first = __builtin_amdgcn_readfirstlane(first);
-        last = __builtin_amdgcn_readfirstlane(last);
-        if (last < 0) {
-            kv_end = 0;  // no visible key for any row
-        } else {
-            if ((int64_t)first * BN > kbeg) kbeg = (int64_t)first * BN;
-            if ((int64_t)(last + 1) * BN < kv_end) kv_end = (int64_t)(last + 1) * BN;
-        }
-    }
-    const int nt = (i0 >= q_used || kv_end <= kbeg) ? 0 : (int)((kv_end - kbeg + BN - 1) / BN);
+        const int nt = (i0 >= q_used || kv_end <= kbeg) ? 0 : (int)((kv_end - kbeg + BN - 1) / BN);
 
-    f32x16 o[D / 32];
+        f32x16 o[D / 32];
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+        for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-    float m_run = kNegInf;  // reference max per query row (scaled base-2 units)
-    float l_half = 0.f;     // this half-wave's share of the row sum
+            for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+        float m_run = kNegInf;  // reference max per query row (scaled base-2 units)
+        float l_half = 0.f;     // this half-wave's share of the row sum
 
-    const int64_t row_bytes = a.kv_stride_s * 2;
-    const char* kbase = reinterpret_cast<const char*>(a.k + kv_off + (int64_t)n2 * a.kv_stride_n) + kbeg * row_bytes;
-    const char* vbase = reinterpret_cast<const char*>(a.v + kv_off + (int64_t)n2 * a.kv_stride_n) + kbeg * row_bytes;
-    int voff[NIW];
+        const char* kbase = reinterpret_cast<const char*>(a.k + kv_off + (int64_t)n2 * a.kv_stride_n) + kbeg * row_bytes;
+        const char* vbase = reinterpret_cast<const char*>(a.v + kv_off + (int64_t)n2 * a.kv_stride_n) + kbeg * row_bytes;
+        int voff[NIW];
 #pragma unroll
-    for (int w = 0; w < NIW; ++w) {
-        const int r = RPI * (wave * NIW + w) + lane / CPR;
-        voff[w] = (int)(r * row_bytes) + (((lane % CPR) ^ swz<D>(r)) << 4);
-    }
-    // Tile loads with their scalars worked out once: the K and V bases of
-    // this (b, n2), the bytes per row (a 64-row tile stays below 2^31 bytes,
-    // which the host checks), the key count in 32 bits and the LDS address of
-    // this wave's share of each buffer; a load then costs a few scalar
-    // instructions and the M0 write.
-    const uint64_t kb64 = (uint64_t)uni64((int64_t)(uintptr_t)kbase);
-    const uint64_t vb64 = (uint64_t)uni64((int64_t)(uintptr_t)vbase);
-    const int32_t rb32 = __builtin_amdgcn_readfirstlane((int32_t)row_bytes);
-    const int32_t L32 = __builtin_amdgcn_readfirstlane((int32_t)(kv_end - kbeg));  // keys in the range
-    // Visible keys of the wave's first row (wrow0), relative to the range's
-    // first key: [c_lo, c_hi] (row wrow0 + col sees [c_lo + col, c_hi + col]),
-    // and the bounds [w_lo, w_hi] within which a key is visible to every row of
-    // the wave, so a tile inside them needs no per-key mask.  All scalars: the
-    // per-lane bounds are rebuilt from the lane id on the masking path only.
-    auto clamp_rel = [](int64_t x) __attribute__((always_inline)) {
-        return (int32_t)(x < -(int64_t(1) << 30) ? -(int64_t(1) << 30) : (x > (int64_t(1) << 30) ? (int64_t(1) << 30) : x));
-    };
-    const int64_t wrow0 = i0 + 32 * wave;
-    int32_t c_lo = 0, c_hi = L32 - 1;
-    if (MASK == 1) c_hi = clamp_rel(wrow0 - kbeg);
-    if (MASK == 4) {
-        c_lo = clamp_rel(wrow0 - a.win_left - kbeg);
-        c_hi = clamp_rel(wrow0 + a.win_right - kbeg);
-    }
-    c_lo = __builtin_amdgcn_readfirstlane(c_lo);
-    c_hi = __builtin_amdgcn_readfirstlane(c_hi);
-    const int32_t w_lo = (MASK == 4) ? c_lo + 31 : 0;
-    const int32_t w_hi = min(L32 - 1, c_hi);
-    const uint32_t wshare = (uint32_t)(wave * NIW * 1024);
-    const uint32_t mK0 = lds_address(sK0) + wshare, mK1 = lds_address(sK1) + wshare;
-    const uint32_t mV0 = lds_address(sV0) + wshare, mV1 = lds_address(sV1) + wshare;
-    // MASK 3 tile loads: wave w fills chunk w%4 (keys 16*(w%4) + [0,16)) of
-    // rows 128*(w/4) + [0,128), 64 rows per wave load; the resource stops at
-    // the last used row's last key, so nothing past the mask tensor is read.
-    const char* mbase = reinterpret_cast<const char*>(a.mask) + b * a.mask_stride[0] +
-                        (int64_t)n1 * a.mask_stride[1] + i0 * a.mask_stride[2];
-    const int32_t mst2 = __builtin_amdgcn_readfirstlane((int32_t)a.mask_stride[2]);
-    int32_t mrec_rows = 0;
-    if (MASK == 3) {
-        int64_t rv = q_used - i0;
-        rv = rv > 32 * NWV ? 32 * NWV : rv;
-        mrec_rows = __builtin_amdgcn_readfirstlane((int32_t)((rv - 1) * a.mask_stride[2]));
-    }
-    const uint32_t mM0 = lds_address(sM0) + (uint32_t)((wave & 3) * (32 * NWV) + 128 * (wave >> 2)) * 16u;
-    const uint32_t mM1 = lds_address(sM1) + (uint32_t)((wave & 3) * (32 * NWV) + 128 * (wave >> 2)) * 16u;
-    // Class of tile jl, asked for in increasing order: the staged word of the
-    // current 16 tiles is kept in a scalar and read from LDS once per word
-    // (an LDS read here would make the slot wait for its in-flight K reads).
-    uint32_t cword = 0u;
-    int cw_idx = -1;
-    auto tile_cls = [&](int jl) __attribute__((always_inline)) -> uint32_t {
-        const int64_t jt = kbeg / BN + jl;
-        if (!summary || jt >= 64 * 16) return 3u;
-        const int wi = (int)(jt >> 4);
-        if (wi != cw_idx) {
-            cword = __builtin_amdgcn_readfirstlane(s_cls[wi]);
-            cw_idx = wi;
+        for (int w = 0; w < NIW; ++w) {
+            const int r = RPI * (wave * NIW + w) + lane / CPR;
+            voff[w] = (int)(r * row_bytes) + (((lane % CPR) ^ swz<D>(r)) << 4);
         }
-        return (cword >> (2 * (jt & 15))) & 3u;
-    };
-    uint32_t cls_cur = 3u, cls_nxt = 3u;  // classes of tiles j and j+1 in slot j
-    // MASK 2 tile loads (rows of 4-aligned key runs): four keys per lane, one
-    // group of 4 rows per wave load (lane l: row 4G + l/16, keys 4(l%16) +
-    // [0, 4)), wave w loading groups 8w .. 8w+7 (its own rows); group G sits at
-    // G*272 in LDS, rows 64 bytes apart (the 16-byte step between groups
-    // spreads a wave's reads over the banks).  Each group's resource stops at
-    // its last used row's last key; groups with no used row are not loaded.
-    constexpr int MGP = 272;
-    const uint32_t mE0 = lds_address(sM0) + (uint32_t)(8 * wave * MGP);
-    const uint32_t mE1 = lds_address(sM1) + (uint32_t)(8 * wave * MGP);
-    auto issue_mask_dwords = [&](int jl, uint32_t m0) __attribute__((always_inline)) {
-        const int64_t j0 = kbeg + (int64_t)jl * BN;
-        int64_t keys = a.kv_seq - j0;
-        keys = keys > BN ? BN : keys;
-        const int ln = (int)__lane_id();
-        const int voff = (ln >> 4) * mst2 + (ln & 15) * 4;
-        const uint64_t gb = (uint64_t)(uintptr_t)(mbase + j0) + (uint64_t)(int64_t)(32 * wave) * (uint64_t)(int64_t)mst2;
-        const int32_t rows = __builtin_amdgcn_readfirstlane((int32_t)(q_used - i0 - 32 * wave));
+        // Tile loads with their scalars worked out once: the K and V bases of
+        // this (b, n2), the bytes per row (a 64-row tile stays below 2^31 bytes,
+        // which the host checks), the key count in 32 bits and the LDS address of
+        // this wave's share of each buffer; a load then costs a few scalar
+        // instructions and the M0 write.
+        const uint64_t kb64 = (uint64_t)uni64((int64_t)(uintptr_t)kbase);
+        const uint64_t vb64 = (uint64_t)uni64((int64_t)(uintptr_t)vbase);
+        const int32_t L32 = __builtin_amdgcn_readfirstlane((int32_t)(kv_end - kbeg));  // keys in the range
+        // Visible keys of the wave's first row (wrow0), relative to the range's
+        // first key: [c_lo, c_hi] (row wrow0 + col sees [c_lo + col, c_hi + col]),
+        // and the bounds [w_lo, w_hi] within which a key is visible to every row of
+        // the wave, so a tile inside them needs no per-key mask.  All scalars: the
+        // per-lane bounds are rebuilt from the lane id on the masking path only.
+        auto clamp_rel = [](int64_t x) __attribute__((always_inline)) {
+            return (int32_t)(x < -(int64_t(1) << 30) ? -(int64_t(1) << 30) : (x > (int64_t(1) << 30) ? (int64_t(1) << 30) : x));
+        };
+        const int64_t wrow0 = i0 + 32 * wave;
+        int32_t c_lo = 0, c_hi = L32 - 1;
+        if (MASK == 1) c_hi = clamp_rel(wrow0 - kbeg);
+        if (MASK == 4) {
+            c_lo = clamp_rel(wrow0 - a.win_left - kbeg);
+            c_hi = clamp_rel(wrow0 + a.win_right - kbeg);
+        }
+        c_lo = __builtin_amdgcn_readfirstlane(c_lo);
+        c_hi = __builtin_amdgcn_readfirstlane(c_hi);
+        const int32_t w_lo = (MASK == 4) ? c_lo + 31 : 0;
+        const int32_t w_hi = min(L32 - 1, c_hi);
+        const uint32_t wshare = (uint32_t)(wave * NIW * 1024);
+        const uint32_t mK0 = lds_address(sK0) + wshare, mK1 = lds_address(sK1) + wshare;
+        const uint32_t mV0 = lds_address(sV0) + wshare, mV1 = lds_address(sV1) + wshare;
+        // MASK 3 tile loads: wave w fills chunk w%4 (keys 16*(w%4) + [0,16)) of
+        // rows 128*(w/4) + [0,128), 64 rows per wave load; the resource stops at
+        // the last used row's last key, so nothing past the mask tensor is read.
+        const char* mbase = reinterpret_cast<const char*>(a.mask) + b * a.mask_stride[0] +
+                            (int64_t)n1 * a.mask_stride[1] + i0 * a.mask_stride[2];
+        const int32_t mst2 = __builtin_amdgcn_readfirstlane((int32_t)a.mask_stride[2]);
+        int32_t mrec_rows = 0;
+        if (MASK == 3) {
+            int64_t rv = q_used - i0;
+            rv = rv > 32 * NWV ? 32 * NWV : rv;
+            mrec_rows = __builtin_amdgcn_readfirstlane((int32_t)((rv - 1) * a.mask_stride[2]));
+        }
+        const uint32_t mM0 = lds_address(sM0) + (uint32_t)((wave & 3) * (32 * NWV) + 128 * (wave >> 2)) * 16u;
+        const uint32_t mM1 = lds_address(sM1) + (uint32_t)((wave & 3) * (32 * NWV) + 128 * (wave >> 2)) * 16u;
+        // Class of tile jl, asked for in increasing order: the staged word of the
+        // current 16 tiles is kept in a scalar and read from LDS once per word
+        // (an LDS read here would make the slot wait for its in-flight K reads).
+        uint32_t cword = 0u;
+        int cw_idx = -1;
+        auto tile_cls = [&](int jl) __attribute__((always_inline)) -> uint32_t {
+            const int64_t jt = kbeg / BN + jl;
+            if (!summary || jt >= 64 * 16) return 3u;
+            const int wi = (int)(jt >> 4);
+            if (wi != cw_idx) {
+                cword = __builtin_amdgcn_readfirstlane(s_cls[wi]);
+                cw_idx = wi;
+            }
+            return (cword >> (2 * (jt & 15))) & 3u;
+        };
+        uint32_t cls_cur = 3u, cls_nxt = 3u;  // classes of tiles j and j+1 in slot j
+        // MASK 2 tile loads (rows of 4-aligned key runs): four keys per lane, one
+        // group of 4 rows per wave load (lane l: row 4G + l/16, keys 4(l%16) +
+        // [0, 4)), wave w loading groups 8w .. 8w+7 (its own rows); group G sits at
+        // G*272 in LDS, rows 64 bytes apart (the 16-byte step between groups
+        // spreads a wave's reads over the banks).  Each group's resource stops at
+        // its last used row's last key; groups with no used row are not loaded.
+        constexpr int MGP = 272;
+        const uint32_t mE0 = lds_address(sM0) + (uint32_t)(8 * wave * MGP);
+        const uint32_t mE1 = lds_address(sM1) + (uint32_t)(8 * wave * MGP);
+        auto issue_mask_dwords = [&](int jl, uint32_t m0) __attribute__((always_inline)) {
+            const int64_t j0 = kbeg + (int64_t)jl * BN;
+            int64_t keys = a.kv_seq - j0;
+            keys = keys > BN ? BN : keys;
+            const int ln = (int)__lane_id();
+            const int voff = (ln >> 4) * mst2 + (ln & 15) * 4;
+            const uint64_t gb = (uint64_t)(uintptr_t)(mbase + j0) + (uint64_t)(int64_t)(32 * wave) * (uint64_t)(int64_t)mst2;
+            const int32_t rows = __builtin_amdgcn_readfirstlane((int32_t)(q_used - i0 - 32 * wave));
 #pragma unroll
-        for (int G = 0; G < 8; ++G) {
-            const int32_t rv = min(rows - 4 * G, 4);
-            if (rv <= 0) break;
-            const uint64_t t = gb + (uint64_t)(int64_t)(4 * G) * (uint64_t)(int64_t)mst2;
+            for (int G = 0; G < 8; ++G) {
+                const int32_t rv = min(rows - 4 * G, 4);
+                if (rv <= 0) break;
+                const uint64_t t = gb + (uint64_t)(int64_t)(4 * G) * (uint64_t)(int64_t)mst2;
+                dma_rsrc r;
+                r[0] = (uint32_t)t;
+                r[1] = (uint32_t)(t >> 32) & 0xffffu;
+                r[2] = (uint32_t)((rv - 1) * mst2 + (int32_t)keys);
+                r[3] = 0x00020000u;
+                lds_dma4_m0(r, m0 + (uint32_t)(G * MGP), voff);
+            }
+        };
+        auto issue_mask = [&](int jl, uint32_t cls, uint32_t m0) __attribute__((always_inline)) {
+            if (!(cls & 2u)) return;  // no key masked (or none visible): nothing to stage
+            const int64_t j0 = kbeg + (int64_t)jl * BN;
+            int64_t keys = a.kv_seq - j0;
+            keys = keys > BN ? BN : keys;
+            const dma_rsrc rm = make_dma_rsrc(mbase + j0, mrec_rows + (int)keys);
+            const int ln = (int)__lane_id();
+#pragma unroll
+            for (int w = 0; w < 2; ++w)
+                lds_dma16_m0(rm, m0 + (uint32_t)(w * 1024),
+                             (128 * (wave >> 2) + 64 * w + ln) * mst2 + (wave & 3) * 16);
+        };
+        // Bytes of a full tile, and of the last one (cut at the length).
+        const uint32_t full_bytes = (uint32_t)(BN * rb32);
+        const uint32_t last_bytes = (uint32_t)((L32 - (nt - 1) * BN) * rb32);
+        auto issue_at = [&](uint64_t t, uint32_t bytes, uint32_t m0) __attribute__((always_inline)) {
             dma_rsrc r;
             r[0] = (uint32_t)t;
             r[1] = (uint32_t)(t >> 32) & 0xffffu;
-            r[2] = (uint32_t)((rv - 1) * mst2 + (int32_t)keys);
+            r[2] = bytes;
             r[3] = 0x00020000u;
-            lds_dma4_m0(r, m0 + (uint32_t)(G * MGP), voff);
-        }
-    };
-    auto issue_mask = [&](int jl, uint32_t cls, uint32_t m0) __attribute__((always_inline)) {
-        if (!(cls & 2u)) return;  // no key masked (or none visible): nothing to stage
-        const int64_t j0 = kbeg + (int64_t)jl * BN;
-        int64_t keys = a.kv_seq - j0;
-        keys = keys > BN ? BN : keys;
-        const dma_rsrc rm = make_dma_rsrc(mbase + j0, mrec_rows + (int)keys);
-        const int ln = (int)__lane_id();
 #pragma unroll
-        for (int w = 0; w < 2; ++w)
-            lds_dma16_m0(rm, m0 + (uint32_t)(w * 1024),
-                         (128 * (wave >> 2) + 64 * w + ln) * mst2 + (wave & 3) * 16);
-    };
-    // Bytes of a full tile, and of the last one (cut at the length).
-    const uint32_t full_bytes = (uint32_t)(BN * rb32);
-    const uint32_t last_bytes = (uint32_t)((L32 - (nt - 1) * BN) * rb32);
-    auto issue = [&](uint64_t base, int jt, uint32_t m0) __attribute__((always_inline)) {
-        const uint64_t t = base + (uint64_t)(uint32_t)jt * (uint64_t)full_bytes;
-        dma_rsrc r;
-        r[0] = (uint32_t)t;
-        r[1] = (uint32_t)(t >> 32) & 0xffffu;
-        r[2] = jt + 1 < nt ? full_bytes : last_bytes;
-        r[3] = 0x00020000u;
-#pragma unroll
-        for (int w = 0; w < NIW; ++w) lds_dma16_m0(r, m0 + (uint32_t)(w * 1024), voff[w]);
-    };
-
-    // LDS read addressing, as in the other prefill kernels.
-    const int krow0 = col, krow1 = 32 + col;
-    const int ks0 = swz<D>(krow0), ks1 = swz<D>(krow1);
-    const int trG = lane >> 4;
-    const int trL = lane & 15;
-    const int vrow_lo = 4 * (trG >> 1) + (trL >> 2);
-    const int vrow_hi = vrow_lo + 8;
-    const int vs_lo = swz<D>(vrow_lo), vs_hi = swz<D>(vrow_hi);
-    const int vx = 2 * (trG & 1) + ((trL & 3) >> 1);
-    const int vbyte = (trL & 1) * 8;
-    auto kread = [&](const unsigned char* Kb, int kk, V8* dst) __attribute__((always_inline)) {
-        dst[0] = __builtin_bit_cast(V8, *reinterpret_cast<const u32x4*>(Kb + krow0 * RB + (((2 * kk + half) ^ ks0) << 4)));
-        dst[1] = __builtin_bit_cast(V8, *reinterpret_cast<const u32x4*>(Kb + krow1 * RB + (((2 * kk + half) ^ ks1) << 4)));
-    };
-    // V^T operand of product (ks, dt): keys 16*ks + .., head-dim columns 32*dt + ..
-    auto vread = [&](const unsigned char* Vb, int i) __attribute__((always_inline)) -> V8 {
-        const int ks = i / NDT, dt = i % NDT;
-        const int lc = 4 * dt + vx;
-        const unsigned char* vb = Vb + ks * 16 * RB;
-        const s16x4 lo = lds_read_tr(vb + vrow_lo * RB + ((lc ^ vs_lo) << 4) + vbyte);
-        const s16x4 hi = lds_read_tr(vb + vrow_hi * RB + ((lc ^ vs_hi) << 4) + vbyte);
-        return __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    const f32x16 zero16 = {};
-
-    // Stage A of a slot: S(j) into Sn (when QK), exponentials of the second
-    // half of tile j-1 (So[1]) into Pd[2..3] and their sum ps1 (when SM).
-    auto stage_a = [&](auto qk_t, auto sm_t, const unsigned char* Kb, f32x16* Sn, const f32x16* So, u32x4* Pd,
-                       float& ps1) __attribute__((always_inline)) {
-        constexpr bool QK = decltype(qk_t)::value;
-        constexpr bool SM = decltype(sm_t)::value;
-        const float nmx = (m_run == kNegInf) ? 0.f : -m_run;
-        constexpr int PF = 2;  // K fragments read two steps ahead
-        V8 kring[PF + 1][2];
-        if constexpr (QK) {
-#pragma unroll
-            for (int p = 0; p < PF; ++p) kread(Kb, p, kring[p]);
-        }
-        float acc = 0.f, pprev = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            if constexpr (QK) {
-                if (kk + PF < KS) kread(Kb, kk + PF, kring[(kk + PF) % (PF + 1)]);
+            for (int w = 0; w < NIW; ++w) lds_dma16_m0(r, m0 + (uint32_t)(w * 1024), voff[w]);
+        };
+        auto issue = [&](uint64_t base, int jt, uint32_t m0) __attribute__((always_inline)) {
+            issue_at(base + (uint64_t)(uint32_t)jt * (uint64_t)full_bytes, jt + 1 < nt ? full_bytes : last_bytes, m0);
+        };
+        // Persistent launch, before the last slot: Q of the next unit into qreg
+        // and its first K tile into sK0.
+        auto fetch_next = [&]() __attribute__((always_inline)) {
+            const int64_t nu = unit + gridDim.x;
+            if (nu >= units) return;
+            const auto& A = fresh_args();
+            const UnitGeom gn = unit_geom(nu, A);
+            if (!gn.valid) return;
+            int ln;  // the lane id produced here, not kept live from the unit's start
+            asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+            load_q(gn, ln, A);
+            const int64_t nkeys = gn.kv_end - gn.kbeg;
+            if ((int64_t)gn.qt * (32 * NWV) < gn.q_used && nkeys > 0) {
+                const char* kb = reinterpret_cast<const char*>(A.k + gn.kv_off + (int64_t)(gn.n1 / A.group) * A.kv_stride_n) +
+                                 gn.kbeg * row_bytes;
+                const int32_t rows = __builtin_amdgcn_readfirstlane((int32_t)(nkeys < BN ? nkeys : BN));
+                issue_at((uint64_t)uni64((int64_t)(uintptr_t)kb), (uint32_t)(rows * rb32), mK0);
             }
-            // each step in this order: fragment reads, vector work, products
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (SM && EPS == 2) {
-                const int r = 2 * kk;
-                const float p0 = fast_exp2(__builtin_fmaf(So[1][r], c, nmx));
-                const float p1 = fast_exp2(__builtin_fmaf(So[1][r + 1], c, nmx));
-                acc += p0;
-                acc += p1;
-                uint32_t w = cvt_pair<ST>(p0, p1);
-                // keep the sum and the conversion in this step (the compiler
-                // would otherwise sink them past the products)
-                asm volatile("" : "+v"(acc), "+v"(w));
-                Pd[2 + (r >> 3)][(r & 7) >> 1] = w;
-            } else if constexpr (SM) {  // one exponential per step, converted in pairs
-                const int r = kk;
-                const float p = fast_exp2(__builtin_fmaf(So[1][r], c, nmx));
-                acc += p;
-                if (r & 1) {
-                    uint32_t w = cvt_pair<ST>(pprev, p);
+            fetched = true;
+        };
+
+        // LDS read addressing, as in the other prefill kernels.
+        const int krow0 = col, krow1 = 32 + col;
+        const int ks0 = swz<D>(krow0), ks1 = swz<D>(krow1);
+        const int trG = lane >> 4;
+        const int trL = lane & 15;
+        const int vrow_lo = 4 * (trG >> 1) + (trL >> 2);
+        const int vrow_hi = vrow_lo + 8;
+        const int vs_lo = swz<D>(vrow_lo), vs_hi = swz<D>(vrow_hi);
+        const int vx = 2 * (trG & 1) + ((trL & 3) >> 1);
+        const int vbyte = (trL & 1) * 8;
+        auto kread = [&](const unsigned char* Kb, int kk, V8* dst) __attribute__((always_inline)) {
+            dst[0] = __builtin_bit_cast(V8, *reinterpret_cast<const u32x4*>(Kb + krow0 * RB + (((2 * kk + half) ^ ks0) << 4)));
+            dst[1] = __builtin_bit_cast(V8, *reinterpret_cast<const u32x4*>(Kb + krow1 * RB + (((2 * kk + half) ^ ks1) << 4)));
+        };
+        // V^T operand of product (ks, dt): keys 16*ks + .., head-dim columns 32*dt + ..
+        auto vread = [&](const unsigned char* Vb, int i) __attribute__((always_inline)) -> V8 {
+            const int ks = i / NDT, dt = i % NDT;
+            const int lc = 4 * dt + vx;
+            const unsigned char* vb = Vb + ks * 16 * RB;
+            const s16x4 lo = lds_read_tr(vb + vrow_lo * RB + ((lc ^ vs_lo) << 4) + vbyte);
+            const s16x4 hi = lds_read_tr(vb + vrow_hi * RB + ((lc ^ vs_hi) << 4) + vbyte);
+            return __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        const f32x16 zero16 = {};
+
+        // Stage A of a slot: S(j) into Sn (when QK), exponentials of the second
+        // half of tile j-1 (So[1]) into Pd[2..3] and their sum ps1 (when SM).
+        auto stage_a = [&](auto qk_t, auto sm_t, const unsigned char* Kb, f32x16* Sn, const f32x16* So, u32x4* Pd,
+                           float& ps1) __attribute__((always_inline)) {
+            constexpr bool QK = decltype(qk_t)::value;
+            constexpr bool SM = decltype(sm_t)::value;
+            const float nmx = (m_run == kNegInf) ? 0.f : -m_run;
+            constexpr int PF = 2;  // K fragments read two steps ahead
+            V8 kring[PF + 1][2];
+            if constexpr (QK) {
+#pragma unroll
+                for (int p = 0; p < PF; ++p) kread(Kb, p, kring[p]);
+            }
+            float acc = 0.f, pprev = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                if constexpr (QK) {
+                    if (kk + PF < KS) kread(Kb, kk + PF, kring[(kk + PF) % (PF + 1)]);
+                }
+                // each step in this order: fragment reads, vector work, products
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (SM && EPS == 2) {
+                    const int r = 2 * kk;
+                    const float p0 = fast_exp2(__builtin_fmaf(So[1][r], c, nmx));
+                    const float p1 = fast_exp2(__builtin_fmaf(So[1][r + 1], c, nmx));
+                    acc += p0;
+                    acc += p1;
+                    uint32_t w = cvt_pair<ST>(p0, p1);
+                    // keep the sum and the conversion in this step (the compiler
+                    // would otherwise sink them past the products)
                     asm volatile("" : "+v"(acc), "+v"(w));
                     Pd[2 + (r >> 3)][(r & 7) >> 1] = w;
-                } else {
-                    pprev = p;
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (QK) {
-                const V8* kf = kring[kk % (PF + 1)];
-                Sn[0] = M::mm(kf[0], qreg[kk], kk == 0 ? zero16 : Sn[0]);
-                Sn[1] = M::mm(kf[1], qreg[kk], kk == 0 ? zero16 : Sn[1]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if constexpr (SM) ps1 = acc;
-    };
-    // Stage B: O += V(j-1)^T P(j-1) (when PV, Po = P(j-1)), exponentials of
-    // the first half of tile j (Sn[0]) into Pn[0..1] and their sum ps0 (when SM).
-    auto stage_b = [&](auto pv_t, auto sm_t, const unsigned char* Vb, const u32x4* Po, const f32x16* Sn, u32x4* Pn,
-                       float& ps0) __attribute__((always_inline)) {
-        constexpr bool PV = decltype(pv_t)::value;
-        constexpr bool SM = decltype(sm_t)::value;
-        const float nmx = (m_run == kNegInf) ? 0.f : -m_run;
-        constexpr int VPF = 3;  // V operands read three products ahead
-        V8 vring[VPF + 1];
-        if constexpr (PV) {
-#pragma unroll
-            for (int p = 0; p < VPF; ++p) vring[p] = vread(Vb, p);
-        }
-        float acc = 0.f, pprev = 0.f;
-#pragma unroll
-        for (int i = 0; i < NPV; ++i) {
-            if constexpr (PV) {
-                if (i + VPF < NPV) vring[(i + VPF) % (VPF + 1)] = vread(Vb, i + VPF);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (SM) {
-                if (i % PPE == 0) {
-                    const int e = i / PPE;
-                    const float p = fast_exp2(__builtin_fmaf(Sn[0][e], c, nmx));
+                } else if constexpr (SM) {  // one exponential per step, converted in pairs
+                    const int r = kk;
+                    const float p = fast_exp2(__builtin_fmaf(So[1][r], c, nmx));
                     acc += p;
-                    if (e & 1) {
+                    if (r & 1) {
                         uint32_t w = cvt_pair<ST>(pprev, p);
                         asm volatile("" : "+v"(acc), "+v"(w));
-                        Pn[e >> 3][(e & 7) >> 1] = w;
+                        Pd[2 + (r >> 3)][(r & 7) >> 1] = w;
                     } else {
                         pprev = p;
                     }
                 }
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (QK) {
+                    const V8* kf = kring[kk % (PF + 1)];
+                    Sn[0] = M::mm(kf[0], qreg[kk], kk == 0 ? zero16 : Sn[0]);
+                    Sn[1] = M::mm(kf[1], qreg[kk], kk == 0 ? zero16 : Sn[1]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (PV) o[i % NDT] = M::mm(vring[i % (VPF + 1)], __builtin_bit_cast(V8, Po[i / NDT]), o[i % NDT]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if constexpr (SM) ps0 = acc;
-    };
-    // Rare paths.  After stage B, the first half of tile j exceeded its bound
-    // (or the row has seen no key yet): the reference moves to the maximum of
-    // the whole tile, so its second half cannot exceed it later; O (which
-    // holds tile j-1 by then) and the row sum are rescaled, and the first
-    // half's exponentials are taken again.
-    auto rescale_b = [&](const f32x16* St, u32x4* Pt, float& ps0) __attribute__((always_inline)) {
-        float tmax = kNegInf;
+            if constexpr (SM) ps1 = acc;
+        };
+        // Stage B: O += V(j-1)^T P(j-1) (when PV, Po = P(j-1)), exponentials of
+        // the first half of tile j (Sn[0]) into Pn[0..1] and their sum ps0 (when SM).
+        auto stage_b = [&](auto pv_t, auto sm_t, const unsigned char* Vb, const u32x4* Po, const f32x16* Sn, u32x4* Pn,
+                           float& ps0) __attribute__((always_inline)) {
+            constexpr bool PV = decltype(pv_t)::value;
+            constexpr bool SM = decltype(sm_t)::value;
+            const float nmx = (m_run == kNegInf) ? 0.f : -m_run;
+            constexpr int VPF = 3;  // V operands read three products ahead
+            V8 vring[VPF + 1];
+            if constexpr (PV) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, St[tt][r]);
-        tmax = fmaxf(tmax, xor32(tmax)) * c;
-        const float mnew = fmaxf(m_run, tmax);
-        const float alpha = fast_exp2(m_run - ((mnew == kNegInf) ? 0.f : mnew));
-        scale_acc<D>(o, alpha);
-        l_half *= alpha;
-        m_run = mnew;
-        const float nmx = (m_run == kNegInf) ? 0.f : -m_run;
-        float s0 = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-            const float p0 = fast_exp2(__builtin_fmaf(St[0][r], c, nmx));
-            const float p1 = fast_exp2(__builtin_fmaf(St[0][r + 1], c, nmx));
-            s0 += p0;
-            s0 += p1;
-            Pt[r >> 3][(r & 7) >> 1] = cvt_pair<ST>(p0, p1);
-        }
-        ps0 = s0;
-    };
-    // After stage A, the second half of tile j-1 exceeded its bound (its
-    // first half passed, so its scores lie below the reference + 8): the
-    // reference moves to the second half's maximum, O (tiles before j-1) and
-    // the row sum are rescaled, the second half's exponentials are taken
-    // again and the first half's 16-bit values and sum are scaled by the same
-    // factor (at most one more rounding of those values, on this rare path).
-    auto rescale_a = [&](const f32x16* St, u32x4* Pt, float& ps0, float& ps1) __attribute__((always_inline)) {
-        float tmax = kNegInf;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, St[1][r]);
-        tmax = fmaxf(tmax, xor32(tmax)) * c;
-        const float mnew = fmaxf(m_run, tmax);
-        // (a row that has seen no key yet -- a window's left edge, rows a
-        // wave shares -- keeps the reference -inf and exponentials against 0)
-        const float alpha = fast_exp2(m_run - ((mnew == kNegInf) ? 0.f : mnew));
-        scale_acc<D>(o, alpha);
-        l_half *= alpha;
-        m_run = mnew;
-        const float nmx = (m_run == kNegInf) ? 0.f : -m_run;
-        float s1 = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-            const float p0 = fast_exp2(__builtin_fmaf(St[1][r], c, nmx));
-            const float p1 = fast_exp2(__builtin_fmaf(St[1][r + 1], c, nmx));
-            s1 += p0;
-            s1 += p1;
-            Pt[2 + (r >> 3)][(r & 7) >> 1] = cvt_pair<ST>(p0, p1);
-        }
-        ps1 = s1;
-#pragma unroll
-        for (int wd = 0; wd < 8; ++wd) {
-            const uint32_t x = Pt[wd >> 2][wd & 3];
-            Pt[wd >> 2][wd & 3] = cvt_pair<ST>(lo_f32<ST>(x) * alpha, hi_f32<ST>(x) * alpha);
-        }
-        ps0 *= alpha;
-    };
-
-    f32x16 SA[2], SB[2];
-    u32x4 PA[4], PB[4];
-    float ps0 = 0.f, ps1 = 0.f;
-    // Slot j (PAR = j & 1): K(j) in sK[PAR], V(j-1) in sV[PAR ^ 1]; tiles
-    // j+1 (K) and j (V) are fetched into the other buffers.  S(j) goes to
-    // SA for even j, SB for odd j; P(j) likewise to PA / PB.
-    auto slot = [&](auto par_t, auto first_t, auto last_t, int j) __attribute__((always_inline)) {
-        constexpr int PAR = decltype(par_t)::value;
-        constexpr bool FIRST = decltype(first_t)::value;  // j == 0: no tile j-1
-        constexpr bool LAST = decltype(last_t)::value;    // j == nt: no tile j
-        const unsigned char* Kc = PAR ? sK1 : sK0;
-        const unsigned char* Vp = PAR ? sV0 : sV1;
-        const uint32_t mKn = PAR ? mK0 : mK1;
-        const uint32_t mVn = PAR ? mV1 : mV0;
-        const unsigned char* Mc = PAR ? sM1 : sM0;  // MASK 2, 3: mask tile j
-        const uint32_t mMn = PAR ? mM0 : mM1;       // ... and where tile j+1's goes
-        const uint32_t mEn = PAR ? mE0 : mE1;
-        f32x16* Sn = PAR ? SB : SA;
-        f32x16* So = PAR ? SA : SB;
-        u32x4* Pn = PAR ? PB : PA;
-        u32x4* Po = PAR ? PA : PB;
-        // K(j+1) now and V(j) after stage A, into the buffers the previous
-        // slot released (issued together, the 8 waves' loads queue for the
-        // address unit at the slot's start)
-        if (j + 1 < nt) {
-            issue(kb64, j + 1, mKn);
-            if constexpr (MASK == 3) {
-                cls_nxt = tile_cls(j + 1);
-                issue_mask(j + 1, cls_nxt, mMn);
+                for (int p = 0; p < VPF; ++p) vring[p] = vread(Vb, p);
             }
-            if constexpr (MASK == 2) issue_mask_dwords(j + 1, mEn);
-        }
-        stage_a(std::integral_constant<bool, !LAST>{}, std::integral_constant<bool, !FIRST>{}, Kc, Sn, So, Po, ps1);
-        if (j < nt) issue(vb64, j, mVn);
-        if constexpr (!FIRST) {
-            // second half of tile j-1 above its bound: rare rescale, then the
-            // row sum takes the whole tile
-            if (__any(ps1 > kPmax)) rescale_a(So, Po, ps0, ps1);
-            l_half += ps0 + ps1;
-        }
-        if constexpr (!LAST) {
-            // Keys past the range (the last tile), and for the masks the tiles
-            // that cross the diagonal or a band edge of one of the wave's rows:
-            // the excluded keys' scores become -inf.
-            const int32_t j0 = j * BN;
-            uint32_t tcls = 3u;
-            if constexpr (MASK == 3) tcls = cls_cur;
-            // One block changes the scores (a single changed path lets the
-            // compiler keep them in the registers the products wrote; with a
-            // second one, every tile paid 32 copies where the paths join).
-            if (MASK == 2 || (MASK == 3 && (tcls != 1u || j0 + BN - 1 > w_hi))) {
-                // the staged mask tile (MASK 3: when the tile's class says a
-                // key is masked): word (tt, g) of this lane holds keys
-                // 32*tt + 8*g + 4*half + [0, 4) of its row; keys past the
-                // range are excluded too.  A tile with no key visible to any
-                // row of the workgroup (class bit 0 clear) is excluded whole,
-                // whether or not its mask was staged.
-                const int ln = (int)__lane_id();
-                const int row = 32 * wave + (ln & 31), h4 = (ln >> 5) * 4;
-                const int32_t hi = (MASK == 3 && !(tcls & 1u)) ? -0x7fffffff : L32 - 1 - j0 - h4;
-                const bool staged = MASK == 2 || (tcls & 2u);
+            float acc = 0.f, pprev = 0.f;
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt) {
-                    uint32_t mw[4] = {0u, 0u, 0u, 0u};
-                    if (staged) {
-#pragma unroll
-                        for (int g = 0; g < 4; ++g) {
-                            if constexpr (MASK == 3)
-                                mw[g] = *reinterpret_cast<const uint32_t*>(
-                                    Mc + ((2 * tt + (g >> 1)) * (32 * NWV) + row) * 16 + 8 * (g & 1) + h4);
-                            else
-                                mw[g] = *reinterpret_cast<const uint32_t*>(Mc + (row >> 2) * 272 + (row & 3) * 64 +
-                                                                           32 * tt + 8 * g + h4);
+            for (int i = 0; i < NPV; ++i) {
+                if constexpr (PV) {
+                    if (i + VPF < NPV) vring[(i + VPF) % (VPF + 1)] = vread(Vb, i + VPF);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (SM) {
+                    if (i % PPE == 0) {
+                        const int e = i / PPE;
+                        const float p = fast_exp2(__builtin_fmaf(Sn[0][e], c, nmx));
+                        acc += p;
+                        if (e & 1) {
+                            uint32_t w = cvt_pair<ST>(pprev, p);
+                            asm volatile("" : "+v"(acc), "+v"(w));
+                            Pn[e >> 3][(e & 7) >> 1] = w;
+                        } else {
+                            pprev = p;
                         }
                     }
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int32_t e = tt * 32 + 8 * (r >> 2) + (r & 3);
-                        const bool ok = e <= hi && ((mw[r >> 2] >> (8 * (r & 3))) & 0xffu) == 0u;
-                        Sn[tt][r] = ok ? Sn[tt][r] : kNegInf;
-                    }
                 }
-            } else if (MASK != 2 && MASK != 3 && (j0 < w_lo || j0 + BN - 1 > w_hi)) {
-                // element (tt, r) is key j0 + e + 4*half, e = 32tt + 8(r/4) + r%4
-                const int ln = (int)__lane_id();
-                const int cl = ln & 31, h4 = (ln >> 5) * 4;
-                int32_t hi = L32 - 1 - j0;
-                if (MASK != 0) hi = min(hi, c_hi - j0 + cl);
-                hi -= h4;
-                const int32_t lo = c_lo - j0 + cl - h4;
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (PV) o[i % NDT] = M::mm(vring[i % (VPF + 1)], __builtin_bit_cast(V8, Po[i / NDT]), o[i % NDT]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (SM) ps0 = acc;
+        };
+        // Rare paths.  After stage B, the first half of tile j exceeded its bound
+        // (or the row has seen no key yet): the reference moves to the maximum of
+        // the whole tile, so its second half cannot exceed it later; O (which
+        // holds tile j-1 by then) and the row sum are rescaled, and the first
+        // half's exponentials are taken again.
+        auto rescale_b = [&](const f32x16* St, u32x4* Pt, float& ps0) __attribute__((always_inline)) {
+            float tmax = kNegInf;
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt)
+            for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int32_t e = tt * 32 + 8 * (r >> 2) + (r & 3);
-                        const bool ok = e <= hi && (MASK != 4 || e >= lo);
-                        Sn[tt][r] = ok ? Sn[tt][r] : kNegInf;
+                for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, St[tt][r]);
+            tmax = fmaxf(tmax, xor32(tmax)) * c;
+            const float mnew = fmaxf(m_run, tmax);
+            const float alpha = fast_exp2(m_run - ((mnew == kNegInf) ? 0.f : mnew));
+            scale_acc<D>(o, alpha);
+            l_half *= alpha;
+            m_run = mnew;
+            const float nmx = (m_run == kNegInf) ? 0.f : -m_run;
+            float s0 = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float p0 = fast_exp2(__builtin_fmaf(St[0][r], c, nmx));
+                const float p1 = fast_exp2(__builtin_fmaf(St[0][r + 1], c, nmx));
+                s0 += p0;
+                s0 += p1;
+                Pt[r >> 3][(r & 7) >> 1] = cvt_pair<ST>(p0, p1);
+            }
+            ps0 = s0;
+        };
+        // After stage A, the second half of tile j-1 exceeded its bound (its
+        // first half passed, so its scores lie below the reference + 8): the
+        // reference moves to the second half's maximum, O (tiles before j-1) and
+        // the row sum are rescaled, the second half's exponentials are taken
+        // again and the first half's 16-bit values and sum are scaled by the same
+        // factor (at most one more rounding of those values, on this rare path).
+        auto rescale_a = [&](const f32x16* St, u32x4* Pt, float& ps0, float& ps1) __attribute__((always_inline)) {
+            float tmax = kNegInf;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, St[1][r]);
+            tmax = fmaxf(tmax, xor32(tmax)) * c;
+            const float mnew = fmaxf(m_run, tmax);
+            // (a row that has seen no key yet -- a window's left edge, rows a
+            // wave shares -- keeps the reference -inf and exponentials against 0)
+            const float alpha = fast_exp2(m_run - ((mnew == kNegInf) ? 0.f : mnew));
+            scale_acc<D>(o, alpha);
+            l_half *= alpha;
+            m_run = mnew;
+            const float nmx = (m_run == kNegInf) ? 0.f : -m_run;
+            float s1 = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float p0 = fast_exp2(__builtin_fmaf(St[1][r], c, nmx));
+                const float p1 = fast_exp2(__builtin_fmaf(St[1][r + 1], c, nmx));
+                s1 += p0;
+                s1 += p1;
+                Pt[2 + (r >> 3)][(r & 7) >> 1] = cvt_pair<ST>(p0, p1);
+            }
+            ps1 = s1;
+#pragma unroll
+            for (int wd = 0; wd < 8; ++wd) {
+                const uint32_t x = Pt[wd >> 2][wd & 3];
+                Pt[wd >> 2][wd & 3] = cvt_pair<ST>(lo_f32<ST>(x) * alpha, hi_f32<ST>(x) * alpha);
+            }
+            ps0 *= alpha;
+        };
+
+        f32x16 SA[2], SB[2];
+        u32x4 PA[4], PB[4];
+        float ps0 = 0.f, ps1 = 0.f;
+        // Slot j (PAR = j & 1): K(j) in sK[PAR], V(j-1) in sV[PAR ^ 1]; tiles
+        // j+1 (K) and j (V) are fetched into the other buffers.  S(j) goes to
+        // SA for even j, SB for odd j; P(j) likewise to PA / PB.
+        auto slot = [&](auto par_t, auto first_t, auto last_t, int j) __attribute__((always_inline)) {
+            constexpr int PAR = decltype(par_t)::value;
+            constexpr bool FIRST = decltype(first_t)::value;  // j == 0: no tile j-1
+            constexpr bool LAST = decltype(last_t)::value;    // j == nt: no tile j
+            const unsigned char* Kc = PAR ? sK1 : sK0;
+            const unsigned char* Vp = PAR ? sV0 : sV1;
+            const uint32_t mKn = PAR ? mK0 : mK1;
+            const uint32_t mVn = PAR ? mV1 : mV0;
+            const unsigned char* Mc = PAR ? sM1 : sM0;  // MASK 2, 3: mask tile j
+            const uint32_t mMn = PAR ? mM0 : mM1;       // ... and where tile j+1's goes
+            const uint32_t mEn = PAR ? mE0 : mE1;
+            f32x16* Sn = PAR ? SB : SA;
+            f32x16* So = PAR ? SA : SB;
+            u32x4* Pn = PAR ? PB : PA;
+            u32x4* Po = PAR ? PA : PB;
+            // K(j+1) now and V(j) after stage A, into the buffers the previous
+            // slot released (issued together, the 8 waves' loads queue for the
+            // address unit at the slot's start)
+            if (j + 1 < nt) {
+                issue(kb64, j + 1, mKn);
+                if constexpr (MASK == 3) {
+                    cls_nxt = tile_cls(j + 1);
+                    issue_mask(j + 1, cls_nxt, mMn);
+                }
+                if constexpr (MASK == 2) issue_mask_dwords(j + 1, mEn);
+            }
+            stage_a(std::integral_constant<bool, !LAST>{}, std::integral_constant<bool, !FIRST>{}, Kc, Sn, So, Po, ps1);
+            if (j < nt) issue(vb64, j, mVn);
+            if constexpr (!FIRST) {
+                // second half of tile j-1 above its bound: rare rescale, then the
+                // row sum takes the whole tile
+                if (__any(ps1 > kPmax)) rescale_a(So, Po, ps0, ps1);
+                l_half += ps0 + ps1;
+            }
+            if constexpr (!LAST) {
+                // Keys past the range (the last tile), and for the masks the tiles
+                // that cross the diagonal or a band edge of one of the wave's rows:
+                // the excluded keys' scores become -inf.
+                const int32_t j0 = j * BN;
+                uint32_t tcls = 3u;
+                if constexpr (MASK == 3) tcls = cls_cur;
+                // One block changes the scores (a single changed path lets the
+                // compiler keep them in the registers the products wrote; with a
+                // second one, every tile paid 32 copies where the paths join).
+                if (MASK == 2 || (MASK == 3 && (tcls != 1u || j0 + BN - 1 > w_hi))) {
+                    // the staged mask tile (MASK 3: when the tile's class says a
+                    // key is masked): word (tt, g) of this lane holds keys
+                    // 32*tt + 8*g + 4*half + [0, 4) of its row; keys past the
+                    // range are excluded too.  A tile with no key visible to any
+                    // row of the workgroup (class bit 0 clear) is excluded whole,
+                    // whether or not its mask was staged.
+                    const int ln = (int)__lane_id();
+                    const int row = 32 * wave + (ln & 31), h4 = (ln >> 5) * 4;
+                    const int32_t hi = (MASK == 3 && !(tcls & 1u)) ? -0x7fffffff : L32 - 1 - j0 - h4;
+                    const bool staged = MASK == 2 || (tcls & 2u);
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt) {
+                        uint32_t mw[4] = {0u, 0u, 0u, 0u};
+                        if (staged) {
+#pragma unroll
+                            for (int g = 0; g < 4; ++g) {
+                                if constexpr (MASK == 3)
+                                    mw[g] = *reinterpret_cast<const uint32_t*>(
+                                        Mc + ((2 * tt + (g >> 1)) * (32 * NWV) + row) * 16 + 8 * (g & 1) + h4);
+                                else
+                                    mw[g] = *reinterpret_cast<const uint32_t*>(Mc + (row >> 2) * 272 + (row & 3) * 64 +
+                                                                               32 * tt + 8 * g + h4);
+                            }
+                        }
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int32_t e = tt * 32 + 8 * (r >> 2) + (r & 3);
+                            const bool ok = e <= hi && ((mw[r >> 2] >> (8 * (r & 3))) & 0xffu) == 0u;
+                            Sn[tt][r] = ok ? Sn[tt][r] : kNegInf;
+                        }
                     }
+                } else if (MASK != 2 && MASK != 3 && (j0 < w_lo || j0 + BN - 1 > w_hi)) {
+                    // element (tt, r) is key j0 + e + 4*half, e = 32tt + 8(r/4) + r%4
+                    const int ln = (int)__lane_id();
+                    const int cl = ln & 31, h4 = (ln >> 5) * 4;
+                    int32_t hi = L32 - 1 - j0;
+                    if (MASK != 0) hi = min(hi, c_hi - j0 + cl);
+                    hi -= h4;
+                    const int32_t lo = c_lo - j0 + cl - h4;
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int32_t e = tt * 32 + 8 * (r >> 2) + (r & 3);
+                            const bool ok = e <= hi && (MASK != 4 || e >= lo);
+                            Sn[tt][r] = ok ? Sn[tt][r] : kNegInf;
+                        }
+                }
             }
-        }
-        stage_b(std::integral_constant<bool, !FIRST>{}, std::integral_constant<bool, !LAST>{}, Vp, Po, Sn, Pn, ps0);
-        if constexpr (!LAST) {
-            // first half of tile j above its bound, or a row that has seen no
-            // key yet: rare rescale against the whole tile's maximum
-            if (__any(ps0 > kPmax || (m_run == kNegInf && qvalid))) rescale_b(Sn, Pn, ps0);
-        }
-        if constexpr (MASK == 3) cls_cur = cls_nxt;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of slot j+1 landed
-        __syncthreads();                                   // ... and everyone else's
-    };
-    using T0 = std::integral_constant<int, 0>;
-    using T1 = std::integral_constant<int, 1>;
-    using BT = std::true_type;
-    using BF = std::false_type;
-
-    if (nt > 0) {
-        issue(kb64, 0, mK0);
-        if constexpr (MASK == 3) {
-            cls_cur = tile_cls(0);
-            issue_mask(0, cls_cur, mM0);
-        }
-        if constexpr (MASK == 2) issue_mask_dwords(0, mE0);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        slot(T0{}, BT{}, BF{}, 0);
-        int j = 1;
-        for (; j + 1 < nt; j += 2) {
-            slot(T1{}, BF{}, BF{}, j);
-            slot(T0{}, BF{}, BF{}, j + 1);
-        }
-        if (j < nt) {
-            slot(T1{}, BF{}, BF{}, j);
-            ++j;
-        }
-        if (nt & 1)
-            slot(T1{}, BF{}, BT{}, nt);
-        else
-            slot(T0{}, BF{}, BT{}, nt);
-    }
-
-    const float l_run = l_half + xor32(l_half);
-    if (qrow < q_full) {
-        const bool empty = !qvalid || (m_run == kNegInf);
-        const float inv = empty ? 0.f : 1.f / l_run;
-        uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + q_off + (int64_t)n1 * a.q_stride_n + qrow * a.q_stride_s;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-#pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4) {
-                const int d0 = dt * 32 + 8 * a4 + 4 * half;
-                float x[4];
-#pragma unroll
-                for (int cc = 0; cc < 4; ++cc) x[cc] = empty ? 0.f : o[dt][4 * a4 + cc] * inv;
-                u32x2 w;
-                w[0] = pack2<ST>(x[0], x[1]);
-                w[1] = pack2<ST>(x[2], x[3]);
-                *reinterpret_cast<u32x2*>(op + d0) = w;
+            stage_b(std::integral_constant<bool, !FIRST>{}, std::integral_constant<bool, !LAST>{}, Vp, Po, Sn, Pn, ps0);
+            if constexpr (!LAST) {
+                // first half of tile j above its bound, or a row that has seen no
+                // key yet: rare rescale against the whole tile's maximum
+                if (__any(ps0 > kPmax || (m_run == kNegInf && qvalid))) rescale_b(Sn, Pn, ps0);
             }
+            if constexpr (MASK == 3) cls_cur = cls_nxt;
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of slot j+1 landed
+            __syncthreads();                                   // ... and everyone else's
+        };
+        using T0 = std::integral_constant<int, 0>;
+        using T1 = std::integral_constant<int, 1>;
+        using BT = std::true_type;
+        using BF = std::false_type;
+
+        const bool have_k0 = fetched;
+        fetched = false;
+        if (nt > 0) {
+            if (!have_k0) {
+                issue(kb64, 0, mK0);
+                if constexpr (MASK == 3) {
+                    cls_cur = tile_cls(0);
+                    issue_mask(0, cls_cur, mM0);
+                }
+                if constexpr (MASK == 2) issue_mask_dwords(0, mE0);
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                __syncthreads();
+            }
+            slot(T0{}, BT{}, BF{}, 0);
+            int j = 1;
+            for (; j + 1 < nt; j += 2) {
+                slot(T1{}, BF{}, BF{}, j);
+                slot(T0{}, BF{}, BF{}, j + 1);
+            }
+            if (j < nt) {
+                slot(T1{}, BF{}, BF{}, j);
+                ++j;
+            }
+            if constexpr (PERSIST) fetch_next();
+            if (nt & 1)
+                slot(T1{}, BF{}, BT{}, nt);
+            else
+                slot(T0{}, BF{}, BT{}, nt);
         }
-        if (half == 0 && a.lse) a.lse[lse_row0 + qrow * lse_step] = empty ? kPosInf : (m_run + log2f(l_run)) * kLn2;
-    }
+
+        const float l_run = l_half + xor32(l_half);
+        if (qrow < q_full) {
+            const bool empty = !qvalid || (m_run == kNegInf);
+            const float inv = empty ? 0.f : 1.f / l_run;
+            uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + q_off + (int64_t)n1 * a.q_stride_n + qrow * a.q_stride_s;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const int d0 = dt * 32 + 8 * a4 + 4 * half;
+                    float x[4];
+#pragma unroll
+                    for (int cc = 0; cc < 4; ++cc) x[cc] = empty ? 0.f : o[dt][4 * a4 + cc] * inv;
+                    u32x2 w;
+                    w[0] = pack2<ST>(x[0], x[1]);
+                    w[1] = pack2<ST>(x[2], x[3]);
+                    *reinterpret_cast<u32x2*>(op + d0) = w;
+                }
+            }
+            if (half == 0 && a.lse) a.lse[lse_row0 + qrow * lse_step] = empty ? kPosInf : (m_run + log2f(l_run)) * kLn2;
+        }
+        if constexpr (!PERSIST) return;
+        unit += gridDim.x;
+        if (unit >= units) return;
+    }  // units
 }
 
 template <typename ST, int D>
@@ -1251,24 +1355,48 @@ static hipError_t dispatch_prefill(const PrefillArgs& a, int mask_mode, int64_t 
     return hipGetLastError();
 }
 
+int64_t prefill_persistent_grid(int head_dim, int mask_mode, bool packed, int64_t units, int cus) {
+    if (head_dim != 128 || !(mask_mode == 0 || mask_mode == 4) || packed) return 0;
+    const int64_t grid = (int64_t)(cus / 8) * 8;
+    return (grid >= 8 && units > grid) ? grid : 0;
+}
+
+template <typename ST, int D, bool P>
+static void launch_il_mask(const PrefillArgs& a, int mask_mode, dim3 grid, dim3 block, hipStream_t s) {
+    switch (mask_mode) {
+        case 0: hipLaunchKernelGGL((prefill_il_kernel<ST, D, 0, P>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((prefill_il_kernel<ST, D, 4, P>), grid, block, 0, s, a); break;
+        default:
+            if constexpr (!P) {
+                switch (mask_mode) {
+                    case 1: hipLaunchKernelGGL((prefill_il_kernel<ST, D, 1, false>), grid, block, 0, s, a); break;
+                    case 2: hipLaunchKernelGGL((prefill_il_kernel<ST, D, 2, false>), grid, block, 0, s, a); break;
+                    case 3: hipLaunchKernelGGL((prefill_il_kernel<ST, D, 3, false>), grid, block, 0, s, a); break;
+                }
+            }
+    }
+}
+
 template <typename ST, int D>
 static hipError_t launch_il(const PrefillArgs& a0, int mask_mode, int64_t batch, hipStream_t s) {
     constexpr int R = 32 * il_waves<D>();  // query rows per workgroup
+    if (mask_mode < 0 || mask_mode > 4) return hipErrorInvalidValue;
     PrefillArgs a = a0;
     a.q_tiles = (int32_t)((a.q_seq + R - 1) / R);
-    const int64_t blocks = a.work ? (int64_t)(a.work_items + 7) / 8 * 8 * a.num_heads
-                                  : (int64_t)a.q_tiles * batch * a.num_heads;
-    if (blocks <= 0) return hipSuccess;
-    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)blocks), block(2 * R);
-    switch (mask_mode) {
-        case 0: hipLaunchKernelGGL((prefill_il_kernel<ST, D, 0>), grid, block, 0, s, a); break;
-        case 1: hipLaunchKernelGGL((prefill_il_kernel<ST, D, 1>), grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((prefill_il_kernel<ST, D, 2>), grid, block, 0, s, a); break;
-        case 3: hipLaunchKernelGGL((prefill_il_kernel<ST, D, 3>), grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((prefill_il_kernel<ST, D, 4>), grid, block, 0, s, a); break;
-        default: return hipErrorInvalidValue;
+    const int64_t units = a.work ? (int64_t)(a.work_items + 7) / 8 * 8 * a.num_heads
+                                 : (int64_t)a.q_tiles * batch * a.num_heads;
+    if (units <= 0) return hipSuccess;
+    if (units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    a.units = units;
+    const int64_t pgrid = prefill_persistent_grid(D, mask_mode, a.work != nullptr, units, a.cus);
+    const dim3 block(2 * R);
+    if constexpr (D == 128) {
+        if (pgrid > 0) {
+            launch_il_mask<ST, D, true>(a, mask_mode, dim3((unsigned)pgrid), block, s);
+            return hipGetLastError();
+        }
     }
+    launch_il_mask<ST, D, false>(a, mask_mode, dim3((unsigned)units), block, s);
     return hipGetLastError();
 }
 

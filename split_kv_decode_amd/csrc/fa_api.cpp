@@ -773,8 +773,9 @@ std::string describe(const fa_params* p, const Shape& s) {
         if (p->layout == FA_TND)
             std::snprintf(grid, sizeof grid, "(work list of <= %lld items) x %lld heads", (long long)varlen_capacity(s),
                           (long long)s.QN);
-        else if (const int64_t pg = il ? fa::prefill_persistent_grid((int)s.D, mk, false, prefill_workgroups(p, s),
-                                                                        device_cus())
+        else if (const int64_t pg = il ? fa::prefill_persistent_grid(
+                                             (int)s.D, mk, false, p->actual_seq_lengths || p->seqused_q,
+                                             prefill_workgroups(p, s), device_cus())
                                        : 0)
             std::snprintf(grid, sizeof grid, "%lld (persistent, over %lld units)", (long long)pg,
                           (long long)prefill_workgroups(p, s));

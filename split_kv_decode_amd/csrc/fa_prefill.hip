@@ -585,7 +585,7 @@ template <typename ST, int D, int MASK, bool PERSIST>
 __global__ __launch_bounds__(64 * il_waves<D>(), 1) void prefill_il_kernel(PrefillArgs a) {
     static_assert(MASK >= 0 && MASK <= 4, "mask kind");
     static_assert(D == 128 || D == 256, "head dim");
-    static_assert(!PERSIST || MASK == 0 || MASK == 4, "persistent launch: mask-free or window");
+    static_assert(!PERSIST || MASK == 0 || MASK == 1 || MASK == 4, "persistent launch: no mask, causal or window");
     using M = Mfma<ST>;
     using V8 = typename M::V8;
     using E = typename M::E;
@@ -756,6 +756,16 @@ __global__ __launch_bounds__(64 * il_waves<D>(), 1) void prefill_il_kernel(Prefi
     // so every unit keeps the XCD the plain launch would give it).  The next
     // unit's Q and first K tile are fetched during the current unit's last
     // slot, which reads neither Q nor a K buffer.
+    // Causal costs fall with the rank and the units come heaviest first, so
+    // the rounds run forward and backward in turn (a snake): a workgroup's
+    // units then sum to about the same cost (ranks 15-r, 8+r, 7-r, r of
+    // sixteen in four rounds).
+    auto slot_unit = [&](int64_t k) __attribute__((always_inline)) -> int64_t {
+        const int64_t G = gridDim.x;
+        return (PERSIST && MASK == 1 && (k & 1)) ? (k + 1) * G - 1 - (int64_t)blockIdx.x
+                                                  : k * G + (int64_t)blockIdx.x;
+    };
+    int64_t round = 0;  // rounds of gridDim.x units
     int64_t unit = blockIdx.x;
     bool fetched = false;  // Q of `unit` in qreg, its first K tile in sK0
     for (;;) {
@@ -966,7 +976,7 @@ __global__ __launch_bounds__(64 * il_waves<D>(), 1) void prefill_il_kernel(Prefi
         // Persistent launch, before the last slot: Q of the next unit into qreg
         // and its first K tile into sK0.
         auto fetch_next = [&]() __attribute__((always_inline)) {
-            const int64_t nu = unit + gridDim.x;
+            const int64_t nu = slot_unit(round + 1);
             if (nu >= units) return;
             const auto& A = fresh_args();
             const UnitGeom gn = unit_geom(nu, A);
@@ -1336,7 +1346,7 @@ __global__ __launch_bounds__(64 * il_waves<D>(), 1) void prefill_il_kernel(Prefi
             if (half == 0 && a.lse) a.lse[lse_row0 + qrow * lse_step] = empty ? kPosInf : (m_run + log2f(l_run)) * kLn2;
         }
         if constexpr (!PERSIST) return;
-        unit += gridDim.x;
+        unit = slot_unit(++round);
         if (unit >= units) return;
     }  // units
 }
@@ -1355,8 +1365,9 @@ static hipError_t dispatch_prefill(const PrefillArgs& a, int mask_mode, int64_t 
     return hipGetLastError();
 }
 
-int64_t prefill_persistent_grid(int head_dim, int mask_mode, bool packed, int64_t units, int cus) {
-    if (head_dim != 128 || !(mask_mode == 0 || mask_mode == 4) || packed) return 0;
+int64_t prefill_persistent_grid(int head_dim, int mask_mode, bool packed, bool ragged, int64_t units, int cus) {
+    if (head_dim != 128 || packed) return 0;
+    if (!(mask_mode == 0 || mask_mode == 4 || (mask_mode == 1 && !ragged))) return 0;
     const int64_t grid = (int64_t)(cus / 8) * 8;
     return (grid >= 8 && units > grid) ? grid : 0;
 }
@@ -1365,11 +1376,11 @@ template <typename ST, int D, bool P>
 static void launch_il_mask(const PrefillArgs& a, int mask_mode, dim3 grid, dim3 block, hipStream_t s) {
     switch (mask_mode) {
         case 0: hipLaunchKernelGGL((prefill_il_kernel<ST, D, 0, P>), grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((prefill_il_kernel<ST, D, 1, P>), grid, block, 0, s, a); break;
         case 4: hipLaunchKernelGGL((prefill_il_kernel<ST, D, 4, P>), grid, block, 0, s, a); break;
         default:
             if constexpr (!P) {
                 switch (mask_mode) {
-                    case 1: hipLaunchKernelGGL((prefill_il_kernel<ST, D, 1, false>), grid, block, 0, s, a); break;
                     case 2: hipLaunchKernelGGL((prefill_il_kernel<ST, D, 2, false>), grid, block, 0, s, a); break;
                     case 3: hipLaunchKernelGGL((prefill_il_kernel<ST, D, 3, false>), grid, block, 0, s, a); break;
                 }
@@ -1388,7 +1399,7 @@ static hipError_t launch_il(const PrefillArgs& a0, int mask_mode, int64_t batch,
     if (units <= 0) return hipSuccess;
     if (units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     a.units = units;
-    const int64_t pgrid = prefill_persistent_grid(D, mask_mode, a.work != nullptr, units, a.cus);
+    const int64_t pgrid = prefill_persistent_grid(D, mask_mode, a.work != nullptr, a.lens || a.used_q, units, a.cus);
     const dim3 block(2 * R);
     if constexpr (D == 128) {
         if (pgrid > 0) {

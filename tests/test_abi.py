@@ -387,7 +387,12 @@ def test_describe_names_path_kernels_and_plan(lib):
               win_left=1024, win_right=0),
          ["prefill_il_kernel<BF16,128,4>", "workgroups=256 (persistent, over 1024 units)"]),
         (dict(batch=2, num_heads=32, q_seq=4096, kv_seq=4096, head_dim=128, layout="BSND", mask_mode="causal"),
+         ["prefill_il_kernel<BF16,128,1>", "workgroups=256 (persistent, over 1024 units)"]),
+        (dict(batch=2, num_heads=32, q_seq=4096, kv_seq=4096, head_dim=128, layout="BSND", mask_mode="causal",
+              actual_seq_lengths=F),
          ["prefill_il_kernel<BF16,128,1>", "workgroups=1024 "]),
+        (dict(batch=2, num_heads=16, q_seq=4096, kv_seq=4096, head_dim=256),
+         ["prefill_il_kernel<BF16,256,0>", "workgroups=1024 "]),
         (dict(batch=1, num_heads=32, q_seq=2048, kv_seq=2048, head_dim=128),
          ["prefill_il_kernel<BF16,128,0>", "workgroups=256 "]),
         (dict(batch=2, num_heads=16, q_seq=4096, kv_seq=4096, head_dim=256, mask_mode="causal", dtype="f16"),

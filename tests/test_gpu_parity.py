@@ -1183,10 +1183,11 @@ def test_scale_zero_gives_the_mean_of_visible_values(case, opts):
     check(got, got_lse, ref, ref_lse, f"scale 0 {case}")
 
 
-# More query tiles of 256 rows than the device has CUs: the mask-free and the
-# window prefill at head dim 128 then run one persistent workgroup per CU that
-# takes the tiles in turn, fetching the next tile's Q and first K tile during
-# the current one's last slot.
+# More query tiles of 256 rows than the device has CUs: the mask-free, the
+# window and (without per-batch lengths) the causal prefill at head dim 128
+# then run one persistent workgroup per CU that takes the tiles in turn,
+# fetching the next tile's Q and first K tile during the current one's last
+# slot; causal rounds alternate direction.
 PERSISTENT_CASES = [
     (dict(B=3, QN=44, KVN=11, QS=300, KVS=300, D=128), (300, 0, 131), None, None),
     (dict(layout="BSND", B=3, QN=44, KVN=4, QS=300, KVS=333, D=128, dtype="f16"), (333, 77, 1),
@@ -1194,13 +1195,15 @@ PERSISTENT_CASES = [
     (dict(B=3, QN=44, KVN=44, QS=300, KVS=700, D=128), (700, 5, 400), (100, 20), None),
     (dict(layout="BSND", B=2, QN=64, KVN=8, QS=520, KVS=520, D=128), None, (300, 0), [520, 400]),
     (dict(B=3, QN=44, KVN=4, QS=300, KVS=600, D=128, scale=1.0), None, (-1, 40), [300, 299, 1]),
+    (dict(B=3, QN=44, KVN=4, QS=300, KVS=300, D=128), None, "causal", None),
+    (dict(layout="BSND", B=1, QN=52, KVN=4, QS=1300, KVS=1400, D=128, dtype="f16"), None, "causal", None),
 ]
 
 
-@pytest.mark.parametrize("case,lens,window,seqused", PERSISTENT_CASES,
+@pytest.mark.parametrize("case,lens,mode,seqused", PERSISTENT_CASES,
                          ids=["none", "none_f16_bsnd_used", "window_back", "window_causal_used",
-                              "window_forward_rescale"])
-def test_persistent_prefill_matches_oracle_and_per_batch_launches(case, lens, window, seqused):
+                              "window_forward_rescale", "causal_partial_round", "causal_six_ranks"])
+def test_persistent_prefill_matches_oracle_and_per_batch_launches(case, lens, mode, seqused):
     """The persistent launch against the oracle, and bit for bit against each batch
     computed alone (fewer tiles than CUs: one workgroup per tile).  KV lengths include
     0 and 1, used query rows include 0 and a partial last tile."""
@@ -1210,18 +1213,21 @@ def test_persistent_prefill_matches_oracle_and_per_batch_launches(case, lens, wi
     s = inp.spec
     units = s.B * s.QN * -(-s.QS // 256)
     assert units > 256, "the case must have more tiles than the CUs of the device"
+    causal = mode == "causal"
+    window = None if (mode is None or causal) else mode
     p = fa.params_for(dev16(inp.q, s.dtype), dev16(inp.k, s.dtype), layout=s.layout,
-                      scale=s.softmax_scale, window=window)
+                      scale=s.softmax_scale, window=window, causal=causal)
     assert "persistent" in fa.fa_describe(p), fa.fa_describe(p)
-    got, got_lse, prob = run_general(inp, window=window, seqused=seqused)
+    got, got_lse, prob = run_general(inp, window=window, causal=causal, seqused=seqused)
     ref, ref_lse = oracle.attention_rows(prob, inp.q, inp.k, inp.v)
-    check(got, got_lse, ref, ref_lse, f"persistent {case} {window}")
+    check(got, got_lse, ref, ref_lse, f"persistent {case} {mode}")
     per_row = s.QN * s.QS
-    for b in range(s.B):
+    for b in range(s.B if s.B > 1 else 0):
         one = dataclasses.replace(
             inp, spec=dataclasses.replace(s, B=1), q=inp.q[b:b + 1], k=inp.k[b:b + 1], v=inp.v[b:b + 1],
             lens=None if inp.lens is None else inp.lens[b:b + 1])
-        o1, l1, _ = run_general(one, window=window, seqused=None if seqused is None else seqused[b:b + 1])
+        o1, l1, _ = run_general(one, window=window, causal=causal,
+                                seqused=None if seqused is None else seqused[b:b + 1])
         assert np.array_equal(o1, got[b * per_row:(b + 1) * per_row]), f"batch {b} output"
         assert np.array_equal(l1, got_lse[b * per_row:(b + 1) * per_row]), f"batch {b} lse"
 

@@ -769,11 +769,11 @@ __global__ __launch_bounds__(64 * il_waves<D>(), 1) void prefill_il_kernel(Prefi
     int64_t unit = blockIdx.x;
     bool fetched = false;  // Q of `unit` in qreg, its first K tile in sK0
     for (;;) {
-        // Lane-derived values come from an opaque copy of the thread id per unit,
-        // so none is kept live across units.
-        int tid = tid0;
-        if constexpr (PERSIST) asm volatile("" : "+v"(tid));
-        const int lane = tid & 63;
+        // The persistent kernel produces the lane id afresh for each unit, so
+        // neither the thread id nor a value derived from it is kept live
+        // across units (which cost copies in the KV loop).
+        int lane = tid0 & 63;
+        if constexpr (PERSIST) asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
         const int half = lane >> 5;
         const int col = lane & 31;
         const UnitGeom ug = [&]() __attribute__((always_inline)) {

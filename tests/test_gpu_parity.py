@@ -1232,6 +1232,39 @@ def test_persistent_prefill_matches_oracle_and_per_batch_launches(case, lens, mo
         assert np.array_equal(l1, got_lse[b * per_row:(b + 1) * per_row]), f"batch {b} lse"
 
 
+def test_persistent_prefill_graph_replays():
+    """The persistent causal prefill captured in a HIP graph: every replay, with new q and
+    eager work in between, equals the eager call bit for bit (the launch keeps no state
+    between calls)."""
+    inp = fa_synth.make(spec(layout="BSND", B=3, QN=44, KVN=4, QS=300, KVS=300, D=128, seed=171))
+    s = inp.spec
+    q, k, v = (dev16(x, s.dtype) for x in (inp.q, inp.k, inp.v))
+    p = fa.params_for(q, k, layout=s.layout, scale=s.softmax_scale, causal=True)
+    assert "persistent" in fa.fa_describe(p), fa.fa_describe(p)
+    out = torch.empty_like(q)
+    lse = torch.empty((s.B, s.QN, s.QS), dtype=torch.float32, device=DEV)
+    qg = q.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm up off the capture
+        fa.fa_fwd(p, qg, k, v, out, lse, None, 0, side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fa.fa_fwd(p, qg, k, v, out, lse, None, 0, torch.cuda.current_stream())
+    for rep in range(3):
+        qn = torch.randn(q.shape, device=DEV).to(q.dtype)
+        qg.copy_(qn)
+        graph.replay()
+        torch.cuda.synchronize()
+        ref_out, ref_lse = fa.fwd(qn, k, v, layout=s.layout, scale=s.softmax_scale, causal=True,
+                                  return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out), f"replay {rep}"
+        assert torch.equal(lse, ref_lse), f"replay {rep}"
+
+
 @pytest.mark.parametrize("paging,g", [(("PA_BBND", 128), 4), (("PA_BNBD", 48), 4), (("PA_BBND", 128), 2),
                                       (("PA_BBND", 128), 1), (("PA_BNBD", 64), 8)])
 def test_decode_fused_on_paged_cache(paging, g):

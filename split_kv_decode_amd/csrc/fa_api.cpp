@@ -769,18 +769,20 @@ std::string describe(const fa_params* p, const Shape& s) {
         const bool il = fa::prefill_interleaved((int)s.D, mk, dw);
         const int64_t rows = fa::prefill_rows_per_tile((int)s.D, mk, dw);
         const MaskSummaryGeom mg = mask_summary_geom(p, s);
-        char grid[96];
-        if (p->layout == FA_TND)
+        char grid[160];
+        const int64_t units =
+            p->layout == FA_TND ? (varlen_capacity(s) + 7) / 8 * 8 * s.QN : prefill_workgroups(p, s);
+        const int64_t pg = il ? fa::prefill_persistent_grid((int)s.D, mk, units, device_cus()) : 0;
+        if (p->layout == FA_TND && pg)
+            std::snprintf(grid, sizeof grid, "%lld (persistent, over the work list of <= %lld items x %lld heads)",
+                          (long long)pg, (long long)varlen_capacity(s), (long long)s.QN);
+        else if (p->layout == FA_TND)
             std::snprintf(grid, sizeof grid, "(work list of <= %lld items) x %lld heads", (long long)varlen_capacity(s),
                           (long long)s.QN);
-        else if (const int64_t pg = il ? fa::prefill_persistent_grid(
-                                             (int)s.D, mk, false, p->actual_seq_lengths || p->seqused_q,
-                                             prefill_workgroups(p, s), device_cus())
-                                       : 0)
-            std::snprintf(grid, sizeof grid, "%lld (persistent, over %lld units)", (long long)pg,
-                          (long long)prefill_workgroups(p, s));
+        else if (pg)
+            std::snprintf(grid, sizeof grid, "%lld (persistent, over %lld units)", (long long)pg, (long long)units);
         else
-            std::snprintf(grid, sizeof grid, "%lld", (long long)prefill_workgroups(p, s));
+            std::snprintf(grid, sizeof grid, "%lld", (long long)units);
         std::snprintf(body, sizeof body, "path=prefill%s%s kernel=%s<%s,%lld,%d> rows=%lld workgroups=%s%s",
                       p->layout == FA_TND ? " pre=varlen_schedule_kernel" : "",
                       mg.blocks > 0 ? " pre=mask_summary_kernel (with a workspace)" : "",

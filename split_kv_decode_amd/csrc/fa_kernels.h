@@ -355,10 +355,9 @@ int prefill_rows_per_tile(int head_dim, int mask_mode, bool mask_dwords);
 bool prefill_interleaved(int head_dim, int mask_mode, bool mask_dwords);
 // Workgroups of a persistent interleaved launch (one per CU, a multiple of 8,
 // each taking units in turn), or 0 when the launch is one workgroup per unit:
-// head dim 128 without a mask, with a window, or causal without per-batch
-// lengths (ragged: KV or used query lengths), padded layouts, more units than
-// CUs.
-int64_t prefill_persistent_grid(int head_dim, int mask_mode, bool packed, bool ragged, int64_t units, int cus);
+// head dim 128 without a mask, with a window or causal, more units than CUs
+// (on the packed layout, entries x heads).
+int64_t prefill_persistent_grid(int head_dim, int mask_mode, int64_t units, int cus);
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int mask_mode,
                           int64_t batch, hipStream_t stream);
 hipError_t launch_varlen_schedule(const VarlenScheduleArgs& a, hipStream_t stream);

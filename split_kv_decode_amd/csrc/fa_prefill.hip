@@ -581,11 +581,12 @@ __global__ __launch_bounds__(256, (D == 256) ? 1 : 2) void prefill_kernel(Prefil
 template <int D>
 constexpr int il_waves() { return D == 256 ? 4 : 8; }
 
-template <typename ST, int D, int MASK, bool PERSIST>
+template <typename ST, int D, int MASK, bool PERSIST, bool PACKED = false>
 __global__ __launch_bounds__(64 * il_waves<D>(), 1) void prefill_il_kernel(PrefillArgs a) {
     static_assert(MASK >= 0 && MASK <= 4, "mask kind");
     static_assert(D == 128 || D == 256, "head dim");
     static_assert(!PERSIST || MASK == 0 || MASK == 1 || MASK == 4, "persistent launch: no mask, causal or window");
+    static_assert(!PACKED || PERSIST, "PACKED: the persistent kernel of the packed layout");
     using M = Mfma<ST>;
     using V8 = typename M::V8;
     using E = typename M::E;
@@ -663,9 +664,9 @@ __global__ __launch_bounds__(64 * il_waves<D>(), 1) void prefill_il_kernel(Prefi
         g.valid = true;
         g.q_used = A.q_seq;
         g.q_full = A.q_seq;
-        // (the persistent kernel is never launched on the packed layout, and
-        // compiling this branch into it cost the padded layouts 0.5-1 %)
-        if (!PERSIST && A.work) {
+        // (the persistent kernel of the padded layouts leaves this branch
+        // out: compiled in, it cost them 0.5-1 %)
+        if ((!PERSIST || PACKED) && A.work) {
             // Packed layout: slot 8k + x (dispatched to XCD x) takes head k % N
             // of work item 8*(k / N) + x, so the heaviest items spread over all
             // XCDs and the heads of one item (which share K/V under GQA) share an L2.
@@ -761,7 +762,7 @@ __global__ __launch_bounds__(64 * il_waves<D>(), 1) void prefill_il_kernel(Prefi
     // Causal costs fall with the rank and the units come heaviest first, so
     // the rounds run forward and backward in turn (a snake): a workgroup's
     // units then sum to about the same cost (ranks 15-r, 8+r, 7-r, r of
-    // sixteen in four rounds).
+    // sixteen in four rounds; with per-batch lengths, nearly so).
     auto slot_unit = [&](int64_t k) __attribute__((always_inline)) -> int64_t {
         const int64_t G = gridDim.x;
         return (PERSIST && MASK == 1 && (k & 1)) ? (k + 1) * G - 1 - (int64_t)blockIdx.x
@@ -784,7 +785,11 @@ __global__ __launch_bounds__(64 * il_waves<D>(), 1) void prefill_il_kernel(Prefi
             else
                 return unit_geom(unit, a);
         }();
-        if (!ug.valid) return;
+        // An entry that pads the packed work list: nothing to compute or write.
+        if (!ug.valid) {
+            if constexpr (!PERSIST) return;
+        }
+        const bool live = ug.valid;
         const int qt = ug.qt, n1 = ug.n1;
         const int64_t b = ug.b, L = ug.L, q_used = ug.q_used, q_full = ug.q_full;
         const int64_t q_off = ug.q_off, kv_off = ug.kv_off, lse_row0 = ug.lse_row0, lse_step = ug.lse_step;
@@ -794,7 +799,7 @@ __global__ __launch_bounds__(64 * il_waves<D>(), 1) void prefill_il_kernel(Prefi
         const int64_t qrow = i0 + 32 * wave + col;
         const bool qvalid = qrow < q_used;
 
-        if (!fetched) {
+        if (!fetched && live) {
             if constexpr (PERSIST)
                 load_q(ug, lane, fresh_args());
             else
@@ -840,7 +845,7 @@ __global__ __launch_bounds__(64 * il_waves<D>(), 1) void prefill_il_kernel(Prefi
                 if ((int64_t)(last + 1) * BN < kv_end) kv_end = (int64_t)(last + 1) * BN;
             }
         }
-        const int nt = (i0 >= q_used || kv_end <= kbeg) ? 0 : (int)((kv_end - kbeg + BN - 1) / BN);
+        const int nt = (!live || i0 >= q_used || kv_end <= kbeg) ? 0 : (int)((kv_end - kbeg + BN - 1) / BN);
 
         f32x16 o[D / 32];
 #pragma unroll
@@ -1327,7 +1332,7 @@ __global__ __launch_bounds__(64 * il_waves<D>(), 1) void prefill_il_kernel(Prefi
         }
 
         const float l_run = l_half + xor32(l_half);
-        if (qrow < q_full) {
+        if (live && qrow < q_full) {
             const bool empty = !qvalid || (m_run == kNegInf);
             const float inv = empty ? 0.f : 1.f / l_run;
             uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + q_off + (int64_t)n1 * a.q_stride_n + qrow * a.q_stride_s;
@@ -1367,19 +1372,19 @@ static hipError_t dispatch_prefill(const PrefillArgs& a, int mask_mode, int64_t 
     return hipGetLastError();
 }
 
-int64_t prefill_persistent_grid(int head_dim, int mask_mode, bool packed, bool ragged, int64_t units, int cus) {
-    if (head_dim != 128 || packed) return 0;
-    if (!(mask_mode == 0 || mask_mode == 4 || (mask_mode == 1 && !ragged))) return 0;
+int64_t prefill_persistent_grid(int head_dim, int mask_mode, int64_t units, int cus) {
+    if (head_dim != 128) return 0;
+    if (!(mask_mode == 0 || mask_mode == 1 || mask_mode == 4)) return 0;
     const int64_t grid = (int64_t)(cus / 8) * 8;
     return (grid >= 8 && units > grid) ? grid : 0;
 }
 
-template <typename ST, int D, bool P>
+template <typename ST, int D, bool P, bool PK = false>
 static void launch_il_mask(const PrefillArgs& a, int mask_mode, dim3 grid, dim3 block, hipStream_t s) {
     switch (mask_mode) {
-        case 0: hipLaunchKernelGGL((prefill_il_kernel<ST, D, 0, P>), grid, block, 0, s, a); break;
-        case 1: hipLaunchKernelGGL((prefill_il_kernel<ST, D, 1, P>), grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((prefill_il_kernel<ST, D, 4, P>), grid, block, 0, s, a); break;
+        case 0: hipLaunchKernelGGL((prefill_il_kernel<ST, D, 0, P, PK>), grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((prefill_il_kernel<ST, D, 1, P, PK>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((prefill_il_kernel<ST, D, 4, P, PK>), grid, block, 0, s, a); break;
         default:
             if constexpr (!P) {
                 switch (mask_mode) {
@@ -1401,11 +1406,14 @@ static hipError_t launch_il(const PrefillArgs& a0, int mask_mode, int64_t batch,
     if (units <= 0) return hipSuccess;
     if (units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     a.units = units;
-    const int64_t pgrid = prefill_persistent_grid(D, mask_mode, a.work != nullptr, a.lens || a.used_q, units, a.cus);
+    const int64_t pgrid = prefill_persistent_grid(D, mask_mode, units, a.cus);
     const dim3 block(2 * R);
     if constexpr (D == 128) {
         if (pgrid > 0) {
-            launch_il_mask<ST, D, true>(a, mask_mode, dim3((unsigned)pgrid), block, s);
+            if (a.work)
+                launch_il_mask<ST, D, true, true>(a, mask_mode, dim3((unsigned)pgrid), block, s);
+            else
+                launch_il_mask<ST, D, true>(a, mask_mode, dim3((unsigned)pgrid), block, s);
             return hipGetLastError();
         }
     }

@@ -390,7 +390,7 @@ def test_describe_names_path_kernels_and_plan(lib):
          ["prefill_il_kernel<BF16,128,1>", "workgroups=256 (persistent, over 1024 units)"]),
         (dict(batch=2, num_heads=32, q_seq=4096, kv_seq=4096, head_dim=128, layout="BSND", mask_mode="causal",
               actual_seq_lengths=F),
-         ["prefill_il_kernel<BF16,128,1>", "workgroups=1024 "]),
+         ["prefill_il_kernel<BF16,128,1>", "workgroups=256 (persistent, over 1024 units)"]),
         (dict(batch=2, num_heads=16, q_seq=4096, kv_seq=4096, head_dim=256),
          ["prefill_il_kernel<BF16,256,0>", "workgroups=1024 "]),
         (dict(batch=1, num_heads=32, q_seq=2048, kv_seq=2048, head_dim=128),
@@ -415,7 +415,11 @@ def test_describe_names_path_kernels_and_plan(lib):
          ["path=general-split", "stage1=decode_mfma_kernel", "then combine_kernel"]),
         (dict(batch=16, num_heads=32, num_kv_heads=8, q_seq=55635, kv_seq=55635, head_dim=128, layout="TND",
               mask_mode="causal", cu_seqlens_q=F, cu_seqlens_kv=F),
-         ["path=prefill", "pre=varlen_schedule_kernel", "prefill_il_kernel<BF16,128,1>", "32 heads"]),
+         ["path=prefill", "pre=varlen_schedule_kernel", "prefill_il_kernel<BF16,128,1>", "32 heads",
+          "workgroups=256 (persistent, over the work list of <= "]),
+        (dict(batch=2, num_heads=4, q_seq=300, kv_seq=300, head_dim=128, layout="TND", mask_mode="causal",
+              cu_seqlens_q=F, cu_seqlens_kv=F),
+         ["prefill_il_kernel<BF16,128,1>", "workgroups=(work list of <= 6 items) x 4 heads"]),
     ]
     for kw, want in cases:
         p = fa.make_params(**kw)

@@ -824,6 +824,38 @@ def test_packed_equals_each_sequence_alone():
         assert torch.equal(lse[q0:q1], l1[0].transpose(0, 1))
 
 
+@pytest.mark.parametrize("mode,window", [("causal", None), ("none", None), ("window", (150, 20))])
+def test_packed_persistent_matches_oracle_and_each_sequence(mode, window):
+    """More work-list entries x heads than CUs: the packed prefill runs one persistent
+    workgroup per CU over the entries (padding entries included, which it skips).  Checked
+    against the oracle, and bit for bit against sequences computed alone (a
+    one-workgroup-per-tile launch)."""
+    x = fa_synth.make_packed(40, 8, 2, 128, q_lens=(0, 300), seed=114)
+    T = int(x.cu_q[-1])
+    entries = -(-T // 128) + 40 + 1
+    assert -(-entries // 8) * 8 * 8 > 256
+    out, lse, q_bits = run_packed(x, mode, window)
+    prob = packed_prob(x, T, mode, window or (-1, -1))
+    ref, ref_lse = oracle.attention(prob, q_bits, x.k, x.v)
+    check(to_np(out).reshape(-1, x.D), to_np(lse).reshape(-1), ref.reshape(-1, x.D), ref_lse.reshape(-1),
+          f"packed persistent {mode}")
+    seen = 0
+    for b in range(40):
+        q0, q1, k0, k1 = (int(v) for v in (x.cu_q[b], x.cu_q[b + 1], x.cu_kv[b], x.cu_kv[b + 1]))
+        if q1 == q0 or k1 == k0:
+            continue
+        q = dev16(x.q[None, q0:q1], x.dtype)
+        k, v = dev16(x.k[None, k0:k1], x.dtype), dev16(x.v[None, k0:k1], x.dtype)
+        o1, l1 = fa.fwd(q, k, v, layout="BSND", scale=x.scale, causal=(mode == "causal"), window=window,
+                        return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(out[q0:q1], o1[0]), f"sequence {b}"
+        assert torch.equal(lse[q0:q1], l1[0].transpose(0, 1)), f"sequence {b}"
+        seen += 1
+        if seen == 6:
+            break
+
+
 def test_workload_prefill_varlen_sampled():
     x = fa_synth.make_packed(**fa_synth.PACKED_WORKLOADS["prefill_varlen"])
     out, lse, _ = run_packed(x, "causal")
@@ -1184,10 +1216,11 @@ def test_scale_zero_gives_the_mean_of_visible_values(case, opts):
 
 
 # More query tiles of 256 rows than the device has CUs: the mask-free, the
-# window and (without per-batch lengths) the causal prefill at head dim 128
-# then run one persistent workgroup per CU that takes the tiles in turn,
-# fetching the next tile's Q and first K tile during the current one's last
-# slot; causal rounds alternate direction.
+# window and the causal prefill at head dim 128 then run one persistent
+# workgroup per CU that takes the tiles in turn, fetching the next tile's Q and
+# first K tile during the current one's last slot; causal rounds alternate
+# direction.  (The packed layout's persistent launch is tested with the packed
+# cases.)
 PERSISTENT_CASES = [
     (dict(B=3, QN=44, KVN=11, QS=300, KVS=300, D=128), (300, 0, 131), None, None),
     (dict(layout="BSND", B=3, QN=44, KVN=4, QS=300, KVS=333, D=128, dtype="f16"), (333, 77, 1),
@@ -1197,12 +1230,14 @@ PERSISTENT_CASES = [
     (dict(B=3, QN=44, KVN=4, QS=300, KVS=600, D=128, scale=1.0), None, (-1, 40), [300, 299, 1]),
     (dict(B=3, QN=44, KVN=4, QS=300, KVS=300, D=128), None, "causal", None),
     (dict(layout="BSND", B=1, QN=52, KVN=4, QS=1300, KVS=1400, D=128, dtype="f16"), None, "causal", None),
+    (dict(B=3, QN=44, KVN=4, QS=520, KVS=600, D=128, dtype="f16"), (600, 3, 311), "causal", [520, 520, 100]),
 ]
 
 
 @pytest.mark.parametrize("case,lens,mode,seqused", PERSISTENT_CASES,
                          ids=["none", "none_f16_bsnd_used", "window_back", "window_causal_used",
-                              "window_forward_rescale", "causal_partial_round", "causal_six_ranks"])
+                              "window_forward_rescale", "causal_partial_round", "causal_six_ranks",
+                              "causal_ragged_used"])
 def test_persistent_prefill_matches_oracle_and_per_batch_launches(case, lens, mode, seqused):
     """The persistent launch against the oracle, and bit for bit against each batch
     computed alone (fewer tiles than CUs: one workgroup per tile).  KV lengths include

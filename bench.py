@@ -242,7 +242,7 @@ def main():
                           "ms": round(pm, 5), "ms_p10_p90": [round(p10, 5), round(p90, 5)],
                           "tflops": round(tflops, 2),
                           "frac_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
-        out["roofline_prefill"] = {"kernel": "prefill_il_kernel<BF16,128,0,true> (persistent)", "bound": "mfma",
+        out["roofline_prefill"] = {"kernel": "prefill_il_kernel<BF16,128,0,true,false> (persistent)", "bound": "mfma",
                                    "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                                    "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                                    "traffic": traffic, "algorithmic_flop_per_launch": pre["flops"]}

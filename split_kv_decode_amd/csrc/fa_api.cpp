@@ -304,11 +304,14 @@ void plan_splits(const fa_params* p, const Shape& s, int num_cus, int64_t* split
                                                vector_masked_decode(p, s));
     const int64_t cus = num_cus > 0 ? num_cus : 256;
     int64_t per_cu = resident > 0 ? resident : kWgPerCu;
-    // The vector stage 1 streams best at four workgroups per CU (measured on
-    // MI355X: BNSD decodes 1.6-2.2 % faster than at the five that fit) when its
-    // units divide that many evenly; an uneven split leaves some CUs a fifth
-    // workgroup that sets the time, so the planner then fills what fits.
-    if (!mm && per_cu > kWgPerCu && (kWgPerCu * cus) % units == 0) per_cu = kWgPerCu;
+    // The vector stage 1 on a cache whose rows of one head are contiguous
+    // (BNSD, or paged with blocks per head) streams best at four workgroups per
+    // CU (measured on MI355X: 1.6-2.2 % faster than at the five that fit) when
+    // its units divide that many evenly; an uneven split leaves some CUs a
+    // fifth workgroup that sets the time, so the planner then fills what fits.
+    // (BSND caches measured either way between runs: they keep what fits.)
+    const bool head_rows = p->kv_layout == FA_KV_PAGED_BNBD || (p->kv_layout == FA_KV_CONTIGUOUS && p->layout == FA_BNSD);
+    if (!mm && head_rows && per_cu > kWgPerCu && (kWgPerCu * cus) % units == 0) per_cu = kWgPerCu;
     const int64_t target = per_cu * cus;
     int64_t want = (target + units - 1) / units;
     if (want < 1) want = 1;

@@ -756,7 +756,9 @@ __global__ __launch_bounds__(64 * il_waves<D>(), 1) void prefill_il_kernel(Prefi
     const int32_t rb32 = __builtin_amdgcn_readfirstlane((int32_t)row_bytes);
     // A persistent launch (PERSIST) runs one workgroup per CU over the units
     // blockIdx.x, blockIdx.x + gridDim.x, ... (gridDim.x is a multiple of 8,
-    // so every unit keeps the XCD the plain launch would give it).  The next
+    // so in these forward rounds every unit keeps the XCD the plain launch
+    // would give it); the packed layout's instantiation (PACKED) walks its
+    // work list the same way and skips the entries that pad it.  The next
     // unit's Q and first K tile are fetched during the current unit's last
     // slot, which reads neither Q nor a K buffer.
     // Causal costs fall with the rank and the units come heaviest first, so

@@ -1075,8 +1075,13 @@ __global__ __launch_bounds__(64 * il_waves<D>(), 1) void prefill_il_kernel(Prefi
                 __builtin_amdgcn_sched_barrier(0);
                 if constexpr (QK) {
                     const V8* kf = kring[kk % (PF + 1)];
+                    // Two waves share a SIMD at D = 128: the one issuing products takes
+                    // priority, which keeps the matrix core fed (at D = 256, one wave per
+                    // SIMD, the priority change only costs).
+                    if constexpr (NWV == 8) __builtin_amdgcn_s_setprio(1);
                     Sn[0] = M::mm(kf[0], qreg[kk], kk == 0 ? zero16 : Sn[0]);
                     Sn[1] = M::mm(kf[1], qreg[kk], kk == 0 ? zero16 : Sn[1]);
+                    if constexpr (NWV == 8) __builtin_amdgcn_s_setprio(0);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -1117,7 +1122,11 @@ __global__ __launch_bounds__(64 * il_waves<D>(), 1) void prefill_il_kernel(Prefi
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                if constexpr (PV) o[i % NDT] = M::mm(vring[i % (VPF + 1)], __builtin_bit_cast(V8, Po[i / NDT]), o[i % NDT]);
+                if constexpr (PV) {
+                    if constexpr (NWV == 8) __builtin_amdgcn_s_setprio(1);
+                    o[i % NDT] = M::mm(vring[i % (VPF + 1)], __builtin_bit_cast(V8, Po[i / NDT]), o[i % NDT]);
+                    if constexpr (NWV == 8) __builtin_amdgcn_s_setprio(0);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (SM) ps0 = acc;
